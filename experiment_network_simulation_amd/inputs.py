@@ -1,0 +1,539 @@
+"""Seeded synthetic inputs for the batched packet simulator.
+
+This module draws and lays out the *inputs* of a batch of independent network
+experiments: switched topologies (nodes, cables, rates, delays, dead cables),
+collective workloads (ring all-reduce / ring all-gather described by message
+size, channel count NC and chunk size C; K-partition pipelined broadcast; sparse
+explicit flows) and per-experiment parameters (queue depth, ECMP seed, packet
+size).  It performs none of the simulator's own arithmetic: it does not turn
+bytes into packets, split messages into channels/rounds/chunks, compute routes
+or simulate anything.  Both the HIP library and the CPU oracle consume exactly
+the arrays built here and derive everything else independently.
+
+The experiment shapes follow the pages:
+  * the usage model (Multiverse, section 3.1 "Architecture": the user sets
+    topology, workload and CCL parameters and lists the experiments to run),
+  * NCCL's channel count NC and chunk size C (AutoCCL, section 2.3, Table 2),
+  * the K-partition pipelined broadcast (AlpaComm, section 3.1, Fig. 3d),
+  * sparse variable-volume rank-to-rank traffic (Perplexity MoE blog, the
+    expert-parallel + data-parallel discussion).
+
+Random draws use SplitMix64 (Steele, Lea and Flood, "Fast splittable
+pseudorandom number generators", OOPSLA 2014; the public-domain reference
+constants of Vigna's splitmix64.c).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+# Node layers: hosts are layer 0; switches 1 (edge/leaf), 2 (agg/spine), 3 (core).
+LAYER_HOST = 0
+
+# Collective kinds (values are part of the C ABI and of the oracle's input).
+COLL_RING_AR = 1
+COLL_RING_AG = 2
+COLL_PIPE_BCAST = 3
+
+KIB = 1024
+MIB = 1024 * 1024
+PKT_BYTES = 4096
+
+_M64 = (1 << 64) - 1
+
+
+class SplitMix64:
+    """SplitMix64 generator (public-domain reference algorithm)."""
+
+    def __init__(self, seed: int):
+        self.state = seed & _M64
+
+    def next(self) -> int:
+        self.state = (self.state + 0x9E3779B97F4A7C15) & _M64
+        z = self.state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+        return z ^ (z >> 31)
+
+    def below(self, n: int) -> int:
+        """Integer in [0, n) (plain modulo reduction; n is tiny here)."""
+        return self.next() % n
+
+    def between(self, lo: int, hi: int) -> int:
+        """Integer in the inclusive range [lo, hi]."""
+        return lo + self.below(hi - lo + 1)
+
+    def u32(self) -> int:
+        return self.next() & 0xFFFFFFFF
+
+    def permutation(self, n: int) -> List[int]:
+        """Fisher-Yates shuffle of range(n), drawn from the high index down."""
+        a = list(range(n))
+        for i in range(n - 1, 0, -1):
+            j = self.below(i + 1)
+            a[i], a[j] = a[j], a[i]
+        return a
+
+
+def exp_rng(base: int, e: int) -> SplitMix64:
+    """Per-experiment stream: seeded with one SplitMix64 output of base ^ e."""
+    return SplitMix64(SplitMix64(base ^ e).next())
+
+
+# ---------------------------------------------------------------------------
+# Topologies
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Topology:
+    """Nodes (by layer) and cables.  A node's ports are numbered by the order in
+    which its cables appear here; rate_ab is the packets/tick from cable_a to
+    cable_b, delay the ticks per traversal (both directions)."""
+    layer: np.ndarray          # uint8 [n_nodes]
+    cable_a: np.ndarray        # uint32 [n_cables]
+    cable_b: np.ndarray        # uint32
+    rate_ab: np.ndarray        # uint8
+    rate_ba: np.ndarray        # uint8
+    delay: np.ndarray          # uint8
+    alive: np.ndarray          # uint8
+    name: str = ""
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.layer.shape[0])
+
+    @property
+    def n_cables(self) -> int:
+        return int(self.cable_a.shape[0])
+
+    def hosts(self) -> np.ndarray:
+        return np.nonzero(self.layer == LAYER_HOST)[0].astype(np.uint32)
+
+    def copy(self, name: Optional[str] = None) -> "Topology":
+        return Topology(self.layer.copy(), self.cable_a.copy(), self.cable_b.copy(),
+                        self.rate_ab.copy(), self.rate_ba.copy(), self.delay.copy(),
+                        self.alive.copy(), name if name is not None else self.name)
+
+
+def topology_from_cables(layers: Sequence[int], cables: Sequence[tuple], name: str = "") -> Topology:
+    """cables: (a, b[, rate_ab, rate_ba, delay, alive]) tuples, defaults 1,1,1,1."""
+    a, b, rab, rba, d, al = [], [], [], [], [], []
+    for c in cables:
+        c = tuple(c) + (1, 1, 1, 1)[len(c) - 2:]
+        a.append(c[0]); b.append(c[1]); rab.append(c[2]); rba.append(c[3]); d.append(c[4]); al.append(c[5])
+    return Topology(np.asarray(layers, np.uint8), np.asarray(a, np.uint32), np.asarray(b, np.uint32),
+                    np.asarray(rab, np.uint8), np.asarray(rba, np.uint8), np.asarray(d, np.uint8),
+                    np.asarray(al, np.uint8), name)
+
+
+def single_switch(n_hosts: int, rate: int = 1, delay: int = 1) -> Topology:
+    """Hosts 0..n-1 on one switch (node n); switch port i faces host i."""
+    layers = [LAYER_HOST] * n_hosts + [1]
+    cables = [(h, n_hosts, rate, rate, delay, 1) for h in range(n_hosts)]
+    return topology_from_cables(layers, cables, f"switch{n_hosts}")
+
+
+def leaf_spine(n_leaf: int, hosts_per_leaf: int, n_spine: int, host_rate: int = 1,
+               up_rate: int = 2, delay: int = 1) -> Topology:
+    """Hosts first (host = leaf*hosts_per_leaf + i), then leaves, then spines.
+    Leaf ports 0..hpl-1 face its hosts, then spines 0..n_spine-1; spine port l
+    faces leaf l."""
+    H = n_leaf * hosts_per_leaf
+    leaf0, spine0 = H, H + n_leaf
+    layers = [LAYER_HOST] * H + [1] * n_leaf + [2] * n_spine
+    cables = []
+    for h in range(H):
+        cables.append((h, leaf0 + h // hosts_per_leaf, host_rate, host_rate, delay, 1))
+    for l in range(n_leaf):
+        for s in range(n_spine):
+            cables.append((leaf0 + l, spine0 + s, up_rate, up_rate, delay, 1))
+    return topology_from_cables(layers, cables, f"leafspine{n_leaf}x{hosts_per_leaf}+{n_spine}")
+
+
+def fat_tree(k: int, rate: int = 1, delay: int = 1, oversub: int = 1) -> Topology:
+    """Standard k-ary fat-tree (k pods; k/2 edge and k/2 agg switches per pod;
+    (k/2)^2 cores).  Host id = pod*k^2/4 + edge*k/2 + i.  Edge ports 0..k/2-1 face
+    its hosts, then its aggs; agg ports 0..k/2-1 face the pod's edges, then its
+    cores; core c = a*(k/2)+j attaches to agg a of every pod, core port = pod.
+    With oversub o, edge e keeps only the aggs a with (a - e) mod (k/2) < (k/2)/o."""
+    h2 = k // 2
+    H = k * h2 * h2
+    n_edge = k * h2
+    edge0, agg0 = H, H + n_edge
+    core0 = agg0 + n_edge
+    layers = [LAYER_HOST] * H + [1] * n_edge + [2] * n_edge + [3] * (h2 * h2)
+    cables = []
+    for h in range(H):
+        cables.append((h, edge0 + h // h2, rate, rate, delay, 1))
+    keep = h2 // oversub
+    for p in range(k):
+        for e in range(h2):
+            for a in range(h2):
+                if (a - e) % h2 < keep:
+                    cables.append((edge0 + p * h2 + e, agg0 + p * h2 + a, rate, rate, delay, 1))
+    for p in range(k):
+        for a in range(h2):
+            for j in range(h2):
+                cables.append((agg0 + p * h2 + a, core0 + a * h2 + j, rate, rate, delay, 1))
+    return topology_from_cables(layers, cables, f"fattree{k}o{oversub}")
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Collective:
+    kind: int                  # COLL_RING_AR / COLL_RING_AG / COLL_PIPE_BCAST
+    nbytes: int                # message size (all-gather: total output size)
+    members: List[int]         # ring order, or broadcast chain (source first)
+    nc: int = 1                # channels (rings)
+    chunk_bytes: int = 0       # chunk size C (rings)
+    k: int = 1                 # partitions (broadcast)
+
+
+@dataclass
+class Workload:
+    colls: List[Collective] = field(default_factory=list)
+    xsrc: np.ndarray = field(default_factory=lambda: np.zeros(0, np.uint32))
+    xdst: np.ndarray = field(default_factory=lambda: np.zeros(0, np.uint32))
+    xpkts: np.ndarray = field(default_factory=lambda: np.zeros(0, np.uint32))
+
+
+def ring(kind: int, nbytes: int, members: Sequence[int], nc: int, chunk_bytes: int) -> Collective:
+    return Collective(kind, int(nbytes), [int(m) for m in members], int(nc), int(chunk_bytes), 1)
+
+
+def bcast(nbytes: int, chain: Sequence[int], k: int) -> Collective:
+    return Collective(COLL_PIPE_BCAST, int(nbytes), [int(m) for m in chain], 1, 0, int(k))
+
+
+def xflows(pairs: Sequence[tuple]) -> Workload:
+    """Explicit flows (src, dst, packets), kept in the given order."""
+    w = Workload()
+    if pairs:
+        arr = np.asarray(pairs, dtype=np.int64)
+        w.xsrc, w.xdst, w.xpkts = (arr[:, 0].astype(np.uint32), arr[:, 1].astype(np.uint32),
+                                   arr[:, 2].astype(np.uint32))
+    return w
+
+
+# ---------------------------------------------------------------------------
+# Batch
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Experiment:
+    topo: int
+    work: int
+    queue_pkts: int
+    ecmp_seed: int
+    pkt_bytes: int = PKT_BYTES
+
+
+@dataclass
+class Batch:
+    """A batch of experiments referencing shared topologies and workloads."""
+    topos: List[Topology]
+    works: List[Workload]
+    exps: List[Experiment]
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def n_exp(self) -> int:
+        return len(self.exps)
+
+    def subset(self, idx: Sequence[int]) -> "Batch":
+        """The listed experiments, with only the topologies/workloads they use."""
+        idx = list(idx)
+        tmap, wmap, topos, works, exps = {}, {}, [], [], []
+        for i in idx:
+            x = self.exps[i]
+            if x.topo not in tmap:
+                tmap[x.topo] = len(topos); topos.append(self.topos[x.topo])
+            if x.work not in wmap:
+                wmap[x.work] = len(works); works.append(self.works[x.work])
+            exps.append(Experiment(tmap[x.topo], wmap[x.work], x.queue_pkts, x.ecmp_seed, x.pkt_bytes))
+        meta = dict(self.meta)
+        meta["subset_of"] = self.name
+        meta["subset_idx"] = idx
+        return Batch(topos, works, exps, self.name, meta)
+
+    def pack(self) -> "PackedBatch":
+        return PackedBatch.from_batch(self)
+
+
+@dataclass
+class PackedBatch:
+    """Flat CSR arrays in the exact layout both consumers read."""
+    n_topo: int
+    n_work: int
+    n_exp: int
+    topo_node_off: np.ndarray    # uint32 [n_topo+1]
+    node_layer: np.ndarray       # uint8
+    topo_cable_off: np.ndarray   # uint32 [n_topo+1]
+    cable_a: np.ndarray          # uint32 (node index local to its topology)
+    cable_b: np.ndarray
+    cable_rate_ab: np.ndarray    # uint8
+    cable_rate_ba: np.ndarray
+    cable_delay: np.ndarray
+    cable_alive: np.ndarray
+    work_coll_off: np.ndarray    # uint32 [n_work+1]
+    coll_type: np.ndarray        # uint8
+    coll_bytes: np.ndarray       # uint64
+    coll_nc: np.ndarray          # uint32
+    coll_chunk_bytes: np.ndarray # uint32
+    coll_k: np.ndarray           # uint32
+    coll_member_off: np.ndarray  # uint32 [n_coll+1]
+    member_host: np.ndarray      # uint32
+    work_xflow_off: np.ndarray   # uint64 [n_work+1]
+    xflow_src: np.ndarray        # uint32
+    xflow_dst: np.ndarray
+    xflow_pkts: np.ndarray
+    exp_topo: np.ndarray         # uint32 [n_exp]
+    exp_work: np.ndarray
+    exp_queue_pkts: np.ndarray
+    exp_ecmp_seed: np.ndarray
+    exp_pkt_bytes: np.ndarray
+
+    @staticmethod
+    def from_batch(b: Batch) -> "PackedBatch":
+        def cat(xs, dt):
+            return np.ascontiguousarray(np.concatenate(xs).astype(dt)) if xs else np.zeros(0, dt)
+
+        t_node_off = np.zeros(len(b.topos) + 1, np.uint32)
+        t_cab_off = np.zeros(len(b.topos) + 1, np.uint32)
+        for i, t in enumerate(b.topos):
+            t_node_off[i + 1] = t_node_off[i] + t.n_nodes
+            t_cab_off[i + 1] = t_cab_off[i] + t.n_cables
+        colls = [c for w in b.works for c in w.colls]
+        w_coll_off = np.zeros(len(b.works) + 1, np.uint32)
+        w_x_off = np.zeros(len(b.works) + 1, np.uint64)
+        for i, w in enumerate(b.works):
+            w_coll_off[i + 1] = w_coll_off[i] + len(w.colls)
+            w_x_off[i + 1] = w_x_off[i] + len(w.xsrc)
+        m_off = np.zeros(len(colls) + 1, np.uint32)
+        for i, c in enumerate(colls):
+            m_off[i + 1] = m_off[i] + len(c.members)
+        return PackedBatch(
+            n_topo=len(b.topos), n_work=len(b.works), n_exp=len(b.exps),
+            topo_node_off=t_node_off,
+            node_layer=cat([t.layer for t in b.topos], np.uint8),
+            topo_cable_off=t_cab_off,
+            cable_a=cat([t.cable_a for t in b.topos], np.uint32),
+            cable_b=cat([t.cable_b for t in b.topos], np.uint32),
+            cable_rate_ab=cat([t.rate_ab for t in b.topos], np.uint8),
+            cable_rate_ba=cat([t.rate_ba for t in b.topos], np.uint8),
+            cable_delay=cat([t.delay for t in b.topos], np.uint8),
+            cable_alive=cat([t.alive for t in b.topos], np.uint8),
+            work_coll_off=w_coll_off,
+            coll_type=np.asarray([c.kind for c in colls], np.uint8),
+            coll_bytes=np.asarray([c.nbytes for c in colls], np.uint64),
+            coll_nc=np.asarray([c.nc for c in colls], np.uint32),
+            coll_chunk_bytes=np.asarray([c.chunk_bytes for c in colls], np.uint32),
+            coll_k=np.asarray([c.k for c in colls], np.uint32),
+            coll_member_off=m_off,
+            member_host=np.asarray([m for c in colls for m in c.members], np.uint32),
+            work_xflow_off=w_x_off,
+            xflow_src=cat([w.xsrc for w in b.works], np.uint32),
+            xflow_dst=cat([w.xdst for w in b.works], np.uint32),
+            xflow_pkts=cat([w.xpkts for w in b.works], np.uint32),
+            exp_topo=np.asarray([x.topo for x in b.exps], np.uint32),
+            exp_work=np.asarray([x.work for x in b.exps], np.uint32),
+            exp_queue_pkts=np.asarray([x.queue_pkts for x in b.exps], np.uint32),
+            exp_ecmp_seed=np.asarray([x.ecmp_seed & 0xFFFFFFFF for x in b.exps], np.uint32),
+            exp_pkt_bytes=np.asarray([x.pkt_bytes for x in b.exps], np.uint32),
+        )
+
+
+def single_batch(topo: Topology, work: Workload, queue_pkts: int = 16, ecmp_seed: int = 0,
+                 pkt_bytes: int = PKT_BYTES, name: str = "custom") -> Batch:
+    return Batch([topo], [work], [Experiment(0, 0, queue_pkts, ecmp_seed, pkt_bytes)], name)
+
+
+# ---------------------------------------------------------------------------
+# The five benchmark configurations
+# ---------------------------------------------------------------------------
+
+BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5}
+FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000}
+CONFIG_NAMES = {
+    1: "C1 ring all-reduce 1 MiB, 8 hosts on one switch, NC x C grid",
+    2: "C2 ring all-reduce 64 MiB over a 4x8 leaf-spine with 4 spines",
+    3: "C3 pipelined broadcast 64 MiB to A hosts, K partitions, random delays",
+    4: "C4 k=8 fat-tree: 16 DP ring all-reduces 256 MiB + 16 TP ring all-gathers 56 MiB",
+    5: "C5 k=16 fat-tree sweep: Zipf(1.1) sparse all-to-all, 8 MiB per host",
+}
+
+
+def _c1(e_list):
+    topo = single_switch(8, 1, 1)
+    works, exps = [], []
+    ncs, chunks = [1, 2, 4, 8], [16, 32, 64, 128]
+    for e in e_list:
+        nc, ck = ncs[(e // 4) % 4], chunks[e % 4]
+        works.append(Workload([ring(COLL_RING_AR, 1 * MIB, range(8), nc, ck * KIB)]))
+        exps.append(Experiment(0, len(works) - 1, 16, 0))
+    return Batch([topo], works, exps, "C1")
+
+
+def _c2(e_list):
+    topo = leaf_spine(4, 8, 4, host_rate=1, up_rate=2, delay=1)
+    works, exps = [], []
+    for e in e_list:
+        g = exp_rng(BASE_SEED[2], e)
+        nc = g.between(1, 16)
+        ck = 4 * KIB * g.between(8, 128)
+        seed = g.u32()
+        works.append(Workload([ring(COLL_RING_AR, 64 * MIB, range(32), nc, ck)]))
+        exps.append(Experiment(0, len(works) - 1, 32, seed))
+    return Batch([topo], works, exps, "C2")
+
+
+_C3_A = [2, 4, 8, 16]
+_C3_K = [1, 2, 4, 8, 16, 32, 64]
+
+
+def _c3(e_list):
+    base = leaf_spine(4, 8, 4, host_rate=1, up_rate=2, delay=1)
+    topos, works, exps = [], [], []
+    for e in e_list:
+        g = exp_rng(BASE_SEED[3], e)
+        cell = e % 28
+        A, K = _C3_A[cell // 7], _C3_K[cell % 7]
+        t = base.copy(f"leafspine-c3-e{e}")
+        t.delay = np.asarray([g.between(1, 4) for _ in range(t.n_cables)], np.uint8)
+        perm = g.permutation(32)
+        seed = g.u32()
+        topos.append(t)
+        works.append(Workload([bcast(64 * MIB, perm[:A + 1], K)]))
+        exps.append(Experiment(len(topos) - 1, len(works) - 1, 32, seed))
+    return Batch(topos, works, exps, "C3")
+
+
+def fat_tree_reachable(k: int, alive_ea: np.ndarray, alive_ac: np.ndarray) -> bool:
+    """True if every pair of edge switches of a k-ary fat-tree is joined by an
+    up-then-down path.  alive_ea[p, e, a]: edge e - agg a cable of pod p alive;
+    alive_ac[p, a, j]: agg a of pod p - core a*(k/2)+j alive.  Input feasibility
+    check for the failure draw (edge switch pairs cover every host pair)."""
+    # cp[p1, p2, a]: some core of group a is alive towards both pods.
+    cp = np.einsum("paj,qaj->pqa", alive_ac.astype(np.int64), alive_ac.astype(np.int64)) > 0
+    same_pod = np.eye(k, dtype=bool)[:, :, None]
+    link = cp | same_pod                                     # [p1, p2, a]
+    ea = alive_ea.astype(bool)                               # [p, e, a]
+    # reach[p1, e1, p2, e2] = any_a ea[p1,e1,a] & ea[p2,e2,a] & link[p1,p2,a]
+    reach = np.einsum("pea,qfa,pqa->peqf", ea.astype(np.int64), ea.astype(np.int64),
+                      link.astype(np.int64)) > 0
+    h2 = k // 2
+    eye = np.zeros((k, h2, k, h2), bool)
+    for p in range(k):
+        for e in range(h2):
+            eye[p, e, p, e] = True
+    return bool(np.all(reach | eye))
+
+
+def _c4_groups():
+    tp = [[8 * t + i for i in range(8)] for t in range(16)]
+    dp = [[g + 16 * j for j in range(8)] for g in range(16)]
+    return dp, tp
+
+
+def _c4(e_list):
+    k = 8
+    base = fat_tree(k, 1, 1)
+    h2 = k // 2
+    H = k * h2 * h2
+    n_host_cables = H
+    n_ea = k * h2 * h2
+    dp, tp = _c4_groups()
+    topos, works, exps = [], [], []
+    for e in e_list:
+        g = exp_rng(BASE_SEED[4], e)
+        pi = g.permutation(H)
+        nc = g.between(1, 16)
+        ck = 4 * KIB * g.between(8, 128)
+        nfail = g.between(0, 4)
+        while True:
+            pool = list(range(n_host_cables, base.n_cables))   # the 256 switch-to-switch cables
+            dead = []
+            for _ in range(nfail):
+                j = g.below(len(pool))
+                dead.append(pool.pop(j))
+            alive = np.ones(base.n_cables, np.uint8)
+            alive[dead] = 0
+            sw = alive[n_host_cables:]
+            a_ea = sw[:n_ea].reshape(k, h2, h2)
+            a_ac = sw[n_ea:].reshape(k, h2, h2)
+            if fat_tree_reachable(k, a_ea, a_ac):
+                break
+        seed = g.u32()
+        t = base.copy(f"fattree8-e{e}")
+        t.alive = alive
+        topos.append(t)
+        colls = [ring(COLL_RING_AR, 256 * MIB, [pi[r] for r in grp], nc, ck) for grp in dp]
+        colls += [ring(COLL_RING_AG, 56 * MIB, [pi[r] for r in grp], nc, ck) for grp in tp]
+        works.append(Workload(colls))
+        exps.append(Experiment(len(topos) - 1, len(works) - 1, 16, seed))
+    return Batch(topos, works, exps, "C4")
+
+
+def zipf_alltoall(n_hosts: int, pkts_per_src: int, s: float, seed: int) -> Workload:
+    """Per source, a seeded permutation ranks the other hosts; rank j (1-based)
+    gets weight j^-s; weights are scaled to pkts_per_src packets by largest
+    remainder (ties to the lower rank); zero-packet pairs carry no flow.  Flows
+    are listed by source, then destination id."""
+    g = SplitMix64(seed)
+    j = np.arange(1, n_hosts, dtype=np.float64)
+    w = j ** (-s)
+    q = pkts_per_src * w / w.sum()
+    base = np.floor(q).astype(np.int64)
+    rem = pkts_per_src - int(base.sum())
+    frac = q - base
+    order = np.argsort(-frac, kind="stable")
+    cnt = base.copy()
+    cnt[order[:rem]] += 1
+    src, dst, pk = [], [], []
+    for h in range(n_hosts):
+        others = [x for x in range(n_hosts) if x != h]
+        perm = g.permutation(n_hosts - 1)
+        per_dst = np.zeros(n_hosts, np.int64)
+        for rank, pi in enumerate(perm):
+            per_dst[others[pi]] = cnt[rank]
+        nz = np.nonzero(per_dst)[0]
+        src.append(np.full(nz.shape, h)); dst.append(nz); pk.append(per_dst[nz])
+    wl = Workload()
+    wl.xsrc = np.concatenate(src).astype(np.uint32)
+    wl.xdst = np.concatenate(dst).astype(np.uint32)
+    wl.xpkts = np.concatenate(pk).astype(np.uint32)
+    return wl
+
+
+def _c5(e_list, k: int = 16):
+    topos = [fat_tree(k, 1, 1, o) for o in (1, 2, 4)]
+    H = k * (k // 2) ** 2
+    work = zipf_alltoall(H, (8 * MIB) // PKT_BYTES, 1.1, BASE_SEED[5])
+    exps = []
+    for e in e_list:
+        g = exp_rng(BASE_SEED[5], e)
+        oi = g.below(3)
+        q = g.between(16, 128)
+        seed = g.u32()
+        exps.append(Experiment(oi, 0, q, seed))
+    return Batch(topos, [work], exps, "C5")
+
+
+def make_config(cid: int, n_exp: Optional[int] = None, exp_ids: Optional[Sequence[int]] = None) -> Batch:
+    """Batch for benchmark configuration cid (1..5).  Experiment e of a config is
+    the same whatever subset is drawn, so exp_ids picks a sample of the full
+    batch and n_exp the first n experiments."""
+    if exp_ids is None:
+        exp_ids = range(FULL_E[cid] if n_exp is None else n_exp)
+    e_list = list(exp_ids)
+    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5}[cid](e_list)
+    b.meta["config"] = cid
+    b.meta["exp_ids"] = e_list
+    return b

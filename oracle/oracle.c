@@ -1,0 +1,869 @@
+/*
+ * oracle.c -- plain, slow CPU reference of the batched packet simulator.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load
+ * this file; only the test-suite, the smoke check and the benchmark's CPU
+ * baseline use it.  It shares no code, header, table or helper with the HIP
+ * library: the two read the same generator arrays and compute everything else
+ * on their own.
+ *
+ * What it computes (one experiment at a time, tick by tick):
+ *   Multiverse ("Accelerating Design Space Exploration for LLM Training Systems
+ *   with Multi-experiment Parallel Simulation"), section 3.2 "System execution
+ *   graph": every simulation step runs Schedule -> Send -> NIC send -> Forward ->
+ *   Transmit -> NIC receive in a fixed order; section 4.2 "Pull-based data
+ *   synchronisation": each ingress keeps a to-do set of egress ports and each
+ *   egress pulls from the ingresses; section 5 "Implementation": the step is the
+ *   smallest link delay, flows come from NCCL's ring algorithms, ECMP balances
+ *   load.  AutoCCL ("Automated Collective Communication Tuning"), section 2.3:
+ *   a message is cut into NC channels processed concurrently, and each channel
+ *   moves its chunks of size C one after the other.  AlpaComm ("On Optimizing
+ *   the Communication of Model Parallelism"), section 3.1, Fig. 3d: a receiver
+ *   forwards a partition once it holds all of it.
+ *
+ * Where the pages leave a step open, the plainest reading is taken; every such
+ * reading is one of the numbered tick rules below.
+ *
+ * Tick rules (integer time; one tick = the smallest link delay):
+ *  R1  A message of B bytes is ceil(B / pkt_bytes) packets.
+ *  R2  A node's ports are numbered by the order of its cables in the input.
+ *      Every host has exactly one cable.  Cables join nodes of different layers.
+ *  R3  Every switch ingress port has room for Q packets.  The room counts every
+ *      packet sent on the cable into it and not yet forwarded, also packets still
+ *      on the wire.  Inside, one FIFO per egress port (virtual output queue) in
+ *      sending order.  A packet is eligible once its arrival tick <= t.  Hosts
+ *      take every packet.
+ *  R4  Routing: at a node, the candidates for destination host h are the alive
+ *      ports whose neighbour lies on a shortest up-then-down path to h (moves to
+ *      a higher layer, then moves to a lower one), in port order; a connection
+ *      picks cand[H mod |cand|] with H = fmix32(key ^ fmix32(node ^ seed)),
+ *      fmix32 being MurmurHash3's 32-bit finaliser; key = connection index.
+ *  R5  A flow is (connection, size >= 1 packets, predecessors).  A predecessor is
+ *      RECV (its last packet has arrived: RD <= t) or SEND (its last packet has
+ *      left: SD <= t, SD = tick of the last send + 1).  The flows of a connection
+ *      are chained by SEND predecessors.
+ *  R6  Phases of tick t:
+ *      A  packets with arrival tick t reach their host: the flow's received count
+ *         grows; at its size, RD = t.
+ *      B  a not yet active flow whose predecessors are all met becomes active
+ *         (activation tick t).
+ *      C  every output takes credit = Q - occupancy of the ingress it feeds
+ *         (occupancy as left by tick t-1; no limit towards a host).
+ *      D  rounds m = 0 .. R-1 (R = largest rate).  In round m every alive output
+ *         with m < rate and credit > 0 grants the first candidate input found
+ *         going round from its pointer rr: at a switch the ingress ports whose
+ *         FIFO for this output has an eligible head; at a host its connections
+ *         (in connection index order) whose active flow still has packets to
+ *         send.  The packet leaves with arrival tick t + delay, credit drops by
+ *         one, rr becomes the granted input + 1.  All grants of a round are
+ *         decided on the state at the start of the round.  A flow whose last
+ *         packet leaves gets SD = t + 1.
+ *      E  done once every flow has an RD; completion tick = the largest RD.  A
+ *         tick with no sending, no activation and nothing on the wire, while not
+ *         done, is a deadlock at that tick.
+ *  W1  Ring all-reduce / all-gather over members m_0..m_{N-1} (rank i sends to
+ *      rank i+1 mod N): P packets; channel c carries P/NC + [c < P mod NC];
+ *      p = chunk_bytes / pkt_bytes; rounds R_c = ceil(P_c / (N p)), the last
+ *      one folded into the previous one when it would hold fewer than N packets;
+ *      a round of X packets has chunks k of X/N + [k < X mod N] packets.
+ *      All-reduce has 2(N-1) steps, all-gather N-1.  At step s rank i sends chunk
+ *      (i - s) mod N (all-gather, and the first N-1 all-reduce steps) or
+ *      (i + 1 - (s - N + 1)) mod N (the later all-reduce steps) to rank i+1.
+ *      Predecessors of flow (c, r, s, i): s >= 1: RECV (c, r, s-1, i-1) and
+ *      SEND (c, r, s-1, i); s = 0, r >= 1: SEND (c, r-1, S-1, i).
+ *  W2  Pipelined broadcast along h_0 (source), h_1 .. h_A with K partitions of
+ *      P/K + [k < P mod K] packets: flow (j, k) runs h_{j-1} -> h_j with
+ *      predecessors RECV (j-1, k) for j >= 2 and SEND (j, k-1) for k >= 1.
+ *  W3  Explicit flows: one connection and one flow each, no predecessors.
+ *  Numbering: connections and flows follow the input order of collectives, then
+ *  explicit flows; a ring numbers its connections by (channel, rank) and its
+ *  flows by (channel, round, step, rank); a broadcast by hop, and (hop, part).
+ *  Digest = sum over flows of mix64((flow << 32) | RD) mod 2^64, mix64 being
+ *  SplitMix64's output function.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_S_INCOMPLETE 1
+#define ORC_S_DEADLOCK 2
+#define ORC_E_INVALID (-1)
+#define ORC_E_UNROUTABLE (-2)
+#define ORC_E_NOMEM (-3)
+#define ORC_E_INVARIANT (-4)
+
+#define NONE 0xFFFFFFFFu
+#define INF_DIST 0x3FFFFFFF
+
+enum { KIND_RING_AR = 1, KIND_RING_AG = 2, KIND_BCAST = 3 };
+enum { PRED_RECV = 0, PRED_SEND = 1 };
+
+/* The batch, exactly as the input generator lays it out. */
+typedef struct {
+    uint32_t n_topo, n_work, n_exp, pad;
+    const uint32_t *topo_node_off;
+    const uint8_t *node_layer;
+    const uint32_t *topo_cable_off;
+    const uint32_t *cable_a, *cable_b;
+    const uint8_t *cable_rate_ab, *cable_rate_ba, *cable_delay, *cable_alive;
+    const uint32_t *work_coll_off;
+    const uint8_t *coll_type;
+    const uint64_t *coll_bytes;
+    const uint32_t *coll_nc, *coll_chunk_bytes, *coll_k, *coll_member_off, *member_host;
+    const uint64_t *work_xflow_off;
+    const uint32_t *xflow_src, *xflow_dst, *xflow_pkts;
+    const uint32_t *exp_topo, *exp_work, *exp_queue_pkts, *exp_ecmp_seed, *exp_pkt_bytes;
+} orc_batch;
+
+typedef struct {
+    int32_t status;        /* ORC_OK (done), ORC_S_INCOMPLETE, ORC_S_DEADLOCK */
+    uint32_t t_end;        /* completion tick, deadlock tick, or ticks run */
+    uint64_t pkt_hops;     /* transmissions on every link, host NICs included */
+    uint64_t delivered;    /* packets received by hosts */
+    uint64_t digest;
+    uint64_t n_flows;
+    uint64_t n_conns;
+    uint32_t max_occupancy;/* largest switch ingress occupancy seen */
+    uint32_t pad;
+} orc_result;
+
+/* ------------------------------------------------------------------ mixers */
+
+static uint32_t fmix32(uint32_t h)
+{
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+static uint64_t mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+static uint32_t ecmp_hash(uint32_t key, uint32_t node, uint32_t seed)
+{
+    return fmix32(key ^ fmix32(node ^ seed));
+}
+
+/* ------------------------------------------------------------- structures */
+
+typedef struct {
+    uint32_t flow;      /* flow id the packet belongs to */
+    uint32_t arrive;    /* arrival tick at the next node */
+    uint32_t hop;       /* index in the connection's path of the node it reaches */
+} Pkt;
+
+typedef struct {       /* FIFO of packets (ring buffer of fixed capacity) */
+    Pkt *buf;
+    uint32_t cap, head, count;
+} Fifo;
+
+typedef struct {
+    uint32_t node;       /* owner */
+    uint32_t peer_node;
+    uint32_t peer_port;  /* global port index of the far end */
+    uint32_t rate;       /* packets/tick leaving through this port */
+    uint32_t delay;
+    uint32_t alive;
+    uint32_t rr;         /* round-robin pointer of the output */
+    uint32_t occ;        /* switch ingress: packets sent into it, not yet forwarded */
+    int64_t credit;      /* phase C snapshot, consumed during phase D */
+    uint32_t granted;    /* phase D decision of the current round (input index or NONE) */
+    Fifo *voq;           /* switch ingress: one FIFO per egress port of the node */
+    Fifo wire;           /* host ingress: packets on the way to the host */
+} Port;
+
+typedef struct {
+    uint32_t conn, size;
+    uint32_t npred;
+    uint32_t pred[2];
+    uint32_t pkind[2];
+    uint32_t sent, recvd, active;
+    uint32_t act, sd, rd;
+} Flow;
+
+typedef struct {
+    uint32_t src, dst;
+    uint32_t flow_off, nflow;   /* its flows, in sending order, in conn_flows */
+    uint32_t cur;               /* position of the flow being / next to be sent */
+    uint32_t path_off, path_len;/* nodes and egress ports from source host to destination host */
+    uint32_t recv_pos;          /* position of the earliest flow not fully received */
+} Conn;
+
+typedef struct {
+    /* topology */
+    uint32_t n_nodes, n_ports;
+    const uint8_t *layer;
+    uint32_t *port_off;         /* n_nodes + 1 */
+    Port *port;
+    /* workload */
+    uint32_t n_conn, n_flow;
+    Conn *conn;
+    Flow *flow;
+    uint32_t *conn_flows;
+    uint32_t *path_node, *path_port; /* egress local port at each path node */
+    /* per host: its connections in index order */
+    uint32_t *host_conn_off, *host_conn;
+    uint32_t Q, seed, R;
+} Exp;
+
+static void fifo_free(Fifo *f) { free(f->buf); f->buf = NULL; }
+
+static int fifo_init(Fifo *f, uint32_t cap)
+{
+    f->buf = (Pkt *)calloc(cap ? cap : 1, sizeof(Pkt));
+    f->cap = cap ? cap : 1;
+    f->head = f->count = 0;
+    return f->buf ? 0 : -1;
+}
+
+static int fifo_push(Fifo *f, Pkt p)
+{
+    if (f->count == f->cap) {            /* grow: only host wires can need it */
+        uint32_t ncap = f->cap * 2;
+        Pkt *nb = (Pkt *)malloc(sizeof(Pkt) * ncap);
+        if (!nb) return -1;
+        for (uint32_t i = 0; i < f->count; i++) nb[i] = f->buf[(f->head + i) % f->cap];
+        free(f->buf);
+        f->buf = nb; f->cap = ncap; f->head = 0;
+    }
+    f->buf[(f->head + f->count) % f->cap] = p;
+    f->count++;
+    return 0;
+}
+
+static Pkt *fifo_front(Fifo *f) { return f->count ? &f->buf[f->head] : NULL; }
+
+static Pkt fifo_pop(Fifo *f)
+{
+    Pkt p = f->buf[f->head];
+    f->head = (f->head + 1) % f->cap;
+    f->count--;
+    return p;
+}
+
+static void exp_free(Exp *x)
+{
+    if (x->port) {
+        for (uint32_t p = 0; p < x->n_ports; p++) {
+            if (x->port[p].voq) {
+                uint32_t n = x->port_off[x->port[p].node + 1] - x->port_off[x->port[p].node];
+                for (uint32_t o = 0; o < n; o++) fifo_free(&x->port[p].voq[o]);
+                free(x->port[p].voq);
+            }
+            fifo_free(&x->port[p].wire);
+        }
+    }
+    free(x->port_off); free(x->port); free(x->conn); free(x->flow); free(x->conn_flows);
+    free(x->path_node); free(x->path_port); free(x->host_conn_off); free(x->host_conn);
+    memset(x, 0, sizeof(*x));
+}
+
+static uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+/* -------------------------------------------------------------- topology */
+
+static int build_topology(const orc_batch *b, uint32_t e, Exp *x)
+{
+    uint32_t t = b->exp_topo[e];
+    uint32_t n0 = b->topo_node_off[t], n1 = b->topo_node_off[t + 1];
+    uint32_t c0 = b->topo_cable_off[t], c1 = b->topo_cable_off[t + 1];
+    x->n_nodes = n1 - n0;
+    x->layer = b->node_layer + n0;
+    x->port_off = (uint32_t *)calloc(x->n_nodes + 1, sizeof(uint32_t));
+    if (!x->port_off) return ORC_E_NOMEM;
+    /* count ports per node (R2) */
+    for (uint32_t c = c0; c < c1; c++) {
+        uint32_t a = b->cable_a[c], bb = b->cable_b[c];
+        if (a >= x->n_nodes || bb >= x->n_nodes || a == bb) return ORC_E_INVALID;
+        if (x->layer[a] == x->layer[bb]) return ORC_E_INVALID;
+        if (b->cable_rate_ab[c] < 1 || b->cable_rate_ba[c] < 1 || b->cable_delay[c] < 1) return ORC_E_INVALID;
+        x->port_off[a + 1]++;
+        x->port_off[bb + 1]++;
+    }
+    for (uint32_t n = 0; n < x->n_nodes; n++) {
+        if (x->layer[n] == 0 && x->port_off[n + 1] != 1) return ORC_E_INVALID;
+        x->port_off[n + 1] += x->port_off[n];
+    }
+    x->n_ports = x->port_off[x->n_nodes];
+    x->port = (Port *)calloc(x->n_ports ? x->n_ports : 1, sizeof(Port));
+    uint32_t *fill = (uint32_t *)calloc(x->n_nodes, sizeof(uint32_t));
+    if (!x->port || !fill) { free(fill); return ORC_E_NOMEM; }
+    x->R = 1;
+    for (uint32_t c = c0; c < c1; c++) {
+        uint32_t a = b->cable_a[c], bb = b->cable_b[c];
+        uint32_t pa = x->port_off[a] + fill[a]++;
+        uint32_t pb = x->port_off[bb] + fill[bb]++;
+        x->port[pa].node = a; x->port[pa].peer_node = bb; x->port[pa].peer_port = pb;
+        x->port[pa].rate = b->cable_rate_ab[c];
+        x->port[pb].node = bb; x->port[pb].peer_node = a; x->port[pb].peer_port = pa;
+        x->port[pb].rate = b->cable_rate_ba[c];
+        x->port[pa].delay = x->port[pb].delay = b->cable_delay[c];
+        x->port[pa].alive = x->port[pb].alive = b->cable_alive[c] ? 1 : 0;
+        if (b->cable_rate_ab[c] > x->R) x->R = b->cable_rate_ab[c];
+        if (b->cable_rate_ba[c] > x->R) x->R = b->cable_rate_ba[c];
+    }
+    free(fill);
+    for (uint32_t p = 0; p < x->n_ports; p++) {
+        Port *pp = &x->port[p];
+        pp->granted = NONE;
+        if (x->layer[pp->node] != 0) {
+            uint32_t deg = x->port_off[pp->node + 1] - x->port_off[pp->node];
+            pp->voq = (Fifo *)calloc(deg, sizeof(Fifo));
+            if (!pp->voq) return ORC_E_NOMEM;
+            for (uint32_t o = 0; o < deg; o++)
+                if (fifo_init(&pp->voq[o], x->Q)) return ORC_E_NOMEM;
+        } else {
+            if (fifo_init(&pp->wire, 64)) return ORC_E_NOMEM;
+        }
+    }
+    return ORC_OK;
+}
+
+/* --------------------------------------------------------------- workload */
+
+/* Chunk sent by rank i at step s (W1). */
+static uint32_t ring_chunk(uint32_t kind, uint32_t N, uint32_t i, uint32_t s)
+{
+    if (kind == KIND_RING_AG || s < N - 1) return (uint32_t)(((int64_t)i - s % N + N) % N);
+    uint32_t s2 = s - (N - 1);
+    return (uint32_t)(((int64_t)i + 1 - s2 + 2 * (int64_t)N) % N);
+}
+
+/* Appends one connection; returns its index. */
+static uint32_t add_conn(Exp *x, uint32_t src, uint32_t dst)
+{
+    Conn *c = &x->conn[x->n_conn];
+    memset(c, 0, sizeof(*c));
+    c->src = src; c->dst = dst;
+    return x->n_conn++;
+}
+
+/* Counts connections and flows of the workload (first pass), validating it. */
+static int count_workload(const orc_batch *b, uint32_t e, uint64_t *nconn, uint64_t *nflow)
+{
+    uint32_t w = b->exp_work[e], t = b->exp_topo[e];
+    uint32_t nn = b->topo_node_off[t + 1] - b->topo_node_off[t];
+    const uint8_t *layer = b->node_layer + b->topo_node_off[t];
+    uint64_t pkt = b->exp_pkt_bytes[e];
+    if (pkt == 0) return ORC_E_INVALID;
+    *nconn = 0; *nflow = 0;
+    for (uint32_t ci = b->work_coll_off[w]; ci < b->work_coll_off[w + 1]; ci++) {
+        uint32_t m0 = b->coll_member_off[ci], m1 = b->coll_member_off[ci + 1];
+        uint32_t N = m1 - m0;
+        for (uint32_t m = m0; m < m1; m++) {
+            if (b->member_host[m] >= nn || layer[b->member_host[m]] != 0) return ORC_E_INVALID;
+            for (uint32_t m2 = m0; m2 < m; m2++)
+                if (b->member_host[m2] == b->member_host[m]) return ORC_E_INVALID;
+        }
+        uint64_t P = ceil_div(b->coll_bytes[ci], pkt);
+        uint32_t kind = b->coll_type[ci];
+        if (kind == KIND_RING_AR || kind == KIND_RING_AG) {
+            uint32_t NC = b->coll_nc[ci];
+            if (N < 2 || NC < 1 || b->coll_chunk_bytes[ci] == 0 || b->coll_chunk_bytes[ci] % pkt) return ORC_E_INVALID;
+            uint64_t p = b->coll_chunk_bytes[ci] / pkt;
+            uint64_t S = kind == KIND_RING_AR ? 2ull * (N - 1) : (uint64_t)(N - 1);
+            for (uint32_t c = 0; c < NC; c++) {
+                uint64_t Pc = P / NC + (c < P % NC);
+                if (Pc < N) return ORC_E_INVALID;
+                uint64_t R = ceil_div(Pc, (uint64_t)N * p);
+                if (R > 1 && Pc - (R - 1) * N * p < N) R--;
+                *nflow += R * S * N;
+                *nconn += N;
+            }
+        } else if (kind == KIND_BCAST) {
+            uint64_t K = b->coll_k[ci];
+            if (N < 2 || K < 1 || K > P) return ORC_E_INVALID;
+            *nconn += N - 1;
+            *nflow += (uint64_t)(N - 1) * K;
+        } else {
+            return ORC_E_INVALID;
+        }
+    }
+    for (uint64_t xi = b->work_xflow_off[w]; xi < b->work_xflow_off[w + 1]; xi++) {
+        uint32_t s = b->xflow_src[xi], d = b->xflow_dst[xi];
+        if (s >= nn || d >= nn || s == d || layer[s] != 0 || layer[d] != 0 || b->xflow_pkts[xi] == 0)
+            return ORC_E_INVALID;
+        *nconn += 1; *nflow += 1;
+    }
+    if (*nflow >= NONE || *nconn >= NONE) return ORC_E_INVALID;
+    return ORC_OK;
+}
+
+static void set_flow(Exp *x, uint32_t f, uint32_t conn, uint32_t size)
+{
+    Flow *fl = &x->flow[f];
+    memset(fl, 0, sizeof(*fl));
+    fl->conn = conn; fl->size = size;
+    fl->act = fl->sd = fl->rd = NONE;
+}
+
+static void add_pred(Exp *x, uint32_t f, uint32_t g, uint32_t kind)
+{
+    Flow *fl = &x->flow[f];
+    fl->pred[fl->npred] = g;
+    fl->pkind[fl->npred] = kind;
+    fl->npred++;
+}
+
+static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
+{
+    uint64_t nconn, nflow;
+    int rc = count_workload(b, e, &nconn, &nflow);
+    if (rc) return rc;
+    uint32_t w = b->exp_work[e];
+    uint64_t pkt = b->exp_pkt_bytes[e];
+    x->conn = (Conn *)calloc(nconn ? nconn : 1, sizeof(Conn));
+    x->flow = (Flow *)calloc(nflow ? nflow : 1, sizeof(Flow));
+    x->conn_flows = (uint32_t *)calloc(nflow ? nflow : 1, sizeof(uint32_t));
+    if (!x->conn || !x->flow || !x->conn_flows) return ORC_E_NOMEM;
+    x->n_conn = 0;
+    uint32_t f = 0;
+    for (uint32_t ci = b->work_coll_off[w]; ci < b->work_coll_off[w + 1]; ci++) {
+        const uint32_t *mem = b->member_host + b->coll_member_off[ci];
+        uint32_t N = b->coll_member_off[ci + 1] - b->coll_member_off[ci];
+        uint64_t P = ceil_div(b->coll_bytes[ci], pkt);
+        uint32_t kind = b->coll_type[ci];
+        if (kind == KIND_RING_AR || kind == KIND_RING_AG) {
+            uint32_t NC = b->coll_nc[ci];
+            uint64_t p = b->coll_chunk_bytes[ci] / pkt;
+            uint32_t S = kind == KIND_RING_AR ? 2 * (N - 1) : N - 1;
+            for (uint32_t c = 0; c < NC; c++) {
+                uint64_t Pc = P / NC + (c < P % NC);
+                uint64_t R = ceil_div(Pc, (uint64_t)N * p);
+                if (R > 1 && Pc - (R - 1) * N * p < N) R--;
+                uint32_t conn0 = x->n_conn;
+                for (uint32_t i = 0; i < N; i++) add_conn(x, mem[i], mem[(i + 1) % N]);
+                uint32_t fbase = f;   /* flow (r, s, i) = fbase + (r*S + s)*N + i */
+                for (uint64_t r = 0; r < R; r++) {
+                    uint64_t X = (r + 1 < R) ? (uint64_t)N * p : Pc - (R - 1) * N * p;
+                    for (uint32_t s = 0; s < S; s++) {
+                        for (uint32_t i = 0; i < N; i++) {
+                            uint32_t k = ring_chunk(kind, N, i, s);
+                            uint32_t size = (uint32_t)(X / N + (k < X % N));
+                            set_flow(x, f, conn0 + i, size);
+                            if (s >= 1) {
+                                uint32_t im1 = (i + N - 1) % N;
+                                add_pred(x, f, fbase + (uint32_t)((r * S + s - 1) * N + im1), PRED_RECV);
+                                add_pred(x, f, fbase + (uint32_t)((r * S + s - 1) * N + i), PRED_SEND);
+                            } else if (r >= 1) {
+                                add_pred(x, f, fbase + (uint32_t)(((r - 1) * S + S - 1) * N + i), PRED_SEND);
+                            }
+                            f++;
+                        }
+                    }
+                }
+            }
+        } else { /* KIND_BCAST */
+            uint32_t K = b->coll_k[ci];
+            uint32_t A = N - 1;
+            uint32_t conn0 = x->n_conn;
+            for (uint32_t j = 1; j <= A; j++) add_conn(x, mem[j - 1], mem[j]);
+            uint32_t fbase = f;   /* flow (j, k) = fbase + (j-1)*K + k */
+            for (uint32_t j = 1; j <= A; j++) {
+                for (uint32_t k = 0; k < K; k++) {
+                    uint32_t size = (uint32_t)(P / K + (k < P % K));
+                    set_flow(x, f, conn0 + j - 1, size);
+                    if (j >= 2) add_pred(x, f, fbase + (j - 2) * K + k, PRED_RECV);
+                    if (k >= 1) add_pred(x, f, fbase + (j - 1) * K + k - 1, PRED_SEND);
+                    f++;
+                }
+            }
+        }
+    }
+    for (uint64_t xi = b->work_xflow_off[w]; xi < b->work_xflow_off[w + 1]; xi++) {
+        uint32_t c = add_conn(x, b->xflow_src[xi], b->xflow_dst[xi]);
+        set_flow(x, f, c, b->xflow_pkts[xi]);
+        f++;
+    }
+    x->n_flow = f;
+    /* each connection's flows, in flow-id order (which is their sending order) */
+    for (uint32_t i = 0; i < f; i++) x->conn[x->flow[i].conn].nflow++;
+    uint32_t acc = 0;
+    for (uint32_t c = 0; c < x->n_conn; c++) { x->conn[c].flow_off = acc; acc += x->conn[c].nflow; x->conn[c].nflow = 0; }
+    for (uint32_t i = 0; i < f; i++) {
+        Conn *c = &x->conn[x->flow[i].conn];
+        x->conn_flows[c->flow_off + c->nflow++] = i;
+    }
+    /* hosts' connections, in connection-index order */
+    x->host_conn_off = (uint32_t *)calloc(x->n_nodes + 1, sizeof(uint32_t));
+    x->host_conn = (uint32_t *)calloc(x->n_conn ? x->n_conn : 1, sizeof(uint32_t));
+    if (!x->host_conn_off || !x->host_conn) return ORC_E_NOMEM;
+    for (uint32_t c = 0; c < x->n_conn; c++) x->host_conn_off[x->conn[c].src + 1]++;
+    for (uint32_t n = 0; n < x->n_nodes; n++) x->host_conn_off[n + 1] += x->host_conn_off[n];
+    uint32_t *fill = (uint32_t *)calloc(x->n_nodes, sizeof(uint32_t));
+    if (!fill) return ORC_E_NOMEM;
+    for (uint32_t c = 0; c < x->n_conn; c++) {
+        uint32_t h = x->conn[c].src;
+        x->host_conn[x->host_conn_off[h] + fill[h]++] = c;
+    }
+    free(fill);
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/* Shortest down-only distance (down) and shortest up-then-down distance (any)
+ * from every node to host dst, over alive cables (R4). */
+static void distances(const Exp *x, uint32_t dst, int32_t *down, int32_t *any)
+{
+    uint32_t maxl = 0;
+    for (uint32_t n = 0; n < x->n_nodes; n++) {
+        down[n] = INF_DIST; any[n] = INF_DIST;
+        if (x->layer[n] > maxl) maxl = x->layer[n];
+    }
+    down[dst] = 0;
+    for (uint32_t L = 1; L <= maxl; L++)
+        for (uint32_t n = 0; n < x->n_nodes; n++) {
+            if (x->layer[n] != L) continue;
+            for (uint32_t p = x->port_off[n]; p < x->port_off[n + 1]; p++) {
+                const Port *pp = &x->port[p];
+                if (!pp->alive || x->layer[pp->peer_node] >= L) continue;
+                if (down[pp->peer_node] + 1 < down[n]) down[n] = down[pp->peer_node] + 1;
+            }
+        }
+    for (int32_t L = (int32_t)maxl; L >= 0; L--)
+        for (uint32_t n = 0; n < x->n_nodes; n++) {
+            if (x->layer[n] != (uint32_t)L) continue;
+            int32_t best = down[n];
+            for (uint32_t p = x->port_off[n]; p < x->port_off[n + 1]; p++) {
+                const Port *pp = &x->port[p];
+                if (!pp->alive || x->layer[pp->peer_node] <= (uint32_t)L) continue;
+                if (any[pp->peer_node] + 1 < best) best = any[pp->peer_node] + 1;
+            }
+            any[n] = best;
+        }
+}
+
+static int build_routes(Exp *x)
+{
+    uint32_t maxlen = 0;
+    int32_t *down = (int32_t *)malloc(sizeof(int32_t) * x->n_nodes);
+    int32_t *any = (int32_t *)malloc(sizeof(int32_t) * x->n_nodes);
+    uint32_t *cand = (uint32_t *)malloc(sizeof(uint32_t) * (x->n_ports + 1));
+    uint32_t *done_for = (uint32_t *)malloc(sizeof(uint32_t) * x->n_nodes);
+    if (!down || !any || !cand || !done_for) { free(down); free(any); free(cand); free(done_for); return ORC_E_NOMEM; }
+    /* a shortest up-then-down path has at most 2 * (max layer) links */
+    uint32_t maxl = 0;
+    for (uint32_t n = 0; n < x->n_nodes; n++) if (x->layer[n] > maxl) maxl = x->layer[n];
+    maxlen = 2 * maxl + 1;
+    x->path_node = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(x->n_conn ? x->n_conn : 1) * (maxlen + 1));
+    x->path_port = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(x->n_conn ? x->n_conn : 1) * (maxlen + 1));
+    if (!x->path_node || !x->path_port) { free(down); free(any); free(cand); free(done_for); return ORC_E_NOMEM; }
+    int rc = ORC_OK;
+    /* group connections by destination so distances are computed once per host */
+    for (uint32_t dst = 0; dst < x->n_nodes && rc == ORC_OK; dst++) {
+        int used = 0;
+        for (uint32_t c = 0; c < x->n_conn; c++) if (x->conn[c].dst == dst) { used = 1; break; }
+        if (!used) continue;
+        distances(x, dst, down, any);
+        for (uint32_t c = 0; c < x->n_conn && rc == ORC_OK; c++) {
+            Conn *cn = &x->conn[c];
+            if (cn->dst != dst) continue;
+            cn->path_off = c * (maxlen + 1);
+            uint32_t node = cn->src, len = 0;
+            int going_down = 0;
+            while (1) {
+                x->path_node[cn->path_off + len] = node;
+                if (node == dst) { x->path_port[cn->path_off + len] = NONE; break; }
+                int32_t need = going_down ? down[node] : any[node];
+                if (need >= INF_DIST || len >= maxlen) { rc = ORC_E_UNROUTABLE; break; }
+                uint32_t nc = 0;
+                for (uint32_t p = x->port_off[node]; p < x->port_off[node + 1]; p++) {
+                    const Port *pp = &x->port[p];
+                    uint32_t m = pp->peer_node;
+                    if (!pp->alive) continue;
+                    if (x->layer[m] < x->layer[node]) {
+                        if (down[m] + 1 == need) cand[nc++] = p;
+                    } else if (!going_down && x->layer[m] > x->layer[node]) {
+                        if (any[m] + 1 == need) cand[nc++] = p;
+                    }
+                }
+                if (nc == 0) { rc = ORC_E_UNROUTABLE; break; }
+                uint32_t pick = cand[ecmp_hash(c, node, x->seed) % nc];
+                x->path_port[cn->path_off + len] = pick - x->port_off[node];
+                uint32_t next = x->port[pick].peer_node;
+                if (x->layer[next] < x->layer[node]) going_down = 1;
+                node = next;
+                len++;
+            }
+            cn->path_len = len + 1;
+        }
+    }
+    free(down); free(any); free(cand); free(done_for);
+    return rc;
+}
+
+/* ------------------------------------------------------------- simulation */
+
+typedef struct {
+    uint32_t *flow_rd, *flow_act, *flow_sd;  /* optional per-flow outputs */
+    uint32_t check;                          /* nonzero: verify invariants each tick */
+} orc_opts;
+
+/* Global port index of the ingress port at path position h+1 (the far end of
+ * the link leaving path position h). */
+static uint32_t out_port(const Exp *x, const Conn *c, uint32_t h)
+{
+    uint32_t node = x->path_node[c->path_off + h];
+    return x->port_off[node] + x->path_port[c->path_off + h];
+}
+
+/* Sends packet (flow f, currently at path position hop) out of port op at tick t. */
+static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t t, uint64_t *hops,
+                    uint32_t *max_arrive, uint32_t *max_occ)
+{
+    Port *o = &x->port[op];
+    Port *in = &x->port[o->peer_port];
+    const Conn *c = &x->conn[x->flow[f].conn];
+    Pkt p;
+    p.flow = f;
+    p.arrive = t + o->delay;
+    p.hop = hop + 1;
+    if (p.arrive > *max_arrive) *max_arrive = p.arrive;
+    (*hops)++;
+    if (x->layer[o->peer_node] == 0) {
+        return fifo_push(&in->wire, p) ? ORC_E_NOMEM : ORC_OK;
+    }
+    uint32_t egress = x->path_port[c->path_off + p.hop];
+    in->occ++;
+    if (in->occ > *max_occ) *max_occ = in->occ;
+    if (in->occ > x->Q) return ORC_E_INVARIANT;        /* credits make this impossible */
+    return fifo_push(&in->voq[egress], p) ? ORC_E_NOMEM : ORC_OK;
+}
+
+static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts *opt)
+{
+    uint64_t hops = 0, delivered = 0, digest = 0;
+    uint32_t flows_left = x->n_flow, t_done = 0;
+    uint32_t max_arrive = 0, max_occ = 0;
+    int rc;
+    if (flows_left == 0) {
+        res->status = ORC_OK; res->t_end = 0;
+        return ORC_OK;
+    }
+    for (uint32_t t = 0; t < max_ticks; t++) {
+        int busy = 0;
+        /* A: deliveries at hosts */
+        for (uint32_t p = 0; p < x->n_ports; p++) {
+            Port *pp = &x->port[p];
+            if (x->layer[pp->node] != 0) continue;
+            Pkt *head;
+            while ((head = fifo_front(&pp->wire)) && head->arrive == t) {
+                Pkt k = fifo_pop(&pp->wire);
+                Flow *fl = &x->flow[k.flow];
+                Conn *c = &x->conn[fl->conn];
+                if (opt->check) {
+                    /* a connection delivers in order: the packet belongs to its
+                     * earliest flow not yet fully received */
+                    if (x->conn_flows[c->flow_off + c->recv_pos] != k.flow) return ORC_E_INVARIANT;
+                    if (c->dst != pp->node) return ORC_E_INVARIANT;
+                }
+                fl->recvd++;
+                delivered++;
+                if (fl->recvd == fl->size) {
+                    fl->rd = t;
+                    c->recv_pos++;
+                    digest += mix64(((uint64_t)k.flow << 32) | t);
+                    if (t > t_done) t_done = t;
+                    flows_left--;
+                }
+            }
+            if (pp->wire.count && fifo_front(&pp->wire)->arrive < t) return ORC_E_INVARIANT;
+        }
+        /* B: activation.  Only the first not yet active flow of a connection can
+         * have all its predecessors met: every later one waits (SEND) on it. */
+        for (uint32_t ci = 0; ci < x->n_conn; ci++) {
+            Conn *c = &x->conn[ci];
+            if (c->cur >= c->nflow) continue;
+            Flow *fl = &x->flow[x->conn_flows[c->flow_off + c->cur]];
+            if (fl->active) continue;
+            int ok = 1;
+            for (uint32_t k = 0; k < fl->npred; k++) {
+                const Flow *g = &x->flow[fl->pred[k]];
+                uint32_t when = fl->pkind[k] == PRED_RECV ? g->rd : g->sd;
+                if (when == NONE || when > t) { ok = 0; break; }
+            }
+            if (ok) { fl->active = 1; fl->act = t; busy = 1; }
+        }
+        /* C: credit snapshot */
+        for (uint32_t p = 0; p < x->n_ports; p++) {
+            Port *pp = &x->port[p];
+            if (x->layer[pp->peer_node] == 0) pp->credit = INT64_MAX;
+            else pp->credit = (int64_t)x->Q - (int64_t)x->port[pp->peer_port].occ;
+        }
+        /* D: rounds of grants; decide on the state at the start of the round, then apply */
+        for (uint32_t m = 0; m < x->R; m++) {
+            for (uint32_t p = 0; p < x->n_ports; p++) {
+                Port *pp = &x->port[p];
+                pp->granted = NONE;
+                if (!pp->alive || m >= pp->rate || pp->credit <= 0) continue;
+                uint32_t node = pp->node;
+                uint32_t me = p - x->port_off[node];
+                if (x->layer[node] == 0) {
+                    uint32_t n_in = x->host_conn_off[node + 1] - x->host_conn_off[node];
+                    for (uint32_t j = 0; j < n_in; j++) {
+                        uint32_t idx = (pp->rr + j) % n_in;
+                        Conn *c = &x->conn[x->host_conn[x->host_conn_off[node] + idx]];
+                        if (c->cur >= c->nflow) continue;
+                        Flow *fl = &x->flow[x->conn_flows[c->flow_off + c->cur]];
+                        if (fl->active && fl->sent < fl->size) { pp->granted = idx; break; }
+                    }
+                } else {
+                    uint32_t deg = x->port_off[node + 1] - x->port_off[node];
+                    for (uint32_t j = 0; j < deg; j++) {
+                        uint32_t i = (pp->rr + j) % deg;
+                        Pkt *head = fifo_front(&x->port[x->port_off[node] + i].voq[me]);
+                        if (head && head->arrive <= t) { pp->granted = i; break; }
+                    }
+                }
+            }
+            for (uint32_t p = 0; p < x->n_ports; p++) {
+                Port *pp = &x->port[p];
+                if (pp->granted == NONE) continue;
+                uint32_t node = pp->node;
+                busy = 1;
+                if (x->layer[node] == 0) {
+                    uint32_t n_in = x->host_conn_off[node + 1] - x->host_conn_off[node];
+                    uint32_t ci = x->host_conn[x->host_conn_off[node] + pp->granted];
+                    Conn *c = &x->conn[ci];
+                    uint32_t f = x->conn_flows[c->flow_off + c->cur];
+                    Flow *fl = &x->flow[f];
+                    if (out_port(x, c, 0) != p) return ORC_E_INVARIANT;
+                    rc = transmit(x, p, f, 0, t, &hops, &max_arrive, &max_occ);
+                    if (rc) return rc;
+                    fl->sent++;
+                    if (fl->sent == fl->size) { fl->sd = t + 1; c->cur++; }
+                    pp->rr = (pp->granted + 1) % n_in;
+                } else {
+                    uint32_t deg = x->port_off[node + 1] - x->port_off[node];
+                    uint32_t me = p - x->port_off[node];
+                    Port *in = &x->port[x->port_off[node] + pp->granted];
+                    Pkt k = fifo_pop(&in->voq[me]);
+                    in->occ--;
+                    const Conn *c = &x->conn[x->flow[k.flow].conn];
+                    if (opt->check && out_port(x, c, k.hop) != p) return ORC_E_INVARIANT;
+                    rc = transmit(x, p, k.flow, k.hop, t, &hops, &max_arrive, &max_occ);
+                    if (rc) return rc;
+                    pp->rr = (pp->granted + 1) % deg;
+                }
+                pp->credit--;
+            }
+        }
+        /* E: completion / static state */
+        if (flows_left == 0) {
+            res->status = ORC_OK;
+            res->t_end = t_done;
+            res->pkt_hops = hops; res->delivered = delivered; res->digest = digest;
+            res->max_occupancy = max_occ;
+            return ORC_OK;
+        }
+        if (!busy && max_arrive <= t) {
+            res->status = ORC_S_DEADLOCK;
+            res->t_end = t;
+            res->pkt_hops = hops; res->delivered = delivered; res->digest = digest;
+            res->max_occupancy = max_occ;
+            return ORC_OK;
+        }
+    }
+    res->status = ORC_S_INCOMPLETE;
+    res->t_end = max_ticks;
+    res->pkt_hops = hops; res->delivered = delivered; res->digest = digest;
+    res->max_occupancy = max_occ;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------- interface */
+
+/* Number of flows and connections of experiment e (validates the workload). */
+int orc_count(const orc_batch *b, uint32_t e, uint64_t *n_flows, uint64_t *n_conns)
+{
+    if (e >= b->n_exp) return ORC_E_INVALID;
+    return count_workload(b, e, n_conns, n_flows);
+}
+
+/* Runs experiment e for at most max_ticks ticks.  Optional per-flow outputs
+ * (NONE where the event did not happen): RD, activation tick, SD.  Returns a
+ * negative error code, or ORC_OK with the status in res->status. */
+int orc_run(const orc_batch *b, uint32_t e, uint32_t max_ticks, uint32_t check, orc_result *res,
+            uint32_t *flow_rd, uint32_t *flow_act, uint32_t *flow_sd)
+{
+    Exp x;
+    memset(&x, 0, sizeof(x));
+    memset(res, 0, sizeof(*res));
+    if (e >= b->n_exp) return ORC_E_INVALID;
+    x.Q = b->exp_queue_pkts[e];
+    x.seed = b->exp_ecmp_seed[e];
+    if (x.Q < 1) return ORC_E_INVALID;
+    int rc = build_topology(b, e, &x);
+    if (!rc) rc = build_workload(b, e, &x);
+    if (!rc) rc = build_routes(&x);
+    orc_opts opt;
+    opt.flow_rd = flow_rd; opt.flow_act = flow_act; opt.flow_sd = flow_sd; opt.check = check;
+    if (!rc) {
+        res->n_flows = x.n_flow;
+        res->n_conns = x.n_conn;
+        rc = simulate(&x, max_ticks, res, &opt);
+    }
+    if (!rc) {
+        for (uint32_t f = 0; f < x.n_flow; f++) {
+            if (flow_rd) flow_rd[f] = x.flow[f].rd;
+            if (flow_act) flow_act[f] = x.flow[f].act;
+            if (flow_sd) flow_sd[f] = x.flow[f].sd;
+        }
+    }
+    exp_free(&x);
+    return rc;
+}
+
+/* Per-connection description for tests: source, destination, number of links
+ * on its path, and the global port index used at each path position (up to
+ * max_len entries per connection; NONE after the end). */
+int orc_paths(const orc_batch *b, uint32_t e, uint32_t *conn_src, uint32_t *conn_dst,
+              uint32_t *conn_links, uint32_t *path_ports, uint32_t max_len)
+{
+    Exp x;
+    memset(&x, 0, sizeof(x));
+    if (e >= b->n_exp) return ORC_E_INVALID;
+    x.Q = b->exp_queue_pkts[e];
+    x.seed = b->exp_ecmp_seed[e];
+    int rc = build_topology(b, e, &x);
+    if (!rc) rc = build_workload(b, e, &x);
+    if (!rc) rc = build_routes(&x);
+    if (!rc) {
+        for (uint32_t c = 0; c < x.n_conn; c++) {
+            Conn *cn = &x.conn[c];
+            conn_src[c] = cn->src; conn_dst[c] = cn->dst; conn_links[c] = cn->path_len - 1;
+            for (uint32_t h = 0; h < max_len; h++)
+                path_ports[(size_t)c * max_len + h] =
+                    h + 1 < cn->path_len ? out_port(&x, cn, h) : NONE;
+        }
+    }
+    exp_free(&x);
+    return rc;
+}
+
+/* Per-flow description for tests: connection and size of every flow. */
+int orc_flows(const orc_batch *b, uint32_t e, uint32_t *flow_conn, uint32_t *flow_size)
+{
+    Exp x;
+    memset(&x, 0, sizeof(x));
+    if (e >= b->n_exp) return ORC_E_INVALID;
+    x.Q = b->exp_queue_pkts[e] ? b->exp_queue_pkts[e] : 1;
+    int rc = build_topology(b, e, &x);
+    if (!rc) rc = build_workload(b, e, &x);
+    if (!rc)
+        for (uint32_t f = 0; f < x.n_flow; f++) { flow_conn[f] = x.flow[f].conn; flow_size[f] = x.flow[f].size; }
+    exp_free(&x);
+    return rc;
+}
+
+uint32_t orc_fmix32(uint32_t h) { return fmix32(h); }
+uint64_t orc_mix64(uint64_t z) { return mix64(z); }

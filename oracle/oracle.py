@@ -1,0 +1,186 @@
+"""Python access to the plain C oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test-suite, by the smoke check and by
+the benchmark's CPU-baseline leg, never by the simulator package.  The oracle
+reads the same generator arrays as the HIP library and computes everything
+else on its own.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+from typing import Dict, Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+OK, S_INCOMPLETE, S_DEADLOCK = 0, 1, 2
+E_INVALID, E_UNROUTABLE, E_NOMEM, E_INVARIANT = -1, -2, -3, -4
+NONE = 0xFFFFFFFF
+
+
+def build(force: bool = True) -> str:
+    """Compiles oracle.c into liboracle.so (plain gcc, -O2)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Wno-unused-parameter",
+                               "-shared", "-fPIC", SRC, "-o", tmp])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_P8, _P32, _P64 = C.POINTER(C.c_uint8), C.POINTER(C.c_uint32), C.POINTER(C.c_uint64)
+
+
+class _Batch(C.Structure):
+    _fields_ = [("n_topo", C.c_uint32), ("n_work", C.c_uint32), ("n_exp", C.c_uint32), ("pad", C.c_uint32),
+                ("topo_node_off", _P32), ("node_layer", _P8), ("topo_cable_off", _P32),
+                ("cable_a", _P32), ("cable_b", _P32),
+                ("cable_rate_ab", _P8), ("cable_rate_ba", _P8), ("cable_delay", _P8), ("cable_alive", _P8),
+                ("work_coll_off", _P32), ("coll_type", _P8), ("coll_bytes", _P64),
+                ("coll_nc", _P32), ("coll_chunk_bytes", _P32), ("coll_k", _P32),
+                ("coll_member_off", _P32), ("member_host", _P32),
+                ("work_xflow_off", _P64), ("xflow_src", _P32), ("xflow_dst", _P32), ("xflow_pkts", _P32),
+                ("exp_topo", _P32), ("exp_work", _P32), ("exp_queue_pkts", _P32),
+                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32)]
+
+
+class _Result(C.Structure):
+    _fields_ = [("status", C.c_int32), ("t_end", C.c_uint32), ("pkt_hops", C.c_uint64),
+                ("delivered", C.c_uint64), ("digest", C.c_uint64), ("n_flows", C.c_uint64),
+                ("n_conns", C.c_uint64), ("max_occupancy", C.c_uint32), ("pad", C.c_uint32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB):
+                build(force=True)
+            lib = C.CDLL(LIB)
+            lib.orc_run.argtypes = [C.POINTER(_Batch), C.c_uint32, C.c_uint32, C.c_uint32,
+                                    C.POINTER(_Result), _P32, _P32, _P32]
+            lib.orc_run.restype = C.c_int
+            lib.orc_count.argtypes = [C.POINTER(_Batch), C.c_uint32, _P64, _P64]
+            lib.orc_count.restype = C.c_int
+            lib.orc_paths.argtypes = [C.POINTER(_Batch), C.c_uint32, _P32, _P32, _P32, _P32, C.c_uint32]
+            lib.orc_paths.restype = C.c_int
+            lib.orc_flows.argtypes = [C.POINTER(_Batch), C.c_uint32, _P32, _P32]
+            lib.orc_flows.restype = C.c_int
+            lib.orc_fmix32.argtypes = [C.c_uint32]
+            lib.orc_fmix32.restype = C.c_uint32
+            lib.orc_mix64.argtypes = [C.c_uint64]
+            lib.orc_mix64.restype = C.c_uint64
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+class OracleBatch:
+    """Keeps the packed arrays alive while the C side points at them."""
+
+    def __init__(self, packed):
+        self.p = packed
+        p = packed
+        self.s = _Batch(p.n_topo, p.n_work, p.n_exp, 0,
+                        _ptr(p.topo_node_off, _P32), _ptr(p.node_layer, _P8), _ptr(p.topo_cable_off, _P32),
+                        _ptr(p.cable_a, _P32), _ptr(p.cable_b, _P32),
+                        _ptr(p.cable_rate_ab, _P8), _ptr(p.cable_rate_ba, _P8), _ptr(p.cable_delay, _P8),
+                        _ptr(p.cable_alive, _P8),
+                        _ptr(p.work_coll_off, _P32), _ptr(p.coll_type, _P8), _ptr(p.coll_bytes, _P64),
+                        _ptr(p.coll_nc, _P32), _ptr(p.coll_chunk_bytes, _P32), _ptr(p.coll_k, _P32),
+                        _ptr(p.coll_member_off, _P32), _ptr(p.member_host, _P32),
+                        _ptr(p.work_xflow_off, _P64), _ptr(p.xflow_src, _P32), _ptr(p.xflow_dst, _P32),
+                        _ptr(p.xflow_pkts, _P32),
+                        _ptr(p.exp_topo, _P32), _ptr(p.exp_work, _P32), _ptr(p.exp_queue_pkts, _P32),
+                        _ptr(p.exp_ecmp_seed, _P32), _ptr(p.exp_pkt_bytes, _P32))
+
+
+def _as_oracle_batch(b) -> OracleBatch:
+    if isinstance(b, OracleBatch):
+        return b
+    if hasattr(b, "pack"):
+        b = b.pack()
+    return OracleBatch(b)
+
+
+def count(batch, e: int):
+    ob = _as_oracle_batch(batch)
+    nf, nc = np.zeros(1, np.uint64), np.zeros(1, np.uint64)
+    rc = _load().orc_count(C.byref(ob.s), e, _ptr(nf, _P64), _ptr(nc, _P64))
+    return rc, int(nf[0]), int(nc[0])
+
+
+def run(batch, e: int, max_ticks: int = 0xFFFFFFFF, check: bool = False,
+        flows: bool = False) -> Dict:
+    """Runs experiment e.  Returns a dict with status, t_end, pkt_hops,
+    delivered, digest, n_flows, n_conns, max_occupancy, rc and, with flows=True,
+    per-flow arrays rd, act, sd (NONE where the event did not happen)."""
+    ob = _as_oracle_batch(batch)
+    lib = _load()
+    out: Dict = {}
+    rd = act = sd = None
+    if flows:
+        rc, nf, _ = count(ob, e)
+        if rc:
+            return {"rc": rc}
+        rd, act, sd = (np.full(max(nf, 1), NONE, np.uint32) for _ in range(3))
+    res = _Result()
+    rc = lib.orc_run(C.byref(ob.s), e, max_ticks, 1 if check else 0, C.byref(res),
+                     _ptr(rd, _P32) if flows else None, _ptr(act, _P32) if flows else None,
+                     _ptr(sd, _P32) if flows else None)
+    out["rc"] = rc
+    if rc:
+        return out
+    out.update(status=res.status, t_end=res.t_end, pkt_hops=res.pkt_hops, delivered=res.delivered,
+               digest=res.digest, n_flows=res.n_flows, n_conns=res.n_conns,
+               max_occupancy=res.max_occupancy)
+    if flows:
+        out["rd"], out["act"], out["sd"] = rd[:res.n_flows], act[:res.n_flows], sd[:res.n_flows]
+    return out
+
+
+def paths(batch, e: int, max_len: int = 16):
+    """Per connection: src host, dst host, number of links, global port index
+    left from at each path position (NONE-padded)."""
+    ob = _as_oracle_batch(batch)
+    rc, nf, nc = count(ob, e)
+    if rc:
+        return rc, None
+    src, dst, links = (np.zeros(max(nc, 1), np.uint32) for _ in range(3))
+    pp = np.full((max(nc, 1), max_len), NONE, np.uint32)
+    rc = _load().orc_paths(C.byref(ob.s), e, _ptr(src, _P32), _ptr(dst, _P32), _ptr(links, _P32),
+                           _ptr(pp, _P32), max_len)
+    return rc, dict(src=src[:nc], dst=dst[:nc], links=links[:nc], ports=pp[:nc])
+
+
+def flows(batch, e: int):
+    """Per flow: connection index and size in packets."""
+    ob = _as_oracle_batch(batch)
+    rc, nf, nc = count(ob, e)
+    if rc:
+        return rc, None
+    conn, size = np.zeros(max(nf, 1), np.uint32), np.zeros(max(nf, 1), np.uint32)
+    rc = _load().orc_flows(C.byref(ob.s), e, _ptr(conn, _P32), _ptr(size, _P32))
+    return rc, dict(conn=conn[:nf], size=size[:nf])
+
+
+def fmix32(h: int) -> int:
+    return int(_load().orc_fmix32(h & 0xFFFFFFFF))
+
+
+def mix64(z: int) -> int:
+    return int(_load().orc_mix64(z & ((1 << 64) - 1)))

@@ -1,0 +1,350 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix.
+
+Every check here is computed independently of the oracle's code: closed forms
+(ring step counts, pipelined-broadcast time, single-flow latency), hand traces
+stored under tests/golden/, lower bounds and conservation laws, and routes
+checked against a breadth-first search written in this file.
+"""
+
+import json
+import os
+from collections import deque
+
+import numpy as np
+import pytest
+
+from experiment_network_simulation_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_traces.json")
+
+
+# ----------------------------------------------------------------- helpers
+
+def port_table(topo: I.Topology):
+    """Port numbering rule: a node's ports follow the order of its cables.
+    Returns per global port (node-major): node, peer node, delay, alive, rate."""
+    per_node = [[] for _ in range(topo.n_nodes)]
+    for c in range(topo.n_cables):
+        a, b = int(topo.cable_a[c]), int(topo.cable_b[c])
+        per_node[a].append((b, int(topo.delay[c]), int(topo.alive[c]), int(topo.rate_ab[c])))
+        per_node[b].append((a, int(topo.delay[c]), int(topo.alive[c]), int(topo.rate_ba[c])))
+    table = []
+    for n in range(topo.n_nodes):
+        for (m, d, al, r) in per_node[n]:
+            table.append(dict(node=n, peer=m, delay=d, alive=al, rate=r))
+    return table
+
+
+def updown_distance(topo: I.Topology, src: int, dst: int) -> int:
+    """Fewest links from src to dst on a path that only climbs layers and then
+    only descends them, over alive cables (BFS over (node, descending))."""
+    adj = [[] for _ in range(topo.n_nodes)]
+    for c in range(topo.n_cables):
+        if topo.alive[c]:
+            a, b = int(topo.cable_a[c]), int(topo.cable_b[c])
+            adj[a].append(b); adj[b].append(a)
+    L = topo.layer
+    seen = {(src, False): 0}
+    q = deque([(src, False)])
+    while q:
+        n, down = q.popleft()
+        if n == dst:
+            return seen[(n, down)]
+        for m in adj[n]:
+            if L[m] > L[n] and not down:
+                st = (m, False)
+            elif L[m] < L[n]:
+                st = (m, True)
+            else:
+                continue
+            if st not in seen:
+                seen[st] = seen[(n, down)] + 1
+                q.append(st)
+    return -1
+
+
+def custom(layers, cables, flows, queue=16, seed=0):
+    topo = I.topology_from_cables(layers, [tuple(c) for c in cables])
+    return I.single_batch(topo, I.xflows([tuple(f) for f in flows]), queue_pkts=queue, ecmp_seed=seed)
+
+
+def path_delay(topo, ports_row, table):
+    return sum(table[p]["delay"] for p in ports_row if p != 0xFFFFFFFF)
+
+
+# ----------------------------------------------------------- hand traces
+
+@pytest.mark.parametrize("case", ["M1_incast", "M2_credit", "M3_two_egress", "M4_round_order"])
+def test_hand_traces(oracle, case):
+    g = json.load(open(GOLDEN))[case]
+    b = custom(g["layers"], g["cables"], g["flows"], g["queue"])
+    r = oracle.run(b, 0, check=True, flows=True)
+    assert r["rc"] == 0 and r["status"] == oracle.OK
+    assert list(r["rd"]) == g["rd"]
+    assert r["t_end"] == g["t_end"]
+    assert r["pkt_hops"] == g["pkt_hops"]
+
+
+def test_credit_spacing_m2(oracle):
+    """Q = 1 and delay 2: one packet per d+1 ticks (M2 sends at 0, 3, 6)."""
+    g = json.load(open(GOLDEN))["M2_credit"]
+    for n in (1, 2, 5):
+        b = custom(g["layers"], g["cables"], [[0, 1, n]], 1)
+        r = oracle.run(b, 0, check=True)
+        assert r["t_end"] == 3 * (n - 1) + 4
+
+
+# ------------------------------------------------- single uncontended flow
+
+@pytest.mark.parametrize("seed", range(12))
+def test_single_flow_latency(oracle, seed):
+    """Uncontended flow: RD - A = (sum of link delays on its path) + P - 1.
+    This is the single-flow form hops x delay + packets - 1 with per-link delays."""
+    rng = np.random.default_rng(seed)
+    kind = seed % 3
+    if kind == 0:
+        topo = I.single_switch(int(rng.integers(2, 9)))
+    elif kind == 1:
+        topo = I.leaf_spine(3, 4, 2, host_rate=1, up_rate=int(rng.integers(1, 3)))
+    else:
+        topo = I.fat_tree(4)
+    topo.delay = rng.integers(1, 5, topo.n_cables).astype(np.uint8)
+    hosts = topo.hosts()
+    s, d = rng.choice(hosts, 2, replace=False)
+    P = int(rng.integers(1, 60))
+    b = I.single_batch(topo, I.xflows([(int(s), int(d), P)]), queue_pkts=2 * (4 + 1),
+                       ecmp_seed=int(rng.integers(0, 2**32)))
+    r = oracle.run(b, 0, check=True, flows=True)
+    rc, pth = oracle.paths(b, 0)
+    assert rc == 0 and r["rc"] == 0
+    table = port_table(topo)
+    L = path_delay(topo, pth["ports"][0], table)
+    assert int(r["act"][0]) == 0
+    assert int(r["rd"][0]) == L + P - 1
+    assert r["pkt_hops"] == P * int(pth["links"][0])
+    assert int(pth["links"][0]) == updown_distance(topo, int(s), int(d))
+
+
+# --------------------------------------------------------- ring closed forms
+
+def ring_closed_form(N, R, p, L, allreduce=True):
+    """NC = 1, every chunk p packets, no contention, path latency L:
+    a step takes tau = L + p - 1 ticks (p packets, the last one L ticks on the
+    wire); steps of a round are back to back through the RECV edges; the next
+    round's first step waits only for the previous round's last send, p ticks
+    after that step began.  S = 2(N-1) steps for all-reduce, N-1 for all-gather."""
+    S = 2 * (N - 1) if allreduce else N - 1
+    tau = L + p - 1
+    return (R - 1) * ((S - 1) * tau + p) + S * tau
+
+
+def test_c1_nc1_values(oracle):
+    """C1 with NC = 1 and C = 16/32/64/128 KiB: 553, 501, 475, 462 ticks."""
+    b = I.make_config(1)
+    got = [oracle.run(b, e)["t_end"] for e in range(4)]
+    assert got == [553, 501, 475, 462]
+    for e, (p, R) in enumerate([(4, 8), (8, 4), (16, 2), (32, 1)]):
+        assert got[e] == ring_closed_form(8, R, p, 2)
+
+
+@pytest.mark.parametrize("N,p,R,d,ag", [(2, 1, 1, 1, False), (3, 2, 3, 1, False), (4, 3, 2, 2, False),
+                                        (5, 1, 4, 3, False), (8, 4, 2, 1, True), (6, 5, 3, 2, True),
+                                        (7, 2, 1, 4, False), (3, 7, 5, 1, True)])
+def test_ring_closed_form(oracle, N, p, R, d, ag):
+    topo = I.single_switch(N, 1, d)
+    P = R * N * p
+    kind = I.COLL_RING_AG if ag else I.COLL_RING_AR
+    w = I.Workload([I.ring(kind, P * I.PKT_BYTES, range(N), 1, p * I.PKT_BYTES)])
+    b = I.single_batch(topo, w, queue_pkts=d + 1)
+    r = oracle.run(b, 0, check=True, flows=True)
+    assert r["status"] == oracle.OK
+    assert r["t_end"] == ring_closed_form(N, R, p, 2 * d, allreduce=not ag)
+    S = 2 * (N - 1) if not ag else N - 1
+    assert r["n_flows"] == R * S * N
+    assert r["delivered"] == R * S * N * p
+
+
+def test_ring_step_count_and_chunks(oracle):
+    """Every channel moves S chunks per rank per round and the chunk sizes of a
+    round add up to the round (bytes are conserved), also with remainders."""
+    for (P, N, NC, p, ag) in [(37, 3, 2, 4, False), (101, 5, 3, 2, True), (64, 4, 4, 16, False)]:
+        topo = I.single_switch(N)
+        kind = I.COLL_RING_AG if ag else I.COLL_RING_AR
+        w = I.Workload([I.ring(kind, P * I.PKT_BYTES, range(N), NC, p * I.PKT_BYTES)])
+        b = I.single_batch(topo, w, queue_pkts=8)
+        rc, fl = oracle.flows(b, 0)
+        assert rc == 0
+        S = 2 * (N - 1) if not ag else N - 1
+        assert fl["size"].min() >= 1
+        # each rank sends, over all its steps, S/N of the message (all-reduce:
+        # 2(N-1)/N of it; all-gather: (N-1)/N of it), summed over channels
+        per_conn = np.bincount(fl["conn"], weights=fl["size"])
+        assert per_conn.sum() == S * P
+        r = oracle.run(b, 0, check=True)
+        assert r["status"] == oracle.OK and r["delivered"] == S * P
+
+
+# ------------------------------------------------------ pipelined broadcast
+
+@pytest.mark.parametrize("A,K,P,seed", [(1, 4, 64, 0), (2, 1, 64, 1), (2, 64, 16384, 2), (4, 8, 256, 3),
+                                        (7, 16, 512, 4), (3, 3, 99, 5), (5, 32, 1024, 6)])
+def test_broadcast_closed_form(oracle, A, K, P, seed):
+    """T = t + (A-1) t / K in ticks: with P packets, K | P and hop latencies L_j,
+    T = P + (A-1) P / K + sum_j (L_j - 1)."""
+    rng = np.random.default_rng(seed)
+    topo = I.single_switch(A + 1)
+    topo.delay = rng.integers(1, 5, topo.n_cables).astype(np.uint8)
+    chain = [int(x) for x in rng.permutation(A + 1)]
+    w = I.Workload([I.bcast(P * I.PKT_BYTES, chain, K)])
+    b = I.single_batch(topo, w, queue_pkts=5)
+    r = oracle.run(b, 0, check=True)
+    table = port_table(topo)
+    rc, pth = oracle.paths(b, 0)
+    Ls = [path_delay(topo, pth["ports"][j], table) for j in range(A)]
+    if P % K == 0:
+        assert r["t_end"] == P + (A - 1) * P // K + sum(L - 1 for L in Ls)
+    else:   # uneven partitions: the first P mod K partitions carry one more packet
+        big = P // K + 1
+        assert r["t_end"] >= P + (A - 1) * (P // K) + sum(L - 1 for L in Ls)
+        assert r["t_end"] <= P + (A - 1) * big + sum(L - 1 for L in Ls)
+
+
+def test_broadcast_golden_leaf(oracle):
+    """64 MiB to A = 2 receivers on one leaf, all delays 1: K=1 -> 32770, K=64 -> 16642."""
+    topo = I.leaf_spine(4, 8, 4, 1, 2, 1)
+    for K, want in [(1, 32770), (64, 16642)]:
+        b = I.single_batch(topo, I.Workload([I.bcast(64 * I.MIB, [0, 1, 2], K)]), queue_pkts=32)
+        assert oracle.run(b, 0, check=True)["t_end"] == want
+
+
+def test_c3_closed_form_where_contention_free(oracle):
+    """On C3's own inputs: wherever no directed link carries more connections
+    than its rate, the broadcast time equals the closed form."""
+    b = I.make_config(3, n_exp=56)
+    checked = 0
+    for e in range(b.n_exp):
+        topo = b.topos[b.exps[e].topo]
+        table = port_table(topo)
+        rc, pth = oracle.paths(b, e)
+        load = {}
+        for row in pth["ports"]:
+            for p in row:
+                if p != 0xFFFFFFFF:
+                    load[int(p)] = load.get(int(p), 0) + 1
+        if any(n > table[p]["rate"] for p, n in load.items()):
+            continue
+        coll = b.works[b.exps[e].work].colls[0]
+        A, K, P = len(coll.members) - 1, coll.k, coll.nbytes // I.PKT_BYTES
+        Ls = [path_delay(topo, pth["ports"][j], table) for j in range(A)]
+        r = oracle.run(b, e)
+        assert r["t_end"] == P + (A - 1) * P // K + sum(L - 1 for L in Ls), (e, A, K)
+        checked += 1
+    assert checked >= 10
+
+
+# ------------------------------------------------ invariants and lower bounds
+
+def check_invariants(oracle, b, e):
+    r = oracle.run(b, e, check=True, flows=True)
+    assert r["rc"] == 0 and r["status"] == oracle.OK
+    rc, fl = oracle.flows(b, e)
+    rc2, pth = oracle.paths(b, e)
+    assert rc == 0 and rc2 == 0
+    topo = b.topos[b.exps[e].topo]
+    table = port_table(topo)
+    links = pth["links"][fl["conn"]].astype(np.int64)
+    size = fl["size"].astype(np.int64)
+    # conservation: every packet delivered once; every packet crosses every link of its path once
+    assert r["delivered"] == size.sum()
+    assert r["pkt_hops"] == int((size * links).sum())
+    # per-flow lower bounds: sending takes size ticks at rate 1, the last packet
+    # then needs the path latency
+    lat = np.array([path_delay(topo, row, table) for row in pth["ports"]], np.int64)[fl["conn"]]
+    act, sd, rd = (r[k].astype(np.int64) for k in ("act", "sd", "rd"))
+    assert np.all(sd >= act + size)
+    assert np.all(rd >= sd - 1 + lat)
+    assert np.all(rd >= act + lat + size - 1)
+    assert r["t_end"] == rd.max()
+    # a host link moves one packet per tick: completion >= busiest uplink's load
+    src_load = np.bincount(pth["src"][fl["conn"]], weights=size)
+    dst_load = np.bincount(pth["dst"][fl["conn"]], weights=size)
+    assert r["t_end"] >= max(src_load.max(), dst_load.max())
+    # routes are shortest up-then-down paths
+    for c in range(len(pth["src"])):
+        assert pth["links"][c] == updown_distance(topo, int(pth["src"][c]), int(pth["dst"][c]))
+    assert r["max_occupancy"] <= b.exps[e].queue_pkts
+    return r
+
+
+@pytest.mark.parametrize("e", [0, 5, 10, 15])
+def test_invariants_c1(oracle, e):
+    check_invariants(oracle, I.make_config(1), e)
+
+
+@pytest.mark.parametrize("e", [0, 1, 2])
+def test_invariants_c2(oracle, e):
+    check_invariants(oracle, I.make_config(2, exp_ids=[e]), 0)
+
+
+@pytest.mark.parametrize("e", [3, 27, 40])
+def test_invariants_c3(oracle, e):
+    check_invariants(oracle, I.make_config(3, exp_ids=[e]), 0)
+
+
+def test_activation_is_earliest(oracle):
+    """A flow activates at the first tick all its predecessors are met: with the
+    ring rules, every step s >= 1 starts exactly when both the previous chunk
+    from rank i-1 has arrived and rank i's own previous send has left."""
+    N, p, R = 4, 3, 2
+    w = I.Workload([I.ring(I.COLL_RING_AR, R * N * p * I.PKT_BYTES, range(N), 1, p * I.PKT_BYTES)])
+    b = I.single_batch(I.single_switch(N), w, queue_pkts=4)
+    r = oracle.run(b, 0, flows=True)
+    S = 2 * (N - 1)
+    fid = lambda rr, s, i: (rr * S + s) * N + i
+    for rr in range(R):
+        for s in range(S):
+            for i in range(N):
+                f = fid(rr, s, i)
+                if s >= 1:
+                    want = max(r["rd"][fid(rr, s - 1, (i - 1) % N)], r["sd"][fid(rr, s - 1, i)])
+                elif rr >= 1:
+                    want = r["sd"][fid(rr - 1, S - 1, i)]
+                else:
+                    want = 0
+                assert r["act"][f] == want
+
+
+def test_empty_and_errors(oracle):
+    topo = I.single_switch(3)
+    b = I.single_batch(topo, I.Workload())
+    r = oracle.run(b, 0)
+    assert r["status"] == oracle.OK and r["t_end"] == 0 and r["pkt_hops"] == 0
+    # a dead host cable makes its host unreachable
+    t2 = topo.copy(); t2.alive[1] = 0
+    assert oracle.run(I.single_batch(t2, I.xflows([(0, 1, 2)])), 0)["rc"] == oracle.E_UNROUTABLE
+    # fewer packets in a channel than ranks is rejected
+    w = I.Workload([I.ring(I.COLL_RING_AR, 2 * I.PKT_BYTES, range(3), 1, I.PKT_BYTES)])
+    assert oracle.run(I.single_batch(topo, w), 0)["rc"] == oracle.E_INVALID
+    # a chunk that is not a whole number of packets is rejected
+    w = I.Workload([I.ring(I.COLL_RING_AR, 64 * I.PKT_BYTES, range(3), 1, 100)])
+    assert oracle.run(I.single_batch(topo, w), 0)["rc"] == oracle.E_INVALID
+
+
+def test_incomplete_and_resume_bound(oracle):
+    b = I.make_config(1, exp_ids=[0])
+    r = oracle.run(b, 0, max_ticks=100)
+    assert r["status"] == oracle.S_INCOMPLETE and r["t_end"] == 100
+
+
+def test_fat_tree_failures_stay_routable(oracle):
+    """C4's failure draw keeps every host pair routable; routes avoid dead cables."""
+    b = I.make_config(4, exp_ids=range(24))
+    for e in range(b.n_exp):
+        topo = b.topos[b.exps[e].topo]
+        rc, pth = oracle.paths(b, e)
+        assert rc == 0
+        table = port_table(topo)
+        for row in pth["ports"]:
+            for p in row:
+                if p != 0xFFFFFFFF:
+                    assert table[p]["alive"]
