@@ -1,0 +1,49 @@
+"""Builds libmsim.so (the HIP library behind include/msim.h) for gfx950.
+
+Run as a script or call build().  The shared library is written next to this
+file, where the Python binding loads it from.
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmsim.so")
+SOURCES = [os.path.join(CSRC, "msim_kernel.hip"), os.path.join(CSRC, "msim_host.cpp")]
+ARCH = os.environ.get("MSIM_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = os.path.join(rocm, "bin", "hipcc")
+    return path if os.path.exists(path) else "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    objs = []
+    common = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
+              "-I", CSRC, "-Wall", "-Wno-unused-result",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    for src in SOURCES:
+        obj = os.path.join(CSRC, os.path.basename(src) + ".o")
+        cmd = [hipcc()] + common + ["-x", "hip", "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + ["-lpthread"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    for o in objs:
+        os.remove(o)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,736 @@
+/*
+ * msim_host.cpp -- host side of the C ABI declared in include/msim.h.
+ *
+ * msim_create validates the batch and compiles every experiment into one
+ * arena (see msim_layout.h): ports numbered by cable order, up/down shortest
+ * path routes with ECMP (Multiverse section 5: ECMP load balancing; the
+ * candidate order and hash are this library's reading), the collectives'
+ * point-to-point connections and flow schedules (Multiverse section 3.1: the
+ * system simulator produces point-to-point flows from NCCL's collective
+ * algorithms; AutoCCL section 2.3: NC channels moving chunks of size C one
+ * after the other; AlpaComm section 3.1 Fig. 3d: pipelined broadcast), and the
+ * initial mutable state.  msim_bind uploads the arenas; msim_run launches the
+ * megakernel; msim_results reads the per-experiment totals back.
+ */
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "msim.h"
+#include "msim_layout.h"
+
+extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t grid, uint32_t block, uint32_t lds,
+                                      hipStream_t stream);
+extern "C" hipError_t msim_launch_reset(const KParams *kp, uint64_t o_rec_all, uint64_t rec_words,
+                                        hipStream_t stream);
+extern "C" hipError_t msim_occupancy(uint32_t block, uint32_t lds, int *blocks_per_cu);
+extern "C" hipError_t msim_set_lds_limit(uint32_t lds);
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct Compiled {
+    std::vector<uint8_t> arena;  /* RO + initial RW image, size multiple of 16 */
+    uint32_t rw_off = 0, bytes = 0;
+    uint64_t n_flows = 0, n_conns = 0, n_ports = 0;
+    uint64_t est_hops = 0, est_delivered = 0;
+    int err = 0;
+    std::string msg;
+};
+
+uint32_t fmix32(uint32_t h)
+{
+    /* MurmurHash3 32-bit finaliser (Appleby, public domain) */
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+int fail(Compiled &c, int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c.err = code;
+    c.msg = buf;
+    return code;
+}
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+/* One connection before layout. */
+struct Conn {
+    uint32_t src, dst, grp, idx;
+    uint32_t route = 0, links = 0, lidx = 0;
+    uint64_t pkts = 0;
+};
+
+/* Chunk rank i sends at step s of a ring round. */
+uint32_t ring_chunk(uint32_t kind, uint32_t N, uint32_t i, uint32_t s)
+{
+    if (kind == GK_RING_AG || s < N - 1) return (i + N - s) % N;
+    uint32_t s2 = s - (N - 1);
+    return (i + 1 + N - s2) % N;
+}
+
+uint32_t first_flow_size(const Grp &g, uint32_t idx)
+{
+    if (g.kind == GK_XFLOW) return idx;
+    if (g.kind == GK_BCAST) return g.p / g.S + (0 < g.p % g.S ? 1u : 0u);
+    if (g.R > 1) return g.p;
+    uint32_t k = ring_chunk(g.kind, g.N, idx, 0);
+    return g.X / g.N + (k < g.X % g.N ? 1u : 0u);
+}
+
+int compile_exp(const msim_batch_spec *s, uint32_t e, Compiled &out)
+{
+    const uint32_t t = s->exp_topo[e], w = s->exp_work[e];
+    if (t >= s->n_topo || w >= s->n_work) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: topology/workload index out of range", e);
+    const uint32_t Q = s->exp_queue_pkts[e], seed = s->exp_ecmp_seed[e];
+    const uint64_t pkt = s->exp_pkt_bytes[e];
+    if (Q < 1 || Q > MSIM_MAX_QUEUE) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: queue %u outside 1..%u", e, Q, MSIM_MAX_QUEUE);
+    if (pkt == 0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: zero packet size", e);
+
+    /* ---- topology: nodes, ports numbered by cable order */
+    const uint32_t n0 = s->topo_node_off[t], nn = s->topo_node_off[t + 1] - n0;
+    const uint32_t c0 = s->topo_cable_off[t], nc = s->topo_cable_off[t + 1] - c0;
+    const uint8_t *layer = s->node_layer + n0;
+    std::vector<uint32_t> deg(nn, 0);
+    uint32_t maxd = 1, maxr = 1;
+    for (uint32_t k = 0; k < nc; k++) {
+        uint32_t a = s->cable_a[c0 + k], b = s->cable_b[c0 + k];
+        if (a >= nn || b >= nn || a == b) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: cable %u has bad endpoints", e, k);
+        if (layer[a] == layer[b]) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: cable %u joins two nodes of layer %u", e, k, layer[a]);
+        uint32_t ra = s->cable_rate_ab[c0 + k], rb = s->cable_rate_ba[c0 + k], d = s->cable_delay[c0 + k];
+        if (ra < 1 || rb < 1 || ra > MSIM_MAX_RATE || rb > MSIM_MAX_RATE) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: cable %u rate outside 1..%u", e, k, MSIM_MAX_RATE);
+        if (d < 1 || d > MSIM_MAX_DELAY) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: cable %u delay outside 1..%u", e, k, MSIM_MAX_DELAY);
+        maxd = std::max(maxd, d);
+        maxr = std::max(maxr, std::max(ra, rb));
+        deg[a]++;
+        deg[b]++;
+    }
+    std::vector<uint32_t> pbase(nn + 1, 0), vbase(nn, 0), host_of(nn, MSIM_NONE);
+    uint32_t n_voq = 0, n_hosts = 0;
+    for (uint32_t n = 0; n < nn; n++) {
+        if (layer[n] == 0) {
+            if (deg[n] != 1) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: host node %u has %u cables (needs exactly 1)", e, n, deg[n]);
+            host_of[n] = n_hosts++;
+        } else {
+            if (deg[n] > MSIM_MAX_SWITCH_PORTS) return fail(out, MSIM_E_LIMIT, "experiment %u: switch %u has %u ports (max %u)", e, n, deg[n], MSIM_MAX_SWITCH_PORTS);
+            vbase[n] = n_voq;
+            n_voq += deg[n] * deg[n];
+        }
+        pbase[n + 1] = pbase[n] + deg[n];
+    }
+    const uint32_t n_ports = pbase[nn];
+    std::vector<PortRO> port(n_ports);
+    std::vector<uint32_t> port_node(n_ports), fill(nn, 0);
+    for (uint32_t k = 0; k < nc; k++) {
+        uint32_t a = s->cable_a[c0 + k], b = s->cable_b[c0 + k];
+        uint32_t pa = pbase[a] + fill[a]++, pb = pbase[b] + fill[b]++;
+        bool alive = s->cable_alive[c0 + k] != 0;
+        PortRO &A = port[pa], &B = port[pb];
+        A.peer = pb; B.peer = pa;
+        A.rate = s->cable_rate_ab[c0 + k]; B.rate = s->cable_rate_ba[c0 + k];
+        A.delay = B.delay = s->cable_delay[c0 + k];
+        A.alive = B.alive = alive ? 1 : 0;
+        port_node[pa] = a; port_node[pb] = b;
+    }
+    for (uint32_t n = 0; n < nn; n++)
+        for (uint32_t p = pbase[n]; p < pbase[n + 1]; p++) {
+            PortRO &P = port[p];
+            P.base = pbase[n];
+            P.vbase = vbase[n];
+            P.host = host_of[n];
+            P.local = (uint8_t)(p - pbase[n]);
+            P.deg = (uint8_t)deg[n];
+            P.is_host = layer[n] == 0;
+            P.peer_is_host = layer[port_node[P.peer]] == 0;
+            P.pad = 0;
+        }
+
+    /* ---- workload: groups and connections */
+    std::vector<Grp> grp;
+    std::vector<Conn> conn;
+    uint64_t fid = 0;
+    auto is_host = [&](uint32_t h) { return h < nn && layer[h] == 0; };
+    for (uint32_t ci = s->work_coll_off[w]; ci < s->work_coll_off[w + 1]; ci++) {
+        const uint32_t *mem = s->member_host + s->coll_member_off[ci];
+        const uint32_t N = s->coll_member_off[ci + 1] - s->coll_member_off[ci];
+        if (N < 2) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u has %u members", e, ci, N);
+        for (uint32_t i = 0; i < N; i++) {
+            if (!is_host(mem[i])) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u member %u is not a host", e, ci, mem[i]);
+            for (uint32_t j = 0; j < i; j++)
+                if (mem[j] == mem[i]) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u repeats host %u", e, ci, mem[i]);
+        }
+        const uint64_t P = (s->coll_bytes[ci] + pkt - 1) / pkt;
+        const uint32_t type = s->coll_type[ci];
+        if (type == MSIM_COLL_RING_ALLREDUCE || type == MSIM_COLL_RING_ALLGATHER) {
+            const uint32_t NC = s->coll_nc[ci];
+            const uint64_t cb = s->coll_chunk_bytes[ci];
+            if (NC < 1 || cb == 0 || cb % pkt) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u needs NC >= 1 and a chunk of whole packets", e, ci);
+            const uint64_t p = cb / pkt;
+            const uint32_t kind = type == MSIM_COLL_RING_ALLREDUCE ? GK_RING_AR : GK_RING_AG;
+            const uint32_t S = kind == GK_RING_AR ? 2 * (N - 1) : N - 1;
+            for (uint32_t c = 0; c < NC; c++) {
+                const uint64_t Pc = P / NC + (c < P % NC ? 1 : 0);
+                if (Pc < N) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u channel %u carries %llu packets for %u ranks", e, ci, c, (unsigned long long)Pc, N);
+                uint64_t R = (Pc + N * p - 1) / (N * p);
+                uint64_t X = Pc - (R - 1) * N * p;
+                if (R > 1 && X < N) { R--; X = Pc - (R - 1) * N * p; }
+                if (R * S > CS_POS_MASK || p > 0xFFFFFFFFull || X > 0xFFFFFFFFull) return fail(out, MSIM_E_LIMIT, "experiment %u: collective %u too large", e, ci);
+                Grp g{};
+                g.kind = kind; g.N = N; g.S = S; g.R = (uint32_t)R; g.p = (uint32_t)p; g.X = (uint32_t)X;
+                g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size();
+                fid += R * S * N;
+                if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
+                for (uint32_t i = 0; i < N; i++) {
+                    Conn cn;
+                    cn.src = mem[i]; cn.dst = mem[(i + 1) % N]; cn.grp = (uint32_t)grp.size(); cn.idx = i;
+                    uint64_t last = 0;
+                    for (uint32_t st = 0; st < S; st++) {
+                        uint32_t k = ring_chunk(kind, N, i, st);
+                        last += X / N + (k < X % N ? 1 : 0);
+                    }
+                    cn.pkts = (R - 1) * S * p + last;
+                    conn.push_back(cn);
+                }
+                grp.push_back(g);
+            }
+        } else if (type == MSIM_COLL_PIPE_BROADCAST) {
+            const uint64_t K = s->coll_k[ci];
+            if (K < 1 || K > P || P > 0xFFFFFFFFull) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: broadcast %u needs 1 <= K <= packets", e, ci);
+            const uint32_t A = N - 1;
+            Grp g{};
+            g.kind = GK_BCAST; g.N = A; g.S = (uint32_t)K; g.R = 1; g.p = (uint32_t)P; g.X = 0;
+            g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size();
+            fid += (uint64_t)A * K;
+            if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
+            for (uint32_t j = 1; j <= A; j++) {
+                Conn cn;
+                cn.src = mem[j - 1]; cn.dst = mem[j]; cn.grp = (uint32_t)grp.size(); cn.idx = j - 1; cn.pkts = P;
+                conn.push_back(cn);
+            }
+            grp.push_back(g);
+        } else {
+            return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u has unknown type %u", e, ci, type);
+        }
+    }
+    const uint64_t x0 = s->work_xflow_off[w], x1 = s->work_xflow_off[w + 1];
+    if (x1 > x0) {
+        Grp g{};
+        g.kind = GK_XFLOW; g.N = (uint32_t)(x1 - x0); g.S = 1; g.R = 1;
+        g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size();
+        fid += x1 - x0;
+        if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
+        for (uint64_t xi = x0; xi < x1; xi++) {
+            uint32_t a = s->xflow_src[xi], b = s->xflow_dst[xi], n = s->xflow_pkts[xi];
+            if (!is_host(a) || !is_host(b) || a == b || n == 0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: explicit flow %llu invalid", e, (unsigned long long)(xi - x0));
+            Conn cn;
+            cn.src = a; cn.dst = b; cn.grp = (uint32_t)grp.size(); cn.idx = n; cn.pkts = n;
+            conn.push_back(cn);
+        }
+        grp.push_back(g);
+    }
+    if (conn.size() >= (1u << (32 - DESC_SHIFT))) return fail(out, MSIM_E_LIMIT, "experiment %u: too many connections", e);
+
+    /* ---- routes: reverse breadth-first search over (node, may-still-climb)
+     * states from every destination, then one walk per connection */
+    std::vector<std::vector<uint32_t>> by_dst(nn);
+    for (uint32_t c = 0; c < conn.size(); c++) by_dst[conn[c].dst].push_back(c);
+    std::vector<int32_t> dist(2 * (size_t)nn);
+    std::deque<uint32_t> bfs;
+    std::vector<uint32_t> cand;
+    for (uint32_t dst = 0; dst < nn; dst++) {
+        if (by_dst[dst].empty()) continue;
+        std::fill(dist.begin(), dist.end(), -1);
+        /* state 2n: at n, may still climb; 2n+1: at n, descending only */
+        dist[2 * dst] = dist[2 * dst + 1] = 0;
+        bfs.clear();
+        bfs.push_back(2 * dst);
+        bfs.push_back(2 * dst + 1);
+        while (!bfs.empty()) {
+            uint32_t st = bfs.front();
+            bfs.pop_front();
+            uint32_t m = st >> 1;
+            bool desc = st & 1;
+            for (uint32_t p = pbase[m]; p < pbase[m + 1]; p++) {
+                if (!port[p].alive) continue;
+                uint32_t n = port_node[port[p].peer];
+                if (!desc && layer[n] < layer[m]) {          /* n climbed to m */
+                    if (dist[2 * n] < 0) { dist[2 * n] = dist[st] + 1; bfs.push_back(2 * n); }
+                } else if (desc && layer[n] > layer[m]) {    /* n descended to m */
+                    for (uint32_t ph = 0; ph < 2; ph++)
+                        if (dist[2 * n + ph] < 0) { dist[2 * n + ph] = dist[st] + 1; bfs.push_back(2 * n + ph); }
+                }
+            }
+        }
+        for (uint32_t c : by_dst[dst]) {
+            Conn &cn = conn[c];
+            uint32_t node = cn.src, state = 2 * node, hop = 0, links = 0;
+            if (dist[state] < 0) return fail(out, MSIM_E_UNROUTABLE, "experiment %u: connection %u (host %u -> host %u) has no path", e, c, cn.src, dst);
+            while (node != dst) {
+                cand.clear();
+                for (uint32_t p = pbase[node]; p < pbase[node + 1]; p++) {
+                    if (!port[p].alive) continue;
+                    uint32_t m = port_node[port[p].peer];
+                    if (layer[m] > layer[node] && !(state & 1)) {
+                        if (dist[2 * m] >= 0 && dist[2 * m] + 1 == dist[state]) cand.push_back(p);
+                    } else if (layer[m] < layer[node]) {
+                        if (dist[2 * m + 1] >= 0 && dist[2 * m + 1] + 1 == dist[state]) cand.push_back(p);
+                    }
+                }
+                if (cand.empty()) return fail(out, MSIM_E_UNROUTABLE, "experiment %u: connection %u stuck at node %u", e, c, node);
+                uint32_t pick = cand[fmix32((uint32_t)c ^ fmix32(node ^ seed)) % cand.size()];
+                if (layer[node] != 0) {
+                    if (hop >= MSIM_MAX_SWITCH_HOPS) return fail(out, MSIM_E_LIMIT, "experiment %u: connection %u crosses more than %u switches", e, c, MSIM_MAX_SWITCH_HOPS);
+                    cn.route |= (pick - pbase[node]) << (4 * hop);
+                    hop++;
+                }
+                uint32_t next = port_node[port[pick].peer];
+                if (layer[next] < layer[node]) state = 2 * next + 1;
+                else state = (state & 1) ? 2 * next + 1 : 2 * next;
+                node = next;
+                links++;
+            }
+            cn.links = links;
+        }
+    }
+
+    /* ---- hosts: outgoing connections in index order, flows to receive */
+    std::vector<HostRO> host(n_hosts);
+    std::vector<uint32_t> n_out(n_hosts, 0), left(n_hosts, 0);
+    for (auto &cn : conn) n_out[host_of[cn.src]]++;
+    std::vector<uint32_t> hout(conn.size());
+    uint32_t acc = 0, words = 0;
+    for (uint32_t n = 0; n < nn; n++) {
+        if (layer[n] != 0) continue;
+        uint32_t h = host_of[n];
+        host[h].port = pbase[n];
+        host[h].out_off = acc;
+        host[h].n_out = 0;
+        host[h].rdy_off = words;
+        acc += n_out[h];
+        words += (n_out[h] + 31) / 32;
+    }
+    uint64_t n_flows = 0;
+    for (uint32_t c = 0; c < conn.size(); c++) {
+        Conn &cn = conn[c];
+        HostRO &hr = host[host_of[cn.src]];
+        cn.lidx = hr.n_out;
+        hout[hr.out_off + hr.n_out++] = c;
+        const Grp &g = grp[cn.grp];
+        uint32_t F = g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
+        left[host_of[cn.dst]] += F;
+        n_flows += F;
+        out.est_hops += cn.pkts * cn.links;
+        out.est_delivered += cn.pkts;
+    }
+
+    /* ---- layout */
+    const uint32_t W = maxd + 1, R = maxr, nconn = (uint32_t)conn.size(), ngrp = (uint32_t)grp.size();
+    ArenaHdr H{};
+    H.n_ports = n_ports; H.n_hosts = n_hosts; H.n_conn = nconn; H.n_grp = ngrp;
+    H.Q = Q; H.W = W; H.R = R; H.n_voq = n_voq; H.n_flows = (uint32_t)n_flows;
+    size_t off = align16(sizeof(ArenaHdr));
+    auto take = [&](uint32_t &field, size_t bytes) { field = (uint32_t)off; off = align16(off + bytes); };
+    take(H.o_port, sizeof(PortRO) * n_ports);
+    take(H.o_conn, sizeof(ConnRO) * nconn);
+    take(H.o_grp, sizeof(Grp) * ngrp);
+    take(H.o_hout, 4ull * nconn);
+    take(H.o_host, sizeof(HostRO) * n_hosts);
+    H.rw_off = (uint32_t)off;
+    take(H.o_arr, n_voq);
+    take(H.o_phead, n_voq);
+    take(H.o_nslot, n_voq);
+    take(H.o_head, n_voq);
+    take(H.o_tslot, n_voq);
+    take(H.o_fcur, n_voq);
+    take(H.o_hseen, n_voq);
+    take(H.o_pdesc, 4ull * n_ports * Q);
+    take(H.o_pnxt, (size_t)n_ports * Q);
+    take(H.o_fstk, (size_t)n_ports * Q);
+    take(H.o_pstate, sizeof(PortRW) * n_ports);
+    take(H.o_scnt, (size_t)n_ports * W);
+    take(H.o_sdesc, 4ull * n_ports * W * R);
+    take(H.o_cstate, sizeof(ConnRW) * nconn);
+    take(H.o_hstate, sizeof(HostRW) * n_hosts);
+    take(H.o_ready, 4ull * words);
+    if (off > 0xFFFFFFF0ull) return fail(out, MSIM_E_LIMIT, "experiment %u: state of %zu bytes too large", e, off);
+    H.bytes = (uint32_t)off;
+    out.arena.assign(off, 0);
+    uint8_t *A = out.arena.data();
+    memcpy(A, &H, sizeof H);
+    memcpy(A + H.o_port, port.data(), sizeof(PortRO) * n_ports);
+    std::vector<ConnRO> cro(nconn);
+    for (uint32_t c = 0; c < nconn; c++) cro[c] = ConnRO{conn[c].route, conn[c].grp, conn[c].idx, conn[c].lidx};
+    if (nconn) memcpy(A + H.o_conn, cro.data(), sizeof(ConnRO) * nconn);
+    if (ngrp) memcpy(A + H.o_grp, grp.data(), sizeof(Grp) * ngrp);
+    if (nconn) memcpy(A + H.o_hout, hout.data(), 4ull * nconn);
+    if (n_hosts) memcpy(A + H.o_host, host.data(), sizeof(HostRO) * n_hosts);
+    PortRW *ps = (PortRW *)(A + H.o_pstate);
+    for (uint32_t p = 0; p < n_ports; p++) {
+        if (port[p].is_host) continue;
+        uint8_t *fs = A + H.o_fstk + (size_t)p * Q;
+        for (uint32_t k = 0; k < Q; k++) fs[k] = (uint8_t)k;
+        ps[p].ftop = Q;
+    }
+    ConnRW *cs = (ConnRW *)(A + H.o_cstate);
+    for (uint32_t c = 0; c < nconn; c++) cs[c].r_rem = first_flow_size(grp[conn[c].grp], conn[c].idx);
+    HostRW *hs = (HostRW *)(A + H.o_hstate);
+    for (uint32_t h = 0; h < n_hosts; h++) hs[h].left = left[h];
+    out.rw_off = H.rw_off;
+    out.bytes = H.bytes;
+    out.n_flows = n_flows;
+    out.n_conns = nconn;
+    out.n_ports = n_ports;
+    return MSIM_OK;
+}
+
+} // namespace
+
+struct msim_ctx {
+    uint32_t n_exp = 0;
+    std::vector<Compiled> exps;
+    std::vector<uint32_t> order;
+    std::vector<uint64_t> arena_off, pristine_off, rec_off;
+    std::vector<uint8_t> recorded;
+    uint64_t o_state = 0, o_arena_off = 0, o_order = 0, o_rec_off = 0, o_pristine = 0, o_rec_all = 0;
+    uint64_t rec_words = 0, ws_bytes = 0;
+    uint32_t block = 0, grid = 0, lds = 0, n_lds = 0, max_ports = 0, force_global = 0;
+    uint64_t max_arena = 0;
+    uint8_t *ws = nullptr;
+    bool bound = false;
+    std::string err;
+    msim_info info{};
+};
+
+static int ctx_fail(msim_ctx *c, int code, const std::string &m)
+{
+    if (c) c->err = m;
+    return code;
+}
+
+static int hip_fail(msim_ctx *c, hipError_t e, const char *what)
+{
+    return ctx_fail(c, MSIM_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts, msim_ctx **out)
+{
+    g_create_error.clear();
+    if (!out) { g_create_error = "null output pointer"; return MSIM_E_ARG; }
+    *out = nullptr;
+    if (!spec) { g_create_error = "null spec"; return MSIM_E_ARG; }
+    if (spec->version != MSIM_ABI_VERSION) { g_create_error = "spec version mismatch"; return MSIM_E_ARG; }
+    if (opts && opts->version != MSIM_ABI_VERSION) { g_create_error = "options version mismatch"; return MSIM_E_ARG; }
+    const uint32_t E = spec->n_exp;
+    if (E == 0 || !spec->exp_topo || !spec->exp_work || !spec->exp_queue_pkts || !spec->exp_ecmp_seed ||
+        !spec->exp_pkt_bytes || !spec->topo_node_off || !spec->topo_cable_off || !spec->work_coll_off ||
+        !spec->work_xflow_off) {
+        g_create_error = "empty batch or missing array";
+        return MSIM_E_ARG;
+    }
+    msim_ctx *ctx = new msim_ctx();
+    ctx->n_exp = E;
+    ctx->exps.resize(E);
+    ctx->force_global = opts ? opts->force_global : 0;
+    unsigned nt = opts && opts->host_threads ? opts->host_threads : std::max(1u, std::thread::hardware_concurrency());
+    nt = std::min<unsigned>(nt, E);
+    std::atomic<uint32_t> next{0};
+    auto worker = [&]() {
+        for (;;) {
+            uint32_t e = next.fetch_add(1);
+            if (e >= E) break;
+            compile_exp(spec, e, ctx->exps[e]);
+        }
+    };
+    std::vector<std::thread> th;
+    for (unsigned i = 1; i < nt; i++) th.emplace_back(worker);
+    worker();
+    for (auto &x : th) x.join();
+    for (uint32_t e = 0; e < E; e++)
+        if (ctx->exps[e].err) {
+            g_create_error = ctx->exps[e].msg;
+            int code = ctx->exps[e].err;
+            delete ctx;
+            return code;
+        }
+    /* recorded experiments */
+    ctx->recorded.assign(E, 0);
+    if (opts && opts->n_record) {
+        if (!opts->record_exp) { g_create_error = "record_exp is null"; delete ctx; return MSIM_E_ARG; }
+        for (uint32_t i = 0; i < opts->n_record; i++) {
+            if (opts->record_exp[i] >= E) { g_create_error = "record_exp index out of range"; delete ctx; return MSIM_E_ARG; }
+            ctx->recorded[opts->record_exp[i]] = 1;
+        }
+    }
+    /* longest-processing-time order: biggest experiments are claimed first */
+    ctx->order.resize(E);
+    for (uint32_t e = 0; e < E; e++) ctx->order[e] = e;
+    std::stable_sort(ctx->order.begin(), ctx->order.end(), [&](uint32_t a, uint32_t b) {
+        return ctx->exps[a].est_hops > ctx->exps[b].est_hops;
+    });
+    /* workspace layout */
+    uint64_t off = 256;
+    auto take = [&](uint64_t bytes) { uint64_t o = off; off = (off + bytes + 255) & ~255ull; return o; };
+    ctx->o_state = take(sizeof(ExpState) * (uint64_t)E);
+    ctx->o_arena_off = take(8ull * E);
+    ctx->o_order = take(4ull * E);
+    ctx->o_rec_off = take(8ull * E);
+    ctx->o_pristine = take(8ull * E);
+    ctx->arena_off.resize(E);
+    ctx->pristine_off.resize(E);
+    ctx->rec_off.assign(E, ~0ull);
+    msim_info &I = ctx->info;
+    for (uint32_t e = 0; e < E; e++) {
+        const Compiled &c = ctx->exps[e];
+        ctx->arena_off[e] = take(c.bytes);
+        ctx->max_arena = std::max<uint64_t>(ctx->max_arena, c.bytes);
+        ctx->max_ports = std::max<uint32_t>(ctx->max_ports, (uint32_t)c.n_ports);
+        I.total_flows += c.n_flows;
+        I.total_conns += c.n_conns;
+        I.est_pkt_hops += c.est_hops;
+        I.est_delivered += c.est_delivered;
+    }
+    for (uint32_t e = 0; e < E; e++) ctx->pristine_off[e] = take(ctx->exps[e].bytes - ctx->exps[e].rw_off);
+    ctx->o_rec_all = off;
+    uint64_t rw = 0;
+    for (uint32_t e = 0; e < E; e++)
+        if (ctx->recorded[e]) { ctx->rec_off[e] = off + 4ull * rw; rw += 3ull * ctx->exps[e].n_flows; }
+    ctx->rec_words = rw;
+    take(4ull * rw);
+    ctx->ws_bytes = off;
+    /* every region a kernel touches must lie inside the workspace */
+    bool inside = ctx->o_pristine + 8ull * E <= ctx->arena_off[0] && ctx->o_rec_all + 4ull * rw <= off;
+    for (uint32_t e = 0; e < E && inside; e++) {
+        const Compiled &c = ctx->exps[e];
+        inside = ctx->arena_off[e] + c.bytes <= ctx->pristine_off[0] &&
+                 ctx->pristine_off[e] + (c.bytes - c.rw_off) <= ctx->o_rec_all &&
+                 (!ctx->recorded[e] || ctx->rec_off[e] + 12ull * c.n_flows <= off);
+    }
+    if (!inside) { g_create_error = "internal error: workspace layout overlaps its bounds"; delete ctx; return MSIM_E_LIMIT; }
+    /* launch shape */
+    uint32_t bt = opts && opts->block_threads ? opts->block_threads : ((ctx->max_ports + 63) / 64) * 64;
+    bt = std::max(64u, std::min(1024u, bt));
+    if (bt % 64) { g_create_error = "block_threads must be a multiple of 64"; delete ctx; return MSIM_E_ARG; }
+    ctx->block = bt;
+    I.n_exp = E;
+    I.block_threads = bt;
+    I.max_ports = ctx->max_ports;
+    I.max_arena_bytes = ctx->max_arena;
+    I.workspace_bytes = ctx->ws_bytes;
+    *out = ctx;
+    return MSIM_OK;
+}
+
+extern "C" int msim_workspace_size(const msim_ctx *ctx, uint64_t *bytes)
+{
+    if (!ctx || !bytes) return MSIM_E_ARG;
+    *bytes = ctx->ws_bytes;
+    return MSIM_OK;
+}
+
+extern "C" int msim_bind(msim_ctx *ctx, void *dev_ws, uint64_t ws_bytes, void *stream_)
+{
+    if (!ctx) return MSIM_E_ARG;
+    hipStream_t stream = (hipStream_t)stream_;
+    if (!dev_ws || ws_bytes < ctx->ws_bytes || ((uintptr_t)dev_ws & 255))
+        return ctx_fail(ctx, MSIM_E_WORKSPACE, "workspace missing, smaller than msim_workspace_size or not 256-byte aligned");
+    ctx->ws = (uint8_t *)dev_ws;
+    const uint32_t E = ctx->n_exp;
+    /* LDS placement: every arena that fits in the LDS a workgroup can get */
+    int dev = 0, max_lds = 0, n_cu = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he == hipSuccess) he = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (he == hipSuccess) he = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (he != hipSuccess) return hip_fail(ctx, he, "device query");
+    const uint32_t static_lds = 2048;
+    uint32_t budget = max_lds > (int)static_lds ? (uint32_t)max_lds - static_lds : 0;
+    ctx->lds = 0;
+    ctx->n_lds = 0;
+    if (!ctx->force_global) {
+        uint32_t need = 0;
+        for (uint32_t e = 0; e < E; e++)
+            if (ctx->exps[e].bytes <= budget) { need = std::max(need, ctx->exps[e].bytes); ctx->n_lds++; }
+        ctx->lds = need ? ((need + 255) / 256) * 256 : 0;
+        if (ctx->lds > budget) ctx->lds = need;
+    }
+    if (ctx->lds) {
+        he = msim_set_lds_limit(ctx->lds);
+        if (he != hipSuccess) return hip_fail(ctx, he, "hipFuncSetAttribute(dynamic LDS)");
+    }
+    int per_cu = 0;
+    he = msim_occupancy(ctx->block, ctx->lds, &per_cu);
+    if (he != hipSuccess) return hip_fail(ctx, he, "occupancy query");
+    if (per_cu < 1) per_cu = 1;
+    ctx->grid = (uint32_t)std::min<uint64_t>(E, (uint64_t)n_cu * per_cu);
+    ctx->info.grid_blocks = ctx->grid;
+    ctx->info.lds_bytes = ctx->lds;
+    ctx->info.n_lds_exp = ctx->n_lds;
+    /* upload: tables, then arenas and their pristine mutable parts */
+    std::vector<uint8_t> head(ctx->exps.empty() ? 0 : (size_t)(ctx->arena_off[0]), 0);
+    WsHdr wh{};
+    wh.n_exp = E;
+    memcpy(head.data(), &wh, sizeof wh);
+    ExpState *st = (ExpState *)(head.data() + ctx->o_state);
+    for (uint32_t e = 0; e < E; e++) {
+        st[e] = ExpState{};
+        st[e].status = ctx->exps[e].n_flows == 0 ? MSIM_EXP_DONE : MSIM_EXP_INCOMPLETE;
+    }
+    memcpy(head.data() + ctx->o_arena_off, ctx->arena_off.data(), 8ull * E);
+    memcpy(head.data() + ctx->o_order, ctx->order.data(), 4ull * E);
+    memcpy(head.data() + ctx->o_rec_off, ctx->rec_off.data(), 8ull * E);
+    memcpy(head.data() + ctx->o_pristine, ctx->pristine_off.data(), 8ull * E);
+    he = hipMemcpyAsync(ctx->ws, head.data(), head.size(), hipMemcpyHostToDevice, stream);
+    /* arenas are contiguous in experiment order: copy them in large batches */
+    std::vector<uint8_t> stage;
+    auto flush = [&](uint64_t dst) -> hipError_t {
+        if (stage.empty()) return hipSuccess;
+        hipError_t r = hipMemcpyAsync(ctx->ws + dst, stage.data(), stage.size(), hipMemcpyHostToDevice, stream);
+        if (r == hipSuccess) r = hipStreamSynchronize(stream);
+        stage.clear();
+        return r;
+    };
+    const size_t chunk = 64u << 20;
+    uint64_t run_start = ctx->arena_off[0];
+    for (uint32_t e = 0; e < E && he == hipSuccess; e++) {
+        if (ctx->arena_off[e] != run_start + stage.size()) {
+            he = flush(run_start);
+            run_start = ctx->arena_off[e];
+        }
+        stage.insert(stage.end(), ctx->exps[e].arena.begin(), ctx->exps[e].arena.end());
+        stage.resize(((stage.size() + 255) / 256) * 256, 0);
+        if (stage.size() >= chunk) { he = flush(run_start); run_start = e + 1 < E ? ctx->arena_off[e + 1] : 0; }
+    }
+    if (he == hipSuccess) he = flush(run_start);
+    if (E) run_start = ctx->pristine_off[0];
+    for (uint32_t e = 0; e < E && he == hipSuccess; e++) {
+        const Compiled &c = ctx->exps[e];
+        if (ctx->pristine_off[e] != run_start + stage.size()) {
+            he = flush(run_start);
+            run_start = ctx->pristine_off[e];
+        }
+        stage.insert(stage.end(), c.arena.begin() + c.rw_off, c.arena.end());
+        stage.resize(((stage.size() + 255) / 256) * 256, 0);
+        if (stage.size() >= chunk) { he = flush(run_start); run_start = e + 1 < E ? ctx->pristine_off[e + 1] : 0; }
+    }
+    if (he == hipSuccess) he = flush(run_start);
+    if (he == hipSuccess) he = hipStreamSynchronize(stream);
+    if (he != hipSuccess) return hip_fail(ctx, he, "upload");
+    ctx->bound = true;
+    int rc = msim_reset(ctx, stream_);
+    if (rc) return rc;
+    he = hipStreamSynchronize(stream);
+    if (he != hipSuccess) return hip_fail(ctx, he, "reset");
+    return MSIM_OK;
+}
+
+static KParams make_params(const msim_ctx *ctx, uint32_t max_ticks)
+{
+    KParams kp{};
+    kp.ws = ctx->ws;
+    kp.o_state = ctx->o_state;
+    kp.o_arena_off = ctx->o_arena_off;
+    kp.o_order = ctx->o_order;
+    kp.o_rec_off = ctx->o_rec_off;
+    kp.o_pristine = ctx->o_pristine;
+    kp.n_exp = ctx->n_exp;
+    kp.max_ticks = max_ticks;
+    kp.lds_bytes = ctx->lds;
+    return kp;
+}
+
+extern "C" int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *stream, uint32_t flags)
+{
+    if (!ctx) return MSIM_E_ARG;
+    if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_run before msim_bind");
+    (void)flags;
+    KParams kp = make_params(ctx, max_ticks);
+    hipError_t he = msim_launch_run(&kp, ctx->grid, ctx->block, ctx->lds, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_fail(ctx, he, "kernel launch");
+    return MSIM_OK;
+}
+
+extern "C" int msim_reset(msim_ctx *ctx, void *stream)
+{
+    if (!ctx) return MSIM_E_ARG;
+    if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_reset before msim_bind");
+    KParams kp = make_params(ctx, 0);
+    hipError_t he = msim_launch_reset(&kp, ctx->o_rec_all, ctx->rec_words, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_fail(ctx, he, "reset launch");
+    return MSIM_OK;
+}
+
+extern "C" int msim_results(msim_ctx *ctx, void *stream, uint8_t *exp_status, uint32_t *exp_tick,
+                            uint64_t *exp_pkt_hops, uint64_t *exp_delivered, uint64_t *exp_digest)
+{
+    if (!ctx) return MSIM_E_ARG;
+    if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_results before msim_bind");
+    hipError_t he = hipStreamSynchronize((hipStream_t)stream);
+    std::vector<ExpState> st(ctx->n_exp);
+    if (he == hipSuccess) he = hipMemcpy(st.data(), ctx->ws + ctx->o_state, sizeof(ExpState) * st.size(), hipMemcpyDeviceToHost);
+    if (he != hipSuccess) return hip_fail(ctx, he, "results copy");
+    bool dead = false, inc = false, fault = false;
+    for (uint32_t e = 0; e < ctx->n_exp; e++) {
+        if (exp_status) exp_status[e] = (uint8_t)st[e].status;
+        if (exp_tick) exp_tick[e] = st[e].t_out;
+        if (exp_pkt_hops) exp_pkt_hops[e] = st[e].pkt_hops;
+        if (exp_delivered) exp_delivered[e] = st[e].delivered;
+        if (exp_digest) exp_digest[e] = st[e].digest;
+        dead |= st[e].status == MSIM_EXP_DEADLOCK;
+        inc |= st[e].status == MSIM_EXP_INCOMPLETE;
+        fault |= st[e].status == MSIM_EXP_FAULT;
+    }
+    if (fault) return ctx_fail(ctx, MSIM_E_STATE, "an experiment reported an internal fault");
+    return dead ? MSIM_S_DEADLOCK : (inc ? MSIM_S_INCOMPLETE : MSIM_OK);
+}
+
+extern "C" int msim_flow_count(const msim_ctx *ctx, uint32_t exp, uint64_t *n)
+{
+    if (!ctx || !n || exp >= ctx->n_exp) return MSIM_E_ARG;
+    *n = ctx->exps[exp].n_flows;
+    return MSIM_OK;
+}
+
+extern "C" int msim_flow_ticks(msim_ctx *ctx, uint32_t exp, void *stream, uint32_t *rd, uint32_t *act, uint32_t *sd)
+{
+    if (!ctx || exp >= ctx->n_exp) return MSIM_E_ARG;
+    if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_flow_ticks before msim_bind");
+    if (!ctx->recorded[exp]) return ctx_fail(ctx, MSIM_E_ARG, "experiment not recorded");
+    hipError_t he = hipStreamSynchronize((hipStream_t)stream);
+    const uint64_t n = ctx->exps[exp].n_flows;
+    uint32_t *dst[3] = {rd, act, sd};
+    for (int k = 0; k < 3 && he == hipSuccess; k++)
+        if (dst[k] && n) he = hipMemcpy(dst[k], ctx->ws + ctx->rec_off[exp] + 4ull * k * n, 4ull * n, hipMemcpyDeviceToHost);
+    if (he != hipSuccess) return hip_fail(ctx, he, "flow ticks copy");
+    return MSIM_OK;
+}
+
+extern "C" int msim_get_info(const msim_ctx *ctx, msim_info *info)
+{
+    if (!ctx || !info) return MSIM_E_ARG;
+    *info = ctx->info;
+    return MSIM_OK;
+}
+
+extern "C" const char *msim_last_error(const msim_ctx *ctx)
+{
+    return ctx ? ctx->err.c_str() : g_create_error.c_str();
+}
+
+extern "C" void msim_destroy(msim_ctx *ctx) { delete ctx; }

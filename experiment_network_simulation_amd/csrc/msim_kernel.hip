@@ -1,0 +1,597 @@
+/*
+ * msim_kernel.hip -- persistent megakernel of the batched packet simulator
+ * (gfx950 / CDNA4).
+ *
+ * One launch simulates a whole batch (Multiverse section 4.3: one kernel per
+ * batch instead of one launch per system).  Unlike the pages' megakernel, which
+ * moves every thread of the grid through one system at a time over all
+ * experiments, each workgroup here claims one experiment at a time and runs its
+ * whole tick loop alone: experiments never interact (single-process
+ * multi-experiment, Multiverse section 2.2), so the only synchronisation is the
+ * workgroup barrier between the two phases of a tick.  The experiment's state
+ * is copied into LDS when it fits and worked on in place in HBM otherwise.
+ *
+ * Tick t (the step order of Multiverse section 3.2 -- Schedule, Send, NIC send,
+ * Forward, Transmit, NIC receive -- folded into two phases):
+ *   phase A, one thread per port (ingress side):
+ *     switch ingress: frees the buffer slots its egresses popped last tick,
+ *       appends the packets arriving at tick t to their virtual output queue
+ *       (the per-ingress to-do set of pull-based forwarding, section 4.2) and
+ *       publishes how many packets have left it (the credit its feeder sees);
+ *     host: takes delivery of arriving packets (a flow is received when its
+ *       last packet lands), then activates every connection whose next flow has
+ *       its predecessors met (the Schedule system, section 3.2).
+ *   barrier
+ *   phase D, one thread per port (output side), rounds m < rate:
+ *     the output pulls from the ingresses of its node -- first eligible one
+ *     going round from its round-robin pointer -- or, at a host, from its
+ *     active connections, while credit (buffer room downstream) lasts, and
+ *     writes the packet into the staging slot of the far ingress for tick
+ *     t + delay.
+ *   barrier
+ * Every datum has one writer per phase (see msim_layout.h), so no atomics are
+ * used inside the tick loop; the experiment queue counter is the only atomic.
+ */
+#include <hip/hip_runtime.h>
+
+#include "msim_layout.h"
+
+#define CHECK_EVERY 16u
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z)
+{
+    /* SplitMix64 output function (Steele, Lea, Flood 2014; Vigna's constants) */
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+struct Ctx {
+    const PortRO *port;
+    const ConnRO *conn;
+    const Grp *grp;
+    const uint32_t *hout;
+    const HostRO *host;
+    uint8_t *arr, *phead, *nslot, *head, *tslot, *fcur, *hseen;
+    uint32_t *pdesc;
+    uint8_t *pnxt, *fstk;
+    PortRW *ps;
+    uint8_t *scnt;
+    uint32_t *sdesc;
+    ConnRW *cs;
+    HostRW *hs;
+    uint32_t *ready;
+    uint32_t n_ports, Q, W, R;
+    uint32_t *rec;       /* per-flow ticks (rd | act | sd), or null */
+    uint32_t n_flows;
+};
+
+struct Acc {
+    uint64_t hops, delivered, digest;
+    uint32_t tmax, last_tx1, last_act1, max_arr;
+    uint32_t left;
+    uint32_t fault;      /* set if an invariant the credits guarantee is ever broken */
+};
+
+/* ---------------------------------------------------------- flow schedule */
+
+/* Chunk rank i sends at step s of a ring round (NCCL ring order). */
+__device__ __forceinline__ uint32_t ring_chunk(uint32_t kind, uint32_t N, uint32_t i, uint32_t s)
+{
+    if (kind == GK_RING_AG || s < N - 1) return (i + N - s) % N;
+    uint32_t s2 = s - (N - 1);
+    return (i + 1 + N - s2) % N;
+}
+
+__device__ __forceinline__ uint32_t flows_per_conn(const Grp &g)
+{
+    return g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
+}
+
+__device__ __forceinline__ uint32_t flow_size(const Grp &g, const ConnRO &cr, uint32_t pos)
+{
+    if (g.kind == GK_XFLOW) return cr.idx;
+    if (g.kind == GK_BCAST) return g.p / g.S + (pos < g.p % g.S ? 1u : 0u);
+    uint32_t r = pos / g.S;
+    if (r + 1 < g.R) return g.p;
+    uint32_t s = pos - r * g.S;
+    uint32_t k = ring_chunk(g.kind, g.N, cr.idx, s);
+    return g.X / g.N + (k < g.X % g.N ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t flow_id(const Grp &g, const ConnRO &cr, uint32_t c, uint32_t pos)
+{
+    if (g.kind == GK_XFLOW) return g.fid_base + (c - g.conn_base);
+    if (g.kind == GK_BCAST) return g.fid_base + cr.idx * g.S + pos;
+    return g.fid_base + pos * g.N + cr.idx;
+}
+
+/* Is the receive predecessor of flow `pos` of connection c met? (the ring's data
+ * dependency on the previous step of rank i-1; the broadcast's dependency on the
+ * same partition one hop earlier) */
+__device__ __forceinline__ bool recv_ok(const Ctx &C, const Grp &g, const ConnRO &cr, uint32_t c,
+                                        uint32_t pos)
+{
+    if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
+        uint32_t s = pos % g.S;
+        if (s == 0) return true;
+        uint32_t cin = g.conn_base + (cr.idx + g.N - 1) % g.N;
+        return C.cs[cin].r_pos >= pos;
+    }
+    if (g.kind == GK_BCAST) {
+        if (cr.idx == 0) return true;
+        return C.cs[c - 1].r_pos > pos;
+    }
+    return true;
+}
+
+/* Connection whose flows wait on flows received over connection c. */
+__device__ __forceinline__ uint32_t dependent_of(const Grp &g, const ConnRO &cr, uint32_t c)
+{
+    if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) return g.conn_base + (cr.idx + 1) % g.N;
+    if (g.kind == GK_BCAST) return cr.idx + 1 < g.N ? c + 1 : MSIM_NONE;
+    return MSIM_NONE;
+}
+
+__device__ __forceinline__ void activate(const Ctx &C, Acc &a, uint32_t c, uint32_t pos, const Grp &g,
+                                         const ConnRO &cr, uint32_t rdy_off, uint32_t t)
+{
+    C.cs[c].s_pos = pos | (CS_ACTIVE << CS_SHIFT);
+    C.cs[c].s_rem = flow_size(g, cr, pos);
+    C.ready[rdy_off + (cr.lidx >> 5)] |= 1u << (cr.lidx & 31);
+    a.last_act1 = t + 1;
+    if (C.rec) C.rec[C.n_flows + flow_id(g, cr, c, pos)] = t;
+}
+
+/* Phase-B decision for a connection whose previous flow has left (or at t = 0). */
+__device__ __forceinline__ void check_conn(const Ctx &C, Acc &a, uint32_t c, uint32_t rdy_off, uint32_t t)
+{
+    const ConnRO cr = C.conn[c];
+    const Grp g = C.grp[cr.grp];
+    uint32_t pos = C.cs[c].s_pos & CS_POS_MASK;
+    if (pos >= flows_per_conn(g)) {
+        C.cs[c].s_pos = pos | (CS_DONE << CS_SHIFT);
+    } else if (recv_ok(C, g, cr, c, pos)) {
+        activate(C, a, c, pos, g, cr, rdy_off, t);
+    } else {
+        C.cs[c].s_pos = pos | (CS_IDLE << CS_SHIFT);
+    }
+}
+
+/* ---------------------------------------------------------------- phase A */
+
+__device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr,
+                                             uint32_t t, uint32_t slot)
+{
+    const HostRO hr = C.host[pr.host];
+    HostRW &hw = C.hs[pr.host];
+    uint32_t si = p * C.W + slot;
+    uint32_t n = C.scnt[si];
+    for (uint32_t k = 0; k < n; k++) {
+        uint32_t c = C.sdesc[si * C.R + k] >> DESC_SHIFT;
+        ConnRW &cw = C.cs[c];
+        a.delivered++;
+        if (--cw.r_rem != 0) continue;
+        const ConnRO cr = C.conn[c];
+        const Grp g = C.grp[cr.grp];
+        uint32_t pos = cw.r_pos;
+        uint32_t fid = flow_id(g, cr, c, pos);
+        a.digest += mix64(((uint64_t)fid << 32) | t);
+        a.tmax = t;
+        a.left--;
+        hw.left--;
+        if (C.rec) C.rec[fid] = t;
+        pos++;
+        cw.r_pos = pos;
+        if (pos < flows_per_conn(g)) cw.r_rem = flow_size(g, cr, pos);
+        uint32_t d = dependent_of(g, cr, c);
+        if (d != MSIM_NONE && (C.cs[d].s_pos >> CS_SHIFT) == CS_IDLE) {
+            const ConnRO dr = C.conn[d];
+            const Grp dg = C.grp[dr.grp];
+            uint32_t dpos = C.cs[d].s_pos & CS_POS_MASK;
+            if (recv_ok(C, dg, dr, d, dpos)) activate(C, a, d, dpos, dg, dr, hr.rdy_off, t);
+        }
+    }
+    if (n) C.scnt[si] = 0;
+    /* activations (phase B of the tick) */
+    if (t == 0) {
+        for (uint32_t j = 0; j < hr.n_out; j++) check_conn(C, a, C.hout[hr.out_off + j], hr.rdy_off, t);
+    } else {
+        uint32_t np = hw.pcnt;
+        for (uint32_t k = 0; k < np; k++) check_conn(C, a, hw.pend[k], hr.rdy_off, t);
+        if (np) hw.pcnt = 0;
+    }
+}
+
+__device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q, const PortRO &pr, uint32_t slot)
+{
+    const uint32_t deg = pr.deg, i = pr.local, Q = C.Q;
+    const uint32_t vrow = pr.vbase + i * deg;      /* ingress-major row of this ingress */
+    uint8_t *pnxt = C.pnxt + q * Q;
+    uint8_t *fstk = C.fstk + q * Q;
+    PortRW &pw = C.ps[q];
+    uint32_t ftop = pw.ftop;
+    uint32_t popped = 0;
+    /* free the slots of the packets the egresses took last tick */
+    for (uint32_t o = 0; o < deg; o++) {
+        uint32_t vi = vrow + o;
+        uint32_t h = C.head[vi], hs = C.hseen[vi];
+        uint32_t k = (h - hs) & 0xFFu;
+        if (!k) continue;
+        popped += k;
+        uint32_t f = C.fcur[vi];
+        for (uint32_t j = 0; j < k; j++) {
+            uint32_t s = f;
+            f = pnxt[s];
+            fstk[ftop++] = (uint8_t)s;
+        }
+        C.fcur[vi] = (uint8_t)f;
+        C.hseen[vi] = (uint8_t)h;
+    }
+    if (popped) pw.popped += popped;
+    /* append the packets that arrive now */
+    uint32_t si = q * C.W + slot;
+    uint32_t n = C.scnt[si];
+    for (uint32_t k = 0; k < n; k++) {
+        uint32_t desc = C.sdesc[si * C.R + k];
+        uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
+        uint32_t o = (C.conn[c].route >> (4 * hop)) & 0xFu;
+        if (ftop == 0 || o >= deg) { a.fault = 1; continue; }   /* cannot happen while credits hold */
+        uint32_t s = fstk[--ftop];
+        C.pdesc[q * Q + s] = desc + 1;
+        uint32_t vi = vrow + o;
+        uint32_t vp = pr.vbase + o * deg + i;
+        if (C.arr[vp] == C.hseen[vi]) {
+            C.nslot[vp] = (uint8_t)s;
+            C.fcur[vi] = (uint8_t)s;
+        } else {
+            pnxt[C.tslot[vi]] = (uint8_t)s;
+        }
+        C.tslot[vi] = (uint8_t)s;
+        C.arr[vp] = (uint8_t)(C.arr[vp] + 1);
+    }
+    if (n) C.scnt[si] = 0;
+    pw.ftop = ftop;
+}
+
+/* ---------------------------------------------------------------- phase D */
+
+__device__ __forceinline__ void transmit(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr, uint32_t desc,
+                                         uint32_t t)
+{
+    uint32_t ta = t + pr.delay;
+    uint32_t si = pr.peer * C.W + ta % C.W;
+    uint32_t k = C.scnt[si];
+    C.scnt[si] = (uint8_t)(k + 1);
+    C.sdesc[si * C.R + k] = desc;
+    a.hops++;
+    a.last_tx1 = t + 1;
+    a.max_arr = max(a.max_arr, ta);
+}
+
+__device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr, uint32_t t)
+{
+    const HostRO hr = C.host[pr.host];
+    if (!pr.alive || hr.n_out == 0) return;
+    PortRW &pw = C.ps[p];
+    int32_t credit = (int32_t)C.Q - (int32_t)(pw.pushed - C.ps[pr.peer].popped);
+    uint32_t rr = pw.rr, pushed = pw.pushed;
+    const uint32_t nw = (hr.n_out + 31) >> 5;
+    uint32_t *rdy = C.ready + hr.rdy_off;
+    HostRW &hw = C.hs[pr.host];
+    bool moved = false;
+    for (uint32_t m = 0; m < pr.rate && credit > 0; m++) {
+        /* first ready connection at or after rr, cyclically */
+        uint32_t w0 = rr >> 5, b0 = rr & 31, j = MSIM_NONE;
+        for (uint32_t k = 0; k <= nw; k++) {
+            uint32_t w = w0 + k;
+            if (w >= nw) w -= nw;
+            uint32_t bits = rdy[w];
+            if (k == 0) bits &= ~0u << b0;
+            else if (k == nw) bits &= (1u << b0) - 1u;
+            if (bits) { j = (w << 5) + __builtin_ctz(bits); break; }
+        }
+        if (j == MSIM_NONE) break;
+        uint32_t c = C.hout[hr.out_off + j];
+        transmit(C, a, p, pr, c << DESC_SHIFT, t);
+        pushed++;
+        credit--;
+        moved = true;
+        rr = j + 1 == hr.n_out ? 0 : j + 1;
+        ConnRW &cw = C.cs[c];
+        if (--cw.s_rem == 0) {
+            rdy[j >> 5] &= ~(1u << (j & 31));
+            uint32_t pos = cw.s_pos & CS_POS_MASK;
+            if (C.rec) {
+                const ConnRO cr = C.conn[c];
+                C.rec[2 * C.n_flows + flow_id(C.grp[cr.grp], cr, c, pos)] = t + 1;
+            }
+            cw.s_pos = (pos + 1) | (CS_WAIT << CS_SHIFT);
+            hw.pend[hw.pcnt++] = c;
+        }
+    }
+    if (moved) { pw.rr = rr; pw.pushed = pushed; }
+}
+
+__device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr, uint32_t t)
+{
+    if (!pr.alive) return;
+    const uint32_t deg = pr.deg, lo = pr.local, Q = C.Q;
+    PortRW &pw = C.ps[p];
+    int32_t credit = pr.peer_is_host ? (int32_t)pr.rate
+                                     : (int32_t)Q - (int32_t)(pw.pushed - C.ps[pr.peer].popped);
+    uint32_t rr = pw.rr, pushed = pw.pushed;
+    const uint32_t prow = pr.vbase + lo * deg;     /* popper-major row of this output */
+    bool moved = false;
+    for (uint32_t m = 0; m < pr.rate && credit > 0; m++) {
+        uint32_t j = MSIM_NONE;
+        uint32_t i = rr;
+        for (uint32_t k = 0; k < deg; k++) {
+            if (C.arr[prow + i] != C.phead[prow + i]) { j = i; break; }
+            i = i + 1 == deg ? 0 : i + 1;
+        }
+        if (j == MSIM_NONE) break;
+        uint32_t vp = prow + j;
+        uint32_t qi = pr.base + j;
+        uint32_t s = C.nslot[vp];
+        uint32_t desc = C.pdesc[qi * Q + s];
+        C.nslot[vp] = C.pnxt[qi * Q + s];
+        uint8_t h = (uint8_t)(C.phead[vp] + 1);
+        C.phead[vp] = h;
+        C.head[pr.vbase + j * deg + lo] = h;
+        rr = j + 1 == deg ? 0 : j + 1;
+        transmit(C, a, p, pr, desc, t);
+        pushed++;
+        credit--;
+        moved = true;
+    }
+    if (moved) { pw.rr = rr; pw.pushed = pushed; }
+}
+
+/* ------------------------------------------------------------ reductions */
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) {
+        uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+        lo = (uint32_t)__shfl_xor((int)lo, o, 64);
+        hi = (uint32_t)__shfl_xor((int)hi, o, 64);
+        v += ((uint64_t)hi << 32) | lo;
+    }
+    return v;
+}
+
+struct Shared {
+    uint32_t exp;
+    uint32_t chk_any[2][16];
+    uint32_t chk_max[2][16];
+    uint64_t sum[3][16];
+    uint32_t mx[5][16];
+};
+
+/* ----------------------------------------------------------- one experiment */
+
+template <bool IN_LDS>
+__device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
+{
+    const uint32_t tid = threadIdx.x, nth = blockDim.x;
+    const uint32_t lane = tid & 63, wave = tid >> 6, nwaves = (nth + 63) >> 6;
+    ExpState *stp = (ExpState *)(kp.ws + kp.o_state) + x;
+    const uint32_t arena_bytes = ((const ArenaHdr *)arena_g)->bytes;
+    const uint32_t rw_off = ((const ArenaHdr *)arena_g)->rw_off;
+    uint8_t *base = IN_LDS ? lds : arena_g;
+    if (IN_LDS) {
+        const uint4 *src = (const uint4 *)arena_g;
+        uint4 *dst = (uint4 *)lds;
+        for (uint32_t i = tid; i < arena_bytes / 16; i += nth) dst[i] = src[i];
+        __syncthreads();
+    }
+    const ArenaHdr *H = (const ArenaHdr *)base;
+    Ctx C;
+    C.port = (const PortRO *)(base + H->o_port);
+    C.conn = (const ConnRO *)(base + H->o_conn);
+    C.grp = (const Grp *)(base + H->o_grp);
+    C.hout = (const uint32_t *)(base + H->o_hout);
+    C.host = (const HostRO *)(base + H->o_host);
+    C.arr = base + H->o_arr;
+    C.phead = base + H->o_phead;
+    C.nslot = base + H->o_nslot;
+    C.head = base + H->o_head;
+    C.tslot = base + H->o_tslot;
+    C.fcur = base + H->o_fcur;
+    C.hseen = base + H->o_hseen;
+    C.pdesc = (uint32_t *)(base + H->o_pdesc);
+    C.pnxt = base + H->o_pnxt;
+    C.fstk = base + H->o_fstk;
+    C.ps = (PortRW *)(base + H->o_pstate);
+    C.scnt = base + H->o_scnt;
+    C.sdesc = (uint32_t *)(base + H->o_sdesc);
+    C.cs = (ConnRW *)(base + H->o_cstate);
+    C.hs = (HostRW *)(base + H->o_hstate);
+    C.ready = (uint32_t *)(base + H->o_ready);
+    C.n_ports = H->n_ports;
+    C.Q = H->Q;
+    C.W = H->W;
+    C.R = H->R;
+    C.n_flows = H->n_flows;
+    uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
+    C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
+
+    const uint32_t t0 = stp->t_now;
+    const uint32_t t_end = (uint64_t)t0 + kp.max_ticks > 0xFFFFFFF0ull ? 0xFFFFFFF0u : t0 + kp.max_ticks;
+    const uint32_t hist = max(max(stp->last_tx1, stp->last_act1), stp->max_arr);
+
+    Acc a;
+    a.hops = a.delivered = a.digest = 0;
+    a.tmax = a.last_tx1 = a.last_act1 = a.max_arr = 0;
+    a.left = 0;
+    a.fault = 0;
+    for (uint32_t p = tid; p < C.n_ports; p += nth) {
+        const PortRO &pr = C.port[p];
+        if (pr.is_host) a.left += C.hs[pr.host].left;
+    }
+
+    uint32_t t = t0, par = 0, slot = t0 % C.W;
+    bool done = false, dead = false;
+    uint32_t t_dead = 0;
+    while (t < t_end) {
+        for (uint32_t p = tid; p < C.n_ports; p += nth) {
+            const PortRO pr = C.port[p];
+            if (pr.is_host) phase_a_host(C, a, p, pr, t, slot);
+            else phase_a_switch(C, a, p, pr, slot);
+        }
+        __syncthreads();
+        for (uint32_t p = tid; p < C.n_ports; p += nth) {
+            const PortRO pr = C.port[p];
+            if (pr.is_host) phase_d_host(C, a, p, pr, t);
+            else phase_d_switch(C, a, p, pr, t);
+        }
+        t++;
+        slot = slot + 1 == C.W ? 0 : slot + 1;
+        if ((t - t0) % CHECK_EVERY == 0 || t == t_end) {
+            uint32_t any = __ballot(a.left > 0) != 0ull;
+            uint32_t ts = wave_max_u32(max(max(a.last_tx1, a.last_act1), a.max_arr));
+            if (lane == 0) { sh.chk_any[par][wave] = any; sh.chk_max[par][wave] = ts; }
+            __syncthreads();
+            any = 0;
+            ts = hist;
+            for (uint32_t w = 0; w < nwaves; w++) { any |= sh.chk_any[par][w]; ts = max(ts, sh.chk_max[par][w]); }
+            par ^= 1;
+            if (!any) { done = true; break; }
+            if (ts <= t - 1) { dead = true; t_dead = ts; break; }
+        } else {
+            __syncthreads();
+        }
+    }
+
+    /* totals of this segment */
+    uint64_t s0 = wave_sum_u64(a.hops), s1 = wave_sum_u64(a.delivered), s2 = wave_sum_u64(a.digest);
+    uint32_t m0 = wave_max_u32(a.tmax), m1 = wave_max_u32(a.last_tx1), m2 = wave_max_u32(a.last_act1),
+             m3 = wave_max_u32(a.max_arr), m4 = wave_max_u32(a.fault);
+    if (lane == 0) {
+        sh.sum[0][wave] = s0; sh.sum[1][wave] = s1; sh.sum[2][wave] = s2;
+        sh.mx[0][wave] = m0; sh.mx[1][wave] = m1; sh.mx[2][wave] = m2; sh.mx[3][wave] = m3; sh.mx[4][wave] = m4;
+    }
+    __syncthreads();
+    if (IN_LDS) {
+        const uint4 *src = (const uint4 *)(lds + rw_off);
+        uint4 *dst = (uint4 *)(arena_g + rw_off);
+        for (uint32_t i = tid; i < (arena_bytes - rw_off) / 16; i += nth) dst[i] = src[i];
+    }
+    if (tid == 0) {
+        uint64_t h = 0, d = 0, g = 0;
+        uint32_t tm = 0, lt = 0, la = 0, ma = 0, fa = 0;
+        for (uint32_t w = 0; w < nwaves; w++) {
+            h += sh.sum[0][w]; d += sh.sum[1][w]; g += sh.sum[2][w];
+            tm = max(tm, sh.mx[0][w]); lt = max(lt, sh.mx[1][w]); la = max(la, sh.mx[2][w]); ma = max(ma, sh.mx[3][w]);
+            fa = max(fa, sh.mx[4][w]);
+        }
+        ExpState st = *stp;
+        st.pkt_hops += h;
+        st.delivered += d;
+        st.digest += g;
+        st.t_max = max(st.t_max, tm);
+        st.last_tx1 = max(st.last_tx1, lt);
+        st.last_act1 = max(st.last_act1, la);
+        st.max_arr = max(st.max_arr, ma);
+        st.t_now = t;
+        st.fault |= fa;
+        if (st.fault) { st.status = 3; st.t_out = t; }
+        else if (done) { st.status = 0; st.t_out = st.t_max; }
+        else if (dead) { st.status = 2; st.t_out = t_dead; }
+        else { st.status = 1; st.t_out = t; }
+        *stp = st;
+    }
+    __syncthreads();
+}
+
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel(KParams kp)
+{
+    extern __shared__ __align__(16) uint8_t lds_dyn[];
+    __shared__ Shared sh;
+    WsHdr *wh = (WsHdr *)kp.ws;
+    const uint64_t *arena_off = (const uint64_t *)(kp.ws + kp.o_arena_off);
+    const uint32_t *order = (const uint32_t *)(kp.ws + kp.o_order);
+    const ExpState *states = (const ExpState *)(kp.ws + kp.o_state);
+    for (;;) {
+        if (threadIdx.x == 0) sh.exp = atomicAdd(&wh->claim, 1u);
+        __syncthreads();
+        const uint32_t e = sh.exp;
+        __syncthreads();
+        if (e >= kp.n_exp) break;
+        const uint32_t x = order[e];
+        if (states[x].status != 1) continue;
+        uint8_t *arena = kp.ws + arena_off[x];
+        const uint32_t bytes = ((const ArenaHdr *)arena)->bytes;
+        if (bytes <= kp.lds_bytes) run_experiment<true>(kp, x, arena, lds_dyn, sh);
+        else run_experiment<false>(kp, x, arena, lds_dyn, sh);
+    }
+}
+
+/* Prepares a launch: resets the experiment queue counter. */
+extern "C" __global__ void msim_prepare(KParams kp)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) ((WsHdr *)kp.ws)->claim = 0;
+}
+
+/* Restores every experiment to tick 0: copies the pristine mutable part back
+ * into each arena, resets progress and clears recorded per-flow ticks. */
+extern "C" __global__ void msim_reset_kernel(KParams kp, uint64_t o_rec_all, uint64_t rec_words)
+{
+    const uint64_t *arena_off = (const uint64_t *)(kp.ws + kp.o_arena_off);
+    const uint64_t *prist = (const uint64_t *)(kp.ws + kp.o_pristine);
+    ExpState *states = (ExpState *)(kp.ws + kp.o_state);
+    for (uint32_t x = blockIdx.x; x < kp.n_exp; x += gridDim.x) {
+        uint8_t *arena = kp.ws + arena_off[x];
+        const uint32_t bytes = ((const ArenaHdr *)arena)->bytes;
+        const uint32_t rw = ((const ArenaHdr *)arena)->rw_off;
+        const uint4 *src = (const uint4 *)(kp.ws + prist[x]);
+        uint4 *dst = (uint4 *)(arena + rw);
+        for (uint32_t i = threadIdx.x; i < (bytes - rw) / 16; i += blockDim.x) dst[i] = src[i];
+        if (threadIdx.x == 0) {
+            ExpState s = {};
+            s.status = ((const ArenaHdr *)arena)->n_flows == 0 ? 0u : 1u;
+            states[x] = s;
+        }
+    }
+    uint32_t *rec = (uint32_t *)(kp.ws + o_rec_all);
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rec_words;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        rec[i] = 0xFFFFFFFFu;
+}
+
+/* --------------------------------------------------------- host launchers */
+
+extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t grid, uint32_t block, uint32_t lds,
+                                      hipStream_t stream)
+{
+    hipLaunchKernelGGL(msim_prepare, dim3(1), dim3(64), 0, stream, *kp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(msim_megakernel, dim3(grid), dim3(block), lds, stream, *kp);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t msim_launch_reset(const KParams *kp, uint64_t o_rec_all, uint64_t rec_words,
+                                        hipStream_t stream)
+{
+    uint32_t grid = kp->n_exp < 4096 ? kp->n_exp : 4096;
+    hipLaunchKernelGGL(msim_reset_kernel, dim3(grid), dim3(256), 0, stream, *kp, o_rec_all, rec_words);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t msim_occupancy(uint32_t block, uint32_t lds, int *blocks_per_cu)
+{
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, msim_megakernel, (int)block, lds);
+}
+
+extern "C" hipError_t msim_set_lds_limit(uint32_t lds)
+{
+    return hipFuncSetAttribute((const void *)msim_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}

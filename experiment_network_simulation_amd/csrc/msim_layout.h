@@ -1,0 +1,145 @@
+/*
+ * msim_layout.h -- private layout of the experiment-major state store shared by
+ * the host compiler (msim_host.cpp) and the megakernel (msim_kernel.hip).
+ *
+ * Every experiment owns one contiguous "arena" in the workspace: a read-only
+ * part (ports, connections, collective groups, host tables) followed by a
+ * mutable part (virtual output queues, buffer pools, staging slots, connection
+ * cursors).  The same byte offsets are valid whether the arena is used in HBM
+ * or copied into a workgroup's LDS, so one kernel serves both placements.
+ *
+ * State owners (each datum has exactly one writer per phase, so the tick loop
+ * needs no atomics -- the pull discipline of Multiverse section 4.2):
+ *  - a switch ingress port q owns its buffer pool (pdesc/pnxt/fstk), the tail
+ *    side of its virtual output queues (arr, tslot, fcur, hseen) and popped[q];
+ *    it runs in phase A (arrivals, frees);
+ *  - a switch output port o owns the head side of the queues it drains (phead,
+ *    nslot, head), its round-robin pointer, pushed[o] and the staging slots of
+ *    the ingress it feeds; it runs in phase D (grant, pop, transmit);
+ *  - a host owns its NIC (phase D), its deliveries and activations (phase A),
+ *    the sender cursors of its outgoing connections and the receiver cursors of
+ *    its incoming ones.
+ */
+#ifndef MSIM_LAYOUT_H
+#define MSIM_LAYOUT_H
+
+#include <stdint.h>
+
+#define MSIM_NONE 0xFFFFFFFFu
+
+/* group kinds */
+#define GK_RING_AR 1
+#define GK_RING_AG 2
+#define GK_BCAST 3
+#define GK_XFLOW 4
+
+/* sender state of a connection (top two bits of ConnRW.s_pos) */
+#define CS_WAIT 0u   /* previous flow just finished sending (or start): check at next phase A */
+#define CS_IDLE 1u   /* waiting for its receive predecessor */
+#define CS_ACTIVE 2u /* sending */
+#define CS_DONE 3u   /* all flows sent */
+#define CS_SHIFT 30
+#define CS_POS_MASK 0x3FFFFFFFu
+
+/* descriptor of a packet: connection << 4 | index of the next switch on its path */
+#define DESC_SHIFT 4
+#define DESC_HOP_MASK 0xFu
+
+struct PortRO {          /* 24 bytes */
+    uint32_t peer;       /* port index at the far end of the cable */
+    uint32_t base;       /* first port index of this node */
+    uint32_t vbase;      /* first queue index of this node (switches) */
+    uint32_t host;       /* host index (host ports), else MSIM_NONE */
+    uint8_t local, deg, rate, delay;
+    uint8_t alive, is_host, peer_is_host, pad;
+};
+
+struct ConnRO {          /* 16 bytes */
+    uint32_t route;      /* egress local port at switch i of the path in bits 4i..4i+3 */
+    uint32_t grp;        /* collective group */
+    uint32_t idx;        /* ring rank / broadcast hop-1 / explicit flow: packets */
+    uint32_t lidx;       /* index among the source host's connections */
+};
+
+struct Grp {             /* 32 bytes */
+    uint32_t kind;
+    uint32_t N;          /* ring members; broadcast: hops A; explicit: flow count */
+    uint32_t S;          /* ring: steps per round; broadcast: partitions K */
+    uint32_t R;          /* ring: rounds */
+    uint32_t p;          /* ring: chunk packets; broadcast: message packets */
+    uint32_t X;          /* ring: packets in the last round */
+    uint32_t fid_base;   /* first flow id */
+    uint32_t conn_base;  /* first connection */
+};
+
+struct HostRO {          /* 16 bytes */
+    uint32_t port;
+    uint32_t out_off;    /* into the host out-connection list */
+    uint32_t n_out;
+    uint32_t rdy_off;    /* first 32-bit word of the host's ready mask */
+};
+
+struct PortRW {          /* 16 bytes */
+    uint32_t popped;     /* switch ingress: packets forwarded out of it (phase A) */
+    uint32_t pushed;     /* output: packets sent on it (phase D) */
+    uint32_t rr;         /* output: round-robin pointer */
+    uint32_t ftop;       /* switch ingress: free-slot stack height */
+};
+
+struct ConnRW {          /* 16 bytes */
+    uint32_t s_pos;      /* sender: flow position | state << 30 */
+    uint32_t s_rem;      /* sender: packets left in the active flow */
+    uint32_t r_pos;      /* receiver: flows fully received */
+    uint32_t r_rem;      /* receiver: packets left in flow r_pos */
+};
+
+struct HostRW {          /* 32 bytes */
+    uint32_t pcnt;       /* connections whose flow finished sending last tick */
+    uint32_t started;    /* first activation pass done */
+    uint32_t left;       /* flows still to be received by this host */
+    uint32_t pad;
+    uint32_t pend[4];    /* MSIM_MAX_RATE */
+};
+
+struct ArenaHdr {        /* 128 bytes, at the start of every arena */
+    uint32_t n_ports, n_hosts, n_conn, n_grp;
+    uint32_t Q, W, R, n_voq;
+    uint32_t rw_off;     /* start of the mutable part */
+    uint32_t bytes;      /* whole arena */
+    uint32_t n_flows;
+    uint32_t o_port, o_conn, o_grp, o_hout, o_host;
+    uint32_t o_arr, o_phead, o_nslot, o_head, o_tslot, o_fcur, o_hseen;
+    uint32_t o_pdesc, o_pnxt, o_fstk, o_pstate, o_scnt, o_sdesc, o_cstate, o_hstate, o_ready;
+};
+
+/* per-experiment progress and totals (workspace, outside the arena) */
+struct ExpState {        /* 64 bytes */
+    uint32_t status;     /* MSIM_EXP_* */
+    uint32_t t_now;      /* next tick to simulate */
+    uint32_t t_out;      /* reported tick */
+    uint32_t t_max;      /* largest RD so far */
+    uint64_t pkt_hops, delivered, digest;
+    uint32_t last_tx1;   /* 1 + last tick with a transmission (0: none) */
+    uint32_t last_act1;  /* 1 + last tick with an activation (0: none) */
+    uint32_t max_arr;    /* largest arrival tick of any packet sent */
+    uint32_t fault;      /* nonzero: an internal invariant broke (status MSIM_EXP_FAULT) */
+    uint32_t pad[2];
+};
+
+/* workspace header */
+struct WsHdr {
+    uint32_t claim;      /* experiment queue counter of the running launch */
+    uint32_t n_exp;
+    uint32_t pad[62];
+};
+
+struct KParams {
+    uint8_t *ws;
+    uint64_t o_state, o_arena_off, o_order, o_rec_off, o_pristine, o_rw_off;
+    uint32_t n_exp;
+    uint32_t max_ticks;
+    uint32_t lds_bytes;  /* dynamic LDS available to an arena (0: HBM only) */
+    uint32_t pad;
+};
+
+#endif

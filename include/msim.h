@@ -1,0 +1,225 @@
+/*
+ * msim.h -- C ABI of the batched packet-level network simulator for AMD MI355X
+ * (gfx950).
+ *
+ * One process simulates a whole batch of independent experiments on one GPU:
+ * the single-process multi-experiment strategy of Multiverse ("Accelerating
+ * Design Space Exploration for LLM Training Systems with Multi-experiment
+ * Parallel Simulation", section 2.2).  Each experiment is a switched topology,
+ * a collective-communication workload and a few parameters, as the user lists
+ * them in Multiverse's usage model (section 3.1 "Architecture").  The network
+ * part of that system -- point-to-point flows produced from NCCL's collective
+ * algorithms, a lockstep packet-level simulation with pull-based forwarding
+ * (section 4.2) and one kernel launch per batch (section 4.3) -- is what this
+ * library computes.  Collective shapes: ring all-reduce and ring all-gather cut
+ * into NC channels and chunks of size C (AutoCCL, "Automated Collective
+ * Communication Tuning", section 2.3), the K-partition pipelined broadcast
+ * (AlpaComm, "On Optimizing the Communication of Model Parallelism", section
+ * 3.1, Fig. 3d), and explicit flows for sparse all-to-all traffic.
+ *
+ * Conventions
+ *  - Plain C, fixed-width integers, no exceptions cross this boundary.
+ *  - Every entry point returns MSIM_OK (0), a positive run status, or a negative
+ *    error code; msim_last_error() gives a message for the last failure.
+ *  - Host arrays passed in are owned by the caller and only read during the
+ *    call.  Device memory (the workspace) is allocated by the caller and must
+ *    outlive the context; the library allocates no device memory itself.
+ *  - A context is used from one host thread at a time.
+ *
+ * Time is counted in integer ticks (one tick = the smallest link delay,
+ * Multiverse section 5); data in whole packets of exp_pkt_bytes bytes.
+ */
+#ifndef MSIM_H
+#define MSIM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSIM_ABI_VERSION 1u
+
+/* return codes */
+#define MSIM_OK 0
+#define MSIM_S_INCOMPLETE 1      /* msim_run: some experiment hit its tick budget */
+#define MSIM_S_DEADLOCK 2        /* msim_run: some experiment reached a static, unfinished state */
+#define MSIM_E_INVALID_SPEC (-1) /* the batch violates a rule listed below */
+#define MSIM_E_UNROUTABLE (-2)   /* a connection has no up/down path over alive cables */
+#define MSIM_E_WORKSPACE (-3)    /* workspace missing, too small or misaligned */
+#define MSIM_E_HIP (-4)          /* a HIP runtime call failed */
+#define MSIM_E_ARG (-5)          /* bad argument (null pointer, index out of range) */
+#define MSIM_E_STATE (-6)        /* call out of order (e.g. run before bind) */
+#define MSIM_E_LIMIT (-7)        /* an input exceeds a compiled-in limit */
+
+/* per-experiment status (msim_results) */
+#define MSIM_EXP_DONE 0          /* every flow received; tick = completion tick */
+#define MSIM_EXP_INCOMPLETE 1    /* tick budget spent; tick = ticks simulated so far */
+#define MSIM_EXP_DEADLOCK 2      /* tick = first tick of the static state */
+#define MSIM_EXP_FAULT 3         /* internal invariant broken (a library bug); results void */
+
+/* collective kinds (coll_type) */
+#define MSIM_COLL_RING_ALLREDUCE 1
+#define MSIM_COLL_RING_ALLGATHER 2
+#define MSIM_COLL_PIPE_BROADCAST 3
+
+/* compiled-in limits */
+#define MSIM_MAX_RATE 4          /* packets per tick per link direction */
+#define MSIM_MAX_DELAY 15        /* ticks per cable */
+#define MSIM_MAX_SWITCH_PORTS 16
+#define MSIM_MAX_SWITCH_HOPS 8   /* switches on one path */
+#define MSIM_MAX_QUEUE 255       /* packets per switch ingress buffer */
+
+/*
+ * A batch of experiments.  Topologies and workloads are listed once and shared
+ * by reference; CSR offset arrays have one entry more than the items they
+ * index.  All arrays are host memory.
+ *
+ * Topology t: nodes topo_node_off[t] .. topo_node_off[t+1]-1 with node_layer
+ *   0 = host, 1..3 = switch layers; cables topo_cable_off[t] ..
+ *   topo_cable_off[t+1]-1 joining nodes cable_a / cable_b (indices local to the
+ *   topology), with packets/tick cable_rate_ab (a to b) and cable_rate_ba,
+ *   delay in ticks (both directions) and an alive flag (0 = failed cable).  A
+ *   node's ports are numbered in the order its cables are listed.  Rules: every
+ *   host has exactly one cable; a cable joins nodes of different layers; rates
+ *   1..MSIM_MAX_RATE; delays 1..MSIM_MAX_DELAY; a switch has at most
+ *   MSIM_MAX_SWITCH_PORTS ports.
+ * Workload w: collectives work_coll_off[w] .. work_coll_off[w+1]-1, each with
+ *   coll_type, coll_bytes (all-gather: total output size), coll_nc channels,
+ *   coll_chunk_bytes (rings; a whole number of packets), coll_k partitions
+ *   (broadcast; 1 <= K <= packets) and members coll_member_off[c] ..
+ *   coll_member_off[c+1]-1 in member_host (ring order, or broadcast chain with
+ *   the source first; distinct hosts, at least 2); then explicit flows
+ *   work_xflow_off[w] .. work_xflow_off[w+1]-1 (source host, destination host,
+ *   packets >= 1).  Every ring channel must carry at least as many packets as
+ *   the ring has members.
+ * Experiment e: topology exp_topo[e], workload exp_work[e], switch ingress
+ *   buffer exp_queue_pkts[e] packets (1..MSIM_MAX_QUEUE), ECMP seed
+ *   exp_ecmp_seed[e], packet size exp_pkt_bytes[e] bytes.
+ */
+typedef struct msim_batch_spec {
+    uint32_t version;            /* MSIM_ABI_VERSION */
+    uint32_t n_topo, n_work, n_exp;
+    const uint32_t *topo_node_off;
+    const uint8_t *node_layer;
+    const uint32_t *topo_cable_off;
+    const uint32_t *cable_a, *cable_b;
+    const uint8_t *cable_rate_ab, *cable_rate_ba, *cable_delay, *cable_alive;
+    const uint32_t *work_coll_off;
+    const uint8_t *coll_type;
+    const uint64_t *coll_bytes;
+    const uint32_t *coll_nc, *coll_chunk_bytes, *coll_k;
+    const uint32_t *coll_member_off, *member_host;
+    const uint64_t *work_xflow_off;
+    const uint32_t *xflow_src, *xflow_dst, *xflow_pkts;
+    const uint32_t *exp_topo, *exp_work, *exp_queue_pkts, *exp_ecmp_seed, *exp_pkt_bytes;
+} msim_batch_spec;
+
+/* Options for msim_create.  Zero-initialise and set what you need. */
+typedef struct msim_options {
+    uint32_t version;            /* MSIM_ABI_VERSION */
+    uint32_t n_record;           /* experiments whose per-flow ticks are kept */
+    const uint32_t *record_exp;  /* their indices (host array of n_record) */
+    uint32_t host_threads;       /* threads for the host-side compile; 0 = all cores */
+    uint32_t force_global;       /* 1: keep experiment state in HBM even where it fits in LDS */
+    uint32_t block_threads;      /* 0 = automatic; else 64..1024, multiple of 64 */
+    uint32_t reserved[8];
+} msim_options;
+
+typedef struct msim_ctx msim_ctx; /* opaque; owned by the library */
+
+/*
+ * Validates the batch and compiles it on the host: ports and cables, up/down
+ * shortest-path ECMP routes (Multiverse section 5: ECMP load balancing), the
+ * collectives' point-to-point connections and flow schedules (Multiverse
+ * section 3.1: the system simulator turns NCCL's collective algorithms into
+ * point-to-point flows), and the experiment-major state layout.  No device
+ * memory is touched.  On error *out is NULL and the return code says why
+ * (MSIM_E_INVALID_SPEC, MSIM_E_UNROUTABLE, MSIM_E_LIMIT); the message is
+ * available from msim_last_error(NULL) on the same thread.
+ */
+int msim_create(const msim_batch_spec *spec, const msim_options *opts, msim_ctx **out);
+
+/* Bytes of device workspace msim_bind needs (256-byte aligned start). */
+int msim_workspace_size(const msim_ctx *ctx, uint64_t *bytes);
+
+/*
+ * Binds a caller-owned device buffer of at least msim_workspace_size bytes and
+ * uploads the compiled batch into it on the given stream (a hipStream_t; NULL =
+ * the default stream), then waits for the upload.  Binding again re-uploads.
+ */
+int msim_bind(msim_ctx *ctx, void *dev_workspace, uint64_t ws_bytes, void *hip_stream);
+
+/*
+ * Launches the simulation of every unfinished experiment for at most max_ticks
+ * more ticks each, as one kernel launch on hip_stream (asynchronous; one launch
+ * per batch, Multiverse section 4.3).  Experiments are independent; their state
+ * stays in the workspace between calls, so several calls continue where the
+ * previous one stopped.  Returns MSIM_OK once enqueued; per-experiment outcome
+ * comes from msim_results.  flags: reserved, pass 0.
+ */
+int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *hip_stream, uint32_t flags);
+
+/* Restores every experiment to tick 0 (asynchronous, on hip_stream). */
+int msim_reset(msim_ctx *ctx, void *hip_stream);
+
+/*
+ * Waits for hip_stream, then copies per-experiment results to host arrays
+ * (any pointer may be NULL to skip it), each of n_exp entries:
+ *   exp_status    MSIM_EXP_*;
+ *   exp_tick      completion tick (DONE), first static tick (DEADLOCK) or ticks
+ *                 simulated so far (INCOMPLETE);
+ *   exp_pkt_hops  packet transmissions on every link, host NICs included;
+ *   exp_delivered packets received by hosts;
+ *   exp_digest    sum over flows f of mix64((f << 32) | RD_f) mod 2^64, mix64
+ *                 being SplitMix64's output function and RD_f the tick the last
+ *                 packet of flow f arrived (flows not yet received add nothing).
+ * Returns MSIM_S_DEADLOCK if any experiment deadlocked, else MSIM_S_INCOMPLETE
+ * if any is unfinished, else MSIM_OK.
+ */
+int msim_results(msim_ctx *ctx, void *hip_stream, uint8_t *exp_status, uint32_t *exp_tick,
+                 uint64_t *exp_pkt_hops, uint64_t *exp_delivered, uint64_t *exp_digest);
+
+/* Number of flows of experiment exp (flows are numbered per experiment: the
+ * collectives in input order -- a ring by channel, round, step, rank; a
+ * broadcast by hop, partition -- then the explicit flows). */
+int msim_flow_count(const msim_ctx *ctx, uint32_t exp, uint64_t *n_flows);
+
+/*
+ * Per-flow ticks of a recorded experiment (listed in msim_options.record_exp):
+ * arrival of the last packet (rd), activation (act) and last send + 1 (sd),
+ * 0xFFFFFFFF where the event has not happened.  Arrays of n_flows entries, or
+ * NULL.  Waits for hip_stream first.  MSIM_E_ARG if exp was not recorded.
+ */
+int msim_flow_ticks(msim_ctx *ctx, uint32_t exp, void *hip_stream, uint32_t *rd, uint32_t *act,
+                    uint32_t *sd);
+
+/* Static description of the compiled batch, for callers and tests. */
+typedef struct msim_info {
+    uint32_t n_exp;
+    uint32_t block_threads;      /* threads per workgroup (one workgroup simulates one experiment at a time) */
+    uint32_t grid_blocks;        /* persistent workgroups launched by msim_run (0 before bind) */
+    uint32_t lds_bytes;          /* dynamic LDS per workgroup (0: experiment state stays in HBM) */
+    uint32_t n_lds_exp;          /* experiments whose state fits in that LDS */
+    uint32_t max_ports;          /* largest experiment: ports */
+    uint64_t max_arena_bytes;    /* largest experiment: state bytes */
+    uint64_t total_flows;        /* over the batch */
+    uint64_t total_conns;
+    uint64_t est_pkt_hops;       /* over the batch: sum of flow size x path links */
+    uint64_t est_delivered;      /* over the batch: sum of flow sizes */
+    uint64_t workspace_bytes;
+} msim_info;
+
+int msim_get_info(const msim_ctx *ctx, msim_info *info);
+
+/* Message of the last error on this context (or, for ctx == NULL, of the last
+ * failed msim_create on the calling thread). */
+const char *msim_last_error(const msim_ctx *ctx);
+
+/* Frees host-side state; the workspace stays the caller's. */
+void msim_destroy(msim_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSIM_H */

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every entry point include/msim.h declares,
+and its host-side compile (validation, routing, flow expansion) behaves, all
+without a GPU."""
+
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from experiment_network_simulation_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msim.h")
+
+
+@pytest.fixture(scope="module")
+def simmod():
+    from experiment_network_simulation_amd import sim
+    sim.load_library()
+    return sim
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char \*)\s*(msim_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(simmod):
+    names = declared_functions()
+    assert len(names) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", simmod.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in names:
+        assert n in exported, n
+    assert sorted(names) == sorted(simmod.EXPORTED)
+
+
+def test_create_reports_sizes(simmod):
+    s = simmod.Sim(I.make_config(1))
+    inf = s.info()
+    assert inf["n_exp"] == 16 and inf["block_threads"] == 64 and inf["max_ports"] == 16
+    assert inf["est_pkt_hops"] == 16 * 7168 and inf["est_delivered"] == 16 * 3584
+    assert s.workspace_bytes > 0
+    assert [s.flow_count(e) for e in range(4)] == [896, 448, 224, 112]
+
+
+def test_flow_counts_match_oracle(simmod, oracle):
+    for cid, n in [(2, 6), (3, 28)]:
+        b = I.make_config(cid, n_exp=n)
+        s = simmod.Sim(b)
+        for e in range(n):
+            rc, nf, nc = oracle.count(b, e)
+            assert rc == 0 and s.flow_count(e) == nf
+
+
+def test_packet_hop_estimate_matches_oracle_paths(simmod, oracle):
+    """The host compile's sum of flow size x path links equals the oracle's."""
+    b = I.make_config(4, exp_ids=[0, 1, 2])
+    s = simmod.Sim(b)
+    tot = 0
+    for e in range(3):
+        rc, fl = oracle.flows(b, e)
+        rc2, pth = oracle.paths(b, e)
+        tot += int((fl["size"].astype(np.int64) * pth["links"][fl["conn"]]).sum())
+    assert s.info()["est_pkt_hops"] == tot
+
+
+def expect_error(simmod, batch, code):
+    with pytest.raises(simmod.MsimError) as ei:
+        simmod.Sim(batch)
+    assert ei.value.code == code
+
+
+def test_validation_errors(simmod):
+    topo = I.single_switch(3)
+    # dead host cable -> unroutable
+    t2 = topo.copy(); t2.alive[1] = 0
+    expect_error(simmod, I.single_batch(t2, I.xflows([(0, 1, 2)])), simmod.E_UNROUTABLE)
+    # too few packets per channel
+    w = I.Workload([I.ring(I.COLL_RING_AR, 2 * I.PKT_BYTES, range(3), 1, I.PKT_BYTES)])
+    expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
+    # chunk not a whole number of packets
+    w = I.Workload([I.ring(I.COLL_RING_AR, 64 * I.PKT_BYTES, range(3), 1, 100)])
+    expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
+    # queue out of range
+    expect_error(simmod, I.single_batch(topo, I.xflows([(0, 1, 2)]), queue_pkts=0), simmod.E_INVALID_SPEC)
+    expect_error(simmod, I.single_batch(topo, I.xflows([(0, 1, 2)]), queue_pkts=256), simmod.E_INVALID_SPEC)
+    # same-layer cable
+    bad = I.topology_from_cables([0, 1, 1], [(0, 1), (1, 2)])
+    expect_error(simmod, I.single_batch(bad, I.Workload()), simmod.E_INVALID_SPEC)
+    # host with two cables
+    bad = I.topology_from_cables([0, 1, 2], [(0, 1), (0, 2), (1, 2)])
+    expect_error(simmod, I.single_batch(bad, I.Workload()), simmod.E_INVALID_SPEC)
+    # rate and delay limits
+    bad = I.topology_from_cables([0, 0, 1], [(0, 2, 5, 1, 1, 1), (1, 2)])
+    expect_error(simmod, I.single_batch(bad, I.Workload()), simmod.E_INVALID_SPEC)
+    bad = I.topology_from_cables([0, 0, 1], [(0, 2, 1, 1, 16, 1), (1, 2)])
+    expect_error(simmod, I.single_batch(bad, I.Workload()), simmod.E_INVALID_SPEC)
+    # repeated ring member, broadcast K > packets, explicit flow to itself
+    w = I.Workload([I.ring(I.COLL_RING_AR, 64 * I.PKT_BYTES, [0, 1, 1], 1, I.PKT_BYTES)])
+    expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
+    w = I.Workload([I.bcast(4 * I.PKT_BYTES, [0, 1], 5)])
+    expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
+    expect_error(simmod, I.single_batch(topo, I.xflows([(1, 1, 2)])), simmod.E_INVALID_SPEC)
+    # switch with more than 16 ports
+    big = I.single_switch(17)
+    expect_error(simmod, I.single_batch(big, I.Workload()), simmod.E_LIMIT)
+
+
+def test_bind_without_workspace_is_rejected(simmod):
+    s = simmod.Sim(I.make_config(1, n_exp=1))
+    lib = simmod.load_library()
+    import ctypes as C
+    rc = lib.msim_bind(s._ctx, None, 0, None)
+    assert rc == simmod.E_WORKSPACE
+    assert lib.msim_run(s._ctx, 10, None, 0) == simmod.E_STATE
+    assert b"before msim_bind" in lib.msim_last_error(s._ctx)
+
+
+def test_workspace_covers_flow_records(simmod):
+    """Recording per-flow ticks (rd, act, sd: 3 x 4 bytes per flow) grows the
+    workspace by at least that much (regression: the record area once fell
+    outside the reported size)."""
+    b = I.make_config(2, n_exp=8)
+    plain = simmod.Sim(b).workspace_bytes
+    rec = [0, 3, 7]
+    s = simmod.Sim(b, record=rec)
+    assert s.workspace_bytes >= plain + 12 * sum(s.flow_count(e) for e in rec)

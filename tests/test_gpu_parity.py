@@ -1,0 +1,253 @@
+"""Parity of the HIP megakernel (through the C ABI) with the CPU oracle.
+
+All state is integer, so the bar is bit-exact equality: per experiment the
+status, completion tick, packet-hops, delivered packets and flow digest; per
+flow (recorded experiments) the arrival, activation and send-completion ticks.
+"""
+
+import os
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+from experiment_network_simulation_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def simmod():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from experiment_network_simulation_amd import sim
+    sim.load_library()
+    return sim
+
+
+def oracle_all(oracle, batch, ids=None, flows=False):
+    ob = oracle.OracleBatch(batch.pack())
+    ids = list(range(batch.n_exp)) if ids is None else list(ids)
+    with ThreadPoolExecutor(THREADS) as ex:
+        return dict(zip(ids, ex.map(lambda e: oracle.run(ob, e, flows=flows), ids)))
+
+
+def gpu_run(simmod, batch, record=(), force_global=False, max_ticks=0xFFFFFFF0, block_threads=0):
+    s = simmod.Sim(batch, record=record, force_global=force_global, block_threads=block_threads)
+    s.bind()
+    s.run(max_ticks)
+    return s, s.results()
+
+
+def assert_exp(g, e, o, ge=None):
+    ge = e if ge is None else ge
+    assert o["rc"] == 0
+    got = (int(g["status"][ge]), int(g["tick"][ge]), int(g["pkt_hops"][ge]), int(g["delivered"][ge]),
+           int(g["digest"][ge]))
+    want = (o["status"], o["t_end"], o["pkt_hops"], o["delivered"], o["digest"])
+    assert got == want, f"experiment {e}: gpu {got} oracle {want}"
+
+
+def assert_flows(s, ge, o):
+    ft = s.flow_ticks(ge)
+    for k in ("rd", "act", "sd"):
+        bad = np.nonzero(ft[k] != o[k])[0]
+        assert bad.size == 0, f"{k} differs at flows {bad[:8]} gpu {ft[k][bad[:8]]} oracle {o[k][bad[:8]]}"
+
+
+# ------------------------------------------------------------ hand traces
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_hand_traces(simmod, oracle, force_global):
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_traces.json")))
+    batch = I.Batch([], [], [], "hand")
+    for name in ("M1_incast", "M2_credit", "M3_two_egress", "M4_round_order"):
+        c = g[name]
+        batch.topos.append(I.topology_from_cables(c["layers"], [tuple(x) for x in c["cables"]]))
+        batch.works.append(I.xflows([tuple(f) for f in c["flows"]]))
+        batch.exps.append(I.Experiment(len(batch.topos) - 1, len(batch.works) - 1, c["queue"], 0))
+    s, r = gpu_run(simmod, batch, record=range(4), force_global=force_global)
+    for e, name in enumerate(("M1_incast", "M2_credit", "M3_two_egress", "M4_round_order")):
+        c = g[name]
+        assert int(r["status"][e]) == 0 and int(r["tick"][e]) == c["t_end"]
+        assert int(r["pkt_hops"][e]) == c["pkt_hops"]
+        assert list(s.flow_ticks(e)["rd"]) == c["rd"]
+
+
+# ------------------------------------------------------------ configs
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_c1_full(simmod, oracle, force_global):
+    b = I.make_config(1)
+    log("C1 full, force_global", force_global)
+    s, r = gpu_run(simmod, b, record=range(16), force_global=force_global)
+    o = oracle_all(oracle, b, flows=True)
+    for e in range(16):
+        assert_exp(r, e, o[e])
+        assert_flows(s, e, o[e])
+
+
+def test_c2_full(simmod, oracle):
+    """All 256 experiments of the C2 batch in the default launch shape; per-flow
+    ticks on a sample of experiments."""
+    b = I.make_config(2)
+    rec = [0, 7, 100, 255]
+    log("C2 full batch")
+    s, r = gpu_run(simmod, b, record=rec)
+    o = oracle_all(oracle, b)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+    of = oracle_all(oracle, b, ids=rec, flows=True)
+    for e in rec:
+        assert_flows(s, e, of[e])
+
+
+def test_c2_hbm_placement(simmod, oracle):
+    b = I.make_config(2, n_exp=24)
+    log("C2 first 24, HBM placement")
+    s, r = gpu_run(simmod, b, record=[3], force_global=True)
+    o = oracle_all(oracle, b)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+    assert_flows(s, 3, oracle.run(b, 3, flows=True))
+
+
+def test_c3_full(simmod, oracle):
+    b = I.make_config(3)
+    rec = [0, 6, 27, 500, 1023]
+    log("C3 full batch")
+    s, r = gpu_run(simmod, b, record=rec)
+    o = oracle_all(oracle, b)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+    of = oracle_all(oracle, b, ids=rec, flows=True)
+    for e in rec:
+        assert_flows(s, e, of[e])
+
+
+def test_c4_sample(simmod, oracle):
+    """Two full-size k=8 fat-tree experiments (each ~93M packet-hops)."""
+    ids = [2, 3]
+    b = I.make_config(4, exp_ids=ids)
+    log("C4 sample", ids)
+    s, r = gpu_run(simmod, b, record=[0])
+    o = oracle_all(oracle, b, flows=False)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+    assert_flows(s, 0, oracle.run(b, 0, flows=True))
+
+
+# ------------------------------------------------------------ semantics
+
+def test_resume_equals_single_run(simmod, oracle):
+    b = I.make_config(2, n_exp=8)
+    s = simmod.Sim(b, record=[1])
+    s.bind()
+    rng = np.random.default_rng(0)
+    steps = 0
+    while True:
+        s.run(int(rng.integers(1, 4000)))
+        r = s.results()
+        steps += 1
+        if (r["status"] != 1).all():
+            break
+        # experiments still running report the ticks simulated so far
+        assert steps < 200
+    o = oracle_all(oracle, b)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+    assert_flows(s, 1, oracle.run(b, 1, flows=True))
+
+
+def test_incomplete_matches_oracle(simmod, oracle):
+    b = I.make_config(1, n_exp=4)
+    s, r = gpu_run(simmod, b, max_ticks=100)
+    for e in range(4):
+        o = oracle.run(b, e, max_ticks=100)
+        assert int(r["status"][e]) == 1 and int(r["tick"][e]) == 100 == o["t_end"]
+        assert int(r["pkt_hops"][e]) == o["pkt_hops"] and int(r["digest"][e]) == o["digest"]
+
+
+def test_reset_and_rerun_is_deterministic(simmod):
+    b = I.make_config(3, n_exp=28)
+    s, r1 = gpu_run(simmod, b)
+    s.reset()
+    s.run()
+    r2 = s.results()
+    for k in ("status", "tick", "pkt_hops", "delivered", "digest"):
+        assert np.array_equal(r1[k], r2[k])
+
+
+def test_batch_composition_does_not_matter(simmod):
+    """An experiment's result does not depend on what else is in the batch."""
+    ids = [5, 9, 33, 120]
+    solo = [gpu_run(simmod, I.make_config(2, exp_ids=[i]))[1] for i in ids]
+    mixed = I.make_config(2, exp_ids=[120, 5, 33, 5, 9, 77])
+    s, r = gpu_run(simmod, mixed)
+    where = {120: 0, 5: 1, 33: 2, 9: 4}
+    for i, so in zip(ids, solo):
+        for k in ("status", "tick", "pkt_hops", "digest"):
+            assert r[k][where[i]] == so[k][0]
+    for k in ("tick", "digest"):
+        assert r[k][1] == r[k][3]
+
+
+def edge_batch():
+    """Degenerate and extreme inputs mixed in one batch."""
+    b = I.Batch([], [], [], "edges")
+
+    def add(topo, work, q=16, seed=0):
+        b.topos.append(topo)
+        b.works.append(work)
+        b.exps.append(I.Experiment(len(b.topos) - 1, len(b.works) - 1, q, seed))
+
+    sw4 = I.single_switch(4)
+    add(sw4, I.Workload())                                            # no traffic at all
+    add(sw4, I.xflows([(0, 1, 1)]))                                   # one packet
+    add(sw4, I.xflows([(0, 1, 5), (2, 1, 5), (3, 1, 5)]), q=1)        # incast with Q = 1
+    fast = I.topology_from_cables([0, 0, 0, 1, 2], [(0, 3, 4, 4, 1, 1), (1, 3, 4, 4, 15, 1),
+                                                    (3, 4, 4, 4, 7, 1), (2, 4, 3, 2, 2, 1)])
+    add(fast, I.xflows([(0, 1, 40), (0, 2, 33), (1, 2, 17), (2, 0, 9)]), q=255)   # rate 4, delay 15
+    add(fast, I.xflows([(0, 2, 50), (1, 2, 50)]), q=3)
+    ls = I.leaf_spine(2, 4, 3, 1, 2, 3)
+    add(ls, I.Workload([I.bcast(37 * I.PKT_BYTES, [7, 0, 4, 1, 5], 37)]), q=32)     # K = packets
+    add(ls, I.Workload([I.ring(I.COLL_RING_AG, 203 * I.PKT_BYTES, [3, 6, 1], 3, 2 * I.PKT_BYTES),
+                        I.ring(I.COLL_RING_AR, 77 * I.PKT_BYTES, [0, 5], 2, 5 * I.PKT_BYTES),
+                        I.bcast(19 * I.PKT_BYTES, [2, 7, 4], 4)]), q=5, seed=12345)
+    pairs = [(s, d, 1 + (3 * s + d) % 7) for s in range(8) for d in range(8) if s != d]
+    add(ls, I.xflows(pairs), q=2, seed=99)                            # all-to-all, tiny buffers
+    ft = I.fat_tree(4)
+    ft.delay = np.asarray([1 + (c % 3) for c in range(ft.n_cables)], np.uint8)
+    add(ft, I.Workload([I.ring(I.COLL_RING_AR, 64 * I.PKT_BYTES, [0, 5, 10, 15, 3, 8], 2, I.PKT_BYTES)]), q=4, seed=7)
+    return b
+
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_edge_cases(simmod, oracle, force_global):
+    b = edge_batch()
+    s, r = gpu_run(simmod, b, record=range(b.n_exp), force_global=force_global)
+    o = oracle_all(oracle, b, flows=True)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+        if o[e]["n_flows"]:
+            assert_flows(s, e, o[e])
+    assert int(r["tick"][0]) == 0 and int(r["status"][0]) == 0
+
+
+@pytest.mark.parametrize("threads", [64, 256])
+def test_block_size_does_not_matter(simmod, oracle, threads):
+    """Fewer threads than ports (strided port loops) give the same results."""
+    b = I.make_config(2, n_exp=6)
+    s, r = gpu_run(simmod, b, block_threads=threads)
+    o = oracle_all(oracle, b)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
