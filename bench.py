@@ -1,0 +1,188 @@
+"""Benchmark: packet-hops/s of the batched simulator on one MI355X.
+
+A step is one pass of the whole hot path over one batch: every experiment of the
+batch simulated from tick 0 to completion by one msim_run launch (the state is
+restored to tick 0 with msim_reset before each step).  The default workload is
+the k=8 fat-tree batch of 4096 experiments (16 data-parallel ring all-reduces of
+256 MiB plus 16 tensor-parallel ring all-gathers of 56 MiB per experiment, 4 KiB
+packets, 0-4 failed cables).  Inputs are synthetic and seeded, and resident in
+HBM before the timed region starts.
+
+Prints one JSON line (rank 0): throughput, the roofline of the megakernel
+(algorithmic bytes: 8 B per packet-hop + 8 B per delivered packet, over the
+kernel's average launch time measured with HIP events on its stream) and the
+CPU oracle timed on a bounded sample of the same batch on the host's cores,
+with its results compared to the GPU's for those experiments.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+ALG_BYTES_PER_HOP = 8
+ALG_BYTES_PER_DELIVERY = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(batch, gpu_res, sample_ids, threads):
+    """The oracle, untouched, on a sample of experiments, in parallel threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import oracle as O
+    ob = O.OracleBatch(batch.pack())
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(lambda e: O.run(ob, e), sample_ids))
+    dt = time.perf_counter() - t0
+    hops = sum(r["pkt_hops"] for r in res)
+    ok = 0
+    for e, r in zip(sample_ids, res):
+        same = (r["rc"] == 0 and r["status"] == int(gpu_res["status"][e]) and r["t_end"] == int(gpu_res["tick"][e])
+                and r["pkt_hops"] == int(gpu_res["pkt_hops"][e]) and r["digest"] == int(gpu_res["digest"][e])
+                and r["delivered"] == int(gpu_res["delivered"][e]))
+        ok += same
+    return hops / dt, dt, hops, ok
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=4, help="workload 1..5 (default 4: k=8 fat-tree, E=4096)")
+    ap.add_argument("--n-exp", type=int, default=0, help="first n experiments only (default: the full batch)")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="experiments in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--force-global", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); experiments are "
+              "independent, so N GPUs would each run their own share of the batch.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from experiment_network_simulation_amd import inputs as I
+    from experiment_network_simulation_amd.sim import Sim
+
+    cid = args.config
+    n = args.n_exp or I.FULL_E[cid]
+    log(f"[bench] generating config C{cid} with {n} experiments")
+    t = time.perf_counter()
+    batch = I.make_config(cid, n_exp=n)
+    log(f"[bench] generated in {time.perf_counter() - t:.1f}s; compiling")
+    t = time.perf_counter()
+    sim = Sim(batch, force_global=args.force_global)
+    info = sim.info()
+    log(f"[bench] compiled in {time.perf_counter() - t:.1f}s: {info}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sim.bind(device="cuda:0", stream=stream)
+    info = sim.info()
+    log(f"[bench] bound: grid {info['grid_blocks']} x {info['block_threads']} threads, lds {info['lds_bytes']} B "
+        f"({info['n_lds_exp']} experiments in LDS), workspace {info['workspace_bytes'] / 2**20:.0f} MiB")
+
+    kernel_ms = []
+
+    def step(timed):
+        sim.reset(stream)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        sim.run(stream=stream)
+        ev1.record(stream)
+        if timed:
+            kernel_ms.append((ev0, ev1))
+
+    for i in range(args.warmup):
+        t = time.perf_counter()
+        step(False)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i} {time.perf_counter() - t:.2f}s")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        log(f"[bench] step {i} done at {time.perf_counter() - t0:.2f}s")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = sim.results(stream)
+    if res["rc"] != 0:
+        raise SystemExit(f"bench: simulation did not complete (rc={res['rc']})")
+    hops = int(res["pkt_hops"].sum())
+    delivered = int(res["delivered"].sum())
+    exp_ticks = int((res["tick"].astype(np.int64) + 1).sum())
+    k_ms = [a.elapsed_time(b) for a, b in kernel_ms]
+    k_avg_s = sum(k_ms) / len(k_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = hops * args.steps / wall
+    alg_bytes = ALG_BYTES_PER_HOP * hops + ALG_BYTES_PER_DELIVERY * delivered
+    achieved = alg_bytes / k_avg_s / 1e9
+    log(f"[bench] kernel {k_ms} ms; packet-hops {hops}, delivered {delivered}, experiment-ticks {exp_ticks}")
+
+    cpu = None
+    if args.cpu_sample and n > 0:
+        k = min(args.cpu_sample, n)
+        sample = sorted(set(int(round(i * n / k)) for i in range(k)) - {n})
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1, len(sample))
+        log(f"[bench] CPU oracle on {len(sample)} experiments with {threads} threads")
+        rate, dt, chops, ok = cpu_baseline(batch, res, sample, threads)
+        cpu = {"value": rate, "unit": "packet-hops/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(sample)} of {n} experiments (evenly spaced indices), run to completion in "
+                         f"{dt:.1f}s ({chops} packet-hops); GPU results identical on {ok}/{len(sample)}",
+               "parity_ok": ok, "parity_n": len(sample)}
+        log(f"[bench] CPU oracle {rate:.3e} packet-hops/s; parity {ok}/{len(sample)}")
+
+    out = {
+        "metric": "packet-hops/sec (batched, 1 GPU) + % of HBM roofline at E=4096",
+        "value": value,
+        "unit": "packet-hops/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": I.CONFIG_NAMES[cid],
+            "experiments": n,
+            "pkt_bytes": I.PKT_BYTES,
+            "experiment_ticks_per_s": exp_ticks * args.steps / wall,
+            "packet_hops_per_step": hops,
+            "delivered_per_step": delivered,
+            "experiment_ticks_per_step": exp_ticks,
+            "grid": info["grid_blocks"],
+            "block_threads": info["block_threads"],
+            "lds_bytes": info["lds_bytes"],
+            "state_in_lds": info["n_lds_exp"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "msim_megakernel",
+            "kernel_ms_avg": k_avg_s * 1e3,
+            "alg_bytes_per_launch": alg_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
