@@ -27,20 +27,27 @@
 #include "msim.h"
 #include "msim_layout.h"
 
-extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t grid, uint32_t block, uint32_t lds,
-                                      hipStream_t stream);
+extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t kind, uint32_t grid, uint32_t block,
+                                      uint32_t lds, bool prepare, hipStream_t stream);
 extern "C" hipError_t msim_launch_reset(const KParams *kp, uint64_t o_rec_all, uint64_t rec_words,
                                         hipStream_t stream);
-extern "C" hipError_t msim_occupancy(uint32_t block, uint32_t lds, int *blocks_per_cu);
-extern "C" hipError_t msim_set_lds_limit(uint32_t lds);
+extern "C" hipError_t msim_occupancy(uint32_t kind, uint32_t block, uint32_t lds, int *blocks_per_cu);
+extern "C" hipError_t msim_set_lds_limit(uint32_t kind, uint32_t lds);
 
 namespace {
 
 thread_local std::string g_create_error;
 
+/* LDS a compact arena may use (gfx950: 160 KiB per workgroup, less the
+ * kernel's static reductions area) */
+constexpr uint32_t COMPACT_LDS_LIMIT = 160u * 1024u - 4096u;
+
 struct Compiled {
     std::vector<uint8_t> arena;  /* RO + initial RW image, size multiple of 16 */
-    uint32_t rw_off = 0, bytes = 0;
+    uint32_t rw_off = 0, bytes = 0, lds_bytes = 0;
+    bool compact = false;
+    uint32_t kind = 0;     /* kernel kind: 0 general; compact 1 + (16-byte rows ? 2 : 0) + (32-bit descriptors ? 1 : 0) */
+    uint32_t nt = 0;       /* compact: thread slots */
     uint64_t n_flows = 0, n_conns = 0, n_ports = 0;
     uint64_t est_hops = 0, est_delivered = 0;
     int err = 0;
@@ -96,7 +103,7 @@ uint32_t first_flow_size(const Grp &g, uint32_t idx)
     return g.X / g.N + (k < g.X % g.N ? 1u : 0u);
 }
 
-int compile_exp(const msim_batch_spec *s, uint32_t e, Compiled &out)
+int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compiled &out)
 {
     const uint32_t t = s->exp_topo[e], w = s->exp_work[e];
     if (t >= s->n_topo || w >= s->n_work) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: topology/workload index out of range", e);
@@ -341,9 +348,123 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, Compiled &out)
         out.est_delivered += cn.pkts;
     }
 
-    /* ---- layout */
     const uint32_t W = maxd + 1, R = maxr, nconn = (uint32_t)conn.size(), ngrp = (uint32_t)grp.size();
+    out.n_flows = n_flows;
+    out.n_conns = nconn;
+    out.n_ports = n_ports;
+
+    /* ---- compact layout, where the experiment qualifies */
+    if (allow_compact) {
+        uint32_t maxdeg = 1, max_out = 0, max_F = 0;
+        uint64_t max_size = 0;
+        for (uint32_t n = 0; n < nn; n++)
+            if (layer[n] != 0) maxdeg = std::max(maxdeg, deg[n]);
+        for (uint32_t h = 0; h < n_hosts; h++) max_out = std::max(max_out, host[h].n_out);
+        for (const Grp &g : grp) {
+            uint32_t F = g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
+            max_F = std::max(max_F, F);
+            if (g.kind == GK_BCAST) max_size = std::max<uint64_t>(max_size, g.p / g.S + 1);
+            else if (g.kind != GK_XFLOW) max_size = std::max<uint64_t>(max_size, std::max<uint64_t>(g.p, g.X / g.N + 1));
+        }
+        for (auto &cn : conn)
+            if (grp[cn.grp].kind == GK_XFLOW) max_size = std::max<uint64_t>(max_size, cn.idx);
+        const uint32_t S = n_ports - n_hosts;
+        const uint32_t SB = ((n_hosts + 63) / 64) * 64, nt = SB + S;
+        const uint32_t rsz = maxdeg <= 8 ? 8 : 16, dt = nconn <= 4096 ? 2 : 4;
+        if (nt <= 1024 && maxdeg <= 16 && Q <= 64 && max_out <= 64 && max_F <= C_POS_MASK && max_size < 65536 &&
+            nconn < (1u << (32 - DESC_SHIFT))) {
+            uint32_t n_sw = 0;
+            for (uint32_t n = 0; n < nn; n++) n_sw += layer[n] != 0;
+            const uint32_t Vc = n_sw * rsz * rsz;
+            ArenaHdr2 H{};
+            H.mode = MODE_COMPACT; H.n_flows = (uint32_t)n_flows;
+            H.nt = nt; H.H = n_hosts; H.SB = SB;
+            H.Q = Q; H.W = W; H.R = R; H.n_conn = nconn; H.n_grp = ngrp; H.rsz = rsz; H.dt = dt;
+            size_t off = align16(sizeof(ArenaHdr2));
+            auto take = [&](uint32_t &field, size_t bytes) { field = (uint32_t)off; off = align16(off + bytes); };
+            take(H.o_route, 4ull * nconn);
+            take(H.o_cgrp, 2ull * nconn);
+            take(H.o_lidx, 2ull * nconn);
+            take(H.o_grp, sizeof(Grp) * ngrp);
+            take(H.o_hout, 4ull * nconn);
+            H.rw_off = (uint32_t)off;
+            take(H.o_arr, Vc);
+            take(H.o_head, Vc);
+            take(H.o_nslot, Vc);
+            take(H.o_pdesc, (size_t)dt * S * Q);
+            take(H.o_pnxt, (size_t)S * Q);
+            take(H.o_popped, 4ull * nt);
+            take(H.o_scnt, (size_t)nt * W);
+            take(H.o_sdesc, (size_t)dt * nt * W * R);
+            take(H.o_crw, sizeof(CRW2) * nconn);
+            H.lds_bytes = (uint32_t)off;
+            take(H.o_port, sizeof(PortRO2) * nt);
+            take(H.o_priv, sizeof(PortPriv) * nt);
+            H.bytes = (uint32_t)off;
+            if (H.lds_bytes <= COMPACT_LDS_LIMIT) {
+                out.arena.assign(off, 0);
+                uint8_t *A = out.arena.data();
+                /* thread slot of every port: hosts first, switches from SB */
+                std::vector<uint32_t> slot(n_ports), sw_of(nn, MSIM_NONE);
+                uint32_t sp = SB, nsw = 0;
+                for (uint32_t n = 0; n < nn; n++) {
+                    if (layer[n] == 0) { slot[pbase[n]] = host_of[n]; continue; }
+                    sw_of[n] = nsw++;
+                    for (uint32_t q = pbase[n]; q < pbase[n + 1]; q++) slot[q] = sp++;
+                }
+                uint32_t *route = (uint32_t *)(A + H.o_route);
+                uint16_t *cg = (uint16_t *)(A + H.o_cgrp);
+                uint16_t *li = (uint16_t *)(A + H.o_lidx);
+                CRW2 *crw = (CRW2 *)(A + H.o_crw);
+                for (uint32_t c = 0; c < nconn; c++) {
+                    route[c] = conn[c].route;
+                    cg[c] = (uint16_t)conn[c].grp;
+                    li[c] = (uint16_t)conn[c].lidx;
+                    const Grp &g = grp[conn[c].grp];
+                    uint32_t first = first_flow_size(g, conn[c].idx);
+                    crw[c].r_rem = (uint16_t)first;
+                    if (g.kind == GK_XFLOW) crw[c].s_rem = (uint16_t)first;
+                }
+                if (ngrp > 65535) return fail(out, MSIM_E_LIMIT, "experiment %u: too many groups", e);
+                if (ngrp) memcpy(A + H.o_grp, grp.data(), sizeof(Grp) * ngrp);
+                if (nconn) memcpy(A + H.o_hout, hout.data(), 4ull * nconn);
+                PortRO2 *pro = (PortRO2 *)(A + H.o_port);
+                PortPriv *pv = (PortPriv *)(A + H.o_priv);
+                for (uint32_t p = 0; p < n_ports; p++) {
+                    const PortRO &P = port[p];
+                    const uint32_t sl = slot[p];
+                    PortRO2 &R2 = pro[sl];
+                    R2.peer = slot[P.peer];
+                    R2.rate = P.rate;
+                    R2.delay = P.delay;
+                    R2.local = P.local;
+                    R2.deg = P.deg;
+                    R2.flags = (uint8_t)(PF_USED | (P.alive ? PF_ALIVE : 0) | (P.is_host ? PF_HOST : 0) |
+                                         (P.peer_is_host ? PF_PEER_HOST : 0));
+                    if (P.is_host) {
+                        R2.vbase = host[P.host].out_off;
+                        R2.n_out = (uint16_t)host[P.host].n_out;
+                        pv[sl].left = left[P.host];
+                    } else {
+                        R2.vbase = sw_of[port_node[p]] * rsz * rsz;
+                        pv[sl].freem = Q == 64 ? ~0ull : ((1ull << Q) - 1ull);
+                    }
+                }
+                memcpy(A, &H, sizeof H);
+                out.rw_off = H.rw_off;
+                out.bytes = H.bytes;
+                out.lds_bytes = H.lds_bytes;
+                out.compact = true;
+                out.kind = 1 + (rsz == 16 ? 2u : 0u) + (dt == 4 ? 1u : 0u);
+                out.nt = nt;
+                return MSIM_OK;
+            }
+        }
+    }
+
+    /* ---- general layout */
     ArenaHdr H{};
+    H.mode = MODE_GENERAL;
     H.n_ports = n_ports; H.n_hosts = n_hosts; H.n_conn = nconn; H.n_grp = ngrp;
     H.Q = Q; H.W = W; H.R = R; H.n_voq = n_voq; H.n_flows = (uint32_t)n_flows;
     size_t off = align16(sizeof(ArenaHdr));
@@ -395,9 +516,6 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, Compiled &out)
     for (uint32_t h = 0; h < n_hosts; h++) hs[h].left = left[h];
     out.rw_off = H.rw_off;
     out.bytes = H.bytes;
-    out.n_flows = n_flows;
-    out.n_conns = nconn;
-    out.n_ports = n_ports;
     return MSIM_OK;
 }
 
@@ -412,6 +530,8 @@ struct msim_ctx {
     uint64_t o_state = 0, o_arena_off = 0, o_order = 0, o_rec_off = 0, o_pristine = 0, o_rec_all = 0;
     uint64_t rec_words = 0, ws_bytes = 0;
     uint32_t block = 0, grid = 0, lds = 0, n_lds = 0, max_ports = 0, force_global = 0;
+    uint32_t k_base[MSIM_KINDS] = {}, k_count[MSIM_KINDS] = {}, k_block[MSIM_KINDS] = {};
+    uint32_t k_grid[MSIM_KINDS] = {}, k_lds[MSIM_KINDS] = {};
     uint64_t max_arena = 0;
     uint8_t *ws = nullptr;
     bool bound = false;
@@ -456,7 +576,7 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
         for (;;) {
             uint32_t e = next.fetch_add(1);
             if (e >= E) break;
-            compile_exp(spec, e, ctx->exps[e]);
+            compile_exp(spec, e, !ctx->force_global, ctx->exps[e]);
         }
     };
     std::vector<std::thread> th;
@@ -483,8 +603,14 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
     ctx->order.resize(E);
     for (uint32_t e = 0; e < E; e++) ctx->order[e] = e;
     std::stable_sort(ctx->order.begin(), ctx->order.end(), [&](uint32_t a, uint32_t b) {
+        if (ctx->exps[a].kind != ctx->exps[b].kind) return ctx->exps[a].kind < ctx->exps[b].kind;
         return ctx->exps[a].est_hops > ctx->exps[b].est_hops;
     });
+    for (uint32_t i = 0; i < E; i++) {
+        uint32_t k = ctx->exps[ctx->order[i]].kind;
+        if (ctx->k_count[k] == 0) ctx->k_base[k] = i;
+        ctx->k_count[k]++;
+    }
     /* workspace layout */
     uint64_t off = 256;
     auto take = [&](uint64_t bytes) { uint64_t o = off; off = (off + bytes + 255) & ~255ull; return o; };
@@ -524,11 +650,32 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
                  (!ctx->recorded[e] || ctx->rec_off[e] + 12ull * c.n_flows <= off);
     }
     if (!inside) { g_create_error = "internal error: workspace layout overlaps its bounds"; delete ctx; return MSIM_E_LIMIT; }
-    /* launch shape */
-    uint32_t bt = opts && opts->block_threads ? opts->block_threads : ((ctx->max_ports + 63) / 64) * 64;
-    bt = std::max(64u, std::min(1024u, bt));
-    if (bt % 64) { g_create_error = "block_threads must be a multiple of 64"; delete ctx; return MSIM_E_ARG; }
-    ctx->block = bt;
+    /* launch shape per kernel kind: a compact experiment needs one thread per
+     * port slot; the general path strides its threads over the ports */
+    for (uint32_t e = 0; e < E; e++) {
+        const Compiled &c = ctx->exps[e];
+        uint32_t need = c.compact ? c.nt : std::min<uint32_t>(1024u, (uint32_t)c.n_ports);
+        ctx->k_block[c.kind] = std::max(ctx->k_block[c.kind], ((need + 63) / 64) * 64);
+        if (c.compact) I.n_compact++;
+    }
+    for (uint32_t k = 0; k < MSIM_KINDS; k++) {
+        if (!ctx->k_count[k]) continue;
+        uint32_t bt = std::max(64u, ctx->k_block[k]);
+        if (opts && opts->block_threads) {
+            bt = opts->block_threads;
+            if (bt % 64 || bt > 1024 || bt < 64 || (k != 0 && bt < ctx->k_block[k])) {
+                g_create_error = "block_threads must be a multiple of 64 (64..1024) covering every compact experiment's ports";
+                delete ctx;
+                return MSIM_E_ARG;
+            }
+        }
+        ctx->k_block[k] = bt;
+    }
+    uint32_t main_kind = 0;
+    for (uint32_t k = 0; k < MSIM_KINDS; k++)
+        if (ctx->k_count[k] > ctx->k_count[main_kind]) main_kind = k;
+    ctx->block = ctx->k_block[main_kind];
+    const uint32_t bt = ctx->block;
     I.n_exp = E;
     I.block_threads = bt;
     I.max_ports = ctx->max_ports;
@@ -559,26 +706,44 @@ extern "C" int msim_bind(msim_ctx *ctx, void *dev_ws, uint64_t ws_bytes, void *s
     if (he == hipSuccess) he = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (he == hipSuccess) he = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (he != hipSuccess) return hip_fail(ctx, he, "device query");
-    const uint32_t static_lds = 2048;
+    const uint32_t static_lds = 4096;
     uint32_t budget = max_lds > (int)static_lds ? (uint32_t)max_lds - static_lds : 0;
-    ctx->lds = 0;
     ctx->n_lds = 0;
-    if (!ctx->force_global) {
-        uint32_t need = 0;
-        for (uint32_t e = 0; e < E; e++)
-            if (ctx->exps[e].bytes <= budget) { need = std::max(need, ctx->exps[e].bytes); ctx->n_lds++; }
-        ctx->lds = need ? ((need + 255) / 256) * 256 : 0;
-        if (ctx->lds > budget) ctx->lds = need;
+    uint32_t main_kind = 0;
+    for (uint32_t k = 0; k < MSIM_KINDS; k++) {
+        ctx->k_lds[k] = 0;
+        ctx->k_grid[k] = 0;
+        if (ctx->k_count[k] > ctx->k_count[main_kind]) main_kind = k;
     }
-    if (ctx->lds) {
-        he = msim_set_lds_limit(ctx->lds);
-        if (he != hipSuccess) return hip_fail(ctx, he, "hipFuncSetAttribute(dynamic LDS)");
+    for (uint32_t e = 0; e < E; e++) {
+        const Compiled &c = ctx->exps[e];
+        if (c.compact) {
+            if (c.lds_bytes > budget)
+                return ctx_fail(ctx, MSIM_E_LIMIT, "device LDS too small for a compact experiment");
+            ctx->k_lds[c.kind] = std::max(ctx->k_lds[c.kind], c.lds_bytes);
+            ctx->n_lds++;
+        } else if (!ctx->force_global && c.bytes <= budget) {
+            ctx->k_lds[0] = std::max(ctx->k_lds[0], c.bytes);
+            ctx->n_lds++;
+        }
     }
-    int per_cu = 0;
-    he = msim_occupancy(ctx->block, ctx->lds, &per_cu);
-    if (he != hipSuccess) return hip_fail(ctx, he, "occupancy query");
-    if (per_cu < 1) per_cu = 1;
-    ctx->grid = (uint32_t)std::min<uint64_t>(E, (uint64_t)n_cu * per_cu);
+    for (uint32_t k = 0; k < MSIM_KINDS; k++) {
+        if (!ctx->k_count[k]) continue;
+        uint32_t l = ctx->k_lds[k] ? ((ctx->k_lds[k] + 255) / 256) * 256 : 0;
+        if (l > budget) l = ctx->k_lds[k];
+        ctx->k_lds[k] = l;
+        if (l) {
+            he = msim_set_lds_limit(k, l);
+            if (he != hipSuccess) return hip_fail(ctx, he, "hipFuncSetAttribute(dynamic LDS)");
+        }
+        int per_cu = 0;
+        he = msim_occupancy(k, ctx->k_block[k], l, &per_cu);
+        if (he != hipSuccess) return hip_fail(ctx, he, "occupancy query");
+        if (per_cu < 1) per_cu = 1;
+        ctx->k_grid[k] = (uint32_t)std::min<uint64_t>(ctx->k_count[k], (uint64_t)n_cu * per_cu);
+    }
+    ctx->lds = ctx->k_lds[main_kind];
+    ctx->grid = ctx->k_grid[main_kind];
     ctx->info.grid_blocks = ctx->grid;
     ctx->info.lds_bytes = ctx->lds;
     ctx->info.n_lds_exp = ctx->n_lds;
@@ -660,9 +825,18 @@ extern "C" int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *stream, uint32_
     if (!ctx) return MSIM_E_ARG;
     if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_run before msim_bind");
     (void)flags;
-    KParams kp = make_params(ctx, max_ticks);
-    hipError_t he = msim_launch_run(&kp, ctx->grid, ctx->block, ctx->lds, (hipStream_t)stream);
-    if (he != hipSuccess) return hip_fail(ctx, he, "kernel launch");
+    bool first = true;
+    for (uint32_t k = 0; k < MSIM_KINDS; k++) {
+        if (!ctx->k_count[k]) continue;
+        KParams kp = make_params(ctx, max_ticks);
+        kp.order_base = ctx->k_base[k];
+        kp.n_run = ctx->k_count[k];
+        kp.lds_bytes = ctx->k_lds[k];
+        hipError_t he = msim_launch_run(&kp, k, ctx->k_grid[k], ctx->k_block[k], ctx->k_lds[k], first,
+                                        (hipStream_t)stream);
+        if (he != hipSuccess) return hip_fail(ctx, he, "kernel launch");
+        first = false;
+    }
     return MSIM_OK;
 }
 

@@ -375,6 +375,34 @@ struct Shared {
     uint32_t mx[5][16];
 };
 
+/* Folds the workgroup's totals of a run into the experiment's state (thread 0). */
+__device__ void finish_state(ExpState *stp, const Shared &sh, uint32_t nwaves, uint32_t t, bool done, bool dead,
+                             uint32_t t_dead)
+{
+    uint64_t h = 0, d = 0, g = 0;
+    uint32_t tm = 0, lt = 0, la = 0, ma = 0, fa = 0;
+    for (uint32_t w = 0; w < nwaves; w++) {
+        h += sh.sum[0][w]; d += sh.sum[1][w]; g += sh.sum[2][w];
+        tm = max(tm, sh.mx[0][w]); lt = max(lt, sh.mx[1][w]); la = max(la, sh.mx[2][w]); ma = max(ma, sh.mx[3][w]);
+        fa = max(fa, sh.mx[4][w]);
+    }
+    ExpState st = *stp;
+    st.pkt_hops += h;
+    st.delivered += d;
+    st.digest += g;
+    st.t_max = max(st.t_max, tm);
+    st.last_tx1 = max(st.last_tx1, lt);
+    st.last_act1 = max(st.last_act1, la);
+    st.max_arr = max(st.max_arr, ma);
+    st.t_now = t;
+    st.fault |= fa;
+    if (st.fault) { st.status = 3; st.t_out = t; }
+    else if (done) { st.status = 0; st.t_out = st.t_max; }
+    else if (dead) { st.status = 2; st.t_out = t_dead; }
+    else { st.status = 1; st.t_out = t; }
+    *stp = st;
+}
+
 /* ----------------------------------------------------------- one experiment */
 
 template <bool IN_LDS>
@@ -484,60 +512,495 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
         uint4 *dst = (uint4 *)(arena_g + rw_off);
         for (uint32_t i = tid; i < (arena_bytes - rw_off) / 16; i += nth) dst[i] = src[i];
     }
-    if (tid == 0) {
-        uint64_t h = 0, d = 0, g = 0;
-        uint32_t tm = 0, lt = 0, la = 0, ma = 0, fa = 0;
-        for (uint32_t w = 0; w < nwaves; w++) {
-            h += sh.sum[0][w]; d += sh.sum[1][w]; g += sh.sum[2][w];
-            tm = max(tm, sh.mx[0][w]); lt = max(lt, sh.mx[1][w]); la = max(la, sh.mx[2][w]); ma = max(ma, sh.mx[3][w]);
-            fa = max(fa, sh.mx[4][w]);
-        }
-        ExpState st = *stp;
-        st.pkt_hops += h;
-        st.delivered += d;
-        st.digest += g;
-        st.t_max = max(st.t_max, tm);
-        st.last_tx1 = max(st.last_tx1, lt);
-        st.last_act1 = max(st.last_act1, la);
-        st.max_arr = max(st.max_arr, ma);
-        st.t_now = t;
-        st.fault |= fa;
-        if (st.fault) { st.status = 3; st.t_out = t; }
-        else if (done) { st.status = 0; st.t_out = st.t_max; }
-        else if (dead) { st.status = 2; st.t_out = t_dead; }
-        else { st.status = 1; st.t_out = t; }
-        *stp = st;
-    }
+    if (tid == 0) finish_state(stp, sh, nwaves, t, done, dead, t_dead);
     __syncthreads();
 }
 
-extern "C" __global__ void __launch_bounds__(1024) msim_megakernel(KParams kp)
+/* ==================================================================== *
+ * Compact path: one thread per port, port-private state in registers,
+ * byte-row (SWAR) queue bookkeeping, shared state in LDS.
+ * ==================================================================== */
+
+/* per-byte a - b (mod 256) of eight packed bytes */
+__device__ __forceinline__ uint64_t bytes_sub(uint64_t a, uint64_t b)
+{
+    const uint64_t H = 0x8080808080808080ull;
+    return ((a | H) - (b & ~H)) ^ ((a ^ ~b) & H);
+}
+
+/* 0x80 in every byte of d that is not zero */
+__device__ __forceinline__ uint64_t bytes_nz(uint64_t d)
+{
+    const uint64_t L = 0x7F7F7F7F7F7F7F7Full;
+    return ((((d & L) + L) | d) & ~L);
+}
+
+/* A row of up to 16 byte counters held in registers (W words). */
+template <int W>
+struct Row {
+    uint64_t w0, w1;
+    __device__ __forceinline__ uint32_t get(uint32_t i) const
+    {
+        uint64_t w = (W == 1 || i < 8) ? w0 : w1;
+        return (uint32_t)(w >> ((i & 7) * 8)) & 0xFFu;
+    }
+    __device__ __forceinline__ void set(uint32_t i, uint32_t v)
+    {
+        const uint32_t sh = (i & 7) * 8;
+        const uint64_t m = ~(0xFFull << sh), b = (uint64_t)(v & 0xFFu) << sh;
+        if (W == 1 || i < 8) w0 = (w0 & m) | b;
+        else w1 = (w1 & m) | b;
+    }
+    __device__ __forceinline__ void load(const uint8_t *p)
+    {
+        w0 = *(const uint64_t *)p;
+        w1 = W == 2 ? *(const uint64_t *)(p + 8) : 0ull;
+    }
+};
+
+/* First set byte-flag at or after byte rr, cyclically over the row; -1 if none. */
+template <int W>
+__device__ __forceinline__ int first_from(uint64_t n0, uint64_t n1, uint32_t rr)
+{
+    if (W == 1) {
+        const uint32_t sh = 8 * rr;
+        uint64_t rot = sh ? (n0 >> sh) | (n0 << (64 - sh)) : n0;
+        if (!rot) return -1;
+        return (int)((rr + (__builtin_ctzll(rot) >> 3)) & 7);
+    }
+    uint64_t a = rr < 8 ? n0 : n1, b = rr < 8 ? n1 : n0;
+    const uint32_t sh = 8 * (rr & 7), base = rr < 8 ? 0 : 8, other = 8 - base;
+    uint64_t m = a & (~0ull << sh);
+    if (m) return (int)(base + (__builtin_ctzll(m) >> 3));
+    if (b) return (int)(other + (__builtin_ctzll(b) >> 3));
+    m = a & ((1ull << sh) - 1ull);
+    if (m) return (int)(base + (__builtin_ctzll(m) >> 3));
+    return -1;
+}
+
+struct CCtx {
+    uint8_t *arr, *head, *nslot, *pnxt, *scnt;
+    uint32_t *popped;
+    const uint32_t *route, *hout;
+    const uint16_t *cgrp, *lidx;
+    CRW2 *crw;
+    const Grp *grp;
+    uint32_t *rec;
+    uint32_t Q, W, R, rsz, n_flows, SB;
+};
+
+template <typename DT>
+struct CBufs {
+    DT *pdesc, *sdesc;
+};
+
+__device__ __forceinline__ uint32_t csize(const Grp &g, uint32_t idx, uint32_t pos)
+{
+    if (g.kind == GK_BCAST) return g.p / g.S + (pos < g.p % g.S ? 1u : 0u);
+    uint32_t r = pos / g.S;
+    if (r + 1 < g.R) return g.p;
+    uint32_t k = ring_chunk(g.kind, g.N, idx, pos - r * g.S);
+    return g.X / g.N + (k < g.X % g.N ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t cfid(const Grp &g, uint32_t idx, uint32_t pos)
+{
+    if (g.kind == GK_XFLOW) return g.fid_base + idx;
+    if (g.kind == GK_BCAST) return g.fid_base + idx * g.S + pos;
+    return g.fid_base + pos * g.N + idx;
+}
+
+__device__ __forceinline__ bool crecv_ok(const CCtx &C, const Grp &g, uint32_t idx, uint32_t c, uint32_t pos)
+{
+    if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
+        if (pos % g.S == 0) return true;
+        uint32_t cin = g.conn_base + (idx == 0 ? g.N - 1 : idx - 1);
+        return C.crw[cin].r_pos >= pos;
+    }
+    if (g.kind == GK_BCAST) return idx == 0 || C.crw[c - 1].r_pos > pos;
+    return true;
+}
+
+struct HostRegs {
+    uint64_t ready;
+    uint32_t pcnt, p0, p1, p2, p3;
+};
+
+__device__ __forceinline__ void cactivate(const CCtx &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t pos,
+                                          const Grp &g, uint32_t idx, uint32_t t)
+{
+    C.crw[c].s_st = (uint16_t)(pos | (CS_ACTIVE << C_STATE_SHIFT));
+    if (g.kind != GK_XFLOW) C.crw[c].s_rem = (uint16_t)csize(g, idx, pos);
+    hr.ready |= 1ull << C.lidx[c];
+    a.last_act1 = t + 1;
+    if (C.rec) C.rec[C.n_flows + cfid(g, idx, pos)] = t;
+}
+
+__device__ __forceinline__ void ccheck(const CCtx &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t t)
+{
+    const Grp g = C.grp[C.cgrp[c]];
+    const uint32_t idx = c - g.conn_base;
+    const uint32_t pos = C.crw[c].s_st & C_POS_MASK;
+    if (pos >= flows_per_conn(g)) C.crw[c].s_st = (uint16_t)(pos | (CS_DONE << C_STATE_SHIFT));
+    else if (crecv_ok(C, g, idx, c, pos)) cactivate(C, a, hr, c, pos, g, idx, t);
+    else C.crw[c].s_st = (uint16_t)(pos | (CS_IDLE << C_STATE_SHIFT));
+}
+
+template <typename DT>
+__device__ __forceinline__ void ctransmit(const CCtx &C, const CBufs<DT> &B, Acc &a, const PortRO2 &pr,
+                                          uint32_t desc, uint32_t t, uint32_t slot)
+{
+    uint32_t s2 = slot + pr.delay;
+    if (s2 >= C.W) s2 -= C.W;
+    const uint32_t si = pr.peer * C.W + s2;
+    const uint32_t k = C.scnt[si];
+    C.scnt[si] = (uint8_t)(k + 1);
+    B.sdesc[si * C.R + k] = (DT)desc;
+    a.hops++;
+    a.last_tx1 = t + 1;
+    a.max_arr = max(a.max_arr, t + pr.delay);
+}
+
+template <int W, typename DT>
+__device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
+{
+    const uint32_t tid = threadIdx.x, nth = blockDim.x;
+    const uint32_t lane = tid & 63, wave = tid >> 6, nwaves = (nth + 63) >> 6;
+    ExpState *stp = (ExpState *)(kp.ws + kp.o_state) + x;
+    const ArenaHdr2 *HG = (const ArenaHdr2 *)arena_g;
+    const uint32_t lds_bytes = HG->lds_bytes, rw_off = HG->rw_off;
+    {
+        const uint4 *src = (const uint4 *)arena_g;
+        uint4 *dst = (uint4 *)lds;
+        for (uint32_t i = tid; i < lds_bytes / 16; i += nth) dst[i] = src[i];
+    }
+    const ArenaHdr2 *H = (const ArenaHdr2 *)arena_g;
+    const uint32_t nt = H->nt, nh = H->H, SB = H->SB;
+    const bool used = tid < nt;
+    PortRO2 pr = {};
+    PortPriv pv = {};
+    if (used) {
+        pr = ((const PortRO2 *)(arena_g + H->o_port))[tid];
+        pv = ((const PortPriv *)(arena_g + H->o_priv))[tid];
+    }
+    CCtx C;
+    C.arr = lds + H->o_arr;
+    C.head = lds + H->o_head;
+    C.nslot = lds + H->o_nslot;
+    C.pnxt = lds + H->o_pnxt;
+    C.scnt = lds + H->o_scnt;
+    C.popped = (uint32_t *)(lds + H->o_popped);
+    C.route = (const uint32_t *)(lds + H->o_route);
+    C.hout = (const uint32_t *)(lds + H->o_hout);
+    C.cgrp = (const uint16_t *)(lds + H->o_cgrp);
+    C.lidx = (const uint16_t *)(lds + H->o_lidx);
+    C.crw = (CRW2 *)(lds + H->o_crw);
+    C.grp = (const Grp *)(lds + H->o_grp);
+    C.Q = H->Q;
+    C.W = H->W;
+    C.R = H->R;
+    C.rsz = H->rsz;
+    C.n_flows = H->n_flows;
+    C.SB = SB;
+    CBufs<DT> B;
+    B.pdesc = (DT *)(lds + H->o_pdesc);
+    B.sdesc = (DT *)(lds + H->o_sdesc);
+    uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
+    C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
+
+    const bool is_host = tid < nh;
+    const bool is_sw = tid >= SB && used;
+    const bool alive = pr.flags & PF_ALIVE;
+    const bool peer_host = pr.flags & PF_PEER_HOST;
+    const uint32_t deg = pr.deg, local = pr.local, Q = C.Q, rsz = C.rsz;
+    /* registers */
+    Row<W> tslot, fcur, hseen, phead, arrv;
+    tslot.w0 = pv.tslot[0]; tslot.w1 = pv.tslot[1];
+    fcur.w0 = pv.fcur[0]; fcur.w1 = pv.fcur[1];
+    hseen.w0 = pv.hseen[0]; hseen.w1 = pv.hseen[1];
+    phead.w0 = pv.phead[0]; phead.w1 = pv.phead[1];
+    arrv.w0 = pv.arrv[0]; arrv.w1 = pv.arrv[1];
+    uint64_t freem = pv.freem;
+    uint32_t popped = pv.popped, pushed = pv.pushed, rr = pv.rr;
+    HostRegs hr;
+    hr.ready = pv.ready;
+    hr.pcnt = pv.pcnt;
+    hr.p0 = pv.pend[0]; hr.p1 = pv.pend[1]; hr.p2 = pv.pend[2]; hr.p3 = pv.pend[3];
+    const uint32_t pool = is_sw ? (tid - SB) * Q : 0;
+    const uint32_t qbase = tid - local;          /* thread slot of this switch's port 0 */
+    const uint32_t rowp = pr.vbase + local * rsz;
+
+    Acc a;
+    a.hops = a.delivered = a.digest = 0;
+    a.tmax = a.last_tx1 = a.last_act1 = a.max_arr = 0;
+    a.left = is_host ? pv.left : 0;
+    a.fault = 0;
+    __syncthreads();
+
+    const uint32_t t0 = stp->t_now;
+    const uint32_t t_end = (uint64_t)t0 + kp.max_ticks > 0xFFFFFFF0ull ? 0xFFFFFFF0u : t0 + kp.max_ticks;
+    const uint32_t hist = max(max(stp->last_tx1, stp->last_act1), stp->max_arr);
+    uint32_t t = t0, par = 0, slot = t0 % C.W;
+    bool done = false, dead = false;
+    uint32_t t_dead = 0;
+    while (t < t_end) {
+        /* ---------------- phase A */
+        if (is_sw) {
+            Row<W> hd;
+            hd.load(C.head + rowp);
+            uint64_t d0 = bytes_sub(hd.w0, hseen.w0);
+            uint64_t d1 = W == 2 ? bytes_sub(hd.w1, hseen.w1) : 0ull;
+            if (d0 | d1) {
+                uint64_t m0 = bytes_nz(d0), m1 = bytes_nz(d1);
+                while (m0 | m1) {
+                    uint32_t o;
+                    if (m0) { o = __builtin_ctzll(m0) >> 3; m0 &= m0 - 1; }
+                    else { o = 8 + (__builtin_ctzll(m1) >> 3); m1 &= m1 - 1; }
+                    uint32_t k = (uint32_t)((o < 8 ? d0 : d1) >> (8 * (o & 7))) & 0xFFu;
+                    popped += k;
+                    uint32_t f = fcur.get(o);
+                    for (uint32_t j = 0; j < k; j++) {
+                        uint32_t s = f;
+                        f = C.pnxt[pool + s];
+                        freem |= 1ull << s;
+                    }
+                    fcur.set(o, f);
+                }
+                hseen = hd;
+                C.popped[tid] = popped;
+            }
+            const uint32_t si = tid * C.W + slot;
+            const uint32_t n = C.scnt[si];
+            for (uint32_t k = 0; k < n; k++) {
+                const uint32_t desc = B.sdesc[si * C.R + k];
+                const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
+                const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
+                if (freem == 0 || o >= deg) { a.fault = 1; continue; }
+                const uint32_t s = __builtin_ctzll(freem);
+                freem &= freem - 1;
+                B.pdesc[pool + s] = (DT)(desc + 1);
+                const uint32_t av = arrv.get(o);
+                const uint32_t vp = pr.vbase + o * rsz + local;
+                if (av == hseen.get(o)) {
+                    C.nslot[vp] = (uint8_t)s;
+                    fcur.set(o, s);
+                } else {
+                    C.pnxt[pool + tslot.get(o)] = (uint8_t)s;
+                }
+                tslot.set(o, s);
+                arrv.set(o, av + 1);
+                C.arr[vp] = (uint8_t)(av + 1);
+            }
+            if (n) C.scnt[si] = 0;
+        } else if (is_host) {
+            const uint32_t si = tid * C.W + slot;
+            const uint32_t n = C.scnt[si];
+            for (uint32_t k = 0; k < n; k++) {
+                const uint32_t c = (uint32_t)B.sdesc[si * C.R + k] >> DESC_SHIFT;
+                CRW2 &cw = C.crw[c];
+                a.delivered++;
+                const uint32_t rem = cw.r_rem - 1u;
+                cw.r_rem = (uint16_t)rem;
+                if (rem) continue;
+                const Grp g = C.grp[C.cgrp[c]];
+                const uint32_t idx = c - g.conn_base;
+                uint32_t pos = cw.r_pos;
+                const uint32_t fid = cfid(g, idx, pos);
+                a.digest += mix64(((uint64_t)fid << 32) | t);
+                a.tmax = t;
+                a.left--;
+                if (C.rec) C.rec[fid] = t;
+                pos++;
+                cw.r_pos = (uint16_t)pos;
+                if (pos < flows_per_conn(g)) cw.r_rem = (uint16_t)csize(g, idx, pos);
+                uint32_t d = MSIM_NONE;
+                if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) d = g.conn_base + (idx + 1 == g.N ? 0 : idx + 1);
+                else if (g.kind == GK_BCAST && idx + 1 < g.N) d = c + 1;
+                if (d != MSIM_NONE && (C.crw[d].s_st >> C_STATE_SHIFT) == CS_IDLE) {
+                    const uint32_t dpos = C.crw[d].s_st & C_POS_MASK;
+                    const uint32_t didx = d - g.conn_base;
+                    if (crecv_ok(C, g, didx, d, dpos)) cactivate(C, a, hr, d, dpos, g, didx, t);
+                }
+            }
+            if (n) C.scnt[si] = 0;
+            if (t == 0) {
+                for (uint32_t j = 0; j < pr.n_out; j++) ccheck(C, a, hr, C.hout[pr.vbase + j], t);
+            } else if (hr.pcnt) {
+                ccheck(C, a, hr, hr.p0, t);
+                if (hr.pcnt > 1) ccheck(C, a, hr, hr.p1, t);
+                if (hr.pcnt > 2) ccheck(C, a, hr, hr.p2, t);
+                if (hr.pcnt > 3) ccheck(C, a, hr, hr.p3, t);
+                hr.pcnt = 0;
+            }
+        }
+        __syncthreads();
+        /* ---------------- phase D */
+        if (is_sw && alive) {
+            Row<W> ar;
+            ar.load(C.arr + rowp);
+            int32_t credit = peer_host ? (int32_t)pr.rate : (int32_t)Q - (int32_t)(pushed - C.popped[pr.peer]);
+            uint64_t v0 = bytes_sub(ar.w0, phead.w0);
+            uint64_t v1 = W == 2 ? bytes_sub(ar.w1, phead.w1) : 0ull;
+            for (uint32_t m = 0; m < pr.rate && credit > 0; m++) {
+                const int i = first_from<W>(bytes_nz(v0), bytes_nz(v1), rr);
+                if (i < 0) break;
+                const uint32_t vp = rowp + (uint32_t)i;
+                const uint32_t qpool = (qbase + (uint32_t)i - SB) * Q;
+                const uint32_t s = C.nslot[vp];
+                const uint32_t desc = B.pdesc[qpool + s];
+                C.nslot[vp] = C.pnxt[qpool + s];
+                const uint32_t hb = phead.get((uint32_t)i) + 1;
+                phead.set((uint32_t)i, hb);
+                C.head[pr.vbase + (uint32_t)i * rsz + local] = (uint8_t)hb;
+                if (i < 8) v0 -= 1ull << (8 * i);
+                else v1 -= 1ull << (8 * (i - 8));
+                rr = (uint32_t)i + 1 == deg ? 0 : (uint32_t)i + 1;
+                ctransmit(C, B, a, pr, desc, t, slot);
+                pushed++;
+                credit--;
+            }
+        } else if (is_host && alive && pr.n_out) {
+            int32_t credit = (int32_t)Q - (int32_t)(pushed - C.popped[pr.peer]);
+            for (uint32_t m = 0; m < pr.rate && credit > 0 && hr.ready; m++) {
+                const uint64_t rot = rr ? (hr.ready >> rr) | (hr.ready << (64 - rr)) : hr.ready;
+                const uint32_t j = (rr + (uint32_t)__builtin_ctzll(rot)) & 63u;
+                const uint32_t c = C.hout[pr.vbase + j];
+                ctransmit(C, B, a, pr, c << DESC_SHIFT, t, slot);
+                pushed++;
+                credit--;
+                rr = j + 1 == pr.n_out ? 0 : j + 1;
+                CRW2 &cw = C.crw[c];
+                const uint32_t rem = cw.s_rem - 1u;
+                cw.s_rem = (uint16_t)rem;
+                if (rem == 0) {
+                    hr.ready &= ~(1ull << j);
+                    const uint32_t pos = cw.s_st & C_POS_MASK;
+                    if (C.rec) {
+                        const Grp g = C.grp[C.cgrp[c]];
+                        C.rec[2 * C.n_flows + cfid(g, c - g.conn_base, pos)] = t + 1;
+                    }
+                    cw.s_st = (uint16_t)(pos + 1);
+                    if (hr.pcnt == 0) hr.p0 = c;
+                    else if (hr.pcnt == 1) hr.p1 = c;
+                    else if (hr.pcnt == 2) hr.p2 = c;
+                    else hr.p3 = c;
+                    hr.pcnt++;
+                }
+            }
+        }
+        t++;
+        slot = slot + 1 == C.W ? 0 : slot + 1;
+        if ((t - t0) % CHECK_EVERY == 0 || t == t_end) {
+            uint32_t any = __ballot(a.left > 0) != 0ull;
+            uint32_t ts = wave_max_u32(max(max(a.last_tx1, a.last_act1), a.max_arr));
+            if (lane == 0) { sh.chk_any[par][wave] = any; sh.chk_max[par][wave] = ts; }
+            __syncthreads();
+            any = 0;
+            ts = hist;
+            for (uint32_t w = 0; w < nwaves; w++) { any |= sh.chk_any[par][w]; ts = max(ts, sh.chk_max[par][w]); }
+            par ^= 1;
+            if (!any) { done = true; break; }
+            if (ts <= t - 1) { dead = true; t_dead = ts; break; }
+        } else {
+            __syncthreads();
+        }
+    }
+
+    /* write back: shared mutable image, registers, totals */
+    {
+        const uint4 *src = (const uint4 *)(lds + rw_off);
+        uint4 *dst = (uint4 *)(arena_g + rw_off);
+        for (uint32_t i = tid; i < (lds_bytes - rw_off) / 16; i += nth) dst[i] = src[i];
+    }
+    if (used) {
+        pv.tslot[0] = tslot.w0; pv.tslot[1] = tslot.w1;
+        pv.fcur[0] = fcur.w0; pv.fcur[1] = fcur.w1;
+        pv.hseen[0] = hseen.w0; pv.hseen[1] = hseen.w1;
+        pv.phead[0] = phead.w0; pv.phead[1] = phead.w1;
+        pv.arrv[0] = arrv.w0; pv.arrv[1] = arrv.w1;
+        pv.freem = freem;
+        pv.popped = popped; pv.pushed = pushed; pv.rr = rr;
+        pv.ready = hr.ready; pv.pcnt = hr.pcnt;
+        pv.pend[0] = hr.p0; pv.pend[1] = hr.p1; pv.pend[2] = hr.p2; pv.pend[3] = hr.p3;
+        pv.left = is_host ? a.left : 0;
+        ((PortPriv *)(arena_g + H->o_priv))[tid] = pv;
+    }
+    uint64_t s0 = wave_sum_u64(a.hops), s1 = wave_sum_u64(a.delivered), s2 = wave_sum_u64(a.digest);
+    uint32_t m0 = wave_max_u32(a.tmax), m1 = wave_max_u32(a.last_tx1), m2 = wave_max_u32(a.last_act1),
+             m3 = wave_max_u32(a.max_arr), m4 = wave_max_u32(a.fault);
+    if (lane == 0) {
+        sh.sum[0][wave] = s0; sh.sum[1][wave] = s1; sh.sum[2][wave] = s2;
+        sh.mx[0][wave] = m0; sh.mx[1][wave] = m1; sh.mx[2][wave] = m2; sh.mx[3][wave] = m3; sh.mx[4][wave] = m4;
+    }
+    __syncthreads();
+    if (tid == 0) finish_state(stp, sh, nwaves, t, done, dead, t_dead);
+    __syncthreads();
+}
+
+/* Kernel kinds: the general path, and the compact path for 8- or 16-byte
+ * queue rows and 16- or 32-bit packet descriptors.  Each kind is its own
+ * kernel so that each gets its own register allocation. */
+template <int KIND>
+__device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *arena, uint8_t *lds, Shared &sh)
+{
+    if (KIND == 0) {
+        if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true>(kp, x, arena, lds, sh);
+        else run_experiment<false>(kp, x, arena, lds, sh);
+    } else if (KIND == 1) {
+        run_compact<1, uint16_t>(kp, x, arena, lds, sh);
+    } else if (KIND == 2) {
+        run_compact<1, uint32_t>(kp, x, arena, lds, sh);
+    } else if (KIND == 3) {
+        run_compact<2, uint16_t>(kp, x, arena, lds, sh);
+    } else {
+        run_compact<2, uint32_t>(kp, x, arena, lds, sh);
+    }
+}
+
+/* Persistent loop: each workgroup claims the next experiment of its kind (the
+ * order array lists the biggest experiments first) until none are left. */
+template <int KIND>
+__device__ void megakernel_body(const KParams &kp)
 {
     extern __shared__ __align__(16) uint8_t lds_dyn[];
     __shared__ Shared sh;
     WsHdr *wh = (WsHdr *)kp.ws;
     const uint64_t *arena_off = (const uint64_t *)(kp.ws + kp.o_arena_off);
-    const uint32_t *order = (const uint32_t *)(kp.ws + kp.o_order);
+    const uint32_t *order = (const uint32_t *)(kp.ws + kp.o_order) + kp.order_base;
     const ExpState *states = (const ExpState *)(kp.ws + kp.o_state);
     for (;;) {
-        if (threadIdx.x == 0) sh.exp = atomicAdd(&wh->claim, 1u);
+        if (threadIdx.x == 0) sh.exp = atomicAdd(&wh->claim[KIND], 1u);
         __syncthreads();
         const uint32_t e = sh.exp;
         __syncthreads();
-        if (e >= kp.n_exp) break;
+        if (e >= kp.n_run) break;
         const uint32_t x = order[e];
         if (states[x].status != 1) continue;
-        uint8_t *arena = kp.ws + arena_off[x];
-        const uint32_t bytes = ((const ArenaHdr *)arena)->bytes;
-        if (bytes <= kp.lds_bytes) run_experiment<true>(kp, x, arena, lds_dyn, sh);
-        else run_experiment<false>(kp, x, arena, lds_dyn, sh);
+        run_one<KIND>(kp, x, kp.ws + arena_off[x], lds_dyn, sh);
     }
 }
 
-/* Prepares a launch: resets the experiment queue counter. */
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel(KParams kp) { megakernel_body<0>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c8h(KParams kp) { megakernel_body<1>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c8w(KParams kp) { megakernel_body<2>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16h(KParams kp) { megakernel_body<3>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w(KParams kp) { megakernel_body<4>(kp); }
+
+static const void *kernel_of(uint32_t kind)
+{
+    switch (kind) {
+    case 0: return (const void *)msim_megakernel;
+    case 1: return (const void *)msim_megakernel_c8h;
+    case 2: return (const void *)msim_megakernel_c8w;
+    case 3: return (const void *)msim_megakernel_c16h;
+    default: return (const void *)msim_megakernel_c16w;
+    }
+}
+
+/* Prepares a launch: resets the experiment queue counters. */
 extern "C" __global__ void msim_prepare(KParams kp)
 {
-    if (threadIdx.x == 0 && blockIdx.x == 0) ((WsHdr *)kp.ws)->claim = 0;
+    if (blockIdx.x == 0 && threadIdx.x < MSIM_KINDS) ((WsHdr *)kp.ws)->claim[threadIdx.x] = 0;
 }
 
 /* Restores every experiment to tick 0: copies the pristine mutable part back
@@ -568,14 +1031,16 @@ extern "C" __global__ void msim_reset_kernel(KParams kp, uint64_t o_rec_all, uin
 
 /* --------------------------------------------------------- host launchers */
 
-extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t grid, uint32_t block, uint32_t lds,
-                                      hipStream_t stream)
+extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t kind, uint32_t grid, uint32_t block,
+                                      uint32_t lds, bool prepare, hipStream_t stream)
 {
-    hipLaunchKernelGGL(msim_prepare, dim3(1), dim3(64), 0, stream, *kp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(msim_megakernel, dim3(grid), dim3(block), lds, stream, *kp);
-    return hipGetLastError();
+    if (prepare) {
+        hipLaunchKernelGGL(msim_prepare, dim3(1), dim3(64), 0, stream, *kp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    void *args[] = {(void *)kp};
+    return hipLaunchKernel(kernel_of(kind), dim3(grid), dim3(block), args, lds, stream);
 }
 
 extern "C" hipError_t msim_launch_reset(const KParams *kp, uint64_t o_rec_all, uint64_t rec_words,
@@ -586,12 +1051,12 @@ extern "C" hipError_t msim_launch_reset(const KParams *kp, uint64_t o_rec_all, u
     return hipGetLastError();
 }
 
-extern "C" hipError_t msim_occupancy(uint32_t block, uint32_t lds, int *blocks_per_cu)
+extern "C" hipError_t msim_occupancy(uint32_t kind, uint32_t block, uint32_t lds, int *blocks_per_cu)
 {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, msim_megakernel, (int)block, lds);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kernel_of(kind), (int)block, lds);
 }
 
-extern "C" hipError_t msim_set_lds_limit(uint32_t lds)
+extern "C" hipError_t msim_set_lds_limit(uint32_t kind, uint32_t lds)
 {
-    return hipFuncSetAttribute((const void *)msim_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    return hipFuncSetAttribute(kernel_of(kind), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }

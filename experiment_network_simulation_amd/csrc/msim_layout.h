@@ -101,15 +101,67 @@ struct HostRW {          /* 32 bytes */
     uint32_t pend[4];    /* MSIM_MAX_RATE */
 };
 
-struct ArenaHdr {        /* 128 bytes, at the start of every arena */
+/* Two arena formats.  Both start with {mode, bytes, rw_off, n_flows}.
+ *  MODE_GENERAL: every datum in the arena (LDS or HBM placement), any thread
+ *    count (threads stride over ports); no size limits beyond the ABI's.
+ *  MODE_COMPACT: one thread per port; port-private state lives in registers
+ *    during a run (saved in the arena between runs); the state other threads
+ *    read is a compact image that is always copied into LDS. */
+#define MODE_GENERAL 1u
+#define MODE_COMPACT 2u
+
+struct ArenaHdr {        /* general format header */
+    uint32_t mode, bytes, rw_off, n_flows;
     uint32_t n_ports, n_hosts, n_conn, n_grp;
     uint32_t Q, W, R, n_voq;
-    uint32_t rw_off;     /* start of the mutable part */
-    uint32_t bytes;      /* whole arena */
-    uint32_t n_flows;
     uint32_t o_port, o_conn, o_grp, o_hout, o_host;
     uint32_t o_arr, o_phead, o_nslot, o_head, o_tslot, o_fcur, o_hseen;
     uint32_t o_pdesc, o_pnxt, o_fstk, o_pstate, o_scnt, o_sdesc, o_cstate, o_hstate, o_ready;
+};
+
+/* ---- compact format ------------------------------------------------------
+ * Thread slots: host ports 0..H-1, then switch ports SB..nt-1 (SB = H rounded
+ * up to a wavefront), so no wavefront mixes hosts and switches.  A switch's
+ * queue rows are rsz bytes (8 or 16): queue (i, o) of switch s is byte
+ * vbase + o*rsz + i of the popper-major arrays and vbase + i*rsz + o of the
+ * ingress-major ones. */
+
+#define C_POS_MASK 0x3FFFu   /* CRW2.s_st: flow position (14 bits) | state << 14 */
+#define C_STATE_SHIFT 14
+
+struct ArenaHdr2 {       /* 128 bytes */
+    uint32_t mode, bytes, rw_off, n_flows;
+    uint32_t lds_bytes;  /* [0, lds_bytes) is the LDS image */
+    uint32_t nt, H, SB;
+    uint32_t Q, W, R, n_conn;
+    uint32_t n_grp, rsz, dt, pad0;
+    uint32_t o_arr, o_head, o_nslot, o_pdesc, o_pnxt, o_popped, o_scnt, o_sdesc;
+    uint32_t o_route, o_cgrp, o_lidx, o_crw, o_grp, o_hout;
+    uint32_t o_port, o_priv;
+};
+
+struct CRW2 {            /* 8 bytes: compact connection cursors */
+    uint16_t s_st, s_rem, r_pos, r_rem;
+};
+
+struct PortRO2 {         /* 16 bytes, one per thread slot (HBM) */
+    uint32_t peer;       /* thread slot at the far end */
+    uint32_t vbase;      /* switch: first queue byte; host: first out-connection list entry */
+    uint16_t n_out;      /* host: outgoing connections */
+    uint8_t local, deg, rate, delay, flags, pad;
+};
+#define PF_ALIVE 1u
+#define PF_HOST 2u
+#define PF_PEER_HOST 4u
+#define PF_USED 8u
+
+struct PortPriv {        /* 144 bytes: registers of a thread slot between runs */
+    uint64_t tslot[2], fcur[2], hseen[2], phead[2], arrv[2];
+    uint64_t freem;      /* switch ingress: free buffer slots */
+    uint64_t ready;      /* host: connections with packets to send */
+    uint32_t popped, pushed, rr, pcnt;
+    uint32_t pend[4];
+    uint32_t left, pad[3];
 };
 
 /* per-experiment progress and totals (workspace, outside the arena) */
@@ -127,10 +179,12 @@ struct ExpState {        /* 64 bytes */
 };
 
 /* workspace header */
+#define MSIM_KINDS 5
+
 struct WsHdr {
-    uint32_t claim;      /* experiment queue counter of the running launch */
+    uint32_t claim[MSIM_KINDS]; /* experiment queue counters of a run, one per kernel kind */
     uint32_t n_exp;
-    uint32_t pad[62];
+    uint32_t pad[58];
 };
 
 struct KParams {
@@ -139,6 +193,8 @@ struct KParams {
     uint32_t n_exp;
     uint32_t max_ticks;
     uint32_t lds_bytes;  /* dynamic LDS available to an arena (0: HBM only) */
+    uint32_t order_base; /* this launch's experiments: order[order_base .. order_base + n_run) */
+    uint32_t n_run;
     uint32_t pad;
 };
 

@@ -55,7 +55,8 @@ class _Options(C.Structure):
 
 class _Info(C.Structure):
     _fields_ = [("n_exp", C.c_uint32), ("block_threads", C.c_uint32), ("grid_blocks", C.c_uint32),
-                ("lds_bytes", C.c_uint32), ("n_lds_exp", C.c_uint32), ("max_ports", C.c_uint32),
+                ("lds_bytes", C.c_uint32), ("n_lds_exp", C.c_uint32), ("n_compact", C.c_uint32),
+                ("pad", C.c_uint32), ("max_ports", C.c_uint32),
                 ("max_arena_bytes", C.c_uint64), ("total_flows", C.c_uint64), ("total_conns", C.c_uint64),
                 ("est_pkt_hops", C.c_uint64), ("est_delivered", C.c_uint64), ("workspace_bytes", C.c_uint64)]
 

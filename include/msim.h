@@ -200,7 +200,9 @@ typedef struct msim_info {
     uint32_t block_threads;      /* threads per workgroup (one workgroup simulates one experiment at a time) */
     uint32_t grid_blocks;        /* persistent workgroups launched by msim_run (0 before bind) */
     uint32_t lds_bytes;          /* dynamic LDS per workgroup (0: experiment state stays in HBM) */
-    uint32_t n_lds_exp;          /* experiments whose state fits in that LDS */
+    uint32_t n_lds_exp;          /* experiments whose state is worked on in LDS */
+    uint32_t n_compact;          /* of those, experiments on the compact path (one thread per port) */
+    uint32_t pad;
     uint32_t max_ports;          /* largest experiment: ports */
     uint64_t max_arena_bytes;    /* largest experiment: state bytes */
     uint64_t total_flows;        /* over the batch */

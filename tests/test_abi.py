@@ -40,7 +40,9 @@ def test_exports_every_declared_symbol(simmod):
 def test_create_reports_sizes(simmod):
     s = simmod.Sim(I.make_config(1))
     inf = s.info()
-    assert inf["n_exp"] == 16 and inf["block_threads"] == 64 and inf["max_ports"] == 16
+    # compact path: 8 host slots padded to a 64-wide wavefront, then 8 switch ports
+    assert inf["n_exp"] == 16 and inf["n_compact"] == 16 and inf["block_threads"] == 128
+    assert inf["max_ports"] == 16
     assert inf["est_pkt_hops"] == 16 * 7168 and inf["est_delivered"] == 16 * 3584
     assert s.workspace_bytes > 0
     assert [s.flow_count(e) for e in range(4)] == [896, 448, 224, 112]

@@ -134,12 +134,13 @@ def test_c3_full(simmod, oracle):
         assert_flows(s, e, of[e])
 
 
-def test_c4_sample(simmod, oracle):
+@pytest.mark.parametrize("force_global", [False, True])
+def test_c4_sample(simmod, oracle, force_global):
     """Two full-size k=8 fat-tree experiments (each ~93M packet-hops)."""
     ids = [2, 3]
     b = I.make_config(4, exp_ids=ids)
-    log("C4 sample", ids)
-    s, r = gpu_run(simmod, b, record=[0])
+    log("C4 sample", ids, "force_global", force_global)
+    s, r = gpu_run(simmod, b, record=[0], force_global=force_global)
     o = oracle_all(oracle, b, flows=False)
     for e in range(b.n_exp):
         assert_exp(r, e, o[e])
@@ -245,9 +246,9 @@ def test_edge_cases(simmod, oracle, force_global):
 
 @pytest.mark.parametrize("threads", [64, 256])
 def test_block_size_does_not_matter(simmod, oracle, threads):
-    """Fewer threads than ports (strided port loops) give the same results."""
+    """General path with fewer threads than ports (strided port loops)."""
     b = I.make_config(2, n_exp=6)
-    s, r = gpu_run(simmod, b, block_threads=threads)
+    s, r = gpu_run(simmod, b, block_threads=threads, force_global=True)
     o = oracle_all(oracle, b)
     for e in range(b.n_exp):
         assert_exp(r, e, o[e])
