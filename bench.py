@@ -61,7 +61,19 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=16, help="experiments in the CPU-oracle sample (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--force-global", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (calibrates HBM byte counters)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        src = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); experiments are "

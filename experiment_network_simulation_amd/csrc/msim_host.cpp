@@ -368,13 +368,25 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         }
         for (auto &cn : conn)
             if (grp[cn.grp].kind == GK_XFLOW) max_size = std::max<uint64_t>(max_size, cn.idx);
-        const uint32_t S = n_ports - n_hosts;
-        const uint32_t SB = ((n_hosts + 63) / 64) * 64, nt = SB + S;
+        /* thread slots: hosts first; each switch's ports consecutive inside one wavefront */
+        const uint32_t SB = ((n_hosts + 63) / 64) * 64;
+        std::vector<uint32_t> slot(n_ports), sw_of(nn, MSIM_NONE);
+        uint32_t nt = SB, n_sw = 0;
+        for (uint32_t n = 0; n < nn; n++) {
+            if (layer[n] == 0) { slot[pbase[n]] = host_of[n]; continue; }
+            if ((nt & 63) + deg[n] > 64) nt = (nt + 63) & ~63u;
+            sw_of[n] = n_sw++;
+            for (uint32_t q = pbase[n]; q < pbase[n + 1]; q++) slot[q] = nt++;
+        }
         const uint32_t rsz = maxdeg <= 8 ? 8 : 16, dt = nconn <= 4096 ? 2 : 4;
+        uint32_t max_ring = 0;
+        for (const Grp &g : grp) {
+            if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) max_ring = std::max(max_ring, g.S);
+            if (g.kind == GK_BCAST && g.N > 65535) max_ring = 1u << 20;   /* too long a chain for CGrp.N */
+        }
         if (nt <= 1024 && maxdeg <= 16 && Q <= 64 && max_out <= 64 && max_F <= C_POS_MASK && max_size < 65536 &&
-            nconn < (1u << (32 - DESC_SHIFT))) {
-            uint32_t n_sw = 0;
-            for (uint32_t n = 0; n < nn; n++) n_sw += layer[n] != 0;
+            max_ring < 1024 && ngrp <= 65535 && nconn < (1u << (32 - DESC_SHIFT))) {
+            const uint32_t S = nt - SB;                 /* switch slots, gaps included */
             const uint32_t Vc = n_sw * rsz * rsz;
             ArenaHdr2 H{};
             H.mode = MODE_COMPACT; H.n_flows = (uint32_t)n_flows;
@@ -384,16 +396,16 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             auto take = [&](uint32_t &field, size_t bytes) { field = (uint32_t)off; off = align16(off + bytes); };
             take(H.o_route, 4ull * nconn);
             take(H.o_cgrp, 2ull * nconn);
-            take(H.o_lidx, 2ull * nconn);
-            take(H.o_grp, sizeof(Grp) * ngrp);
-            take(H.o_hout, 4ull * nconn);
+            take(H.o_lidx, (size_t)nconn);
+            take(H.o_grp, sizeof(CGrp) * ngrp);
+            take(H.o_hout, (size_t)dt * nconn);
             H.rw_off = (uint32_t)off;
             take(H.o_arr, Vc);
             take(H.o_head, Vc);
             take(H.o_nslot, Vc);
             take(H.o_pdesc, (size_t)dt * S * Q);
             take(H.o_pnxt, (size_t)S * Q);
-            take(H.o_popped, 4ull * nt);
+            take(H.o_popped, 8ull * nt);
             take(H.o_scnt, (size_t)nt * W);
             take(H.o_sdesc, (size_t)dt * nt * W * R);
             take(H.o_crw, sizeof(CRW2) * nconn);
@@ -404,30 +416,38 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             if (H.lds_bytes <= COMPACT_LDS_LIMIT) {
                 out.arena.assign(off, 0);
                 uint8_t *A = out.arena.data();
-                /* thread slot of every port: hosts first, switches from SB */
-                std::vector<uint32_t> slot(n_ports), sw_of(nn, MSIM_NONE);
-                uint32_t sp = SB, nsw = 0;
-                for (uint32_t n = 0; n < nn; n++) {
-                    if (layer[n] == 0) { slot[pbase[n]] = host_of[n]; continue; }
-                    sw_of[n] = nsw++;
-                    for (uint32_t q = pbase[n]; q < pbase[n + 1]; q++) slot[q] = sp++;
-                }
                 uint32_t *route = (uint32_t *)(A + H.o_route);
                 uint16_t *cg = (uint16_t *)(A + H.o_cgrp);
-                uint16_t *li = (uint16_t *)(A + H.o_lidx);
+                uint8_t *li = A + H.o_lidx;
                 CRW2 *crw = (CRW2 *)(A + H.o_crw);
                 for (uint32_t c = 0; c < nconn; c++) {
                     route[c] = conn[c].route;
                     cg[c] = (uint16_t)conn[c].grp;
-                    li[c] = (uint16_t)conn[c].lidx;
+                    li[c] = (uint8_t)conn[c].lidx;
                     const Grp &g = grp[conn[c].grp];
                     uint32_t first = first_flow_size(g, conn[c].idx);
                     crw[c].r_rem = (uint16_t)first;
                     if (g.kind == GK_XFLOW) crw[c].s_rem = (uint16_t)first;
                 }
-                if (ngrp > 65535) return fail(out, MSIM_E_LIMIT, "experiment %u: too many groups", e);
-                if (ngrp) memcpy(A + H.o_grp, grp.data(), sizeof(Grp) * ngrp);
-                if (nconn) memcpy(A + H.o_hout, hout.data(), 4ull * nconn);
+                CGrp *cgt = (CGrp *)(A + H.o_grp);
+                for (uint32_t k = 0; k < ngrp; k++) {
+                    const Grp &g = grp[k];
+                    CGrp &o = cgt[k];
+                    o.kind = (uint16_t)g.kind;
+                    o.N = (uint16_t)g.N;
+                    o.S = g.S;
+                    o.R = g.R;
+                    o.fid_base = g.fid_base;
+                    o.conn_base = g.conn_base;
+                    o.mS = (uint32_t)(((1ull << 24) + g.S - 1) / g.S);
+                    if (g.kind == GK_BCAST) { o.p = g.p / g.S; o.Xq = g.p % g.S; o.Xr = 0; }
+                    else if (g.kind == GK_XFLOW) { o.p = 0; o.Xq = 0; o.Xr = 0; }
+                    else { o.p = g.p; o.Xq = g.X / g.N; o.Xr = g.X % g.N; }
+                }
+                for (uint32_t c = 0; c < nconn; c++) {
+                    if (dt == 2) ((uint16_t *)(A + H.o_hout))[c] = (uint16_t)hout[c];
+                    else ((uint32_t *)(A + H.o_hout))[c] = hout[c];
+                }
                 PortRO2 *pro = (PortRO2 *)(A + H.o_port);
                 PortPriv *pv = (PortPriv *)(A + H.o_priv);
                 for (uint32_t p = 0; p < n_ports; p++) {

@@ -578,43 +578,65 @@ __device__ __forceinline__ int first_from(uint64_t n0, uint64_t n1, uint32_t rr)
     return -1;
 }
 
+template <typename DT>
 struct CCtx {
     uint8_t *arr, *head, *nslot, *pnxt, *scnt;
-    uint32_t *popped;
-    const uint32_t *route, *hout;
-    const uint16_t *cgrp, *lidx;
+    uint32_t *popped;          /* [2][nt], tick parity */
+    const uint32_t *route;
+    const DT *hout;
+    const uint16_t *cgrp;
+    const uint8_t *lidx;
     CRW2 *crw;
-    const Grp *grp;
-    uint32_t *rec;
-    uint32_t Q, W, R, rsz, n_flows, SB;
-};
-
-template <typename DT>
-struct CBufs {
+    const CGrp *grp;
     DT *pdesc, *sdesc;
+    uint32_t *rec;
+    uint32_t Q, W, R, rsz, n_flows, SB, nt;
 };
 
-__device__ __forceinline__ uint32_t csize(const Grp &g, uint32_t idx, uint32_t pos)
+__device__ __forceinline__ uint32_t cdiv_S(const CGrp &g, uint32_t pos)
 {
-    if (g.kind == GK_BCAST) return g.p / g.S + (pos < g.p % g.S ? 1u : 0u);
-    uint32_t r = pos / g.S;
-    if (r + 1 < g.R) return g.p;
-    uint32_t k = ring_chunk(g.kind, g.N, idx, pos - r * g.S);
-    return g.X / g.N + (k < g.X % g.N ? 1u : 0u);
+    return __umulhi(pos << 8, g.mS);
 }
 
-__device__ __forceinline__ uint32_t cfid(const Grp &g, uint32_t idx, uint32_t pos)
+/* Chunk index rank i sends at step s (s < S): ring order, without division. */
+__device__ __forceinline__ uint32_t cchunk(const CGrp &g, uint32_t i, uint32_t s)
+{
+    const uint32_t N = g.N;
+    uint32_t v;
+    if (g.kind == GK_RING_AG || s < N - 1) v = i + N - s;            /* in [1, 2N) */
+    else v = i + 1 + N - (s - (N - 1));                              /* in [1, 2N] */
+    if (v >= N) v -= N;
+    if (v >= N) v -= N;
+    return v;
+}
+
+__device__ __forceinline__ uint32_t csize(const CGrp &g, uint32_t idx, uint32_t pos)
+{
+    if (g.kind == GK_BCAST) return g.p + (pos < g.Xq ? 1u : 0u);
+    const uint32_t r = cdiv_S(g, pos);
+    if (r + 1 < g.R) return g.p;
+    const uint32_t k = cchunk(g, idx, pos - r * g.S);
+    return g.Xq + (k < g.Xr ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t cfid(const CGrp &g, uint32_t idx, uint32_t pos)
 {
     if (g.kind == GK_XFLOW) return g.fid_base + idx;
     if (g.kind == GK_BCAST) return g.fid_base + idx * g.S + pos;
     return g.fid_base + pos * g.N + idx;
 }
 
-__device__ __forceinline__ bool crecv_ok(const CCtx &C, const Grp &g, uint32_t idx, uint32_t c, uint32_t pos)
+__device__ __forceinline__ uint32_t cflows(const CGrp &g)
+{
+    return g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
+}
+
+template <typename DT>
+__device__ __forceinline__ bool crecv_ok(const CCtx<DT> &C, const CGrp &g, uint32_t idx, uint32_t c, uint32_t pos)
 {
     if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
-        if (pos % g.S == 0) return true;
-        uint32_t cin = g.conn_base + (idx == 0 ? g.N - 1 : idx - 1);
+        if (pos - cdiv_S(g, pos) * g.S == 0) return true;
+        const uint32_t cin = g.conn_base + (idx == 0 ? g.N - 1u : idx - 1u);
         return C.crw[cin].r_pos >= pos;
     }
     if (g.kind == GK_BCAST) return idx == 0 || C.crw[c - 1].r_pos > pos;
@@ -626,8 +648,9 @@ struct HostRegs {
     uint32_t pcnt, p0, p1, p2, p3;
 };
 
-__device__ __forceinline__ void cactivate(const CCtx &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t pos,
-                                          const Grp &g, uint32_t idx, uint32_t t)
+template <typename DT>
+__device__ __forceinline__ void cactivate(const CCtx<DT> &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t pos,
+                                          const CGrp &g, uint32_t idx, uint32_t t)
 {
     C.crw[c].s_st = (uint16_t)(pos | (CS_ACTIVE << C_STATE_SHIFT));
     if (g.kind != GK_XFLOW) C.crw[c].s_rem = (uint16_t)csize(g, idx, pos);
@@ -636,45 +659,65 @@ __device__ __forceinline__ void cactivate(const CCtx &C, Acc &a, HostRegs &hr, u
     if (C.rec) C.rec[C.n_flows + cfid(g, idx, pos)] = t;
 }
 
-__device__ __forceinline__ void ccheck(const CCtx &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t t)
+template <typename DT>
+__device__ __forceinline__ void ccheck(const CCtx<DT> &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t t)
 {
-    const Grp g = C.grp[C.cgrp[c]];
+    const CGrp g = C.grp[C.cgrp[c]];
     const uint32_t idx = c - g.conn_base;
     const uint32_t pos = C.crw[c].s_st & C_POS_MASK;
-    if (pos >= flows_per_conn(g)) C.crw[c].s_st = (uint16_t)(pos | (CS_DONE << C_STATE_SHIFT));
+    if (pos >= cflows(g)) C.crw[c].s_st = (uint16_t)(pos | (CS_DONE << C_STATE_SHIFT));
     else if (crecv_ok(C, g, idx, c, pos)) cactivate(C, a, hr, c, pos, g, idx, t);
     else C.crw[c].s_st = (uint16_t)(pos | (CS_IDLE << C_STATE_SHIFT));
 }
 
 template <typename DT>
-__device__ __forceinline__ void ctransmit(const CCtx &C, const CBufs<DT> &B, Acc &a, const PortRO2 &pr,
-                                          uint32_t desc, uint32_t t, uint32_t slot)
+__device__ __forceinline__ void ctransmit(const CCtx<DT> &C, Acc &a, const PortRO2 &pr, uint32_t desc, uint32_t t,
+                                          uint32_t slot)
 {
     uint32_t s2 = slot + pr.delay;
     if (s2 >= C.W) s2 -= C.W;
     const uint32_t si = pr.peer * C.W + s2;
     const uint32_t k = C.scnt[si];
     C.scnt[si] = (uint8_t)(k + 1);
-    B.sdesc[si * C.R + k] = (DT)desc;
+    C.sdesc[si * C.R + k] = (DT)desc;
     a.hops++;
     a.last_tx1 = t + 1;
     a.max_arr = max(a.max_arr, t + pr.delay);
 }
 
+/* Orders this wavefront's LDS accesses (lanes of one switch talk through LDS
+ * inside a tick; a wavefront's LDS operations execute in issue order). */
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+/*
+ * One tick t of a compact experiment, per wavefront, with one workgroup
+ * barrier at its end:
+ *   arrivals    switch ingress: packets with arrival tick t join their queue;
+ *               host: deliveries, then activations (Schedule);
+ *   forwarding  every output pulls while credit lasts (credit from the far
+ *               ingress's popped count through t-1, published last tick);
+ *   frees       switch ingress: releases the slots its egresses popped during
+ *               this tick and publishes its popped count for tick t+1.
+ * Arrivals read staging written at least one barrier earlier (delay >= 1);
+ * forwarding reads queues filled by the arrivals of the same switch (same
+ * wavefront); the frees read heads advanced by the same switch's outputs.
+ */
 template <int W, typename DT>
 __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
 {
     const uint32_t tid = threadIdx.x, nth = blockDim.x;
     const uint32_t lane = tid & 63, wave = tid >> 6, nwaves = (nth + 63) >> 6;
     ExpState *stp = (ExpState *)(kp.ws + kp.o_state) + x;
-    const ArenaHdr2 *HG = (const ArenaHdr2 *)arena_g;
-    const uint32_t lds_bytes = HG->lds_bytes, rw_off = HG->rw_off;
+    const ArenaHdr2 *H = (const ArenaHdr2 *)arena_g;
+    const uint32_t lds_bytes = H->lds_bytes, rw_off = H->rw_off;
     {
         const uint4 *src = (const uint4 *)arena_g;
         uint4 *dst = (uint4 *)lds;
         for (uint32_t i = tid; i < lds_bytes / 16; i += nth) dst[i] = src[i];
     }
-    const ArenaHdr2 *H = (const ArenaHdr2 *)arena_g;
     const uint32_t nt = H->nt, nh = H->H, SB = H->SB;
     const bool used = tid < nt;
     PortRO2 pr = {};
@@ -683,7 +726,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         pr = ((const PortRO2 *)(arena_g + H->o_port))[tid];
         pv = ((const PortPriv *)(arena_g + H->o_priv))[tid];
     }
-    CCtx C;
+    CCtx<DT> C;
     C.arr = lds + H->o_arr;
     C.head = lds + H->o_head;
     C.nslot = lds + H->o_nslot;
@@ -691,29 +734,28 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     C.scnt = lds + H->o_scnt;
     C.popped = (uint32_t *)(lds + H->o_popped);
     C.route = (const uint32_t *)(lds + H->o_route);
-    C.hout = (const uint32_t *)(lds + H->o_hout);
+    C.hout = (const DT *)(lds + H->o_hout);
     C.cgrp = (const uint16_t *)(lds + H->o_cgrp);
-    C.lidx = (const uint16_t *)(lds + H->o_lidx);
+    C.lidx = (const uint8_t *)(lds + H->o_lidx);
     C.crw = (CRW2 *)(lds + H->o_crw);
-    C.grp = (const Grp *)(lds + H->o_grp);
+    C.grp = (const CGrp *)(lds + H->o_grp);
+    C.pdesc = (DT *)(lds + H->o_pdesc);
+    C.sdesc = (DT *)(lds + H->o_sdesc);
     C.Q = H->Q;
     C.W = H->W;
     C.R = H->R;
     C.rsz = H->rsz;
     C.n_flows = H->n_flows;
     C.SB = SB;
-    CBufs<DT> B;
-    B.pdesc = (DT *)(lds + H->o_pdesc);
-    B.sdesc = (DT *)(lds + H->o_sdesc);
+    C.nt = nt;
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
-    const bool is_host = tid < nh;
-    const bool is_sw = tid >= SB && used;
+    const bool is_host = tid < nh && (pr.flags & PF_USED);
+    const bool is_sw = tid >= SB && (pr.flags & PF_USED);
     const bool alive = pr.flags & PF_ALIVE;
     const bool peer_host = pr.flags & PF_PEER_HOST;
     const uint32_t deg = pr.deg, local = pr.local, Q = C.Q, rsz = C.rsz;
-    /* registers */
     Row<W> tslot, fcur, hseen, phead, arrv;
     tslot.w0 = pv.tslot[0]; tslot.w1 = pv.tslot[1];
     fcur.w0 = pv.fcur[0]; fcur.w1 = pv.fcur[1];
@@ -744,41 +786,19 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     bool done = false, dead = false;
     uint32_t t_dead = 0;
     while (t < t_end) {
-        /* ---------------- phase A */
+        const uint32_t tp = (t & 1u) * nt;
+        /* ---------------- arrivals */
         if (is_sw) {
-            Row<W> hd;
-            hd.load(C.head + rowp);
-            uint64_t d0 = bytes_sub(hd.w0, hseen.w0);
-            uint64_t d1 = W == 2 ? bytes_sub(hd.w1, hseen.w1) : 0ull;
-            if (d0 | d1) {
-                uint64_t m0 = bytes_nz(d0), m1 = bytes_nz(d1);
-                while (m0 | m1) {
-                    uint32_t o;
-                    if (m0) { o = __builtin_ctzll(m0) >> 3; m0 &= m0 - 1; }
-                    else { o = 8 + (__builtin_ctzll(m1) >> 3); m1 &= m1 - 1; }
-                    uint32_t k = (uint32_t)((o < 8 ? d0 : d1) >> (8 * (o & 7))) & 0xFFu;
-                    popped += k;
-                    uint32_t f = fcur.get(o);
-                    for (uint32_t j = 0; j < k; j++) {
-                        uint32_t s = f;
-                        f = C.pnxt[pool + s];
-                        freem |= 1ull << s;
-                    }
-                    fcur.set(o, f);
-                }
-                hseen = hd;
-                C.popped[tid] = popped;
-            }
             const uint32_t si = tid * C.W + slot;
             const uint32_t n = C.scnt[si];
             for (uint32_t k = 0; k < n; k++) {
-                const uint32_t desc = B.sdesc[si * C.R + k];
+                const uint32_t desc = C.sdesc[si * C.R + k];
                 const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
                 const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
                 if (freem == 0 || o >= deg) { a.fault = 1; continue; }
                 const uint32_t s = __builtin_ctzll(freem);
                 freem &= freem - 1;
-                B.pdesc[pool + s] = (DT)(desc + 1);
+                C.pdesc[pool + s] = (DT)(desc + 1);
                 const uint32_t av = arrv.get(o);
                 const uint32_t vp = pr.vbase + o * rsz + local;
                 if (av == hseen.get(o)) {
@@ -796,13 +816,13 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             const uint32_t si = tid * C.W + slot;
             const uint32_t n = C.scnt[si];
             for (uint32_t k = 0; k < n; k++) {
-                const uint32_t c = (uint32_t)B.sdesc[si * C.R + k] >> DESC_SHIFT;
+                const uint32_t c = (uint32_t)C.sdesc[si * C.R + k] >> DESC_SHIFT;
                 CRW2 &cw = C.crw[c];
                 a.delivered++;
                 const uint32_t rem = cw.r_rem - 1u;
                 cw.r_rem = (uint16_t)rem;
                 if (rem) continue;
-                const Grp g = C.grp[C.cgrp[c]];
+                const CGrp g = C.grp[C.cgrp[c]];
                 const uint32_t idx = c - g.conn_base;
                 uint32_t pos = cw.r_pos;
                 const uint32_t fid = cfid(g, idx, pos);
@@ -812,10 +832,10 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 if (C.rec) C.rec[fid] = t;
                 pos++;
                 cw.r_pos = (uint16_t)pos;
-                if (pos < flows_per_conn(g)) cw.r_rem = (uint16_t)csize(g, idx, pos);
+                if (pos < cflows(g)) cw.r_rem = (uint16_t)csize(g, idx, pos);
                 uint32_t d = MSIM_NONE;
-                if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) d = g.conn_base + (idx + 1 == g.N ? 0 : idx + 1);
-                else if (g.kind == GK_BCAST && idx + 1 < g.N) d = c + 1;
+                if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) d = g.conn_base + (idx + 1u == g.N ? 0u : idx + 1u);
+                else if (g.kind == GK_BCAST && idx + 1u < g.N) d = c + 1;
                 if (d != MSIM_NONE && (C.crw[d].s_st >> C_STATE_SHIFT) == CS_IDLE) {
                     const uint32_t dpos = C.crw[d].s_st & C_POS_MASK;
                     const uint32_t didx = d - g.conn_base;
@@ -824,7 +844,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             }
             if (n) C.scnt[si] = 0;
             if (t == 0) {
-                for (uint32_t j = 0; j < pr.n_out; j++) ccheck(C, a, hr, C.hout[pr.vbase + j], t);
+                for (uint32_t j = 0; j < pr.n_out; j++) ccheck(C, a, hr, (uint32_t)C.hout[pr.vbase + j], t);
             } else if (hr.pcnt) {
                 ccheck(C, a, hr, hr.p0, t);
                 if (hr.pcnt > 1) ccheck(C, a, hr, hr.p1, t);
@@ -833,12 +853,12 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 hr.pcnt = 0;
             }
         }
-        __syncthreads();
-        /* ---------------- phase D */
+        wave_lds_fence();
+        /* ---------------- forwarding */
         if (is_sw && alive) {
             Row<W> ar;
             ar.load(C.arr + rowp);
-            int32_t credit = peer_host ? (int32_t)pr.rate : (int32_t)Q - (int32_t)(pushed - C.popped[pr.peer]);
+            int32_t credit = peer_host ? (int32_t)pr.rate : (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
             uint64_t v0 = bytes_sub(ar.w0, phead.w0);
             uint64_t v1 = W == 2 ? bytes_sub(ar.w1, phead.w1) : 0ull;
             for (uint32_t m = 0; m < pr.rate && credit > 0; m++) {
@@ -847,7 +867,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 const uint32_t vp = rowp + (uint32_t)i;
                 const uint32_t qpool = (qbase + (uint32_t)i - SB) * Q;
                 const uint32_t s = C.nslot[vp];
-                const uint32_t desc = B.pdesc[qpool + s];
+                const uint32_t desc = C.pdesc[qpool + s];
                 C.nslot[vp] = C.pnxt[qpool + s];
                 const uint32_t hb = phead.get((uint32_t)i) + 1;
                 phead.set((uint32_t)i, hb);
@@ -855,17 +875,17 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 if (i < 8) v0 -= 1ull << (8 * i);
                 else v1 -= 1ull << (8 * (i - 8));
                 rr = (uint32_t)i + 1 == deg ? 0 : (uint32_t)i + 1;
-                ctransmit(C, B, a, pr, desc, t, slot);
+                ctransmit(C, a, pr, desc, t, slot);
                 pushed++;
                 credit--;
             }
         } else if (is_host && alive && pr.n_out) {
-            int32_t credit = (int32_t)Q - (int32_t)(pushed - C.popped[pr.peer]);
+            int32_t credit = (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
             for (uint32_t m = 0; m < pr.rate && credit > 0 && hr.ready; m++) {
                 const uint64_t rot = rr ? (hr.ready >> rr) | (hr.ready << (64 - rr)) : hr.ready;
                 const uint32_t j = (rr + (uint32_t)__builtin_ctzll(rot)) & 63u;
                 const uint32_t c = C.hout[pr.vbase + j];
-                ctransmit(C, B, a, pr, c << DESC_SHIFT, t, slot);
+                ctransmit(C, a, pr, c << DESC_SHIFT, t, slot);
                 pushed++;
                 credit--;
                 rr = j + 1 == pr.n_out ? 0 : j + 1;
@@ -876,7 +896,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     hr.ready &= ~(1ull << j);
                     const uint32_t pos = cw.s_st & C_POS_MASK;
                     if (C.rec) {
-                        const Grp g = C.grp[C.cgrp[c]];
+                        const CGrp g = C.grp[C.cgrp[c]];
                         C.rec[2 * C.n_flows + cfid(g, c - g.conn_base, pos)] = t + 1;
                     }
                     cw.s_st = (uint16_t)(pos + 1);
@@ -887,6 +907,33 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     hr.pcnt++;
                 }
             }
+        }
+        wave_lds_fence();
+        /* ---------------- frees, and the popped count for tick t+1 */
+        if (is_sw) {
+            Row<W> hd;
+            hd.load(C.head + rowp);
+            uint64_t d0 = bytes_sub(hd.w0, hseen.w0);
+            uint64_t d1 = W == 2 ? bytes_sub(hd.w1, hseen.w1) : 0ull;
+            if (d0 | d1) {
+                uint64_t m0 = bytes_nz(d0), m1 = bytes_nz(d1);
+                while (m0 | m1) {
+                    uint32_t o;
+                    if (m0) { o = __builtin_ctzll(m0) >> 3; m0 &= m0 - 1; }
+                    else { o = 8 + (__builtin_ctzll(m1) >> 3); m1 &= m1 - 1; }
+                    const uint32_t k = (uint32_t)((o < 8 ? d0 : d1) >> (8 * (o & 7))) & 0xFFu;
+                    popped += k;
+                    uint32_t f = fcur.get(o);
+                    for (uint32_t j = 0; j < k; j++) {
+                        const uint32_t s = f;
+                        f = C.pnxt[pool + s];
+                        freem |= 1ull << s;
+                    }
+                    fcur.set(o, f);
+                }
+                hseen = hd;
+            }
+            C.popped[(tp ^ nt) + tid] = popped;
         }
         t++;
         slot = slot + 1 == C.W ? 0 : slot + 1;

@@ -120,8 +120,10 @@ struct ArenaHdr {        /* general format header */
 };
 
 /* ---- compact format ------------------------------------------------------
- * Thread slots: host ports 0..H-1, then switch ports SB..nt-1 (SB = H rounded
- * up to a wavefront), so no wavefront mixes hosts and switches.  A switch's
+ * Thread slots: host ports 0..H-1, then switch ports from SB (H rounded up to a
+ * wavefront); a switch's ports are consecutive and never straddle two
+ * wavefronts, so everything a switch's ports exchange inside a tick stays in
+ * one wavefront and a tick needs a single workgroup barrier.  A switch's
  * queue rows are rsz bytes (8 or 16): queue (i, o) of switch s is byte
  * vbase + o*rsz + i of the popper-major arrays and vbase + i*rsz + o of the
  * ingress-major ones. */
@@ -138,6 +140,24 @@ struct ArenaHdr2 {       /* 128 bytes */
     uint32_t o_arr, o_head, o_nslot, o_pdesc, o_pnxt, o_popped, o_scnt, o_sdesc;
     uint32_t o_route, o_cgrp, o_lidx, o_crw, o_grp, o_hout;
     uint32_t o_port, o_priv;
+};
+/* popped (switch ingress: packets forwarded out of it) is published twice,
+ * indexed by tick parity: [(t&1) * nt + slot] holds the count through tick t-1
+ * and is written at the end of tick t-1, so tick t's readers in other
+ * wavefronts never see a value being overwritten. */
+
+/* Collective group as the compact path reads it: the constant quotients of
+ * the flow-size rules are precomputed, and pos / S is umulhi(pos << 8, mS),
+ * exact for pos < 2^14 and S < 2^10. */
+struct CGrp {            /* 36 bytes */
+    uint16_t kind, N;    /* ring members; broadcast hops; explicit: flow count (low 16 bits) */
+    uint32_t S;          /* ring: steps per round; broadcast: partitions K */
+    uint32_t R;          /* ring: rounds */
+    uint32_t p;          /* ring: chunk packets; broadcast: packets / K */
+    uint32_t Xq;         /* ring: last-round packets / N; broadcast: packets mod K */
+    uint32_t Xr;         /* ring: last-round packets mod N */
+    uint32_t fid_base, conn_base;
+    uint32_t mS;         /* ceil(2^24 / S) */
 };
 
 struct CRW2 {            /* 8 bytes: compact connection cursors */

@@ -154,30 +154,31 @@ def leaf_spine(n_leaf: int, hosts_per_leaf: int, n_spine: int, host_rate: int = 
 
 
 def fat_tree(k: int, rate: int = 1, delay: int = 1, oversub: int = 1) -> Topology:
-    """Standard k-ary fat-tree (k pods; k/2 edge and k/2 agg switches per pod;
-    (k/2)^2 cores).  Host id = pod*k^2/4 + edge*k/2 + i.  Edge ports 0..k/2-1 face
-    its hosts, then its aggs; agg ports 0..k/2-1 face the pod's edges, then its
-    cores; core c = a*(k/2)+j attaches to agg a of every pod, core port = pod.
-    With oversub o, edge e keeps only the aggs a with (a - e) mod (k/2) < (k/2)/o."""
+    """k-ary fat-tree: k pods of k/2 edge switches, each edge switch serving k/2
+    hosts (host id = pod*k^2/4 + edge*k/2 + i).  With oversubscription o each pod
+    keeps a = k/(2o) aggregation switches, every edge switch links to all of
+    them (k/2 host ports, a uplinks: o:1 at the edge layer) and aggregation
+    switch j of every pod links to the k/2 core switches of group j.  o = 1 is
+    the standard fat-tree.  Ports: edge 0..k/2-1 hosts, then aggs; agg 0..k/2-1
+    edges, then cores; core port = pod.  Node order: hosts, edges, aggs, cores."""
     h2 = k // 2
+    na = h2 // oversub
     H = k * h2 * h2
-    n_edge = k * h2
-    edge0, agg0 = H, H + n_edge
-    core0 = agg0 + n_edge
-    layers = [LAYER_HOST] * H + [1] * n_edge + [2] * n_edge + [3] * (h2 * h2)
+    edge0 = H
+    agg0 = edge0 + k * h2
+    core0 = agg0 + k * na
+    layers = [LAYER_HOST] * H + [1] * (k * h2) + [2] * (k * na) + [3] * (na * h2)
     cables = []
     for h in range(H):
         cables.append((h, edge0 + h // h2, rate, rate, delay, 1))
-    keep = h2 // oversub
     for p in range(k):
         for e in range(h2):
-            for a in range(h2):
-                if (a - e) % h2 < keep:
-                    cables.append((edge0 + p * h2 + e, agg0 + p * h2 + a, rate, rate, delay, 1))
+            for a in range(na):
+                cables.append((edge0 + p * h2 + e, agg0 + p * na + a, rate, rate, delay, 1))
     for p in range(k):
-        for a in range(h2):
+        for a in range(na):
             for j in range(h2):
-                cables.append((agg0 + p * h2 + a, core0 + a * h2 + j, rate, rate, delay, 1))
+                cables.append((agg0 + p * na + a, core0 + a * h2 + j, rate, rate, delay, 1))
     return topology_from_cables(layers, cables, f"fattree{k}o{oversub}")
 
 

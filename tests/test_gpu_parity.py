@@ -147,6 +147,20 @@ def test_c4_sample(simmod, oracle, force_global):
     assert_flows(s, 0, oracle.run(b, 0, flows=True))
 
 
+def test_c5_sample(simmod, oracle):
+    """Three full-size k=16 fat-tree experiments (one per oversubscription
+    level, 6144 ports and 521,216 Zipf all-to-all flows each) on the general
+    path, state in HBM."""
+    b = I.make_config(5, exp_ids=[0, 1, 3])
+    assert sorted(x.topo for x in b.exps) == [0, 1, 2]
+    log("C5 sample", [(x.topo, x.queue_pkts) for x in b.exps])
+    s, r = gpu_run(simmod, b, record=[0])
+    o = oracle_all(oracle, b, flows=False)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+    assert_flows(s, 0, oracle.run(b, 0, flows=True))
+
+
 # ------------------------------------------------------------ semantics
 
 def test_resume_equals_single_run(simmod, oracle):

@@ -348,3 +348,22 @@ def test_fat_tree_failures_stay_routable(oracle):
             for p in row:
                 if p != 0xFFFFFFFF:
                     assert table[p]["alive"]
+
+
+@pytest.mark.parametrize("o", [1, 2, 4])
+def test_oversubscribed_fat_tree_shape_and_routes(oracle, o):
+    """k=16 fat-tree with oversubscription o: k/2 host ports and k/(2o) uplinks
+    per edge switch, every host pair reachable on a shortest up/down path."""
+    k = 16
+    t = I.fat_tree(k, oversub=o)
+    deg = np.bincount(np.concatenate([t.cable_a, t.cable_b]), minlength=t.n_nodes)
+    H = k * (k // 2) ** 2
+    edges = range(H, H + k * k // 2)
+    assert all(deg[e] == k // 2 + k // (2 * o) for e in edges)
+    rng = np.random.default_rng(o)
+    pairs = [(int(a), int(b)) for a, b in rng.integers(0, H, (40, 2)) if a != b]
+    b = I.single_batch(t, I.xflows([(a, c, 1) for a, c in pairs]), queue_pkts=16, ecmp_seed=o)
+    rc, pth = oracle.paths(b, 0)
+    assert rc == 0
+    for i, (a, c) in enumerate(pairs):
+        assert pth["links"][i] == updown_distance(t, a, c)
