@@ -51,6 +51,26 @@ def cpu_baseline(batch, gpu_res, sample_ids, threads):
     return hops / dt, dt, hops, ok
 
 
+def measured_traffic(kernel: str, workload_cfg: int, n: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on this kernel source and this workload; else None."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        rec = json.load(open(os.path.join(here, "profiles", "traffic.json")))
+    except (OSError, ValueError):
+        return None
+    csrc = os.path.join(here, "experiment_network_simulation_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("msim_kernel.hip", "msim_layout.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if rec.get("kernel") != kernel or rec.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    if workload_cfg != 4 or n != 4096:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,7 +103,7 @@ def main():
     import numpy as np
     import torch
     from experiment_network_simulation_amd import inputs as I
-    from experiment_network_simulation_amd.sim import Sim
+    from experiment_network_simulation_amd.sim import KERNEL_NAMES, Sim
 
     cid = args.config
     n = args.n_exp or I.FULL_E[cid]
@@ -98,7 +118,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    t = time.perf_counter()
     sim.bind(device="cuda:0", stream=stream)
+    log(f"[bench] bind (upload + reset) {time.perf_counter() - t:.2f}s")
     info = sim.info()
     log(f"[bench] bound: grid {info['grid_blocks']} x {info['block_threads']} threads, lds {info['lds_bytes']} B "
         f"({info['n_lds_exp']} experiments in LDS), workspace {info['workspace_bytes'] / 2**20:.0f} MiB")
@@ -186,8 +208,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "kernel": "msim_megakernel",
+            "traffic": measured_traffic(KERNEL_NAMES[info["main_kernel"]], cid, n),
+            "kernel": KERNEL_NAMES[info["main_kernel"]],
             "kernel_ms_avg": k_avg_s * 1e3,
             "alg_bytes_per_launch": alg_bytes,
         },

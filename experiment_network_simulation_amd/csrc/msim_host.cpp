@@ -695,6 +695,7 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
     for (uint32_t k = 0; k < MSIM_KINDS; k++)
         if (ctx->k_count[k] > ctx->k_count[main_kind]) main_kind = k;
     ctx->block = ctx->k_block[main_kind];
+    I.main_kernel = main_kind;
     const uint32_t bt = ctx->block;
     I.n_exp = E;
     I.block_threads = bt;

@@ -22,6 +22,9 @@ E_INVALID_SPEC, E_UNROUTABLE, E_WORKSPACE, E_HIP, E_ARG, E_STATE, E_LIMIT = -1, 
 EXP_DONE, EXP_INCOMPLETE, EXP_DEADLOCK = 0, 1, 2
 NONE = 0xFFFFFFFF
 
+KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h", "msim_megakernel_c8w", "msim_megakernel_c16h",
+                "msim_megakernel_c16w"]
+
 EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_reset", "msim_results",
             "msim_flow_count", "msim_flow_ticks", "msim_get_info", "msim_last_error", "msim_destroy"]
 
@@ -56,7 +59,7 @@ class _Options(C.Structure):
 class _Info(C.Structure):
     _fields_ = [("n_exp", C.c_uint32), ("block_threads", C.c_uint32), ("grid_blocks", C.c_uint32),
                 ("lds_bytes", C.c_uint32), ("n_lds_exp", C.c_uint32), ("n_compact", C.c_uint32),
-                ("pad", C.c_uint32), ("max_ports", C.c_uint32),
+                ("main_kernel", C.c_uint32), ("max_ports", C.c_uint32),
                 ("max_arena_bytes", C.c_uint64), ("total_flows", C.c_uint64), ("total_conns", C.c_uint64),
                 ("est_pkt_hops", C.c_uint64), ("est_delivered", C.c_uint64), ("workspace_bytes", C.c_uint64)]
 

@@ -202,7 +202,9 @@ typedef struct msim_info {
     uint32_t lds_bytes;          /* dynamic LDS per workgroup (0: experiment state stays in HBM) */
     uint32_t n_lds_exp;          /* experiments whose state is worked on in LDS */
     uint32_t n_compact;          /* of those, experiments on the compact path (one thread per port) */
-    uint32_t pad;
+    uint32_t main_kernel;        /* kernel running most experiments: 0 msim_megakernel (general path),
+                                    1..4 msim_megakernel_c8h / _c8w / _c16h / _c16w (compact path,
+                                    8- or 16-byte queue rows, 16- or 32-bit packet descriptors) */
     uint32_t max_ports;          /* largest experiment: ports */
     uint64_t max_arena_bytes;    /* largest experiment: state bytes */
     uint64_t total_flows;        /* over the batch */

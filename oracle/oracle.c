@@ -80,6 +80,14 @@
  *  flows by (channel, round, step, rank); a broadcast by hop, and (hop, part).
  *  Digest = sum over flows of mix64((flow << 32) | RD) mod 2^64, mix64 being
  *  SplitMix64's output function.
+ *
+ * Pins (tests/test_oracle_pins.py): closed forms for a single flow, NC = 1
+ * rings and the pipelined broadcast; four hand traces; conservation, per-flow
+ * bounds and route lengths against an independent breadth-first search.
+ * Parity unpinned (the pages fix no value): which of several equal-cost ECMP
+ * candidates the hash picks (only validity and length of a route are pinned),
+ * the digest mixer (a checksum; per-flow ticks are compared as well), and the
+ * DEADLOCK status (no valid input reaches it under up/down routing).
  */
 #include <stdint.h>
 #include <stdlib.h>
