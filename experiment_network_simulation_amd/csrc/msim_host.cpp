@@ -46,7 +46,7 @@ struct Compiled {
     std::vector<uint8_t> arena;  /* RO + initial RW image, size multiple of 16 */
     uint32_t rw_off = 0, bytes = 0, lds_bytes = 0;
     bool compact = false;
-    uint32_t kind = 0;     /* kernel kind: 0 general; compact 1 + (16-byte rows ? 2 : 0) + (32-bit descriptors ? 1 : 0) */
+    uint32_t kind = 0;     /* kernel kind: 0 general; compact 1 + (16-byte rows << 2 | 32-bit descriptors << 1 | rate > 1) */
     uint32_t nt = 0;       /* compact: thread slots */
     uint64_t n_flows = 0, n_conns = 0, n_ports = 0;
     uint64_t est_hops = 0, est_delivered = 0;
@@ -406,8 +406,9 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             take(H.o_pdesc, (size_t)dt * S * Q);
             take(H.o_pnxt, (size_t)S * Q);
             take(H.o_popped, 8ull * nt);
-            take(H.o_scnt, (size_t)nt * W);
-            take(H.o_sdesc, (size_t)dt * nt * W * R);
+            const uint32_t RP = R <= 1 ? 1 : (R <= 2 ? 2 : 4);
+            H.o_scnt = 0;
+            take(H.o_sdesc, (size_t)dt * nt * W * RP);
             take(H.o_crw, sizeof(CRW2) * nconn);
             H.lds_bytes = (uint32_t)off;
             take(H.o_port, sizeof(PortRO2) * nt);
@@ -475,7 +476,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                 out.bytes = H.bytes;
                 out.lds_bytes = H.lds_bytes;
                 out.compact = true;
-                out.kind = 1 + (rsz == 16 ? 2u : 0u) + (dt == 4 ? 1u : 0u);
+                out.kind = 1 + ((rsz == 16 ? 4u : 0u) | (dt == 4 ? 2u : 0u) | (R > 1 ? 1u : 0u));
                 out.nt = nt;
                 return MSIM_OK;
             }

@@ -34,6 +34,8 @@
  */
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "msim_layout.h"
 
 #define CHECK_EVERY 16u
@@ -580,7 +582,7 @@ __device__ __forceinline__ int first_from(uint64_t n0, uint64_t n1, uint32_t rr)
 
 template <typename DT>
 struct CCtx {
-    uint8_t *arr, *head, *nslot, *pnxt, *scnt;
+    uint8_t *arr, *head, *nslot, *pnxt;
     uint32_t *popped;          /* [2][nt], tick parity */
     const uint32_t *route;
     const DT *hout;
@@ -591,6 +593,8 @@ struct CCtx {
     DT *pdesc, *sdesc;
     uint32_t *rec;
     uint32_t Q, W, R, rsz, n_flows, SB, nt;
+    uint32_t RP;               /* staging entries per (tick slot, port): R rounded up to 1, 2 or 4 */
+    uint32_t S;                /* switch thread slots; pools are slot-major: [buffer slot][S] */
 };
 
 __device__ __forceinline__ uint32_t cdiv_S(const CGrp &g, uint32_t pos)
@@ -670,26 +674,28 @@ __device__ __forceinline__ void ccheck(const CCtx<DT> &C, Acc &a, HostRegs &hr, 
     else C.crw[c].s_st = (uint16_t)(pos | (CS_IDLE << C_STATE_SHIFT));
 }
 
+/* Stages the m-th packet this output sends in tick t for arrival at t + delay:
+ * entry m of the far port's record for that tick slot holds desc + 1 (0 means
+ * empty), so the sender never reads the record. */
 template <typename DT>
 __device__ __forceinline__ void ctransmit(const CCtx<DT> &C, Acc &a, const PortRO2 &pr, uint32_t desc, uint32_t t,
-                                          uint32_t slot)
+                                          uint32_t slot, uint32_t m)
 {
     uint32_t s2 = slot + pr.delay;
     if (s2 >= C.W) s2 -= C.W;
-    const uint32_t si = pr.peer * C.W + s2;
-    const uint32_t k = C.scnt[si];
-    C.scnt[si] = (uint8_t)(k + 1);
-    C.sdesc[si * C.R + k] = (DT)desc;
+    C.sdesc[(s2 * C.nt + pr.peer) * C.RP + m] = (DT)(desc + 1);
     a.hops++;
     a.last_tx1 = t + 1;
     a.max_arr = max(a.max_arr, t + pr.delay);
 }
 
-/* Orders this wavefront's LDS accesses (lanes of one switch talk through LDS
- * inside a tick; a wavefront's LDS operations execute in issue order). */
+/* Keeps the compiler from moving LDS accesses across a phase boundary.  Lanes
+ * of one switch talk through LDS inside a tick; the LDS executes a wavefront's
+ * instructions in issue order, so no hardware wait is needed, only program
+ * order. */
 __device__ __forceinline__ void wave_lds_fence()
 {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    asm volatile("" ::: "memory");
 }
 
 /*
@@ -705,7 +711,7 @@ __device__ __forceinline__ void wave_lds_fence()
  * forwarding reads queues filled by the arrivals of the same switch (same
  * wavefront); the frees read heads advanced by the same switch's outputs.
  */
-template <int W, typename DT>
+template <int W, typename DT, bool R1>
 __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
 {
     const uint32_t tid = threadIdx.x, nth = blockDim.x;
@@ -731,7 +737,6 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     C.head = lds + H->o_head;
     C.nslot = lds + H->o_nslot;
     C.pnxt = lds + H->o_pnxt;
-    C.scnt = lds + H->o_scnt;
     C.popped = (uint32_t *)(lds + H->o_popped);
     C.route = (const uint32_t *)(lds + H->o_route);
     C.hout = (const DT *)(lds + H->o_hout);
@@ -748,6 +753,8 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     C.n_flows = H->n_flows;
     C.SB = SB;
     C.nt = nt;
+    C.RP = H->R <= 1 ? 1u : (H->R <= 2 ? 2u : 4u);
+    C.S = nt - SB;
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
@@ -768,7 +775,8 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     hr.ready = pv.ready;
     hr.pcnt = pv.pcnt;
     hr.p0 = pv.pend[0]; hr.p1 = pv.pend[1]; hr.p2 = pv.pend[2]; hr.p3 = pv.pend[3];
-    const uint32_t pool = is_sw ? (tid - SB) * Q : 0;
+    const uint32_t pool = is_sw ? tid - SB : 0;   /* buffer slot s of this ingress: pool + s * C.S */
+    const bool q32 = Q <= 32;                      /* free-slot mask fits one 32-bit word */
     const uint32_t qbase = tid - local;          /* thread slot of this switch's port 0 */
     const uint32_t rowp = pr.vbase + local * rsz;
 
@@ -789,34 +797,49 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         const uint32_t tp = (t & 1u) * nt;
         /* ---------------- arrivals */
         if (is_sw) {
-            const uint32_t si = tid * C.W + slot;
-            const uint32_t n = C.scnt[si];
-            for (uint32_t k = 0; k < n; k++) {
-                const uint32_t desc = C.sdesc[si * C.R + k];
+            DT *rec = C.sdesc + (slot * nt + tid) * C.RP;
+            bool any = false;
+            for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
+                const uint32_t e = rec[k];
+                if (e == 0) break;
+                any = true;
+                /* e = descriptor + 1: the same packet with its hop index advanced */
+                const uint32_t desc = e - 1;
                 const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
                 const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
                 if (freem == 0 || o >= deg) { a.fault = 1; continue; }
-                const uint32_t s = __builtin_ctzll(freem);
-                freem &= freem - 1;
-                C.pdesc[pool + s] = (DT)(desc + 1);
+                uint32_t s;
+                if (q32) {
+                    const uint32_t lo = (uint32_t)freem;
+                    s = __builtin_ctz(lo);
+                    freem = lo & (lo - 1u);
+                } else {
+                    s = __builtin_ctzll(freem);
+                    freem &= freem - 1;
+                }
+                C.pdesc[pool + s * C.S] = (DT)e;
                 const uint32_t av = arrv.get(o);
                 const uint32_t vp = pr.vbase + o * rsz + local;
                 if (av == hseen.get(o)) {
                     C.nslot[vp] = (uint8_t)s;
                     fcur.set(o, s);
                 } else {
-                    C.pnxt[pool + tslot.get(o)] = (uint8_t)s;
+                    C.pnxt[pool + tslot.get(o) * C.S] = (uint8_t)s;
                 }
                 tslot.set(o, s);
                 arrv.set(o, av + 1);
                 C.arr[vp] = (uint8_t)(av + 1);
             }
-            if (n) C.scnt[si] = 0;
+            if (any)
+                for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
         } else if (is_host) {
-            const uint32_t si = tid * C.W + slot;
-            const uint32_t n = C.scnt[si];
-            for (uint32_t k = 0; k < n; k++) {
-                const uint32_t c = (uint32_t)C.sdesc[si * C.R + k] >> DESC_SHIFT;
+            DT *rec = C.sdesc + (slot * nt + tid) * C.RP;
+            bool any = false;
+            for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
+                const uint32_t e = rec[k];
+                if (e == 0) break;
+                any = true;
+                const uint32_t c = (e - 1) >> DESC_SHIFT;
                 CRW2 &cw = C.crw[c];
                 a.delivered++;
                 const uint32_t rem = cw.r_rem - 1u;
@@ -842,7 +865,8 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     if (crecv_ok(C, g, didx, d, dpos)) cactivate(C, a, hr, d, dpos, g, didx, t);
                 }
             }
-            if (n) C.scnt[si] = 0;
+            if (any)
+                for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
             if (t == 0) {
                 for (uint32_t j = 0; j < pr.n_out; j++) ccheck(C, a, hr, (uint32_t)C.hout[pr.vbase + j], t);
             } else if (hr.pcnt) {
@@ -861,31 +885,33 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             int32_t credit = peer_host ? (int32_t)pr.rate : (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
             uint64_t v0 = bytes_sub(ar.w0, phead.w0);
             uint64_t v1 = W == 2 ? bytes_sub(ar.w1, phead.w1) : 0ull;
-            for (uint32_t m = 0; m < pr.rate && credit > 0; m++) {
+            for (uint32_t m = 0; m < (R1 ? 1u : pr.rate) && credit > 0; m++) {
                 const int i = first_from<W>(bytes_nz(v0), bytes_nz(v1), rr);
                 if (i < 0) break;
                 const uint32_t vp = rowp + (uint32_t)i;
-                const uint32_t qpool = (qbase + (uint32_t)i - SB) * Q;
+                const uint32_t qpool = qbase + (uint32_t)i - SB;
                 const uint32_t s = C.nslot[vp];
-                const uint32_t desc = C.pdesc[qpool + s];
-                C.nslot[vp] = C.pnxt[qpool + s];
+                const uint32_t desc = C.pdesc[qpool + s * C.S];
+                C.nslot[vp] = C.pnxt[qpool + s * C.S];
                 const uint32_t hb = phead.get((uint32_t)i) + 1;
                 phead.set((uint32_t)i, hb);
                 C.head[pr.vbase + (uint32_t)i * rsz + local] = (uint8_t)hb;
-                if (i < 8) v0 -= 1ull << (8 * i);
-                else v1 -= 1ull << (8 * (i - 8));
+                if (!R1) {
+                    if (i < 8) v0 -= 1ull << (8 * i);
+                    else v1 -= 1ull << (8 * (i - 8));
+                }
                 rr = (uint32_t)i + 1 == deg ? 0 : (uint32_t)i + 1;
-                ctransmit(C, a, pr, desc, t, slot);
+                ctransmit(C, a, pr, desc, t, slot, m);
                 pushed++;
                 credit--;
             }
         } else if (is_host && alive && pr.n_out) {
             int32_t credit = (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
-            for (uint32_t m = 0; m < pr.rate && credit > 0 && hr.ready; m++) {
+            for (uint32_t m = 0; m < (R1 ? 1u : pr.rate) && credit > 0 && hr.ready; m++) {
                 const uint64_t rot = rr ? (hr.ready >> rr) | (hr.ready << (64 - rr)) : hr.ready;
                 const uint32_t j = (rr + (uint32_t)__builtin_ctzll(rot)) & 63u;
                 const uint32_t c = C.hout[pr.vbase + j];
-                ctransmit(C, a, pr, c << DESC_SHIFT, t, slot);
+                ctransmit(C, a, pr, c << DESC_SHIFT, t, slot, m);
                 pushed++;
                 credit--;
                 rr = j + 1 == pr.n_out ? 0 : j + 1;
@@ -926,8 +952,9 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     uint32_t f = fcur.get(o);
                     for (uint32_t j = 0; j < k; j++) {
                         const uint32_t s = f;
-                        f = C.pnxt[pool + s];
-                        freem |= 1ull << s;
+                        f = C.pnxt[pool + s * C.S];
+                        if (q32) freem = (uint32_t)freem | (1u << s);
+                        else freem |= 1ull << s;
                     }
                     fcur.set(o, f);
                 }
@@ -993,14 +1020,11 @@ __device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *
     if (KIND == 0) {
         if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true>(kp, x, arena, lds, sh);
         else run_experiment<false>(kp, x, arena, lds, sh);
-    } else if (KIND == 1) {
-        run_compact<1, uint16_t>(kp, x, arena, lds, sh);
-    } else if (KIND == 2) {
-        run_compact<1, uint32_t>(kp, x, arena, lds, sh);
-    } else if (KIND == 3) {
-        run_compact<2, uint16_t>(kp, x, arena, lds, sh);
     } else {
-        run_compact<2, uint32_t>(kp, x, arena, lds, sh);
+        /* compact kinds: 1 + (16-byte rows << 2 | 32-bit descriptors << 1 | some link faster than 1) */
+        constexpr int c = KIND - 1;
+        run_compact<(c & 4) ? 2 : 1, typename std::conditional<(c & 2) != 0, uint32_t, uint16_t>::type, (c & 1) == 0>(
+            kp, x, arena, lds, sh);
     }
 }
 
@@ -1028,18 +1052,26 @@ __device__ void megakernel_body(const KParams &kp)
 }
 
 extern "C" __global__ void __launch_bounds__(1024) msim_megakernel(KParams kp) { megakernel_body<0>(kp); }
-extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c8h(KParams kp) { megakernel_body<1>(kp); }
-extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c8w(KParams kp) { megakernel_body<2>(kp); }
-extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16h(KParams kp) { megakernel_body<3>(kp); }
-extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w(KParams kp) { megakernel_body<4>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c8h_r1(KParams kp) { megakernel_body<1>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c8h(KParams kp) { megakernel_body<2>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c8w_r1(KParams kp) { megakernel_body<3>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c8w(KParams kp) { megakernel_body<4>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16h_r1(KParams kp) { megakernel_body<5>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16h(KParams kp) { megakernel_body<6>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w_r1(KParams kp) { megakernel_body<7>(kp); }
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w(KParams kp) { megakernel_body<8>(kp); }
 
 static const void *kernel_of(uint32_t kind)
 {
     switch (kind) {
     case 0: return (const void *)msim_megakernel;
-    case 1: return (const void *)msim_megakernel_c8h;
-    case 2: return (const void *)msim_megakernel_c8w;
-    case 3: return (const void *)msim_megakernel_c16h;
+    case 1: return (const void *)msim_megakernel_c8h_r1;
+    case 2: return (const void *)msim_megakernel_c8h;
+    case 3: return (const void *)msim_megakernel_c8w_r1;
+    case 4: return (const void *)msim_megakernel_c8w;
+    case 5: return (const void *)msim_megakernel_c16h_r1;
+    case 6: return (const void *)msim_megakernel_c16h;
+    case 7: return (const void *)msim_megakernel_c16w_r1;
     default: return (const void *)msim_megakernel_c16w;
     }
 }

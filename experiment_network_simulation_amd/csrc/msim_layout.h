@@ -141,6 +141,13 @@ struct ArenaHdr2 {       /* 128 bytes */
     uint32_t o_route, o_cgrp, o_lidx, o_crw, o_grp, o_hout;
     uint32_t o_port, o_priv;
 };
+/* Buffer pools are slot-major: slot s of the ingress on switch thread slot
+ * SB + j lives at index s * (nt - SB) + j of pdesc / pnxt, so lanes touching
+ * the same slot number of their own pools hit different LDS banks.
+ * Staging (o_sdesc; o_scnt unused): for tick slot w and port slot p, RP
+ * entries at (w * nt + p) * RP, entry m = descriptor + 1 of the m-th packet the
+ * far output sent for that tick, 0 = empty; RP = the largest rate rounded up
+ * to 1, 2 or 4. */
 /* popped (switch ingress: packets forwarded out of it) is published twice,
  * indexed by tick parity: [(t&1) * nt + slot] holds the count through tick t-1
  * and is written at the end of tick t-1, so tick t's readers in other
@@ -199,7 +206,7 @@ struct ExpState {        /* 64 bytes */
 };
 
 /* workspace header */
-#define MSIM_KINDS 5
+#define MSIM_KINDS 9
 
 struct WsHdr {
     uint32_t claim[MSIM_KINDS]; /* experiment queue counters of a run, one per kernel kind */

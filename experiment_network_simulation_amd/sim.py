@@ -22,7 +22,8 @@ E_INVALID_SPEC, E_UNROUTABLE, E_WORKSPACE, E_HIP, E_ARG, E_STATE, E_LIMIT = -1, 
 EXP_DONE, EXP_INCOMPLETE, EXP_DEADLOCK = 0, 1, 2
 NONE = 0xFFFFFFFF
 
-KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h", "msim_megakernel_c8w", "msim_megakernel_c16h",
+KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h_r1", "msim_megakernel_c8h", "msim_megakernel_c8w_r1",
+                "msim_megakernel_c8w", "msim_megakernel_c16h_r1", "msim_megakernel_c16h", "msim_megakernel_c16w_r1",
                 "msim_megakernel_c16w"]
 
 EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_reset", "msim_results",

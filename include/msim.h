@@ -202,9 +202,11 @@ typedef struct msim_info {
     uint32_t lds_bytes;          /* dynamic LDS per workgroup (0: experiment state stays in HBM) */
     uint32_t n_lds_exp;          /* experiments whose state is worked on in LDS */
     uint32_t n_compact;          /* of those, experiments on the compact path (one thread per port) */
-    uint32_t main_kernel;        /* kernel running most experiments: 0 msim_megakernel (general path),
-                                    1..4 msim_megakernel_c8h / _c8w / _c16h / _c16w (compact path,
-                                    8- or 16-byte queue rows, 16- or 32-bit packet descriptors) */
+    uint32_t main_kernel;        /* kernel running most experiments: 0 msim_megakernel (general path);
+                                    1..8 the compact path, msim_megakernel_c{8,16}{h,w}[_r1]: 8- or
+                                    16-byte queue rows, 16- (h) or 32-bit (w) packet descriptors,
+                                    _r1 when every link moves one packet per tick; kind =
+                                    1 + (rows16 << 2 | desc32 << 1 | !r1) */
     uint32_t max_ports;          /* largest experiment: ports */
     uint64_t max_arena_bytes;    /* largest experiment: state bytes */
     uint64_t total_flows;        /* over the batch */
