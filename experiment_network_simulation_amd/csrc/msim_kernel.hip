@@ -39,6 +39,7 @@
 #include "msim_layout.h"
 
 #define CHECK_EVERY 16u
+#define LDSP __attribute__((address_space(3)))
 
 __device__ __forceinline__ uint64_t mix64(uint64_t z)
 {
@@ -530,6 +531,13 @@ __device__ __forceinline__ uint64_t bytes_sub(uint64_t a, uint64_t b)
     return ((a | H) - (b & ~H)) ^ ((a ^ ~b) & H);
 }
 
+/* per-byte a + b (mod 256) of eight packed bytes */
+__device__ __forceinline__ uint64_t bytes_add(uint64_t a, uint64_t b)
+{
+    const uint64_t H = 0x8080808080808080ull;
+    return ((a & ~H) + (b & ~H)) ^ ((a ^ b) & H);
+}
+
 /* 0x80 in every byte of d that is not zero */
 __device__ __forceinline__ uint64_t bytes_nz(uint64_t d)
 {
@@ -553,10 +561,10 @@ struct Row {
         if (W == 1 || i < 8) w0 = (w0 & m) | b;
         else w1 = (w1 & m) | b;
     }
-    __device__ __forceinline__ void load(const uint8_t *p)
+    __device__ __forceinline__ void load(const LDSP uint8_t *p)
     {
-        w0 = *(const uint64_t *)p;
-        w1 = W == 2 ? *(const uint64_t *)(p + 8) : 0ull;
+        w0 = *(const LDSP uint64_t *)p;
+        w1 = W == 2 ? *(const LDSP uint64_t *)(p + 8) : 0ull;
     }
 };
 
@@ -580,22 +588,41 @@ __device__ __forceinline__ int first_from(uint64_t n0, uint64_t n1, uint32_t rr)
     return -1;
 }
 
+/* LDS-qualified pointers keep address arithmetic in 32 bits. */
 template <typename DT>
 struct CCtx {
-    uint8_t *arr, *head, *nslot, *pnxt;
-    uint32_t *popped;          /* [2][nt], tick parity */
-    const uint32_t *route;
-    const DT *hout;
-    const uint16_t *cgrp;
-    const uint8_t *lidx;
-    CRW2 *crw;
-    const CGrp *grp;
-    DT *pdesc, *sdesc;
+    LDSP uint8_t *arr, *head, *nslot, *pnxt;
+    LDSP uint32_t *popped;     /* [2][nt], tick parity */
+    const LDSP uint32_t *route;
+    const LDSP DT *hout;
+    const LDSP uint16_t *cgrp;
+    const LDSP uint8_t *lidx;
+    LDSP CRW2 *crw;
+    const LDSP CGrp *grp;
+    LDSP DT *pdesc, *sdesc;
     uint32_t *rec;
-    uint32_t Q, W, R, rsz, n_flows, SB, nt;
+    uint32_t Q, W, R, n_flows, SB, nt;
     uint32_t RP;               /* staging entries per (tick slot, port): R rounded up to 1, 2 or 4 */
     uint32_t S;                /* switch thread slots; pools are slot-major: [buffer slot][S] */
 };
+
+/* Collective group of connection c, copied out of LDS field by field. */
+template <typename DT>
+__device__ __forceinline__ CGrp cgrp_at(const CCtx<DT> &C, uint32_t c)
+{
+    const LDSP CGrp &q = C.grp[C.cgrp[c]];
+    CGrp g;
+    g.kind = q.kind; g.N = q.N; g.S = q.S; g.R = q.R; g.p = q.p; g.Xq = q.Xq; g.Xr = q.Xr;
+    g.fid_base = q.fid_base; g.conn_base = q.conn_base; g.mS = q.mS;
+    return g;
+}
+
+/* Pool index of buffer slot s of the ingress in switch thread slot q (s < 64, S < 1024). */
+template <typename DT>
+__device__ __forceinline__ uint32_t cpool(const CCtx<DT> &C, uint32_t q, uint32_t s)
+{
+    return (s & 63u) * (C.S & 1023u) + q;   /* operands known to fit 24 bits: one full-rate multiply */
+}
 
 __device__ __forceinline__ uint32_t cdiv_S(const CGrp &g, uint32_t pos)
 {
@@ -666,7 +693,7 @@ __device__ __forceinline__ void cactivate(const CCtx<DT> &C, Acc &a, HostRegs &h
 template <typename DT>
 __device__ __forceinline__ void ccheck(const CCtx<DT> &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t t)
 {
-    const CGrp g = C.grp[C.cgrp[c]];
+    const CGrp g = cgrp_at(C, c);
     const uint32_t idx = c - g.conn_base;
     const uint32_t pos = C.crw[c].s_st & C_POS_MASK;
     if (pos >= cflows(g)) C.crw[c].s_st = (uint16_t)(pos | (CS_DONE << C_STATE_SHIFT));
@@ -679,11 +706,9 @@ __device__ __forceinline__ void ccheck(const CCtx<DT> &C, Acc &a, HostRegs &hr, 
  * empty), so the sender never reads the record. */
 template <typename DT>
 __device__ __forceinline__ void ctransmit(const CCtx<DT> &C, Acc &a, const PortRO2 &pr, uint32_t desc, uint32_t t,
-                                          uint32_t slot, uint32_t m)
+                                          uint32_t dst)
 {
-    uint32_t s2 = slot + pr.delay;
-    if (s2 >= C.W) s2 -= C.W;
-    C.sdesc[(s2 * C.nt + pr.peer) * C.RP + m] = (DT)(desc + 1);
+    C.sdesc[dst] = (DT)(desc + 1);
     a.hops++;
     a.last_tx1 = t + 1;
     a.max_arr = max(a.max_arr, t + pr.delay);
@@ -732,28 +757,28 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         pr = ((const PortRO2 *)(arena_g + H->o_port))[tid];
         pv = ((const PortPriv *)(arena_g + H->o_priv))[tid];
     }
+    LDSP uint8_t *L = (LDSP uint8_t *)lds;
     CCtx<DT> C;
-    C.arr = lds + H->o_arr;
-    C.head = lds + H->o_head;
-    C.nslot = lds + H->o_nslot;
-    C.pnxt = lds + H->o_pnxt;
-    C.popped = (uint32_t *)(lds + H->o_popped);
-    C.route = (const uint32_t *)(lds + H->o_route);
-    C.hout = (const DT *)(lds + H->o_hout);
-    C.cgrp = (const uint16_t *)(lds + H->o_cgrp);
-    C.lidx = (const uint8_t *)(lds + H->o_lidx);
-    C.crw = (CRW2 *)(lds + H->o_crw);
-    C.grp = (const CGrp *)(lds + H->o_grp);
-    C.pdesc = (DT *)(lds + H->o_pdesc);
-    C.sdesc = (DT *)(lds + H->o_sdesc);
+    C.arr = L + H->o_arr;
+    C.head = L + H->o_head;
+    C.nslot = L + H->o_nslot;
+    C.pnxt = L + H->o_pnxt;
+    C.popped = (LDSP uint32_t *)(L + H->o_popped);
+    C.route = (const LDSP uint32_t *)(L + H->o_route);
+    C.hout = (const LDSP DT *)(L + H->o_hout);
+    C.cgrp = (const LDSP uint16_t *)(L + H->o_cgrp);
+    C.lidx = (const LDSP uint8_t *)(L + H->o_lidx);
+    C.crw = (LDSP CRW2 *)(L + H->o_crw);
+    C.grp = (const LDSP CGrp *)(L + H->o_grp);
+    C.pdesc = (LDSP DT *)(L + H->o_pdesc);
+    C.sdesc = (LDSP DT *)(L + H->o_sdesc);
     C.Q = H->Q;
     C.W = H->W;
     C.R = H->R;
-    C.rsz = H->rsz;
     C.n_flows = H->n_flows;
     C.SB = SB;
     C.nt = nt;
-    C.RP = H->R <= 1 ? 1u : (H->R <= 2 ? 2u : 4u);
+    C.RP = R1 ? 1u : (H->R <= 1 ? 1u : (H->R <= 2 ? 2u : 4u));
     C.S = nt - SB;
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
@@ -762,7 +787,8 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     const bool is_sw = tid >= SB && (pr.flags & PF_USED);
     const bool alive = pr.flags & PF_ALIVE;
     const bool peer_host = pr.flags & PF_PEER_HOST;
-    const uint32_t deg = pr.deg, local = pr.local, Q = C.Q, rsz = C.rsz;
+    constexpr uint32_t RSZ = 8u * W;              /* bytes per VOQ row: one per input port */
+    const uint32_t deg = pr.deg, local = pr.local, Q = C.Q;
     Row<W> tslot, fcur, hseen, phead, arrv;
     tslot.w0 = pv.tslot[0]; tslot.w1 = pv.tslot[1];
     fcur.w0 = pv.fcur[0]; fcur.w1 = pv.fcur[1];
@@ -778,7 +804,10 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     const uint32_t pool = is_sw ? tid - SB : 0;   /* buffer slot s of this ingress: pool + s * C.S */
     const bool q32 = Q <= 32;                      /* free-slot mask fits one 32-bit word */
     const uint32_t qbase = tid - local;          /* thread slot of this switch's port 0 */
-    const uint32_t rowp = pr.vbase + local * rsz;
+    const uint32_t rowp = pr.vbase + local * RSZ;
+    /* staging: the record of (tick slot, port) starts at slot * tstride + port * RP */
+    const uint32_t RP = C.RP, tstride = nt * RP, wsz = C.W * tstride;
+    const uint32_t doff = pr.delay * tstride, poff = pr.peer * RP, myoff = tid * RP;
 
     Acc a;
     a.hops = a.delivered = a.digest = 0;
@@ -790,14 +819,13 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     const uint32_t t0 = stp->t_now;
     const uint32_t t_end = (uint64_t)t0 + kp.max_ticks > 0xFFFFFFF0ull ? 0xFFFFFFF0u : t0 + kp.max_ticks;
     const uint32_t hist = max(max(stp->last_tx1, stp->last_act1), stp->max_arr);
-    uint32_t t = t0, par = 0, slot = t0 % C.W;
+    uint32_t t = t0, par = 0, sb = (t0 % C.W) * tstride, tp = (t0 & 1u) ? nt : 0u;
     bool done = false, dead = false;
     uint32_t t_dead = 0;
     while (t < t_end) {
-        const uint32_t tp = (t & 1u) * nt;
         /* ---------------- arrivals */
         if (is_sw) {
-            DT *rec = C.sdesc + (slot * nt + tid) * C.RP;
+            LDSP DT *rec = C.sdesc + sb + myoff;
             bool any = false;
             for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
                 const uint32_t e = rec[k];
@@ -817,14 +845,14 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     s = __builtin_ctzll(freem);
                     freem &= freem - 1;
                 }
-                C.pdesc[pool + s * C.S] = (DT)e;
+                C.pdesc[cpool(C, pool, s)] = (DT)e;
                 const uint32_t av = arrv.get(o);
-                const uint32_t vp = pr.vbase + o * rsz + local;
+                const uint32_t vp = pr.vbase + o * RSZ + local;
                 if (av == hseen.get(o)) {
                     C.nslot[vp] = (uint8_t)s;
-                    fcur.set(o, s);
+                    if (!R1) fcur.set(o, s);
                 } else {
-                    C.pnxt[pool + tslot.get(o) * C.S] = (uint8_t)s;
+                    C.pnxt[cpool(C, pool, tslot.get(o))] = (uint8_t)s;
                 }
                 tslot.set(o, s);
                 arrv.set(o, av + 1);
@@ -833,19 +861,19 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             if (any)
                 for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
         } else if (is_host) {
-            DT *rec = C.sdesc + (slot * nt + tid) * C.RP;
+            LDSP DT *rec = C.sdesc + sb + myoff;
             bool any = false;
             for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
                 const uint32_t e = rec[k];
                 if (e == 0) break;
                 any = true;
                 const uint32_t c = (e - 1) >> DESC_SHIFT;
-                CRW2 &cw = C.crw[c];
+                LDSP CRW2 &cw = C.crw[c];
                 a.delivered++;
                 const uint32_t rem = cw.r_rem - 1u;
                 cw.r_rem = (uint16_t)rem;
                 if (rem) continue;
-                const CGrp g = C.grp[C.cgrp[c]];
+                const CGrp g = cgrp_at(C, c);
                 const uint32_t idx = c - g.conn_base;
                 uint32_t pos = cw.r_pos;
                 const uint32_t fid = cfid(g, idx, pos);
@@ -879,6 +907,9 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         }
         wave_lds_fence();
         /* ---------------- forwarding */
+        uint32_t dst = sb + doff;
+        if (dst >= wsz) dst -= wsz;
+        dst += poff;
         if (is_sw && alive) {
             Row<W> ar;
             ar.load(C.arr + rowp);
@@ -891,17 +922,20 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 const uint32_t vp = rowp + (uint32_t)i;
                 const uint32_t qpool = qbase + (uint32_t)i - SB;
                 const uint32_t s = C.nslot[vp];
-                const uint32_t desc = C.pdesc[qpool + s * C.S];
-                C.nslot[vp] = C.pnxt[qpool + s * C.S];
+                const uint32_t desc = C.pdesc[cpool(C, qpool, s)];
+                C.nslot[vp] = C.pnxt[cpool(C, qpool, s)];
                 const uint32_t hb = phead.get((uint32_t)i) + 1;
                 phead.set((uint32_t)i, hb);
-                C.head[pr.vbase + (uint32_t)i * rsz + local] = (uint8_t)hb;
+                /* rate 1: at most one pop per queue and tick, so the queue's byte
+                 * carries the freed slot itself (flag 0x80 | slot); otherwise it
+                 * carries the running pop count */
+                C.head[pr.vbase + (uint32_t)i * RSZ + local] = (uint8_t)(R1 ? (0x80u | s) : hb);
                 if (!R1) {
                     if (i < 8) v0 -= 1ull << (8 * i);
                     else v1 -= 1ull << (8 * (i - 8));
                 }
                 rr = (uint32_t)i + 1 == deg ? 0 : (uint32_t)i + 1;
-                ctransmit(C, a, pr, desc, t, slot, m);
+                ctransmit(C, a, pr, desc, t, dst + m);
                 pushed++;
                 credit--;
             }
@@ -911,18 +945,18 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 const uint64_t rot = rr ? (hr.ready >> rr) | (hr.ready << (64 - rr)) : hr.ready;
                 const uint32_t j = (rr + (uint32_t)__builtin_ctzll(rot)) & 63u;
                 const uint32_t c = C.hout[pr.vbase + j];
-                ctransmit(C, a, pr, c << DESC_SHIFT, t, slot, m);
+                ctransmit(C, a, pr, c << DESC_SHIFT, t, dst + m);
                 pushed++;
                 credit--;
                 rr = j + 1 == pr.n_out ? 0 : j + 1;
-                CRW2 &cw = C.crw[c];
+                LDSP CRW2 &cw = C.crw[c];
                 const uint32_t rem = cw.s_rem - 1u;
                 cw.s_rem = (uint16_t)rem;
                 if (rem == 0) {
                     hr.ready &= ~(1ull << j);
                     const uint32_t pos = cw.s_st & C_POS_MASK;
                     if (C.rec) {
-                        const CGrp g = C.grp[C.cgrp[c]];
+                        const CGrp g = cgrp_at(C, c);
                         C.rec[2 * C.n_flows + cfid(g, c - g.conn_base, pos)] = t + 1;
                     }
                     cw.s_st = (uint16_t)(pos + 1);
@@ -936,7 +970,36 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         }
         wave_lds_fence();
         /* ---------------- frees, and the popped count for tick t+1 */
-        if (is_sw) {
+        if (is_sw && R1) {
+            Row<W> hd;
+            hd.load(C.head + rowp);
+            const uint64_t HB = 0x8080808080808080ull;
+            uint64_t m0 = hd.w0 & HB, m1 = W == 2 ? hd.w1 & HB : 0ull;
+            if (m0 | m1) {
+                popped += __popcll(m0) + (W == 2 ? __popcll(m1) : 0u);
+                hseen.w0 = bytes_add(hseen.w0, m0 >> 7);
+                if (W == 2) hseen.w1 = bytes_add(hseen.w1, m1 >> 7);
+                /* bit 7 of byte o flags a pop by output o; bits 0..5 are the slot */
+                while (m0) {
+                    const uint32_t b7 = __builtin_ctzll(m0);
+                    const uint32_t s = (uint32_t)(hd.w0 >> (b7 - 7)) & 0x3Fu;
+                    if (q32) freem = (uint32_t)freem | (1u << s);
+                    else freem |= 1ull << s;
+                    m0 &= m0 - 1;
+                }
+                if (W == 2)
+                    while (m1) {
+                        const uint32_t b7 = __builtin_ctzll(m1);
+                        const uint32_t s = (uint32_t)(hd.w1 >> (b7 - 7)) & 0x3Fu;
+                        if (q32) freem = (uint32_t)freem | (1u << s);
+                        else freem |= 1ull << s;
+                        m1 &= m1 - 1;
+                    }
+                *(LDSP uint64_t *)(C.head + rowp) = 0ull;
+                if (W == 2) *(LDSP uint64_t *)(C.head + rowp + 8) = 0ull;
+            }
+            C.popped[(tp ^ nt) + tid] = popped;
+        } else if (is_sw) {
             Row<W> hd;
             hd.load(C.head + rowp);
             uint64_t d0 = bytes_sub(hd.w0, hseen.w0);
@@ -952,7 +1015,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     uint32_t f = fcur.get(o);
                     for (uint32_t j = 0; j < k; j++) {
                         const uint32_t s = f;
-                        f = C.pnxt[pool + s * C.S];
+                        f = C.pnxt[cpool(C, pool, s)];
                         if (q32) freem = (uint32_t)freem | (1u << s);
                         else freem |= 1ull << s;
                     }
@@ -963,7 +1026,9 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             C.popped[(tp ^ nt) + tid] = popped;
         }
         t++;
-        slot = slot + 1 == C.W ? 0 : slot + 1;
+        sb += tstride;
+        if (sb == wsz) sb = 0;
+        tp ^= nt;
         if ((t - t0) % CHECK_EVERY == 0 || t == t_end) {
             uint32_t any = __ballot(a.left > 0) != 0ull;
             uint32_t ts = wave_max_u32(max(max(a.last_tx1, a.last_act1), a.max_arr));
@@ -987,6 +1052,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         for (uint32_t i = tid; i < (lds_bytes - rw_off) / 16; i += nth) dst[i] = src[i];
     }
     if (used) {
+        pv = PortPriv{};
         pv.tslot[0] = tslot.w0; pv.tslot[1] = tslot.w1;
         pv.fcur[0] = fcur.w0; pv.fcur[1] = fcur.w1;
         pv.hseen[0] = hseen.w0; pv.hseen[1] = hseen.w1;
