@@ -407,7 +407,8 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             take(H.o_pnxt, (size_t)S * Q);
             take(H.o_popped, 8ull * nt);
             const uint32_t RP = R <= 1 ? 1 : (R <= 2 ? 2 : 4);
-            H.o_scnt = 0;
+            if (R == 1) take(H.o_elig, 4ull * nt);
+            else H.o_elig = 0;
             take(H.o_sdesc, (size_t)dt * nt * W * RP);
             take(H.o_crw, sizeof(CRW2) * nconn);
             H.lds_bytes = (uint32_t)off;
@@ -847,17 +848,23 @@ extern "C" int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *stream, uint32_
     if (!ctx) return MSIM_E_ARG;
     if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_run before msim_bind");
     (void)flags;
-    bool first = true;
-    for (uint32_t k = 0; k < MSIM_KINDS; k++) {
-        if (!ctx->k_count[k]) continue;
-        KParams kp = make_params(ctx, max_ticks);
-        kp.order_base = ctx->k_base[k];
-        kp.n_run = ctx->k_count[k];
-        kp.lds_bytes = ctx->k_lds[k];
-        hipError_t he = msim_launch_run(&kp, k, ctx->k_grid[k], ctx->k_block[k], ctx->k_lds[k], first,
-                                        (hipStream_t)stream);
-        if (he != hipSuccess) return hip_fail(ctx, he, "kernel launch");
-        first = false;
+    /* launches of at most 2^30 ticks each: the kernels count a port's
+     * packet-hops of one launch in 32 bits (rate <= 4) */
+    for (uint64_t left = max_ticks; left > 0;) {
+        const uint32_t chunk = left > MSIM_LAUNCH_TICKS ? MSIM_LAUNCH_TICKS : (uint32_t)left;
+        left -= chunk;
+        bool first = true;
+        for (uint32_t k = 0; k < MSIM_KINDS; k++) {
+            if (!ctx->k_count[k]) continue;
+            KParams kp = make_params(ctx, chunk);
+            kp.order_base = ctx->k_base[k];
+            kp.n_run = ctx->k_count[k];
+            kp.lds_bytes = ctx->k_lds[k];
+            hipError_t he = msim_launch_run(&kp, k, ctx->k_grid[k], ctx->k_block[k], ctx->k_lds[k], first,
+                                            (hipStream_t)stream);
+            if (he != hipSuccess) return hip_fail(ctx, he, "kernel launch");
+            first = false;
+        }
     }
     return MSIM_OK;
 }

@@ -531,13 +531,6 @@ __device__ __forceinline__ uint64_t bytes_sub(uint64_t a, uint64_t b)
     return ((a | H) - (b & ~H)) ^ ((a ^ ~b) & H);
 }
 
-/* per-byte a + b (mod 256) of eight packed bytes */
-__device__ __forceinline__ uint64_t bytes_add(uint64_t a, uint64_t b)
-{
-    const uint64_t H = 0x8080808080808080ull;
-    return ((a & ~H) + (b & ~H)) ^ ((a ^ b) & H);
-}
-
 /* 0x80 in every byte of d that is not zero */
 __device__ __forceinline__ uint64_t bytes_nz(uint64_t d)
 {
@@ -598,6 +591,7 @@ struct CCtx {
     const LDSP uint16_t *cgrp;
     const LDSP uint8_t *lidx;
     LDSP CRW2 *crw;
+    LDSP uint32_t *elig;       /* rate 1: per output, inputs with a non-empty queue toward it */
     const LDSP CGrp *grp;
     LDSP DT *pdesc, *sdesc;
     uint32_t *rec;
@@ -704,14 +698,13 @@ __device__ __forceinline__ void ccheck(const CCtx<DT> &C, Acc &a, HostRegs &hr, 
 /* Stages the m-th packet this output sends in tick t for arrival at t + delay:
  * entry m of the far port's record for that tick slot holds desc + 1 (0 means
  * empty), so the sender never reads the record. */
+/* Packet-hops are counted from the output's pushed total, and the latest
+ * arrival tick from its last transmission plus its fixed delay. */
 template <typename DT>
-__device__ __forceinline__ void ctransmit(const CCtx<DT> &C, Acc &a, const PortRO2 &pr, uint32_t desc, uint32_t t,
-                                          uint32_t dst)
+__device__ __forceinline__ void ctransmit(const CCtx<DT> &C, Acc &a, uint32_t desc, uint32_t t, uint32_t dst)
 {
     C.sdesc[dst] = (DT)(desc + 1);
-    a.hops++;
     a.last_tx1 = t + 1;
-    a.max_arr = max(a.max_arr, t + pr.delay);
 }
 
 /* Keeps the compiler from moving LDS accesses across a phase boundary.  Lanes
@@ -769,6 +762,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     C.cgrp = (const LDSP uint16_t *)(L + H->o_cgrp);
     C.lidx = (const LDSP uint8_t *)(L + H->o_lidx);
     C.crw = (LDSP CRW2 *)(L + H->o_crw);
+    C.elig = (LDSP uint32_t *)(L + H->o_elig);
     C.grp = (const LDSP CGrp *)(L + H->o_grp);
     C.pdesc = (LDSP DT *)(L + H->o_pdesc);
     C.sdesc = (LDSP DT *)(L + H->o_sdesc);
@@ -808,6 +802,8 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     /* staging: the record of (tick slot, port) starts at slot * tstride + port * RP */
     const uint32_t RP = C.RP, tstride = nt * RP, wsz = C.W * tstride;
     const uint32_t doff = pr.delay * tstride, poff = pr.peer * RP, myoff = tid * RP;
+    const uint32_t mybit = 1u << local;            /* rate 1: this input's bit in its outputs' masks */
+    const uint32_t pushed0 = pushed;               /* packet-hops of this run: pushed - pushed0 */
 
     Acc a;
     a.hops = a.delivered = a.digest = 0;
@@ -824,7 +820,42 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     uint32_t t_dead = 0;
     while (t < t_end) {
         /* ---------------- arrivals */
-        if (is_sw) {
+        if (R1 && is_sw) {
+            /* rate 1: at most one packet per ingress and tick */
+            LDSP DT *rec = C.sdesc + sb + myoff;
+            const uint32_t e = rec[0];
+            if (e != 0) {
+                rec[0] = 0;
+                const uint32_t desc = e - 1;
+                const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
+                const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
+                if (freem == 0 || o >= deg) {
+                    a.fault = 1;
+                } else {
+                    uint32_t s;
+                    if (q32) {
+                        const uint32_t lo = (uint32_t)freem;
+                        s = __builtin_ctz(lo);
+                        freem = lo & (lo - 1u);
+                    } else {
+                        s = __builtin_ctzll(freem);
+                        freem &= freem - 1;
+                    }
+                    C.pdesc[cpool(C, pool, s)] = (DT)e;
+                    const uint32_t vq = pr.vbase + o * RSZ + local;   /* queue (this input, o) */
+                    LDSP uint32_t *el = C.elig + qbase + o;
+                    /* the read precedes every lane's update of the mask, and only
+                     * this input changes its own bit during arrivals */
+                    if (__hip_atomic_load(el, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & mybit) {
+                        C.pnxt[cpool(C, pool, C.arr[vq])] = (uint8_t)s;
+                    } else {
+                        C.nslot[vq] = (uint8_t)s;
+                        __hip_atomic_fetch_or(el, mybit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                    C.arr[vq] = (uint8_t)s;
+                }
+            }
+        } else if (is_sw) {
             LDSP DT *rec = C.sdesc + sb + myoff;
             bool any = false;
             for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
@@ -910,7 +941,25 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         uint32_t dst = sb + doff;
         if (dst >= wsz) dst -= wsz;
         dst += poff;
-        if (is_sw && alive) {
+        if (R1 && is_sw && alive) {
+            /* rate 1: one grant at most, cyclic from rr over the non-empty inputs */
+            const uint32_t E = C.elig[tid];
+            const int32_t credit = peer_host ? 1 : (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
+            if (E != 0 && credit > 0) {
+                const uint32_t up = E >> rr;
+                const uint32_t i = up ? rr + __builtin_ctz(up) : __builtin_ctz(E);
+                const uint32_t vq = rowp + i;                           /* queue (i, this output) */
+                const uint32_t qpool = qbase + i - SB;
+                const uint32_t s = C.nslot[vq];
+                const uint32_t desc = C.pdesc[cpool(C, qpool, s)];
+                if (s == C.arr[vq]) C.elig[tid] = E & ~(1u << i);       /* popped the tail: now empty */
+                else C.nslot[vq] = C.pnxt[cpool(C, qpool, s)];
+                C.head[pr.vbase + i * RSZ + local] = (uint8_t)(0x80u | s);
+                rr = i + 1 == deg ? 0 : i + 1;
+                ctransmit(C, a, desc, t, dst);
+                pushed++;
+            }
+        } else if (is_sw && alive) {
             Row<W> ar;
             ar.load(C.arr + rowp);
             int32_t credit = peer_host ? (int32_t)pr.rate : (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
@@ -935,7 +984,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     else v1 -= 1ull << (8 * (i - 8));
                 }
                 rr = (uint32_t)i + 1 == deg ? 0 : (uint32_t)i + 1;
-                ctransmit(C, a, pr, desc, t, dst + m);
+                ctransmit(C, a, desc, t, dst + m);
                 pushed++;
                 credit--;
             }
@@ -945,7 +994,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 const uint64_t rot = rr ? (hr.ready >> rr) | (hr.ready << (64 - rr)) : hr.ready;
                 const uint32_t j = (rr + (uint32_t)__builtin_ctzll(rot)) & 63u;
                 const uint32_t c = C.hout[pr.vbase + j];
-                ctransmit(C, a, pr, c << DESC_SHIFT, t, dst + m);
+                ctransmit(C, a, c << DESC_SHIFT, t, dst + m);
                 pushed++;
                 credit--;
                 rr = j + 1 == pr.n_out ? 0 : j + 1;
@@ -977,8 +1026,6 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             uint64_t m0 = hd.w0 & HB, m1 = W == 2 ? hd.w1 & HB : 0ull;
             if (m0 | m1) {
                 popped += __popcll(m0) + (W == 2 ? __popcll(m1) : 0u);
-                hseen.w0 = bytes_add(hseen.w0, m0 >> 7);
-                if (W == 2) hseen.w1 = bytes_add(hseen.w1, m1 >> 7);
                 /* bit 7 of byte o flags a pop by output o; bits 0..5 are the slot */
                 while (m0) {
                     const uint32_t b7 = __builtin_ctzll(m0);
@@ -1030,6 +1077,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         if (sb == wsz) sb = 0;
         tp ^= nt;
         if ((t - t0) % CHECK_EVERY == 0 || t == t_end) {
+            a.max_arr = a.last_tx1 ? a.last_tx1 - 1 + pr.delay : 0;
             uint32_t any = __ballot(a.left > 0) != 0ull;
             uint32_t ts = wave_max_u32(max(max(a.last_tx1, a.last_act1), a.max_arr));
             if (lane == 0) { sh.chk_any[par][wave] = any; sh.chk_max[par][wave] = ts; }
@@ -1044,6 +1092,10 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             __syncthreads();
         }
     }
+
+    /* one launch runs at most 2^30 ticks, so a port at rate <= 4 pushes fewer than 2^32 packets */
+    a.hops = pushed - pushed0;
+    a.max_arr = a.last_tx1 ? a.last_tx1 - 1 + pr.delay : 0;
 
     /* write back: shared mutable image, registers, totals */
     {

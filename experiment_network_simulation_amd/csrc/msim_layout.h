@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #define MSIM_NONE 0xFFFFFFFFu
+#define MSIM_LAUNCH_TICKS (1u << 30)   /* most ticks one kernel launch simulates */
 
 /* group kinds */
 #define GK_RING_AR 1
@@ -137,17 +138,25 @@ struct ArenaHdr2 {       /* 128 bytes */
     uint32_t nt, H, SB;
     uint32_t Q, W, R, n_conn;
     uint32_t n_grp, rsz, dt, pad0;
-    uint32_t o_arr, o_head, o_nslot, o_pdesc, o_pnxt, o_popped, o_scnt, o_sdesc;
+    uint32_t o_arr, o_head, o_nslot, o_pdesc, o_pnxt, o_popped, o_elig, o_sdesc;
     uint32_t o_route, o_cgrp, o_lidx, o_crw, o_grp, o_hout;
     uint32_t o_port, o_priv;
 };
 /* Buffer pools are slot-major: slot s of the ingress on switch thread slot
  * SB + j lives at index s * (nt - SB) + j of pdesc / pnxt, so lanes touching
  * the same slot number of their own pools hit different LDS banks.
- * Staging (o_sdesc; o_scnt unused): for tick slot w and port slot p, RP
+ * Staging (o_sdesc): for tick slot w and port slot p, RP
  * entries at (w * nt + p) * RP, entry m = descriptor + 1 of the m-th packet the
  * far output sent for that tick, 0 = empty; RP = the largest rate rounded up
  * to 1, 2 or 4. */
+/* Queues when every link runs at rate 1 (R == 1): the byte of queue (i, o) in
+ * o_nslot is its head slot and in o_arr its tail slot; o_elig holds, per
+ * switch output thread slot, a 32-bit mask of the inputs whose queue toward it
+ * is non-empty (set by the ingress on an append to an empty queue, cleared by
+ * the output when it pops the tail); byte o of ingress i's o_head row is
+ * 0x80 | slot when output o popped that slot of i's pool this tick, else 0.
+ * With a faster link, o_arr / o_head bytes are running append / pop counts and
+ * o_elig is absent (0). */
 /* popped (switch ingress: packets forwarded out of it) is published twice,
  * indexed by tick parity: [(t&1) * nt + slot] holds the count through tick t-1
  * and is written at the end of tick t-1, so tick t's readers in other
