@@ -94,9 +94,23 @@ uint32_t ring_chunk(uint32_t kind, uint32_t N, uint32_t i, uint32_t s)
     return (i + 1 + N - s2) % N;
 }
 
+/* Flows each connection of group g carries, in sending order. */
+uint32_t flows_per_conn(const Grp &g)
+{
+    switch (g.kind) {
+    case GK_BCAST: return g.S;
+    case GK_XFLOW:
+    case GK_SEQ: return 1u;
+    case GK_TREE: return g.R;
+    default: return g.R * g.S;
+    }
+}
+
 uint32_t first_flow_size(const Grp &g, uint32_t idx)
 {
     if (g.kind == GK_XFLOW) return idx;
+    if (g.kind == GK_SEQ) return g.p;
+    if (g.kind == GK_TREE) return g.R > 1 ? g.p : g.X;
     if (g.kind == GK_BCAST) return g.p / g.S + (0 < g.p % g.S ? 1u : 0u);
     if (g.R > 1) return g.p;
     uint32_t k = ring_chunk(g.kind, g.N, idx, 0);
@@ -175,7 +189,10 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     std::vector<Conn> conn;
     uint64_t fid = 0;
     auto is_host = [&](uint32_t h) { return h < nn && layer[h] == 0; };
+    const uint32_t cw0 = s->work_coll_off[w];
+    std::vector<uint32_t> grp_of_coll(s->work_coll_off[w + 1] - cw0, MSIM_NONE);   /* first group of each collective */
     for (uint32_t ci = s->work_coll_off[w]; ci < s->work_coll_off[w + 1]; ci++) {
+        grp_of_coll[ci - cw0] = (uint32_t)grp.size();
         const uint32_t *mem = s->member_host + s->coll_member_off[ci];
         const uint32_t N = s->coll_member_off[ci + 1] - s->coll_member_off[ci];
         if (N < 2) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u has %u members", e, ci, N);
@@ -186,12 +203,30 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         }
         const uint64_t P = (s->coll_bytes[ci] + pkt - 1) / pkt;
         const uint32_t type = s->coll_type[ci];
-        if (type == MSIM_COLL_RING_ALLREDUCE || type == MSIM_COLL_RING_ALLGATHER) {
+        const bool is_ring = type == MSIM_COLL_RING_ALLREDUCE || type == MSIM_COLL_RING_ALLGATHER ||
+                             type == MSIM_COLL_RING_REDUCESCATTER;
+        /* a ring may be gated on an earlier send/recv whose receivers are its members, in order */
+        uint32_t gate_grp = MSIM_NONE;
+        const uint32_t gate = s->coll_gate ? s->coll_gate[ci] : MSIM_NO_GATE;
+        if (gate != MSIM_NO_GATE) {
+            const uint32_t gi = cw0 + gate;
+            if (!is_ring || gi >= ci || s->coll_type[gi] != MSIM_COLL_SENDRECV ||
+                s->coll_member_off[gi + 1] - s->coll_member_off[gi] != N + 1)
+                return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u has an invalid gate %u", e, ci, gate);
+            for (uint32_t i = 0; i < N; i++)
+                if (s->member_host[s->coll_member_off[gi] + 1 + i] != mem[i])
+                    return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u: gate receivers differ from its members", e, ci);
+            gate_grp = grp_of_coll[gate];
+            if (grp[gate_grp].X != 0)
+                return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: send/recv %u gates more than one collective", e, gi);
+        }
+        if (is_ring) {
             const uint32_t NC = s->coll_nc[ci];
             const uint64_t cb = s->coll_chunk_bytes[ci];
             if (NC < 1 || cb == 0 || cb % pkt) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u needs NC >= 1 and a chunk of whole packets", e, ci);
             const uint64_t p = cb / pkt;
-            const uint32_t kind = type == MSIM_COLL_RING_ALLREDUCE ? GK_RING_AR : GK_RING_AG;
+            const uint32_t kind = type == MSIM_COLL_RING_ALLREDUCE ? GK_RING_AR : GK_RING_AG;   /* RS: as AG */
+            if (gate_grp != MSIM_NONE) { grp[gate_grp].link = (uint32_t)grp.size(); grp[gate_grp].X = NC; }
             const uint32_t S = kind == GK_RING_AR ? 2 * (N - 1) : N - 1;
             for (uint32_t c = 0; c < NC; c++) {
                 const uint64_t Pc = P / NC + (c < P % NC ? 1 : 0);
@@ -202,7 +237,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                 if (R * S > CS_POS_MASK || p > 0xFFFFFFFFull || X > 0xFFFFFFFFull) return fail(out, MSIM_E_LIMIT, "experiment %u: collective %u too large", e, ci);
                 Grp g{};
                 g.kind = kind; g.N = N; g.S = S; g.R = (uint32_t)R; g.p = (uint32_t)p; g.X = (uint32_t)X;
-                g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size();
+                g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size(); g.link = gate_grp;
                 fid += R * S * N;
                 if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
                 for (uint32_t i = 0; i < N; i++) {
@@ -224,12 +259,53 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             const uint32_t A = N - 1;
             Grp g{};
             g.kind = GK_BCAST; g.N = A; g.S = (uint32_t)K; g.R = 1; g.p = (uint32_t)P; g.X = 0;
-            g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size();
+            g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size(); g.link = MSIM_NONE;
             fid += (uint64_t)A * K;
             if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
             for (uint32_t j = 1; j <= A; j++) {
                 Conn cn;
                 cn.src = mem[j - 1]; cn.dst = mem[j]; cn.grp = (uint32_t)grp.size(); cn.idx = j - 1; cn.pkts = P;
+                conn.push_back(cn);
+            }
+            grp.push_back(g);
+        } else if (type == MSIM_COLL_TREE_ALLREDUCE) {
+            /* binary tree in member order; per channel: up connections of members
+             * 1..N-1 (to their parent (i-1)/2), then down connections of 1..N-1 */
+            const uint32_t NC = s->coll_nc[ci];
+            const uint64_t cb = s->coll_chunk_bytes[ci];
+            if (NC < 1 || cb == 0 || cb % pkt) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: tree %u needs NC >= 1 and a chunk of whole packets", e, ci);
+            const uint64_t p = cb / pkt;
+            for (uint32_t c = 0; c < NC; c++) {
+                const uint64_t Pc = P / NC + (c < P % NC ? 1 : 0);
+                if (Pc < 1) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: tree %u channel %u carries no packet", e, ci, c);
+                const uint64_t R = (Pc + p - 1) / p;
+                if (R > CS_POS_MASK || p > 0xFFFFFFFFull) return fail(out, MSIM_E_LIMIT, "experiment %u: tree %u too large", e, ci);
+                Grp g{};
+                g.kind = GK_TREE; g.N = N; g.S = 1; g.R = (uint32_t)R; g.p = (uint32_t)p;
+                g.X = (uint32_t)(Pc - (R - 1) * p);
+                g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size(); g.link = MSIM_NONE;
+                fid += R * 2 * (N - 1);
+                if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
+                for (uint32_t j = 0; j < 2 * (N - 1); j++) {
+                    const uint32_t i = j < N - 1 ? j + 1 : j - (N - 1) + 1;
+                    Conn cn;
+                    cn.src = j < N - 1 ? mem[i] : mem[(i - 1) / 2];
+                    cn.dst = j < N - 1 ? mem[(i - 1) / 2] : mem[i];
+                    cn.grp = (uint32_t)grp.size(); cn.idx = j; cn.pkts = Pc;
+                    conn.push_back(cn);
+                }
+                grp.push_back(g);
+            }
+        } else if (type == MSIM_COLL_SENDRECV) {
+            if (P < 1 || P > 0xFFFFFFFFull) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: send/recv %u needs 1 .. 2^32-1 packets", e, ci);
+            Grp g{};
+            g.kind = GK_SEQ; g.N = N - 1; g.S = 1; g.R = 1; g.p = (uint32_t)P; g.X = 0;
+            g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size(); g.link = MSIM_NONE;
+            fid += N - 1;
+            if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
+            for (uint32_t j = 1; j < N; j++) {
+                Conn cn;
+                cn.src = mem[0]; cn.dst = mem[j]; cn.grp = (uint32_t)grp.size(); cn.idx = j - 1; cn.pkts = P;
                 conn.push_back(cn);
             }
             grp.push_back(g);
@@ -241,7 +317,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     if (x1 > x0) {
         Grp g{};
         g.kind = GK_XFLOW; g.N = (uint32_t)(x1 - x0); g.S = 1; g.R = 1;
-        g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size();
+        g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size(); g.link = MSIM_NONE;
         fid += x1 - x0;
         if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
         for (uint64_t xi = x0; xi < x1; xi++) {
@@ -340,8 +416,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         HostRO &hr = host[host_of[cn.src]];
         cn.lidx = hr.n_out;
         hout[hr.out_off + hr.n_out++] = c;
-        const Grp &g = grp[cn.grp];
-        uint32_t F = g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
+        const uint32_t F = flows_per_conn(grp[cn.grp]);
         left[host_of[cn.dst]] += F;
         n_flows += F;
         out.est_hops += cn.pkts * cn.links;
@@ -361,8 +436,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             if (layer[n] != 0) maxdeg = std::max(maxdeg, deg[n]);
         for (uint32_t h = 0; h < n_hosts; h++) max_out = std::max(max_out, host[h].n_out);
         for (const Grp &g : grp) {
-            uint32_t F = g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
-            max_F = std::max(max_F, F);
+            max_F = std::max(max_F, flows_per_conn(g));
             if (g.kind == GK_BCAST) max_size = std::max<uint64_t>(max_size, g.p / g.S + 1);
             else if (g.kind != GK_XFLOW) max_size = std::max<uint64_t>(max_size, std::max<uint64_t>(g.p, g.X / g.N + 1));
         }
@@ -383,6 +457,8 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         for (const Grp &g : grp) {
             if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) max_ring = std::max(max_ring, g.S);
             if (g.kind == GK_BCAST && g.N > 65535) max_ring = 1u << 20;   /* too long a chain for CGrp.N */
+            /* the compact kernels carry ungated rings, broadcasts and explicit flows */
+            if (g.kind == GK_SEQ || g.kind == GK_TREE || g.link != MSIM_NONE) max_ring = 1u << 20;
         }
         if (nt <= 1024 && maxdeg <= 16 && Q <= 64 && max_out <= 64 && max_F <= C_POS_MASK && max_size < 65536 &&
             max_ring < 1024 && ngrp <= 65535 && nconn < (1u << (32 - DESC_SHIFT))) {

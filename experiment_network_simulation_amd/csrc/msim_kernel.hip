@@ -88,12 +88,20 @@ __device__ __forceinline__ uint32_t ring_chunk(uint32_t kind, uint32_t N, uint32
 
 __device__ __forceinline__ uint32_t flows_per_conn(const Grp &g)
 {
-    return g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
+    switch (g.kind) {
+    case GK_BCAST: return g.S;
+    case GK_XFLOW:
+    case GK_SEQ: return 1u;
+    case GK_TREE: return g.R;
+    default: return g.R * g.S;
+    }
 }
 
 __device__ __forceinline__ uint32_t flow_size(const Grp &g, const ConnRO &cr, uint32_t pos)
 {
     if (g.kind == GK_XFLOW) return cr.idx;
+    if (g.kind == GK_SEQ) return g.p;
+    if (g.kind == GK_TREE) return pos + 1 < g.R ? g.p : g.X;
     if (g.kind == GK_BCAST) return g.p / g.S + (pos < g.p % g.S ? 1u : 0u);
     uint32_t r = pos / g.S;
     if (r + 1 < g.R) return g.p;
@@ -105,8 +113,50 @@ __device__ __forceinline__ uint32_t flow_size(const Grp &g, const ConnRO &cr, ui
 __device__ __forceinline__ uint32_t flow_id(const Grp &g, const ConnRO &cr, uint32_t c, uint32_t pos)
 {
     if (g.kind == GK_XFLOW) return g.fid_base + (c - g.conn_base);
+    if (g.kind == GK_SEQ) return g.fid_base + cr.idx;
+    if (g.kind == GK_TREE) return g.fid_base + pos * 2u * (g.N - 1u) + cr.idx;
     if (g.kind == GK_BCAST) return g.fid_base + cr.idx * g.S + pos;
     return g.fid_base + pos * g.N + cr.idx;
+}
+
+/* Tree connection j (up of member j+1 for j < N-1, else down of member
+ * j-N+2): has chunk pos arrived from everything it waits on?  Up: from the
+ * member's children; down from the root: from the root's children; other
+ * down: at its source from above.  Connection of the up link of member i:
+ * i-1; of its down link: N-1+i-1. */
+template <typename RPos>
+__device__ __forceinline__ bool tree_ready(uint32_t N, uint32_t j, uint32_t pos, RPos rpos)
+{
+    uint32_t ch;
+    if (j < N - 1) {
+        ch = 2 * (j + 1) + 1;                      /* first child of member j+1 */
+    } else {
+        const uint32_t i = j - (N - 1) + 1, par = (i - 1) / 2;
+        if (par != 0) return rpos(N - 1 + par - 1) > pos;
+        ch = 1;                                    /* the root's children */
+    }
+    if (ch < N && rpos(ch - 1) <= pos) return false;
+    if (ch + 1 < N && rpos(ch) <= pos) return false;
+    return true;
+}
+
+/* Tree connections whose next flow may wait on a flow just received over
+ * connection j; calls f(index within the group) for each. */
+template <typename F>
+__device__ __forceinline__ void tree_dependents(uint32_t N, uint32_t j, F f)
+{
+    if (j < N - 1) {
+        const uint32_t par = j / 2;                /* parent of member j+1 */
+        if (par != 0) {
+            f(par - 1);
+        } else {
+            f(N - 1);
+            if (N > 2) f(N);
+        }
+    } else {
+        const uint32_t i = j - (N - 1) + 1;
+        for (uint32_t ch = 2 * i + 1; ch <= 2 * i + 2 && ch < N; ch++) f(N - 1 + ch - 1);
+    }
 }
 
 /* Is the receive predecessor of flow `pos` of connection c met? (the ring's data
@@ -117,7 +167,11 @@ __device__ __forceinline__ bool recv_ok(const Ctx &C, const Grp &g, const ConnRO
 {
     if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
         uint32_t s = pos % g.S;
-        if (s == 0) return true;
+        if (s == 0) {
+            /* a gated ring's first step waits for this rank's piece of the send/recv */
+            if (pos == 0 && g.link != MSIM_NONE) return C.cs[C.grp[g.link].conn_base + cr.idx].r_pos >= 1;
+            return true;
+        }
         uint32_t cin = g.conn_base + (cr.idx + g.N - 1) % g.N;
         return C.cs[cin].r_pos >= pos;
     }
@@ -125,15 +179,10 @@ __device__ __forceinline__ bool recv_ok(const Ctx &C, const Grp &g, const ConnRO
         if (cr.idx == 0) return true;
         return C.cs[c - 1].r_pos > pos;
     }
+    if (g.kind == GK_SEQ) return cr.idx == 0 || (C.cs[c - 1].s_pos & CS_POS_MASK) >= 1;
+    if (g.kind == GK_TREE)
+        return tree_ready(g.N, cr.idx, pos, [&](uint32_t j) { return C.cs[g.conn_base + j].r_pos; });
     return true;
-}
-
-/* Connection whose flows wait on flows received over connection c. */
-__device__ __forceinline__ uint32_t dependent_of(const Grp &g, const ConnRO &cr, uint32_t c)
-{
-    if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) return g.conn_base + (cr.idx + 1) % g.N;
-    if (g.kind == GK_BCAST) return cr.idx + 1 < g.N ? c + 1 : MSIM_NONE;
-    return MSIM_NONE;
 }
 
 __device__ __forceinline__ void activate(const Ctx &C, Acc &a, uint32_t c, uint32_t pos, const Grp &g,
@@ -146,6 +195,33 @@ __device__ __forceinline__ void activate(const Ctx &C, Acc &a, uint32_t c, uint3
     if (C.rec) C.rec[C.n_flows + flow_id(g, cr, c, pos)] = t;
 }
 
+/* Activates connection d's next flow if it was waiting and is now ready.
+ * Every caller passes a connection whose source is the calling host. */
+__device__ __forceinline__ void wake(const Ctx &C, Acc &a, uint32_t d, uint32_t rdy_off, uint32_t t)
+{
+    if ((C.cs[d].s_pos >> CS_SHIFT) != CS_IDLE) return;
+    const ConnRO dr = C.conn[d];
+    const Grp dg = C.grp[dr.grp];
+    const uint32_t dpos = C.cs[d].s_pos & CS_POS_MASK;
+    if (recv_ok(C, dg, dr, d, dpos)) activate(C, a, d, dpos, dg, dr, rdy_off, t);
+}
+
+/* After a flow over connection c (group g) has been fully received: the
+ * connections leaving this host whose next flow waits on it. */
+__device__ __forceinline__ void wake_dependents(const Ctx &C, Acc &a, const Grp &g, const ConnRO &cr, uint32_t c,
+                                                uint32_t rdy_off, uint32_t t)
+{
+    if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
+        wake(C, a, g.conn_base + (cr.idx + 1) % g.N, rdy_off, t);
+    } else if (g.kind == GK_BCAST) {
+        if (cr.idx + 1 < g.N) wake(C, a, c + 1, rdy_off, t);
+    } else if (g.kind == GK_SEQ) {
+        for (uint32_t k = 0; k < g.X; k++) wake(C, a, C.grp[g.link + k].conn_base + cr.idx, rdy_off, t);
+    } else if (g.kind == GK_TREE) {
+        tree_dependents(g.N, cr.idx, [&](uint32_t j) { wake(C, a, g.conn_base + j, rdy_off, t); });
+    }
+}
+
 /* Phase-B decision for a connection whose previous flow has left (or at t = 0). */
 __device__ __forceinline__ void check_conn(const Ctx &C, Acc &a, uint32_t c, uint32_t rdy_off, uint32_t t)
 {
@@ -154,6 +230,8 @@ __device__ __forceinline__ void check_conn(const Ctx &C, Acc &a, uint32_t c, uin
     uint32_t pos = C.cs[c].s_pos & CS_POS_MASK;
     if (pos >= flows_per_conn(g)) {
         C.cs[c].s_pos = pos | (CS_DONE << CS_SHIFT);
+        /* a send/recv's next receiver waits on this send (its SEND predecessor) */
+        if (g.kind == GK_SEQ && cr.idx + 1 < g.N) wake(C, a, c + 1, rdy_off, t);
     } else if (recv_ok(C, g, cr, c, pos)) {
         activate(C, a, c, pos, g, cr, rdy_off, t);
     } else {
@@ -187,13 +265,7 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
         pos++;
         cw.r_pos = pos;
         if (pos < flows_per_conn(g)) cw.r_rem = flow_size(g, cr, pos);
-        uint32_t d = dependent_of(g, cr, c);
-        if (d != MSIM_NONE && (C.cs[d].s_pos >> CS_SHIFT) == CS_IDLE) {
-            const ConnRO dr = C.conn[d];
-            const Grp dg = C.grp[dr.grp];
-            uint32_t dpos = C.cs[d].s_pos & CS_POS_MASK;
-            if (recv_ok(C, dg, dr, d, dpos)) activate(C, a, d, dpos, dg, dr, hr.rdy_off, t);
-        }
+        wake_dependents(C, a, g, cr, c, hr.rdy_off, t);
     }
     if (n) C.scnt[si] = 0;
     /* activations (phase B of the tick) */
@@ -600,15 +672,21 @@ struct CCtx {
     uint32_t S;                /* switch thread slots; pools are slot-major: [buffer slot][S] */
 };
 
-/* Collective group of connection c, copied out of LDS field by field. */
-template <typename DT>
-__device__ __forceinline__ CGrp cgrp_at(const CCtx<DT> &C, uint32_t c)
+/* A collective group copied out of LDS field by field. */
+__device__ __forceinline__ CGrp cgrp_load(const LDSP CGrp *p)
 {
-    const LDSP CGrp &q = C.grp[C.cgrp[c]];
+    const LDSP CGrp &q = *p;
     CGrp g;
     g.kind = q.kind; g.N = q.N; g.S = q.S; g.R = q.R; g.p = q.p; g.Xq = q.Xq; g.Xr = q.Xr;
     g.fid_base = q.fid_base; g.conn_base = q.conn_base; g.mS = q.mS;
     return g;
+}
+
+/* Collective group of connection c. */
+template <typename DT>
+__device__ __forceinline__ CGrp cgrp_at(const CCtx<DT> &C, uint32_t c)
+{
+    return cgrp_load(C.grp + C.cgrp[c]);
 }
 
 /* Pool index of buffer slot s of the ingress in switch thread slot q (s < 64, S < 1024). */
@@ -682,6 +760,26 @@ __device__ __forceinline__ void cactivate(const CCtx<DT> &C, Acc &a, HostRegs &h
     hr.ready |= 1ull << C.lidx[c];
     a.last_act1 = t + 1;
     if (C.rec) C.rec[C.n_flows + cfid(g, idx, pos)] = t;
+}
+
+/* Activates connection d (of group g) if it was waiting and is now ready.
+ * The compact path carries rings, broadcasts and explicit flows only. */
+template <typename DT>
+__device__ __forceinline__ void cwake(const CCtx<DT> &C, Acc &a, HostRegs &hr, const CGrp &g, uint32_t d, uint32_t t)
+{
+    if ((C.crw[d].s_st >> C_STATE_SHIFT) != CS_IDLE) return;
+    const uint32_t didx = d - g.conn_base, dpos = C.crw[d].s_st & C_POS_MASK;
+    if (crecv_ok(C, g, didx, d, dpos)) cactivate(C, a, hr, d, dpos, g, didx, t);
+}
+
+/* After a flow over connection c (group g, index idx) has been fully
+ * received: the connection leaving this host whose next flow waits on it. */
+template <typename DT>
+__device__ __forceinline__ void cwake_dependents(const CCtx<DT> &C, Acc &a, HostRegs &hr, const CGrp &g, uint32_t idx,
+                                                 uint32_t c, uint32_t t)
+{
+    if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) cwake(C, a, hr, g, g.conn_base + (idx + 1u == g.N ? 0u : idx + 1u), t);
+    else if (g.kind == GK_BCAST && idx + 1u < g.N) cwake(C, a, hr, g, c + 1, t);
 }
 
 template <typename DT>
@@ -915,14 +1013,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 pos++;
                 cw.r_pos = (uint16_t)pos;
                 if (pos < cflows(g)) cw.r_rem = (uint16_t)csize(g, idx, pos);
-                uint32_t d = MSIM_NONE;
-                if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) d = g.conn_base + (idx + 1u == g.N ? 0u : idx + 1u);
-                else if (g.kind == GK_BCAST && idx + 1u < g.N) d = c + 1;
-                if (d != MSIM_NONE && (C.crw[d].s_st >> C_STATE_SHIFT) == CS_IDLE) {
-                    const uint32_t dpos = C.crw[d].s_st & C_POS_MASK;
-                    const uint32_t didx = d - g.conn_base;
-                    if (crecv_ok(C, g, didx, d, dpos)) cactivate(C, a, hr, d, dpos, g, didx, t);
-                }
+                cwake_dependents(C, a, hr, g, idx, c, t);
             }
             if (any)
                 for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;

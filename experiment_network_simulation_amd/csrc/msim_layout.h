@@ -30,9 +30,11 @@
 
 /* group kinds */
 #define GK_RING_AR 1
-#define GK_RING_AG 2
+#define GK_RING_AG 2     /* also the ring reduce-scatter: the same chunks along the same ring */
 #define GK_BCAST 3
 #define GK_XFLOW 4
+#define GK_SEQ 5         /* send/recv unit task: one source, receivers in turn */
+#define GK_TREE 6        /* binary-tree all-reduce, pipelined in chunks */
 
 /* sender state of a connection (top two bits of ConnRW.s_pos) */
 #define CS_WAIT 0u   /* previous flow just finished sending (or start): check at next phase A */
@@ -62,15 +64,19 @@ struct ConnRO {          /* 16 bytes */
     uint32_t lidx;       /* index among the source host's connections */
 };
 
-struct Grp {             /* 32 bytes */
+struct Grp {             /* 36 bytes */
     uint32_t kind;
-    uint32_t N;          /* ring members; broadcast: hops A; explicit: flow count */
-    uint32_t S;          /* ring: steps per round; broadcast: partitions K */
-    uint32_t R;          /* ring: rounds */
-    uint32_t p;          /* ring: chunk packets; broadcast: message packets */
-    uint32_t X;          /* ring: packets in the last round */
+    uint32_t N;          /* ring / tree members; broadcast: hops A; explicit: flow count;
+                            send/recv: receivers */
+    uint32_t S;          /* ring: steps per round; broadcast: partitions K; send/recv, tree: 1 */
+    uint32_t R;          /* ring: rounds; tree: chunks */
+    uint32_t p;          /* ring, tree: chunk packets; broadcast, send/recv: message packets */
+    uint32_t X;          /* ring: packets in the last round; tree: in the last chunk;
+                            send/recv: number of groups it gates */
     uint32_t fid_base;   /* first flow id */
     uint32_t conn_base;  /* first connection */
+    uint32_t link;       /* ring: the send/recv group gating its first step, or MSIM_NONE;
+                            send/recv: the first group it gates (they are consecutive) */
 };
 
 struct HostRO {          /* 16 bytes */
@@ -165,7 +171,7 @@ struct ArenaHdr2 {       /* 128 bytes */
 /* Collective group as the compact path reads it: the constant quotients of
  * the flow-size rules are precomputed, and pos / S is umulhi(pos << 8, mS),
  * exact for pos < 2^14 and S < 2^10. */
-struct CGrp {            /* 36 bytes */
+struct CGrp {            /* 36 bytes; rings (ungated), broadcasts and explicit flows only */
     uint16_t kind, N;    /* ring members; broadcast hops; explicit: flow count (low 16 bits) */
     uint32_t S;          /* ring: steps per round; broadcast: partitions K */
     uint32_t R;          /* ring: rounds */

@@ -37,6 +37,10 @@ LAYER_HOST = 0
 COLL_RING_AR = 1
 COLL_RING_AG = 2
 COLL_PIPE_BCAST = 3
+COLL_RING_RS = 4        # ring reduce-scatter (message = total input)
+COLL_TREE_AR = 5        # binary-tree all-reduce, pipelined in chunks
+COLL_SENDRECV = 6       # one source sends the whole message to each receiver in turn
+NO_GATE = 0xFFFFFFFF
 
 KIB = 1024
 MIB = 1024 * 1024
@@ -188,12 +192,17 @@ def fat_tree(k: int, rate: int = 1, delay: int = 1, oversub: int = 1) -> Topolog
 
 @dataclass
 class Collective:
-    kind: int                  # COLL_RING_AR / COLL_RING_AG / COLL_PIPE_BCAST
-    nbytes: int                # message size (all-gather: total output size)
-    members: List[int]         # ring order, or broadcast chain (source first)
-    nc: int = 1                # channels (rings)
-    chunk_bytes: int = 0       # chunk size C (rings)
+    kind: int                  # one of the COLL_* kinds
+    nbytes: int                # message size (all-gather: total output; reduce-scatter: total
+                               # input; send/recv: bytes each receiver gets)
+    members: List[int]         # ring order; broadcast chain or send/recv (source first);
+                               # tree in heap order (member 0 the root)
+    nc: int = 1                # channels (rings, trees)
+    chunk_bytes: int = 0       # chunk size C (rings, trees)
     k: int = 1                 # partitions (broadcast)
+    gate: int = NO_GATE        # rings: index, within the workload, of an earlier send/recv
+                               # whose receivers are these members; each rank then starts
+                               # once its piece from that send/recv has arrived
 
 
 @dataclass
@@ -210,6 +219,43 @@ def ring(kind: int, nbytes: int, members: Sequence[int], nc: int, chunk_bytes: i
 
 def bcast(nbytes: int, chain: Sequence[int], k: int) -> Collective:
     return Collective(COLL_PIPE_BCAST, int(nbytes), [int(m) for m in chain], 1, 0, int(k))
+
+
+def tree(nbytes: int, members: Sequence[int], nc: int, chunk_bytes: int) -> Collective:
+    return Collective(COLL_TREE_AR, int(nbytes), [int(m) for m in members], int(nc), int(chunk_bytes), 1)
+
+
+def sendrecv(nbytes_each: int, source: int, receivers: Sequence[int]) -> Collective:
+    return Collective(COLL_SENDRECV, int(nbytes_each), [int(source)] + [int(m) for m in receivers], 1, 0, 1)
+
+
+def unit_task(strategy: str, nbytes: int, source: int, nodes: Sequence[Sequence[int]],
+              chunk_bytes: int = 0, first_index: int = 0) -> List[Collective]:
+    """A unit communication task: one slice of nbytes from `source` to every
+    device of A receiving nodes of B devices each (AlpaComm section 3.1,
+    Figure 3), as collectives of this simulator:
+      "sendrecv"  the source sends the whole slice to each device in turn;
+      "local_ag"  it sends a 1/B part to each device (the nodes then assemble
+                  the slice over their intra-node links, which this network
+                  model does not carry);
+      "global_ag" it sends a 1/(A B) part to each device, then the devices run
+                  a ring all-gather of the whole slice, each one starting when
+                  its part has arrived (chunk_bytes: the ring's chunk);
+      "broadcast" a pipelined broadcast along the devices (use bcast).
+    first_index: where the returned collectives start in their workload (the
+    all-gather's gate names the send/recv by that index)."""
+    devs = [int(d) for node in nodes for d in node]
+    A, B = len(nodes), len(nodes[0])
+    if strategy == "sendrecv":
+        return [sendrecv(nbytes, source, devs)]
+    if strategy == "local_ag":
+        return [sendrecv(nbytes // B, source, devs)]
+    if strategy == "global_ag":
+        part = sendrecv(nbytes // (A * B), source, devs)
+        ag = ring(COLL_RING_AG, nbytes, devs, 1, chunk_bytes)
+        ag.gate = int(first_index)
+        return [part, ag]
+    raise ValueError(strategy)
 
 
 def xflows(pairs: Sequence[tuple]) -> Workload:
@@ -291,6 +337,7 @@ class PackedBatch:
     coll_k: np.ndarray           # uint32
     coll_member_off: np.ndarray  # uint32 [n_coll+1]
     member_host: np.ndarray      # uint32
+    coll_gate: np.ndarray        # uint32 (NO_GATE, or a collective index within the workload)
     work_xflow_off: np.ndarray   # uint64 [n_work+1]
     xflow_src: np.ndarray        # uint32
     xflow_dst: np.ndarray
@@ -339,6 +386,7 @@ class PackedBatch:
             coll_k=np.asarray([c.k for c in colls], np.uint32),
             coll_member_off=m_off,
             member_host=np.asarray([m for c in colls for m in c.members], np.uint32),
+            coll_gate=np.asarray([c.gate for c in colls], np.uint32),
             work_xflow_off=w_x_off,
             xflow_src=cat([w.xsrc for w in b.works], np.uint32),
             xflow_dst=cat([w.xdst for w in b.works], np.uint32),
@@ -360,14 +408,15 @@ def single_batch(topo: Topology, work: Workload, queue_pkts: int = 16, ecmp_seed
 # The five benchmark configurations
 # ---------------------------------------------------------------------------
 
-BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5}
-FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000}
+BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5, 6: 0xC6}
+FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000, 6: 768}
 CONFIG_NAMES = {
     1: "C1 ring all-reduce 1 MiB, 8 hosts on one switch, NC x C grid",
     2: "C2 ring all-reduce 64 MiB over a 4x8 leaf-spine with 4 spines",
     3: "C3 pipelined broadcast 64 MiB to A hosts, K partitions, random delays",
     4: "C4 k=8 fat-tree: 16 DP ring all-reduces 256 MiB + 16 TP ring all-gathers 56 MiB",
     5: "C5 k=16 fat-tree sweep: Zipf(1.1) sparse all-to-all, 8 MiB per host",
+    6: "C6 k=8 fat-tree collectives mix: tree all-reduces, ring reduce-scatters, send/recv unit tasks",
 }
 
 
@@ -527,14 +576,54 @@ def _c5(e_list, k: int = 16):
     return Batch(topos, [work], exps, "C5")
 
 
+def _c6(e_list):
+    """The further collective shapes on C4's fabric (k=8 fat-tree, rate 1,
+    delay 1, Q = 16, no failures), hosts placed by a seeded permutation pi of
+    the 128 ranks.  Experiment e carries, by e mod 3:
+      0  eight binary-tree all-reduces of 64 MiB over ranks 16g .. 16g+15,
+         NC ~ U{1..4}, chunk ~ 4 KiB U{8..64} (one draw for all eight);
+      1  sixteen ring reduce-scatters of 56 MiB over ranks 8t .. 8t+7 (the TP
+         groups of C4), NC ~ U{1..8}, chunk ~ 4 KiB U{8..128};
+      2  eight unit tasks: source rank g sends an 8 MiB slice to two nodes of
+         four devices (ranks 8 + 8g .. 8 + 8g + 7), strategy by (e div 3) mod 3
+         in send/recv, local all-gather, global all-gather (ring chunk
+         ~ 4 KiB U{1..16})."""
+    topo = fat_tree(8, 1, 1)
+    H = topo.hosts().size
+    works, exps = [], []
+    strategies = ["sendrecv", "local_ag", "global_ag"]
+    for e in e_list:
+        g = exp_rng(BASE_SEED[6], e)
+        pi = g.permutation(H)
+        v = e % 3
+        colls = []
+        if v == 0:
+            nc, ck = g.between(1, 4), 4 * KIB * g.between(8, 64)
+            colls = [tree(64 * MIB, [pi[r] for r in range(16 * j, 16 * j + 16)], nc, ck) for j in range(8)]
+        elif v == 1:
+            nc, ck = g.between(1, 8), 4 * KIB * g.between(8, 128)
+            colls = [ring(COLL_RING_RS, 56 * MIB, [pi[r] for r in range(8 * j, 8 * j + 8)], nc, ck)
+                     for j in range(16)]
+        else:
+            strat = strategies[(e // 3) % 3]
+            ck = 4 * KIB * g.between(1, 16)
+            for j in range(8):
+                base = 8 + 8 * j
+                nodes = [[pi[base + 4 * a + i] for i in range(4)] for a in range(2)]
+                colls += unit_task(strat, 8 * MIB, pi[j], nodes, chunk_bytes=ck, first_index=len(colls))
+        works.append(Workload(colls))
+        exps.append(Experiment(0, len(works) - 1, 16, g.u32()))
+    return Batch([topo], works, exps, "C6")
+
+
 def make_config(cid: int, n_exp: Optional[int] = None, exp_ids: Optional[Sequence[int]] = None) -> Batch:
-    """Batch for benchmark configuration cid (1..5).  Experiment e of a config is
+    """Batch for benchmark configuration cid (1..6).  Experiment e of a config is
     the same whatever subset is drawn, so exp_ids picks a sample of the full
     batch and n_exp the first n experiments."""
     if exp_ids is None:
         exp_ids = range(FULL_E[cid] if n_exp is None else n_exp)
     e_list = list(exp_ids)
-    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5}[cid](e_list)
+    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5, 6: _c6}[cid](e_list)
     b.meta["config"] = cid
     b.meta["exp_ids"] = e_list
     return b

@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsim.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 OK, S_INCOMPLETE, S_DEADLOCK = 0, 1, 2
 E_INVALID_SPEC, E_UNROUTABLE, E_WORKSPACE, E_HIP, E_ARG, E_STATE, E_LIMIT = -1, -2, -3, -4, -5, -6, -7
 EXP_DONE, EXP_INCOMPLETE, EXP_DEADLOCK = 0, 1, 2
@@ -48,7 +48,7 @@ class _Spec(C.Structure):
                 ("coll_member_off", _P32), ("member_host", _P32),
                 ("work_xflow_off", _P64), ("xflow_src", _P32), ("xflow_dst", _P32), ("xflow_pkts", _P32),
                 ("exp_topo", _P32), ("exp_work", _P32), ("exp_queue_pkts", _P32),
-                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32)]
+                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32), ("coll_gate", _P32)]
 
 
 class _Options(C.Structure):
@@ -131,7 +131,8 @@ class Sim:
                            _ptr(p.work_xflow_off, _P64), _ptr(p.xflow_src, _P32), _ptr(p.xflow_dst, _P32),
                            _ptr(p.xflow_pkts, _P32),
                            _ptr(p.exp_topo, _P32), _ptr(p.exp_work, _P32), _ptr(p.exp_queue_pkts, _P32),
-                           _ptr(p.exp_ecmp_seed, _P32), _ptr(p.exp_pkt_bytes, _P32))
+                           _ptr(p.exp_ecmp_seed, _P32), _ptr(p.exp_pkt_bytes, _P32),
+                        _ptr(p.coll_gate, _P32))
         self._rec = np.ascontiguousarray(np.asarray(list(record), np.uint32))
         self.record = [int(x) for x in self._rec]
         opts = _Options(ABI_VERSION, len(self._rec), _ptr(self._rec, _P32) if len(self._rec) else None,

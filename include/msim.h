@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MSIM_ABI_VERSION 1u
+#define MSIM_ABI_VERSION 2u
 
 /* return codes */
 #define MSIM_OK 0
@@ -62,6 +62,10 @@ extern "C" {
 #define MSIM_COLL_RING_ALLREDUCE 1
 #define MSIM_COLL_RING_ALLGATHER 2
 #define MSIM_COLL_PIPE_BROADCAST 3
+#define MSIM_COLL_RING_REDUCESCATTER 4   /* Multiverse section 5 lists it among its collectives */
+#define MSIM_COLL_TREE_ALLREDUCE 5       /* AutoCCL section 4.1: tree (log2 N) against ring (2(N-1)) */
+#define MSIM_COLL_SENDRECV 6             /* AlpaComm section 3.1, Figure 3a: one source, receivers in turn */
+#define MSIM_NO_GATE 0xFFFFFFFFu
 
 /* compiled-in limits */
 #define MSIM_MAX_RATE 4          /* packets per tick per link direction */
@@ -85,14 +89,20 @@ extern "C" {
  *   1..MSIM_MAX_RATE; delays 1..MSIM_MAX_DELAY; a switch has at most
  *   MSIM_MAX_SWITCH_PORTS ports.
  * Workload w: collectives work_coll_off[w] .. work_coll_off[w+1]-1, each with
- *   coll_type, coll_bytes (all-gather: total output size), coll_nc channels,
- *   coll_chunk_bytes (rings; a whole number of packets), coll_k partitions
- *   (broadcast; 1 <= K <= packets) and members coll_member_off[c] ..
- *   coll_member_off[c+1]-1 in member_host (ring order, or broadcast chain with
- *   the source first; distinct hosts, at least 2); then explicit flows
+ *   coll_type, coll_bytes (all-gather: total output size; reduce-scatter:
+ *   total input size; send/recv: bytes each receiver gets), coll_nc channels
+ *   (rings, trees), coll_chunk_bytes (rings, trees; a whole number of
+ *   packets), coll_k partitions (broadcast; 1 <= K <= packets), coll_gate
+ *   (MSIM_NO_GATE, or for a ring the index within the workload of an earlier
+ *   send/recv whose receivers are exactly the ring's members in ring order:
+ *   each rank then starts once its piece of that send/recv has arrived) and
+ *   members coll_member_off[c] .. coll_member_off[c+1]-1 in member_host (ring
+ *   order; broadcast chain or send/recv with the source first; tree in heap
+ *   order, member 0 the root, the parent of member i being member (i-1)/2;
+ *   distinct hosts, at least 2); then explicit flows
  *   work_xflow_off[w] .. work_xflow_off[w+1]-1 (source host, destination host,
  *   packets >= 1).  Every ring channel must carry at least as many packets as
- *   the ring has members.
+ *   the ring has members, every tree channel at least one packet.
  * Experiment e: topology exp_topo[e], workload exp_work[e], switch ingress
  *   buffer exp_queue_pkts[e] packets (1..MSIM_MAX_QUEUE), ECMP seed
  *   exp_ecmp_seed[e], packet size exp_pkt_bytes[e] bytes.
@@ -113,6 +123,7 @@ typedef struct msim_batch_spec {
     const uint64_t *work_xflow_off;
     const uint32_t *xflow_src, *xflow_dst, *xflow_pkts;
     const uint32_t *exp_topo, *exp_work, *exp_queue_pkts, *exp_ecmp_seed, *exp_pkt_bytes;
+    const uint32_t *coll_gate;   /* one per collective; NULL = no gates */
 } msim_batch_spec;
 
 /* Options for msim_create.  Zero-initialise and set what you need. */

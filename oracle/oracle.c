@@ -75,9 +75,33 @@
  *      P/K + [k < P mod K] packets: flow (j, k) runs h_{j-1} -> h_j with
  *      predecessors RECV (j-1, k) for j >= 2 and SEND (j, k-1) for k >= 1.
  *  W3  Explicit flows: one connection and one flow each, no predecessors.
+ *  W5  Ring reduce-scatter (one of the collective algorithms Multiverse section 5
+ *      lists): the message is the total input; channels,
+ *      rounds and chunks as in W1; N-1 steps in which rank i sends chunk
+ *      (i - s) mod N, i.e. the first half of the all-reduce.  With a reduction
+ *      that costs no time (A7) its traffic equals the all-gather's.
+ *  W6  Send/recv unit task (AlpaComm section 3.1, Figure 3a): member 0 sends the
+ *      whole message to members 1 .. A in that order, flow j on connection
+ *      (m_0 -> m_j) with predecessor SEND (j-1), so that sends are sequential.
+ *      A ring may be gated on an earlier send/recv whose receivers are exactly
+ *      its members, in order: rank i's step-0 flow of round 0 of every channel
+ *      then also waits on RECV of the send/recv's flow i (Figure 3c's global
+ *      all-gather after the scatter).
+ *  W7  Tree all-reduce (the tree that AutoCCL section 4.1 contrasts with the
+ *      ring, cost log2 N against 2(N-1)): members form a binary tree in order (the parent of
+ *      i is (i-1)/2, member 0 the root).  Per channel (split as in W1), the
+ *      message goes in chunks of p packets, the last one holding the rest.
+ *      For chunk k, node i > 0 sends up to its parent once it has received
+ *      chunk k from each of its children; the root's children receive chunk k
+ *      once the root has it from all its children, and every other node's
+ *      children once that node has received it from its parent.  Each
+ *      connection sends its chunks in order (SEND on chunk k-1).
  *  Numbering: connections and flows follow the input order of collectives, then
  *  explicit flows; a ring numbers its connections by (channel, rank) and its
- *  flows by (channel, round, step, rank); a broadcast by hop, and (hop, part).
+ *  flows by (channel, round, step, rank); a broadcast by hop, and (hop, part);
+ *  a send/recv by receiver; a tree by channel, then its up connections for
+ *  nodes 1 .. N-1 and its down connections for nodes 1 .. N-1, and its flows
+ *  by (channel, chunk, connection).
  *  Digest = sum over flows of mix64((flow << 32) | RD) mod 2^64, mix64 being
  *  SplitMix64's output function.
  *
@@ -104,7 +128,7 @@
 #define NONE 0xFFFFFFFFu
 #define INF_DIST 0x3FFFFFFF
 
-enum { KIND_RING_AR = 1, KIND_RING_AG = 2, KIND_BCAST = 3 };
+enum { KIND_RING_AR = 1, KIND_RING_AG = 2, KIND_BCAST = 3, KIND_RING_RS = 4, KIND_TREE = 5, KIND_SENDRECV = 6 };
 enum { PRED_RECV = 0, PRED_SEND = 1 };
 
 /* The batch, exactly as the input generator lays it out. */
@@ -122,6 +146,7 @@ typedef struct {
     const uint64_t *work_xflow_off;
     const uint32_t *xflow_src, *xflow_dst, *xflow_pkts;
     const uint32_t *exp_topo, *exp_work, *exp_queue_pkts, *exp_ecmp_seed, *exp_pkt_bytes;
+    const uint32_t *coll_gate;   /* per collective: earlier send/recv collective of the workload, or NONE */
 } orc_batch;
 
 typedef struct {
@@ -191,8 +216,8 @@ typedef struct {
 typedef struct {
     uint32_t conn, size;
     uint32_t npred;
-    uint32_t pred[2];
-    uint32_t pkind[2];
+    uint32_t pred[3];
+    uint32_t pkind[3];
     uint32_t sent, recvd, active;
     uint32_t act, sd, rd;
 } Flow;
@@ -337,10 +362,12 @@ static int build_topology(const orc_batch *b, uint32_t e, Exp *x)
 
 /* --------------------------------------------------------------- workload */
 
-/* Chunk sent by rank i at step s (W1). */
+static int is_ring(uint32_t kind) { return kind == KIND_RING_AR || kind == KIND_RING_AG || kind == KIND_RING_RS; }
+
+/* Chunk sent by rank i at step s (W1; the reduce-scatter takes the all-reduce's first half, W5). */
 static uint32_t ring_chunk(uint32_t kind, uint32_t N, uint32_t i, uint32_t s)
 {
-    if (kind == KIND_RING_AG || s < N - 1) return (uint32_t)(((int64_t)i - s % N + N) % N);
+    if (kind != KIND_RING_AR || s < N - 1) return (uint32_t)(((int64_t)i - s % N + N) % N);
     uint32_t s2 = s - (N - 1);
     return (uint32_t)(((int64_t)i + 1 - s2 + 2 * (int64_t)N) % N);
 }
@@ -373,10 +400,30 @@ static int count_workload(const orc_batch *b, uint32_t e, uint64_t *nconn, uint6
         }
         uint64_t P = ceil_div(b->coll_bytes[ci], pkt);
         uint32_t kind = b->coll_type[ci];
-        if (kind == KIND_RING_AR || kind == KIND_RING_AG) {
+        uint32_t gate = b->coll_gate ? b->coll_gate[ci] : NONE;
+        if (gate != NONE) {
+            /* W6: the gate is an earlier send/recv of this workload whose receivers are these members */
+            uint32_t gi = b->work_coll_off[w] + gate;
+            if (!is_ring(kind) || gi >= ci || b->coll_type[gi] != KIND_SENDRECV) return ORC_E_INVALID;
+            if (b->coll_member_off[gi + 1] - b->coll_member_off[gi] != N + 1) return ORC_E_INVALID;
+            for (uint32_t i = 0; i < N; i++)
+                if (b->member_host[b->coll_member_off[gi] + 1 + i] != b->member_host[m0 + i]) return ORC_E_INVALID;
+            for (uint32_t cj = b->work_coll_off[w]; cj < ci; cj++)   /* a send/recv gates one collective */
+                if (b->coll_gate[cj] == gate) return ORC_E_INVALID;
+        }
+        if (is_ring(kind) || kind == KIND_TREE) {
             uint32_t NC = b->coll_nc[ci];
             if (N < 2 || NC < 1 || b->coll_chunk_bytes[ci] == 0 || b->coll_chunk_bytes[ci] % pkt) return ORC_E_INVALID;
             uint64_t p = b->coll_chunk_bytes[ci] / pkt;
+            if (kind == KIND_TREE) {
+                for (uint32_t c = 0; c < NC; c++) {
+                    uint64_t Pc = P / NC + (c < P % NC);
+                    if (Pc < 1) return ORC_E_INVALID;
+                    *nflow += ceil_div(Pc, p) * 2 * (N - 1);
+                    *nconn += 2 * (N - 1);
+                }
+                continue;
+            }
             uint64_t S = kind == KIND_RING_AR ? 2ull * (N - 1) : (uint64_t)(N - 1);
             for (uint32_t c = 0; c < NC; c++) {
                 uint64_t Pc = P / NC + (c < P % NC);
@@ -391,6 +438,10 @@ static int count_workload(const orc_batch *b, uint32_t e, uint64_t *nconn, uint6
             if (N < 2 || K < 1 || K > P) return ORC_E_INVALID;
             *nconn += N - 1;
             *nflow += (uint64_t)(N - 1) * K;
+        } else if (kind == KIND_SENDRECV) {
+            if (N < 2 || P < 1 || P >= NONE) return ORC_E_INVALID;
+            *nconn += N - 1;
+            *nflow += N - 1;
         } else {
             return ORC_E_INVALID;
         }
@@ -434,12 +485,17 @@ static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
     if (!x->conn || !x->flow || !x->conn_flows) return ORC_E_NOMEM;
     x->n_conn = 0;
     uint32_t f = 0;
+    uint32_t ncoll = b->work_coll_off[w + 1] - b->work_coll_off[w];
+    uint32_t *coll_f0 = (uint32_t *)calloc(ncoll ? ncoll : 1, sizeof(uint32_t));   /* first flow of each collective */
+    if (!coll_f0) return ORC_E_NOMEM;
     for (uint32_t ci = b->work_coll_off[w]; ci < b->work_coll_off[w + 1]; ci++) {
         const uint32_t *mem = b->member_host + b->coll_member_off[ci];
         uint32_t N = b->coll_member_off[ci + 1] - b->coll_member_off[ci];
         uint64_t P = ceil_div(b->coll_bytes[ci], pkt);
         uint32_t kind = b->coll_type[ci];
-        if (kind == KIND_RING_AR || kind == KIND_RING_AG) {
+        uint32_t gate = b->coll_gate ? b->coll_gate[ci] : NONE;
+        coll_f0[ci - b->work_coll_off[w]] = f;
+        if (is_ring(kind)) {
             uint32_t NC = b->coll_nc[ci];
             uint64_t p = b->coll_chunk_bytes[ci] / pkt;
             uint32_t S = kind == KIND_RING_AR ? 2 * (N - 1) : N - 1;
@@ -463,11 +519,59 @@ static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
                                 add_pred(x, f, fbase + (uint32_t)((r * S + s - 1) * N + i), PRED_SEND);
                             } else if (r >= 1) {
                                 add_pred(x, f, fbase + (uint32_t)(((r - 1) * S + S - 1) * N + i), PRED_SEND);
+                            } else if (gate != NONE) {
+                                /* W6: rank i starts once its piece from the send/recv has arrived */
+                                add_pred(x, f, coll_f0[gate] + i, PRED_RECV);
                             }
                             f++;
                         }
                     }
                 }
+            }
+        } else if (kind == KIND_TREE) {
+            /* W7: binary tree in member order (parent of i is (i-1)/2); per chunk,
+             * every node reduces up once all its children's pieces arrived, and
+             * the result flows back down from the root */
+            uint32_t NC = b->coll_nc[ci];
+            uint64_t p = b->coll_chunk_bytes[ci] / pkt;
+            uint32_t E = 2 * (N - 1);   /* connections per channel: up of node i at i-1, down at N-1+i-1 */
+            for (uint32_t c = 0; c < NC; c++) {
+                uint64_t Pc = P / NC + (c < P % NC);
+                uint64_t R = ceil_div(Pc, p);
+                uint32_t conn0 = x->n_conn;
+                for (uint32_t i = 1; i < N; i++) add_conn(x, mem[i], mem[(i - 1) / 2]);
+                for (uint32_t i = 1; i < N; i++) add_conn(x, mem[(i - 1) / 2], mem[i]);
+                uint32_t fbase = f;   /* flow (k, connection j) = fbase + k*E + j */
+                for (uint64_t k = 0; k < R; k++) {
+                    uint32_t size = (uint32_t)(k + 1 < R ? p : Pc - (R - 1) * p);
+                    uint32_t fk = fbase + (uint32_t)(k * E);
+                    for (uint32_t j = 0; j < E; j++) {
+                        set_flow(x, f, conn0 + j, size);
+                        if (j < N - 1) {
+                            uint32_t i = j + 1;
+                            for (uint32_t ch = 2 * i + 1; ch <= 2 * i + 2 && ch < N; ch++)
+                                add_pred(x, f, fk + ch - 1, PRED_RECV);
+                        } else {
+                            uint32_t i = j - (N - 1) + 1, par = (i - 1) / 2;
+                            if (par == 0) {
+                                for (uint32_t ch = 1; ch <= 2 && ch < N; ch++) add_pred(x, f, fk + ch - 1, PRED_RECV);
+                            } else {
+                                add_pred(x, f, fk + (N - 1) + par - 1, PRED_RECV);
+                            }
+                        }
+                        if (k >= 1) add_pred(x, f, fk - E + j, PRED_SEND);
+                        f++;
+                    }
+                }
+            }
+        } else if (kind == KIND_SENDRECV) {
+            /* W6: member 0 sends the whole message to members 1, 2, ... one after another */
+            uint32_t conn0 = x->n_conn;
+            for (uint32_t j = 1; j < N; j++) add_conn(x, mem[0], mem[j]);
+            for (uint32_t j = 0; j + 1 < N; j++) {
+                set_flow(x, f, conn0 + j, (uint32_t)P);
+                if (j >= 1) add_pred(x, f, f - 1, PRED_SEND);
+                f++;
             }
         } else { /* KIND_BCAST */
             uint32_t K = b->coll_k[ci];
@@ -486,6 +590,7 @@ static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
             }
         }
     }
+    free(coll_f0);
     for (uint64_t xi = b->work_xflow_off[w]; xi < b->work_xflow_off[w + 1]; xi++) {
         uint32_t c = add_conn(x, b->xflow_src[xi], b->xflow_dst[xi]);
         set_flow(x, f, c, b->xflow_pkts[xi]);

@@ -48,7 +48,7 @@ class _Batch(C.Structure):
                 ("coll_member_off", _P32), ("member_host", _P32),
                 ("work_xflow_off", _P64), ("xflow_src", _P32), ("xflow_dst", _P32), ("xflow_pkts", _P32),
                 ("exp_topo", _P32), ("exp_work", _P32), ("exp_queue_pkts", _P32),
-                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32)]
+                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32), ("coll_gate", _P32)]
 
 
 class _Result(C.Structure):
@@ -106,7 +106,8 @@ class OracleBatch:
                         _ptr(p.work_xflow_off, _P64), _ptr(p.xflow_src, _P32), _ptr(p.xflow_dst, _P32),
                         _ptr(p.xflow_pkts, _P32),
                         _ptr(p.exp_topo, _P32), _ptr(p.exp_work, _P32), _ptr(p.exp_queue_pkts, _P32),
-                        _ptr(p.exp_ecmp_seed, _P32), _ptr(p.exp_pkt_bytes, _P32))
+                        _ptr(p.exp_ecmp_seed, _P32), _ptr(p.exp_pkt_bytes, _P32),
+                        _ptr(p.coll_gate, _P32))
 
 
 def _as_oracle_batch(b) -> OracleBatch:

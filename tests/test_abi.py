@@ -130,3 +130,34 @@ def test_workspace_covers_flow_records(simmod):
     rec = [0, 3, 7]
     s = simmod.Sim(b, record=rec)
     assert s.workspace_bytes >= plain + 12 * sum(s.flow_count(e) for e in rec)
+
+
+def test_further_collectives_compile(simmod, oracle):
+    """Trees, reduce-scatters and send/recv unit tasks: flow counts equal the
+    oracle's, and only the ungated rings take the compact kernels."""
+    b = I.make_config(6, exp_ids=list(range(9)))
+    s = simmod.Sim(b)
+    for e in range(b.n_exp):
+        rc, nf, nc = oracle.count(b, e)
+        assert rc == 0 and s.flow_count(e) == nf
+    assert s.info()["n_compact"] == 3          # the three reduce-scatter experiments
+
+
+def test_gate_validation_errors(simmod):
+    topo = I.single_switch(5)
+    part = I.sendrecv(2 * I.PKT_BYTES, 0, [1, 2, 3])
+    for members, gate, first in (([2, 1, 3], 0, part), ([1, 2], 0, part), ([1, 2, 3], 1, part),
+                                 ([1, 2, 3], 0, I.bcast(2 * I.PKT_BYTES, [0, 1, 2, 3], 1))):
+        ag = I.ring(I.COLL_RING_AG, 6 * I.PKT_BYTES, members, 1, I.PKT_BYTES)
+        ag.gate = gate
+        expect_error(simmod, I.single_batch(topo, I.Workload([first, ag])), simmod.E_INVALID_SPEC)
+    # a send/recv gates one collective only
+    a1 = I.ring(I.COLL_RING_AG, 6 * I.PKT_BYTES, [1, 2, 3], 1, I.PKT_BYTES)
+    a2 = I.ring(I.COLL_RING_RS, 6 * I.PKT_BYTES, [1, 2, 3], 1, I.PKT_BYTES)
+    a1.gate = a2.gate = 0
+    expect_error(simmod, I.single_batch(topo, I.Workload([part, a1, a2])), simmod.E_INVALID_SPEC)
+    # trees need whole-packet chunks, send/recv at least one packet
+    w = I.Workload([I.tree(8 * I.PKT_BYTES, [0, 1, 2], 1, 100)])
+    expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
+    w = I.Workload([I.sendrecv(0, 0, [1, 2])])
+    expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)

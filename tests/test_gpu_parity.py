@@ -266,3 +266,85 @@ def test_block_size_does_not_matter(simmod, oracle, threads):
     o = oracle_all(oracle, b)
     for e in range(b.n_exp):
         assert_exp(r, e, o[e])
+
+
+# -------------------------------------- tree, reduce-scatter, send/recv unit tasks
+
+def collectives_batch(n, seed):
+    """Small seeded mix of the further collective shapes on three fabrics, with
+    random per-cable delays: trees of 2..16 members (1..3 channels, ragged last
+    chunks), ring reduce-scatters, and unit tasks in all three send/recv
+    strategies (the global all-gather gated on its scatter)."""
+    rng = np.random.default_rng(seed)
+    b = I.Batch([], [], [], "collectives")
+    fabrics = [I.single_switch(12), I.leaf_spine(3, 4, 2), I.fat_tree(4)]
+    for f in fabrics:
+        f.delay = rng.integers(1, 4, f.n_cables).astype(np.uint8)
+        b.topos.append(f)
+    for e in range(n):
+        ti = e % 3
+        hosts = [int(x) for x in rng.permutation(b.topos[ti].hosts())]
+        kind = (e // 3) % 3
+        if kind == 0:
+            N = int(rng.integers(2, min(12, len(hosts)) + 1))
+            P, p = int(rng.integers(1, 90)), int(rng.integers(1, 12))
+            colls = [I.tree(P * I.PKT_BYTES, hosts[:N], int(rng.integers(1, 4)) if P >= 3 else 1, p * I.PKT_BYTES)]
+            if N + 3 <= len(hosts):
+                colls.append(I.tree(40 * I.PKT_BYTES, hosts[N - 1:N + 3], 1, 3 * I.PKT_BYTES))
+        elif kind == 1:
+            N = int(rng.integers(2, 9))
+            p = int(rng.integers(1, 5))
+            colls = [I.ring(I.COLL_RING_RS, (N * p * int(rng.integers(1, 4)) + int(rng.integers(0, N))) * I.PKT_BYTES,
+                            hosts[:N], int(rng.integers(1, 3)), p * I.PKT_BYTES)]
+        else:
+            A, B = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+            nodes = [hosts[1 + a * B:1 + (a + 1) * B] for a in range(A)]
+            strat = ["sendrecv", "local_ag", "global_ag"][e % 3]
+            P = A * B * int(rng.integers(1, 6))
+            colls = I.unit_task(strat, P * I.PKT_BYTES, hosts[0], nodes, chunk_bytes=int(rng.integers(1, 3)) * I.PKT_BYTES)
+        b.works.append(I.Workload(colls))
+        b.exps.append(I.Experiment(ti, len(b.works) - 1, int(rng.integers(2, 20)), int(rng.integers(0, 2**32))))
+    return b
+
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_collectives_mix(simmod, oracle, force_global):
+    """Trees, reduce-scatters and unit tasks, every flow's ticks compared."""
+    b = collectives_batch(27, 11)
+    log("collectives mix", b.n_exp, "force_global", force_global)
+    s, r = gpu_run(simmod, b, record=range(b.n_exp), force_global=force_global)
+    o = oracle_all(oracle, b, flows=True)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+        assert_flows(s, e, o[e])
+
+
+def test_collective_hand_traces_gpu(simmod, oracle):
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "collective_traces.json")))
+    b = I.Batch([I.single_switch(3)], [], [], "collective traces")
+    b.works.append(I.Workload([I.tree(2 * I.PKT_BYTES, [0, 1, 2], 1, 2 * I.PKT_BYTES)]))
+    b.works.append(I.Workload(I.unit_task("global_ag", 4 * I.PKT_BYTES, 0, [[1], [2]], chunk_bytes=2 * I.PKT_BYTES)))
+    b.exps = [I.Experiment(0, 0, 16, 0), I.Experiment(0, 1, 16, 0)]
+    s, r = gpu_run(simmod, b, record=[0, 1])
+    for e, name in enumerate(("T1_tree3", "T2_global_ag")):
+        c = g[name]
+        assert int(r["tick"][e]) == c["t_end"] and int(r["pkt_hops"][e]) == c["pkt_hops"]
+        ft = s.flow_ticks(e)
+        assert [int(x) for x in ft["rd"]] == c["rd"]
+        assert [int(x) for x in ft["act"]] == c["act"]
+        assert [int(x) for x in ft["sd"]] == c["sd"]
+
+
+def test_c6_sample(simmod, oracle):
+    """Full-size C6 experiments: a tree batch, two reduce-scatter batches and
+    the three unit-task strategies."""
+    ids = [0, 1, 2, 4, 5, 8]
+    b = I.make_config(6, exp_ids=ids)
+    log("C6 sample", ids)
+    s, r = gpu_run(simmod, b, record=[2, 4, 5])
+    o = oracle_all(oracle, b, flows=False)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+    for e in (2, 4, 5):
+        assert_flows(s, e, oracle.run(b, e, flows=True))
