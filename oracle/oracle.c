@@ -108,6 +108,10 @@
  * Pins (tests/test_oracle_pins.py): closed forms for a single flow, NC = 1
  * rings and the pipelined broadcast; four hand traces; conservation, per-flow
  * bounds and route lengths against an independent breadth-first search.
+ * (tests/test_oracle_collectives.py): two hand traces (a tree, a gated global
+ * all-gather), closed forms for two-member trees, sequential sends and the
+ * send/recv strategies, reduce-scatter equal to all-gather, and the W6/W7
+ * predecessor rules rebuilt in the test and checked through activation ticks.
  * Parity unpinned (the pages fix no value): which of several equal-cost ECMP
  * candidates the hash picks (only validity and length of a route are pinned),
  * the digest mixer (a checksum; per-flow ticks are compared as well), and the
