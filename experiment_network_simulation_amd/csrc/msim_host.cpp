@@ -631,6 +631,7 @@ struct msim_ctx {
     uint32_t k_base[MSIM_KINDS] = {}, k_count[MSIM_KINDS] = {}, k_block[MSIM_KINDS] = {};
     uint32_t k_grid[MSIM_KINDS] = {}, k_lds[MSIM_KINDS] = {};
     uint64_t max_arena = 0;
+    uint64_t max_exp_hops = 0;   /* largest packet-hop total of one experiment */
     uint8_t *ws = nullptr;
     bool bound = false;
     std::string err;
@@ -729,6 +730,7 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
         I.total_flows += c.n_flows;
         I.total_conns += c.n_conns;
         I.est_pkt_hops += c.est_hops;
+        ctx->max_exp_hops = std::max(ctx->max_exp_hops, c.est_hops);
         I.est_delivered += c.est_delivered;
     }
     for (uint32_t e = 0; e < E; e++) ctx->pristine_off[e] = take(ctx->exps[e].bytes - ctx->exps[e].rw_off);
@@ -924,10 +926,13 @@ extern "C" int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *stream, uint32_
     if (!ctx) return MSIM_E_ARG;
     if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_run before msim_bind");
     (void)flags;
-    /* launches of at most 2^30 ticks each: the kernels count a port's
-     * packet-hops of one launch in 32 bits (rate <= 4) */
+    /* The kernels count a port's packet-hops of one launch in 32 bits.  A port
+     * never sends more than its experiment's packet-hop total, so one launch
+     * suffices unless an experiment reaches 2^32 packet-hops; then launches of
+     * at most 2^30 ticks keep every port (rate <= 4) below 2^32 per launch. */
+    const uint64_t step = ctx->max_exp_hops < (1ull << 32) ? max_ticks : MSIM_LAUNCH_TICKS;
     for (uint64_t left = max_ticks; left > 0;) {
-        const uint32_t chunk = left > MSIM_LAUNCH_TICKS ? MSIM_LAUNCH_TICKS : (uint32_t)left;
+        const uint32_t chunk = (uint32_t)(left > step ? step : left);
         left -= chunk;
         bool first = true;
         for (uint32_t k = 0; k < MSIM_KINDS; k++) {

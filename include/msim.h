@@ -164,9 +164,10 @@ int msim_bind(msim_ctx *ctx, void *dev_workspace, uint64_t ws_bytes, void *hip_s
 /*
  * Launches the simulation of every unfinished experiment for at most max_ticks
  * more ticks each, as one kernel launch per kernel kind present in the batch on
- * hip_stream (asynchronous; one launch per batch, Multiverse section 4.3).  A
- * max_ticks above 2^30 is split into consecutive launches of at most 2^30
- * ticks, with the same result.  Experiments are independent; their state
+ * hip_stream (asynchronous; one launch per batch, Multiverse section 4.3).  In a
+ * batch where some experiment moves 2^32 or more packet-hops, a max_ticks above
+ * 2^30 is split into consecutive launches of at most 2^30 ticks, with the same
+ * result.  Experiments are independent; their state
  * stays in the workspace between calls, so several calls continue where the
  * previous one stopped.  Returns MSIM_OK once enqueued; per-experiment outcome
  * comes from msim_results.  flags: reserved, pass 0.
