@@ -477,14 +477,20 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             take(H.o_hout, (size_t)dt * nconn);
             H.rw_off = (uint32_t)off;
             take(H.o_arr, Vc);
-            take(H.o_head, Vc);
+            if (R != 1) take(H.o_head, Vc);
+            else H.o_head = 0;
             take(H.o_nslot, Vc);
             take(H.o_pdesc, (size_t)dt * S * Q);
             take(H.o_pnxt, (size_t)S * Q);
             take(H.o_popped, 8ull * nt);
             const uint32_t RP = R <= 1 ? 1 : (R <= 2 ? 2 : 4);
-            if (R == 1) take(H.o_elig, 4ull * nt);
-            else H.o_elig = 0;
+            if (R == 1) {
+                take(H.o_elig, 4ull * nt);
+                take(H.o_fmask, 8ull * S);
+            } else {
+                H.o_elig = 0;
+                H.o_fmask = 0;
+            }
             take(H.o_sdesc, (size_t)dt * nt * W * RP);
             take(H.o_crw, sizeof(CRW2) * nconn);
             H.lds_bytes = (uint32_t)off;
@@ -545,7 +551,9 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                         pv[sl].left = left[P.host];
                     } else {
                         R2.vbase = sw_of[port_node[p]] * rsz * rsz;
-                        pv[sl].freem = Q == 64 ? ~0ull : ((1ull << Q) - 1ull);
+                        const uint64_t all = Q == 64 ? ~0ull : ((1ull << Q) - 1ull);
+                        if (R == 1) ((uint64_t *)(A + H.o_fmask))[sl - SB] = all;
+                        else pv[sl].freem = all;
                     }
                 }
                 memcpy(A, &H, sizeof H);

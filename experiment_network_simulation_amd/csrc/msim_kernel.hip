@@ -664,6 +664,7 @@ struct CCtx {
     const LDSP uint8_t *lidx;
     LDSP CRW2 *crw;
     LDSP uint32_t *elig;       /* rate 1: per output, inputs with a non-empty queue toward it */
+    LDSP uint64_t *fmask;      /* rate 1: per switch ingress (slot - SB), its free buffer slots */
     const LDSP CGrp *grp;
     LDSP DT *pdesc, *sdesc;
     uint32_t *rec;
@@ -861,6 +862,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     C.lidx = (const LDSP uint8_t *)(L + H->o_lidx);
     C.crw = (LDSP CRW2 *)(L + H->o_crw);
     C.elig = (LDSP uint32_t *)(L + H->o_elig);
+    C.fmask = (LDSP uint64_t *)(L + H->o_fmask);
     C.grp = (const LDSP CGrp *)(L + H->o_grp);
     C.pdesc = (LDSP DT *)(L + H->o_pdesc);
     C.sdesc = (LDSP DT *)(L + H->o_sdesc);
@@ -881,13 +883,14 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     const bool peer_host = pr.flags & PF_PEER_HOST;
     constexpr uint32_t RSZ = 8u * W;              /* bytes per VOQ row: one per input port */
     const uint32_t deg = pr.deg, local = pr.local, Q = C.Q;
+    /* byte rows of the counter-based queues (rate-1 kinds keep their queue state in LDS) */
     Row<W> tslot, fcur, hseen, phead, arrv;
-    tslot.w0 = pv.tslot[0]; tslot.w1 = pv.tslot[1];
-    fcur.w0 = pv.fcur[0]; fcur.w1 = pv.fcur[1];
-    hseen.w0 = pv.hseen[0]; hseen.w1 = pv.hseen[1];
-    phead.w0 = pv.phead[0]; phead.w1 = pv.phead[1];
-    arrv.w0 = pv.arrv[0]; arrv.w1 = pv.arrv[1];
-    uint64_t freem = pv.freem;
+    tslot.w0 = R1 ? 0 : pv.tslot[0]; tslot.w1 = R1 ? 0 : pv.tslot[1];
+    fcur.w0 = R1 ? 0 : pv.fcur[0]; fcur.w1 = R1 ? 0 : pv.fcur[1];
+    hseen.w0 = R1 ? 0 : pv.hseen[0]; hseen.w1 = R1 ? 0 : pv.hseen[1];
+    phead.w0 = R1 ? 0 : pv.phead[0]; phead.w1 = R1 ? 0 : pv.phead[1];
+    arrv.w0 = R1 ? 0 : pv.arrv[0]; arrv.w1 = R1 ? 0 : pv.arrv[1];
+    uint64_t freem = R1 ? 0 : pv.freem;            /* rate 1: the free masks live in LDS */
     uint32_t popped = pv.popped, pushed = pv.pushed, rr = pv.rr;
     HostRegs hr;
     hr.ready = pv.ready;
@@ -919,7 +922,10 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     while (t < t_end) {
         /* ---------------- arrivals */
         if (R1 && is_sw) {
-            /* rate 1: at most one packet per ingress and tick */
+            /* rate 1: at most one packet per ingress and tick.  First carry the
+             * popped count through t-1 into the buffer that tick t+1 reads; the
+             * outputs add this tick's pops to it while they forward. */
+            C.popped[(tp ^ nt) + tid] = C.popped[tp + tid];
             LDSP DT *rec = C.sdesc + sb + myoff;
             const uint32_t e = rec[0];
             if (e != 0) {
@@ -927,23 +933,26 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 const uint32_t desc = e - 1;
                 const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
                 const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
-                if (freem == 0 || o >= deg) {
+                const uint64_t fm = C.fmask[pool];
+                if (fm == 0 || o >= deg) {
                     a.fault = 1;
                 } else {
                     uint32_t s;
                     if (q32) {
-                        const uint32_t lo = (uint32_t)freem;
+                        const uint32_t lo = (uint32_t)fm;
                         s = __builtin_ctz(lo);
-                        freem = lo & (lo - 1u);
+                        C.fmask[pool] = lo & (lo - 1u);
                     } else {
-                        s = __builtin_ctzll(freem);
-                        freem &= freem - 1;
+                        s = __builtin_ctzll(fm);
+                        C.fmask[pool] = fm & (fm - 1);
                     }
                     C.pdesc[cpool(C, pool, s)] = (DT)e;
                     const uint32_t vq = pr.vbase + o * RSZ + local;   /* queue (this input, o) */
                     LDSP uint32_t *el = C.elig + qbase + o;
                     /* the read precedes every lane's update of the mask, and only
-                     * this input changes its own bit during arrivals */
+                     * this input changes its own bit during arrivals; several
+                     * inputs of one switch may set bits of one mask in one
+                     * instruction, hence the atomic */
                     if (__hip_atomic_load(el, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & mybit) {
                         C.pnxt[cpool(C, pool, C.arr[vq])] = (uint8_t)s;
                     } else {
@@ -1034,18 +1043,27 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         dst += poff;
         if (R1 && is_sw && alive) {
             /* rate 1: one grant at most, cyclic from rr over the non-empty inputs */
+            /* one round of reads: the mask, the far credit, and this output's
+             * head-slot and tail-slot rows (one byte per input) */
             const uint32_t E = C.elig[tid];
             const int32_t credit = peer_host ? 1 : (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
+            Row<W> hrow, trow;
+            hrow.load(C.nslot + rowp);
+            trow.load(C.arr + rowp);
             if (E != 0 && credit > 0) {
                 const uint32_t up = E >> rr;
                 const uint32_t i = up ? rr + __builtin_ctz(up) : __builtin_ctz(E);
                 const uint32_t vq = rowp + i;                           /* queue (i, this output) */
                 const uint32_t qpool = qbase + i - SB;
-                const uint32_t s = C.nslot[vq];
+                const uint32_t s = hrow.get(i);
                 const uint32_t desc = C.pdesc[cpool(C, qpool, s)];
-                if (s == C.arr[vq]) C.elig[tid] = E & ~(1u << i);       /* popped the tail: now empty */
+                if (s == trow.get(i)) C.elig[tid] = E & ~(1u << i);     /* popped the tail: now empty */
                 else C.nslot[vq] = C.pnxt[cpool(C, qpool, s)];
-                C.head[pr.vbase + i * RSZ + local] = (uint8_t)(0x80u | s);
+                /* the slot goes straight back to the ingress's free mask and the
+                 * pop into its count for tick t+1 (other outputs of this switch
+                 * may hit the same ingress in the same instruction) */
+                __hip_atomic_fetch_or(C.fmask + qpool, 1ull << s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(C.popped + (tp ^ nt) + qbase + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 rr = i + 1 == deg ? 0 : i + 1;
                 ctransmit(C, a, desc, t, dst);
                 pushed++;
@@ -1066,10 +1084,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 C.nslot[vp] = C.pnxt[cpool(C, qpool, s)];
                 const uint32_t hb = phead.get((uint32_t)i) + 1;
                 phead.set((uint32_t)i, hb);
-                /* rate 1: at most one pop per queue and tick, so the queue's byte
-                 * carries the freed slot itself (flag 0x80 | slot); otherwise it
-                 * carries the running pop count */
-                C.head[pr.vbase + (uint32_t)i * RSZ + local] = (uint8_t)(R1 ? (0x80u | s) : hb);
+                C.head[pr.vbase + (uint32_t)i * RSZ + local] = (uint8_t)hb;   /* running pop count */
                 if (!R1) {
                     if (i < 8) v0 -= 1ull << (8 * i);
                     else v1 -= 1ull << (8 * (i - 8));
@@ -1110,34 +1125,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         }
         wave_lds_fence();
         /* ---------------- frees, and the popped count for tick t+1 */
-        if (is_sw && R1) {
-            Row<W> hd;
-            hd.load(C.head + rowp);
-            const uint64_t HB = 0x8080808080808080ull;
-            uint64_t m0 = hd.w0 & HB, m1 = W == 2 ? hd.w1 & HB : 0ull;
-            if (m0 | m1) {
-                popped += __popcll(m0) + (W == 2 ? __popcll(m1) : 0u);
-                /* bit 7 of byte o flags a pop by output o; bits 0..5 are the slot */
-                while (m0) {
-                    const uint32_t b7 = __builtin_ctzll(m0);
-                    const uint32_t s = (uint32_t)(hd.w0 >> (b7 - 7)) & 0x3Fu;
-                    if (q32) freem = (uint32_t)freem | (1u << s);
-                    else freem |= 1ull << s;
-                    m0 &= m0 - 1;
-                }
-                if (W == 2)
-                    while (m1) {
-                        const uint32_t b7 = __builtin_ctzll(m1);
-                        const uint32_t s = (uint32_t)(hd.w1 >> (b7 - 7)) & 0x3Fu;
-                        if (q32) freem = (uint32_t)freem | (1u << s);
-                        else freem |= 1ull << s;
-                        m1 &= m1 - 1;
-                    }
-                *(LDSP uint64_t *)(C.head + rowp) = 0ull;
-                if (W == 2) *(LDSP uint64_t *)(C.head + rowp + 8) = 0ull;
-            }
-            C.popped[(tp ^ nt) + tid] = popped;
-        } else if (is_sw) {
+        if (!R1 && is_sw) {
             Row<W> hd;
             hd.load(C.head + rowp);
             uint64_t d0 = bytes_sub(hd.w0, hseen.w0);

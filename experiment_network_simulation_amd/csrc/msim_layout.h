@@ -143,7 +143,7 @@ struct ArenaHdr2 {       /* 128 bytes */
     uint32_t lds_bytes;  /* [0, lds_bytes) is the LDS image */
     uint32_t nt, H, SB;
     uint32_t Q, W, R, n_conn;
-    uint32_t n_grp, rsz, dt, pad0;
+    uint32_t n_grp, rsz, dt, o_fmask;
     uint32_t o_arr, o_head, o_nslot, o_pdesc, o_pnxt, o_popped, o_elig, o_sdesc;
     uint32_t o_route, o_cgrp, o_lidx, o_crw, o_grp, o_hout;
     uint32_t o_port, o_priv;
@@ -159,10 +159,11 @@ struct ArenaHdr2 {       /* 128 bytes */
  * o_nslot is its head slot and in o_arr its tail slot; o_elig holds, per
  * switch output thread slot, a 32-bit mask of the inputs whose queue toward it
  * is non-empty (set by the ingress on an append to an empty queue, cleared by
- * the output when it pops the tail); byte o of ingress i's o_head row is
- * 0x80 | slot when output o popped that slot of i's pool this tick, else 0.
- * With a faster link, o_arr / o_head bytes are running append / pop counts and
- * o_elig is absent (0). */
+ * the output when it pops the tail); o_fmask holds each switch ingress's free
+ * buffer slots (64 bits, index slot - SB), taken by the ingress and returned by
+ * the output that pops; o_head is absent.  With a faster link, o_arr / o_head
+ * bytes are running append / pop counts, the free masks live in registers and
+ * o_elig / o_fmask are absent (0). */
 /* popped (switch ingress: packets forwarded out of it) is published twice,
  * indexed by tick parity: [(t&1) * nt + slot] holds the count through tick t-1
  * and is written at the end of tick t-1, so tick t's readers in other
