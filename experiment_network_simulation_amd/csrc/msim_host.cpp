@@ -468,6 +468,9 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             H.mode = MODE_COMPACT; H.n_flows = (uint32_t)n_flows;
             H.nt = nt; H.H = n_hosts; H.SB = SB;
             H.Q = Q; H.W = W; H.R = R; H.n_conn = nconn; H.n_grp = ngrp; H.rsz = rsz; H.dt = dt;
+            H.flags = 0;
+            if (std::all_of(grp.begin(), grp.end(), [](const Grp &g) { return g.kind == GK_RING_AR || g.kind == GK_RING_AG; }))
+                H.flags |= AF_RINGS_ONLY;
             size_t off = align16(sizeof(ArenaHdr2));
             auto take = [&](uint32_t &field, size_t bytes) { field = (uint32_t)off; off = align16(off + bytes); };
             take(H.o_route, 4ull * nconn);

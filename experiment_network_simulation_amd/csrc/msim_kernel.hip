@@ -714,31 +714,37 @@ __device__ __forceinline__ uint32_t cchunk(const CGrp &g, uint32_t i, uint32_t s
     return v;
 }
 
+/* RO: the experiment's groups are all rings, known for the whole experiment,
+ * so the kind tests below fold away instead of branching per lane. */
+template <bool RO>
 __device__ __forceinline__ uint32_t csize(const CGrp &g, uint32_t idx, uint32_t pos)
 {
-    if (g.kind == GK_BCAST) return g.p + (pos < g.Xq ? 1u : 0u);
+    if (!RO && g.kind == GK_BCAST) return g.p + (pos < g.Xq ? 1u : 0u);
     const uint32_t r = cdiv_S(g, pos);
     if (r + 1 < g.R) return g.p;
     const uint32_t k = cchunk(g, idx, pos - r * g.S);
     return g.Xq + (k < g.Xr ? 1u : 0u);
 }
 
+template <bool RO>
 __device__ __forceinline__ uint32_t cfid(const CGrp &g, uint32_t idx, uint32_t pos)
 {
-    if (g.kind == GK_XFLOW) return g.fid_base + idx;
-    if (g.kind == GK_BCAST) return g.fid_base + idx * g.S + pos;
+    if (!RO && g.kind == GK_XFLOW) return g.fid_base + idx;
+    if (!RO && g.kind == GK_BCAST) return g.fid_base + idx * g.S + pos;
     return g.fid_base + pos * g.N + idx;
 }
 
+template <bool RO>
 __device__ __forceinline__ uint32_t cflows(const CGrp &g)
 {
+    if (RO) return g.R * g.S;
     return g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
 }
 
-template <typename DT>
+template <bool RO, typename DT>
 __device__ __forceinline__ bool crecv_ok(const CCtx<DT> &C, const CGrp &g, uint32_t idx, uint32_t c, uint32_t pos)
 {
-    if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
+    if (RO || g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
         if (pos - cdiv_S(g, pos) * g.S == 0) return true;
         const uint32_t cin = g.conn_base + (idx == 0 ? g.N - 1u : idx - 1u);
         return C.crw[cin].r_pos >= pos;
@@ -752,46 +758,92 @@ struct HostRegs {
     uint32_t pcnt, p0, p1, p2, p3;
 };
 
-template <typename DT>
+template <bool RO, typename DT>
 __device__ __forceinline__ void cactivate(const CCtx<DT> &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t pos,
                                           const CGrp &g, uint32_t idx, uint32_t t)
 {
     C.crw[c].s_st = (uint16_t)(pos | (CS_ACTIVE << C_STATE_SHIFT));
-    if (g.kind != GK_XFLOW) C.crw[c].s_rem = (uint16_t)csize(g, idx, pos);
+    if (RO || g.kind != GK_XFLOW) C.crw[c].s_rem = (uint16_t)csize<RO>(g, idx, pos);
     hr.ready |= 1ull << C.lidx[c];
     a.last_act1 = t + 1;
-    if (C.rec) C.rec[C.n_flows + cfid(g, idx, pos)] = t;
+    if (C.rec) C.rec[C.n_flows + cfid<RO>(g, idx, pos)] = t;
 }
 
 /* Activates connection d (of group g) if it was waiting and is now ready.
  * The compact path carries rings, broadcasts and explicit flows only. */
-template <typename DT>
+template <bool RO, typename DT>
 __device__ __forceinline__ void cwake(const CCtx<DT> &C, Acc &a, HostRegs &hr, const CGrp &g, uint32_t d, uint32_t t)
 {
     if ((C.crw[d].s_st >> C_STATE_SHIFT) != CS_IDLE) return;
     const uint32_t didx = d - g.conn_base, dpos = C.crw[d].s_st & C_POS_MASK;
-    if (crecv_ok(C, g, didx, d, dpos)) cactivate(C, a, hr, d, dpos, g, didx, t);
+    if (crecv_ok<RO>(C, g, didx, d, dpos)) cactivate<RO>(C, a, hr, d, dpos, g, didx, t);
 }
 
 /* After a flow over connection c (group g, index idx) has been fully
  * received: the connection leaving this host whose next flow waits on it. */
-template <typename DT>
+template <bool RO, typename DT>
 __device__ __forceinline__ void cwake_dependents(const CCtx<DT> &C, Acc &a, HostRegs &hr, const CGrp &g, uint32_t idx,
                                                  uint32_t c, uint32_t t)
 {
-    if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) cwake(C, a, hr, g, g.conn_base + (idx + 1u == g.N ? 0u : idx + 1u), t);
-    else if (g.kind == GK_BCAST && idx + 1u < g.N) cwake(C, a, hr, g, c + 1, t);
+    if (RO || g.kind == GK_RING_AR || g.kind == GK_RING_AG)
+        cwake<RO>(C, a, hr, g, g.conn_base + (idx + 1u == g.N ? 0u : idx + 1u), t);
+    else if (g.kind == GK_BCAST && idx + 1u < g.N)
+        cwake<RO>(C, a, hr, g, c + 1, t);
 }
 
-template <typename DT>
+template <bool RO, typename DT>
 __device__ __forceinline__ void ccheck(const CCtx<DT> &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t t)
 {
     const CGrp g = cgrp_at(C, c);
     const uint32_t idx = c - g.conn_base;
     const uint32_t pos = C.crw[c].s_st & C_POS_MASK;
-    if (pos >= cflows(g)) C.crw[c].s_st = (uint16_t)(pos | (CS_DONE << C_STATE_SHIFT));
-    else if (crecv_ok(C, g, idx, c, pos)) cactivate(C, a, hr, c, pos, g, idx, t);
+    if (pos >= cflows<RO>(g)) C.crw[c].s_st = (uint16_t)(pos | (CS_DONE << C_STATE_SHIFT));
+    else if (crecv_ok<RO>(C, g, idx, c, pos)) cactivate<RO>(C, a, hr, c, pos, g, idx, t);
     else C.crw[c].s_st = (uint16_t)(pos | (CS_IDLE << C_STATE_SHIFT));
+}
+
+/* A host's arrivals (deliveries, receive completions, the activations they
+ * enable) and its pending activations (connections whose previous flow left
+ * last tick), phases A and B of the tick. */
+template <bool RO, bool R1, typename DT>
+__device__ __forceinline__ void chost_arrivals(const CCtx<DT> &C, Acc &a, HostRegs &hr, const PortRO2 &pr,
+                                               LDSP DT *rec, uint32_t t)
+{
+    bool any = false;
+    for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
+        const uint32_t e = rec[k];
+        if (e == 0) break;
+        any = true;
+        const uint32_t c = (e - 1) >> DESC_SHIFT;
+        LDSP CRW2 &cw = C.crw[c];
+        a.delivered++;
+        const uint32_t rem = cw.r_rem - 1u;
+        cw.r_rem = (uint16_t)rem;
+        if (rem) continue;
+        const CGrp g = cgrp_at(C, c);
+        const uint32_t idx = c - g.conn_base;
+        uint32_t pos = cw.r_pos;
+        const uint32_t fid = cfid<RO>(g, idx, pos);
+        a.digest += mix64(((uint64_t)fid << 32) | t);
+        a.tmax = t;
+        a.left--;
+        if (C.rec) C.rec[fid] = t;
+        pos++;
+        cw.r_pos = (uint16_t)pos;
+        if (pos < cflows<RO>(g)) cw.r_rem = (uint16_t)csize<RO>(g, idx, pos);
+        cwake_dependents<RO>(C, a, hr, g, idx, c, t);
+    }
+    if (any)
+        for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
+    if (t == 0) {
+        for (uint32_t j = 0; j < pr.n_out; j++) ccheck<RO>(C, a, hr, (uint32_t)C.hout[pr.vbase + j], t);
+    } else if (hr.pcnt) {
+        ccheck<RO>(C, a, hr, hr.p0, t);
+        if (hr.pcnt > 1) ccheck<RO>(C, a, hr, hr.p1, t);
+        if (hr.pcnt > 2) ccheck<RO>(C, a, hr, hr.p2, t);
+        if (hr.pcnt > 3) ccheck<RO>(C, a, hr, hr.p3, t);
+        hr.pcnt = 0;
+    }
 }
 
 /* Stages the m-th packet this output sends in tick t for arrival at t + delay:
@@ -877,6 +929,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
+    const bool rings_only = (H->flags & AF_RINGS_ONLY) != 0;   /* uniform: one experiment per workgroup */
     const bool is_host = tid < nh && (pr.flags & PF_USED);
     const bool is_sw = tid >= SB && (pr.flags & PF_USED);
     const bool alive = pr.flags & PF_ALIVE;
@@ -1000,41 +1053,9 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
         } else if (is_host) {
             LDSP DT *rec = C.sdesc + sb + myoff;
-            bool any = false;
-            for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
-                const uint32_t e = rec[k];
-                if (e == 0) break;
-                any = true;
-                const uint32_t c = (e - 1) >> DESC_SHIFT;
-                LDSP CRW2 &cw = C.crw[c];
-                a.delivered++;
-                const uint32_t rem = cw.r_rem - 1u;
-                cw.r_rem = (uint16_t)rem;
-                if (rem) continue;
-                const CGrp g = cgrp_at(C, c);
-                const uint32_t idx = c - g.conn_base;
-                uint32_t pos = cw.r_pos;
-                const uint32_t fid = cfid(g, idx, pos);
-                a.digest += mix64(((uint64_t)fid << 32) | t);
-                a.tmax = t;
-                a.left--;
-                if (C.rec) C.rec[fid] = t;
-                pos++;
-                cw.r_pos = (uint16_t)pos;
-                if (pos < cflows(g)) cw.r_rem = (uint16_t)csize(g, idx, pos);
-                cwake_dependents(C, a, hr, g, idx, c, t);
-            }
-            if (any)
-                for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
-            if (t == 0) {
-                for (uint32_t j = 0; j < pr.n_out; j++) ccheck(C, a, hr, (uint32_t)C.hout[pr.vbase + j], t);
-            } else if (hr.pcnt) {
-                ccheck(C, a, hr, hr.p0, t);
-                if (hr.pcnt > 1) ccheck(C, a, hr, hr.p1, t);
-                if (hr.pcnt > 2) ccheck(C, a, hr, hr.p2, t);
-                if (hr.pcnt > 3) ccheck(C, a, hr, hr.p3, t);
-                hr.pcnt = 0;
-            }
+            /* the ring-only copy costs registers the faster-link kinds do not have */
+            if (R1 && rings_only) chost_arrivals<R1, R1>(C, a, hr, pr, rec, t);
+            else chost_arrivals<false, R1>(C, a, hr, pr, rec, t);
         }
         wave_lds_fence();
         /* ---------------- forwarding */
@@ -1112,7 +1133,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     const uint32_t pos = cw.s_st & C_POS_MASK;
                     if (C.rec) {
                         const CGrp g = cgrp_at(C, c);
-                        C.rec[2 * C.n_flows + cfid(g, c - g.conn_base, pos)] = t + 1;
+                        C.rec[2 * C.n_flows + cfid<false>(g, c - g.conn_base, pos)] = t + 1;
                     }
                     cw.s_st = (uint16_t)(pos + 1);
                     if (hr.pcnt == 0) hr.p0 = c;

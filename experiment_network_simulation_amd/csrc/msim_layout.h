@@ -138,7 +138,7 @@ struct ArenaHdr {        /* general format header */
 #define C_POS_MASK 0x3FFFu   /* CRW2.s_st: flow position (14 bits) | state << 14 */
 #define C_STATE_SHIFT 14
 
-struct ArenaHdr2 {       /* 128 bytes */
+struct ArenaHdr2 {       /* 144 bytes */
     uint32_t mode, bytes, rw_off, n_flows;
     uint32_t lds_bytes;  /* [0, lds_bytes) is the LDS image */
     uint32_t nt, H, SB;
@@ -147,7 +147,9 @@ struct ArenaHdr2 {       /* 128 bytes */
     uint32_t o_arr, o_head, o_nslot, o_pdesc, o_pnxt, o_popped, o_elig, o_sdesc;
     uint32_t o_route, o_cgrp, o_lidx, o_crw, o_grp, o_hout;
     uint32_t o_port, o_priv;
+    uint32_t flags, pad1[3];     /* AF_* */
 };
+#define AF_RINGS_ONLY 1u         /* every collective group is a ring */
 /* Buffer pools are slot-major: slot s of the ingress on switch thread slot
  * SB + j lives at index s * (nt - SB) + j of pdesc / pnxt, so lanes touching
  * the same slot number of their own pools hit different LDS banks.
