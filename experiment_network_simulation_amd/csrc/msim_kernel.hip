@@ -665,6 +665,8 @@ struct CCtx {
     LDSP CRW2 *crw;
     LDSP uint32_t *elig;       /* rate 1: per output, inputs with a non-empty queue toward it */
     LDSP uint64_t *fmask;      /* rate 1: per switch ingress (slot - SB), its free buffer slots */
+    LDSP uint8_t *L;           /* the LDS image, and byte offsets of two of its arrays */
+    uint32_t o_nslot, o_pnxt;
     const LDSP CGrp *grp;
     LDSP DT *pdesc, *sdesc;
     uint32_t *rec;
@@ -802,12 +804,10 @@ __device__ __forceinline__ void ccheck(const CCtx<DT> &C, Acc &a, HostRegs &hr, 
     else C.crw[c].s_st = (uint16_t)(pos | (CS_IDLE << C_STATE_SHIFT));
 }
 
-/* A host's arrivals (deliveries, receive completions, the activations they
- * enable) and its pending activations (connections whose previous flow left
- * last tick), phases A and B of the tick. */
+/* A host's arrivals: deliveries, receive completions and the activations
+ * they enable (phases A and B of the tick). */
 template <bool RO, bool R1, typename DT>
-__device__ __forceinline__ void chost_arrivals(const CCtx<DT> &C, Acc &a, HostRegs &hr, const PortRO2 &pr,
-                                               LDSP DT *rec, uint32_t t)
+__device__ __forceinline__ void chost_deliver(const CCtx<DT> &C, Acc &a, HostRegs &hr, LDSP DT *rec, uint32_t t)
 {
     bool any = false;
     for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
@@ -835,6 +835,13 @@ __device__ __forceinline__ void chost_arrivals(const CCtx<DT> &C, Acc &a, HostRe
     }
     if (any)
         for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
+}
+
+/* A host's pending activations (phase B): every connection at t = 0, then the
+ * connections whose previous flow left during the last tick. */
+template <bool RO, typename DT>
+__device__ __forceinline__ void chost_pending(const CCtx<DT> &C, Acc &a, HostRegs &hr, const PortRO2 &pr, uint32_t t)
+{
     if (t == 0) {
         for (uint32_t j = 0; j < pr.n_out; j++) ccheck<RO>(C, a, hr, (uint32_t)C.hout[pr.vbase + j], t);
     } else if (hr.pcnt) {
@@ -915,6 +922,9 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     C.crw = (LDSP CRW2 *)(L + H->o_crw);
     C.elig = (LDSP uint32_t *)(L + H->o_elig);
     C.fmask = (LDSP uint64_t *)(L + H->o_fmask);
+    C.L = L;
+    C.o_nslot = H->o_nslot;
+    C.o_pnxt = H->o_pnxt;
     C.grp = (const LDSP CGrp *)(L + H->o_grp);
     C.pdesc = (LDSP DT *)(L + H->o_pdesc);
     C.sdesc = (LDSP DT *)(L + H->o_sdesc);
@@ -1005,13 +1015,16 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     /* the read precedes every lane's update of the mask, and only
                      * this input changes its own bit during arrivals; several
                      * inputs of one switch may set bits of one mask in one
-                     * instruction, hence the atomic */
-                    if (__hip_atomic_load(el, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & mybit) {
-                        C.pnxt[cpool(C, pool, C.arr[vq])] = (uint8_t)s;
-                    } else {
-                        C.nslot[vq] = (uint8_t)s;
-                        __hip_atomic_fetch_or(el, mybit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    }
+                     * instruction, hence the atomic.  Without branches: the new
+                     * slot goes to the head byte of an empty queue or behind the
+                     * tail of a non-empty one, and the OR adds nothing if the
+                     * queue was non-empty. */
+                    const uint32_t tail = C.arr[vq];
+                    const uint32_t nonempty = __hip_atomic_load(el, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & mybit;
+                    const uint32_t keep = 0u - (nonempty >> local);          /* all ones if non-empty */
+                    const uint32_t at_head = C.o_nslot + vq, at_tail = C.o_pnxt + cpool(C, pool, tail);
+                    C.L[at_head ^ ((at_head ^ at_tail) & keep)] = (uint8_t)s;
+                    __hip_atomic_fetch_or(el, mybit & ~keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                     C.arr[vq] = (uint8_t)s;
                 }
             }
@@ -1054,8 +1067,13 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         } else if (is_host) {
             LDSP DT *rec = C.sdesc + sb + myoff;
             /* the ring-only copy costs registers the faster-link kinds do not have */
-            if (R1 && rings_only) chost_arrivals<R1, R1>(C, a, hr, pr, rec, t);
-            else chost_arrivals<false, R1>(C, a, hr, pr, rec, t);
+            if (R1 && rings_only) {
+                chost_deliver<R1, R1>(C, a, hr, rec, t);
+                chost_pending<R1>(C, a, hr, pr, t);
+            } else {
+                chost_deliver<false, R1>(C, a, hr, rec, t);
+                chost_pending<false>(C, a, hr, pr, t);
+            }
         }
         wave_lds_fence();
         /* ---------------- forwarding */
@@ -1078,8 +1096,12 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 const uint32_t qpool = qbase + i - SB;
                 const uint32_t s = hrow.get(i);
                 const uint32_t desc = C.pdesc[cpool(C, qpool, s)];
-                if (s == trow.get(i)) C.elig[tid] = E & ~(1u << i);     /* popped the tail: now empty */
-                else C.nslot[vq] = C.pnxt[cpool(C, qpool, s)];
+                /* popping the tail empties the queue; the head byte of an empty
+                 * queue is rewritten by the next append, so both stores can go
+                 * unconditionally */
+                const bool emptied = s == trow.get(i);
+                C.elig[tid] = emptied ? E & ~(1u << i) : E;
+                C.nslot[vq] = C.pnxt[cpool(C, qpool, s)];
                 /* the slot goes straight back to the ingress's free mask and the
                  * pop into its count for tick t+1 (other outputs of this switch
                  * may hit the same ingress in the same instruction) */
@@ -1136,10 +1158,11 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                         C.rec[2 * C.n_flows + cfid<false>(g, c - g.conn_base, pos)] = t + 1;
                     }
                     cw.s_st = (uint16_t)(pos + 1);
-                    if (hr.pcnt == 0) hr.p0 = c;
-                    else if (hr.pcnt == 1) hr.p1 = c;
-                    else if (hr.pcnt == 2) hr.p2 = c;
-                    else hr.p3 = c;
+                    /* append c to the pending list (selects, not branches) */
+                    hr.p0 = hr.pcnt == 0 ? c : hr.p0;
+                    hr.p1 = hr.pcnt == 1 ? c : hr.p1;
+                    hr.p2 = hr.pcnt == 2 ? c : hr.p2;
+                    hr.p3 = hr.pcnt == 3 ? c : hr.p3;
                     hr.pcnt++;
                 }
             }
@@ -1260,7 +1283,9 @@ __device__ void megakernel_body(const KParams &kp)
     for (;;) {
         if (threadIdx.x == 0) sh.exp = atomicAdd(&wh->claim[KIND], 1u);
         __syncthreads();
-        const uint32_t e = sh.exp;
+        /* the same for every lane: saying so keeps everything derived from it
+         * (arena, header fields, per-experiment flags) in scalar registers */
+        const uint32_t e = __builtin_amdgcn_readfirstlane(sh.exp);
         __syncthreads();
         if (e >= kp.n_run) break;
         const uint32_t x = order[e];
