@@ -42,6 +42,11 @@ COLL_TREE_AR = 5        # binary-tree all-reduce, pipelined in chunks
 COLL_SENDRECV = 6       # one source sends the whole message to each receiver in turn
 NO_GATE = 0xFFFFFFFF
 
+# Task kinds of a workload's task graph (values are part of the C ABI).
+TASK_COMPUTE = 0        # a computation of `ticks` ticks
+TASK_INTRA = 1          # an intra-server collective: alpha + ceil(bytes / beta) ticks
+TASK_COLL = 2           # a collective of the workload, simulated packet by packet
+
 KIB = 1024
 MIB = 1024 * 1024
 PKT_BYTES = 4096
@@ -206,11 +211,36 @@ class Collective:
 
 
 @dataclass
+class Task:
+    """A node of the workload's task graph: it starts once every predecessor
+    (an index of an earlier task) has finished."""
+    kind: int
+    ticks: int = 0             # compute: duration; intra-server: alpha (ticks)
+    nbytes: int = 0            # intra-server: message bytes
+    beta: int = 1              # intra-server: bytes per tick
+    coll: int = -1             # collective task: index of the collective in the workload
+    preds: List[int] = field(default_factory=list)
+
+
+def compute(ticks: int, preds: Sequence[int] = ()) -> Task:
+    return Task(TASK_COMPUTE, int(ticks), preds=[int(p) for p in preds])
+
+
+def intra(alpha: int, nbytes: int, beta: int, preds: Sequence[int] = ()) -> Task:
+    return Task(TASK_INTRA, int(alpha), int(nbytes), int(beta), preds=[int(p) for p in preds])
+
+
+def comm(coll: int, preds: Sequence[int] = ()) -> Task:
+    return Task(TASK_COLL, coll=int(coll), preds=[int(p) for p in preds])
+
+
+@dataclass
 class Workload:
     colls: List[Collective] = field(default_factory=list)
     xsrc: np.ndarray = field(default_factory=lambda: np.zeros(0, np.uint32))
     xdst: np.ndarray = field(default_factory=lambda: np.zeros(0, np.uint32))
     xpkts: np.ndarray = field(default_factory=lambda: np.zeros(0, np.uint32))
+    tasks: List[Task] = field(default_factory=list)
 
 
 def ring(kind: int, nbytes: int, members: Sequence[int], nc: int, chunk_bytes: int) -> Collective:
@@ -338,6 +368,14 @@ class PackedBatch:
     coll_member_off: np.ndarray  # uint32 [n_coll+1]
     member_host: np.ndarray      # uint32
     coll_gate: np.ndarray        # uint32 (NO_GATE, or a collective index within the workload)
+    work_task_off: np.ndarray    # uint32 [n_work+1]
+    task_type: np.ndarray        # uint8
+    task_ticks: np.ndarray       # uint32
+    task_bytes: np.ndarray       # uint64
+    task_beta: np.ndarray        # uint32
+    task_coll: np.ndarray        # uint32
+    task_pred_off: np.ndarray    # uint32 [n_task+1]
+    task_pred: np.ndarray        # uint32 (task indices within the workload)
     work_xflow_off: np.ndarray   # uint64 [n_work+1]
     xflow_src: np.ndarray        # uint32
     xflow_dst: np.ndarray
@@ -367,6 +405,13 @@ class PackedBatch:
         m_off = np.zeros(len(colls) + 1, np.uint32)
         for i, c in enumerate(colls):
             m_off[i + 1] = m_off[i] + len(c.members)
+        tasks = [k for w in b.works for k in w.tasks]
+        w_task_off = np.zeros(len(b.works) + 1, np.uint32)
+        for i, w in enumerate(b.works):
+            w_task_off[i + 1] = w_task_off[i] + len(w.tasks)
+        p_off = np.zeros(len(tasks) + 1, np.uint32)
+        for i, k in enumerate(tasks):
+            p_off[i + 1] = p_off[i] + len(k.preds)
         return PackedBatch(
             n_topo=len(b.topos), n_work=len(b.works), n_exp=len(b.exps),
             topo_node_off=t_node_off,
@@ -387,6 +432,14 @@ class PackedBatch:
             coll_member_off=m_off,
             member_host=np.asarray([m for c in colls for m in c.members], np.uint32),
             coll_gate=np.asarray([c.gate for c in colls], np.uint32),
+            work_task_off=w_task_off,
+            task_type=np.asarray([k.kind for k in tasks], np.uint8),
+            task_ticks=np.asarray([k.ticks for k in tasks], np.uint32),
+            task_bytes=np.asarray([k.nbytes for k in tasks], np.uint64),
+            task_beta=np.asarray([k.beta for k in tasks], np.uint32),
+            task_coll=np.asarray([k.coll & 0xFFFFFFFF for k in tasks], np.uint32),
+            task_pred_off=p_off,
+            task_pred=np.asarray([q for k in tasks for q in k.preds], np.uint32),
             work_xflow_off=w_x_off,
             xflow_src=cat([w.xsrc for w in b.works], np.uint32),
             xflow_dst=cat([w.xdst for w in b.works], np.uint32),

@@ -96,6 +96,19 @@
  *      once the root has it from all its children, and every other node's
  *      children once that node has received it from its parent.  Each
  *      connection sends its chunks in order (SEND on chunk k-1).
+ *  W8  Task graph (the System Simulator's compute graph, Multiverse section 3.1;
+ *      the Schedule and AnalyticalSys systems of section 3.2): per workload a
+ *      list of tasks in topological order, each a computation of D ticks, an
+ *      intra-server collective of D = alpha + ceil(bytes / beta) ticks (the
+ *      analytical model of section 4.1, parameters given by the input), or one
+ *      of the workload's collectives.  A task starts at the first tick by which
+ *      every predecessor has finished; a compute or intra-server task finishes
+ *      D ticks later (D >= 1), a collective task when its last flow arrives.  A
+ *      collective named by a task cannot start before it: the first flow of
+ *      each of its connections also waits for the task's start.  Collectives no
+ *      task names start at tick 0.  The experiment is done when every flow has
+ *      arrived and every task has finished; its completion tick is the latest
+ *      RD or task finish.
  *  Numbering: connections and flows follow the input order of collectives, then
  *  explicit flows; a ring numbers its connections by (channel, rank) and its
  *  flows by (channel, round, step, rank); a broadcast by hop, and (hop, part);
@@ -108,6 +121,9 @@
  * Pins (tests/test_oracle_pins.py): closed forms for a single flow, NC = 1
  * rings and the pipelined broadcast; four hand traces; conservation, per-flow
  * bounds and route lengths against an independent breadth-first search.
+ * (tests/test_oracle_tasks.py): task chains and fork-joins against the ring
+ * closed form plus durations, the analytical duration, and the start rule on a
+ * random mixed graph.
  * (tests/test_oracle_collectives.py): two hand traces (a tree, a gated global
  * all-gather), closed forms for two-member trees, sequential sends and the
  * send/recv strategies, reduce-scatter equal to all-gather, and the W6/W7
@@ -133,7 +149,8 @@
 #define INF_DIST 0x3FFFFFFF
 
 enum { KIND_RING_AR = 1, KIND_RING_AG = 2, KIND_BCAST = 3, KIND_RING_RS = 4, KIND_TREE = 5, KIND_SENDRECV = 6 };
-enum { PRED_RECV = 0, PRED_SEND = 1 };
+enum { PRED_RECV = 0, PRED_SEND = 1, PRED_TASK = 2 };
+enum { TASK_COMPUTE = 0, TASK_INTRA = 1, TASK_COLL = 2 };
 
 /* The batch, exactly as the input generator lays it out. */
 typedef struct {
@@ -151,6 +168,15 @@ typedef struct {
     const uint32_t *xflow_src, *xflow_dst, *xflow_pkts;
     const uint32_t *exp_topo, *exp_work, *exp_queue_pkts, *exp_ecmp_seed, *exp_pkt_bytes;
     const uint32_t *coll_gate;   /* per collective: earlier send/recv collective of the workload, or NONE */
+    /* tasks (may be NULL): per workload a list in topological order */
+    const uint32_t *work_task_off;
+    const uint8_t *task_type;
+    const uint32_t *task_ticks;      /* compute: duration; intra: alpha */
+    const uint64_t *task_bytes;      /* intra: bytes */
+    const uint32_t *task_beta;       /* intra: bytes per tick */
+    const uint32_t *task_coll;       /* collective task: collective index within the workload */
+    const uint32_t *task_pred_off;   /* CSR over all tasks */
+    const uint32_t *task_pred;       /* task indices within the workload, each below its task */
 } orc_batch;
 
 typedef struct {
@@ -227,6 +253,13 @@ typedef struct {
 } Flow;
 
 typedef struct {
+    uint32_t type, dur;         /* kind; duration of a compute or intra-server task */
+    uint32_t pred_off, npred;   /* into Exp.task_pred */
+    uint32_t left;              /* collective task: flows not yet received */
+    uint32_t start, finish;     /* ticks, NONE until known */
+} Task;
+
+typedef struct {
     uint32_t src, dst;
     uint32_t flow_off, nflow;   /* its flows, in sending order, in conn_flows */
     uint32_t cur;               /* position of the flow being / next to be sent */
@@ -249,6 +282,11 @@ typedef struct {
     /* per host: its connections in index order */
     uint32_t *host_conn_off, *host_conn;
     uint32_t Q, seed, R;
+    /* tasks */
+    uint32_t n_task;
+    Task *task;
+    uint32_t *task_pred;
+    uint32_t *flow_task;        /* per flow: the collective task it belongs to, or NONE */
 } Exp;
 
 static void fifo_free(Fifo *f) { free(f->buf); f->buf = NULL; }
@@ -300,6 +338,7 @@ static void exp_free(Exp *x)
     }
     free(x->port_off); free(x->port); free(x->conn); free(x->flow); free(x->conn_flows);
     free(x->path_node); free(x->path_port); free(x->host_conn_off); free(x->host_conn);
+    free(x->task); free(x->task_pred); free(x->flow_task);
     memset(x, 0, sizeof(*x));
 }
 
@@ -456,6 +495,31 @@ static int count_workload(const orc_batch *b, uint32_t e, uint64_t *nconn, uint6
             return ORC_E_INVALID;
         *nconn += 1; *nflow += 1;
     }
+    if (b->work_task_off) {
+        /* tasks: durations of at least one tick; a collective task names a
+         * collective of this workload that no other task names; predecessors
+         * come earlier in the list */
+        uint32_t t0 = b->work_task_off[w], t1 = b->work_task_off[w + 1];
+        uint32_t ncoll = b->work_coll_off[w + 1] - b->work_coll_off[w];
+        for (uint32_t k = t0; k < t1; k++) {
+            uint32_t ty = b->task_type[k];
+            if (ty == TASK_COMPUTE) {
+                if (b->task_ticks[k] < 1) return ORC_E_INVALID;
+            } else if (ty == TASK_INTRA) {
+                if (b->task_beta[k] < 1) return ORC_E_INVALID;
+                uint64_t d = (uint64_t)b->task_ticks[k] + ceil_div(b->task_bytes[k], b->task_beta[k]);
+                if (d < 1 || d >= NONE) return ORC_E_INVALID;
+            } else if (ty == TASK_COLL) {
+                if (b->task_coll[k] >= ncoll) return ORC_E_INVALID;
+                for (uint32_t j = t0; j < k; j++)
+                    if (b->task_type[j] == TASK_COLL && b->task_coll[j] == b->task_coll[k]) return ORC_E_INVALID;
+            } else {
+                return ORC_E_INVALID;
+            }
+            for (uint32_t q = b->task_pred_off[k]; q < b->task_pred_off[k + 1]; q++)
+                if (b->task_pred[q] >= k - t0) return ORC_E_INVALID;
+        }
+    }
     if (*nflow >= NONE || *nconn >= NONE) return ORC_E_INVALID;
     return ORC_OK;
 }
@@ -476,6 +540,50 @@ static void add_pred(Exp *x, uint32_t f, uint32_t g, uint32_t kind)
     fl->npred++;
 }
 
+/* Tasks of workload w (the task schedule of the System Simulator, Multiverse
+ * section 3.1; Schedule and AnalyticalSys of section 3.2).  A collective
+ * task's collective cannot start before the task: the first flow of each of
+ * its connections gets the task as one more predecessor. */
+static int build_tasks(const orc_batch *b, uint32_t w, Exp *x, const uint32_t *coll_f0, const uint32_t *coll_c0)
+{
+    x->flow_task = (uint32_t *)malloc(sizeof(uint32_t) * (x->n_flow ? x->n_flow : 1));
+    if (!x->flow_task) return ORC_E_NOMEM;
+    for (uint32_t f = 0; f < x->n_flow; f++) x->flow_task[f] = NONE;
+    if (!b->work_task_off) return ORC_OK;
+    uint32_t t0 = b->work_task_off[w], t1 = b->work_task_off[w + 1];
+    x->n_task = t1 - t0;
+    uint32_t np = b->task_pred_off[t1] - b->task_pred_off[t0];
+    x->task = (Task *)calloc(x->n_task ? x->n_task : 1, sizeof(Task));
+    x->task_pred = (uint32_t *)calloc(np ? np : 1, sizeof(uint32_t));
+    if (!x->task || !x->task_pred) return ORC_E_NOMEM;
+    for (uint32_t k = 0; k < x->n_task; k++) {
+        Task *tk = &x->task[k];
+        uint32_t g = t0 + k;
+        tk->type = b->task_type[g];
+        tk->start = tk->finish = NONE;
+        tk->pred_off = b->task_pred_off[g] - b->task_pred_off[t0];
+        tk->npred = b->task_pred_off[g + 1] - b->task_pred_off[g];
+        for (uint32_t q = 0; q < tk->npred; q++) x->task_pred[tk->pred_off + q] = b->task_pred[b->task_pred_off[g] + q];
+        if (tk->type == TASK_COMPUTE) {
+            tk->dur = b->task_ticks[g];
+        } else if (tk->type == TASK_INTRA) {
+            /* the analytical model of section 4.1: alpha + size / beta, in ticks */
+            tk->dur = b->task_ticks[g] + (uint32_t)ceil_div(b->task_bytes[g], b->task_beta[g]);
+        } else {
+            uint32_t cl = b->task_coll[g];
+            tk->left = coll_f0[cl + 1] - coll_f0[cl];
+            for (uint32_t f = coll_f0[cl]; f < coll_f0[cl + 1]; f++) x->flow_task[f] = k;
+            for (uint32_t c = coll_c0[cl]; c < coll_c0[cl + 1]; c++) {
+                Flow *fl = &x->flow[x->conn_flows[x->conn[c].flow_off]];
+                fl->pred[fl->npred] = k;
+                fl->pkind[fl->npred] = PRED_TASK;
+                fl->npred++;
+            }
+        }
+    }
+    return ORC_OK;
+}
+
 static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
 {
     uint64_t nconn, nflow;
@@ -490,8 +598,10 @@ static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
     x->n_conn = 0;
     uint32_t f = 0;
     uint32_t ncoll = b->work_coll_off[w + 1] - b->work_coll_off[w];
-    uint32_t *coll_f0 = (uint32_t *)calloc(ncoll ? ncoll : 1, sizeof(uint32_t));   /* first flow of each collective */
-    if (!coll_f0) return ORC_E_NOMEM;
+    /* first flow and first connection of each collective (one more entry: the end) */
+    uint32_t *coll_f0 = (uint32_t *)calloc(ncoll + 1, sizeof(uint32_t));
+    uint32_t *coll_c0 = (uint32_t *)calloc(ncoll + 1, sizeof(uint32_t));
+    if (!coll_f0 || !coll_c0) { free(coll_f0); free(coll_c0); return ORC_E_NOMEM; }
     for (uint32_t ci = b->work_coll_off[w]; ci < b->work_coll_off[w + 1]; ci++) {
         const uint32_t *mem = b->member_host + b->coll_member_off[ci];
         uint32_t N = b->coll_member_off[ci + 1] - b->coll_member_off[ci];
@@ -499,6 +609,7 @@ static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
         uint32_t kind = b->coll_type[ci];
         uint32_t gate = b->coll_gate ? b->coll_gate[ci] : NONE;
         coll_f0[ci - b->work_coll_off[w]] = f;
+        coll_c0[ci - b->work_coll_off[w]] = x->n_conn;
         if (is_ring(kind)) {
             uint32_t NC = b->coll_nc[ci];
             uint64_t p = b->coll_chunk_bytes[ci] / pkt;
@@ -594,7 +705,7 @@ static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
             }
         }
     }
-    free(coll_f0);
+    uint32_t coll_end_conn = x->n_conn;
     for (uint64_t xi = b->work_xflow_off[w]; xi < b->work_xflow_off[w + 1]; xi++) {
         uint32_t c = add_conn(x, b->xflow_src[xi], b->xflow_dst[xi]);
         set_flow(x, f, c, b->xflow_pkts[xi]);
@@ -622,7 +733,11 @@ static int build_workload(const orc_batch *b, uint32_t e, Exp *x)
         x->host_conn[x->host_conn_off[h] + fill[h]++] = c;
     }
     free(fill);
-    return ORC_OK;
+    coll_f0[ncoll] = f - (uint32_t)(b->work_xflow_off[w + 1] - b->work_xflow_off[w]);
+    coll_c0[ncoll] = coll_end_conn;
+    rc = build_tasks(b, w, x, coll_f0, coll_c0);
+    free(coll_f0); free(coll_c0);
+    return rc;
 }
 
 /* ---------------------------------------------------------------- routing */
@@ -760,9 +875,10 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
 {
     uint64_t hops = 0, delivered = 0, digest = 0;
     uint32_t flows_left = x->n_flow, t_done = 0;
+    uint32_t tasks_left = x->n_task;   /* not yet finished (a compute task counts until its finish tick) */
     uint32_t max_arrive = 0, max_occ = 0;
     int rc;
-    if (flows_left == 0) {
+    if (flows_left == 0 && tasks_left == 0) {
         res->status = ORC_OK; res->t_end = 0;
         return ORC_OK;
     }
@@ -791,9 +907,38 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     digest += mix64(((uint64_t)k.flow << 32) | t);
                     if (t > t_done) t_done = t;
                     flows_left--;
+                    uint32_t tk = x->flow_task[k.flow];
+                    if (tk != NONE && --x->task[tk].left == 0) {
+                        x->task[tk].finish = t;     /* the collective's last flow arrived */
+                        tasks_left--;
+                    }
                 }
             }
             if (pp->wire.count && fifo_front(&pp->wire)->arrive < t) return ORC_E_INVARIANT;
+        }
+        /* Schedule: a task starts at the first tick by which all its
+         * predecessors have finished; a compute or intra-server task finishes
+         * its duration later (at least one tick, so no task both starts and
+         * finishes within one tick) */
+        for (uint32_t k = 0; k < x->n_task; k++) {
+            Task *tk = &x->task[k];
+            if (tk->start != NONE) {
+                if (tk->type != TASK_COLL && tk->finish == t) tasks_left--;
+                continue;
+            }
+            int ok = 1;
+            for (uint32_t q = 0; q < tk->npred && ok; q++) {
+                uint32_t fin = x->task[x->task_pred[tk->pred_off + q]].finish;
+                if (fin == NONE || fin > t) ok = 0;
+            }
+            if (!ok) continue;
+            tk->start = t;
+            busy = 1;
+            if (tk->type != TASK_COLL) {
+                tk->finish = t + tk->dur;
+                if (tk->finish > max_arrive) max_arrive = tk->finish;
+                if (tk->finish > t_done) t_done = tk->finish;
+            }
         }
         /* B: activation.  Only the first not yet active flow of a connection can
          * have all its predecessors met: every later one waits (SEND) on it. */
@@ -804,8 +949,9 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
             if (fl->active) continue;
             int ok = 1;
             for (uint32_t k = 0; k < fl->npred; k++) {
-                const Flow *g = &x->flow[fl->pred[k]];
-                uint32_t when = fl->pkind[k] == PRED_RECV ? g->rd : g->sd;
+                uint32_t when;
+                if (fl->pkind[k] == PRED_TASK) when = x->task[fl->pred[k]].start;
+                else when = fl->pkind[k] == PRED_RECV ? x->flow[fl->pred[k]].rd : x->flow[fl->pred[k]].sd;
                 if (when == NONE || when > t) { ok = 0; break; }
             }
             if (ok) { fl->active = 1; fl->act = t; busy = 1; }
@@ -875,7 +1021,7 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
             }
         }
         /* E: completion / static state */
-        if (flows_left == 0) {
+        if (flows_left == 0 && tasks_left == 0) {
             res->status = ORC_OK;
             res->t_end = t_done;
             res->pkt_hops = hops; res->delivered = delivered; res->digest = digest;
@@ -907,10 +1053,11 @@ int orc_count(const orc_batch *b, uint32_t e, uint64_t *n_flows, uint64_t *n_con
 }
 
 /* Runs experiment e for at most max_ticks ticks.  Optional per-flow outputs
- * (NONE where the event did not happen): RD, activation tick, SD.  Returns a
+ * (NONE where the event did not happen): RD, activation tick, SD; per task:
+ * start and finish ticks.  Returns a
  * negative error code, or ORC_OK with the status in res->status. */
 int orc_run(const orc_batch *b, uint32_t e, uint32_t max_ticks, uint32_t check, orc_result *res,
-            uint32_t *flow_rd, uint32_t *flow_act, uint32_t *flow_sd)
+            uint32_t *flow_rd, uint32_t *flow_act, uint32_t *flow_sd, uint32_t *task_start, uint32_t *task_finish)
 {
     Exp x;
     memset(&x, 0, sizeof(x));
@@ -934,6 +1081,10 @@ int orc_run(const orc_batch *b, uint32_t e, uint32_t max_ticks, uint32_t check, 
             if (flow_rd) flow_rd[f] = x.flow[f].rd;
             if (flow_act) flow_act[f] = x.flow[f].act;
             if (flow_sd) flow_sd[f] = x.flow[f].sd;
+        }
+        for (uint32_t k = 0; k < x.n_task; k++) {
+            if (task_start) task_start[k] = x.task[k].start;
+            if (task_finish) task_finish[k] = x.task[k].finish;
         }
     }
     exp_free(&x);

@@ -48,7 +48,9 @@ class _Batch(C.Structure):
                 ("coll_member_off", _P32), ("member_host", _P32),
                 ("work_xflow_off", _P64), ("xflow_src", _P32), ("xflow_dst", _P32), ("xflow_pkts", _P32),
                 ("exp_topo", _P32), ("exp_work", _P32), ("exp_queue_pkts", _P32),
-                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32), ("coll_gate", _P32)]
+                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32), ("coll_gate", _P32),
+                ("work_task_off", _P32), ("task_type", _P8), ("task_ticks", _P32), ("task_bytes", _P64),
+                ("task_beta", _P32), ("task_coll", _P32), ("task_pred_off", _P32), ("task_pred", _P32)]
 
 
 class _Result(C.Structure):
@@ -69,7 +71,7 @@ def _load():
                 build(force=True)
             lib = C.CDLL(LIB)
             lib.orc_run.argtypes = [C.POINTER(_Batch), C.c_uint32, C.c_uint32, C.c_uint32,
-                                    C.POINTER(_Result), _P32, _P32, _P32]
+                                    C.POINTER(_Result), _P32, _P32, _P32, _P32, _P32]
             lib.orc_run.restype = C.c_int
             lib.orc_count.argtypes = [C.POINTER(_Batch), C.c_uint32, _P64, _P64]
             lib.orc_count.restype = C.c_int
@@ -107,7 +109,10 @@ class OracleBatch:
                         _ptr(p.xflow_pkts, _P32),
                         _ptr(p.exp_topo, _P32), _ptr(p.exp_work, _P32), _ptr(p.exp_queue_pkts, _P32),
                         _ptr(p.exp_ecmp_seed, _P32), _ptr(p.exp_pkt_bytes, _P32),
-                        _ptr(p.coll_gate, _P32))
+                        _ptr(p.coll_gate, _P32),
+                        _ptr(p.work_task_off, _P32), _ptr(p.task_type, _P8), _ptr(p.task_ticks, _P32),
+                        _ptr(p.task_bytes, _P64), _ptr(p.task_beta, _P32), _ptr(p.task_coll, _P32),
+                        _ptr(p.task_pred_off, _P32), _ptr(p.task_pred, _P32))
 
 
 def _as_oracle_batch(b) -> OracleBatch:
@@ -129,20 +134,25 @@ def run(batch, e: int, max_ticks: int = 0xFFFFFFFF, check: bool = False,
         flows: bool = False) -> Dict:
     """Runs experiment e.  Returns a dict with status, t_end, pkt_hops,
     delivered, digest, n_flows, n_conns, max_occupancy, rc and, with flows=True,
-    per-flow arrays rd, act, sd (NONE where the event did not happen)."""
+    per-flow arrays rd, act, sd and per-task arrays task_start, task_finish
+    (NONE where the event did not happen)."""
     ob = _as_oracle_batch(batch)
     lib = _load()
     out: Dict = {}
-    rd = act = sd = None
+    rd = act = sd = ts = tf = None
     if flows:
         rc, nf, _ = count(ob, e)
         if rc:
             return {"rc": rc}
         rd, act, sd = (np.full(max(nf, 1), NONE, np.uint32) for _ in range(3))
+        w = int(ob.p.exp_work[e])
+        nt = int(ob.p.work_task_off[w + 1] - ob.p.work_task_off[w])
+        ts, tf = (np.full(max(nt, 1), NONE, np.uint32) for _ in range(2))
     res = _Result()
     rc = lib.orc_run(C.byref(ob.s), e, max_ticks, 1 if check else 0, C.byref(res),
                      _ptr(rd, _P32) if flows else None, _ptr(act, _P32) if flows else None,
-                     _ptr(sd, _P32) if flows else None)
+                     _ptr(sd, _P32) if flows else None, _ptr(ts, _P32) if flows else None,
+                     _ptr(tf, _P32) if flows else None)
     out["rc"] = rc
     if rc:
         return out
@@ -151,6 +161,7 @@ def run(batch, e: int, max_ticks: int = 0xFFFFFFFF, check: bool = False,
                max_occupancy=res.max_occupancy)
     if flows:
         out["rd"], out["act"], out["sd"] = rd[:res.n_flows], act[:res.n_flows], sd[:res.n_flows]
+        out["task_start"], out["task_finish"] = ts[:nt], tf[:nt]
     return out
 
 
