@@ -46,10 +46,12 @@ struct Compiled {
     std::vector<uint8_t> arena;  /* RO + initial RW image, size multiple of 16 */
     uint32_t rw_off = 0, bytes = 0, lds_bytes = 0;
     bool compact = false;
-    uint32_t kind = 0;     /* kernel kind: 0 general; compact 1 + (16-byte rows << 2 | 32-bit descriptors << 1 | rate > 1) */
+    uint32_t kind = 0;     /* kernel kind: 0 general; compact 1 + (16-byte rows << 2 | 32-bit descriptors << 1 | rate > 1);
+                              KIND_GENERAL_TASKS: general with a task graph */
     uint32_t nt = 0;       /* compact: thread slots */
     uint64_t n_flows = 0, n_conns = 0, n_ports = 0;
     uint64_t est_hops = 0, est_delivered = 0;
+    uint32_t n_task = 0, o_trw = 0;   /* task graph (general format) */
     int err = 0;
     std::string msg;
 };
@@ -104,6 +106,12 @@ uint32_t flows_per_conn(const Grp &g)
     case GK_TREE: return g.R;
     default: return g.R * g.S;
     }
+}
+
+/* Connections of group g. */
+uint32_t conns_of(const Grp &g)
+{
+    return g.kind == GK_TREE ? 2 * (g.N - 1) : g.N;
 }
 
 uint32_t first_flow_size(const Grp &g, uint32_t idx)
@@ -313,6 +321,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: collective %u has unknown type %u", e, ci, type);
         }
     }
+    const uint32_t coll_grp_end = (uint32_t)grp.size();
     const uint64_t x0 = s->work_xflow_off[w], x1 = s->work_xflow_off[w + 1];
     if (x1 > x0) {
         Grp g{};
@@ -330,6 +339,58 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         grp.push_back(g);
     }
     if (conn.size() >= (1u << (32 - DESC_SHIFT))) return fail(out, MSIM_E_LIMIT, "experiment %u: too many connections", e);
+
+    /* ---- task graph: validated as the spec states; a collective task's
+     * groups carry the task's index */
+    for (Grp &g : grp) g.task = MSIM_NONE;
+    std::vector<TaskRO> tasks;
+    std::vector<TaskRW> task_rw;
+    std::vector<uint32_t> tpred;
+    if (s->work_task_off) {
+        const uint32_t t0 = s->work_task_off[w], t1 = s->work_task_off[w + 1];
+        const uint32_t ncoll = s->work_coll_off[w + 1] - cw0;
+        std::vector<uint8_t> named(ncoll, 0);
+        for (uint32_t k = t0; k < t1; k++) {
+            TaskRO tk{};
+            TaskRW tw{};
+            tw.start = tw.finish = MSIM_NONE;
+            tk.type = s->task_type[k];
+            tk.grp_first = MSIM_NONE;
+            if (tk.type == MSIM_TASK_COMPUTE) {
+                if (s->task_ticks[k] < 1) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: task %u lasts no tick", e, k - t0);
+                tk.dur = s->task_ticks[k];
+            } else if (tk.type == MSIM_TASK_INTRA) {
+                if (s->task_beta[k] < 1) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: task %u has no bandwidth", e, k - t0);
+                const uint64_t d = (uint64_t)s->task_ticks[k] + (s->task_bytes[k] + s->task_beta[k] - 1) / s->task_beta[k];
+                if (d < 1 || d >= MSIM_NONE) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: task %u duration out of range", e, k - t0);
+                tk.dur = (uint32_t)d;
+            } else if (tk.type == MSIM_TASK_COLL) {
+                const uint32_t cl = s->task_coll[k];
+                if (cl >= ncoll || named[cl]) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: task %u names collective %u badly", e, k - t0, cl);
+                named[cl] = 1;
+                tk.grp_first = grp_of_coll[cl];
+                const uint32_t gend = cl + 1 < ncoll ? grp_of_coll[cl + 1] : coll_grp_end;
+                tk.ngrp = gend - tk.grp_first;
+                uint64_t nf = 0;
+                for (uint32_t gi = tk.grp_first; gi < gend; gi++) {
+                    grp[gi].task = k - t0;
+                    nf += (uint64_t)flows_per_conn(grp[gi]) * conns_of(grp[gi]);
+                }
+                tw.left = (uint32_t)nf;
+            } else {
+                return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: task %u has unknown type %u", e, k - t0, tk.type);
+            }
+            tk.pred_off = (uint32_t)tpred.size();
+            tk.npred = s->task_pred_off[k + 1] - s->task_pred_off[k];
+            for (uint32_t q = s->task_pred_off[k]; q < s->task_pred_off[k + 1]; q++) {
+                if (s->task_pred[q] >= k - t0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: task %u has a predecessor not before it", e, k - t0);
+                tpred.push_back(s->task_pred[q]);
+            }
+            tasks.push_back(tk);
+            task_rw.push_back(tw);
+        }
+    }
+    const uint32_t n_task = (uint32_t)tasks.size();
 
     /* ---- routes: reverse breadth-first search over (node, may-still-climb)
      * states from every destination, then one walk per connection */
@@ -428,8 +489,8 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     out.n_conns = nconn;
     out.n_ports = n_ports;
 
-    /* ---- compact layout, where the experiment qualifies */
-    if (allow_compact) {
+    /* ---- compact layout, where the experiment qualifies (no task graph) */
+    if (allow_compact && n_task == 0) {
         uint32_t maxdeg = 1, max_out = 0, max_F = 0;
         uint64_t max_size = 0;
         for (uint32_t n = 0; n < nn; n++)
@@ -583,6 +644,9 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     take(H.o_grp, sizeof(Grp) * ngrp);
     take(H.o_hout, 4ull * nconn);
     take(H.o_host, sizeof(HostRO) * n_hosts);
+    H.n_task = n_task;
+    take(H.o_task, sizeof(TaskRO) * n_task);
+    take(H.o_tpred, 4ull * tpred.size());
     H.rw_off = (uint32_t)off;
     take(H.o_arr, n_voq);
     take(H.o_phead, n_voq);
@@ -600,6 +664,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     take(H.o_cstate, sizeof(ConnRW) * nconn);
     take(H.o_hstate, sizeof(HostRW) * n_hosts);
     take(H.o_ready, 4ull * words);
+    take(H.o_trw, sizeof(TaskRW) * n_task);
     if (off > 0xFFFFFFF0ull) return fail(out, MSIM_E_LIMIT, "experiment %u: state of %zu bytes too large", e, off);
     H.bytes = (uint32_t)off;
     out.arena.assign(off, 0);
@@ -623,6 +688,14 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     for (uint32_t c = 0; c < nconn; c++) cs[c].r_rem = first_flow_size(grp[conn[c].grp], conn[c].idx);
     HostRW *hs = (HostRW *)(A + H.o_hstate);
     for (uint32_t h = 0; h < n_hosts; h++) hs[h].left = left[h];
+    if (n_task) {
+        memcpy(A + H.o_task, tasks.data(), sizeof(TaskRO) * n_task);
+        if (!tpred.empty()) memcpy(A + H.o_tpred, tpred.data(), 4ull * tpred.size());
+        memcpy(A + H.o_trw, task_rw.data(), sizeof(TaskRW) * n_task);
+    }
+    out.n_task = n_task;
+    out.o_trw = H.o_trw;
+    out.kind = n_task ? KIND_GENERAL_TASKS : 0;
     out.rw_off = H.rw_off;
     out.bytes = H.bytes;
     return MSIM_OK;
@@ -765,7 +838,8 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
      * port slot; the general path strides its threads over the ports */
     for (uint32_t e = 0; e < E; e++) {
         const Compiled &c = ctx->exps[e];
-        uint32_t need = c.compact ? c.nt : std::min<uint32_t>(1024u, (uint32_t)c.n_ports);
+        const uint32_t cap = c.kind == KIND_GENERAL_TASKS ? 512u : 1024u;   /* the task kernel's launch bound */
+        uint32_t need = c.compact ? c.nt : std::min<uint32_t>(cap, (uint32_t)c.n_ports);
         ctx->k_block[c.kind] = std::max(ctx->k_block[c.kind], ((need + 63) / 64) * 64);
         if (c.compact) I.n_compact++;
     }
@@ -774,7 +848,8 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
         uint32_t bt = std::max(64u, ctx->k_block[k]);
         if (opts && opts->block_threads) {
             bt = opts->block_threads;
-            if (bt % 64 || bt > 1024 || bt < 64 || (k != 0 && bt < ctx->k_block[k])) {
+            const bool general = k == 0 || k == KIND_GENERAL_TASKS;
+            if (bt % 64 || bt > (k == KIND_GENERAL_TASKS ? 512u : 1024u) || bt < 64 || (!general && bt < ctx->k_block[k])) {
                 g_create_error = "block_threads must be a multiple of 64 (64..1024) covering every compact experiment's ports";
                 delete ctx;
                 return MSIM_E_ARG;
@@ -835,7 +910,7 @@ extern "C" int msim_bind(msim_ctx *ctx, void *dev_ws, uint64_t ws_bytes, void *s
             ctx->k_lds[c.kind] = std::max(ctx->k_lds[c.kind], c.lds_bytes);
             ctx->n_lds++;
         } else if (!ctx->force_global && c.bytes <= budget) {
-            ctx->k_lds[0] = std::max(ctx->k_lds[0], c.bytes);
+            ctx->k_lds[c.kind] = std::max(ctx->k_lds[c.kind], c.bytes);
             ctx->n_lds++;
         }
     }
@@ -1013,6 +1088,31 @@ extern "C" int msim_flow_ticks(msim_ctx *ctx, uint32_t exp, void *stream, uint32
     for (int k = 0; k < 3 && he == hipSuccess; k++)
         if (dst[k] && n) he = hipMemcpy(dst[k], ctx->ws + ctx->rec_off[exp] + 4ull * k * n, 4ull * n, hipMemcpyDeviceToHost);
     if (he != hipSuccess) return hip_fail(ctx, he, "flow ticks copy");
+    return MSIM_OK;
+}
+
+extern "C" int msim_task_count(const msim_ctx *ctx, uint32_t exp, uint32_t *n_tasks)
+{
+    if (!ctx || !n_tasks || exp >= ctx->n_exp) return MSIM_E_ARG;
+    *n_tasks = ctx->exps[exp].n_task;
+    return MSIM_OK;
+}
+
+extern "C" int msim_task_ticks(msim_ctx *ctx, uint32_t exp, void *stream, uint32_t *start, uint32_t *finish)
+{
+    if (!ctx || exp >= ctx->n_exp) return MSIM_E_ARG;
+    if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_task_ticks before msim_bind");
+    const Compiled &c = ctx->exps[exp];
+    if (!c.n_task) return MSIM_OK;
+    hipError_t he = hipStreamSynchronize((hipStream_t)stream);
+    std::vector<TaskRW> tw(c.n_task);
+    if (he == hipSuccess)
+        he = hipMemcpy(tw.data(), ctx->ws + ctx->arena_off[exp] + c.o_trw, sizeof(TaskRW) * c.n_task, hipMemcpyDeviceToHost);
+    if (he != hipSuccess) return hip_fail(ctx, he, "task ticks copy");
+    for (uint32_t k = 0; k < c.n_task; k++) {
+        if (start) start[k] = tw[k].start;
+        if (finish) finish[k] = tw[k].finish;
+    }
     return MSIM_OK;
 }
 

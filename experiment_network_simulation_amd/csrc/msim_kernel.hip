@@ -67,6 +67,10 @@ struct Ctx {
     uint32_t n_ports, Q, W, R;
     uint32_t *rec;       /* per-flow ticks (rd | act | sd), or null */
     uint32_t n_flows;
+    uint32_t n_task;     /* task graph */
+    const TaskRO *task;
+    const uint32_t *tpred;
+    TaskRW *trw;
 };
 
 struct Acc {
@@ -165,6 +169,9 @@ __device__ __forceinline__ void tree_dependents(uint32_t N, uint32_t j, F f)
 __device__ __forceinline__ bool recv_ok(const Ctx &C, const Grp &g, const ConnRO &cr, uint32_t c,
                                         uint32_t pos)
 {
+    /* a collective a task names starts with the task: the first flow of each
+     * of its connections waits for the task's start */
+    if (pos == 0 && g.task != MSIM_NONE && C.trw[g.task].start == MSIM_NONE) return false;
     if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
         uint32_t s = pos % g.S;
         if (s == 0) {
@@ -265,6 +272,9 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
         pos++;
         cw.r_pos = pos;
         if (pos < flows_per_conn(g)) cw.r_rem = flow_size(g, cr, pos);
+        /* the last flow of a collective task's collective finishes the task
+         * (hosts count down concurrently) */
+        if (g.task != MSIM_NONE && atomicSub(&C.trw[g.task].left, 1u) == 1u) C.trw[g.task].finish = t;
         wake_dependents(C, a, g, cr, c, hr.rdy_off, t);
     }
     if (n) C.scnt[si] = 0;
@@ -276,6 +286,57 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
         for (uint32_t k = 0; k < np; k++) check_conn(C, a, hw.pend[k], hr.rdy_off, t);
         if (np) hw.pcnt = 0;
     }
+}
+
+/* Schedule (tasks k = first, first + stride, ...): a task starts at the first
+ * tick by which all its predecessors have finished; a compute or intra-server
+ * task's finish is then known.  Durations are >= 1 tick, so a task started
+ * now cannot let another one start in the same tick.  Returns whether one
+ * started. */
+__device__ __forceinline__ bool schedule_tasks(const Ctx &C, Acc &a, uint32_t first, uint32_t stride, uint32_t t)
+{
+    bool started = false;
+    for (uint32_t k = first; k < C.n_task; k += stride) {
+        TaskRW &tw = C.trw[k];
+        if (tw.start != MSIM_NONE) continue;
+        const TaskRO tk = C.task[k];
+        bool ok = true;
+        for (uint32_t q = 0; q < tk.npred && ok; q++) {
+            const uint32_t fin = C.trw[C.tpred[tk.pred_off + q]].finish;
+            ok = fin != MSIM_NONE && fin <= t;
+        }
+        if (!ok) continue;
+        tw.start = t;
+        started = true;
+        a.last_act1 = t + 1;
+        if (tk.type != TK_COLL) {
+            tw.finish = t + tk.dur;
+            a.max_arr = max(a.max_arr, tw.finish);
+            a.tmax = max(a.tmax, tw.finish);
+        }
+    }
+    return started;
+}
+
+/* A host's connections whose collective's task started this tick. */
+__device__ __forceinline__ void task_wake_host(const Ctx &C, Acc &a, const PortRO &pr, uint32_t t)
+{
+    const HostRO hr = C.host[pr.host];
+    for (uint32_t j = 0; j < hr.n_out; j++) {
+        const uint32_t c = C.hout[hr.out_off + j];
+        const uint32_t tk = C.grp[C.conn[c].grp].task;
+        if (tk != MSIM_NONE && C.trw[tk].start == t) wake(C, a, c, hr.rdy_off, t);
+    }
+}
+
+/* Has every task finished by tick t - 1? (threads k = first, first + stride, ...) */
+__device__ __forceinline__ bool tasks_pending(const Ctx &C, uint32_t first, uint32_t stride, uint32_t t)
+{
+    for (uint32_t k = first; k < C.n_task; k += stride) {
+        const TaskRW tw = C.trw[k];
+        if (tw.start == MSIM_NONE || tw.finish == MSIM_NONE || tw.finish >= t) return true;
+    }
+    return false;
 }
 
 __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q, const PortRO &pr, uint32_t slot)
@@ -480,7 +541,7 @@ __device__ void finish_state(ExpState *stp, const Shared &sh, uint32_t nwaves, u
 
 /* ----------------------------------------------------------- one experiment */
 
-template <bool IN_LDS>
+template <bool IN_LDS, bool TASKS>
 __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
 {
     const uint32_t tid = threadIdx.x, nth = blockDim.x;
@@ -523,6 +584,10 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     C.W = H->W;
     C.R = H->R;
     C.n_flows = H->n_flows;
+    C.n_task = H->n_task;
+    C.task = (const TaskRO *)(base + H->o_task);
+    C.tpred = (const uint32_t *)(base + H->o_tpred);
+    C.trw = (TaskRW *)(base + H->o_trw);
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
@@ -550,6 +615,16 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
             else phase_a_switch(C, a, p, pr, slot);
         }
         __syncthreads();
+        if (TASKS) {
+            /* Schedule, then the first flows of collectives whose task started */
+            if (__syncthreads_or(schedule_tasks(C, a, tid, nth, t))) {
+                for (uint32_t p = tid; p < C.n_ports; p += nth) {
+                    const PortRO pr = C.port[p];
+                    if (pr.is_host) task_wake_host(C, a, pr, t);
+                }
+                __syncthreads();
+            }
+        }
         for (uint32_t p = tid; p < C.n_ports; p += nth) {
             const PortRO pr = C.port[p];
             if (pr.is_host) phase_d_host(C, a, p, pr, t);
@@ -558,7 +633,7 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
         t++;
         slot = slot + 1 == C.W ? 0 : slot + 1;
         if ((t - t0) % CHECK_EVERY == 0 || t == t_end) {
-            uint32_t any = __ballot(a.left > 0) != 0ull;
+            uint32_t any = __ballot(a.left > 0 || (TASKS && tasks_pending(C, tid, nth, t))) != 0ull;
             uint32_t ts = wave_max_u32(max(max(a.last_tx1, a.last_act1), a.max_arr));
             if (lane == 0) { sh.chk_any[par][wave] = any; sh.chk_max[par][wave] = ts; }
             __syncthreads();
@@ -1258,9 +1333,10 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
 template <int KIND>
 __device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *arena, uint8_t *lds, Shared &sh)
 {
-    if (KIND == 0) {
-        if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true>(kp, x, arena, lds, sh);
-        else run_experiment<false>(kp, x, arena, lds, sh);
+    if (KIND == 0 || KIND == KIND_GENERAL_TASKS) {
+        constexpr bool T = KIND == KIND_GENERAL_TASKS;
+        if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true, T>(kp, x, arena, lds, sh);
+        else run_experiment<false, T>(kp, x, arena, lds, sh);
     } else {
         /* compact kinds: 1 + (16-byte rows << 2 | 32-bit descriptors << 1 | some link faster than 1) */
         constexpr int c = KIND - 1;
@@ -1303,6 +1379,8 @@ extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16h_r1(KPara
 extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16h(KParams kp) { megakernel_body<6>(kp); }
 extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w_r1(KParams kp) { megakernel_body<7>(kp); }
 extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w(KParams kp) { megakernel_body<8>(kp); }
+/* at most 512 threads: the task code needs more than 128 registers per lane */
+extern "C" __global__ void __launch_bounds__(512) msim_megakernel_t(KParams kp) { megakernel_body<KIND_GENERAL_TASKS>(kp); }
 
 static const void *kernel_of(uint32_t kind)
 {
@@ -1315,7 +1393,8 @@ static const void *kernel_of(uint32_t kind)
     case 5: return (const void *)msim_megakernel_c16h_r1;
     case 6: return (const void *)msim_megakernel_c16h;
     case 7: return (const void *)msim_megakernel_c16w_r1;
-    default: return (const void *)msim_megakernel_c16w;
+    case 8: return (const void *)msim_megakernel_c16w;
+    default: return (const void *)msim_megakernel_t;
     }
 }
 
@@ -1341,7 +1420,8 @@ extern "C" __global__ void msim_reset_kernel(KParams kp, uint64_t o_rec_all, uin
         for (uint32_t i = threadIdx.x; i < (bytes - rw) / 16; i += blockDim.x) dst[i] = src[i];
         if (threadIdx.x == 0) {
             ExpState s = {};
-            s.status = ((const ArenaHdr *)arena)->n_flows == 0 ? 0u : 1u;
+            const ArenaHdr *ah = (const ArenaHdr *)arena;
+            s.status = ah->n_flows == 0 && (ah->mode != MODE_GENERAL || ah->n_task == 0) ? 0u : 1u;
             states[x] = s;
         }
     }

@@ -64,7 +64,7 @@ struct ConnRO {          /* 16 bytes */
     uint32_t lidx;       /* index among the source host's connections */
 };
 
-struct Grp {             /* 36 bytes */
+struct Grp {             /* 40 bytes */
     uint32_t kind;
     uint32_t N;          /* ring / tree members; broadcast: hops A; explicit: flow count;
                             send/recv: receivers */
@@ -77,6 +77,25 @@ struct Grp {             /* 36 bytes */
     uint32_t conn_base;  /* first connection */
     uint32_t link;       /* ring: the send/recv group gating its first step, or MSIM_NONE;
                             send/recv: the first group it gates (they are consecutive) */
+    uint32_t task;       /* the task that starts this group's collective, or MSIM_NONE */
+};
+
+/* task graph (general format only) */
+#define TK_COMPUTE 0u
+#define TK_INTRA 1u
+#define TK_COLL 2u
+
+struct TaskRO {          /* 24 bytes */
+    uint32_t type;       /* TK_* */
+    uint32_t dur;        /* compute / intra-server: duration in ticks (>= 1) */
+    uint32_t pred_off, npred;  /* into the task predecessor list */
+    uint32_t grp_first, ngrp;  /* collective task: its collective's groups */
+};
+
+struct TaskRW {          /* 16 bytes */
+    uint32_t start, finish;    /* ticks, MSIM_NONE until known */
+    uint32_t left;             /* collective task: flows not yet received */
+    uint32_t pad;
 };
 
 struct HostRO {          /* 16 bytes */
@@ -124,6 +143,7 @@ struct ArenaHdr {        /* general format header */
     uint32_t o_port, o_conn, o_grp, o_hout, o_host;
     uint32_t o_arr, o_phead, o_nslot, o_head, o_tslot, o_fcur, o_hseen;
     uint32_t o_pdesc, o_pnxt, o_fstk, o_pstate, o_scnt, o_sdesc, o_cstate, o_hstate, o_ready;
+    uint32_t n_task, o_task, o_tpred, o_trw;
 };
 
 /* ---- compact format ------------------------------------------------------
@@ -224,7 +244,8 @@ struct ExpState {        /* 64 bytes */
 };
 
 /* workspace header */
-#define MSIM_KINDS 9
+#define MSIM_KINDS 10
+#define KIND_GENERAL_TASKS 9   /* the general path with a task graph */
 
 struct WsHdr {
     uint32_t claim[MSIM_KINDS]; /* experiment queue counters of a run, one per kernel kind */

@@ -461,8 +461,8 @@ def single_batch(topo: Topology, work: Workload, queue_pkts: int = 16, ecmp_seed
 # The five benchmark configurations
 # ---------------------------------------------------------------------------
 
-BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5, 6: 0xC6}
-FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000, 6: 768}
+BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5, 6: 0xC6, 7: 0xC7}
+FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000, 6: 768, 7: 256}
 CONFIG_NAMES = {
     1: "C1 ring all-reduce 1 MiB, 8 hosts on one switch, NC x C grid",
     2: "C2 ring all-reduce 64 MiB over a 4x8 leaf-spine with 4 spines",
@@ -470,6 +470,7 @@ CONFIG_NAMES = {
     4: "C4 k=8 fat-tree: 16 DP ring all-reduces 256 MiB + 16 TP ring all-gathers 56 MiB",
     5: "C5 k=16 fat-tree sweep: Zipf(1.1) sparse all-to-all, 8 MiB per host",
     6: "C6 k=8 fat-tree collectives mix: tree all-reduces, ring reduce-scatters, send/recv unit tasks",
+    7: "C7 k=8 fat-tree training iteration: compute, intra-server TP collectives, bucketed DP ring all-reduces",
 }
 
 
@@ -669,14 +670,76 @@ def _c6(e_list):
     return Batch([topo], works, exps, "C6")
 
 
+# A tick is one 4 KiB packet on a rate-1 link; at 400 Gb/s that is about 82 ns,
+# in which an 900 GB/s intra-server link moves about 72 KiB.
+INTRA_BYTES_PER_TICK = 72 * KIB
+
+
+def training_iteration(pi: Sequence[int], layers: int, fwd: int, bwd: int, buckets: int, nc: int, chunk: int,
+                       tp_bytes: int = 56 * MIB, dp_bytes: int = 256 * MIB, alpha: int = 50) -> Workload:
+    """One training iteration as a task graph (the System Simulator's input).
+    Each of the 128 hosts is a server whose GPUs form one tensor-parallel
+    group, so TP collectives are intra-server (the analytical model); data
+    parallelism runs across servers in 16 ring groups of 8, group g being the
+    servers pi[g], pi[g+16], .., pi[g+112] (C4's DP groups).
+      forward:  per layer, compute(fwd) then an intra-server TP all-gather of
+                tp_bytes (alpha + bytes / INTRA_BYTES_PER_TICK ticks);
+      backward: per layer, compute(bwd) then an intra-server TP reduce-scatter;
+      DP:       the gradients of dp_bytes per DP group in `buckets` buckets;
+                bucket j (layers in reverse order) starts on each of the 16 DP
+                rings once the backward layer that completes it is done;
+      step:     an optimizer compute of fwd ticks after the last bucket."""
+    tasks: List[Task] = []
+    colls: List[Collective] = []
+    prev = []
+    for _ in range(layers):
+        tasks.append(compute(fwd, prev)); k = len(tasks) - 1
+        tasks.append(intra(alpha, tp_bytes, INTRA_BYTES_PER_TICK, [k])); prev = [len(tasks) - 1]
+    per_bucket = max(1, layers // buckets)
+    dp_groups = [[pi[g + 16 * j] for j in range(8)] for g in range(16)]
+    bucket_tasks: List[int] = []
+    for l in range(layers):
+        tasks.append(compute(bwd, prev)); k = len(tasks) - 1
+        tasks.append(intra(alpha, tp_bytes, INTRA_BYTES_PER_TICK, [k])); prev = [len(tasks) - 1]
+        if (l + 1) % per_bucket == 0 or l == layers - 1:
+            for grp in dp_groups:
+                colls.append(ring(COLL_RING_AR, dp_bytes // buckets, grp, nc, chunk))
+                tasks.append(comm(len(colls) - 1, [k]))
+                bucket_tasks.append(len(tasks) - 1)
+    tasks.append(compute(fwd, prev + bucket_tasks))
+    w = Workload(colls)
+    w.tasks = tasks
+    return w
+
+
+def _c7(e_list):
+    """Training iterations on C4's fabric (k=8 fat-tree, rate 1, delay 1,
+    Q = 16, no failures): 8 layers, per-layer forward compute ~ U{1000..4000}
+    ticks and backward twice that, DP buckets ~ {1, 2, 4, 8}, NC ~ U{1..8},
+    C ~ 4 KiB U{8..128}, a seeded placement pi of the 128 ranks.  The compute
+    durations and the intra-server model's parameters are synthetic: the pages
+    calibrate theirs on hardware and print none."""
+    topo = fat_tree(8, 1, 1)
+    works, exps = [], []
+    for e in e_list:
+        g = exp_rng(BASE_SEED[7], e)
+        pi = g.permutation(128)
+        fwd = g.between(1000, 4000)
+        buckets = [1, 2, 4, 8][g.below(4)]
+        nc, ck = g.between(1, 8), 4 * KIB * g.between(8, 128)
+        works.append(training_iteration(pi, 8, fwd, 2 * fwd, buckets, nc, ck))
+        exps.append(Experiment(0, len(works) - 1, 16, g.u32()))
+    return Batch([topo], works, exps, "C7")
+
+
 def make_config(cid: int, n_exp: Optional[int] = None, exp_ids: Optional[Sequence[int]] = None) -> Batch:
-    """Batch for benchmark configuration cid (1..6).  Experiment e of a config is
+    """Batch for benchmark configuration cid (1..7).  Experiment e of a config is
     the same whatever subset is drawn, so exp_ids picks a sample of the full
     batch and n_exp the first n experiments."""
     if exp_ids is None:
         exp_ids = range(FULL_E[cid] if n_exp is None else n_exp)
     e_list = list(exp_ids)
-    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5, 6: _c6}[cid](e_list)
+    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5, 6: _c6, 7: _c7}[cid](e_list)
     b.meta["config"] = cid
     b.meta["exp_ids"] = e_list
     return b

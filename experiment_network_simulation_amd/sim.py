@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsim.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 OK, S_INCOMPLETE, S_DEADLOCK = 0, 1, 2
 E_INVALID_SPEC, E_UNROUTABLE, E_WORKSPACE, E_HIP, E_ARG, E_STATE, E_LIMIT = -1, -2, -3, -4, -5, -6, -7
 EXP_DONE, EXP_INCOMPLETE, EXP_DEADLOCK = 0, 1, 2
@@ -24,10 +24,11 @@ NONE = 0xFFFFFFFF
 
 KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h_r1", "msim_megakernel_c8h", "msim_megakernel_c8w_r1",
                 "msim_megakernel_c8w", "msim_megakernel_c16h_r1", "msim_megakernel_c16h", "msim_megakernel_c16w_r1",
-                "msim_megakernel_c16w"]
+                "msim_megakernel_c16w", "msim_megakernel_t"]
 
 EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_reset", "msim_results",
-            "msim_flow_count", "msim_flow_ticks", "msim_get_info", "msim_last_error", "msim_destroy"]
+            "msim_flow_count", "msim_flow_ticks", "msim_task_count", "msim_task_ticks", "msim_get_info",
+            "msim_last_error", "msim_destroy"]
 
 _P8, _P32, _P64 = C.POINTER(C.c_uint8), C.POINTER(C.c_uint32), C.POINTER(C.c_uint64)
 
@@ -48,7 +49,9 @@ class _Spec(C.Structure):
                 ("coll_member_off", _P32), ("member_host", _P32),
                 ("work_xflow_off", _P64), ("xflow_src", _P32), ("xflow_dst", _P32), ("xflow_pkts", _P32),
                 ("exp_topo", _P32), ("exp_work", _P32), ("exp_queue_pkts", _P32),
-                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32), ("coll_gate", _P32)]
+                ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32), ("coll_gate", _P32),
+                ("work_task_off", _P32), ("task_type", _P8), ("task_ticks", _P32), ("task_bytes", _P64),
+                ("task_beta", _P32), ("task_coll", _P32), ("task_pred_off", _P32), ("task_pred", _P32)]
 
 
 class _Options(C.Structure):
@@ -86,6 +89,8 @@ def load_library():
     lib.msim_results.argtypes = [vp, vp, _P8, _P32, _P64, _P64, _P64]
     lib.msim_flow_count.argtypes = [vp, C.c_uint32, _P64]
     lib.msim_flow_ticks.argtypes = [vp, C.c_uint32, vp, _P32, _P32, _P32]
+    lib.msim_task_count.argtypes = [vp, C.c_uint32, _P32]
+    lib.msim_task_ticks.argtypes = [vp, C.c_uint32, vp, _P32, _P32]
     lib.msim_get_info.argtypes = [vp, C.POINTER(_Info)]
     lib.msim_last_error.argtypes = [vp]
     lib.msim_last_error.restype = C.c_char_p
@@ -132,7 +137,10 @@ class Sim:
                            _ptr(p.xflow_pkts, _P32),
                            _ptr(p.exp_topo, _P32), _ptr(p.exp_work, _P32), _ptr(p.exp_queue_pkts, _P32),
                            _ptr(p.exp_ecmp_seed, _P32), _ptr(p.exp_pkt_bytes, _P32),
-                        _ptr(p.coll_gate, _P32))
+                        _ptr(p.coll_gate, _P32),
+                        _ptr(p.work_task_off, _P32), _ptr(p.task_type, _P8), _ptr(p.task_ticks, _P32),
+                        _ptr(p.task_bytes, _P64), _ptr(p.task_beta, _P32), _ptr(p.task_coll, _P32),
+                        _ptr(p.task_pred_off, _P32), _ptr(p.task_pred, _P32))
         self._rec = np.ascontiguousarray(np.asarray(list(record), np.uint32))
         self.record = [int(x) for x in self._rec]
         opts = _Options(ABI_VERSION, len(self._rec), _ptr(self._rec, _P32) if len(self._rec) else None,
@@ -194,6 +202,19 @@ class Sim:
         self._check(self._lib.msim_flow_ticks(self._ctx, exp, C.c_void_p(_stream_ptr(stream)), _ptr(rd, _P32),
                                               _ptr(act, _P32), _ptr(sd, _P32)))
         return dict(rd=rd[:n], act=act[:n], sd=sd[:n])
+
+    def task_count(self, exp: int) -> int:
+        n = np.zeros(1, np.uint32)
+        self._check(self._lib.msim_task_count(self._ctx, exp, _ptr(n, _P32)))
+        return int(n[0])
+
+    def task_ticks(self, exp: int, stream=None) -> Dict[str, np.ndarray]:
+        """Start and finish tick of every task of experiment exp (NONE if not yet)."""
+        n = self.task_count(exp)
+        st, fi = np.zeros(max(n, 1), np.uint32), np.zeros(max(n, 1), np.uint32)
+        self._check(self._lib.msim_task_ticks(self._ctx, exp, C.c_void_p(_stream_ptr(stream)), _ptr(st, _P32),
+                                              _ptr(fi, _P32)))
+        return dict(start=st[:n], finish=fi[:n])
 
     def close(self):
         if getattr(self, "_ctx", None):

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MSIM_ABI_VERSION 2u
+#define MSIM_ABI_VERSION 3u
 
 /* return codes */
 #define MSIM_OK 0
@@ -66,6 +66,13 @@ extern "C" {
 #define MSIM_COLL_TREE_ALLREDUCE 5       /* AutoCCL section 4.1: tree (log2 N) against ring (2(N-1)) */
 #define MSIM_COLL_SENDRECV 6             /* AlpaComm section 3.1, Figure 3a: one source, receivers in turn */
 #define MSIM_NO_GATE 0xFFFFFFFFu
+
+/* task kinds (task_type): the System Simulator's task graph, Multiverse
+ * sections 3.1 and 3.2 (Schedule, AnalyticalSys) */
+#define MSIM_TASK_COMPUTE 0      /* lasts task_ticks ticks */
+#define MSIM_TASK_INTRA 1        /* intra-server collective: task_ticks + ceil(task_bytes / task_beta)
+                                    ticks, the alpha + size / beta model of section 4.1 */
+#define MSIM_TASK_COLL 2         /* the workload's collective task_coll, simulated packet by packet */
 
 /* compiled-in limits */
 #define MSIM_MAX_RATE 4          /* packets per tick per link direction */
@@ -103,6 +110,16 @@ extern "C" {
  *   work_xflow_off[w] .. work_xflow_off[w+1]-1 (source host, destination host,
  *   packets >= 1).  Every ring channel must carry at least as many packets as
  *   the ring has members, every tree channel at least one packet.
+ *   Tasks (optional; work_task_off NULL = none): tasks work_task_off[w] ..
+ *   work_task_off[w+1]-1 of workload w, in topological order, with task_type,
+ *   task_ticks, task_bytes, task_beta, task_coll (a collective index within
+ *   the workload; each collective named by at most one task) and predecessors
+ *   task_pred[task_pred_off[k] .. task_pred_off[k+1]-1] (task indices within
+ *   the workload, each below k).  A task starts at the first tick by which
+ *   every predecessor has finished; a compute or intra-server task finishes its
+ *   duration (>= 1 tick) later, a collective task when its last flow arrives.
+ *   A collective a task names starts with that task; the others start at tick
+ *   0.  An experiment with tasks runs on the general path.
  * Experiment e: topology exp_topo[e], workload exp_work[e], switch ingress
  *   buffer exp_queue_pkts[e] packets (1..MSIM_MAX_QUEUE), ECMP seed
  *   exp_ecmp_seed[e], packet size exp_pkt_bytes[e] bytes.
@@ -124,6 +141,12 @@ typedef struct msim_batch_spec {
     const uint32_t *xflow_src, *xflow_dst, *xflow_pkts;
     const uint32_t *exp_topo, *exp_work, *exp_queue_pkts, *exp_ecmp_seed, *exp_pkt_bytes;
     const uint32_t *coll_gate;   /* one per collective; NULL = no gates */
+    const uint32_t *work_task_off;
+    const uint8_t *task_type;
+    const uint32_t *task_ticks;
+    const uint64_t *task_bytes;
+    const uint32_t *task_beta, *task_coll;
+    const uint32_t *task_pred_off, *task_pred;
 } msim_batch_spec;
 
 /* Options for msim_create.  Zero-initialise and set what you need. */
@@ -207,6 +230,18 @@ int msim_flow_count(const msim_ctx *ctx, uint32_t exp, uint64_t *n_flows);
  */
 int msim_flow_ticks(msim_ctx *ctx, uint32_t exp, void *hip_stream, uint32_t *rd, uint32_t *act,
                     uint32_t *sd);
+
+/* Number of tasks of experiment exp (its workload's task list). */
+int msim_task_count(const msim_ctx *ctx, uint32_t exp, uint32_t *n_tasks);
+
+/*
+ * Start and finish tick of every task of experiment exp (the Schedule system,
+ * Multiverse section 3.2), MSIM_NONE where the event has not happened yet;
+ * arrays of msim_task_count entries, host memory, either may be NULL.
+ * Synchronises hip_stream first.  Needs no recording; available for every
+ * experiment after msim_bind.
+ */
+int msim_task_ticks(msim_ctx *ctx, uint32_t exp, void *hip_stream, uint32_t *start, uint32_t *finish);
 
 /* Static description of the compiled batch, for callers and tests. */
 typedef struct msim_info {

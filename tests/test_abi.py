@@ -161,3 +161,23 @@ def test_gate_validation_errors(simmod):
     expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
     w = I.Workload([I.sendrecv(0, 0, [1, 2])])
     expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
+
+
+def test_task_graph_compile_and_validation(simmod, oracle):
+    """Task graphs compile onto the general task kernel, and invalid graphs are
+    rejected as the oracle rejects them."""
+    b = I.make_config(7, exp_ids=[0, 3])
+    s = simmod.Sim(b)
+    inf = s.info()
+    assert inf["n_compact"] == 0 and simmod.KERNEL_NAMES[inf["main_kernel"]] == "msim_megakernel_t"
+    for e in range(b.n_exp):
+        assert s.task_count(e) == len(b.works[b.exps[e].work].tasks)
+        assert s.flow_count(e) == oracle.count(b, e)[1]
+    topo = I.single_switch(4)
+    ring = I.ring(I.COLL_RING_AG, 4 * I.PKT_BYTES, range(4), 1, I.PKT_BYTES)
+    for tasks in ([I.compute(0)], [I.compute(2, [0])], [I.comm(1)], [I.comm(0), I.comm(0)],
+                  [I.intra(0, 0, 5)], [I.intra(1, 10, 0)]):
+        w = I.Workload([ring])
+        w.tasks = tasks
+        expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
+        assert oracle.run(I.single_batch(topo, w), 0)["rc"] == oracle.E_INVALID

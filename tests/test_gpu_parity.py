@@ -348,3 +348,73 @@ def test_c6_sample(simmod, oracle):
         assert_exp(r, e, o[e])
     for e in (2, 4, 5):
         assert_flows(s, e, oracle.run(b, e, flows=True))
+
+
+# ------------------------------------------------------------ task graphs
+
+def task_batch(n, seed):
+    """Seeded task graphs: compute and intra-server tasks in chains and
+    fork-joins, gating rings, trees, broadcasts and send/recv groups, beside
+    collectives no task names, on three small fabrics."""
+    rng = np.random.default_rng(seed)
+    b = I.Batch([I.single_switch(8), I.leaf_spine(2, 4, 2), I.fat_tree(4)], [], [], "tasks")
+    for e in range(n):
+        ti = e % 3
+        hosts = [int(x) for x in rng.permutation(b.topos[ti].hosts())]
+        colls = []
+        for j in range(int(rng.integers(1, 5))):
+            kind = int(rng.integers(0, 4))
+            mem = hosts[(3 * j) % 4: (3 * j) % 4 + int(rng.integers(2, 5))]
+            if kind == 0:
+                colls.append(I.ring(I.COLL_RING_AR, len(mem) * int(rng.integers(1, 9)) * I.PKT_BYTES, mem, 1, I.PKT_BYTES))
+            elif kind == 1:
+                colls.append(I.tree(int(rng.integers(1, 20)) * I.PKT_BYTES, mem, 1, 2 * I.PKT_BYTES))
+            elif kind == 2:
+                colls.append(I.bcast(int(rng.integers(2, 20)) * I.PKT_BYTES, mem, 2))
+            else:
+                colls.append(I.sendrecv(int(rng.integers(1, 6)) * I.PKT_BYTES, mem[0], mem[1:]))
+        tasks = []
+        for j in range(len(colls)):
+            if rng.integers(0, 4) == 0:
+                continue                              # this collective starts at tick 0
+            preds = [int(q) for q in rng.choice(len(tasks), size=min(len(tasks), int(rng.integers(0, 3))),
+                                                replace=False)] if tasks else []
+            if rng.integers(0, 2):
+                tasks.append(I.compute(int(rng.integers(1, 40)), preds))
+            else:
+                tasks.append(I.intra(int(rng.integers(0, 9)), int(rng.integers(1, 9000)), 1024, preds))
+            tasks.append(I.comm(j, [len(tasks) - 1]))
+        tasks.append(I.compute(int(rng.integers(1, 30)), list(range(len(tasks)))))
+        w = I.Workload(colls)
+        w.tasks = tasks
+        b.works.append(w)
+        b.exps.append(I.Experiment(ti, len(b.works) - 1, int(rng.integers(2, 16)), int(rng.integers(0, 2**32))))
+    return b
+
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_task_graphs(simmod, oracle, force_global):
+    """Every flow's and every task's ticks equal the oracle's."""
+    b = task_batch(24, 21)
+    log("task graphs", b.n_exp, "force_global", force_global)
+    s, r = gpu_run(simmod, b, record=range(b.n_exp), force_global=force_global)
+    o = oracle_all(oracle, b, flows=True)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+        assert_flows(s, e, o[e])
+        tt = s.task_ticks(e)
+        assert np.array_equal(tt["start"], o[e]["task_start"]) and np.array_equal(tt["finish"], o[e]["task_finish"])
+
+
+def test_c7_sample(simmod, oracle):
+    """Two full-size training iterations (tasks, intra-server collectives, DP
+    all-reduce buckets on the k=8 fat-tree)."""
+    b = I.make_config(7, exp_ids=[0, 1])
+    log("C7 sample")
+    s, r = gpu_run(simmod, b, record=[1])
+    o = oracle_all(oracle, b, flows=True)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+        tt = s.task_ticks(e)
+        assert np.array_equal(tt["start"], o[e]["task_start"]) and np.array_equal(tt["finish"], o[e]["task_finish"])
+    assert_flows(s, 1, o[1])
