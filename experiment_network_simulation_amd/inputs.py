@@ -671,7 +671,7 @@ def _c6(e_list):
 
 
 # A tick is one 4 KiB packet on a rate-1 link; at 400 Gb/s that is about 82 ns,
-# in which an 900 GB/s intra-server link moves about 72 KiB.
+# in which a 900 GB/s intra-server link moves about 72 KiB.
 INTRA_BYTES_PER_TICK = 72 * KIB
 
 
