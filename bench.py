@@ -81,6 +81,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=16, help="experiments in the CPU-oracle sample (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--force-global", action="store_true")
+    ap.add_argument("--dse", choices=["tune", "reshard"], default=None,
+                    help="time a design-space-exploration driver instead: AutoCCL tuning or AlpaComm schedules")
+    ap.add_argument("--dse-n", type=int, default=0, help="tuning tasks / resharding instances (default 256 / 64)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -99,6 +102,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); experiments are "
               "independent, so N GPUs would each run their own share of the batch.", file=sys.stderr)
         sys.exit(2)
+
+    if args.dse:
+        return dse_bench(args)
 
     import numpy as np
     import torch
@@ -212,6 +218,112 @@ def main():
             "kernel": KERNEL_NAMES[info["main_kernel"]],
             "kernel_ms_avg": k_avg_s * 1e3,
             "alg_bytes_per_launch": alg_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def dse_bench(args):
+    """One driver run: every candidate of every search scored on the GPU, one
+    batch per lockstep step.  value = candidates scored per second of wall time
+    (host compile of each batch included); the roofline is over the simulation
+    kernels of all batches (HIP events around each msim_run)."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from experiment_network_simulation_amd import dse as P
+    from experiment_network_simulation_amd import inputs as I
+
+    ev = P.GpuEvaluator()
+    threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+    if args.dse == "tune":
+        n = args.dse_n or 256
+        tasks = I.tune_tasks_c2(n)
+        starts = I.tune_starts(0xA7C5, n)
+        workload = (f"AutoCCL coordinate descent over (algorithm ring/tree, NC 1..16, C 32..512 KiB) for {n} "
+                    "64 MiB all-reduces over 32 hosts of C2's leaf-spine (seeded ring order and ECMP seed each)")
+        t0 = time.perf_counter()
+        res = P.tune(tasks, starts, ev, log=log)
+        wall = time.perf_counter() - t0
+        detail = {"tasks": n, "tree_chosen": sum(r.algo == I.COLL_TREE_AR for r in res),
+                  "mean_best_ticks": float(np.mean([r.ticks for r in res]))}
+        unit = "probes/s"
+        cpu = None
+        if args.cpu_sample:
+            from oracle import dse as D
+            ids = sorted(set(int(round(i * n / min(args.cpu_sample, n))) for i in range(min(args.cpu_sample, n))) - {n})
+            t1 = time.perf_counter()
+            with ThreadPoolExecutor(min(threads, len(ids))) as ex:
+                refs = list(ex.map(lambda t: D.tune(tasks[t], starts[t]), ids))
+            dt = time.perf_counter() - t1
+            probes = sum(len(r["profiled"]) for ref in refs for r in ref["runs"])
+            ok = sum(ref["ticks"] == res[t].ticks and ref["algo"] == res[t].algo for t, ref in zip(ids, refs))
+            cpu = {"value": probes / dt, "unit": unit, "cores": min(threads, len(ids)), "kind": "oracle",
+                   "sample": f"{len(ids)} of {n} tuning tasks, {probes} probes in {dt:.1f}s; same result on "
+                             f"{ok}/{len(ids)}", "parity_ok": ok, "parity_n": len(ids)}
+    else:
+        n = args.dse_n or 64
+        topo = I.fat_tree(8)
+        K, G = 16, 32
+        insts = [(topo, I.resharding_tasks(0x5C00 + i, 48, range(64), range(64, 128))) for i in range(n)]
+        keys = [I.greedy_keys(0x6E00 + g, 48, 8) for g in range(G)]
+        workload = (f"AlpaComm schedulers on {n} cross-mesh resharding instances of 48 unit tasks (mesh A: hosts "
+                    f"0-63, mesh B: 64-127 of a k=8 fat-tree; 1-3 holders, 1-4 receivers, 256 KiB-2 MiB slices; "
+                    f"broadcast K = {K}): naive, load balance and {G} randomised greedy schedules each, "
+                    "scored by simulation")
+        t0 = time.perf_counter()
+        res = P.reshard(insts, K, keys, ev)
+        wall = time.perf_counter() - t0
+        gain = [float(r.simulated[0]) / float(r.simulated.min()) for r in res]
+        detail = {"instances": n, "schedules_per_instance": len(res[0].names),
+                  "mean_naive_over_best": float(np.mean(gain)),
+                  "best_is_greedy": sum(r.names[r.best].startswith("greedy") for r in res)}
+        unit = "schedules/s"
+        cpu = None
+        if args.cpu_sample:
+            from oracle import dse as D
+            flat = [(i, k) for i in range(n) for k in range(len(res[i].names))]
+            m = min(args.cpu_sample, len(flat))
+            ids = [flat[int(round(j * len(flat) / m))] for j in range(m) if int(round(j * len(flat) / m)) < len(flat)]
+            t1 = time.perf_counter()
+            with ThreadPoolExecutor(min(threads, len(ids))) as ex:
+                refs = list(ex.map(lambda ik: D.simulate_schedule(
+                    topo, insts[ik[0]][1], res[ik[0]].schedules[ik[1]].sender,
+                    res[ik[0]].schedules[ik[1]].order, K), ids))
+            dt = time.perf_counter() - t1
+            ok = sum(r["t_end"] == int(res[i].simulated[k]) for (i, k), r in zip(ids, refs))
+            cpu = {"value": len(ids) / dt, "unit": unit, "cores": min(threads, len(ids)), "kind": "oracle",
+                   "sample": f"{len(ids)} of {len(flat)} schedules simulated in {dt:.1f}s; same completion tick "
+                             f"on {ok}/{len(ids)}", "parity_ok": ok, "parity_n": len(ids)}
+    st = ev.stats
+    alg_bytes = ALG_BYTES_PER_HOP * st.pkt_hops + ALG_BYTES_PER_DELIVERY * st.delivered
+    achieved = alg_bytes / (st.kernel_ms / 1e3) / 1e9
+    out = {
+        "metric": f"{unit} (design-space exploration scored by the batched simulator, 1 GPU)",
+        "value": st.experiments / wall,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": st.batches,
+        "warmup": 0,
+        "ms_per_step": wall / max(st.batches, 1) * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": workload, "batches": st.batches, "experiments": st.experiments,
+                   "packet_hops": st.pkt_hops, "kernel_ms_total": st.kernel_ms, "host_s": st.host_s,
+                   "wall_s": wall, **detail},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "all simulation launches of the run (ring probes compact, tree probes and task graphs general)",
+            "kernel_ms_avg": st.kernel_ms / max(st.batches, 1),
+            "alg_bytes_total": alg_bytes,
         },
         "cpu_baseline": cpu,
     }

@@ -743,3 +743,91 @@ def make_config(cid: int, n_exp: Optional[int] = None, exp_ids: Optional[Sequenc
     b.meta["config"] = cid
     b.meta["exp_ids"] = e_list
     return b
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the design-space-exploration drivers
+# ---------------------------------------------------------------------------
+
+# Resource-parameter grids of the collective tuner: channels NC and chunk size C
+# (AutoCCL section 4.2 tunes NC, NT and C; a packet network has no thread count).
+TUNE_NC = list(range(1, 17))
+TUNE_CHUNK = [32 * KIB * j for j in range(1, 17)]          # 32 KiB .. 512 KiB
+
+
+@dataclass
+class TuneTask:
+    """One communication task to tune: a collective of `kind` (ring all-reduce,
+    all-gather or reduce-scatter) of nbytes over members, on a topology with the
+    experiment's queue capacity and ECMP seed."""
+    topo: Topology
+    kind: int
+    nbytes: int
+    members: List[int]
+    queue_pkts: int
+    ecmp_seed: int
+
+
+def tune_starts(seed: int, n_tasks: int, n_subspaces: int = 2,
+                dims: Sequence[int] = (len(TUNE_NC), len(TUNE_CHUNK))) -> np.ndarray:
+    """The random starting point of every (task, subspace) search, as grid
+    indices [n_tasks, n_subspaces, len(dims)], from one SplitMix64 stream per
+    task."""
+    out = np.zeros((n_tasks, n_subspaces, len(dims)), np.int64)
+    for t in range(n_tasks):
+        g = exp_rng(seed, t)
+        for s in range(n_subspaces):
+            for d, n in enumerate(dims):
+                out[t, s, d] = g.below(n)
+    return out
+
+
+def tune_tasks_c2(n: int, seed: int = 0xA7C) -> List[TuneTask]:
+    """n tuning tasks on C2's leaf-spine (4 leaves x 8 hosts, 4 spines, host
+    links rate 1, uplinks rate 2, delay 1, Q = 32): a 64 MiB all-reduce over
+    the 32 hosts in a seeded ring order, with a seeded ECMP seed."""
+    topo = leaf_spine(4, 8, 4, host_rate=1, up_rate=2, delay=1)
+    out = []
+    for t in range(n):
+        g = exp_rng(seed ^ 0x5EED, t)
+        out.append(TuneTask(topo, COLL_RING_AR, 64 * MIB, g.permutation(32), 32, g.u32()))
+    return out
+
+
+@dataclass
+class UnitComm:
+    """A unit communication task of a cross-mesh resharding (AlpaComm section
+    3.2): a data slice of nbytes held by each host in `holders`, needed by every
+    host in `receivers` (in broadcast-chain order)."""
+    holders: List[int]
+    receivers: List[int]
+    nbytes: int
+
+
+def resharding_tasks(seed: int, n_tasks: int, mesh_a: Sequence[int], mesh_b: Sequence[int],
+                     max_holders: int = 3, max_receivers: int = 4,
+                     pkts_choices: Sequence[int] = (64, 128, 256, 512)) -> List[UnitComm]:
+    """n_tasks unit tasks: holders drawn from mesh_a (1..max_holders hosts),
+    receivers from mesh_b (1..max_receivers hosts), slice sizes from
+    pkts_choices packets; one SplitMix64 stream."""
+    g = exp_rng(seed, 0x7A5C)
+    out = []
+    for _ in range(n_tasks):
+        pa, pb = g.permutation(len(mesh_a)), g.permutation(len(mesh_b))
+        nh, nr = g.between(1, max_holders), g.between(1, max_receivers)
+        out.append(UnitComm([int(mesh_a[i]) for i in pa[:nh]], [int(mesh_b[i]) for i in pb[:nr]],
+                            int(pkts_choices[g.below(len(pkts_choices))]) * PKT_BYTES))
+    return out
+
+
+def greedy_keys(seed: int, n_tasks: int, n_rounds: int, n_stages: Optional[int] = None) -> np.ndarray:
+    """Random sort keys [n_stages, n_rounds, n_tasks] (u64) for the randomised
+    greedy scheduler: round r of stage s visits the remaining tasks in order of
+    (key, index)."""
+    n_stages = n_tasks if n_stages is None else n_stages
+    g = SplitMix64(seed)
+    out = np.zeros((n_stages, n_rounds, n_tasks), np.uint64)
+    flat = out.reshape(-1)
+    for i in range(flat.size):
+        flat[i] = g.next()
+    return out

@@ -418,3 +418,66 @@ def test_c7_sample(simmod, oracle):
         tt = s.task_ticks(e)
         assert np.array_equal(tt["start"], o[e]["task_start"]) and np.array_equal(tt["finish"], o[e]["task_finish"])
     assert_flows(s, 1, o[1])
+
+
+# ---------------------------------------------------------------------------
+# Design-space exploration scored on the GPU (AutoCCL tuning, AlpaComm schedules)
+# ---------------------------------------------------------------------------
+
+def small_tune_tasks():
+    """Five tuning tasks on C2's leaf-spine: 8 MiB all-reduces (ring and tree
+    subspaces) over 16 hosts in seeded orders, and one all-gather."""
+    topo = I.leaf_spine(4, 8, 4, host_rate=1, up_rate=2, delay=1)
+    out = []
+    for t in range(5):
+        g = I.exp_rng(0x7E57, t)
+        hosts = g.permutation(32)[:16]
+        kind = I.COLL_RING_AG if t == 4 else I.COLL_RING_AR
+        out.append(I.TuneTask(topo, kind, 8 * I.MIB, hosts, 32, g.u32()))
+    return out
+
+
+def test_autoccl_tuning_matches_oracle(simmod, oracle):
+    from experiment_network_simulation_amd import dse as P
+    from oracle import dse as D
+    tasks = small_tune_tasks()
+    starts = I.tune_starts(0x5A, len(tasks))
+    ev = P.GpuEvaluator()
+    got = P.tune(tasks, starts, ev)
+    log(f"tuning: {ev.stats.batches} batches, {ev.stats.experiments} probes")
+    with ThreadPoolExecutor(THREADS) as ex:
+        refs = list(ex.map(lambda t: D.tune(tasks[t], starts[t]), range(len(tasks))))
+    for t, ref in enumerate(refs):
+        assert got[t].algo == ref["algo"] and got[t].ticks == ref["ticks"], t
+        assert (got[t].nc, got[t].chunk) == (I.TUNE_NC[ref["best"][0]], I.TUNE_CHUNK[ref["best"][1]])
+        for k, run in enumerate(ref["runs"]):
+            assert got[t].per_subspace[k]["trace"] == run["probes"], (t, k)
+
+
+def test_alpacomm_schedules_match_oracle(simmod, oracle):
+    """Every scheduler's schedule on two resharding instances of a k=4
+    fat-tree (mesh A hosts 0-7, mesh B hosts 8-15), scored on the GPU, against
+    the oracle's schedulers and the oracle's simulation of each schedule."""
+    from experiment_network_simulation_amd import dse as P
+    from oracle import dse as D
+    topo = I.fat_tree(4)
+    K = 4
+    insts = [(topo, I.resharding_tasks(s, n, range(8), range(8, 16), pkts_choices=(16, 32, 64)))
+             for s, n in ((1, 6), (2, 10))]
+    keys = [I.greedy_keys(100 + g, 10, 4) for g in range(3)]
+    got = P.reshard(insts, K, keys, P.GpuEvaluator(), dfs_max_tasks=6)
+    for (tp, tasks), r in zip(insts, got):
+        ref = D.schedules(tasks, K, keys[0], with_dfs=len(tasks) <= 6)
+        dur = P.durations(tasks, K)
+        for name, s, t in zip(r.names, r.schedules, r.simulated):
+            if name in ("naive", "load_balance", "greedy0"):
+                rn = "greedy" if name == "greedy0" else name
+                assert (s.sender, s.order) == (ref[rn]["sender"], ref[rn]["order"]), name
+            if name.startswith("greedy") and name != "greedy0":
+                g = D.greedy(tasks, dur, keys[int(name[6:])])
+                assert (s.sender, s.order) == (g["sender"], g["order"]), name
+            if name == "dfs":
+                assert s.complete and s.makespan == ref["dfs"]["makespan"]
+            o = D.simulate_schedule(tp, tasks, s.sender, s.order, K)
+            assert int(t) == o["t_end"], (name, int(t), o["t_end"])
+        log(f"reshard {len(tasks)} tasks: " + ", ".join(f"{n} {int(t)}" for n, t in zip(r.names, r.simulated)))
