@@ -47,6 +47,9 @@ TASK_COMPUTE = 0        # a computation of `ticks` ticks
 TASK_INTRA = 1          # an intra-server collective: alpha + ceil(bytes / beta) ticks
 TASK_COLL = 2           # a collective of the workload, simulated packet by packet
 
+CC_NONE = 0             # congestion control of an experiment
+CC_DCTCP = 1            # ECN marking at switches, ACKs, DCTCP windows per connection
+
 KIB = 1024
 MIB = 1024 * 1024
 PKT_BYTES = 4096
@@ -309,6 +312,9 @@ class Experiment:
     queue_pkts: int
     ecmp_seed: int
     pkt_bytes: int = PKT_BYTES
+    cc: int = CC_NONE          # CC_NONE or CC_DCTCP
+    ecn_k: int = 0             # DCTCP: marking threshold (packets)
+    cwnd0: int = 0             # DCTCP: initial window (packets, >= 1)
 
 
 @dataclass
@@ -334,7 +340,8 @@ class Batch:
                 tmap[x.topo] = len(topos); topos.append(self.topos[x.topo])
             if x.work not in wmap:
                 wmap[x.work] = len(works); works.append(self.works[x.work])
-            exps.append(Experiment(tmap[x.topo], wmap[x.work], x.queue_pkts, x.ecmp_seed, x.pkt_bytes))
+            exps.append(Experiment(tmap[x.topo], wmap[x.work], x.queue_pkts, x.ecmp_seed, x.pkt_bytes,
+                                   x.cc, x.ecn_k, x.cwnd0))
         meta = dict(self.meta)
         meta["subset_of"] = self.name
         meta["subset_idx"] = idx
@@ -385,6 +392,9 @@ class PackedBatch:
     exp_queue_pkts: np.ndarray
     exp_ecmp_seed: np.ndarray
     exp_pkt_bytes: np.ndarray
+    exp_cc: np.ndarray           # uint8
+    exp_ecn_k: np.ndarray        # uint32
+    exp_cwnd0: np.ndarray        # uint32
 
     @staticmethod
     def from_batch(b: Batch) -> "PackedBatch":
@@ -449,12 +459,16 @@ class PackedBatch:
             exp_queue_pkts=np.asarray([x.queue_pkts for x in b.exps], np.uint32),
             exp_ecmp_seed=np.asarray([x.ecmp_seed & 0xFFFFFFFF for x in b.exps], np.uint32),
             exp_pkt_bytes=np.asarray([x.pkt_bytes for x in b.exps], np.uint32),
+            exp_cc=np.asarray([x.cc for x in b.exps], np.uint8),
+            exp_ecn_k=np.asarray([x.ecn_k for x in b.exps], np.uint32),
+            exp_cwnd0=np.asarray([x.cwnd0 for x in b.exps], np.uint32),
         )
 
 
 def single_batch(topo: Topology, work: Workload, queue_pkts: int = 16, ecmp_seed: int = 0,
-                 pkt_bytes: int = PKT_BYTES, name: str = "custom") -> Batch:
-    return Batch([topo], [work], [Experiment(0, 0, queue_pkts, ecmp_seed, pkt_bytes)], name)
+                 pkt_bytes: int = PKT_BYTES, name: str = "custom", cc: int = CC_NONE, ecn_k: int = 0,
+                 cwnd0: int = 0) -> Batch:
+    return Batch([topo], [work], [Experiment(0, 0, queue_pkts, ecmp_seed, pkt_bytes, cc, ecn_k, cwnd0)], name)
 
 
 # ---------------------------------------------------------------------------

@@ -109,6 +109,27 @@
  *      task names start at tick 0.  The experiment is done when every flow has
  *      arrived and every task has finished; its completion tick is the latest
  *      RD or task finish.
+ *  W9  Congestion control (Multiverse section 3.2: flows carry congestion-control
+ *      variables and an ACK system closes each step; section 5 names DCTCP
+ *      among the supported algorithms).  Per experiment, none or DCTCP
+ *      (Alizadeh et al., SIGCOMM 2010), restated in integer arithmetic:
+ *      - ECN: a packet reaching a switch at tick t is marked when the packets
+ *        there for the same egress that arrived before t and were not
+ *        forwarded before t number at least K; a mark is kept to the end.
+ *      - ACK: a packet delivered at t acknowledges itself at its connection's
+ *        source at t + L (L: the sum of the path's link delays, i.e. the same
+ *        cables backwards); ACKs take no link capacity and never queue.
+ *      - Sender, per connection: window cwnd in 1/256 packet (initially W0
+ *        packets), alpha in 1/1024 (initially 1), counters of packets sent and
+ *        acknowledged.  The NIC may send for a connection only while sent -
+ *        acked < floor(cwnd).  The k ACKs (m marked) arriving in one tick are
+ *        applied together: acked += k; cwnd += (k - m) * 65536 / cwnd (one
+ *        1/cwnd per unmarked ACK, the pre-batch cwnd); then, once acked reaches
+ *        the window end, alpha = alpha - alpha/16 + F/16 with F = 1024 *
+ *        marked / acknowledged over the window, cwnd = max(1 packet, cwnd *
+ *        (1 - alpha/2)) if any was marked, and the next window ends at the
+ *        packets sent so far (the first ends at 0).  cwnd is capped at 65535
+ *        packets; every division floors.
  *  Numbering: connections and flows follow the input order of collectives, then
  *  explicit flows; a ring numbers its connections by (channel, rank) and its
  *  flows by (channel, round, step, rank); a broadcast by hop, and (hop, part);
@@ -128,6 +149,10 @@
  * all-gather), closed forms for two-member trees, sequential sends and the
  * send/recv strategies, reduce-scatter equal to all-gather, and the W6/W7
  * predecessor rules rebuilt in the test and checked through activation ticks.
+ * (tests/test_oracle_cc.py): three hand traces of W9 (additive increase, a
+ * marked window, an incast whose marks cut both windows), the every-ACK-marked
+ * closed form 2L(P-1) + L on three fabrics, and the base model reproduced flow
+ * by flow when neither windows nor marks can act.
  * Parity unpinned (the pages fix no value): which of several equal-cost ECMP
  * candidates the hash picks (only validity and length of a route are pinned),
  * the digest mixer (a checksum; per-flow ticks are compared as well), and the
@@ -151,6 +176,8 @@
 enum { KIND_RING_AR = 1, KIND_RING_AG = 2, KIND_BCAST = 3, KIND_RING_RS = 4, KIND_TREE = 5, KIND_SENDRECV = 6 };
 enum { PRED_RECV = 0, PRED_SEND = 1, PRED_TASK = 2 };
 enum { TASK_COMPUTE = 0, TASK_INTRA = 1, TASK_COLL = 2 };
+enum { CC_NONE = 0, CC_DCTCP = 1 };
+#define CWND_MAX (65535u << 8)
 
 /* The batch, exactly as the input generator lays it out. */
 typedef struct {
@@ -177,6 +204,10 @@ typedef struct {
     const uint32_t *task_coll;       /* collective task: collective index within the workload */
     const uint32_t *task_pred_off;   /* CSR over all tasks */
     const uint32_t *task_pred;       /* task indices within the workload, each below its task */
+    /* congestion control (may be NULL: none) */
+    const uint8_t *exp_cc;           /* 0 none, 1 DCTCP */
+    const uint32_t *exp_ecn_k;       /* marking threshold, packets */
+    const uint32_t *exp_cwnd0;       /* initial window, packets */
 } orc_batch;
 
 typedef struct {
@@ -221,6 +252,7 @@ typedef struct {
     uint32_t flow;      /* flow id the packet belongs to */
     uint32_t arrive;    /* arrival tick at the next node */
     uint32_t hop;       /* index in the connection's path of the node it reaches */
+    uint32_t mark;      /* ECN mark */
 } Pkt;
 
 typedef struct {       /* FIFO of packets (ring buffer of fixed capacity) */
@@ -265,6 +297,13 @@ typedef struct {
     uint32_t cur;               /* position of the flow being / next to be sent */
     uint32_t path_off, path_len;/* nodes and egress ports from source host to destination host */
     uint32_t recv_pos;          /* position of the earliest flow not fully received */
+    /* congestion control */
+    uint32_t lat;               /* sum of the path's link delays */
+    uint32_t cwnd, alpha;       /* 1/256 packet, 1/1024 */
+    uint32_t sent, acked;       /* packets over the connection */
+    uint32_t wend, wa, wm;      /* window end; ACKs and marked ACKs in the window */
+    uint32_t *ackq;             /* ACKs on their way back: (tick << 1 | mark), FIFO */
+    uint32_t aq_cap, aq_head, aq_n;
 } Conn;
 
 typedef struct {
@@ -282,6 +321,7 @@ typedef struct {
     /* per host: its connections in index order */
     uint32_t *host_conn_off, *host_conn;
     uint32_t Q, seed, R;
+    uint32_t cc, ecn_k, cwnd0;
     /* tasks */
     uint32_t n_task;
     Task *task;
@@ -336,9 +376,11 @@ static void exp_free(Exp *x)
             fifo_free(&x->port[p].wire);
         }
     }
-    free(x->port_off); free(x->port); free(x->conn); free(x->flow); free(x->conn_flows);
+    free(x->port_off); free(x->port); free(x->flow); free(x->conn_flows);
     free(x->path_node); free(x->path_port); free(x->host_conn_off); free(x->host_conn);
     free(x->task); free(x->task_pred); free(x->flow_task);
+    if (x->conn) for (uint32_t c = 0; c < x->n_conn; c++) free(x->conn[c].ackq);
+    free(x->conn);
     memset(x, 0, sizeof(*x));
 }
 
@@ -821,6 +863,7 @@ static int build_routes(Exp *x)
                 if (nc == 0) { rc = ORC_E_UNROUTABLE; break; }
                 uint32_t pick = cand[ecmp_hash(c, node, x->seed) % nc];
                 x->path_port[cn->path_off + len] = pick - x->port_off[node];
+                cn->lat += x->port[pick].delay;
                 uint32_t next = x->port[pick].peer_node;
                 if (x->layer[next] < x->layer[node]) going_down = 1;
                 node = next;
@@ -848,8 +891,9 @@ static uint32_t out_port(const Exp *x, const Conn *c, uint32_t h)
     return x->port_off[node] + x->path_port[c->path_off + h];
 }
 
-/* Sends packet (flow f, currently at path position hop) out of port op at tick t. */
-static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t t, uint64_t *hops,
+/* Sends packet (flow f, currently at path position hop, ECN mark) out of port
+ * op at tick t. */
+static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t mark, uint32_t t, uint64_t *hops,
                     uint32_t *max_arrive, uint32_t *max_occ)
 {
     Port *o = &x->port[op];
@@ -859,6 +903,7 @@ static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t t, u
     p.flow = f;
     p.arrive = t + o->delay;
     p.hop = hop + 1;
+    p.mark = mark;
     if (p.arrive > *max_arrive) *max_arrive = p.arrive;
     (*hops)++;
     if (x->layer[o->peer_node] == 0) {
@@ -869,6 +914,55 @@ static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t t, u
     if (in->occ > *max_occ) *max_occ = in->occ;
     if (in->occ > x->Q) return ORC_E_INVARIANT;        /* credits make this impossible */
     return fifo_push(&in->voq[egress], p) ? ORC_E_NOMEM : ORC_OK;
+}
+
+/* W9 ECN: marks the packets that reach switch ingresses at tick t, against
+ * each egress's backlog as it stood before any of them arrived. */
+static void ecn_mark(Exp *x, uint32_t t)
+{
+    for (uint32_t n = 0; n < x->n_nodes; n++) {
+        if (x->layer[n] == 0) continue;
+        uint32_t deg = x->port_off[n + 1] - x->port_off[n];
+        for (uint32_t o = 0; o < deg; o++) {
+            uint32_t backlog = 0;
+            for (uint32_t i = 0; i < deg; i++) {
+                Fifo *q = &x->port[x->port_off[n] + i].voq[o];
+                for (uint32_t j = 0; j < q->count; j++)
+                    if (q->buf[(q->head + j) % q->cap].arrive < t) backlog++;
+            }
+            if (backlog < x->ecn_k) continue;
+            for (uint32_t i = 0; i < deg; i++) {
+                Fifo *q = &x->port[x->port_off[n] + i].voq[o];
+                for (uint32_t j = 0; j < q->count; j++) {
+                    Pkt *k = &q->buf[(q->head + j) % q->cap];
+                    if (k->arrive == t) k->mark = 1;
+                }
+            }
+        }
+    }
+}
+
+/* W9 DCTCP: k ACKs, m of them marked, reach connection c's source together. */
+static void dctcp_acks(Exp *x, Conn *c, uint32_t k, uint32_t m)
+{
+    (void)x;
+    c->acked += k;
+    c->wa += k;
+    c->wm += m;
+    if (k > m) {
+        uint64_t w = (uint64_t)c->cwnd + (uint64_t)(k - m) * 65536u / c->cwnd;
+        c->cwnd = w > CWND_MAX ? CWND_MAX : (uint32_t)w;
+    }
+    if (c->acked >= c->wend) {
+        uint32_t F = (uint32_t)((uint64_t)c->wm * 1024u / c->wa);
+        c->alpha = c->alpha - (c->alpha >> 4) + (F >> 4);
+        if (c->wm) {
+            uint32_t cut = (uint32_t)(((uint64_t)c->cwnd * c->alpha) >> 11);
+            c->cwnd = c->cwnd - cut < 256u ? 256u : c->cwnd - cut;
+        }
+        c->wend = c->sent;
+        c->wa = c->wm = 0;
+    }
 }
 
 static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts *opt)
@@ -882,8 +976,34 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
         res->status = ORC_OK; res->t_end = 0;
         return ORC_OK;
     }
+    if (x->cc) {
+        for (uint32_t ci = 0; ci < x->n_conn; ci++) {
+            Conn *c = &x->conn[ci];
+            c->cwnd = x->cwnd0 << 8;
+            c->alpha = 1024;
+            c->aq_cap = c->lat * x->R + 1;
+            c->ackq = (uint32_t *)malloc(sizeof(uint32_t) * c->aq_cap);
+            if (!c->ackq) return ORC_E_NOMEM;
+        }
+    }
     for (uint32_t t = 0; t < max_ticks; t++) {
         int busy = 0;
+        /* A: ECN marks at switch arrivals, then ACKs reaching their sources */
+        if (x->cc) {
+            ecn_mark(x, t);
+            for (uint32_t ci = 0; ci < x->n_conn; ci++) {
+                Conn *c = &x->conn[ci];
+                uint32_t k = 0, m = 0;
+                while (c->aq_n && (c->ackq[c->aq_head] >> 1) == t) {
+                    m += c->ackq[c->aq_head] & 1u;
+                    k++;
+                    c->aq_head = (c->aq_head + 1) % c->aq_cap;
+                    c->aq_n--;
+                }
+                if (c->aq_n && (c->ackq[c->aq_head] >> 1) < t) return ORC_E_INVARIANT;
+                if (k) dctcp_acks(x, c, k, m);
+            }
+        }
         /* A: deliveries at hosts */
         for (uint32_t p = 0; p < x->n_ports; p++) {
             Port *pp = &x->port[p];
@@ -901,6 +1021,13 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                 }
                 fl->recvd++;
                 delivered++;
+                if (x->cc) {
+                    /* the ACK of this packet reaches the source L ticks later */
+                    if (c->aq_n == c->aq_cap) return ORC_E_INVARIANT;
+                    c->ackq[(c->aq_head + c->aq_n) % c->aq_cap] = ((t + c->lat) << 1) | k.mark;
+                    c->aq_n++;
+                    if (t + c->lat > max_arrive) max_arrive = t + c->lat;
+                }
                 if (fl->recvd == fl->size) {
                     fl->rd = t;
                     c->recv_pos++;
@@ -977,6 +1104,7 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                         Conn *c = &x->conn[x->host_conn[x->host_conn_off[node] + idx]];
                         if (c->cur >= c->nflow) continue;
                         Flow *fl = &x->flow[x->conn_flows[c->flow_off + c->cur]];
+                        if (x->cc && c->sent - c->acked >= (c->cwnd >> 8)) continue;   /* window full */
                         if (fl->active && fl->sent < fl->size) { pp->granted = idx; break; }
                     }
                 } else {
@@ -1000,9 +1128,10 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     uint32_t f = x->conn_flows[c->flow_off + c->cur];
                     Flow *fl = &x->flow[f];
                     if (out_port(x, c, 0) != p) return ORC_E_INVARIANT;
-                    rc = transmit(x, p, f, 0, t, &hops, &max_arrive, &max_occ);
+                    rc = transmit(x, p, f, 0, 0, t, &hops, &max_arrive, &max_occ);
                     if (rc) return rc;
                     fl->sent++;
+                    c->sent++;
                     if (fl->sent == fl->size) { fl->sd = t + 1; c->cur++; }
                     pp->rr = (pp->granted + 1) % n_in;
                 } else {
@@ -1013,7 +1142,7 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     in->occ--;
                     const Conn *c = &x->conn[x->flow[k.flow].conn];
                     if (opt->check && out_port(x, c, k.hop) != p) return ORC_E_INVARIANT;
-                    rc = transmit(x, p, k.flow, k.hop, t, &hops, &max_arrive, &max_occ);
+                    rc = transmit(x, p, k.flow, k.hop, k.mark, t, &hops, &max_arrive, &max_occ);
                     if (rc) return rc;
                     pp->rr = (pp->granted + 1) % deg;
                 }
@@ -1066,6 +1195,13 @@ int orc_run(const orc_batch *b, uint32_t e, uint32_t max_ticks, uint32_t check, 
     x.Q = b->exp_queue_pkts[e];
     x.seed = b->exp_ecmp_seed[e];
     if (x.Q < 1) return ORC_E_INVALID;
+    x.cc = b->exp_cc ? b->exp_cc[e] : CC_NONE;
+    if (x.cc > CC_DCTCP) return ORC_E_INVALID;
+    if (x.cc) {
+        x.ecn_k = b->exp_ecn_k[e];
+        x.cwnd0 = b->exp_cwnd0[e];
+        if (x.cwnd0 < 1 || x.cwnd0 > 65535) return ORC_E_INVALID;
+    }
     int rc = build_topology(b, e, &x);
     if (!rc) rc = build_workload(b, e, &x);
     if (!rc) rc = build_routes(&x);
