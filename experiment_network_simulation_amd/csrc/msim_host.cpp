@@ -47,7 +47,8 @@ struct Compiled {
     uint32_t rw_off = 0, bytes = 0, lds_bytes = 0;
     bool compact = false;
     uint32_t kind = 0;     /* kernel kind: 0 general; compact 1 + (16-byte rows << 2 | 32-bit descriptors << 1 | rate > 1);
-                              KIND_GENERAL_TASKS: general with a task graph */
+                              KIND_GENERAL_TASKS: general with a task graph;
+                              KIND_GENERAL_CC: general with congestion control */
     uint32_t nt = 0;       /* compact: thread slots */
     uint64_t n_flows = 0, n_conns = 0, n_ports = 0;
     uint64_t est_hops = 0, est_delivered = 0;
@@ -84,7 +85,7 @@ size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 /* One connection before layout. */
 struct Conn {
     uint32_t src, dst, grp, idx;
-    uint32_t route = 0, links = 0, lidx = 0;
+    uint32_t route = 0, links = 0, lidx = 0, lat = 0;
     uint64_t pkts = 0;
 };
 
@@ -133,6 +134,15 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     const uint64_t pkt = s->exp_pkt_bytes[e];
     if (Q < 1 || Q > MSIM_MAX_QUEUE) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: queue %u outside 1..%u", e, Q, MSIM_MAX_QUEUE);
     if (pkt == 0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: zero packet size", e);
+    const uint32_t cc = s->exp_cc ? s->exp_cc[e] : MSIM_CC_NONE;
+    uint32_t ecn_k = 0, cwnd0 = 0;
+    if (cc > MSIM_CC_DCTCP) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: unknown congestion control %u", e, cc);
+    if (cc == MSIM_CC_DCTCP) {
+        if (!s->exp_ecn_k || !s->exp_cwnd0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: DCTCP needs exp_ecn_k and exp_cwnd0", e);
+        ecn_k = s->exp_ecn_k[e];
+        cwnd0 = s->exp_cwnd0[e];
+        if (cwnd0 < 1 || cwnd0 > MSIM_MAX_CWND) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: initial window %u outside 1..%u", e, cwnd0, MSIM_MAX_CWND);
+    }
 
     /* ---- topology: nodes, ports numbered by cable order */
     const uint32_t n0 = s->topo_node_off[t], nn = s->topo_node_off[t + 1] - n0;
@@ -338,7 +348,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         }
         grp.push_back(g);
     }
-    if (conn.size() >= (1u << (32 - DESC_SHIFT))) return fail(out, MSIM_E_LIMIT, "experiment %u: too many connections", e);
+    if (conn.size() >= (1u << (31 - DESC_SHIFT))) return fail(out, MSIM_E_LIMIT, "experiment %u: too many connections", e);
 
     /* ---- task graph: validated as the spec states; a collective task's
      * groups carry the task's index */
@@ -445,6 +455,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                     cn.route |= (pick - pbase[node]) << (4 * hop);
                     hop++;
                 }
+                cn.lat += port[pick].delay;
                 uint32_t next = port_node[port[pick].peer];
                 if (layer[next] < layer[node]) state = 2 * next + 1;
                 else state = (state & 1) ? 2 * next + 1 : 2 * next;
@@ -489,8 +500,9 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     out.n_conns = nconn;
     out.n_ports = n_ports;
 
-    /* ---- compact layout, where the experiment qualifies (no task graph) */
-    if (allow_compact && n_task == 0) {
+    /* ---- compact layout, where the experiment qualifies (no task graph, no
+     * congestion control) */
+    if (allow_compact && n_task == 0 && cc == MSIM_CC_NONE) {
         uint32_t maxdeg = 1, max_out = 0, max_F = 0;
         uint64_t max_size = 0;
         for (uint32_t n = 0; n < nn; n++)
@@ -665,6 +677,17 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     take(H.o_hstate, sizeof(HostRW) * n_hosts);
     take(H.o_ready, 4ull * words);
     take(H.o_trw, sizeof(TaskRW) * n_task);
+    H.cc = cc;
+    H.ecn_k = ecn_k;
+    H.WA = 1;
+    if (cc != MSIM_CC_NONE) {
+        uint32_t max_lat = 0;
+        for (const Conn &cn : conn) max_lat = std::max(max_lat, cn.lat);
+        while (H.WA <= max_lat) H.WA <<= 1;
+        take(H.o_cc, sizeof(CcRW) * nconn);
+        take(H.o_ack, 2ull * nconn * H.WA);
+        take(H.o_bl, 4ull * n_ports);
+    }
     if (off > 0xFFFFFFF0ull) return fail(out, MSIM_E_LIMIT, "experiment %u: state of %zu bytes too large", e, off);
     H.bytes = (uint32_t)off;
     out.arena.assign(off, 0);
@@ -688,6 +711,15 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     for (uint32_t c = 0; c < nconn; c++) cs[c].r_rem = first_flow_size(grp[conn[c].grp], conn[c].idx);
     HostRW *hs = (HostRW *)(A + H.o_hstate);
     for (uint32_t h = 0; h < n_hosts; h++) hs[h].left = left[h];
+    if (cc != MSIM_CC_NONE) {
+        CcRW *cr = (CcRW *)(A + H.o_cc);
+        for (uint32_t c = 0; c < nconn; c++) {
+            cr[c] = CcRW{};
+            cr[c].cwnd = cwnd0 << 8;
+            cr[c].alpha = 1024;
+            cr[c].lat = conn[c].lat;
+        }
+    }
     if (n_task) {
         memcpy(A + H.o_task, tasks.data(), sizeof(TaskRO) * n_task);
         if (!tpred.empty()) memcpy(A + H.o_tpred, tpred.data(), 4ull * tpred.size());
@@ -695,7 +727,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     }
     out.n_task = n_task;
     out.o_trw = H.o_trw;
-    out.kind = n_task ? KIND_GENERAL_TASKS : 0;
+    out.kind = cc != MSIM_CC_NONE ? KIND_GENERAL_CC : n_task ? KIND_GENERAL_TASKS : 0;
     out.rw_off = H.rw_off;
     out.bytes = H.bytes;
     return MSIM_OK;
@@ -838,7 +870,7 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
      * port slot; the general path strides its threads over the ports */
     for (uint32_t e = 0; e < E; e++) {
         const Compiled &c = ctx->exps[e];
-        const uint32_t cap = c.kind == KIND_GENERAL_TASKS ? 512u : 1024u;   /* the task kernel's launch bound */
+        const uint32_t cap = c.kind >= KIND_GENERAL_TASKS ? 512u : 1024u;   /* those kernels' launch bound */
         uint32_t need = c.compact ? c.nt : std::min<uint32_t>(cap, (uint32_t)c.n_ports);
         ctx->k_block[c.kind] = std::max(ctx->k_block[c.kind], ((need + 63) / 64) * 64);
         if (c.compact) I.n_compact++;
@@ -848,8 +880,8 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
         uint32_t bt = std::max(64u, ctx->k_block[k]);
         if (opts && opts->block_threads) {
             bt = opts->block_threads;
-            const bool general = k == 0 || k == KIND_GENERAL_TASKS;
-            if (bt % 64 || bt > (k == KIND_GENERAL_TASKS ? 512u : 1024u) || bt < 64 || (!general && bt < ctx->k_block[k])) {
+            const bool general = k == 0 || k >= KIND_GENERAL_TASKS;
+            if (bt % 64 || bt > (k >= KIND_GENERAL_TASKS ? 512u : 1024u) || bt < 64 || (!general && bt < ctx->k_block[k])) {
                 g_create_error = "block_threads must be a multiple of 64 (64..1024) covering every compact experiment's ports";
                 delete ctx;
                 return MSIM_E_ARG;

@@ -71,6 +71,10 @@ struct Ctx {
     const TaskRO *task;
     const uint32_t *tpred;
     TaskRW *trw;
+    uint32_t cc, ecn_k, WA;  /* congestion control */
+    CcRW *ccs;
+    uint16_t *ack;
+    uint32_t *bl;
 };
 
 struct Acc {
@@ -192,12 +196,43 @@ __device__ __forceinline__ bool recv_ok(const Ctx &C, const Grp &g, const ConnRO
     return true;
 }
 
+/* DCTCP (Alizadeh et al., SIGCOMM 2010) in integer arithmetic: may the
+ * connection put another packet in flight? */
+__device__ __forceinline__ bool window_open(const CcRW &q)
+{
+    return q.sent - q.acked < (q.cwnd >> 8);
+}
+
+/* k ACKs, m of them ECN-marked, reach the connection's source in one tick:
+ * additive increase of 1/cwnd per unmarked ACK; at the end of each window of
+ * data, alpha moves 1/16 of the way to the window's marked fraction and a
+ * window that saw a mark shrinks by alpha/2. */
+__device__ __forceinline__ void dctcp_acks(CcRW &q, uint32_t k, uint32_t m)
+{
+    q.acked += k;
+    q.wa += k;
+    q.wm += m;
+    if (k > m) q.cwnd = (uint32_t)min((uint64_t)q.cwnd + (uint64_t)(k - m) * 65536u / q.cwnd, (uint64_t)CWND_MAX_FP);
+    if (q.acked >= q.wend) {
+        const uint32_t F = (uint32_t)((uint64_t)q.wm * 1024u / q.wa);
+        q.alpha = q.alpha - (q.alpha >> 4) + (F >> 4);
+        if (q.wm) {
+            const uint32_t cut = (uint32_t)(((uint64_t)q.cwnd * q.alpha) >> 11);
+            q.cwnd = max(q.cwnd - cut, 256u);
+        }
+        q.wend = q.sent;
+        q.wa = q.wm = 0;
+    }
+}
+
 __device__ __forceinline__ void activate(const Ctx &C, Acc &a, uint32_t c, uint32_t pos, const Grp &g,
                                          const ConnRO &cr, uint32_t rdy_off, uint32_t t)
 {
     C.cs[c].s_pos = pos | (CS_ACTIVE << CS_SHIFT);
     C.cs[c].s_rem = flow_size(g, cr, pos);
-    C.ready[rdy_off + (cr.lidx >> 5)] |= 1u << (cr.lidx & 31);
+    /* with congestion control a closed window keeps it out of the NIC's
+     * candidates until an ACK reopens it */
+    if (!C.cc || window_open(C.ccs[c])) C.ready[rdy_off + (cr.lidx >> 5)] |= 1u << (cr.lidx & 31);
     a.last_act1 = t + 1;
     if (C.rec) C.rec[C.n_flows + flow_id(g, cr, c, pos)] = t;
 }
@@ -253,12 +288,38 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
 {
     const HostRO hr = C.host[pr.host];
     HostRW &hw = C.hs[pr.host];
+    if (C.cc) {
+        /* the ACKs due now at this host's outgoing connections */
+        const uint32_t as = t & (C.WA - 1);
+        for (uint32_t j = 0; j < hr.n_out; j++) {
+            const uint32_t c = C.hout[hr.out_off + j];
+            const uint32_t v = C.ack[c * C.WA + as];
+            if (!v) continue;
+            C.ack[c * C.WA + as] = 0;
+            CcRW &q = C.ccs[c];
+            dctcp_acks(q, v & 0xFFu, v >> 8);
+            /* a grown window may let a waiting flow send again, and a window cut
+             * below the packets in flight stops it */
+            const uint32_t bit = 1u << (j & 31);
+            if ((C.cs[c].s_pos >> CS_SHIFT) == CS_ACTIVE && C.cs[c].s_rem && window_open(q))
+                C.ready[hr.rdy_off + (j >> 5)] |= bit;
+            else
+                C.ready[hr.rdy_off + (j >> 5)] &= ~bit;
+        }
+    }
     uint32_t si = p * C.W + slot;
     uint32_t n = C.scnt[si];
     for (uint32_t k = 0; k < n; k++) {
-        uint32_t c = C.sdesc[si * C.R + k] >> DESC_SHIFT;
+        const uint32_t desc = C.sdesc[si * C.R + k];
+        uint32_t c = (desc & ~DESC_MARK) >> DESC_SHIFT;
         ConnRW &cw = C.cs[c];
         a.delivered++;
+        if (C.cc) {
+            /* the packet's ACK reaches the source one path latency later */
+            const uint32_t ta = t + C.ccs[c].lat;
+            C.ack[c * C.WA + (ta & (C.WA - 1))] += 1u + ((desc >> 31) << 8);
+            a.max_arr = max(a.max_arr, ta);
+        }
         if (--cw.r_rem != 0) continue;
         const ConnRO cr = C.conn[c];
         const Grp g = C.grp[cr.grp];
@@ -370,9 +431,11 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
     uint32_t n = C.scnt[si];
     for (uint32_t k = 0; k < n; k++) {
         uint32_t desc = C.sdesc[si * C.R + k];
-        uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
+        uint32_t c = (desc & ~DESC_MARK) >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
         uint32_t o = (C.conn[c].route >> (4 * hop)) & 0xFu;
         if (ftop == 0 || o >= deg) { a.fault = 1; continue; }   /* cannot happen while credits hold */
+        /* ECN: marked when the egress's backlog before this tick reaches K */
+        if (C.cc && C.bl[pr.base + o] >= C.ecn_k) desc |= DESC_MARK;
         uint32_t s = fstk[--ftop];
         C.pdesc[q * Q + s] = desc + 1;
         uint32_t vi = vrow + o;
@@ -435,6 +498,11 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
         moved = true;
         rr = j + 1 == hr.n_out ? 0 : j + 1;
         ConnRW &cw = C.cs[c];
+        if (C.cc) {
+            CcRW &q = C.ccs[c];
+            q.sent++;
+            if (!window_open(q)) rdy[j >> 5] &= ~(1u << (j & 31));
+        }
         if (--cw.s_rem == 0) {
             rdy[j >> 5] &= ~(1u << (j & 31));
             uint32_t pos = cw.s_pos & CS_POS_MASK;
@@ -482,6 +550,12 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
         moved = true;
     }
     if (moved) { pw.rr = rr; pw.pushed = pushed; }
+    if (C.cc) {
+        /* packets arrived and not yet forwarded: what next tick's arrivals see */
+        uint32_t b = 0;
+        for (uint32_t i = 0; i < deg; i++) b += (uint8_t)(C.arr[prow + i] - C.phead[prow + i]);
+        C.bl[p] = b;
+    }
 }
 
 /* ------------------------------------------------------------ reductions */
@@ -541,7 +615,7 @@ __device__ void finish_state(ExpState *stp, const Shared &sh, uint32_t nwaves, u
 
 /* ----------------------------------------------------------- one experiment */
 
-template <bool IN_LDS, bool TASKS>
+template <bool IN_LDS, bool TASKS, bool CC>
 __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
 {
     const uint32_t tid = threadIdx.x, nth = blockDim.x;
@@ -588,6 +662,14 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     C.task = (const TaskRO *)(base + H->o_task);
     C.tpred = (const uint32_t *)(base + H->o_tpred);
     C.trw = (TaskRW *)(base + H->o_trw);
+    /* a compile-time 0 in the kernels without congestion control removes its
+     * code (and registers) from them */
+    C.cc = CC ? H->cc : 0u;
+    C.ecn_k = H->ecn_k;
+    C.WA = H->WA;
+    C.ccs = (CcRW *)(base + H->o_cc);
+    C.ack = (uint16_t *)(base + H->o_ack);
+    C.bl = (uint32_t *)(base + H->o_bl);
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
@@ -615,7 +697,7 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
             else phase_a_switch(C, a, p, pr, slot);
         }
         __syncthreads();
-        if (TASKS) {
+        if (TASKS && C.n_task) {
             /* Schedule, then the first flows of collectives whose task started */
             if (__syncthreads_or(schedule_tasks(C, a, tid, nth, t))) {
                 for (uint32_t p = tid; p < C.n_ports; p += nth) {
@@ -1333,10 +1415,10 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
 template <int KIND>
 __device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *arena, uint8_t *lds, Shared &sh)
 {
-    if (KIND == 0 || KIND == KIND_GENERAL_TASKS) {
-        constexpr bool T = KIND == KIND_GENERAL_TASKS;
-        if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true, T>(kp, x, arena, lds, sh);
-        else run_experiment<false, T>(kp, x, arena, lds, sh);
+    if (KIND == 0 || KIND == KIND_GENERAL_TASKS || KIND == KIND_GENERAL_CC) {
+        constexpr bool T = KIND != 0, CC = KIND == KIND_GENERAL_CC;
+        if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true, T, CC>(kp, x, arena, lds, sh);
+        else run_experiment<false, T, CC>(kp, x, arena, lds, sh);
     } else {
         /* compact kinds: 1 + (16-byte rows << 2 | 32-bit descriptors << 1 | some link faster than 1) */
         constexpr int c = KIND - 1;
@@ -1381,6 +1463,8 @@ extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w_r1(KPara
 extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w(KParams kp) { megakernel_body<8>(kp); }
 /* at most 512 threads: the task code needs more than 128 registers per lane */
 extern "C" __global__ void __launch_bounds__(512) msim_megakernel_t(KParams kp) { megakernel_body<KIND_GENERAL_TASKS>(kp); }
+/* the general path with congestion control (and a task graph if the experiment has one) */
+extern "C" __global__ void __launch_bounds__(512) msim_megakernel_cc(KParams kp) { megakernel_body<KIND_GENERAL_CC>(kp); }
 
 static const void *kernel_of(uint32_t kind)
 {
@@ -1394,7 +1478,8 @@ static const void *kernel_of(uint32_t kind)
     case 6: return (const void *)msim_megakernel_c16h;
     case 7: return (const void *)msim_megakernel_c16w_r1;
     case 8: return (const void *)msim_megakernel_c16w;
-    default: return (const void *)msim_megakernel_t;
+    case KIND_GENERAL_TASKS: return (const void *)msim_megakernel_t;
+    default: return (const void *)msim_megakernel_cc;
     }
 }
 

@@ -44,9 +44,11 @@
 #define CS_SHIFT 30
 #define CS_POS_MASK 0x3FFFFFFFu
 
-/* descriptor of a packet: connection << 4 | index of the next switch on its path */
+/* descriptor of a packet: connection << 4 | index of the next switch on its path;
+ * in the general format bit 31 carries the ECN mark (connections < 2^27) */
 #define DESC_SHIFT 4
 #define DESC_HOP_MASK 0xFu
+#define DESC_MARK 0x80000000u
 
 struct PortRO {          /* 24 bytes */
     uint32_t peer;       /* port index at the far end of the cable */
@@ -119,6 +121,20 @@ struct ConnRW {          /* 16 bytes */
     uint32_t r_rem;      /* receiver: packets left in flow r_pos */
 };
 
+/* congestion control of a connection (general format, exp_cc = DCTCP) */
+#define CC_NONE 0u
+#define CC_DCTCP 1u
+#define CWND_MAX_FP (65535u << 8)
+
+struct CcRW {            /* 32 bytes */
+    uint32_t cwnd;       /* window, 1/256 packet */
+    uint32_t alpha;      /* 1/1024 */
+    uint32_t sent, acked;/* packets over the connection */
+    uint32_t wend;       /* acknowledged count that ends the current window */
+    uint32_t wa, wm;     /* ACKs and marked ACKs in the window */
+    uint32_t lat;        /* sum of the path's link delays: ACK delay */
+};
+
 struct HostRW {          /* 32 bytes */
     uint32_t pcnt;       /* connections whose flow finished sending last tick */
     uint32_t started;    /* first activation pass done */
@@ -144,6 +160,11 @@ struct ArenaHdr {        /* general format header */
     uint32_t o_arr, o_phead, o_nslot, o_head, o_tslot, o_fcur, o_hseen;
     uint32_t o_pdesc, o_pnxt, o_fstk, o_pstate, o_scnt, o_sdesc, o_cstate, o_hstate, o_ready;
     uint32_t n_task, o_task, o_tpred, o_trw;
+    /* congestion control: ACKs of connection c due at tick t are counted in the
+     * 16-bit word o_ack[c * WA + t % WA] (ACKs | marked << 8), written by c's
+     * destination host, read and cleared by its source at tick t; o_bl[o] is
+     * switch output o's backlog after the pops of the previous tick */
+    uint32_t cc, ecn_k, WA, o_cc, o_ack, o_bl, pad_cc[2];
 };
 
 /* ---- compact format ------------------------------------------------------
@@ -244,8 +265,9 @@ struct ExpState {        /* 64 bytes */
 };
 
 /* workspace header */
-#define MSIM_KINDS 10
+#define MSIM_KINDS 11
 #define KIND_GENERAL_TASKS 9   /* the general path with a task graph */
+#define KIND_GENERAL_CC 10     /* the general path with congestion control (and tasks, if any) */
 
 struct WsHdr {
     uint32_t claim[MSIM_KINDS]; /* experiment queue counters of a run, one per kernel kind */

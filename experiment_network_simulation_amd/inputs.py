@@ -475,8 +475,8 @@ def single_batch(topo: Topology, work: Workload, queue_pkts: int = 16, ecmp_seed
 # The five benchmark configurations
 # ---------------------------------------------------------------------------
 
-BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5, 6: 0xC6, 7: 0xC7}
-FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000, 6: 768, 7: 256}
+BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5, 6: 0xC6, 7: 0xC7, 8: 0xC8}
+FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000, 6: 768, 7: 256, 8: 256}
 CONFIG_NAMES = {
     1: "C1 ring all-reduce 1 MiB, 8 hosts on one switch, NC x C grid",
     2: "C2 ring all-reduce 64 MiB over a 4x8 leaf-spine with 4 spines",
@@ -485,6 +485,8 @@ CONFIG_NAMES = {
     5: "C5 k=16 fat-tree sweep: Zipf(1.1) sparse all-to-all, 8 MiB per host",
     6: "C6 k=8 fat-tree collectives mix: tree all-reduces, ring reduce-scatters, send/recv unit tasks",
     7: "C7 k=8 fat-tree training iteration: compute, intra-server TP collectives, bucketed DP ring all-reduces",
+    8: "C8 k=8 fat-tree with DCTCP: C4's groups and failures at a quarter of the bytes, ECN threshold and "
+       "initial window swept",
 }
 
 
@@ -746,14 +748,30 @@ def _c7(e_list):
     return Batch([topo], works, exps, "C7")
 
 
+def _c8(e_list):
+    """C4's experiments (same placements, NC, C, failed cables and ECMP seeds)
+    with every message a quarter of C4's (64 MiB all-reduces, 14 MiB
+    all-gathers) and DCTCP: ECN threshold K ~ U{2..16} packets and initial
+    window W0 ~ U{8..64} packets, drawn from a stream of their own."""
+    b = _c4(e_list)
+    for w in b.works:
+        for c in w.colls:
+            c.nbytes //= 4
+    for x, e in zip(b.exps, e_list):
+        g = exp_rng(BASE_SEED[8], e)
+        x.cc, x.ecn_k, x.cwnd0 = CC_DCTCP, g.between(2, 16), g.between(8, 64)
+    b.name = "C8"
+    return b
+
+
 def make_config(cid: int, n_exp: Optional[int] = None, exp_ids: Optional[Sequence[int]] = None) -> Batch:
-    """Batch for benchmark configuration cid (1..7).  Experiment e of a config is
+    """Batch for benchmark configuration cid (1..8).  Experiment e of a config is
     the same whatever subset is drawn, so exp_ids picks a sample of the full
     batch and n_exp the first n experiments."""
     if exp_ids is None:
         exp_ids = range(FULL_E[cid] if n_exp is None else n_exp)
     e_list = list(exp_ids)
-    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5, 6: _c6, 7: _c7}[cid](e_list)
+    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5, 6: _c6, 7: _c7, 8: _c8}[cid](e_list)
     b.meta["config"] = cid
     b.meta["exp_ids"] = e_list
     return b

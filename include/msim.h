@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MSIM_ABI_VERSION 3u
+#define MSIM_ABI_VERSION 4u
 
 /* return codes */
 #define MSIM_OK 0
@@ -73,6 +73,13 @@ extern "C" {
 #define MSIM_TASK_INTRA 1        /* intra-server collective: task_ticks + ceil(task_bytes / task_beta)
                                     ticks, the alpha + size / beta model of section 4.1 */
 #define MSIM_TASK_COLL 2         /* the workload's collective task_coll, simulated packet by packet */
+
+/* congestion control (exp_cc): Multiverse section 3.2 gives flows
+ * congestion-control variables and closes each simulation step with an ACK
+ * system; section 5 names DCTCP among the algorithms it integrates */
+#define MSIM_CC_NONE 0
+#define MSIM_CC_DCTCP 1          /* ECN marks at switches, ACKs, a DCTCP window per connection */
+#define MSIM_MAX_CWND 65535      /* packets */
 
 /* compiled-in limits */
 #define MSIM_MAX_RATE 4          /* packets per tick per link direction */
@@ -122,7 +129,24 @@ extern "C" {
  *   0.  An experiment with tasks runs on the general path.
  * Experiment e: topology exp_topo[e], workload exp_work[e], switch ingress
  *   buffer exp_queue_pkts[e] packets (1..MSIM_MAX_QUEUE), ECMP seed
- *   exp_ecmp_seed[e], packet size exp_pkt_bytes[e] bytes.
+ *   exp_ecmp_seed[e], packet size exp_pkt_bytes[e] bytes, congestion control
+ *   exp_cc[e] (exp_cc NULL = MSIM_CC_NONE for all).  With MSIM_CC_DCTCP
+ *   (DCTCP, Alizadeh et al., SIGCOMM 2010, in integer arithmetic):
+ *   - a packet reaching a switch at tick t is ECN-marked when at least
+ *     exp_ecn_k[e] packets for the same egress had arrived there before t and
+ *     not left before t; the mark stays with the packet;
+ *   - a packet delivered at t acknowledges itself at its connection's source at
+ *     t + L, L the sum of the path's link delays; ACKs use no link capacity;
+ *   - each connection keeps a window cwnd (1/256 packet; initially
+ *     exp_cwnd0[e] packets, 1..MSIM_MAX_CWND) and alpha (1/1024; initially 1),
+ *     and sends only while packets sent - packets acknowledged < floor(cwnd);
+ *   - the k ACKs (m marked) of a tick add (k - m) * 65536 / cwnd to cwnd (at
+ *     most MSIM_MAX_CWND packets); when the acknowledged count reaches the
+ *     window end, alpha = alpha - alpha/16 + F/16 (F = 1024 * marked /
+ *     acknowledged in the window), cwnd = max(1 packet, cwnd - cwnd * alpha /
+ *     2048) if any was marked, and the next window ends at the packets sent so
+ *     far (the first window ends at 0).
+ *   An experiment with congestion control runs on the general path.
  */
 typedef struct msim_batch_spec {
     uint32_t version;            /* MSIM_ABI_VERSION */
@@ -147,6 +171,8 @@ typedef struct msim_batch_spec {
     const uint64_t *task_bytes;
     const uint32_t *task_beta, *task_coll;
     const uint32_t *task_pred_off, *task_pred;
+    const uint8_t *exp_cc;       /* one per experiment; NULL = no congestion control */
+    const uint32_t *exp_ecn_k, *exp_cwnd0;
 } msim_batch_spec;
 
 /* Options for msim_create.  Zero-initialise and set what you need. */

@@ -181,3 +181,24 @@ def test_task_graph_compile_and_validation(simmod, oracle):
         w.tasks = tasks
         expect_error(simmod, I.single_batch(topo, w), simmod.E_INVALID_SPEC)
         assert oracle.run(I.single_batch(topo, w), 0)["rc"] == oracle.E_INVALID
+
+
+def test_congestion_control_compile_and_validation(simmod, oracle):
+    """Experiments with DCTCP compile onto the congestion-control kernel (the
+    same batch without it stays compact), and bad parameters are rejected as
+    the oracle rejects them."""
+    b = I.make_config(8, exp_ids=[0, 5])
+    s = simmod.Sim(b)
+    inf = s.info()
+    assert inf["n_compact"] == 0 and simmod.KERNEL_NAMES[inf["main_kernel"]] == "msim_megakernel_cc"
+    for e in range(b.n_exp):
+        assert s.flow_count(e) == oracle.count(b, e)[1]
+    for x in b.exps:
+        x.cc = I.CC_NONE
+    assert simmod.Sim(b).info()["n_compact"] == 2
+    topo = I.single_switch(2)
+    w = I.xflows([(0, 1, 3)])
+    for cc, k, w0 in ((I.CC_DCTCP, 1, 0), (I.CC_DCTCP, 1, 65536), (2, 1, 1)):
+        bb = I.single_batch(topo, w, cc=cc, ecn_k=k, cwnd0=w0)
+        expect_error(simmod, bb, simmod.E_INVALID_SPEC)
+        assert oracle.run(bb, 0)["rc"] == oracle.E_INVALID

@@ -481,3 +481,67 @@ def test_alpacomm_schedules_match_oracle(simmod, oracle):
             o = D.simulate_schedule(tp, tasks, s.sender, s.order, K)
             assert int(t) == o["t_end"], (name, int(t), o["t_end"])
         log(f"reshard {len(tasks)} tasks: " + ", ".join(f"{n} {int(t)}" for n, t in zip(r.names, r.simulated)))
+
+
+# ---------------------------------------------------------------------------
+# Congestion control (ECN marks, ACK path, DCTCP windows)
+# ---------------------------------------------------------------------------
+
+def cc_batch(n, seed):
+    """Rings, broadcasts, trees and explicit flows on three fabrics, DCTCP with
+    thresholds and initial windows from tight to loose."""
+    rng = np.random.default_rng(seed)
+    topos = [I.single_switch(8), I.leaf_spine(2, 4, 2, host_rate=1, up_rate=2), I.fat_tree(4)]
+    works, exps = [], []
+    for e in range(n):
+        t = e % 3
+        nh = [8, 8, 16][t]
+        hosts = [int(h) for h in rng.permutation(nh)]
+        colls = [I.ring(I.COLL_RING_AR, 4 * 8 * I.PKT_BYTES * int(rng.integers(1, 4)), hosts[:4],
+                        int(rng.integers(1, 3)), 2 * I.PKT_BYTES),
+                 I.bcast(24 * I.PKT_BYTES, hosts[4:7], int(rng.choice([1, 4, 8])))]
+        if t == 2:
+            colls.append(I.tree(32 * I.PKT_BYTES, hosts[8:15], 2, 4 * I.PKT_BYTES))
+        w = I.Workload(colls)
+        pairs = [(hosts[i], hosts[(i + 3) % nh], int(rng.integers(1, 40))) for i in range(nh)]
+        w.xsrc, w.xdst, w.xpkts = (np.array([p[k] for p in pairs], np.uint32) for k in range(3))
+        works.append(w)
+        K = int(rng.choice([0, 1, 2, 4, 8, 1000]))
+        exps.append(I.Experiment(t, e, int(rng.integers(2, 17)), int(rng.integers(0, 2**32)), I.PKT_BYTES,
+                                 I.CC_DCTCP, K, int(rng.choice([1, 2, 4, 16, 64]))))
+    return I.Batch(topos, works, exps, "cc")
+
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_congestion_control(simmod, oracle, force_global):
+    b = cc_batch(24, 13)
+    s, g = gpu_run(simmod, b, record=range(b.n_exp), force_global=force_global)
+    assert simmod.KERNEL_NAMES[s.info()["main_kernel"]] == "msim_megakernel_cc"
+    ref = oracle_all(oracle, b, flows=True)
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+        assert_flows(s, e, ref[e])
+
+
+def test_congestion_control_hand_traces_gpu(simmod, oracle):
+    import json
+    G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "cc_traces.json")))
+    for name in ("AI_single_flow", "K0_window4", "incast_K1"):
+        gd = G[name]
+        b = I.single_batch(I.single_switch(gd["hosts"]), I.xflows([tuple(f) for f in gd["flows"]]), 16, 0,
+                           cc=I.CC_DCTCP, ecn_k=gd["K"], cwnd0=gd["W0"])
+        s, g = gpu_run(simmod, b, record=[0])
+        ft = s.flow_ticks(0)
+        assert list(ft["rd"]) == gd["rd"] and list(ft["sd"]) == gd["sd"], name
+        assert int(g["tick"][0]) == max(gd["rd"])
+
+
+def test_c8_sample(simmod, oracle):
+    ids = [0, 101, 255]
+    b = I.make_config(8, exp_ids=ids)
+    s, g = gpu_run(simmod, b, record=[0])
+    ref = oracle_all(oracle, b, flows=False)
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+    o = oracle.run(b, 0, flows=True)
+    assert_flows(s, 0, o)
