@@ -77,6 +77,62 @@ struct Ctx {
     uint32_t *bl;
 };
 
+/* per-byte a - b (mod 256) of eight packed bytes */
+__device__ __forceinline__ uint64_t bytes_sub(uint64_t a, uint64_t b)
+{
+    const uint64_t H = 0x8080808080808080ull;
+    return ((a | H) - (b & ~H)) ^ ((a ^ ~b) & H);
+}
+
+/* 0x80 in every byte of d that is not zero */
+__device__ __forceinline__ uint64_t bytes_nz(uint64_t d)
+{
+    const uint64_t L = 0x7F7F7F7F7F7F7F7Full;
+    return ((((d & L) + L) | d) & ~L);
+}
+
+/* First set byte-flag at or after byte rr, cyclically over the row; -1 if none. */
+template <int W>
+__device__ __forceinline__ int first_from(uint64_t n0, uint64_t n1, uint32_t rr)
+{
+    if (W == 1) {
+        const uint32_t sh = 8 * rr;
+        uint64_t rot = sh ? (n0 >> sh) | (n0 << (64 - sh)) : n0;
+        if (!rot) return -1;
+        return (int)((rr + (__builtin_ctzll(rot) >> 3)) & 7);
+    }
+    uint64_t a = rr < 8 ? n0 : n1, b = rr < 8 ? n1 : n0;
+    const uint32_t sh = 8 * (rr & 7), base = rr < 8 ? 0 : 8, other = 8 - base;
+    uint64_t m = a & (~0ull << sh);
+    if (m) return (int)(base + (__builtin_ctzll(m) >> 3));
+    if (b) return (int)(other + (__builtin_ctzll(b) >> 3));
+    m = a & ((1ull << sh) - 1ull);
+    if (m) return (int)(base + (__builtin_ctzll(m) >> 3));
+    return -1;
+}
+
+/* The first n (<= 16) bytes at p as two packed words, byte i at bits 8i..8i+7;
+ * the loads are independent, so their latencies overlap. */
+__device__ __forceinline__ void row_bytes(const uint8_t *p, uint32_t n, uint64_t &w0, uint64_t &w1)
+{
+    w0 = w1 = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < 16; i++)
+        if (i < n) {
+            const uint64_t b = p[i];
+            if (i < 8) w0 |= b << (8 * i);
+            else w1 |= b << (8 * (i - 8));
+        }
+}
+
+/* Sum of the 16 bytes of (w0, w1). */
+__device__ __forceinline__ uint32_t bytes_sum(uint64_t w0, uint64_t w1)
+{
+    const uint64_t M = 0x00FF00FF00FF00FFull;
+    const uint64_t h = (w0 & M) + ((w0 >> 8) & M) + (w1 & M) + ((w1 >> 8) & M);   /* four 16-bit lanes */
+    return (uint32_t)((h * 0x0001000100010001ull) >> 48);
+}
+
 struct Acc {
     uint64_t hops, delivered, digest;
     uint32_t tmax, last_tx1, last_act1, max_arr;
@@ -409,12 +465,19 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
     PortRW &pw = C.ps[q];
     uint32_t ftop = pw.ftop;
     uint32_t popped = 0;
-    /* free the slots of the packets the egresses took last tick */
-    for (uint32_t o = 0; o < deg; o++) {
-        uint32_t vi = vrow + o;
-        uint32_t h = C.head[vi], hs = C.hseen[vi];
-        uint32_t k = (h - hs) & 0xFFu;
-        if (!k) continue;
+    /* free the slots of the packets the egresses took last tick: the pop
+     * counts of this ingress's queues against what it has already freed */
+    uint64_t g0, g1, e0, e1;
+    row_bytes(C.head + vrow, deg, g0, g1);
+    row_bytes(C.hseen + vrow, deg, e0, e1);
+    const uint64_t k0 = bytes_sub(g0, e0), k1 = bytes_sub(g1, e1);
+    uint64_t n0 = bytes_nz(k0), n1 = bytes_nz(k1);
+    while (n0 | n1) {
+        const uint32_t o = n0 ? (uint32_t)__builtin_ctzll(n0) >> 3 : 8u + ((uint32_t)__builtin_ctzll(n1) >> 3);
+        if (o < 8) n0 &= n0 - 1; else n1 &= n1 - 1;
+        const uint32_t sh = 8 * (o & 7);
+        const uint32_t k = (uint32_t)(((o < 8 ? k0 : k1) >> sh) & 0xFFu);
+        const uint32_t vi = vrow + o;
         popped += k;
         uint32_t f = C.fcur[vi];
         for (uint32_t j = 0; j < k; j++) {
@@ -423,7 +486,7 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
             fstk[ftop++] = (uint8_t)s;
         }
         C.fcur[vi] = (uint8_t)f;
-        C.hseen[vi] = (uint8_t)h;
+        C.hseen[vi] = (uint8_t)((o < 8 ? g0 : g1) >> sh);
     }
     if (popped) pw.popped += popped;
     /* append the packets that arrive now */
@@ -526,15 +589,17 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
                                      : (int32_t)Q - (int32_t)(pw.pushed - C.ps[pr.peer].popped);
     uint32_t rr = pw.rr, pushed = pw.pushed;
     const uint32_t prow = pr.vbase + lo * deg;     /* popper-major row of this output */
+    /* packets waiting at each input for this output: appended - popped, bytewise */
+    uint64_t a0, a1, h0, h1;
+    row_bytes(C.arr + prow, deg, a0, a1);
+    row_bytes(C.phead + prow, deg, h0, h1);
+    uint64_t d0 = bytes_sub(a0, h0), d1 = bytes_sub(a1, h1);
     bool moved = false;
     for (uint32_t m = 0; m < pr.rate && credit > 0; m++) {
-        uint32_t j = MSIM_NONE;
-        uint32_t i = rr;
-        for (uint32_t k = 0; k < deg; k++) {
-            if (C.arr[prow + i] != C.phead[prow + i]) { j = i; break; }
-            i = i + 1 == deg ? 0 : i + 1;
-        }
-        if (j == MSIM_NONE) break;
+        const int jj = first_from<2>(bytes_nz(d0), bytes_nz(d1), rr);
+        if (jj < 0) break;
+        const uint32_t j = (uint32_t)jj;
+        if (j < 8) d0 -= 1ull << (8 * j); else d1 -= 1ull << (8 * (j - 8));
         uint32_t vp = prow + j;
         uint32_t qi = pr.base + j;
         uint32_t s = C.nslot[vp];
@@ -550,12 +615,8 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
         moved = true;
     }
     if (moved) { pw.rr = rr; pw.pushed = pushed; }
-    if (C.cc) {
-        /* packets arrived and not yet forwarded: what next tick's arrivals see */
-        uint32_t b = 0;
-        for (uint32_t i = 0; i < deg; i++) b += (uint8_t)(C.arr[prow + i] - C.phead[prow + i]);
-        C.bl[p] = b;
-    }
+    /* packets arrived and not yet forwarded: what next tick's arrivals see */
+    if (C.cc) C.bl[p] = bytes_sum(d0, d1);
 }
 
 /* ------------------------------------------------------------ reductions */
@@ -753,20 +814,6 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
  * byte-row (SWAR) queue bookkeeping, shared state in LDS.
  * ==================================================================== */
 
-/* per-byte a - b (mod 256) of eight packed bytes */
-__device__ __forceinline__ uint64_t bytes_sub(uint64_t a, uint64_t b)
-{
-    const uint64_t H = 0x8080808080808080ull;
-    return ((a | H) - (b & ~H)) ^ ((a ^ ~b) & H);
-}
-
-/* 0x80 in every byte of d that is not zero */
-__device__ __forceinline__ uint64_t bytes_nz(uint64_t d)
-{
-    const uint64_t L = 0x7F7F7F7F7F7F7F7Full;
-    return ((((d & L) + L) | d) & ~L);
-}
-
 /* A row of up to 16 byte counters held in registers (W words). */
 template <int W>
 struct Row {
@@ -789,26 +836,6 @@ struct Row {
         w1 = W == 2 ? *(const LDSP uint64_t *)(p + 8) : 0ull;
     }
 };
-
-/* First set byte-flag at or after byte rr, cyclically over the row; -1 if none. */
-template <int W>
-__device__ __forceinline__ int first_from(uint64_t n0, uint64_t n1, uint32_t rr)
-{
-    if (W == 1) {
-        const uint32_t sh = 8 * rr;
-        uint64_t rot = sh ? (n0 >> sh) | (n0 << (64 - sh)) : n0;
-        if (!rot) return -1;
-        return (int)((rr + (__builtin_ctzll(rot) >> 3)) & 7);
-    }
-    uint64_t a = rr < 8 ? n0 : n1, b = rr < 8 ? n1 : n0;
-    const uint32_t sh = 8 * (rr & 7), base = rr < 8 ? 0 : 8, other = 8 - base;
-    uint64_t m = a & (~0ull << sh);
-    if (m) return (int)(base + (__builtin_ctzll(m) >> 3));
-    if (b) return (int)(other + (__builtin_ctzll(b) >> 3));
-    m = a & ((1ull << sh) - 1ull);
-    if (m) return (int)(base + (__builtin_ctzll(m) >> 3));
-    return -1;
-}
 
 /* LDS-qualified pointers keep address arithmetic in 32 bits. */
 template <typename DT>
