@@ -126,6 +126,14 @@ uint32_t first_flow_size(const Grp &g, uint32_t idx)
     return g.X / g.N + (k < g.X % g.N ? 1u : 0u);
 }
 
+/* Launch bound of each kernel kind (threads per workgroup). */
+uint32_t kind_max_threads(uint32_t kind)
+{
+    if (kind == KIND_GENERAL_TASKS || kind == KIND_GENERAL_CC) return 512u;
+    if (kind == KIND_COMPACT_X8 || kind == KIND_COMPACT_X16) return COMPACT_X_THREADS;
+    return 1024u;
+}
+
 int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compiled &out)
 {
     const uint32_t t = s->exp_topo[e], w = s->exp_work[e];
@@ -527,14 +535,18 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         }
         const uint32_t rsz = maxdeg <= 8 ? 8 : 16, dt = nconn <= 4096 ? 2 : 4;
         uint32_t max_ring = 0;
+        bool xneed = false;      /* trees, send/recv groups or gated rings */
         for (const Grp &g : grp) {
             if (g.kind == GK_RING_AR || g.kind == GK_RING_AG) max_ring = std::max(max_ring, g.S);
-            if (g.kind == GK_BCAST && g.N > 65535) max_ring = 1u << 20;   /* too long a chain for CGrp.N */
-            /* the compact kernels carry ungated rings, broadcasts and explicit flows */
-            if (g.kind == GK_SEQ || g.kind == GK_TREE || g.link != MSIM_NONE) max_ring = 1u << 20;
+            if ((g.kind == GK_BCAST || g.kind == GK_SEQ || g.kind == GK_TREE) && g.N > 65535)
+                max_ring = 1u << 20;   /* too many members for CGrp.N */
+            if (g.kind == GK_SEQ || g.kind == GK_TREE || g.link != MSIM_NONE) xneed = true;
         }
+        const uint32_t base_kind = 1 + ((maxdeg > 8 ? 4u : 0u) | (nconn > 4096 ? 2u : 0u) | (R > 1 ? 1u : 0u));
+        /* the two kernels with those rules, and their thread bound */
+        const bool x_ok = !xneed || ((base_kind == 1 || base_kind == 6) && nt <= COMPACT_X_THREADS);
         if (nt <= 1024 && maxdeg <= 16 && Q <= 64 && max_out <= 64 && max_F <= C_POS_MASK && max_size < 65536 &&
-            max_ring < 1024 && ngrp <= 65535 && nconn < (1u << (32 - DESC_SHIFT))) {
+            max_ring < 1024 && ngrp <= 65535 && nconn < (1u << (32 - DESC_SHIFT)) && x_ok) {
             const uint32_t S = nt - SB;                 /* switch slots, gaps included */
             const uint32_t Vc = n_sw * rsz * rsz;
             ArenaHdr2 H{};
@@ -600,8 +612,11 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                     o.fid_base = g.fid_base;
                     o.conn_base = g.conn_base;
                     o.mS = (uint32_t)(((1ull << 24) + g.S - 1) / g.S);
+                    o.link = g.link;
                     if (g.kind == GK_BCAST) { o.p = g.p / g.S; o.Xq = g.p % g.S; o.Xr = 0; }
                     else if (g.kind == GK_XFLOW) { o.p = 0; o.Xq = 0; o.Xr = 0; }
+                    else if (g.kind == GK_TREE) { o.p = g.p; o.Xq = g.X; o.Xr = 0; }
+                    else if (g.kind == GK_SEQ) { o.p = g.p; o.Xq = 0; o.Xr = g.X; }
                     else { o.p = g.p; o.Xq = g.X / g.N; o.Xr = g.X % g.N; }
                 }
                 for (uint32_t c = 0; c < nconn; c++) {
@@ -638,6 +653,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                 out.lds_bytes = H.lds_bytes;
                 out.compact = true;
                 out.kind = 1 + ((rsz == 16 ? 4u : 0u) | (dt == 4 ? 2u : 0u) | (R > 1 ? 1u : 0u));
+                if (xneed) out.kind = out.kind == 1 ? KIND_COMPACT_X8 : KIND_COMPACT_X16;
                 out.nt = nt;
                 return MSIM_OK;
             }
@@ -870,8 +886,7 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
      * port slot; the general path strides its threads over the ports */
     for (uint32_t e = 0; e < E; e++) {
         const Compiled &c = ctx->exps[e];
-        const uint32_t cap = c.kind >= KIND_GENERAL_TASKS ? 512u : 1024u;   /* those kernels' launch bound */
-        uint32_t need = c.compact ? c.nt : std::min<uint32_t>(cap, (uint32_t)c.n_ports);
+        uint32_t need = c.compact ? c.nt : std::min<uint32_t>(kind_max_threads(c.kind), (uint32_t)c.n_ports);
         ctx->k_block[c.kind] = std::max(ctx->k_block[c.kind], ((need + 63) / 64) * 64);
         if (c.compact) I.n_compact++;
     }
@@ -880,9 +895,9 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
         uint32_t bt = std::max(64u, ctx->k_block[k]);
         if (opts && opts->block_threads) {
             bt = opts->block_threads;
-            const bool general = k == 0 || k >= KIND_GENERAL_TASKS;
-            if (bt % 64 || bt > (k >= KIND_GENERAL_TASKS ? 512u : 1024u) || bt < 64 || (!general && bt < ctx->k_block[k])) {
-                g_create_error = "block_threads must be a multiple of 64 (64..1024) covering every compact experiment's ports";
+            const bool general = k == 0 || k == KIND_GENERAL_TASKS || k == KIND_GENERAL_CC;
+            if (bt % 64 || bt > kind_max_threads(k) || bt < 64 || (!general && bt < ctx->k_block[k])) {
+                g_create_error = "block_threads must be a multiple of 64 within the kernel's launch bound, covering every compact experiment's ports";
                 delete ctx;
                 return MSIM_E_ARG;
             }

@@ -865,7 +865,7 @@ __device__ __forceinline__ CGrp cgrp_load(const LDSP CGrp *p)
     const LDSP CGrp &q = *p;
     CGrp g;
     g.kind = q.kind; g.N = q.N; g.S = q.S; g.R = q.R; g.p = q.p; g.Xq = q.Xq; g.Xr = q.Xr;
-    g.fid_base = q.fid_base; g.conn_base = q.conn_base; g.mS = q.mS;
+    g.fid_base = q.fid_base; g.conn_base = q.conn_base; g.mS = q.mS; g.link = q.link;
     return g;
 }
 
@@ -900,42 +900,59 @@ __device__ __forceinline__ uint32_t cchunk(const CGrp &g, uint32_t i, uint32_t s
     return v;
 }
 
-/* RO: the experiment's groups are all rings, known for the whole experiment,
- * so the kind tests below fold away instead of branching per lane. */
-template <bool RO>
+/* F, the group kinds the code must handle, is fixed per kernel and per
+ * experiment, so the kind tests below fold away where they cannot be true:
+ *   0  rings only;
+ *   1  rings, broadcasts and explicit flows;
+ *   2  also trees, send/recv groups and gated rings. */
+template <int F>
 __device__ __forceinline__ uint32_t csize(const CGrp &g, uint32_t idx, uint32_t pos)
 {
-    if (!RO && g.kind == GK_BCAST) return g.p + (pos < g.Xq ? 1u : 0u);
+    if (F != 0 && g.kind == GK_BCAST) return g.p + (pos < g.Xq ? 1u : 0u);
+    if (F == 2 && g.kind == GK_TREE) return pos + 1u < g.R ? g.p : g.Xq;
+    if (F == 2 && g.kind == GK_SEQ) return g.p;
     const uint32_t r = cdiv_S(g, pos);
     if (r + 1 < g.R) return g.p;
     const uint32_t k = cchunk(g, idx, pos - r * g.S);
     return g.Xq + (k < g.Xr ? 1u : 0u);
 }
 
-template <bool RO>
+template <int F>
 __device__ __forceinline__ uint32_t cfid(const CGrp &g, uint32_t idx, uint32_t pos)
 {
-    if (!RO && g.kind == GK_XFLOW) return g.fid_base + idx;
-    if (!RO && g.kind == GK_BCAST) return g.fid_base + idx * g.S + pos;
+    if (F != 0 && g.kind == GK_XFLOW) return g.fid_base + idx;
+    if (F != 0 && g.kind == GK_BCAST) return g.fid_base + idx * g.S + pos;
+    if (F == 2 && g.kind == GK_TREE) return g.fid_base + pos * 2u * (g.N - 1u) + idx;
+    if (F == 2 && g.kind == GK_SEQ) return g.fid_base + idx;
     return g.fid_base + pos * g.N + idx;
 }
 
-template <bool RO>
+template <int F>
 __device__ __forceinline__ uint32_t cflows(const CGrp &g)
 {
-    if (RO) return g.R * g.S;
+    if (F == 0) return g.R * g.S;
+    if (F == 2 && g.kind == GK_TREE) return g.R;
+    if (F == 2 && g.kind == GK_SEQ) return 1u;
     return g.kind == GK_BCAST ? g.S : (g.kind == GK_XFLOW ? 1u : g.R * g.S);
 }
 
-template <bool RO, typename DT>
+template <int F, typename DT>
 __device__ __forceinline__ bool crecv_ok(const CCtx<DT> &C, const CGrp &g, uint32_t idx, uint32_t c, uint32_t pos)
 {
-    if (RO || g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
-        if (pos - cdiv_S(g, pos) * g.S == 0) return true;
+    if (F == 0 || g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
+        if (pos - cdiv_S(g, pos) * g.S == 0) {
+            /* a gated ring's first step waits for this rank's piece of its send/recv */
+            if (F == 2 && pos == 0 && g.link != MSIM_NONE) return C.crw[C.grp[g.link].conn_base + idx].r_pos >= 1;
+            return true;
+        }
         const uint32_t cin = g.conn_base + (idx == 0 ? g.N - 1u : idx - 1u);
         return C.crw[cin].r_pos >= pos;
     }
     if (g.kind == GK_BCAST) return idx == 0 || C.crw[c - 1].r_pos > pos;
+    /* send/recv: the previous receiver's copy has left the source */
+    if (F == 2 && g.kind == GK_SEQ) return idx == 0 || (C.crw[c - 1].s_st & C_POS_MASK) >= 1;
+    if (F == 2 && g.kind == GK_TREE)
+        return tree_ready(g.N, idx, pos, [&](uint32_t j) { return (uint32_t)C.crw[g.conn_base + j].r_pos; });
     return true;
 }
 
@@ -944,53 +961,68 @@ struct HostRegs {
     uint32_t pcnt, p0, p1, p2, p3;
 };
 
-template <bool RO, typename DT>
+template <int F, typename DT>
 __device__ __forceinline__ void cactivate(const CCtx<DT> &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t pos,
                                           const CGrp &g, uint32_t idx, uint32_t t)
 {
     C.crw[c].s_st = (uint16_t)(pos | (CS_ACTIVE << C_STATE_SHIFT));
-    if (RO || g.kind != GK_XFLOW) C.crw[c].s_rem = (uint16_t)csize<RO>(g, idx, pos);
+    if (F == 0 || g.kind != GK_XFLOW) C.crw[c].s_rem = (uint16_t)csize<F>(g, idx, pos);
     hr.ready |= 1ull << C.lidx[c];
     a.last_act1 = t + 1;
-    if (C.rec) C.rec[C.n_flows + cfid<RO>(g, idx, pos)] = t;
+    if (C.rec) C.rec[C.n_flows + cfid<F>(g, idx, pos)] = t;
 }
 
 /* Activates connection d (of group g) if it was waiting and is now ready.
- * The compact path carries rings, broadcasts and explicit flows only. */
-template <bool RO, typename DT>
+ * Every caller passes a connection whose source is the calling host. */
+template <int F, typename DT>
 __device__ __forceinline__ void cwake(const CCtx<DT> &C, Acc &a, HostRegs &hr, const CGrp &g, uint32_t d, uint32_t t)
 {
     if ((C.crw[d].s_st >> C_STATE_SHIFT) != CS_IDLE) return;
     const uint32_t didx = d - g.conn_base, dpos = C.crw[d].s_st & C_POS_MASK;
-    if (crecv_ok<RO>(C, g, didx, d, dpos)) cactivate<RO>(C, a, hr, d, dpos, g, didx, t);
+    if (crecv_ok<F>(C, g, didx, d, dpos)) cactivate<F>(C, a, hr, d, dpos, g, didx, t);
 }
 
 /* After a flow over connection c (group g, index idx) has been fully
- * received: the connection leaving this host whose next flow waits on it. */
-template <bool RO, typename DT>
+ * received: the connections leaving this host whose next flow waits on it. */
+template <int F, typename DT>
 __device__ __forceinline__ void cwake_dependents(const CCtx<DT> &C, Acc &a, HostRegs &hr, const CGrp &g, uint32_t idx,
                                                  uint32_t c, uint32_t t)
 {
-    if (RO || g.kind == GK_RING_AR || g.kind == GK_RING_AG)
-        cwake<RO>(C, a, hr, g, g.conn_base + (idx + 1u == g.N ? 0u : idx + 1u), t);
-    else if (g.kind == GK_BCAST && idx + 1u < g.N)
-        cwake<RO>(C, a, hr, g, c + 1, t);
+    if (F == 0 || g.kind == GK_RING_AR || g.kind == GK_RING_AG) {
+        cwake<F>(C, a, hr, g, g.conn_base + (idx + 1u == g.N ? 0u : idx + 1u), t);
+    } else if (g.kind == GK_BCAST) {
+        if (idx + 1u < g.N) cwake<F>(C, a, hr, g, c + 1, t);
+    } else if (F == 2 && g.kind == GK_SEQ) {
+        /* this host's piece has arrived: its rank of every ring the send/recv gates */
+        for (uint32_t k = 0; k < g.Xr; k++) {
+            const CGrp h = cgrp_load(C.grp + g.link + k);
+            cwake<F>(C, a, hr, h, h.conn_base + idx, t);
+        }
+    } else if (F == 2 && g.kind == GK_TREE) {
+        tree_dependents(g.N, idx, [&](uint32_t j) { cwake<F>(C, a, hr, g, g.conn_base + j, t); });
+    }
 }
 
-template <bool RO, typename DT>
+template <int F, typename DT>
 __device__ __forceinline__ void ccheck(const CCtx<DT> &C, Acc &a, HostRegs &hr, uint32_t c, uint32_t t)
 {
     const CGrp g = cgrp_at(C, c);
     const uint32_t idx = c - g.conn_base;
     const uint32_t pos = C.crw[c].s_st & C_POS_MASK;
-    if (pos >= cflows<RO>(g)) C.crw[c].s_st = (uint16_t)(pos | (CS_DONE << C_STATE_SHIFT));
-    else if (crecv_ok<RO>(C, g, idx, c, pos)) cactivate<RO>(C, a, hr, c, pos, g, idx, t);
-    else C.crw[c].s_st = (uint16_t)(pos | (CS_IDLE << C_STATE_SHIFT));
+    if (pos >= cflows<F>(g)) {
+        C.crw[c].s_st = (uint16_t)(pos | (CS_DONE << C_STATE_SHIFT));
+        /* a send/recv's next receiver waits on this send (its SEND predecessor) */
+        if (F == 2 && g.kind == GK_SEQ && idx + 1u < g.N) cwake<F>(C, a, hr, g, c + 1, t);
+    } else if (crecv_ok<F>(C, g, idx, c, pos)) {
+        cactivate<F>(C, a, hr, c, pos, g, idx, t);
+    } else {
+        C.crw[c].s_st = (uint16_t)(pos | (CS_IDLE << C_STATE_SHIFT));
+    }
 }
 
 /* A host's arrivals: deliveries, receive completions and the activations
  * they enable (phases A and B of the tick). */
-template <bool RO, bool R1, typename DT>
+template <int F, bool R1, typename DT>
 __device__ __forceinline__ void chost_deliver(const CCtx<DT> &C, Acc &a, HostRegs &hr, LDSP DT *rec, uint32_t t)
 {
     bool any = false;
@@ -1007,15 +1039,15 @@ __device__ __forceinline__ void chost_deliver(const CCtx<DT> &C, Acc &a, HostReg
         const CGrp g = cgrp_at(C, c);
         const uint32_t idx = c - g.conn_base;
         uint32_t pos = cw.r_pos;
-        const uint32_t fid = cfid<RO>(g, idx, pos);
+        const uint32_t fid = cfid<F>(g, idx, pos);
         a.digest += mix64(((uint64_t)fid << 32) | t);
         a.tmax = t;
         a.left--;
         if (C.rec) C.rec[fid] = t;
         pos++;
         cw.r_pos = (uint16_t)pos;
-        if (pos < cflows<RO>(g)) cw.r_rem = (uint16_t)csize<RO>(g, idx, pos);
-        cwake_dependents<RO>(C, a, hr, g, idx, c, t);
+        if (pos < cflows<F>(g)) cw.r_rem = (uint16_t)csize<F>(g, idx, pos);
+        cwake_dependents<F>(C, a, hr, g, idx, c, t);
     }
     if (any)
         for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
@@ -1023,16 +1055,16 @@ __device__ __forceinline__ void chost_deliver(const CCtx<DT> &C, Acc &a, HostReg
 
 /* A host's pending activations (phase B): every connection at t = 0, then the
  * connections whose previous flow left during the last tick. */
-template <bool RO, typename DT>
+template <int F, typename DT>
 __device__ __forceinline__ void chost_pending(const CCtx<DT> &C, Acc &a, HostRegs &hr, const PortRO2 &pr, uint32_t t)
 {
     if (t == 0) {
-        for (uint32_t j = 0; j < pr.n_out; j++) ccheck<RO>(C, a, hr, (uint32_t)C.hout[pr.vbase + j], t);
+        for (uint32_t j = 0; j < pr.n_out; j++) ccheck<F>(C, a, hr, (uint32_t)C.hout[pr.vbase + j], t);
     } else if (hr.pcnt) {
-        ccheck<RO>(C, a, hr, hr.p0, t);
-        if (hr.pcnt > 1) ccheck<RO>(C, a, hr, hr.p1, t);
-        if (hr.pcnt > 2) ccheck<RO>(C, a, hr, hr.p2, t);
-        if (hr.pcnt > 3) ccheck<RO>(C, a, hr, hr.p3, t);
+        ccheck<F>(C, a, hr, hr.p0, t);
+        if (hr.pcnt > 1) ccheck<F>(C, a, hr, hr.p1, t);
+        if (hr.pcnt > 2) ccheck<F>(C, a, hr, hr.p2, t);
+        if (hr.pcnt > 3) ccheck<F>(C, a, hr, hr.p3, t);
         hr.pcnt = 0;
     }
 }
@@ -1071,7 +1103,7 @@ __device__ __forceinline__ void wave_lds_fence()
  * forwarding reads queues filled by the arrivals of the same switch (same
  * wavefront); the frees read heads advanced by the same switch's outputs.
  */
-template <int W, typename DT, bool R1>
+template <int W, typename DT, bool R1, bool X>
 __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
 {
     const uint32_t tid = threadIdx.x, nth = blockDim.x;
@@ -1251,12 +1283,12 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         } else if (is_host) {
             LDSP DT *rec = C.sdesc + sb + myoff;
             /* the ring-only copy costs registers the faster-link kinds do not have */
-            if (R1 && rings_only) {
-                chost_deliver<R1, R1>(C, a, hr, rec, t);
-                chost_pending<R1>(C, a, hr, pr, t);
+            if (R1 && !X && rings_only) {
+                chost_deliver<0, R1>(C, a, hr, rec, t);
+                chost_pending<0>(C, a, hr, pr, t);
             } else {
-                chost_deliver<false, R1>(C, a, hr, rec, t);
-                chost_pending<false>(C, a, hr, pr, t);
+                chost_deliver<X ? 2 : 1, R1>(C, a, hr, rec, t);
+                chost_pending<X ? 2 : 1>(C, a, hr, pr, t);
             }
         }
         wave_lds_fence();
@@ -1339,7 +1371,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     const uint32_t pos = cw.s_st & C_POS_MASK;
                     if (C.rec) {
                         const CGrp g = cgrp_at(C, c);
-                        C.rec[2 * C.n_flows + cfid<false>(g, c - g.conn_base, pos)] = t + 1;
+                        C.rec[2 * C.n_flows + cfid<X ? 2 : 1>(g, c - g.conn_base, pos)] = t + 1;
                     }
                     cw.s_st = (uint16_t)(pos + 1);
                     /* append c to the pending list (selects, not branches) */
@@ -1436,21 +1468,26 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     __syncthreads();
 }
 
-/* Kernel kinds: the general path, and the compact path for 8- or 16-byte
- * queue rows and 16- or 32-bit packet descriptors.  Each kind is its own
- * kernel so that each gets its own register allocation. */
+/* Kernel kinds: the general path (plain, with tasks, with congestion control),
+ * and the compact path for 8- or 16-byte queue rows and 16- or 32-bit packet
+ * descriptors, two of them also with trees, send/recv groups and gated rings.
+ * Each kind is its own kernel so that each gets its own register allocation. */
 template <int KIND>
 __device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *arena, uint8_t *lds, Shared &sh)
 {
-    if (KIND == 0 || KIND == KIND_GENERAL_TASKS || KIND == KIND_GENERAL_CC) {
+    if constexpr (KIND == 0 || KIND == KIND_GENERAL_TASKS || KIND == KIND_GENERAL_CC) {
         constexpr bool T = KIND != 0, CC = KIND == KIND_GENERAL_CC;
         if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true, T, CC>(kp, x, arena, lds, sh);
         else run_experiment<false, T, CC>(kp, x, arena, lds, sh);
+    } else if constexpr (KIND == KIND_COMPACT_X8) {
+        run_compact<1, uint16_t, true, true>(kp, x, arena, lds, sh);
+    } else if constexpr (KIND == KIND_COMPACT_X16) {
+        run_compact<2, uint16_t, false, true>(kp, x, arena, lds, sh);
     } else {
         /* compact kinds: 1 + (16-byte rows << 2 | 32-bit descriptors << 1 | some link faster than 1) */
         constexpr int c = KIND - 1;
-        run_compact<(c & 4) ? 2 : 1, typename std::conditional<(c & 2) != 0, uint32_t, uint16_t>::type, (c & 1) == 0>(
-            kp, x, arena, lds, sh);
+        run_compact<(c & 4) ? 2 : 1, typename std::conditional<(c & 2) != 0, uint32_t, uint16_t>::type, (c & 1) == 0,
+                    false>(kp, x, arena, lds, sh);
     }
 }
 
@@ -1492,6 +1529,10 @@ extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_c16w(KParams 
 extern "C" __global__ void __launch_bounds__(512) msim_megakernel_t(KParams kp) { megakernel_body<KIND_GENERAL_TASKS>(kp); }
 /* the general path with congestion control (and a task graph if the experiment has one) */
 extern "C" __global__ void __launch_bounds__(512) msim_megakernel_cc(KParams kp) { megakernel_body<KIND_GENERAL_CC>(kp); }
+/* compact kinds that also carry trees, send/recv groups and gated rings; their
+ * extra rules need registers that 1024-thread kernels do not have */
+extern "C" __global__ void __launch_bounds__(768) msim_megakernel_c8h_r1_x(KParams kp) { megakernel_body<KIND_COMPACT_X8>(kp); }
+extern "C" __global__ void __launch_bounds__(768) msim_megakernel_c16h_x(KParams kp) { megakernel_body<KIND_COMPACT_X16>(kp); }
 
 static const void *kernel_of(uint32_t kind)
 {
@@ -1506,7 +1547,9 @@ static const void *kernel_of(uint32_t kind)
     case 7: return (const void *)msim_megakernel_c16w_r1;
     case 8: return (const void *)msim_megakernel_c16w;
     case KIND_GENERAL_TASKS: return (const void *)msim_megakernel_t;
-    default: return (const void *)msim_megakernel_cc;
+    case KIND_GENERAL_CC: return (const void *)msim_megakernel_cc;
+    case KIND_COMPACT_X8: return (const void *)msim_megakernel_c8h_r1_x;
+    default: return (const void *)msim_megakernel_c16h_x;
     }
 }
 

@@ -215,15 +215,17 @@ struct ArenaHdr2 {       /* 144 bytes */
 /* Collective group as the compact path reads it: the constant quotients of
  * the flow-size rules are precomputed, and pos / S is umulhi(pos << 8, mS),
  * exact for pos < 2^14 and S < 2^10. */
-struct CGrp {            /* 36 bytes; rings (ungated), broadcasts and explicit flows only */
-    uint16_t kind, N;    /* ring members; broadcast hops; explicit: flow count (low 16 bits) */
-    uint32_t S;          /* ring: steps per round; broadcast: partitions K */
-    uint32_t R;          /* ring: rounds */
-    uint32_t p;          /* ring: chunk packets; broadcast: packets / K */
-    uint32_t Xq;         /* ring: last-round packets / N; broadcast: packets mod K */
-    uint32_t Xr;         /* ring: last-round packets mod N */
+struct CGrp {            /* 40 bytes */
+    uint16_t kind, N;    /* ring / tree members; broadcast hops; send/recv receivers;
+                            explicit: flow count (low 16 bits) */
+    uint32_t S;          /* ring: steps per round; broadcast: partitions K; tree, send/recv: 1 */
+    uint32_t R;          /* ring: rounds; tree: chunks */
+    uint32_t p;          /* ring, tree: chunk packets; broadcast: packets / K; send/recv: message packets */
+    uint32_t Xq;         /* ring: last-round packets / N; broadcast: packets mod K; tree: last chunk */
+    uint32_t Xr;         /* ring: last-round packets mod N; send/recv: groups it gates */
     uint32_t fid_base, conn_base;
     uint32_t mS;         /* ceil(2^24 / S) */
+    uint32_t link;       /* gated ring: its send/recv group; send/recv: first gated group; else MSIM_NONE */
 };
 
 struct CRW2 {            /* 8 bytes: compact connection cursors */
@@ -265,9 +267,12 @@ struct ExpState {        /* 64 bytes */
 };
 
 /* workspace header */
-#define MSIM_KINDS 11
+#define MSIM_KINDS 13
 #define KIND_GENERAL_TASKS 9   /* the general path with a task graph */
 #define KIND_GENERAL_CC 10     /* the general path with congestion control (and tasks, if any) */
+#define KIND_COMPACT_X8 11     /* compact, 8-byte rows, rate 1, with trees / send-recv / gates */
+#define KIND_COMPACT_X16 12    /* compact, 16-byte rows, a faster link, with trees / send-recv / gates */
+#define COMPACT_X_THREADS 768  /* launch bound of the two kinds above */
 
 struct WsHdr {
     uint32_t claim[MSIM_KINDS]; /* experiment queue counters of a run, one per kernel kind */

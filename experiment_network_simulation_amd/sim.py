@@ -24,7 +24,8 @@ NONE = 0xFFFFFFFF
 
 KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h_r1", "msim_megakernel_c8h", "msim_megakernel_c8w_r1",
                 "msim_megakernel_c8w", "msim_megakernel_c16h_r1", "msim_megakernel_c16h", "msim_megakernel_c16w_r1",
-                "msim_megakernel_c16w", "msim_megakernel_t", "msim_megakernel_cc"]
+                "msim_megakernel_c16w", "msim_megakernel_t", "msim_megakernel_cc", "msim_megakernel_c8h_r1_x",
+                "msim_megakernel_c16h_x"]
 
 EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_reset", "msim_results",
             "msim_flow_count", "msim_flow_ticks", "msim_task_count", "msim_task_ticks", "msim_get_info",

@@ -134,13 +134,19 @@ def test_workspace_covers_flow_records(simmod):
 
 def test_further_collectives_compile(simmod, oracle):
     """Trees, reduce-scatters and send/recv unit tasks: flow counts equal the
-    oracle's, and only the ungated rings take the compact kernels."""
+    oracle's; all of them run compact, the trees and unit tasks on the kernel
+    that carries those rules, and with force_global none does."""
     b = I.make_config(6, exp_ids=list(range(9)))
     s = simmod.Sim(b)
     for e in range(b.n_exp):
         rc, nf, nc = oracle.count(b, e)
         assert rc == 0 and s.flow_count(e) == nf
-    assert s.info()["n_compact"] == 3          # the three reduce-scatter experiments
+    inf = s.info()
+    assert inf["n_compact"] == 9
+    assert simmod.KERNEL_NAMES[inf["main_kernel"]] == "msim_megakernel_c8h_r1_x"   # 6 of the 9
+    rs = simmod.Sim(b.subset([1, 4, 7]))                                           # reduce-scatters only
+    assert simmod.KERNEL_NAMES[rs.info()["main_kernel"]] == "msim_megakernel_c8h_r1"
+    assert simmod.Sim(b, force_global=True).info()["n_compact"] == 0
 
 
 def test_gate_validation_errors(simmod):
