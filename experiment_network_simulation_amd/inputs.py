@@ -50,6 +50,9 @@ TASK_COLL = 2           # a collective of the workload, simulated packet by pack
 CC_NONE = 0             # congestion control of an experiment
 CC_DCTCP = 1            # ECN marking at switches, ACKs, DCTCP windows per connection
 
+LB_ECMP = 0             # load balancing of an experiment: one route per connection
+LB_SPRAY = 1            # every packet chooses among the equal-cost egresses at every switch
+
 KIB = 1024
 MIB = 1024 * 1024
 PKT_BYTES = 4096
@@ -315,6 +318,7 @@ class Experiment:
     cc: int = CC_NONE          # CC_NONE or CC_DCTCP
     ecn_k: int = 0             # DCTCP: marking threshold (packets)
     cwnd0: int = 0             # DCTCP: initial window (packets, >= 1)
+    lb: int = LB_ECMP          # LB_ECMP or LB_SPRAY
 
 
 @dataclass
@@ -341,7 +345,7 @@ class Batch:
             if x.work not in wmap:
                 wmap[x.work] = len(works); works.append(self.works[x.work])
             exps.append(Experiment(tmap[x.topo], wmap[x.work], x.queue_pkts, x.ecmp_seed, x.pkt_bytes,
-                                   x.cc, x.ecn_k, x.cwnd0))
+                                   x.cc, x.ecn_k, x.cwnd0, x.lb))
         meta = dict(self.meta)
         meta["subset_of"] = self.name
         meta["subset_idx"] = idx
@@ -395,6 +399,7 @@ class PackedBatch:
     exp_cc: np.ndarray           # uint8
     exp_ecn_k: np.ndarray        # uint32
     exp_cwnd0: np.ndarray        # uint32
+    exp_lb: np.ndarray           # uint8
 
     @staticmethod
     def from_batch(b: Batch) -> "PackedBatch":
@@ -462,13 +467,14 @@ class PackedBatch:
             exp_cc=np.asarray([x.cc for x in b.exps], np.uint8),
             exp_ecn_k=np.asarray([x.ecn_k for x in b.exps], np.uint32),
             exp_cwnd0=np.asarray([x.cwnd0 for x in b.exps], np.uint32),
+            exp_lb=np.asarray([x.lb for x in b.exps], np.uint8),
         )
 
 
 def single_batch(topo: Topology, work: Workload, queue_pkts: int = 16, ecmp_seed: int = 0,
                  pkt_bytes: int = PKT_BYTES, name: str = "custom", cc: int = CC_NONE, ecn_k: int = 0,
-                 cwnd0: int = 0) -> Batch:
-    return Batch([topo], [work], [Experiment(0, 0, queue_pkts, ecmp_seed, pkt_bytes, cc, ecn_k, cwnd0)], name)
+                 cwnd0: int = 0, lb: int = LB_ECMP) -> Batch:
+    return Batch([topo], [work], [Experiment(0, 0, queue_pkts, ecmp_seed, pkt_bytes, cc, ecn_k, cwnd0, lb)], name)
 
 
 # ---------------------------------------------------------------------------

@@ -130,6 +130,18 @@
  *        (1 - alpha/2)) if any was marked, and the next window ends at the
  *        packets sent so far (the first ends at 0).  cwnd is capped at 65535
  *        packets; every division floors.
+ *  W10 Packet spraying (Multiverse section 5 lists it beside ECMP as a load
+ *      balancing algorithm).  Per experiment, ECMP (every packet of a
+ *      connection on its one route, R4) or spraying: every packet chooses at
+ *      every switch among the same equal-cost candidates, keyed by its
+ *      connection and its sequence number s (the count of packets the
+ *      connection sent before it): key = conn ^ fmix32(s + 1), egress =
+ *      cand[fmix32(key ^ fmix32(switch ^ seed)) mod |cand|].  A packet that
+ *      has moved down a layer only moves down.  Delivery stays in order per
+ *      connection, as a reliable connection's receiver delivers: a packet that
+ *      overtook an earlier one waits until the earlier one has arrived, and a
+ *      flow is received when all of its packets and all earlier ones of its
+ *      connection have arrived.
  *  Numbering: connections and flows follow the input order of collectives, then
  *  explicit flows; a ring numbers its connections by (channel, rank) and its
  *  flows by (channel, round, step, rank); a broadcast by hop, and (hop, part);
@@ -153,6 +165,10 @@
  * marked window, an incast whose marks cut both windows), the every-ACK-marked
  * closed form 2L(P-1) + L on three fabrics, and the base model reproduced flow
  * by flow when neither windows nor marks can act.
+ * (tests/test_oracle_spray.py): the mixer against the published MurmurHash3
+ * vectors; single-path fabrics spray exactly like ECMP; a contention-free
+ * two-spine fabric whose sprayed arrivals and in-order completions have a
+ * closed form given the hash; equal packet-hops on multi-path fabrics.
  * Parity unpinned (the pages fix no value): which of several equal-cost ECMP
  * candidates the hash picks (only validity and length of a route are pinned),
  * the digest mixer (a checksum; per-flow ticks are compared as well), and the
@@ -177,6 +193,7 @@ enum { KIND_RING_AR = 1, KIND_RING_AG = 2, KIND_BCAST = 3, KIND_RING_RS = 4, KIN
 enum { PRED_RECV = 0, PRED_SEND = 1, PRED_TASK = 2 };
 enum { TASK_COMPUTE = 0, TASK_INTRA = 1, TASK_COLL = 2 };
 enum { CC_NONE = 0, CC_DCTCP = 1 };
+enum { LB_ECMP = 0, LB_SPRAY = 1 };
 #define CWND_MAX (65535u << 8)
 
 /* The batch, exactly as the input generator lays it out. */
@@ -208,6 +225,7 @@ typedef struct {
     const uint8_t *exp_cc;           /* 0 none, 1 DCTCP */
     const uint32_t *exp_ecn_k;       /* marking threshold, packets */
     const uint32_t *exp_cwnd0;       /* initial window, packets */
+    const uint8_t *exp_lb;           /* may be NULL: 0 ECMP, 1 packet spraying */
 } orc_batch;
 
 typedef struct {
@@ -253,6 +271,7 @@ typedef struct {
     uint32_t arrive;    /* arrival tick at the next node */
     uint32_t hop;       /* index in the connection's path of the node it reaches */
     uint32_t mark;      /* ECN mark */
+    uint32_t seq;       /* packets its connection sent before it */
 } Pkt;
 
 typedef struct {       /* FIFO of packets (ring buffer of fixed capacity) */
@@ -304,6 +323,9 @@ typedef struct {
     uint32_t wend, wa, wm;      /* window end; ACKs and marked ACKs in the window */
     uint32_t *ackq;             /* ACKs on their way back: (tick << 1 | mark), FIFO */
     uint32_t aq_cap, aq_head, aq_n;
+    /* packet spraying: arrival flags by sequence number, in-order point */
+    uint8_t *got;
+    uint32_t pkts, rnext;
 } Conn;
 
 typedef struct {
@@ -322,6 +344,8 @@ typedef struct {
     uint32_t *host_conn_off, *host_conn;
     uint32_t Q, seed, R;
     uint32_t cc, ecn_k, cwnd0;
+    uint32_t lb;
+    int32_t *dist_down, *dist_any;  /* spraying: per destination node, n_nodes entries each */
     /* tasks */
     uint32_t n_task;
     Task *task;
@@ -379,7 +403,8 @@ static void exp_free(Exp *x)
     free(x->port_off); free(x->port); free(x->flow); free(x->conn_flows);
     free(x->path_node); free(x->path_port); free(x->host_conn_off); free(x->host_conn);
     free(x->task); free(x->task_pred); free(x->flow_task);
-    if (x->conn) for (uint32_t c = 0; c < x->n_conn; c++) free(x->conn[c].ackq);
+    if (x->conn) for (uint32_t c = 0; c < x->n_conn; c++) { free(x->conn[c].ackq); free(x->conn[c].got); }
+    free(x->dist_down); free(x->dist_any);
     free(x->conn);
     memset(x, 0, sizeof(*x));
 }
@@ -828,6 +853,11 @@ static int build_routes(Exp *x)
     uint32_t maxl = 0;
     for (uint32_t n = 0; n < x->n_nodes; n++) if (x->layer[n] > maxl) maxl = x->layer[n];
     maxlen = 2 * maxl + 1;
+    if (x->lb == LB_SPRAY) {
+        x->dist_down = (int32_t *)malloc(sizeof(int32_t) * (size_t)x->n_nodes * x->n_nodes);
+        x->dist_any = (int32_t *)malloc(sizeof(int32_t) * (size_t)x->n_nodes * x->n_nodes);
+        if (!x->dist_down || !x->dist_any) { free(down); free(any); free(cand); free(done_for); return ORC_E_NOMEM; }
+    }
     x->path_node = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(x->n_conn ? x->n_conn : 1) * (maxlen + 1));
     x->path_port = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(x->n_conn ? x->n_conn : 1) * (maxlen + 1));
     if (!x->path_node || !x->path_port) { free(down); free(any); free(cand); free(done_for); return ORC_E_NOMEM; }
@@ -838,6 +868,10 @@ static int build_routes(Exp *x)
         for (uint32_t c = 0; c < x->n_conn; c++) if (x->conn[c].dst == dst) { used = 1; break; }
         if (!used) continue;
         distances(x, dst, down, any);
+        if (x->lb == LB_SPRAY) {
+            memcpy(x->dist_down + (size_t)dst * x->n_nodes, down, sizeof(int32_t) * x->n_nodes);
+            memcpy(x->dist_any + (size_t)dst * x->n_nodes, any, sizeof(int32_t) * x->n_nodes);
+        }
         for (uint32_t c = 0; c < x->n_conn && rc == ORC_OK; c++) {
             Conn *cn = &x->conn[c];
             if (cn->dst != dst) continue;
@@ -883,6 +917,31 @@ typedef struct {
     uint32_t check;                          /* nonzero: verify invariants each tick */
 } orc_opts;
 
+/* W10: the egress local port that a sprayed packet (connection c, sequence
+ * number seq) takes at switch node, toward c's destination; down_only once it
+ * has moved down a layer.  The candidates are those of the ECMP walk. */
+static uint32_t spray_egress(const Exp *x, uint32_t c, uint32_t seq, uint32_t node, int down_only)
+{
+    const uint32_t dst = x->conn[c].dst;
+    const int32_t *down = x->dist_down + (size_t)dst * x->n_nodes;
+    const int32_t *any = x->dist_any + (size_t)dst * x->n_nodes;
+    const int32_t need = down_only ? down[node] : any[node];
+    uint32_t cand[64], nc = 0;
+    for (uint32_t p = x->port_off[node]; p < x->port_off[node + 1]; p++) {
+        const Port *pp = &x->port[p];
+        uint32_t m = pp->peer_node;
+        if (!pp->alive) continue;
+        if (x->layer[m] < x->layer[node]) {
+            if (down[m] + 1 == need) cand[nc++] = p - x->port_off[node];
+        } else if (!down_only && x->layer[m] > x->layer[node]) {
+            if (any[m] + 1 == need) cand[nc++] = p - x->port_off[node];
+        }
+    }
+    if (nc == 0) return NONE;
+    const uint32_t key = c ^ fmix32(seq + 1u);
+    return cand[ecmp_hash(key, node, x->seed) % nc];
+}
+
 /* Global port index of the ingress port at path position h+1 (the far end of
  * the link leaving path position h). */
 static uint32_t out_port(const Exp *x, const Conn *c, uint32_t h)
@@ -893,8 +952,8 @@ static uint32_t out_port(const Exp *x, const Conn *c, uint32_t h)
 
 /* Sends packet (flow f, currently at path position hop, ECN mark) out of port
  * op at tick t. */
-static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t mark, uint32_t t, uint64_t *hops,
-                    uint32_t *max_arrive, uint32_t *max_occ)
+static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t mark, uint32_t seq, uint32_t t,
+                    uint64_t *hops, uint32_t *max_arrive, uint32_t *max_occ)
 {
     Port *o = &x->port[op];
     Port *in = &x->port[o->peer_port];
@@ -904,12 +963,19 @@ static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t mark
     p.arrive = t + o->delay;
     p.hop = hop + 1;
     p.mark = mark;
+    p.seq = seq;
     if (p.arrive > *max_arrive) *max_arrive = p.arrive;
     (*hops)++;
     if (x->layer[o->peer_node] == 0) {
         return fifo_push(&in->wire, p) ? ORC_E_NOMEM : ORC_OK;
     }
-    uint32_t egress = x->path_port[c->path_off + p.hop];
+    uint32_t egress;
+    if (x->lb == LB_SPRAY) {
+        egress = spray_egress(x, x->flow[f].conn, seq, o->peer_node, x->layer[o->node] > x->layer[o->peer_node]);
+        if (egress == NONE) return ORC_E_INVARIANT;    /* the candidate sets keep every packet routable */
+    } else {
+        egress = x->path_port[c->path_off + p.hop];
+    }
     in->occ++;
     if (in->occ > *max_occ) *max_occ = in->occ;
     if (in->occ > x->Q) return ORC_E_INVARIANT;        /* credits make this impossible */
@@ -976,6 +1042,15 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
         res->status = ORC_OK; res->t_end = 0;
         return ORC_OK;
     }
+    if (x->lb == LB_SPRAY) {
+        for (uint32_t ci = 0; ci < x->n_conn; ci++) {
+            Conn *c = &x->conn[ci];
+            c->pkts = 0;
+            for (uint32_t j = 0; j < c->nflow; j++) c->pkts += x->flow[x->conn_flows[c->flow_off + j]].size;
+            c->got = (uint8_t *)calloc(c->pkts ? c->pkts : 1, 1);
+            if (!c->got) return ORC_E_NOMEM;
+        }
+    }
     if (x->cc) {
         for (uint32_t ci = 0; ci < x->n_conn; ci++) {
             Conn *c = &x->conn[ci];
@@ -1011,15 +1086,13 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
             Pkt *head;
             while ((head = fifo_front(&pp->wire)) && head->arrive == t) {
                 Pkt k = fifo_pop(&pp->wire);
-                Flow *fl = &x->flow[k.flow];
-                Conn *c = &x->conn[fl->conn];
+                Conn *c = &x->conn[x->flow[k.flow].conn];
                 if (opt->check) {
-                    /* a connection delivers in order: the packet belongs to its
-                     * earliest flow not yet fully received */
-                    if (x->conn_flows[c->flow_off + c->recv_pos] != k.flow) return ORC_E_INVARIANT;
                     if (c->dst != pp->node) return ORC_E_INVARIANT;
+                    /* ECMP keeps a connection in order: the packet belongs to its
+                     * earliest flow not yet fully received */
+                    if (x->lb == LB_ECMP && x->conn_flows[c->flow_off + c->recv_pos] != k.flow) return ORC_E_INVARIANT;
                 }
-                fl->recvd++;
                 delivered++;
                 if (x->cc) {
                     /* the ACK of this packet reaches the source L ticks later */
@@ -1028,13 +1101,25 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     c->aq_n++;
                     if (t + c->lat > max_arrive) max_arrive = t + c->lat;
                 }
-                if (fl->recvd == fl->size) {
+                /* packets handed to their flows now, in connection order: with
+                 * spraying, this one and any later ones it was holding back */
+                uint32_t n_in_order = 1;
+                if (x->lb == LB_SPRAY) {
+                    if (k.seq >= c->pkts || c->got[k.seq]) return ORC_E_INVARIANT;
+                    c->got[k.seq] = 1;
+                    n_in_order = 0;
+                    while (c->rnext < c->pkts && c->got[c->rnext]) { c->rnext++; n_in_order++; }
+                }
+                for (uint32_t j = 0; j < n_in_order; j++) {
+                    const uint32_t f = x->conn_flows[c->flow_off + c->recv_pos];
+                    Flow *fl = &x->flow[f];
+                    if (++fl->recvd < fl->size) continue;
                     fl->rd = t;
                     c->recv_pos++;
-                    digest += mix64(((uint64_t)k.flow << 32) | t);
+                    digest += mix64(((uint64_t)f << 32) | t);
                     if (t > t_done) t_done = t;
                     flows_left--;
-                    uint32_t tk = x->flow_task[k.flow];
+                    uint32_t tk = x->flow_task[f];
                     if (tk != NONE && --x->task[tk].left == 0) {
                         x->task[tk].finish = t;     /* the collective's last flow arrived */
                         tasks_left--;
@@ -1128,7 +1213,7 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     uint32_t f = x->conn_flows[c->flow_off + c->cur];
                     Flow *fl = &x->flow[f];
                     if (out_port(x, c, 0) != p) return ORC_E_INVARIANT;
-                    rc = transmit(x, p, f, 0, 0, t, &hops, &max_arrive, &max_occ);
+                    rc = transmit(x, p, f, 0, 0, c->sent, t, &hops, &max_arrive, &max_occ);
                     if (rc) return rc;
                     fl->sent++;
                     c->sent++;
@@ -1141,8 +1226,8 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     Pkt k = fifo_pop(&in->voq[me]);
                     in->occ--;
                     const Conn *c = &x->conn[x->flow[k.flow].conn];
-                    if (opt->check && out_port(x, c, k.hop) != p) return ORC_E_INVARIANT;
-                    rc = transmit(x, p, k.flow, k.hop, k.mark, t, &hops, &max_arrive, &max_occ);
+                    if (opt->check && x->lb == LB_ECMP && out_port(x, c, k.hop) != p) return ORC_E_INVARIANT;
+                    rc = transmit(x, p, k.flow, k.hop, k.mark, k.seq, t, &hops, &max_arrive, &max_occ);
                     if (rc) return rc;
                     pp->rr = (pp->granted + 1) % deg;
                 }
@@ -1197,6 +1282,10 @@ int orc_run(const orc_batch *b, uint32_t e, uint32_t max_ticks, uint32_t check, 
     if (x.Q < 1) return ORC_E_INVALID;
     x.cc = b->exp_cc ? b->exp_cc[e] : CC_NONE;
     if (x.cc > CC_DCTCP) return ORC_E_INVALID;
+    x.lb = b->exp_lb ? b->exp_lb[e] : LB_ECMP;
+    /* sprayed packets of one connection see different path latencies, which
+     * the ACK timing of W9 does not describe */
+    if (x.lb > LB_SPRAY || (x.lb == LB_SPRAY && x.cc != CC_NONE)) return ORC_E_INVALID;
     if (x.cc) {
         x.ecn_k = b->exp_ecn_k[e];
         x.cwnd0 = b->exp_cwnd0[e];

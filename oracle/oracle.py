@@ -51,7 +51,7 @@ class _Batch(C.Structure):
                 ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32), ("coll_gate", _P32),
                 ("work_task_off", _P32), ("task_type", _P8), ("task_ticks", _P32), ("task_bytes", _P64),
                 ("task_beta", _P32), ("task_coll", _P32), ("task_pred_off", _P32), ("task_pred", _P32),
-                ("exp_cc", _P8), ("exp_ecn_k", _P32), ("exp_cwnd0", _P32)]
+                ("exp_cc", _P8), ("exp_ecn_k", _P32), ("exp_cwnd0", _P32), ("exp_lb", _P8)]
 
 
 class _Result(C.Structure):
@@ -114,7 +114,8 @@ class OracleBatch:
                         _ptr(p.work_task_off, _P32), _ptr(p.task_type, _P8), _ptr(p.task_ticks, _P32),
                         _ptr(p.task_bytes, _P64), _ptr(p.task_beta, _P32), _ptr(p.task_coll, _P32),
                         _ptr(p.task_pred_off, _P32), _ptr(p.task_pred, _P32),
-                        _ptr(p.exp_cc, _P8), _ptr(p.exp_ecn_k, _P32), _ptr(p.exp_cwnd0, _P32))
+                        _ptr(p.exp_cc, _P8), _ptr(p.exp_ecn_k, _P32), _ptr(p.exp_cwnd0, _P32),
+                        _ptr(p.exp_lb, _P8))
 
 
 def _as_oracle_batch(b) -> OracleBatch:
