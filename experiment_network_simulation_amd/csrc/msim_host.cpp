@@ -129,7 +129,7 @@ uint32_t first_flow_size(const Grp &g, uint32_t idx)
 /* Launch bound of each kernel kind (threads per workgroup). */
 uint32_t kind_max_threads(uint32_t kind)
 {
-    if (kind == KIND_GENERAL_TASKS || kind == KIND_GENERAL_CC) return 512u;
+    if (kind == KIND_GENERAL_TASKS || kind == KIND_GENERAL_CC || kind == KIND_GENERAL_SPRAY) return 512u;
     if (kind == KIND_COMPACT_X8 || kind == KIND_COMPACT_X16) return COMPACT_X_THREADS;
     return 1024u;
 }
@@ -151,6 +151,10 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         cwnd0 = s->exp_cwnd0[e];
         if (cwnd0 < 1 || cwnd0 > MSIM_MAX_CWND) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: initial window %u outside 1..%u", e, cwnd0, MSIM_MAX_CWND);
     }
+    const uint32_t lb = s->exp_lb ? s->exp_lb[e] : MSIM_LB_ECMP;
+    if (lb > MSIM_LB_SPRAY) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: unknown load balancing %u", e, lb);
+    if (lb == MSIM_LB_SPRAY && cc != MSIM_CC_NONE)
+        return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: packet spraying with congestion control is not supported", e);
 
     /* ---- topology: nodes, ports numbered by cable order */
     const uint32_t n0 = s->topo_node_off[t], nn = s->topo_node_off[t + 1] - n0;
@@ -410,6 +414,18 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     }
     const uint32_t n_task = (uint32_t)tasks.size();
 
+    /* ---- packet spraying: every switch's equal-cost egresses toward every
+     * destination host, in both climbing states (filled by the search below) */
+    std::vector<uint32_t> sw_row(nn, MSIM_NONE);
+    uint32_t n_sw_rows = 0;
+    std::vector<uint16_t> cand_tbl;
+    if (lb == MSIM_LB_SPRAY) {
+        for (uint32_t n = 0; n < nn; n++)
+            if (layer[n] != 0) sw_row[n] = n_sw_rows++;
+        if (nn > 65536 || n_sw_rows > 32768) return fail(out, MSIM_E_LIMIT, "experiment %u: too many nodes for packet spraying", e);
+        cand_tbl.assign((size_t)n_sw_rows * n_hosts * 2, 0);
+    }
+
     /* ---- routes: reverse breadth-first search over (node, may-still-climb)
      * states from every destination, then one walk per connection */
     std::vector<std::vector<uint32_t>> by_dst(nn);
@@ -438,6 +454,27 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                 } else if (desc && layer[n] > layer[m]) {    /* n descended to m */
                     for (uint32_t ph = 0; ph < 2; ph++)
                         if (dist[2 * n + ph] < 0) { dist[2 * n + ph] = dist[st] + 1; bfs.push_back(2 * n + ph); }
+                }
+            }
+        }
+        if (lb == MSIM_LB_SPRAY) {
+            /* the candidates of the walk below, for every switch and state */
+            for (uint32_t n = 0; n < nn; n++) {
+                if (layer[n] == 0) continue;
+                for (uint32_t st = 0; st < 2; st++) {
+                    const int32_t need = dist[2 * n + st];
+                    if (need < 0) continue;
+                    uint32_t mask = 0;
+                    for (uint32_t p = pbase[n]; p < pbase[n + 1]; p++) {
+                        if (!port[p].alive) continue;
+                        uint32_t m = port_node[port[p].peer];
+                        if (layer[m] > layer[n] && st == 0) {
+                            if (dist[2 * m] >= 0 && dist[2 * m] + 1 == need) mask |= 1u << (p - pbase[n]);
+                        } else if (layer[m] < layer[n]) {
+                            if (dist[2 * m + 1] >= 0 && dist[2 * m + 1] + 1 == need) mask |= 1u << (p - pbase[n]);
+                        }
+                    }
+                    cand_tbl[((size_t)sw_row[n] * n_hosts + host_of[dst]) * 2 + st] = (uint16_t)mask;
                 }
             }
         }
@@ -509,8 +546,8 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     out.n_ports = n_ports;
 
     /* ---- compact layout, where the experiment qualifies (no task graph, no
-     * congestion control) */
-    if (allow_compact && n_task == 0 && cc == MSIM_CC_NONE) {
+     * congestion control, ECMP) */
+    if (allow_compact && n_task == 0 && cc == MSIM_CC_NONE && lb == MSIM_LB_ECMP) {
         uint32_t maxdeg = 1, max_out = 0, max_F = 0;
         uint64_t max_size = 0;
         for (uint32_t n = 0; n < nn; n++)
@@ -675,6 +712,24 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     H.n_task = n_task;
     take(H.o_task, sizeof(TaskRO) * n_task);
     take(H.o_tpred, 4ull * tpred.size());
+    /* packet spraying: descriptor widths, port info, candidates, bitmap offsets */
+    H.lb = lb;
+    H.seed = seed;
+    std::vector<uint32_t> rwoff;
+    if (lb == MSIM_LB_SPRAY) {
+        uint64_t smax = 1;
+        for (const Conn &cn : conn) smax = std::max<uint64_t>(smax, cn.pkts);
+        uint32_t sbits = 1, cbits = 1;
+        while ((1ull << sbits) < smax) sbits++;
+        while ((1ull << cbits) < nconn) cbits++;
+        if (sbits + cbits > 32) return fail(out, MSIM_E_LIMIT, "experiment %u: connections x packets too large for sprayed descriptors", e);
+        H.sbits = sbits;
+        take(H.o_spi, 4ull * n_ports);
+        take(H.o_cand, 2ull * cand_tbl.size());
+        rwoff.assign(nconn + 1, 0);
+        for (uint32_t c = 0; c < nconn; c++) rwoff[c + 1] = rwoff[c] + (uint32_t)((conn[c].pkts + 31) / 32);
+        take(H.o_rwoff, 4ull * (nconn + 1));
+    }
     H.rw_off = (uint32_t)off;
     take(H.o_arr, n_voq);
     take(H.o_phead, n_voq);
@@ -704,6 +759,11 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         take(H.o_ack, 2ull * nconn * H.WA);
         take(H.o_bl, 4ull * n_ports);
     }
+    if (lb == MSIM_LB_SPRAY) {
+        take(H.o_sseq, 4ull * nconn);
+        take(H.o_rnext, 4ull * nconn);
+        take(H.o_rbits, 4ull * rwoff[nconn]);
+    }
     if (off > 0xFFFFFFF0ull) return fail(out, MSIM_E_LIMIT, "experiment %u: state of %zu bytes too large", e, off);
     H.bytes = (uint32_t)off;
     out.arena.assign(off, 0);
@@ -711,7 +771,19 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     memcpy(A, &H, sizeof H);
     memcpy(A + H.o_port, port.data(), sizeof(PortRO) * n_ports);
     std::vector<ConnRO> cro(nconn);
-    for (uint32_t c = 0; c < nconn; c++) cro[c] = ConnRO{conn[c].route, conn[c].grp, conn[c].idx, conn[c].lidx};
+    for (uint32_t c = 0; c < nconn; c++)   /* sprayed: the route field holds the destination host */
+        cro[c] = ConnRO{lb == MSIM_LB_SPRAY ? host_of[conn[c].dst] : conn[c].route, conn[c].grp, conn[c].idx, conn[c].lidx};
+    if (lb == MSIM_LB_SPRAY) {
+        uint32_t *spi = (uint32_t *)(A + H.o_spi);
+        for (uint32_t p = 0; p < n_ports; p++) {
+            const uint32_t n = port_node[p];
+            if (layer[n] == 0) continue;
+            const bool from_above = layer[port_node[port[p].peer]] > layer[n];
+            spi[p] = n | (sw_row[n] << 16) | (from_above ? 0x80000000u : 0u);
+        }
+        memcpy(A + H.o_cand, cand_tbl.data(), 2ull * cand_tbl.size());
+        memcpy(A + H.o_rwoff, rwoff.data(), 4ull * (nconn + 1));
+    }
     if (nconn) memcpy(A + H.o_conn, cro.data(), sizeof(ConnRO) * nconn);
     if (ngrp) memcpy(A + H.o_grp, grp.data(), sizeof(Grp) * ngrp);
     if (nconn) memcpy(A + H.o_hout, hout.data(), 4ull * nconn);
@@ -743,7 +815,8 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     }
     out.n_task = n_task;
     out.o_trw = H.o_trw;
-    out.kind = cc != MSIM_CC_NONE ? KIND_GENERAL_CC : n_task ? KIND_GENERAL_TASKS : 0;
+    out.kind = cc != MSIM_CC_NONE ? KIND_GENERAL_CC : lb == MSIM_LB_SPRAY ? KIND_GENERAL_SPRAY
+             : n_task ? KIND_GENERAL_TASKS : 0;
     out.rw_off = H.rw_off;
     out.bytes = H.bytes;
     return MSIM_OK;
@@ -895,7 +968,7 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
         uint32_t bt = std::max(64u, ctx->k_block[k]);
         if (opts && opts->block_threads) {
             bt = opts->block_threads;
-            const bool general = k == 0 || k == KIND_GENERAL_TASKS || k == KIND_GENERAL_CC;
+            const bool general = k == 0 || k == KIND_GENERAL_TASKS || k == KIND_GENERAL_CC || k == KIND_GENERAL_SPRAY;
             if (bt % 64 || bt > kind_max_threads(k) || bt < 64 || (!general && bt < ctx->k_block[k])) {
                 g_create_error = "block_threads must be a multiple of 64 within the kernel's launch bound, covering every compact experiment's ports";
                 delete ctx;

@@ -75,6 +75,10 @@ struct Ctx {
     CcRW *ccs;
     uint16_t *ack;
     uint32_t *bl;
+    uint32_t sp, sbits, seed, n_hosts;   /* packet spraying */
+    const uint32_t *spi, *rwoff;
+    const uint16_t *cand;
+    uint32_t *sseq, *rnext, *rbits;
 };
 
 /* per-byte a - b (mod 256) of eight packed bytes */
@@ -337,6 +341,30 @@ __device__ __forceinline__ void check_conn(const Ctx &C, Acc &a, uint32_t c, uin
     }
 }
 
+/* MurmurHash3's 32-bit finaliser (Appleby, public domain). */
+__device__ __forceinline__ uint32_t fmix32(uint32_t h)
+{
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+/* Packet spraying: the egress local port of packet (connection c, sequence
+ * number seq) at switch `node` among the set bits of mask (the equal-cost
+ * egresses, in port order); 0xFF if there is none. */
+__device__ __forceinline__ uint32_t spray_pick(uint32_t mask, uint32_t c, uint32_t seq, uint32_t node, uint32_t seed)
+{
+    const uint32_t n = __builtin_popcount(mask);
+    if (!n) return 0xFFu;
+    const uint32_t key = c ^ fmix32(seq + 1u);
+    uint32_t k = fmix32(key ^ fmix32(node ^ seed)) % n;
+    for (; k; k--) mask &= mask - 1u;
+    return (uint32_t)__builtin_ctz(mask);
+}
+
 /* ---------------------------------------------------------------- phase A */
 
 __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr,
@@ -367,7 +395,23 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
     uint32_t n = C.scnt[si];
     for (uint32_t k = 0; k < n; k++) {
         const uint32_t desc = C.sdesc[si * C.R + k];
-        uint32_t c = (desc & ~DESC_MARK) >> DESC_SHIFT;
+        uint32_t c, in_order = 1;
+        if (C.sp) {
+            /* sprayed: note the arrival, then hand over every packet of the
+             * connection that is now in order (this one may hold back none,
+             * or release several that overtook it) */
+            c = desc >> C.sbits;
+            const uint32_t seq = desc & ((1u << C.sbits) - 1u);
+            uint32_t *bits = C.rbits + C.rwoff[c];
+            bits[seq >> 5] |= 1u << (seq & 31);
+            const uint32_t lim = (C.rwoff[c + 1] - C.rwoff[c]) * 32u;
+            uint32_t r = C.rnext[c];
+            in_order = 0;
+            while (r < lim && ((bits[r >> 5] >> (r & 31)) & 1u)) { r++; in_order++; }
+            C.rnext[c] = r;
+        } else {
+            c = (desc & ~DESC_MARK) >> DESC_SHIFT;
+        }
         ConnRW &cw = C.cs[c];
         a.delivered++;
         if (C.cc) {
@@ -376,6 +420,7 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
             C.ack[c * C.WA + (ta & (C.WA - 1))] += 1u + ((desc >> 31) << 8);
             a.max_arr = max(a.max_arr, ta);
         }
+        for (; in_order; in_order--) {
         if (--cw.r_rem != 0) continue;
         const ConnRO cr = C.conn[c];
         const Grp g = C.grp[cr.grp];
@@ -393,6 +438,7 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
          * (hosts count down concurrently) */
         if (g.task != MSIM_NONE && atomicSub(&C.trw[g.task].left, 1u) == 1u) C.trw[g.task].finish = t;
         wake_dependents(C, a, g, cr, c, hr.rdy_off, t);
+        }
     }
     if (n) C.scnt[si] = 0;
     /* activations (phase B of the tick) */
@@ -494,13 +540,24 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
     uint32_t n = C.scnt[si];
     for (uint32_t k = 0; k < n; k++) {
         uint32_t desc = C.sdesc[si * C.R + k];
-        uint32_t c = (desc & ~DESC_MARK) >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
-        uint32_t o = (C.conn[c].route >> (4 * hop)) & 0xFu;
+        uint32_t c, o;
+        if (C.sp) {
+            /* sprayed: this switch's equal-cost egresses toward the destination,
+             * in the climbing state the ingress implies, picked by the hash */
+            c = desc >> C.sbits;
+            const uint32_t info = C.spi[q];
+            const uint32_t row = (info >> 16) & 0x7FFFu;
+            const uint32_t mask = C.cand[((size_t)row * C.n_hosts + C.conn[c].route) * 2u + (info >> 31)];
+            o = spray_pick(mask, c, desc & ((1u << C.sbits) - 1u), info & 0xFFFFu, C.seed);
+        } else {
+            c = (desc & ~DESC_MARK) >> DESC_SHIFT;
+            o = (C.conn[c].route >> (4 * (desc & DESC_HOP_MASK))) & 0xFu;
+        }
         if (ftop == 0 || o >= deg) { a.fault = 1; continue; }   /* cannot happen while credits hold */
         /* ECN: marked when the egress's backlog before this tick reaches K */
         if (C.cc && C.bl[pr.base + o] >= C.ecn_k) desc |= DESC_MARK;
         uint32_t s = fstk[--ftop];
-        C.pdesc[q * Q + s] = desc + 1;
+        C.pdesc[q * Q + s] = C.sp ? desc : desc + 1;     /* ECMP: on to the next switch of the route */
         uint32_t vi = vrow + o;
         uint32_t vp = pr.vbase + o * deg + i;
         if (C.arr[vp] == C.hseen[vi]) {
@@ -555,7 +612,7 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
         }
         if (j == MSIM_NONE) break;
         uint32_t c = C.hout[hr.out_off + j];
-        transmit(C, a, p, pr, c << DESC_SHIFT, t);
+        transmit(C, a, p, pr, C.sp ? (c << C.sbits) | C.sseq[c]++ : c << DESC_SHIFT, t);
         pushed++;
         credit--;
         moved = true;
@@ -676,7 +733,7 @@ __device__ void finish_state(ExpState *stp, const Shared &sh, uint32_t nwaves, u
 
 /* ----------------------------------------------------------- one experiment */
 
-template <bool IN_LDS, bool TASKS, bool CC>
+template <bool IN_LDS, bool TASKS, bool CC, bool SP>
 __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
 {
     const uint32_t tid = threadIdx.x, nth = blockDim.x;
@@ -731,6 +788,16 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     C.ccs = (CcRW *)(base + H->o_cc);
     C.ack = (uint16_t *)(base + H->o_ack);
     C.bl = (uint32_t *)(base + H->o_bl);
+    C.sp = SP ? H->lb : 0u;       /* a compile-time 0 elsewhere, as for C.cc */
+    C.sbits = H->sbits;
+    C.seed = H->seed;
+    C.n_hosts = H->n_hosts;
+    C.spi = (const uint32_t *)(base + H->o_spi);
+    C.cand = (const uint16_t *)(base + H->o_cand);
+    C.rwoff = (const uint32_t *)(base + H->o_rwoff);
+    C.sseq = (uint32_t *)(base + H->o_sseq);
+    C.rnext = (uint32_t *)(base + H->o_rnext);
+    C.rbits = (uint32_t *)(base + H->o_rbits);
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
@@ -1475,10 +1542,10 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
 template <int KIND>
 __device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *arena, uint8_t *lds, Shared &sh)
 {
-    if constexpr (KIND == 0 || KIND == KIND_GENERAL_TASKS || KIND == KIND_GENERAL_CC) {
-        constexpr bool T = KIND != 0, CC = KIND == KIND_GENERAL_CC;
-        if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true, T, CC>(kp, x, arena, lds, sh);
-        else run_experiment<false, T, CC>(kp, x, arena, lds, sh);
+    if constexpr (KIND == 0 || KIND == KIND_GENERAL_TASKS || KIND == KIND_GENERAL_CC || KIND == KIND_GENERAL_SPRAY) {
+        constexpr bool T = KIND != 0, CC = KIND == KIND_GENERAL_CC, SP = KIND == KIND_GENERAL_SPRAY;
+        if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true, T, CC, SP>(kp, x, arena, lds, sh);
+        else run_experiment<false, T, CC, SP>(kp, x, arena, lds, sh);
     } else if constexpr (KIND == KIND_COMPACT_X8) {
         run_compact<1, uint16_t, true, true>(kp, x, arena, lds, sh);
     } else if constexpr (KIND == KIND_COMPACT_X16) {
@@ -1533,6 +1600,8 @@ extern "C" __global__ void __launch_bounds__(512) msim_megakernel_cc(KParams kp)
  * extra rules need registers that 1024-thread kernels do not have */
 extern "C" __global__ void __launch_bounds__(768) msim_megakernel_c8h_r1_x(KParams kp) { megakernel_body<KIND_COMPACT_X8>(kp); }
 extern "C" __global__ void __launch_bounds__(768) msim_megakernel_c16h_x(KParams kp) { megakernel_body<KIND_COMPACT_X16>(kp); }
+/* the general path with packet spraying (and a task graph if the experiment has one) */
+extern "C" __global__ void __launch_bounds__(512) msim_megakernel_sp(KParams kp) { megakernel_body<KIND_GENERAL_SPRAY>(kp); }
 
 static const void *kernel_of(uint32_t kind)
 {
@@ -1549,7 +1618,8 @@ static const void *kernel_of(uint32_t kind)
     case KIND_GENERAL_TASKS: return (const void *)msim_megakernel_t;
     case KIND_GENERAL_CC: return (const void *)msim_megakernel_cc;
     case KIND_COMPACT_X8: return (const void *)msim_megakernel_c8h_r1_x;
-    default: return (const void *)msim_megakernel_c16h_x;
+    case KIND_COMPACT_X16: return (const void *)msim_megakernel_c16h_x;
+    default: return (const void *)msim_megakernel_sp;
     }
 }
 

@@ -165,6 +165,14 @@ struct ArenaHdr {        /* general format header */
      * destination host, read and cleared by its source at tick t; o_bl[o] is
      * switch output o's backlog after the pops of the previous tick */
     uint32_t cc, ecn_k, WA, o_cc, o_ack, o_bl, pad_cc[2];
+    /* packet spraying (lb = 1): descriptors are conn << sbits | sequence number;
+     * o_spi[p] = node | (table row of the switch) << 16 | (fed from above) << 31;
+     * o_cand[(row * n_hosts + dst) * 2 + down_only] = the switch's equal-cost
+     * egress ports toward host dst (a 16-bit mask); ConnRO.route holds the
+     * destination host; o_sseq / o_rnext: per connection, packets sent and
+     * packets delivered in order; o_rbits: per connection, a bitmap of arrived
+     * sequence numbers, words o_rwoff[c] .. o_rwoff[c+1]-1 */
+    uint32_t lb, sbits, seed, o_spi, o_cand, o_sseq, o_rnext, o_rwoff, o_rbits, pad_lb[3];
 };
 
 /* ---- compact format ------------------------------------------------------
@@ -267,11 +275,12 @@ struct ExpState {        /* 64 bytes */
 };
 
 /* workspace header */
-#define MSIM_KINDS 13
+#define MSIM_KINDS 14
 #define KIND_GENERAL_TASKS 9   /* the general path with a task graph */
 #define KIND_GENERAL_CC 10     /* the general path with congestion control (and tasks, if any) */
 #define KIND_COMPACT_X8 11     /* compact, 8-byte rows, rate 1, with trees / send-recv / gates */
 #define KIND_COMPACT_X16 12    /* compact, 16-byte rows, a faster link, with trees / send-recv / gates */
+#define KIND_GENERAL_SPRAY 13  /* the general path with packet spraying (and tasks, if any) */
 #define COMPACT_X_THREADS 768  /* launch bound of the two kinds above */
 
 struct WsHdr {

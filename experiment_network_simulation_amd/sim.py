@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmsim.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 OK, S_INCOMPLETE, S_DEADLOCK = 0, 1, 2
 E_INVALID_SPEC, E_UNROUTABLE, E_WORKSPACE, E_HIP, E_ARG, E_STATE, E_LIMIT = -1, -2, -3, -4, -5, -6, -7
 EXP_DONE, EXP_INCOMPLETE, EXP_DEADLOCK = 0, 1, 2
@@ -25,7 +25,7 @@ NONE = 0xFFFFFFFF
 KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h_r1", "msim_megakernel_c8h", "msim_megakernel_c8w_r1",
                 "msim_megakernel_c8w", "msim_megakernel_c16h_r1", "msim_megakernel_c16h", "msim_megakernel_c16w_r1",
                 "msim_megakernel_c16w", "msim_megakernel_t", "msim_megakernel_cc", "msim_megakernel_c8h_r1_x",
-                "msim_megakernel_c16h_x"]
+                "msim_megakernel_c16h_x", "msim_megakernel_sp"]
 
 EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_reset", "msim_results",
             "msim_flow_count", "msim_flow_ticks", "msim_task_count", "msim_task_ticks", "msim_get_info",
@@ -53,7 +53,7 @@ class _Spec(C.Structure):
                 ("exp_ecmp_seed", _P32), ("exp_pkt_bytes", _P32), ("coll_gate", _P32),
                 ("work_task_off", _P32), ("task_type", _P8), ("task_ticks", _P32), ("task_bytes", _P64),
                 ("task_beta", _P32), ("task_coll", _P32), ("task_pred_off", _P32), ("task_pred", _P32),
-                ("exp_cc", _P8), ("exp_ecn_k", _P32), ("exp_cwnd0", _P32)]
+                ("exp_cc", _P8), ("exp_ecn_k", _P32), ("exp_cwnd0", _P32), ("exp_lb", _P8)]
 
 
 class _Options(C.Structure):
@@ -143,7 +143,8 @@ class Sim:
                         _ptr(p.work_task_off, _P32), _ptr(p.task_type, _P8), _ptr(p.task_ticks, _P32),
                         _ptr(p.task_bytes, _P64), _ptr(p.task_beta, _P32), _ptr(p.task_coll, _P32),
                         _ptr(p.task_pred_off, _P32), _ptr(p.task_pred, _P32),
-                        _ptr(p.exp_cc, _P8), _ptr(p.exp_ecn_k, _P32), _ptr(p.exp_cwnd0, _P32))
+                        _ptr(p.exp_cc, _P8), _ptr(p.exp_ecn_k, _P32), _ptr(p.exp_cwnd0, _P32),
+                        _ptr(p.exp_lb, _P8))
         self._rec = np.ascontiguousarray(np.asarray(list(record), np.uint32))
         self.record = [int(x) for x in self._rec]
         opts = _Options(ABI_VERSION, len(self._rec), _ptr(self._rec, _P32) if len(self._rec) else None,

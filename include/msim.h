@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MSIM_ABI_VERSION 4u
+#define MSIM_ABI_VERSION 5u
 
 /* return codes */
 #define MSIM_OK 0
@@ -80,6 +80,10 @@ extern "C" {
 #define MSIM_CC_NONE 0
 #define MSIM_CC_DCTCP 1          /* ECN marks at switches, ACKs, a DCTCP window per connection */
 #define MSIM_MAX_CWND 65535      /* packets */
+
+/* load balancing (exp_lb), Multiverse section 5: ECMP and packet spraying */
+#define MSIM_LB_ECMP 0           /* one route per connection (hash of the connection) */
+#define MSIM_LB_SPRAY 1          /* every packet chooses at every switch (hash of connection and sequence) */
 
 /* compiled-in limits */
 #define MSIM_MAX_RATE 4          /* packets per tick per link direction */
@@ -147,6 +151,15 @@ extern "C" {
  *     2048) if any was marked, and the next window ends at the packets sent so
  *     far (the first window ends at 0).
  *   An experiment with congestion control runs on the general path.
+ *   Load balancing exp_lb[e] (exp_lb NULL = MSIM_LB_ECMP for all): with
+ *   MSIM_LB_SPRAY a packet with sequence number s (packets its connection sent
+ *   before it) leaves switch n through cand[fmix32(key ^ fmix32(n ^ seed)) mod
+ *   |cand|], key = connection ^ fmix32(s + 1), cand the same equal-cost
+ *   egresses as ECMP (sorted by port; only downward once the packet has moved
+ *   down a layer).  Each connection still delivers in order: a flow is received
+ *   once all its packets and all earlier ones of its connection have arrived.
+ *   Spraying runs on the general path, and not together with congestion
+ *   control (MSIM_E_INVALID_SPEC).
  */
 typedef struct msim_batch_spec {
     uint32_t version;            /* MSIM_ABI_VERSION */
@@ -173,6 +186,7 @@ typedef struct msim_batch_spec {
     const uint32_t *task_pred_off, *task_pred;
     const uint8_t *exp_cc;       /* one per experiment; NULL = no congestion control */
     const uint32_t *exp_ecn_k, *exp_cwnd0;
+    const uint8_t *exp_lb;       /* one per experiment; NULL = MSIM_LB_ECMP */
 } msim_batch_spec;
 
 /* Options for msim_create.  Zero-initialise and set what you need. */

@@ -208,3 +208,20 @@ def test_congestion_control_compile_and_validation(simmod, oracle):
         bb = I.single_batch(topo, w, cc=cc, ecn_k=k, cwnd0=w0)
         expect_error(simmod, bb, simmod.E_INVALID_SPEC)
         assert oracle.run(bb, 0)["rc"] == oracle.E_INVALID
+
+
+def test_packet_spraying_compile_and_validation(simmod, oracle):
+    """Sprayed experiments compile onto the spraying kernel; unknown modes and
+    spraying with congestion control are rejected as the oracle rejects them."""
+    b = I.make_config(9, exp_ids=[0, 3])
+    s = simmod.Sim(b)
+    inf = s.info()
+    assert inf["n_compact"] == 0 and simmod.KERNEL_NAMES[inf["main_kernel"]] == "msim_megakernel_sp"
+    for e in range(b.n_exp):
+        assert s.flow_count(e) == oracle.count(b, e)[1]
+    topo = I.single_switch(2)
+    w = I.xflows([(0, 1, 3)])
+    for bb in (I.single_batch(topo, w, lb=2),
+               I.single_batch(topo, w, lb=I.LB_SPRAY, cc=I.CC_DCTCP, ecn_k=2, cwnd0=2)):
+        expect_error(simmod, bb, simmod.E_INVALID_SPEC)
+        assert oracle.run(bb, 0)["rc"] == oracle.E_INVALID

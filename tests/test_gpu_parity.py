@@ -545,3 +545,70 @@ def test_c8_sample(simmod, oracle):
         assert_exp(g, e, ref[e])
     o = oracle.run(b, 0, flows=True)
     assert_flows(s, 0, o)
+
+
+# ---------------------------------------------------------------------------
+# Packet spraying (per-packet equal-cost choice, in-order delivery)
+# ---------------------------------------------------------------------------
+
+def spray_batch(n, seed):
+    """Rings, broadcasts, trees and explicit flows on multi-path fabrics (a
+    k=4 fat-tree, an oversubscribed one, a two-spine leaf-spine with rate-2
+    uplinks, random cable delays on some), every packet sprayed."""
+    rng = np.random.default_rng(seed)
+    topos = [I.fat_tree(4), I.fat_tree(4, oversub=2), I.leaf_spine(2, 4, 2, host_rate=1, up_rate=2)]
+    slow = I.fat_tree(4)
+    slow.delay = rng.integers(1, 5, slow.n_cables).astype(np.uint8)
+    topos.append(slow)
+    works, exps = [], []
+    for e in range(n):
+        t = e % 4
+        nh = int((topos[t].layer == 0).sum())
+        hosts = [int(h) for h in rng.permutation(nh)]
+        colls = [I.ring(I.COLL_RING_AR, 4 * 8 * I.PKT_BYTES * int(rng.integers(1, 4)), hosts[:4],
+                        int(rng.integers(1, 3)), 2 * I.PKT_BYTES),
+                 I.bcast(32 * I.PKT_BYTES, hosts[4:7], int(rng.choice([1, 4, 8])))]
+        if nh >= 16:
+            colls.append(I.tree(32 * I.PKT_BYTES, hosts[8:15], 2, 4 * I.PKT_BYTES))
+        w = I.Workload(colls)
+        pairs = [(hosts[i], hosts[(i + 5) % nh], int(rng.integers(1, 60))) for i in range(nh)]
+        w.xsrc, w.xdst, w.xpkts = (np.array([p[k] for p in pairs], np.uint32) for k in range(3))
+        works.append(w)
+        exps.append(I.Experiment(t, e, int(rng.integers(2, 17)), int(rng.integers(0, 2**32)), I.PKT_BYTES,
+                                 lb=I.LB_SPRAY))
+    return I.Batch(topos, works, exps, "spray")
+
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_packet_spraying(simmod, oracle, force_global):
+    b = spray_batch(24, 31)
+    s, g = gpu_run(simmod, b, record=range(b.n_exp), force_global=force_global)
+    assert simmod.KERNEL_NAMES[s.info()["main_kernel"]] == "msim_megakernel_sp"
+    ref = oracle_all(oracle, b, flows=True)
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+        assert_flows(s, e, ref[e])
+
+
+def test_packet_spraying_closed_form_gpu(simmod, oracle):
+    """The two-spine fabric of the oracle's pins: sprayed arrivals and
+    in-order completions, on the GPU."""
+    topo = I.topology_from_cables([0, 0, 1, 1, 2, 2], [(0, 2), (1, 3), (2, 4, 1, 1, 1), (2, 5, 1, 1, 5),
+                                                       (3, 4, 1, 1, 1), (3, 5, 1, 1, 5)])
+    f = oracle.fmix32
+    for seed in (0, 1, 7, 123456789):
+        P, K = 8, 4
+        arrive = [j + (4 if 1 + f(f(j + 1) ^ f(2 ^ seed)) % 2 == 1 else 12) for j in range(P)]
+        b = I.single_batch(topo, I.Workload([I.bcast(P * I.PKT_BYTES, [0, 1], K)]), 16, seed, lb=I.LB_SPRAY)
+        s, g = gpu_run(simmod, b, record=[0])
+        assert list(s.flow_ticks(0)["rd"]) == [max(arrive[:2 * (k + 1)]) for k in range(K)]
+
+
+def test_c9_sample(simmod, oracle):
+    ids = [0, 77, 200]
+    b = I.make_config(9, exp_ids=ids)
+    s, g = gpu_run(simmod, b, record=[0])
+    ref = oracle_all(oracle, b, flows=False)
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+    assert_flows(s, 0, oracle.run(b, 0, flows=True))
