@@ -53,6 +53,7 @@ struct Compiled {
     uint64_t n_flows = 0, n_conns = 0, n_ports = 0;
     uint64_t est_hops = 0, est_delivered = 0;
     uint32_t n_task = 0, o_trw = 0;   /* task graph (general format) */
+    uint32_t split_bytes = 0;         /* general format: LDS bytes of the switch/NIC state alone */
     int err = 0;
     std::string msg;
 };
@@ -698,21 +699,25 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     }
 
     /* ---- general layout */
+    /* switch ports own the buffer pools; a switch port's host field gives the
+     * pool index of its switch's port 0 (its own is that + its local index) */
+    std::vector<PortRO> gport = port;
+    uint32_t n_swp = 0;
+    for (uint32_t n = 0; n < nn; n++) {
+        if (layer[n] == 0) continue;
+        for (uint32_t p = pbase[n]; p < pbase[n + 1]; p++) gport[p].host = n_swp;
+        n_swp += deg[n];
+    }
     ArenaHdr H{};
     H.mode = MODE_GENERAL;
     H.n_ports = n_ports; H.n_hosts = n_hosts; H.n_conn = nconn; H.n_grp = ngrp;
     H.Q = Q; H.W = W; H.R = R; H.n_voq = n_voq; H.n_flows = (uint32_t)n_flows;
     size_t off = align16(sizeof(ArenaHdr));
     auto take = [&](uint32_t &field, size_t bytes) { field = (uint32_t)off; off = align16(off + bytes); };
+    /* read-only, touched by every port every tick: header, ports, hosts (and
+     * the sprayed port info); then the per-connection tables */
     take(H.o_port, sizeof(PortRO) * n_ports);
-    take(H.o_conn, sizeof(ConnRO) * nconn);
-    take(H.o_grp, sizeof(Grp) * ngrp);
-    take(H.o_hout, 4ull * nconn);
     take(H.o_host, sizeof(HostRO) * n_hosts);
-    H.n_task = n_task;
-    take(H.o_task, sizeof(TaskRO) * n_task);
-    take(H.o_tpred, 4ull * tpred.size());
-    /* packet spraying: descriptor widths, port info, candidates, bitmap offsets */
     H.lb = lb;
     H.seed = seed;
     std::vector<uint32_t> rwoff;
@@ -725,6 +730,15 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         if (sbits + cbits > 32) return fail(out, MSIM_E_LIMIT, "experiment %u: connections x packets too large for sprayed descriptors", e);
         H.sbits = sbits;
         take(H.o_spi, 4ull * n_ports);
+    }
+    H.ro_hot = (uint32_t)off;
+    take(H.o_conn, sizeof(ConnRO) * nconn);
+    take(H.o_grp, sizeof(Grp) * ngrp);
+    take(H.o_hout, 4ull * nconn);
+    H.n_task = n_task;
+    take(H.o_task, sizeof(TaskRO) * n_task);
+    take(H.o_tpred, 4ull * tpred.size());
+    if (lb == MSIM_LB_SPRAY) {
         take(H.o_cand, 2ull * cand_tbl.size());
         rwoff.assign(nconn + 1, 0);
         for (uint32_t c = 0; c < nconn; c++) rwoff[c + 1] = rwoff[c] + (uint32_t)((conn[c].pkts + 31) / 32);
@@ -738,26 +752,33 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     take(H.o_tslot, n_voq);
     take(H.o_fcur, n_voq);
     take(H.o_hseen, n_voq);
-    take(H.o_pdesc, 4ull * n_ports * Q);
-    take(H.o_pnxt, (size_t)n_ports * Q);
-    take(H.o_fstk, (size_t)n_ports * Q);
+    take(H.o_pdesc, 4ull * n_swp * Q);
+    take(H.o_pnxt, (size_t)n_swp * Q);
+    take(H.o_fstk, (size_t)n_swp * Q);
     take(H.o_pstate, sizeof(PortRW) * n_ports);
     take(H.o_scnt, (size_t)n_ports * W);
     take(H.o_sdesc, 4ull * n_ports * W * R);
-    take(H.o_cstate, sizeof(ConnRW) * nconn);
-    take(H.o_hstate, sizeof(HostRW) * n_hosts);
-    take(H.o_ready, 4ull * words);
-    take(H.o_trw, sizeof(TaskRW) * n_task);
     H.cc = cc;
     H.ecn_k = ecn_k;
     H.WA = 1;
+    H.n_rdy = words;
     if (cc != MSIM_CC_NONE) {
         uint32_t max_lat = 0;
         for (const Conn &cn : conn) max_lat = std::max(max_lat, cn.lat);
         while (H.WA <= max_lat) H.WA <<= 1;
+        take(H.o_bl, 4ull * n_ports);
+        take(H.o_ackm, 4ull * H.WA * words);
+    }
+    take(H.o_hstate, sizeof(HostRW) * n_hosts);
+    take(H.o_ready, 4ull * words);
+    /* [rw_off, rw_hot) with [0, ro_hot): the state of the switch and NIC phases,
+     * placed in LDS on its own when the whole arena does not fit */
+    H.rw_hot = (uint32_t)off;
+    take(H.o_cstate, sizeof(ConnRW) * nconn);
+    take(H.o_trw, sizeof(TaskRW) * n_task);
+    if (cc != MSIM_CC_NONE) {
         take(H.o_cc, sizeof(CcRW) * nconn);
         take(H.o_ack, 2ull * nconn * H.WA);
-        take(H.o_bl, 4ull * n_ports);
     }
     if (lb == MSIM_LB_SPRAY) {
         take(H.o_sseq, 4ull * nconn);
@@ -769,7 +790,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     out.arena.assign(off, 0);
     uint8_t *A = out.arena.data();
     memcpy(A, &H, sizeof H);
-    memcpy(A + H.o_port, port.data(), sizeof(PortRO) * n_ports);
+    memcpy(A + H.o_port, gport.data(), sizeof(PortRO) * n_ports);
     std::vector<ConnRO> cro(nconn);
     for (uint32_t c = 0; c < nconn; c++)   /* sprayed: the route field holds the destination host */
         cro[c] = ConnRO{lb == MSIM_LB_SPRAY ? host_of[conn[c].dst] : conn[c].route, conn[c].grp, conn[c].idx, conn[c].lidx};
@@ -791,7 +812,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     PortRW *ps = (PortRW *)(A + H.o_pstate);
     for (uint32_t p = 0; p < n_ports; p++) {
         if (port[p].is_host) continue;
-        uint8_t *fs = A + H.o_fstk + (size_t)p * Q;
+        uint8_t *fs = A + H.o_fstk + (size_t)(gport[p].host + gport[p].local) * Q;
         for (uint32_t k = 0; k < Q; k++) fs[k] = (uint8_t)k;
         ps[p].ftop = Q;
     }
@@ -806,6 +827,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             cr[c].cwnd = cwnd0 << 8;
             cr[c].alpha = 1024;
             cr[c].lat = conn[c].lat;
+            cr[c].aword = host[host_of[conn[c].src]].rdy_off + (conn[c].lidx >> 5);
         }
     }
     if (n_task) {
@@ -819,6 +841,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
              : n_task ? KIND_GENERAL_TASKS : 0;
     out.rw_off = H.rw_off;
     out.bytes = H.bytes;
+    out.split_bytes = H.ro_hot + (H.rw_hot - H.rw_off);
     return MSIM_OK;
 }
 
@@ -1031,6 +1054,9 @@ extern "C" int msim_bind(msim_ctx *ctx, void *dev_ws, uint64_t ws_bytes, void *s
             ctx->n_lds++;
         } else if (!ctx->force_global && c.bytes <= budget) {
             ctx->k_lds[c.kind] = std::max(ctx->k_lds[c.kind], c.bytes);
+            ctx->n_lds++;
+        } else if (!ctx->force_global && c.split_bytes && c.split_bytes <= budget) {
+            ctx->k_lds[c.kind] = std::max(ctx->k_lds[c.kind], c.split_bytes);   /* switch/NIC state only */
             ctx->n_lds++;
         }
     }

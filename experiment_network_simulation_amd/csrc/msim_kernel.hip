@@ -71,10 +71,10 @@ struct Ctx {
     const TaskRO *task;
     const uint32_t *tpred;
     TaskRW *trw;
-    uint32_t cc, ecn_k, WA;  /* congestion control */
+    uint32_t cc, ecn_k, WA, n_rdy;  /* congestion control */
     CcRW *ccs;
     uint16_t *ack;
-    uint32_t *bl;
+    uint32_t *bl, *ackm;
     uint32_t sp, sbits, seed, n_hosts;   /* packet spraying */
     const uint32_t *spi, *rwoff;
     const uint16_t *cand;
@@ -373,12 +373,18 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
     const HostRO hr = C.host[pr.host];
     HostRW &hw = C.hs[pr.host];
     if (C.cc) {
-        /* the ACKs due now at this host's outgoing connections */
+        /* the ACKs due now at this host's outgoing connections: the pending
+         * masks name the connections that have some */
         const uint32_t as = t & (C.WA - 1);
-        for (uint32_t j = 0; j < hr.n_out; j++) {
+        uint32_t *pend = C.ackm + as * C.n_rdy + hr.rdy_off;
+        for (uint32_t w = 0; w < (hr.n_out + 31) / 32; w++) {
+            uint32_t m = pend[w];
+            if (!m) continue;
+            pend[w] = 0;
+            for (; m; m &= m - 1) {
+            const uint32_t j = 32 * w + __builtin_ctz(m);
             const uint32_t c = C.hout[hr.out_off + j];
             const uint32_t v = C.ack[c * C.WA + as];
-            if (!v) continue;
             C.ack[c * C.WA + as] = 0;
             CcRW &q = C.ccs[c];
             dctcp_acks(q, v & 0xFFu, v >> 8);
@@ -389,6 +395,7 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
                 C.ready[hr.rdy_off + (j >> 5)] |= bit;
             else
                 C.ready[hr.rdy_off + (j >> 5)] &= ~bit;
+            }
         }
     }
     uint32_t si = p * C.W + slot;
@@ -415,9 +422,13 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
         ConnRW &cw = C.cs[c];
         a.delivered++;
         if (C.cc) {
-            /* the packet's ACK reaches the source one path latency later */
-            const uint32_t ta = t + C.ccs[c].lat;
-            C.ack[c * C.WA + (ta & (C.WA - 1))] += 1u + ((desc >> 31) << 8);
+            /* the packet's ACK reaches the source one path latency later; the
+             * source's pending mask for that tick gets the connection's bit
+             * (other destinations may set bits of the same word) */
+            const CcRW &q = C.ccs[c];
+            const uint32_t ta = t + q.lat, as = ta & (C.WA - 1);
+            C.ack[c * C.WA + as] += 1u + ((desc >> 31) << 8);
+            atomicOr(C.ackm + as * C.n_rdy + q.aword, 1u << (C.conn[c].lidx & 31));
             a.max_arr = max(a.max_arr, ta);
         }
         for (; in_order; in_order--) {
@@ -506,8 +517,9 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
 {
     const uint32_t deg = pr.deg, i = pr.local, Q = C.Q;
     const uint32_t vrow = pr.vbase + i * deg;      /* ingress-major row of this ingress */
-    uint8_t *pnxt = C.pnxt + q * Q;
-    uint8_t *fstk = C.fstk + q * Q;
+    const uint32_t qp = pr.host + i;               /* this ingress's buffer pool */
+    uint8_t *pnxt = C.pnxt + qp * Q;
+    uint8_t *fstk = C.fstk + qp * Q;
     PortRW &pw = C.ps[q];
     uint32_t ftop = pw.ftop;
     uint32_t popped = 0;
@@ -557,7 +569,7 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
         /* ECN: marked when the egress's backlog before this tick reaches K */
         if (C.cc && C.bl[pr.base + o] >= C.ecn_k) desc |= DESC_MARK;
         uint32_t s = fstk[--ftop];
-        C.pdesc[q * Q + s] = C.sp ? desc : desc + 1;     /* ECMP: on to the next switch of the route */
+        C.pdesc[qp * Q + s] = C.sp ? desc : desc + 1;    /* ECMP: on to the next switch of the route */
         uint32_t vi = vrow + o;
         uint32_t vp = pr.vbase + o * deg + i;
         if (C.arr[vp] == C.hseen[vi]) {
@@ -658,10 +670,10 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
         const uint32_t j = (uint32_t)jj;
         if (j < 8) d0 -= 1ull << (8 * j); else d1 -= 1ull << (8 * (j - 8));
         uint32_t vp = prow + j;
-        uint32_t qi = pr.base + j;
+        uint32_t qi = pr.host + j;                 /* switch ports: pr.host is the pool of port 0 */
         uint32_t s = C.nslot[vp];
         uint32_t desc = C.pdesc[qi * Q + s];
-        C.nslot[vp] = C.pnxt[qi * Q + s];
+        C.nslot[vp] = C.pnxt[qi * Q + s];   /* qi: pool of input j */
         uint8_t h = (uint8_t)(C.phead[vp] + 1);
         C.phead[vp] = h;
         C.head[pr.vbase + j * deg + lo] = h;
@@ -739,65 +751,82 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     const uint32_t tid = threadIdx.x, nth = blockDim.x;
     const uint32_t lane = tid & 63, wave = tid >> 6, nwaves = (nth + 63) >> 6;
     ExpState *stp = (ExpState *)(kp.ws + kp.o_state) + x;
-    const uint32_t arena_bytes = ((const ArenaHdr *)arena_g)->bytes;
-    const uint32_t rw_off = ((const ArenaHdr *)arena_g)->rw_off;
-    uint8_t *base = IN_LDS ? lds : arena_g;
-    if (IN_LDS) {
+    const ArenaHdr *H = (const ArenaHdr *)arena_g;
+    const uint32_t arena_bytes = H->bytes, rw_off = H->rw_off;
+    const uint32_t ro_hot = H->ro_hot, rw_hot = H->rw_hot;
+    /* placement: the whole arena in LDS (IN_LDS); else, if it fits, only the
+     * switch / NIC state ([0, ro_hot) then [rw_off, rw_hot), back to back);
+     * else all in HBM */
+    const bool split = !IN_LDS && kp.lds_bytes && ro_hot + (rw_hot - rw_off) <= kp.lds_bytes;
+    if (IN_LDS || split) {
         const uint4 *src = (const uint4 *)arena_g;
         uint4 *dst = (uint4 *)lds;
-        for (uint32_t i = tid; i < arena_bytes / 16; i += nth) dst[i] = src[i];
+        const uint32_t n0 = (IN_LDS ? arena_bytes : ro_hot) / 16;
+        for (uint32_t i = tid; i < n0; i += nth) dst[i] = src[i];
+        if (split) {
+            const uint4 *s2 = (const uint4 *)(arena_g + rw_off);
+            uint4 *d2 = (uint4 *)(lds + ro_hot);
+            for (uint32_t i = tid; i < (rw_hot - rw_off) / 16; i += nth) d2[i] = s2[i];
+        }
         __syncthreads();
     }
-    const ArenaHdr *H = (const ArenaHdr *)base;
+    auto at = [&](uint32_t off) -> uint8_t * {
+        if (IN_LDS) return lds + off;
+        if (split && off < ro_hot) return lds + off;
+        if (split && off >= rw_off && off < rw_hot) return lds + ro_hot + (off - rw_off);
+        return arena_g + off;
+    };
     Ctx C;
-    C.port = (const PortRO *)(base + H->o_port);
-    C.conn = (const ConnRO *)(base + H->o_conn);
-    C.grp = (const Grp *)(base + H->o_grp);
-    C.hout = (const uint32_t *)(base + H->o_hout);
-    C.host = (const HostRO *)(base + H->o_host);
-    C.arr = base + H->o_arr;
-    C.phead = base + H->o_phead;
-    C.nslot = base + H->o_nslot;
-    C.head = base + H->o_head;
-    C.tslot = base + H->o_tslot;
-    C.fcur = base + H->o_fcur;
-    C.hseen = base + H->o_hseen;
-    C.pdesc = (uint32_t *)(base + H->o_pdesc);
-    C.pnxt = base + H->o_pnxt;
-    C.fstk = base + H->o_fstk;
-    C.ps = (PortRW *)(base + H->o_pstate);
-    C.scnt = base + H->o_scnt;
-    C.sdesc = (uint32_t *)(base + H->o_sdesc);
-    C.cs = (ConnRW *)(base + H->o_cstate);
-    C.hs = (HostRW *)(base + H->o_hstate);
-    C.ready = (uint32_t *)(base + H->o_ready);
+    C.port = (const PortRO *)at(H->o_port);
+    C.conn = (const ConnRO *)at(H->o_conn);
+    C.grp = (const Grp *)at(H->o_grp);
+    C.hout = (const uint32_t *)at(H->o_hout);
+    C.host = (const HostRO *)at(H->o_host);
+    C.arr = at(H->o_arr);
+    C.phead = at(H->o_phead);
+    C.nslot = at(H->o_nslot);
+    C.head = at(H->o_head);
+    C.tslot = at(H->o_tslot);
+    C.fcur = at(H->o_fcur);
+    C.hseen = at(H->o_hseen);
+    C.pdesc = (uint32_t *)at(H->o_pdesc);
+    C.pnxt = at(H->o_pnxt);
+    C.fstk = at(H->o_fstk);
+    C.ps = (PortRW *)at(H->o_pstate);
+    C.scnt = at(H->o_scnt);
+    C.sdesc = (uint32_t *)at(H->o_sdesc);
+    C.cs = (ConnRW *)at(H->o_cstate);
+    C.hs = (HostRW *)at(H->o_hstate);
+    C.ready = (uint32_t *)at(H->o_ready);
     C.n_ports = H->n_ports;
     C.Q = H->Q;
     C.W = H->W;
     C.R = H->R;
     C.n_flows = H->n_flows;
     C.n_task = H->n_task;
-    C.task = (const TaskRO *)(base + H->o_task);
-    C.tpred = (const uint32_t *)(base + H->o_tpred);
-    C.trw = (TaskRW *)(base + H->o_trw);
+    C.task = (const TaskRO *)at(H->o_task);
+    C.tpred = (const uint32_t *)at(H->o_tpred);
+    C.trw = (TaskRW *)at(H->o_trw);
     /* a compile-time 0 in the kernels without congestion control removes its
      * code (and registers) from them */
     C.cc = CC ? H->cc : 0u;
     C.ecn_k = H->ecn_k;
     C.WA = H->WA;
-    C.ccs = (CcRW *)(base + H->o_cc);
-    C.ack = (uint16_t *)(base + H->o_ack);
-    C.bl = (uint32_t *)(base + H->o_bl);
+    C.ccs = (CcRW *)at(H->o_cc);
+    C.ack = (uint16_t *)at(H->o_ack);
+    C.bl = (uint32_t *)at(H->o_bl);
+    C.ackm = (uint32_t *)at(H->o_ackm);
+    C.n_rdy = H->n_rdy;
     C.sp = SP ? H->lb : 0u;       /* a compile-time 0 elsewhere, as for C.cc */
     C.sbits = H->sbits;
     C.seed = H->seed;
     C.n_hosts = H->n_hosts;
-    C.spi = (const uint32_t *)(base + H->o_spi);
-    C.cand = (const uint16_t *)(base + H->o_cand);
-    C.rwoff = (const uint32_t *)(base + H->o_rwoff);
-    C.sseq = (uint32_t *)(base + H->o_sseq);
-    C.rnext = (uint32_t *)(base + H->o_rnext);
-    C.rbits = (uint32_t *)(base + H->o_rbits);
+    C.spi = (const uint32_t *)at(H->o_spi);
+    C.cand = (const uint16_t *)at(H->o_cand);
+    C.rwoff = (const uint32_t *)at(H->o_rwoff);
+    C.sseq = (uint32_t *)at(H->o_sseq);
+    C.rnext = (uint32_t *)at(H->o_rnext);
+    C.rbits = (uint32_t *)at(H->o_rbits);
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
@@ -867,10 +896,11 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
         sh.mx[0][wave] = m0; sh.mx[1][wave] = m1; sh.mx[2][wave] = m2; sh.mx[3][wave] = m3; sh.mx[4][wave] = m4;
     }
     __syncthreads();
-    if (IN_LDS) {
-        const uint4 *src = (const uint4 *)(lds + rw_off);
+    if (IN_LDS || split) {
+        const uint4 *src = (const uint4 *)(lds + (IN_LDS ? rw_off : ro_hot));
         uint4 *dst = (uint4 *)(arena_g + rw_off);
-        for (uint32_t i = tid; i < (arena_bytes - rw_off) / 16; i += nth) dst[i] = src[i];
+        const uint32_t n = ((IN_LDS ? arena_bytes : rw_hot) - rw_off) / 16;
+        for (uint32_t i = tid; i < n; i += nth) dst[i] = src[i];
     }
     if (tid == 0) finish_state(stp, sh, nwaves, t, done, dead, t_dead);
     __syncthreads();

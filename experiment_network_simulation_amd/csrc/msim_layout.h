@@ -54,7 +54,8 @@ struct PortRO {          /* 24 bytes */
     uint32_t peer;       /* port index at the far end of the cable */
     uint32_t base;       /* first port index of this node */
     uint32_t vbase;      /* first queue index of this node (switches) */
-    uint32_t host;       /* host index (host ports), else MSIM_NONE */
+    uint32_t host;       /* host ports: host index; switch ports (general format): buffer pool
+                            of the switch's port 0 (port k's pool is that + k) */
     uint8_t local, deg, rate, delay;
     uint8_t alive, is_host, peer_is_host, pad;
 };
@@ -126,13 +127,15 @@ struct ConnRW {          /* 16 bytes */
 #define CC_DCTCP 1u
 #define CWND_MAX_FP (65535u << 8)
 
-struct CcRW {            /* 32 bytes */
+struct CcRW {            /* 48 bytes */
     uint32_t cwnd;       /* window, 1/256 packet */
     uint32_t alpha;      /* 1/1024 */
     uint32_t sent, acked;/* packets over the connection */
     uint32_t wend;       /* acknowledged count that ends the current window */
     uint32_t wa, wm;     /* ACKs and marked ACKs in the window */
     uint32_t lat;        /* sum of the path's link delays: ACK delay */
+    uint32_t aword;      /* the source host's ACK-pending word holding this connection's bit */
+    uint32_t pad[3];
 };
 
 struct HostRW {          /* 32 bytes */
@@ -162,9 +165,11 @@ struct ArenaHdr {        /* general format header */
     uint32_t n_task, o_task, o_tpred, o_trw;
     /* congestion control: ACKs of connection c due at tick t are counted in the
      * 16-bit word o_ack[c * WA + t % WA] (ACKs | marked << 8), written by c's
-     * destination host, read and cleared by its source at tick t; o_bl[o] is
-     * switch output o's backlog after the pops of the previous tick */
-    uint32_t cc, ecn_k, WA, o_cc, o_ack, o_bl, pad_cc[2];
+     * destination host, read and cleared by its source at tick t, which finds
+     * them through its ACK-pending masks o_ackm[(t % WA) * n_rdy + word] (one
+     * bit per outgoing connection, the host's ready-mask layout, n_rdy words);
+     * o_bl[o] is switch output o's backlog after the pops of the previous tick */
+    uint32_t cc, ecn_k, WA, o_cc, o_ack, o_bl, o_ackm, n_rdy;
     /* packet spraying (lb = 1): descriptors are conn << sbits | sequence number;
      * o_spi[p] = node | (table row of the switch) << 16 | (fed from above) << 31;
      * o_cand[(row * n_hosts + dst) * 2 + down_only] = the switch's equal-cost
@@ -172,7 +177,13 @@ struct ArenaHdr {        /* general format header */
      * destination host; o_sseq / o_rnext: per connection, packets sent and
      * packets delivered in order; o_rbits: per connection, a bitmap of arrived
      * sequence numbers, words o_rwoff[c] .. o_rwoff[c+1]-1 */
-    uint32_t lb, sbits, seed, o_spi, o_cand, o_sseq, o_rnext, o_rwoff, o_rbits, pad_lb[3];
+    uint32_t lb, sbits, seed, o_spi, o_cand, o_sseq, o_rnext, o_rwoff, o_rbits;
+    /* split placement: [0, ro_hot) and [rw_off, rw_hot) hold everything the
+     * switch phases and the host NICs touch each tick (ports, hosts, queues,
+     * pools, staging, backlogs, host state); a workgroup that cannot hold the
+     * whole arena in LDS copies these two ranges there, back to back, and
+     * leaves the per-connection state in HBM */
+    uint32_t ro_hot, rw_hot, pad_lb[1];
 };
 
 /* ---- compact format ------------------------------------------------------
