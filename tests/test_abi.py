@@ -225,3 +225,13 @@ def test_packet_spraying_compile_and_validation(simmod, oracle):
                I.single_batch(topo, w, lb=I.LB_SPRAY, cc=I.CC_DCTCP, ecn_k=2, cwnd0=2)):
         expect_error(simmod, bb, simmod.E_INVALID_SPEC)
         assert oracle.run(bb, 0)["rc"] == oracle.E_INVALID
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; asked for more it exits with a message (no GPU
+    is touched before that check)."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
