@@ -49,6 +49,7 @@ TASK_COLL = 2           # a collective of the workload, simulated packet by pack
 
 CC_NONE = 0             # congestion control of an experiment
 CC_DCTCP = 1            # ECN marking at switches, ACKs, DCTCP windows per connection
+CC_DCQCN = 2            # ECN marking at switches, CNPs, DCQCN rates per connection
 
 LB_ECMP = 0             # load balancing of an experiment: one route per connection
 LB_SPRAY = 1            # every packet chooses among the equal-cost egresses at every switch
@@ -315,8 +316,8 @@ class Experiment:
     queue_pkts: int
     ecmp_seed: int
     pkt_bytes: int = PKT_BYTES
-    cc: int = CC_NONE          # CC_NONE or CC_DCTCP
-    ecn_k: int = 0             # DCTCP: marking threshold (packets)
+    cc: int = CC_NONE          # CC_NONE, CC_DCTCP or CC_DCQCN
+    ecn_k: int = 0             # DCTCP, DCQCN: marking threshold (packets)
     cwnd0: int = 0             # DCTCP: initial window (packets, >= 1)
     lb: int = LB_ECMP          # LB_ECMP or LB_SPRAY
 

@@ -130,6 +130,23 @@
  *        (1 - alpha/2)) if any was marked, and the next window ends at the
  *        packets sent so far (the first ends at 0).  cwnd is capped at 65535
  *        packets; every division floors.
+ *  W9b DCQCN (Zhu et al., SIGCOMM 2015), the other congestion control: the same
+ *      ECN marks; the receiver of a marked packet sends a CNP, at most one
+ *      per connection every 608 ticks, reaching the source L ticks later; the
+ *      sender keeps a rate RC and target RT (1/65536 packet per tick, both
+ *      initially one packet per tick) and alpha (1/1024, initially 1).  A CNP:
+ *      RT = RC, RC = max(64, RC - RC alpha / 2048), alpha = alpha - alpha/256 +
+ *      4, and the timer, byte and stage counters restart.  Every 640 ticks
+ *      without a CNP alpha decays by alpha/256; every 640 ticks and every 2560
+ *      packets sent a rate-increase event raises the timer or byte stage count
+ *      and: below 5 in both, RT stays (fast recovery); above 5 in both, RT +=
+ *      160 (min stage - 5) (hyper increase); else RT += 64 (additive); RT is
+ *      capped at one packet per tick; then RC = (RT + RC) / 2.  Timer events
+ *      due by a tick come before that tick's CNP and sends (alpha's before the
+ *      increase on a tie).  Pacing: a packet leaves no earlier than the
+ *      connection's next send time, which the send at tick t sets to
+ *      max(previous, t - 65535/65536) + 2^32 / RC in 1/65536 tick (a pacer
+ *      that may lag its schedule by under one tick).
  *  W10 Packet spraying (Multiverse section 5 lists it beside ECMP as a load
  *      balancing algorithm).  Per experiment, ECMP (every packet of a
  *      connection on its one route, R4) or spraying: every packet chooses at
@@ -192,7 +209,16 @@
 enum { KIND_RING_AR = 1, KIND_RING_AG = 2, KIND_BCAST = 3, KIND_RING_RS = 4, KIND_TREE = 5, KIND_SENDRECV = 6 };
 enum { PRED_RECV = 0, PRED_SEND = 1, PRED_TASK = 2 };
 enum { TASK_COMPUTE = 0, TASK_INTRA = 1, TASK_COLL = 2 };
-enum { CC_NONE = 0, CC_DCTCP = 1 };
+enum { CC_NONE = 0, CC_DCTCP = 1, CC_DCQCN = 2 };
+#define QCN_ONE 65536u          /* one packet per tick */
+#define QCN_RMIN 64u
+#define QCN_T_INC 640u
+#define QCN_T_ALPHA 640u
+#define QCN_BYTES 2560u         /* packets between byte-counter events */
+#define QCN_F 5u
+#define QCN_AI 64u
+#define QCN_HAI 160u
+#define QCN_CNP_GAP 608u
 enum { LB_ECMP = 0, LB_SPRAY = 1 };
 #define CWND_MAX (65535u << 8)
 
@@ -323,6 +349,9 @@ typedef struct {
     uint32_t wend, wa, wm;      /* window end; ACKs and marked ACKs in the window */
     uint32_t *ackq;             /* ACKs on their way back: (tick << 1 | mark), FIFO */
     uint32_t aq_cap, aq_head, aq_n;
+    /* DCQCN: rate, target, stage counters, timers, CNP rate limit, pacing */
+    uint32_t rc, rt, tcnt, bcnt, bsent, next_inc, next_alpha, last_cnp;
+    uint64_t next_fp;           /* next send time, 1/65536 tick */
     /* packet spraying: arrival flags by sequence number, in-order point */
     uint8_t *got;
     uint32_t pkts, rnext;
@@ -1031,6 +1060,57 @@ static void dctcp_acks(Exp *x, Conn *c, uint32_t k, uint32_t m)
     }
 }
 
+/* W9b: a rate-increase event (timer or byte counter). */
+static void qcn_increase(Conn *c)
+{
+    const uint32_t hi = c->tcnt > c->bcnt ? c->tcnt : c->bcnt;
+    const uint32_t lo = c->tcnt < c->bcnt ? c->tcnt : c->bcnt;
+    if (hi >= QCN_F) {
+        const uint32_t add = lo > QCN_F ? (lo - QCN_F) * QCN_HAI : QCN_AI;
+        c->rt = c->rt + add > QCN_ONE ? QCN_ONE : c->rt + add;
+    }
+    c->rc = (c->rt + c->rc) / 2;
+}
+
+/* W9b: the timer events due by tick t, in time order. */
+static void qcn_timers(Conn *c, uint32_t t)
+{
+    for (;;) {
+        const uint32_t e = c->next_inc < c->next_alpha ? c->next_inc : c->next_alpha;
+        if (e > t) return;
+        if (c->next_alpha == e) { c->alpha -= c->alpha >> 8; c->next_alpha += QCN_T_ALPHA; }
+        if (c->next_inc == e) { c->tcnt++; qcn_increase(c); c->next_inc += QCN_T_INC; }
+    }
+}
+
+/* W9b: a CNP reaches connection c's source at tick t. */
+static void qcn_cnp(Conn *c, uint32_t t)
+{
+    qcn_timers(c, t);
+    c->rt = c->rc;
+    const uint32_t cut = (uint32_t)(((uint64_t)c->rc * c->alpha) >> 11);
+    c->rc = c->rc - cut < QCN_RMIN ? QCN_RMIN : c->rc - cut;
+    c->alpha = c->alpha - (c->alpha >> 8) + 4u;
+    c->tcnt = c->bcnt = c->bsent = 0;
+    c->next_inc = t + QCN_T_INC;
+    c->next_alpha = t + QCN_T_ALPHA;
+}
+
+/* W9b: the source sends a packet of connection c at tick t: timers, byte
+ * counter, then the pacer's next send time.  Returns the first tick at which
+ * the connection may send again. */
+static uint32_t qcn_sent(Conn *c, uint32_t t)
+{
+    qcn_timers(c, t);
+    if (++c->bsent == QCN_BYTES) { c->bsent = 0; c->bcnt++; qcn_increase(c); }
+    /* the pacer lags at most one tick behind its schedule, so fractional gaps
+     * average out, and an idle connection gains less than one packet of
+     * credit */
+    const uint64_t now = ((uint64_t)t << 16) > 65535u ? ((uint64_t)t << 16) - 65535u : 0;
+    c->next_fp = (c->next_fp > now ? c->next_fp : now) + (1ull << 32) / c->rc;
+    return (uint32_t)((c->next_fp + 65535u) >> 16);
+}
+
 static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts *opt)
 {
     uint64_t hops = 0, delivered = 0, digest = 0;
@@ -1056,6 +1136,10 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
             Conn *c = &x->conn[ci];
             c->cwnd = x->cwnd0 << 8;
             c->alpha = 1024;
+            c->rc = c->rt = QCN_ONE;
+            c->next_inc = QCN_T_INC;
+            c->next_alpha = QCN_T_ALPHA;
+            c->last_cnp = NONE;
             c->aq_cap = c->lat * x->R + 1;
             c->ackq = (uint32_t *)malloc(sizeof(uint32_t) * c->aq_cap);
             if (!c->ackq) return ORC_E_NOMEM;
@@ -1076,7 +1160,11 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     c->aq_n--;
                 }
                 if (c->aq_n && (c->ackq[c->aq_head] >> 1) < t) return ORC_E_INVARIANT;
-                if (k) dctcp_acks(x, c, k, m);
+                if (k && x->cc == CC_DCTCP) dctcp_acks(x, c, k, m);
+                if (k && x->cc == CC_DCQCN) {
+                    if (k > 1) return ORC_E_INVARIANT;     /* CNPs are 608 ticks apart */
+                    qcn_cnp(c, t);
+                }
             }
         }
         /* A: deliveries at hosts */
@@ -1094,8 +1182,12 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     if (x->lb == LB_ECMP && x->conn_flows[c->flow_off + c->recv_pos] != k.flow) return ORC_E_INVARIANT;
                 }
                 delivered++;
-                if (x->cc) {
-                    /* the ACK of this packet reaches the source L ticks later */
+                const int notify = x->cc == CC_DCTCP ||
+                    (x->cc == CC_DCQCN && k.mark && (c->last_cnp == NONE || t - c->last_cnp >= QCN_CNP_GAP));
+                if (notify) {
+                    /* DCTCP: this packet's ACK; DCQCN: a CNP.  It reaches the
+                     * source L ticks later */
+                    if (x->cc == CC_DCQCN) c->last_cnp = t;
                     if (c->aq_n == c->aq_cap) return ORC_E_INVARIANT;
                     c->ackq[(c->aq_head + c->aq_n) % c->aq_cap] = ((t + c->lat) << 1) | k.mark;
                     c->aq_n++;
@@ -1189,7 +1281,8 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                         Conn *c = &x->conn[x->host_conn[x->host_conn_off[node] + idx]];
                         if (c->cur >= c->nflow) continue;
                         Flow *fl = &x->flow[x->conn_flows[c->flow_off + c->cur]];
-                        if (x->cc && c->sent - c->acked >= (c->cwnd >> 8)) continue;   /* window full */
+                        if (x->cc == CC_DCTCP && c->sent - c->acked >= (c->cwnd >> 8)) continue;   /* window full */
+                        if (x->cc == CC_DCQCN && ((uint64_t)t << 16) < c->next_fp) continue;        /* paced */
                         if (fl->active && fl->sent < fl->size) { pp->granted = idx; break; }
                     }
                 } else {
@@ -1217,6 +1310,10 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     if (rc) return rc;
                     fl->sent++;
                     c->sent++;
+                    if (x->cc == CC_DCQCN) {
+                        const uint32_t next_tick = qcn_sent(c, t);
+                        if (next_tick > max_arrive) max_arrive = next_tick;
+                    }
                     if (fl->sent == fl->size) { fl->sd = t + 1; c->cur++; }
                     pp->rr = (pp->granted + 1) % n_in;
                 } else {
@@ -1281,7 +1378,7 @@ int orc_run(const orc_batch *b, uint32_t e, uint32_t max_ticks, uint32_t check, 
     x.seed = b->exp_ecmp_seed[e];
     if (x.Q < 1) return ORC_E_INVALID;
     x.cc = b->exp_cc ? b->exp_cc[e] : CC_NONE;
-    if (x.cc > CC_DCTCP) return ORC_E_INVALID;
+    if (x.cc > CC_DCQCN) return ORC_E_INVALID;
     x.lb = b->exp_lb ? b->exp_lb[e] : LB_ECMP;
     /* sprayed packets of one connection see different path latencies, which
      * the ACK timing of W9 does not describe */
@@ -1289,7 +1386,7 @@ int orc_run(const orc_batch *b, uint32_t e, uint32_t max_ticks, uint32_t check, 
     if (x.cc) {
         x.ecn_k = b->exp_ecn_k[e];
         x.cwnd0 = b->exp_cwnd0[e];
-        if (x.cwnd0 < 1 || x.cwnd0 > 65535) return ORC_E_INVALID;
+        if (x.cc == CC_DCTCP && (x.cwnd0 < 1 || x.cwnd0 > 65535)) return ORC_E_INVALID;
     }
     int rc = build_topology(b, e, &x);
     if (!rc) rc = build_workload(b, e, &x);
@@ -1359,4 +1456,30 @@ int orc_flows(const orc_batch *b, uint32_t e, uint32_t *flow_conn, uint32_t *flo
 }
 
 uint32_t orc_fmix32(uint32_t h) { return fmix32(h); }
+
+/* W9b's per-connection rate machine on its own, for pins: a fresh
+ * connection receives n events in tick order, what[i] = 0 a CNP and 1 a
+ * packet sent, at tick[i]; after each, state[4 i ..] = RC, RT, alpha and the
+ * first tick the pacer allows the next packet (the tick itself after a CNP). */
+int orc_qcn_script(uint32_t n, const uint32_t *tick, const uint8_t *what, uint32_t *state)
+{
+    Conn c;
+    memset(&c, 0, sizeof c);
+    c.rc = c.rt = QCN_ONE;
+    c.alpha = 1024;
+    c.next_inc = QCN_T_INC;
+    c.next_alpha = QCN_T_ALPHA;
+    for (uint32_t i = 0; i < n; i++) {
+        if (i && tick[i] < tick[i - 1]) return ORC_E_INVALID;
+        uint32_t next = tick[i];
+        if (what[i] == 0) qcn_cnp(&c, tick[i]);
+        else if (what[i] == 1) next = qcn_sent(&c, tick[i]);
+        else return ORC_E_INVALID;
+        state[4 * i] = c.rc;
+        state[4 * i + 1] = c.rt;
+        state[4 * i + 2] = c.alpha;
+        state[4 * i + 3] = next;
+    }
+    return ORC_OK;
+}
 uint64_t orc_mix64(uint64_t z) { return mix64(z); }

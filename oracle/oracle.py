@@ -80,6 +80,8 @@ def _load():
             lib.orc_paths.restype = C.c_int
             lib.orc_flows.argtypes = [C.POINTER(_Batch), C.c_uint32, _P32, _P32]
             lib.orc_flows.restype = C.c_int
+            lib.orc_qcn_script.argtypes = [C.c_uint32, _P32, C.POINTER(C.c_uint8), _P32]
+            lib.orc_qcn_script.restype = C.c_int
             lib.orc_fmix32.argtypes = [C.c_uint32]
             lib.orc_fmix32.restype = C.c_uint32
             lib.orc_mix64.argtypes = [C.c_uint64]
@@ -195,6 +197,21 @@ def flows(batch, e: int):
 
 def fmix32(h: int) -> int:
     return int(_load().orc_fmix32(h & 0xFFFFFFFF))
+
+
+def qcn_script(events):
+    """events: (tick, 'cnp' | 'send') in tick order, applied to one fresh
+    DCQCN connection.  Returns one (RC, RT, alpha, next allowed tick) per
+    event."""
+    n = len(events)
+    tick = np.array([t for t, _ in events], np.uint32)
+    what = np.array([{"cnp": 0, "send": 1}[w] for _, w in events], np.uint8)
+    state = np.zeros(4 * max(n, 1), np.uint32)
+    rc = _load().orc_qcn_script(n, tick.ctypes.data_as(_P32), what.ctypes.data_as(C.POINTER(C.c_uint8)),
+                                state.ctypes.data_as(_P32))
+    if rc != 0:
+        raise ValueError(f"orc_qcn_script: {rc}")
+    return [tuple(int(v) for v in state[4 * i:4 * i + 4]) for i in range(n)]
 
 
 def mix64(z: int) -> int:

@@ -48,7 +48,7 @@ def test_every_ack_marked_keeps_one_packet_per_round_trip(oracle, topo, src, dst
     assert r["status"] == oracle.OK and int(r["rd"][0]) == 2 * L * (P - 1) + L
 
 
-def random_batch(seed, cc_params):
+def random_batch(seed, cc_params, cc=I.CC_DCTCP):
     rng = np.random.default_rng(seed)
     topos = [I.single_switch(8), I.leaf_spine(2, 4, 2), I.fat_tree(4)]
     works, exps = [], []
@@ -67,7 +67,7 @@ def random_batch(seed, cc_params):
         w.xpkts = np.array([n for _, _, n in pairs], np.uint32)
         works.append(w)
         exps.append(I.Experiment(t, e, int(rng.integers(2, 16)), int(rng.integers(0, 2**32)), I.PKT_BYTES,
-                                 I.CC_DCTCP, K, w0))
+                                 cc, K, w0))
     return I.Batch(topos, works, exps, "cc")
 
 
@@ -109,5 +109,5 @@ def test_conservation_and_bounds_under_control(oracle):
 def test_cc_validation(oracle):
     topo = I.single_switch(2)
     w = I.xflows([(0, 1, 3)])
-    for cc, k, w0 in ((I.CC_DCTCP, 1, 0), (I.CC_DCTCP, 1, 65536), (2, 1, 1)):
+    for cc, k, w0 in ((I.CC_DCTCP, 1, 0), (I.CC_DCTCP, 1, 65536), (3, 1, 1)):
         assert oracle.run(I.single_batch(topo, w, cc=cc, ecn_k=k, cwnd0=w0), 0)["rc"] == oracle.E_INVALID
