@@ -27,6 +27,8 @@
 #include "msim.h"
 #include "msim_layout.h"
 
+static_assert(CC_DCTCP == MSIM_CC_DCTCP && CC_DCQCN == MSIM_CC_DCQCN, "congestion-control codes");
+
 extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t kind, uint32_t grid, uint32_t block,
                                       uint32_t lds, bool prepare, hipStream_t stream);
 extern "C" hipError_t msim_launch_reset(const KParams *kp, uint64_t o_rec_all, uint64_t rec_words,
@@ -145,12 +147,16 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     if (pkt == 0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: zero packet size", e);
     const uint32_t cc = s->exp_cc ? s->exp_cc[e] : MSIM_CC_NONE;
     uint32_t ecn_k = 0, cwnd0 = 0;
-    if (cc > MSIM_CC_DCTCP) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: unknown congestion control %u", e, cc);
+    if (cc > MSIM_CC_DCQCN) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: unknown congestion control %u", e, cc);
     if (cc == MSIM_CC_DCTCP) {
         if (!s->exp_ecn_k || !s->exp_cwnd0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: DCTCP needs exp_ecn_k and exp_cwnd0", e);
         ecn_k = s->exp_ecn_k[e];
         cwnd0 = s->exp_cwnd0[e];
         if (cwnd0 < 1 || cwnd0 > MSIM_MAX_CWND) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: initial window %u outside 1..%u", e, cwnd0, MSIM_MAX_CWND);
+    }
+    if (cc == MSIM_CC_DCQCN) {
+        if (!s->exp_ecn_k) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: DCQCN needs exp_ecn_k", e);
+        ecn_k = s->exp_ecn_k[e];
     }
     const uint32_t lb = s->exp_lb ? s->exp_lb[e] : MSIM_LB_ECMP;
     if (lb > MSIM_LB_SPRAY) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: unknown load balancing %u", e, lb);
@@ -822,12 +828,24 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     for (uint32_t h = 0; h < n_hosts; h++) hs[h].left = left[h];
     if (cc != MSIM_CC_NONE) {
         CcRW *cr = (CcRW *)(A + H.o_cc);
+        QcnRW *qr = (QcnRW *)(A + H.o_cc);
         for (uint32_t c = 0; c < nconn; c++) {
-            cr[c] = CcRW{};
-            cr[c].cwnd = cwnd0 << 8;
-            cr[c].alpha = 1024;
-            cr[c].lat = conn[c].lat;
-            cr[c].aword = host[host_of[conn[c].src]].rdy_off + (conn[c].lidx >> 5);
+            const uint32_t aword = host[host_of[conn[c].src]].rdy_off + (conn[c].lidx >> 5);
+            if (cc == MSIM_CC_DCTCP) {
+                cr[c] = CcRW{};
+                cr[c].cwnd = cwnd0 << 8;
+                cr[c].alpha = 1024;
+                cr[c].lat = conn[c].lat;
+                cr[c].aword = aword;
+            } else {
+                qr[c] = QcnRW{};
+                qr[c].rc = qr[c].rt = QCN_ONE;
+                qr[c].alpha = 1024;
+                qr[c].last_cnp = MSIM_NONE;
+                qr[c].next_inc = qr[c].next_alpha = QCN_PERIOD;
+                qr[c].lat = conn[c].lat;
+                qr[c].aword = aword;
+            }
         }
     }
     if (n_task) {

@@ -73,6 +73,7 @@ struct Ctx {
     TaskRW *trw;
     uint32_t cc, ecn_k, WA, n_rdy;  /* congestion control */
     CcRW *ccs;
+    QcnRW *qcs;         /* the same slots, DCQCN's view */
     uint16_t *ack;
     uint32_t *bl, *ackm;
     uint32_t sp, sbits, seed, n_hosts;   /* packet spraying */
@@ -285,6 +286,55 @@ __device__ __forceinline__ void dctcp_acks(CcRW &q, uint32_t k, uint32_t m)
     }
 }
 
+/* DCQCN (Zhu et al., SIGCOMM 2015, section 3) at the source, in integer
+ * arithmetic.  An increase event: the timer or byte-counter stage has just
+ * grown.  Below F stages in both it is fast recovery (RT kept), beyond F in
+ * both a hyper increase, else an additive one; RC then moves halfway to RT. */
+__device__ __forceinline__ void qcn_increase(QcnRW &q)
+{
+    const uint32_t hi = max(q.tcnt, q.bcnt), lo = min(q.tcnt, q.bcnt);
+    if (hi >= QCN_F) q.rt = min(q.rt + (lo > QCN_F ? (lo - QCN_F) * QCN_HAI : QCN_AI), QCN_ONE);
+    q.rc = (q.rt + q.rc) >> 1;
+}
+
+/* Applies the timer events due by tick t in time order (alpha's decay before
+ * the rate increase when both fall on one tick). */
+__device__ __forceinline__ void qcn_timers(QcnRW &q, uint32_t t)
+{
+    uint32_t ni = q.next_inc, na = q.next_alpha;
+    while (min(ni, na) <= t) {
+        const uint32_t e = min(ni, na);
+        if (na == e) { q.alpha -= q.alpha >> 8; na += QCN_PERIOD; }
+        if (ni == e) { q.tcnt++; qcn_increase(q); ni += QCN_PERIOD; }
+    }
+    q.next_inc = ni;
+    q.next_alpha = na;
+}
+
+/* A CNP reaches the source at t: the rate cut by alpha/2, alpha raised,
+ * stages and timers restarted. */
+__device__ __forceinline__ void qcn_cnp(QcnRW &q, uint32_t t)
+{
+    qcn_timers(q, t);
+    q.rt = q.rc;
+    q.rc = max(q.rc - (uint32_t)(((uint64_t)q.rc * q.alpha) >> 11), QCN_RMIN);
+    q.alpha = q.alpha - (q.alpha >> 8) + 4u;
+    q.tcnt = q.bcnt = q.bsent = 0;
+    q.next_inc = q.next_alpha = t + QCN_PERIOD;
+}
+
+/* The source sent a packet at t: timers, byte counter, and the pacer's next
+ * send time (which may lag the schedule by under one tick, so fractional gaps
+ * average out).  Returns the first tick the connection may send again. */
+__device__ __forceinline__ uint32_t qcn_sent(QcnRW &q, uint32_t t)
+{
+    qcn_timers(q, t);
+    if (++q.bsent == QCN_BYTES) { q.bsent = 0; q.bcnt++; qcn_increase(q); }
+    const uint64_t now = (uint64_t)t << 16, lag = now > 65535u ? now - 65535u : 0;
+    q.next_fp = max(q.next_fp, lag) + (1ull << 32) / q.rc;
+    return (uint32_t)((q.next_fp + 65535u) >> 16);
+}
+
 __device__ __forceinline__ void activate(const Ctx &C, Acc &a, uint32_t c, uint32_t pos, const Grp &g,
                                          const ConnRO &cr, uint32_t rdy_off, uint32_t t)
 {
@@ -292,7 +342,7 @@ __device__ __forceinline__ void activate(const Ctx &C, Acc &a, uint32_t c, uint3
     C.cs[c].s_rem = flow_size(g, cr, pos);
     /* with congestion control a closed window keeps it out of the NIC's
      * candidates until an ACK reopens it */
-    if (!C.cc || window_open(C.ccs[c])) C.ready[rdy_off + (cr.lidx >> 5)] |= 1u << (cr.lidx & 31);
+    if (C.cc != CC_DCTCP || window_open(C.ccs[c])) C.ready[rdy_off + (cr.lidx >> 5)] |= 1u << (cr.lidx & 31);
     a.last_act1 = t + 1;
     if (C.rec) C.rec[C.n_flows + flow_id(g, cr, c, pos)] = t;
 }
@@ -386,6 +436,10 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
             const uint32_t c = C.hout[hr.out_off + j];
             const uint32_t v = C.ack[c * C.WA + as];
             C.ack[c * C.WA + as] = 0;
+            if (C.cc == CC_DCQCN) {
+                qcn_cnp(C.qcs[c], t);     /* at most one: CNPs are 608 ticks apart */
+                continue;
+            }
             CcRW &q = C.ccs[c];
             dctcp_acks(q, v & 0xFFu, v >> 8);
             /* a grown window may let a waiting flow send again, and a window cut
@@ -422,14 +476,24 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
         ConnRW &cw = C.cs[c];
         a.delivered++;
         if (C.cc) {
-            /* the packet's ACK reaches the source one path latency later; the
-             * source's pending mask for that tick gets the connection's bit
-             * (other destinations may set bits of the same word) */
-            const CcRW &q = C.ccs[c];
-            const uint32_t ta = t + q.lat, as = ta & (C.WA - 1);
-            C.ack[c * C.WA + as] += 1u + ((desc >> 31) << 8);
-            atomicOr(C.ackm + as * C.n_rdy + q.aword, 1u << (C.conn[c].lidx & 31));
-            a.max_arr = max(a.max_arr, ta);
+            /* DCTCP: the packet's ACK; DCQCN: a CNP for a marked packet, at most
+             * one per connection every 608 ticks.  It reaches the source one
+             * path latency later; the source's pending mask for that tick gets
+             * the connection's bit (other destinations may set bits of the same
+             * word) */
+            bool notify = true;
+            if (C.cc == CC_DCQCN) {
+                QcnRW &q = C.qcs[c];
+                notify = (desc & DESC_MARK) && (q.last_cnp == MSIM_NONE || t - q.last_cnp >= QCN_CNP_GAP);
+                if (notify) q.last_cnp = t;
+            }
+            if (notify) {
+                const CcRW &q = C.ccs[c];
+                const uint32_t ta = t + q.lat, as = ta & (C.WA - 1);
+                C.ack[c * C.WA + as] += 1u + ((desc >> 31) << 8);
+                atomicOr(C.ackm + as * C.n_rdy + q.aword, 1u << (C.conn[c].lidx & 31));
+                a.max_arr = max(a.max_arr, ta);
+            }
         }
         for (; in_order; in_order--) {
         if (--cw.r_rem != 0) continue;
@@ -620,7 +684,14 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
             uint32_t bits = rdy[w];
             if (k == 0) bits &= ~0u << b0;
             else if (k == nw) bits &= (1u << b0) - 1u;
-            if (bits) { j = (w << 5) + __builtin_ctz(bits); break; }
+            if (C.cc == CC_DCQCN) {
+                /* DCQCN: skip connections their pacer holds back */
+                for (; bits; bits &= bits - 1) {
+                    const uint32_t jj = (w << 5) + __builtin_ctz(bits);
+                    if (((uint64_t)t << 16) >= C.qcs[C.hout[hr.out_off + jj]].next_fp) { j = jj; break; }
+                }
+                if (j != MSIM_NONE) break;
+            } else if (bits) { j = (w << 5) + __builtin_ctz(bits); break; }
         }
         if (j == MSIM_NONE) break;
         uint32_t c = C.hout[hr.out_off + j];
@@ -630,10 +701,12 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
         moved = true;
         rr = j + 1 == hr.n_out ? 0 : j + 1;
         ConnRW &cw = C.cs[c];
-        if (C.cc) {
+        if (C.cc == CC_DCTCP) {
             CcRW &q = C.ccs[c];
             q.sent++;
             if (!window_open(q)) rdy[j >> 5] &= ~(1u << (j & 31));
+        } else if (C.cc == CC_DCQCN) {
+            a.max_arr = max(a.max_arr, qcn_sent(C.qcs[c], t));
         }
         if (--cw.s_rem == 0) {
             rdy[j >> 5] &= ~(1u << (j & 31));
@@ -813,6 +886,7 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     C.ecn_k = H->ecn_k;
     C.WA = H->WA;
     C.ccs = (CcRW *)at(H->o_cc);
+    C.qcs = (QcnRW *)at(H->o_cc);
     C.ack = (uint16_t *)at(H->o_ack);
     C.bl = (uint32_t *)at(H->o_bl);
     C.ackm = (uint32_t *)at(H->o_ackm);

@@ -23,9 +23,13 @@
 #ifndef MSIM_LAYOUT_H
 #define MSIM_LAYOUT_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #define MSIM_NONE 0xFFFFFFFFu
+/* ArenaHdr.cc: the experiment's congestion control (msim.h's MSIM_CC_* values) */
+#define CC_DCTCP 1u
+#define CC_DCQCN 2u
 #define MSIM_LAUNCH_TICKS (1u << 30)   /* most ticks one kernel launch simulates */
 
 /* group kinds */
@@ -127,7 +131,7 @@ struct ConnRW {          /* 16 bytes */
 #define CC_DCTCP 1u
 #define CWND_MAX_FP (65535u << 8)
 
-struct CcRW {            /* 48 bytes */
+struct CcRW {            /* 64 bytes: DCTCP */
     uint32_t cwnd;       /* window, 1/256 packet */
     uint32_t alpha;      /* 1/1024 */
     uint32_t sent, acked;/* packets over the connection */
@@ -135,8 +139,34 @@ struct CcRW {            /* 48 bytes */
     uint32_t wa, wm;     /* ACKs and marked ACKs in the window */
     uint32_t lat;        /* sum of the path's link delays: ACK delay */
     uint32_t aword;      /* the source host's ACK-pending word holding this connection's bit */
-    uint32_t pad[3];
+    uint32_t pad[7];
 };
+
+/* DCQCN (Zhu et al., SIGCOMM 2015) per connection, in the same 64-byte slot;
+ * lat and aword where CcRW has them */
+#define QCN_ONE 65536u          /* one packet per tick */
+#define QCN_RMIN 64u
+#define QCN_PERIOD 640u         /* rate-increase and alpha timers, ticks */
+#define QCN_BYTES 2560u         /* packets between byte-counter events */
+#define QCN_F 5u                /* stages of fast recovery */
+#define QCN_AI 64u
+#define QCN_HAI 160u
+#define QCN_CNP_GAP 608u        /* ticks between a connection's CNPs */
+struct QcnRW {
+    uint32_t rc, rt;     /* current and target rate, 1/65536 packet per tick */
+    uint32_t alpha;      /* 1/1024 */
+    uint32_t tcnt, bcnt; /* timer and byte-counter stages */
+    uint32_t bsent;      /* packets sent since the last byte-counter event */
+    uint32_t last_cnp;   /* destination side: tick of the last CNP sent, or MSIM_NONE */
+    uint32_t lat, aword;
+    uint32_t next_inc, next_alpha;  /* next timer events */
+    uint32_t pad0;
+    uint64_t next_fp;    /* next send time, 1/65536 tick */
+    uint32_t pad[2];
+};
+static_assert(sizeof(CcRW) == 64 && sizeof(QcnRW) == 64, "congestion-control slots");
+static_assert(offsetof(CcRW, lat) == offsetof(QcnRW, lat) && offsetof(CcRW, aword) == offsetof(QcnRW, aword),
+              "shared fields");
 
 struct HostRW {          /* 32 bytes */
     uint32_t pcnt;       /* connections whose flow finished sending last tick */

@@ -79,6 +79,7 @@ extern "C" {
  * system; section 5 names DCTCP among the algorithms it integrates */
 #define MSIM_CC_NONE 0
 #define MSIM_CC_DCTCP 1          /* ECN marks at switches, ACKs, a DCTCP window per connection */
+#define MSIM_CC_DCQCN 2          /* ECN marks at switches, CNPs, a DCQCN rate per connection */
 #define MSIM_MAX_CWND 65535      /* packets */
 
 /* load balancing (exp_lb), Multiverse section 5: ECMP and packet spraying */
@@ -150,6 +151,25 @@ extern "C" {
  *     acknowledged in the window), cwnd = max(1 packet, cwnd - cwnd * alpha /
  *     2048) if any was marked, and the next window ends at the packets sent so
  *     far (the first window ends at 0).
+ *   With MSIM_CC_DCQCN (DCQCN, Zhu et al., SIGCOMM 2015, in integer
+ *   arithmetic; exp_cwnd0 unused, may be NULL):
+ *   - the same ECN marks (threshold exp_ecn_k[e]);
+ *   - a marked packet delivered at t sends a CNP to its connection's source,
+ *     arriving at t + L, unless the connection's previous CNP was sent less
+ *     than 608 ticks before t;
+ *   - each connection keeps a rate RC and target RT (1/65536 packet per tick,
+ *     initially 65536: the line rate is one packet per tick) and alpha (1/1024,
+ *     initially 1).  A CNP at t: RT = RC, RC = max(64, RC - RC * alpha / 2048),
+ *     alpha = alpha - alpha/256 + 4, and the stage counters and both timers
+ *     restart at t.  Every 640 ticks without a CNP alpha loses alpha/256; every
+ *     640 ticks and every 2560 packets sent an increase event raises its stage
+ *     count, then: both stages below 5, RT stays; both above 5, RT += 160 *
+ *     (min stage - 5); else RT += 64; RT <= 65536; RC = (RT + RC) / 2.  Timer
+ *     events due by t come before a CNP or send at t, alpha's before the
+ *     increase on the same tick;
+ *   - a connection sends only at ticks t with t * 65536 >= its next send time
+ *     N (initially 0); a packet sent at t sets N = max(N, t * 65536 - 65535) +
+ *     floor(2^32 / RC).
  *   An experiment with congestion control runs on the general path.
  *   Load balancing exp_lb[e] (exp_lb NULL = MSIM_LB_ECMP for all): with
  *   MSIM_LB_SPRAY a packet with sequence number s (packets its connection sent

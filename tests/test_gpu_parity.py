@@ -547,6 +547,87 @@ def test_c8_sample(simmod, oracle):
     assert_flows(s, 0, o)
 
 
+def dcqcn_batch(n, seed):
+    """Rings, broadcasts, trees and explicit flows on three fabrics with DCQCN,
+    thresholds from always-marking to never; every other experiment carries
+    long explicit flows (timer and byte-counter stages), every fourth a long
+    broadcast held back by a computation (timers due while idle)."""
+    rng = np.random.default_rng(seed)
+    topos = [I.single_switch(8), I.leaf_spine(2, 4, 2, host_rate=1, up_rate=2), I.fat_tree(4)]
+    works, exps = [], []
+    for e in range(n):
+        t = e % 3
+        nh = [8, 8, 16][t]
+        hosts = [int(h) for h in rng.permutation(nh)]
+        colls = [I.ring(I.COLL_RING_AR, 4 * 8 * I.PKT_BYTES * int(rng.integers(1, 4)), hosts[:4],
+                        int(rng.integers(1, 3)), 2 * I.PKT_BYTES),
+                 I.bcast(24 * I.PKT_BYTES, hosts[4:7], int(rng.choice([1, 4, 8])))]
+        if t == 2:
+            colls.append(I.tree(32 * I.PKT_BYTES, hosts[8:15], 2, 4 * I.PKT_BYTES))
+        tasks = []
+        if e % 4 == 1:
+            colls.append(I.bcast(int(rng.integers(200, 1500)) * I.PKT_BYTES, [hosts[0], hosts[5]], 4))
+            tasks = [I.compute(int(rng.integers(100, 1500))), I.comm(len(colls) - 1, [0])]
+        w = I.Workload(colls)
+        w.tasks = tasks
+        top = 2500 if e % 2 == 0 else 40
+        pairs = [(hosts[i], hosts[(i + 3) % nh], int(rng.integers(1, top))) for i in range(nh)]
+        w.xsrc, w.xdst, w.xpkts = (np.array([p[k] for p in pairs], np.uint32) for k in range(3))
+        works.append(w)
+        K = int(rng.choice([0, 1, 2, 4, 8, 1000]))
+        exps.append(I.Experiment(t, e, int(rng.integers(2, 17)), int(rng.integers(0, 2**32)), I.PKT_BYTES,
+                                 I.CC_DCQCN, K, 0))
+    return I.Batch(topos, works, exps, "dcqcn")
+
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_dcqcn(simmod, oracle, force_global):
+    b = dcqcn_batch(24, 29)
+    s, g = gpu_run(simmod, b, record=range(b.n_exp), force_global=force_global)
+    assert simmod.KERNEL_NAMES[s.info()["main_kernel"]] == "msim_megakernel_cc"
+    ref = oracle_all(oracle, b, flows=True)
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+        assert_flows(s, e, ref[e])
+
+
+def test_dcqcn_pinned_scenarios_gpu(simmod, oracle):
+    """The scenarios the oracle's DCQCN pins derive by hand (an always-marked
+    flow, an incast with fast recovery, a second cut with additive and hyper
+    increase, alpha decaying before a CNP), per flow on the GPU."""
+    per = lambda P, src, dst: I.Workload([I.bcast(P * I.PKT_BYTES, [src, dst], P)])
+    w1 = I.xflows([(0, 1, 538)])
+    w2 = per(2000, 0, 2)
+    w2.xsrc, w2.xdst, w2.xpkts = (np.array([v], np.uint32) for v in (1, 2, 2))
+    w3 = per(40000, 0, 2)
+    w3.xsrc, w3.xdst, w3.xpkts = (np.array([v], np.uint32) for v in (1, 2, 700))
+    w4 = I.Workload([I.bcast(400 * I.PKT_BYTES, [0, 1], 400)])
+    w4.tasks = [I.compute(5006), I.comm(0, [0])]
+    topos = [I.single_switch(2), I.single_switch(3)]
+    exps = [I.Experiment(0, 0, 16, 0, I.PKT_BYTES, I.CC_DCQCN, 0, 0),
+            I.Experiment(1, 1, 16, 0, I.PKT_BYTES, I.CC_DCQCN, 1, 0),
+            I.Experiment(1, 2, 16, 0, I.PKT_BYTES, I.CC_DCQCN, 1, 0),
+            I.Experiment(0, 3, 16, 0, I.PKT_BYTES, I.CC_DCQCN, 0, 0)]
+    b = I.Batch(topos, [w1, w2, w3, w4], exps, "dcqcn-pins")
+    s, g = gpu_run(simmod, b, record=range(b.n_exp))
+    ref = oracle_all(oracle, b, flows=True)
+    assert [ref[0]["t_end"], ref[1]["t_end"]] == [1220 + 8 * 77 + 2, 2603]
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+        assert_flows(s, e, ref[e])
+
+
+def test_c10_sample(simmod, oracle):
+    ids = [0, 101, 255]
+    b = I.make_config(10, exp_ids=ids)
+    s, g = gpu_run(simmod, b, record=[0])
+    ref = oracle_all(oracle, b, flows=False)
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+    o = oracle.run(b, 0, flows=True)
+    assert_flows(s, 0, o)
+
+
 # ---------------------------------------------------------------------------
 # Packet spraying (per-packet equal-cost choice, in-order delivery)
 # ---------------------------------------------------------------------------
