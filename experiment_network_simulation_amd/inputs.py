@@ -50,6 +50,7 @@ TASK_COLL = 2           # a collective of the workload, simulated packet by pack
 CC_NONE = 0             # congestion control of an experiment
 CC_DCTCP = 1            # ECN marking at switches, ACKs, DCTCP windows per connection
 CC_DCQCN = 2            # ECN marking at switches, CNPs, DCQCN rates per connection
+CC_HPCC = 3             # in-band telemetry at switch egresses, ACKs, HPCC windows per connection
 
 LB_ECMP = 0             # load balancing of an experiment: one route per connection
 LB_SPRAY = 1            # every packet chooses among the equal-cost egresses at every switch

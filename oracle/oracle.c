@@ -147,6 +147,25 @@
  *      connection's next send time, which the send at tick t sets to
  *      max(previous, t - 65535/65536) + 2^32 / RC in 1/65536 tick (a pacer
  *      that may lag its schedule by under one tick).
+ *  W9c HPCC (Li et al., SIGCOMM 2019), the third congestion control: every
+ *      switch egress a packet leaves through stamps it with in-band telemetry
+ *      (the tick, the egress's count of packets sent, its backlog at the start
+ *      of the tick as W9 defines it, its rate); the destination echoes it in
+ *      the packet's ACK, which reaches the source L ticks later.  Each
+ *      connection keeps a window W (1/256 packet; at most and initially
+ *      W_init = T packets, T = 2 L the base round trip, i.e. line rate times T),
+ *      a reference window Wc, a utilisation U (1/65536) and an increase stage.
+ *      ACKs are taken one by one in sequence order.  The first only records
+ *      its telemetry.  Each later one estimates, per hop with a tick between
+ *      the two samples, u = min(qlen, previous qlen) / (B T) + (packets sent
+ *      between the samples) / (B ticks between them), keeps the largest u and
+ *      its tick gap tau (at most T), and sets U = ((T - tau) U + tau u) / T.
+ *      Then: with U >= eta = 0.95 or the stage at 5, W = Wc eta / U + W_AI
+ *      (stage back to 0), else W = Wc + W_AI (stage + 1); W is kept within 1
+ *      packet .. W_init, and Wc and the stage change only on the first ACK
+ *      of a packet sent after the previous change (once per round trip).
+ *      W_AI = W_init (1 - eta) / 16.  The NIC sends only while sent - acked <
+ *      floor(W).
  *  W10 Packet spraying (Multiverse section 5 lists it beside ECMP as a load
  *      balancing algorithm).  Per experiment, ECMP (every packet of a
  *      connection on its one route, R4) or spraying: every packet chooses at
@@ -209,7 +228,11 @@
 enum { KIND_RING_AR = 1, KIND_RING_AG = 2, KIND_BCAST = 3, KIND_RING_RS = 4, KIND_TREE = 5, KIND_SENDRECV = 6 };
 enum { PRED_RECV = 0, PRED_SEND = 1, PRED_TASK = 2 };
 enum { TASK_COMPUTE = 0, TASK_INTRA = 1, TASK_COLL = 2 };
-enum { CC_NONE = 0, CC_DCTCP = 1, CC_DCQCN = 2 };
+enum { CC_NONE = 0, CC_DCTCP = 1, CC_DCQCN = 2, CC_HPCC = 3 };
+#define HP_ETA 62259u           /* 0.95 in 1/65536 */
+#define HP_MAX_STAGE 5u
+#define HP_N 16u                /* flows expected to share a link, in W_AI */
+#define HP_HOPS 8u              /* switches on a path carrying telemetry */
 #define QCN_ONE 65536u          /* one packet per tick */
 #define QCN_RMIN 64u
 #define QCN_T_INC 640u
@@ -298,6 +321,9 @@ typedef struct {
     uint32_t hop;       /* index in the connection's path of the node it reaches */
     uint32_t mark;      /* ECN mark */
     uint32_t seq;       /* packets its connection sent before it */
+    /* HPCC telemetry per switch on the path: tick, egress packets sent,
+     * egress backlog, egress rate */
+    uint32_t int_ts[HP_HOPS], int_tx[HP_HOPS], int_q[HP_HOPS], int_b[HP_HOPS];
 } Pkt;
 
 typedef struct {       /* FIFO of packets (ring buffer of fixed capacity) */
@@ -316,6 +342,8 @@ typedef struct {
     uint32_t occ;        /* switch ingress: packets sent into it, not yet forwarded */
     int64_t credit;      /* phase C snapshot, consumed during phase D */
     uint32_t granted;    /* phase D decision of the current round (input index or NONE) */
+    uint32_t tx;         /* packets sent through this port so far */
+    uint32_t bl;         /* switch egress: backlog at the start of the tick (HPCC) */
     Fifo *voq;           /* switch ingress: one FIFO per egress port of the node */
     Fifo wire;           /* host ingress: packets on the way to the host */
 } Port;
@@ -352,6 +380,11 @@ typedef struct {
     /* DCQCN: rate, target, stage counters, timers, CNP rate limit, pacing */
     uint32_t rc, rt, tcnt, bcnt, bsent, next_inc, next_alpha, last_cnp;
     uint64_t next_fp;           /* next send time, 1/65536 tick */
+    /* HPCC: base round trip, windows, utilisation, stage, the packets sent
+     * when Wc last changed, additive step, telemetry of the last ACK */
+    uint32_t hT, hw, hwc, hU, hstage, hlast, hwai, hhave, nsw;
+    uint32_t L_ts[HP_HOPS], L_tx[HP_HOPS], L_q[HP_HOPS];
+    uint32_t *ackint;           /* telemetry riding each ACK in ackq: 4 x HP_HOPS words */
     /* packet spraying: arrival flags by sequence number, in-order point */
     uint8_t *got;
     uint32_t pkts, rnext;
@@ -432,7 +465,7 @@ static void exp_free(Exp *x)
     free(x->port_off); free(x->port); free(x->flow); free(x->conn_flows);
     free(x->path_node); free(x->path_port); free(x->host_conn_off); free(x->host_conn);
     free(x->task); free(x->task_pred); free(x->flow_task);
-    if (x->conn) for (uint32_t c = 0; c < x->n_conn; c++) { free(x->conn[c].ackq); free(x->conn[c].got); }
+    if (x->conn) for (uint32_t c = 0; c < x->n_conn; c++) { free(x->conn[c].ackq); free(x->conn[c].ackint); free(x->conn[c].got); }
     free(x->dist_down); free(x->dist_any);
     free(x->conn);
     memset(x, 0, sizeof(*x));
@@ -981,13 +1014,24 @@ static uint32_t out_port(const Exp *x, const Conn *c, uint32_t h)
 
 /* Sends packet (flow f, currently at path position hop, ECN mark) out of port
  * op at tick t. */
-static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t mark, uint32_t seq, uint32_t t,
-                    uint64_t *hops, uint32_t *max_arrive, uint32_t *max_occ)
+static int transmit(Exp *x, uint32_t op, const Pkt *from, uint32_t f, uint32_t hop, uint32_t mark, uint32_t seq,
+                    uint32_t t, uint64_t *hops, uint32_t *max_arrive, uint32_t *max_occ)
 {
     Port *o = &x->port[op];
     Port *in = &x->port[o->peer_port];
     const Conn *c = &x->conn[x->flow[f].conn];
     Pkt p;
+    if (from) p = *from;
+    else memset(&p, 0, sizeof p);
+    o->tx++;
+    if (x->cc == CC_HPCC && hop > 0) {
+        /* W9c: the switch at path position hop stamps its egress */
+        if (hop > HP_HOPS) return ORC_E_INVARIANT;
+        p.int_ts[hop - 1] = t;
+        p.int_tx[hop - 1] = o->tx;
+        p.int_q[hop - 1] = o->bl;
+        p.int_b[hop - 1] = o->rate;
+    }
     p.flow = f;
     p.arrive = t + o->delay;
     p.hop = hop + 1;
@@ -1011,6 +1055,20 @@ static int transmit(Exp *x, uint32_t op, uint32_t f, uint32_t hop, uint32_t mark
     return fifo_push(&in->voq[egress], p) ? ORC_E_NOMEM : ORC_OK;
 }
 
+/* W9: packets for egress o of switch n that arrived before tick t and are
+ * still queued: the egress's backlog at the start of t. */
+static uint32_t egress_backlog(const Exp *x, uint32_t n, uint32_t o, uint32_t t)
+{
+    const uint32_t deg = x->port_off[n + 1] - x->port_off[n];
+    uint32_t backlog = 0;
+    for (uint32_t i = 0; i < deg; i++) {
+        const Fifo *q = &x->port[x->port_off[n] + i].voq[o];
+        for (uint32_t j = 0; j < q->count; j++)
+            if (q->buf[(q->head + j) % q->cap].arrive < t) backlog++;
+    }
+    return backlog;
+}
+
 /* W9 ECN: marks the packets that reach switch ingresses at tick t, against
  * each egress's backlog as it stood before any of them arrived. */
 static void ecn_mark(Exp *x, uint32_t t)
@@ -1019,13 +1077,7 @@ static void ecn_mark(Exp *x, uint32_t t)
         if (x->layer[n] == 0) continue;
         uint32_t deg = x->port_off[n + 1] - x->port_off[n];
         for (uint32_t o = 0; o < deg; o++) {
-            uint32_t backlog = 0;
-            for (uint32_t i = 0; i < deg; i++) {
-                Fifo *q = &x->port[x->port_off[n] + i].voq[o];
-                for (uint32_t j = 0; j < q->count; j++)
-                    if (q->buf[(q->head + j) % q->cap].arrive < t) backlog++;
-            }
-            if (backlog < x->ecn_k) continue;
+            if (egress_backlog(x, n, o, t) < x->ecn_k) continue;
             for (uint32_t i = 0; i < deg; i++) {
                 Fifo *q = &x->port[x->port_off[n] + i].voq[o];
                 for (uint32_t j = 0; j < q->count; j++) {
@@ -1058,6 +1110,61 @@ static void dctcp_acks(Exp *x, Conn *c, uint32_t k, uint32_t m)
         c->wend = c->sent;
         c->wa = c->wm = 0;
     }
+}
+
+/* W9c HPCC: the utilisation estimate from one ACK's telemetry against the
+ * previous ACK's (the largest over the hops), folded into U. */
+static void hpcc_measure(Conn *c, const uint32_t *ts, const uint32_t *tx, const uint32_t *q, const uint32_t *b)
+{
+    const uint64_t T = c->hT;
+    uint64_t u = 0;
+    uint32_t tau = 0;
+    for (uint32_t i = 0; i < c->nsw; i++) {
+        const uint32_t dts = ts[i] - c->L_ts[i];
+        if (dts == 0) continue;                /* no time between the samples */
+        const uint64_t mq = q[i] < c->L_q[i] ? q[i] : c->L_q[i];
+        const uint64_t up = (65536ull * (mq * dts + (uint64_t)(tx[i] - c->L_tx[i]) * T)) / ((uint64_t)b[i] * T * dts);
+        if (up > u) { u = up; tau = dts; }
+    }
+    if (tau > T) tau = (uint32_t)T;
+    c->hU = (uint32_t)(((T - tau) * c->hU + tau * u) / T);
+}
+
+/* W9c HPCC: the new window from U; the reference window and stage move when
+ * `update` (once per round trip). */
+static void hpcc_window(Conn *c, int update)
+{
+    const uint64_t cap = (uint64_t)c->hT << 8;
+    const int mult = c->hU >= HP_ETA || c->hstage >= HP_MAX_STAGE;
+    uint64_t w;
+    if (mult) w = (c->hU ? (uint64_t)c->hwc * HP_ETA / c->hU : cap) + c->hwai;
+    else w = (uint64_t)c->hwc + c->hwai;
+    if (w > cap) w = cap;
+    if (w < 256) w = 256;
+    c->hw = (uint32_t)w;
+    if (update) {
+        c->hstage = mult ? 0 : c->hstage + 1;
+        c->hwc = c->hw;
+    }
+}
+
+/* W9c HPCC: one ACK, carrying the telemetry of the packet it acknowledges,
+ * reaches connection c's source (after acked was counted up for it). */
+static void hpcc_ack(Conn *c, const uint32_t *in)
+{
+    const uint32_t *ts = in, *tx = in + HP_HOPS, *q = in + 2 * HP_HOPS, *b = in + 3 * HP_HOPS;
+    if (c->hhave) {
+        const int update = c->acked > c->hlast;
+        hpcc_measure(c, ts, tx, q, b);
+        hpcc_window(c, update);
+        if (update) c->hlast = c->sent;
+    } else {
+        c->hhave = 1;
+        c->hlast = c->sent;
+    }
+    memcpy(c->L_ts, ts, sizeof c->L_ts);
+    memcpy(c->L_tx, tx, sizeof c->L_tx);
+    memcpy(c->L_q, q, sizeof c->L_q);
 }
 
 /* W9b: a rate-increase event (timer or byte counter). */
@@ -1143,19 +1250,33 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
             c->aq_cap = c->lat * x->R + 1;
             c->ackq = (uint32_t *)malloc(sizeof(uint32_t) * c->aq_cap);
             if (!c->ackq) return ORC_E_NOMEM;
+            if (x->cc == CC_HPCC) {
+                c->ackint = (uint32_t *)malloc(sizeof(uint32_t) * 4 * HP_HOPS * c->aq_cap);
+                if (!c->ackint) return ORC_E_NOMEM;
+                c->hT = 2 * c->lat;
+                c->hw = c->hwc = c->hT << 8;
+                c->hwai = (uint32_t)(((uint64_t)c->hT * 256u * (65536u - HP_ETA)) / (65536ull * HP_N));
+                if (c->hwai == 0) c->hwai = 1;
+                c->nsw = c->path_len - 2;
+                if (c->nsw > HP_HOPS) return ORC_E_INVALID;
+            }
         }
     }
     for (uint32_t t = 0; t < max_ticks; t++) {
         int busy = 0;
         /* A: ECN marks at switch arrivals, then ACKs reaching their sources */
         if (x->cc) {
-            ecn_mark(x, t);
+            if (x->cc != CC_HPCC) ecn_mark(x, t);
             for (uint32_t ci = 0; ci < x->n_conn; ci++) {
                 Conn *c = &x->conn[ci];
                 uint32_t k = 0, m = 0;
                 while (c->aq_n && (c->ackq[c->aq_head] >> 1) == t) {
                     m += c->ackq[c->aq_head] & 1u;
                     k++;
+                    if (x->cc == CC_HPCC) {
+                        c->acked++;
+                        hpcc_ack(c, c->ackint + 4 * HP_HOPS * c->aq_head);
+                    }
                     c->aq_head = (c->aq_head + 1) % c->aq_cap;
                     c->aq_n--;
                 }
@@ -1182,14 +1303,22 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     if (x->lb == LB_ECMP && x->conn_flows[c->flow_off + c->recv_pos] != k.flow) return ORC_E_INVARIANT;
                 }
                 delivered++;
-                const int notify = x->cc == CC_DCTCP ||
+                const int notify = x->cc == CC_DCTCP || x->cc == CC_HPCC ||
                     (x->cc == CC_DCQCN && k.mark && (c->last_cnp == NONE || t - c->last_cnp >= QCN_CNP_GAP));
                 if (notify) {
                     /* DCTCP: this packet's ACK; DCQCN: a CNP.  It reaches the
                      * source L ticks later */
                     if (x->cc == CC_DCQCN) c->last_cnp = t;
                     if (c->aq_n == c->aq_cap) return ORC_E_INVARIANT;
-                    c->ackq[(c->aq_head + c->aq_n) % c->aq_cap] = ((t + c->lat) << 1) | k.mark;
+                    const uint32_t slot = (c->aq_head + c->aq_n) % c->aq_cap;
+                    c->ackq[slot] = ((t + c->lat) << 1) | k.mark;
+                    if (x->cc == CC_HPCC) {
+                        uint32_t *d = c->ackint + 4 * HP_HOPS * slot;
+                        memcpy(d, k.int_ts, sizeof k.int_ts);
+                        memcpy(d + HP_HOPS, k.int_tx, sizeof k.int_tx);
+                        memcpy(d + 2 * HP_HOPS, k.int_q, sizeof k.int_q);
+                        memcpy(d + 3 * HP_HOPS, k.int_b, sizeof k.int_b);
+                    }
                     c->aq_n++;
                     if (t + c->lat > max_arrive) max_arrive = t + c->lat;
                 }
@@ -1266,6 +1395,13 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
             if (x->layer[pp->peer_node] == 0) pp->credit = INT64_MAX;
             else pp->credit = (int64_t)x->Q - (int64_t)x->port[pp->peer_port].occ;
         }
+        /* W9c: every switch egress's backlog at the start of the tick, for telemetry */
+        if (x->cc == CC_HPCC)
+            for (uint32_t n = 0; n < x->n_nodes; n++) {
+                if (x->layer[n] == 0) continue;
+                for (uint32_t o = 0; o < x->port_off[n + 1] - x->port_off[n]; o++)
+                    x->port[x->port_off[n] + o].bl = egress_backlog(x, n, o, t);
+            }
         /* D: rounds of grants; decide on the state at the start of the round, then apply */
         for (uint32_t m = 0; m < x->R; m++) {
             for (uint32_t p = 0; p < x->n_ports; p++) {
@@ -1282,6 +1418,7 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                         if (c->cur >= c->nflow) continue;
                         Flow *fl = &x->flow[x->conn_flows[c->flow_off + c->cur]];
                         if (x->cc == CC_DCTCP && c->sent - c->acked >= (c->cwnd >> 8)) continue;   /* window full */
+                        if (x->cc == CC_HPCC && c->sent - c->acked >= (c->hw >> 8)) continue;      /* window full */
                         if (x->cc == CC_DCQCN && ((uint64_t)t << 16) < c->next_fp) continue;        /* paced */
                         if (fl->active && fl->sent < fl->size) { pp->granted = idx; break; }
                     }
@@ -1306,7 +1443,7 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     uint32_t f = x->conn_flows[c->flow_off + c->cur];
                     Flow *fl = &x->flow[f];
                     if (out_port(x, c, 0) != p) return ORC_E_INVARIANT;
-                    rc = transmit(x, p, f, 0, 0, c->sent, t, &hops, &max_arrive, &max_occ);
+                    rc = transmit(x, p, NULL, f, 0, 0, c->sent, t, &hops, &max_arrive, &max_occ);
                     if (rc) return rc;
                     fl->sent++;
                     c->sent++;
@@ -1324,7 +1461,7 @@ static int simulate(Exp *x, uint32_t max_ticks, orc_result *res, const orc_opts 
                     in->occ--;
                     const Conn *c = &x->conn[x->flow[k.flow].conn];
                     if (opt->check && x->lb == LB_ECMP && out_port(x, c, k.hop) != p) return ORC_E_INVARIANT;
-                    rc = transmit(x, p, k.flow, k.hop, k.mark, k.seq, t, &hops, &max_arrive, &max_occ);
+                    rc = transmit(x, p, &k, k.flow, k.hop, k.mark, k.seq, t, &hops, &max_arrive, &max_occ);
                     if (rc) return rc;
                     pp->rr = (pp->granted + 1) % deg;
                 }
@@ -1378,7 +1515,7 @@ int orc_run(const orc_batch *b, uint32_t e, uint32_t max_ticks, uint32_t check, 
     x.seed = b->exp_ecmp_seed[e];
     if (x.Q < 1) return ORC_E_INVALID;
     x.cc = b->exp_cc ? b->exp_cc[e] : CC_NONE;
-    if (x.cc > CC_DCQCN) return ORC_E_INVALID;
+    if (x.cc > CC_HPCC) return ORC_E_INVALID;
     x.lb = b->exp_lb ? b->exp_lb[e] : LB_ECMP;
     /* sprayed packets of one connection see different path latencies, which
      * the ACK timing of W9 does not describe */
@@ -1456,6 +1593,38 @@ int orc_flows(const orc_batch *b, uint32_t e, uint32_t *flow_conn, uint32_t *flo
 }
 
 uint32_t orc_fmix32(uint32_t h) { return fmix32(h); }
+
+/* W9c's per-connection window machine on its own, for pins: a fresh
+ * connection with base round trip T and nsw switches on its path receives n
+ * ACKs in order; ACK i comes when the source has sent sent[i] packets and
+ * carries telemetry tel[4 nsw i ..] (ticks, packets sent, backlogs, rates,
+ * nsw each).  After each, state[4 i ..] = U, W, Wc and the stage. */
+int orc_hpcc_script(uint32_t T, uint32_t nsw, uint32_t n, const uint32_t *sent, const uint32_t *tel, uint32_t *state)
+{
+    if (T == 0 || nsw == 0 || nsw > HP_HOPS) return ORC_E_INVALID;
+    Conn c;
+    memset(&c, 0, sizeof c);
+    c.hT = T;
+    c.hw = c.hwc = T << 8;
+    c.hwai = (uint32_t)(((uint64_t)T * 256u * (65536u - HP_ETA)) / (65536ull * HP_N));
+    if (c.hwai == 0) c.hwai = 1;
+    c.nsw = nsw;
+    for (uint32_t i = 0; i < n; i++) {
+        uint32_t in[4 * HP_HOPS] = {0};
+        for (uint32_t k = 0; k < 4; k++)
+            for (uint32_t h = 0; h < nsw; h++) in[k * HP_HOPS + h] = tel[4 * nsw * i + k * nsw + h];
+        for (uint32_t h = 0; h < nsw; h++) if (in[3 * HP_HOPS + h] == 0) return ORC_E_INVALID;
+        if (sent[i] < c.acked + 1) return ORC_E_INVALID;
+        c.sent = sent[i];
+        c.acked++;
+        hpcc_ack(&c, in);
+        state[4 * i] = c.hU;
+        state[4 * i + 1] = c.hw;
+        state[4 * i + 2] = c.hwc;
+        state[4 * i + 3] = c.hstage;
+    }
+    return ORC_OK;
+}
 
 /* W9b's per-connection rate machine on its own, for pins: a fresh
  * connection receives n events in tick order, what[i] = 0 a CNP and 1 a

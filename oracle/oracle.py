@@ -82,6 +82,8 @@ def _load():
             lib.orc_flows.restype = C.c_int
             lib.orc_qcn_script.argtypes = [C.c_uint32, _P32, C.POINTER(C.c_uint8), _P32]
             lib.orc_qcn_script.restype = C.c_int
+            lib.orc_hpcc_script.argtypes = [C.c_uint32, C.c_uint32, C.c_uint32, _P32, _P32, _P32]
+            lib.orc_hpcc_script.restype = C.c_int
             lib.orc_fmix32.argtypes = [C.c_uint32]
             lib.orc_fmix32.restype = C.c_uint32
             lib.orc_mix64.argtypes = [C.c_uint64]
@@ -211,6 +213,26 @@ def qcn_script(events):
                                 state.ctypes.data_as(_P32))
     if rc != 0:
         raise ValueError(f"orc_qcn_script: {rc}")
+    return [tuple(int(v) for v in state[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def hpcc_script(T, acks):
+    """acks: (sent, [(tick, packets sent, backlog, rate) per switch]) in order,
+    applied to one fresh HPCC connection with base round trip T.  Returns one
+    (U, W, Wc, stage) per ACK."""
+    n = len(acks)
+    nsw = len(acks[0][1]) if n else 1
+    sent = np.array([a[0] for a in acks], np.uint32)
+    rows = []
+    for _, hops in acks:
+        assert len(hops) == nsw
+        rows.extend([h[k] for k in range(4) for h in hops])
+    tel = np.array(rows, np.uint32)
+    state = np.zeros(4 * max(n, 1), np.uint32)
+    rc = _load().orc_hpcc_script(T, nsw, n, sent.ctypes.data_as(_P32), tel.ctypes.data_as(_P32),
+                                 state.ctypes.data_as(_P32))
+    if rc != 0:
+        raise ValueError(f"orc_hpcc_script: {rc}")
     return [tuple(int(v) for v in state[4 * i:4 * i + 4]) for i in range(n)]
 
 

@@ -204,7 +204,7 @@ def test_congestion_control_compile_and_validation(simmod, oracle):
     assert simmod.Sim(b).info()["n_compact"] == 2
     topo = I.single_switch(2)
     w = I.xflows([(0, 1, 3)])
-    for cc, k, w0 in ((I.CC_DCTCP, 1, 0), (I.CC_DCTCP, 1, 65536), (3, 1, 1)):
+    for cc, k, w0 in ((I.CC_DCTCP, 1, 0), (I.CC_DCTCP, 1, 65536), (4, 1, 1)):
         bb = I.single_batch(topo, w, cc=cc, ecn_k=k, cwnd0=w0)
         expect_error(simmod, bb, simmod.E_INVALID_SPEC)
         assert oracle.run(bb, 0)["rc"] == oracle.E_INVALID

@@ -109,5 +109,5 @@ def test_conservation_and_bounds_under_control(oracle):
 def test_cc_validation(oracle):
     topo = I.single_switch(2)
     w = I.xflows([(0, 1, 3)])
-    for cc, k, w0 in ((I.CC_DCTCP, 1, 0), (I.CC_DCTCP, 1, 65536), (3, 1, 1)):
+    for cc, k, w0 in ((I.CC_DCTCP, 1, 0), (I.CC_DCTCP, 1, 65536), (4, 1, 1)):
         assert oracle.run(I.single_batch(topo, w, cc=cc, ecn_k=k, cwnd0=w0), 0)["rc"] == oracle.E_INVALID
