@@ -27,7 +27,7 @@
 #include "msim.h"
 #include "msim_layout.h"
 
-static_assert(CC_DCTCP == MSIM_CC_DCTCP && CC_DCQCN == MSIM_CC_DCQCN, "congestion-control codes");
+static_assert(CC_DCTCP == MSIM_CC_DCTCP && CC_DCQCN == MSIM_CC_DCQCN && CC_HPCC == MSIM_CC_HPCC, "congestion-control codes");
 
 extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t kind, uint32_t grid, uint32_t block,
                                       uint32_t lds, bool prepare, hipStream_t stream);
@@ -147,7 +147,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     if (pkt == 0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: zero packet size", e);
     const uint32_t cc = s->exp_cc ? s->exp_cc[e] : MSIM_CC_NONE;
     uint32_t ecn_k = 0, cwnd0 = 0;
-    if (cc > MSIM_CC_DCQCN) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: unknown congestion control %u", e, cc);
+    if (cc > MSIM_CC_HPCC) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: unknown congestion control %u", e, cc);
     if (cc == MSIM_CC_DCTCP) {
         if (!s->exp_ecn_k || !s->exp_cwnd0) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: DCTCP needs exp_ecn_k and exp_cwnd0", e);
         ecn_k = s->exp_ecn_k[e];
@@ -158,6 +158,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
         if (!s->exp_ecn_k) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: DCQCN needs exp_ecn_k", e);
         ecn_k = s->exp_ecn_k[e];
     }
+    if (cc == MSIM_CC_HPCC) ecn_k = 0xFFFFFFFFu;     /* telemetry, no ECN marks */
     const uint32_t lb = s->exp_lb ? s->exp_lb[e] : MSIM_LB_ECMP;
     if (lb > MSIM_LB_SPRAY) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: unknown load balancing %u", e, lb);
     if (lb == MSIM_LB_SPRAY && cc != MSIM_CC_NONE)
@@ -768,6 +769,23 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     H.ecn_k = ecn_k;
     H.WA = 1;
     H.n_rdy = words;
+    /* HPCC: telemetry records of up to hx switches, one per packet in flight
+     * (the window never exceeds T = 2 L packets), found from the descriptor */
+    H.cshift = DESC_SHIFT;
+    uint64_t int_records = 0;
+    if (cc == MSIM_CC_HPCC) {
+        uint32_t smax = 1;
+        for (const Conn &cn : conn) {
+            H.hx = std::max(H.hx, cn.links - 1);
+            smax = std::max(smax, 2 * cn.lat);
+            int_records += 2ull * cn.lat;
+        }
+        uint32_t sb = 0;
+        while ((1u << sb) < smax) sb++;
+        H.cshift = 4 + sb;
+        if (H.cshift >= 31 || (uint64_t)nconn > (1ull << (31 - H.cshift)))
+            return fail(out, MSIM_E_LIMIT, "experiment %u: too many connections for HPCC descriptors", e);
+    }
     if (cc != MSIM_CC_NONE) {
         uint32_t max_lat = 0;
         for (const Conn &cn : conn) max_lat = std::max(max_lat, cn.lat);
@@ -785,6 +803,10 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     if (cc != MSIM_CC_NONE) {
         take(H.o_cc, sizeof(CcRW) * nconn);
         take(H.o_ack, 2ull * nconn * H.WA);
+    }
+    if (cc == MSIM_CC_HPCC) {
+        take(H.o_hl, 12ull * H.hx * nconn);
+        take(H.o_int, 12ull * H.hx * int_records);
     }
     if (lb == MSIM_LB_SPRAY) {
         take(H.o_sseq, 4ull * nconn);
@@ -829,6 +851,8 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     if (cc != MSIM_CC_NONE) {
         CcRW *cr = (CcRW *)(A + H.o_cc);
         QcnRW *qr = (QcnRW *)(A + H.o_cc);
+        HpRW *hr = (HpRW *)(A + H.o_cc);
+        uint32_t int_off = 0;
         for (uint32_t c = 0; c < nconn; c++) {
             const uint32_t aword = host[host_of[conn[c].src]].rdy_off + (conn[c].lidx >> 5);
             if (cc == MSIM_CC_DCTCP) {
@@ -837,6 +861,16 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                 cr[c].alpha = 1024;
                 cr[c].lat = conn[c].lat;
                 cr[c].aword = aword;
+            } else if (cc == MSIM_CC_HPCC) {
+                hr[c] = HpRW{};
+                hr[c].T = hr[c].slots = 2 * conn[c].lat;
+                hr[c].w = hr[c].wc = hr[c].T << 8;
+                hr[c].wai = std::max(1u, (uint32_t)((uint64_t)hr[c].T * 256u * (65536u - HP_ETA) / (65536ull * HP_N)));
+                hr[c].lat = conn[c].lat;
+                hr[c].aword = aword;
+                hr[c].nsw = conn[c].links - 1;
+                hr[c].int_off = int_off;
+                int_off += hr[c].slots;
             } else {
                 qr[c] = QcnRW{};
                 qr[c].rc = qr[c].rt = QCN_ONE;

@@ -74,6 +74,9 @@ struct Ctx {
     uint32_t cc, ecn_k, WA, n_rdy;  /* congestion control */
     CcRW *ccs;
     QcnRW *qcs;         /* the same slots, DCQCN's view */
+    HpRW *hps;          /* and HPCC's */
+    uint32_t cshift, hx;/* descriptor: conn << cshift; HPCC: switches per telemetry record */
+    uint32_t *hl, *hint;/* HPCC: last ACK's telemetry, telemetry records */
     uint16_t *ack;
     uint32_t *bl, *ackm;
     uint32_t sp, sbits, seed, n_hosts;   /* packet spraying */
@@ -335,6 +338,52 @@ __device__ __forceinline__ uint32_t qcn_sent(QcnRW &q, uint32_t t)
     return (uint32_t)((q.next_fp + 65535u) >> 16);
 }
 
+/* HPCC (Li et al., SIGCOMM 2019, Algorithm 1) at the source, in integer
+ * arithmetic: may the connection put another packet in flight? */
+__device__ __forceinline__ bool hp_open(const HpRW &h)
+{
+    return h.sent - h.acked < (h.w >> 8);
+}
+
+/* One ACK (acked already counted up for it) with the telemetry `rec` of the
+ * packet it acknowledges, 3 words per switch; L holds the previous ACK's.
+ * The utilisation sample of each switch with time between its two records,
+ * the largest one folded into U, then the window; Wc and the stage move once
+ * per round trip. */
+__device__ __forceinline__ void hpcc_ack(HpRW &h, uint32_t *L, const uint32_t *rec)
+{
+    if (h.have) {
+        const bool update = h.acked > h.hlast;
+        const uint64_t T = h.T;
+        uint64_t u = 0;
+        uint32_t tau = 0;
+        for (uint32_t i = 0; i < h.nsw; i++) {
+            const uint32_t dts = rec[3 * i] - L[3 * i];
+            if (dts == 0) continue;
+            const uint32_t qb = rec[3 * i + 2];
+            const uint64_t mq = min(qb & 0xFFFFFFu, L[3 * i + 2] & 0xFFFFFFu);
+            const uint64_t up = (65536ull * (mq * dts + (uint64_t)(rec[3 * i + 1] - L[3 * i + 1]) * T)) /
+                                ((uint64_t)(qb >> 24) * T * dts);
+            if (up > u) { u = up; tau = dts; }
+        }
+        tau = (uint32_t)min((uint64_t)tau, T);
+        h.U = (uint32_t)(((T - tau) * h.U + tau * u) / T);
+        const uint64_t cap = T << 8;
+        const bool mult = h.U >= HP_ETA || h.stage >= HP_MAX_STAGE;
+        uint64_t w = mult ? (h.U ? (uint64_t)h.wc * HP_ETA / h.U : cap) + h.wai : (uint64_t)h.wc + h.wai;
+        h.w = (uint32_t)max(min(w, cap), (uint64_t)256);
+        if (update) {
+            h.stage = mult ? 0 : h.stage + 1;
+            h.wc = h.w;
+            h.hlast = h.sent;
+        }
+    } else {
+        h.have = 1;
+        h.hlast = h.sent;
+    }
+    for (uint32_t i = 0; i < 3 * h.nsw; i++) L[i] = rec[i];
+}
+
 __device__ __forceinline__ void activate(const Ctx &C, Acc &a, uint32_t c, uint32_t pos, const Grp &g,
                                          const ConnRO &cr, uint32_t rdy_off, uint32_t t)
 {
@@ -342,7 +391,8 @@ __device__ __forceinline__ void activate(const Ctx &C, Acc &a, uint32_t c, uint3
     C.cs[c].s_rem = flow_size(g, cr, pos);
     /* with congestion control a closed window keeps it out of the NIC's
      * candidates until an ACK reopens it */
-    if (C.cc != CC_DCTCP || window_open(C.ccs[c])) C.ready[rdy_off + (cr.lidx >> 5)] |= 1u << (cr.lidx & 31);
+    const bool open = C.cc == CC_DCTCP ? window_open(C.ccs[c]) : C.cc == CC_HPCC ? hp_open(C.hps[c]) : true;
+    if (open) C.ready[rdy_off + (cr.lidx >> 5)] |= 1u << (cr.lidx & 31);
     a.last_act1 = t + 1;
     if (C.rec) C.rec[C.n_flows + flow_id(g, cr, c, pos)] = t;
 }
@@ -440,12 +490,26 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
                 qcn_cnp(C.qcs[c], t);     /* at most one: CNPs are 608 ticks apart */
                 continue;
             }
-            CcRW &q = C.ccs[c];
-            dctcp_acks(q, v & 0xFFu, v >> 8);
+            bool open;
+            if (C.cc == CC_HPCC) {
+                /* ACKs one by one, in sequence order, each with its packet's
+                 * telemetry record */
+                HpRW &h = C.hps[c];
+                uint32_t *L = C.hl + 3 * C.hx * c;
+                for (uint32_t i = v & 0xFFu; i; i--) {
+                    const uint32_t seq = h.acked++;
+                    hpcc_ack(h, L, C.hint + 3 * C.hx * (h.int_off + seq % h.slots));
+                }
+                open = hp_open(h);
+            } else {
+                CcRW &q = C.ccs[c];
+                dctcp_acks(q, v & 0xFFu, v >> 8);
+                open = window_open(q);
+            }
             /* a grown window may let a waiting flow send again, and a window cut
              * below the packets in flight stops it */
             const uint32_t bit = 1u << (j & 31);
-            if ((C.cs[c].s_pos >> CS_SHIFT) == CS_ACTIVE && C.cs[c].s_rem && window_open(q))
+            if ((C.cs[c].s_pos >> CS_SHIFT) == CS_ACTIVE && C.cs[c].s_rem && open)
                 C.ready[hr.rdy_off + (j >> 5)] |= bit;
             else
                 C.ready[hr.rdy_off + (j >> 5)] &= ~bit;
@@ -471,7 +535,7 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
             while (r < lim && ((bits[r >> 5] >> (r & 31)) & 1u)) { r++; in_order++; }
             C.rnext[c] = r;
         } else {
-            c = (desc & ~DESC_MARK) >> DESC_SHIFT;
+            c = (desc & ~DESC_MARK) >> C.cshift;
         }
         ConnRW &cw = C.cs[c];
         a.delivered++;
@@ -626,7 +690,7 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
             const uint32_t mask = C.cand[((size_t)row * C.n_hosts + C.conn[c].route) * 2u + (info >> 31)];
             o = spray_pick(mask, c, desc & ((1u << C.sbits) - 1u), info & 0xFFFFu, C.seed);
         } else {
-            c = (desc & ~DESC_MARK) >> DESC_SHIFT;
+            c = (desc & ~DESC_MARK) >> C.cshift;
             o = (C.conn[c].route >> (4 * (desc & DESC_HOP_MASK))) & 0xFu;
         }
         if (ftop == 0 || o >= deg) { a.fault = 1; continue; }   /* cannot happen while credits hold */
@@ -695,7 +759,10 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
         }
         if (j == MSIM_NONE) break;
         uint32_t c = C.hout[hr.out_off + j];
-        transmit(C, a, p, pr, C.sp ? (c << C.sbits) | C.sseq[c]++ : c << DESC_SHIFT, t);
+        uint32_t desc = c << C.cshift;
+        if (C.sp) desc = (c << C.sbits) | C.sseq[c]++;
+        else if (C.cc == CC_HPCC) desc |= (C.hps[c].sent % C.hps[c].slots) << 4;   /* its telemetry record */
+        transmit(C, a, p, pr, desc, t);
         pushed++;
         credit--;
         moved = true;
@@ -707,6 +774,10 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
             if (!window_open(q)) rdy[j >> 5] &= ~(1u << (j & 31));
         } else if (C.cc == CC_DCQCN) {
             a.max_arr = max(a.max_arr, qcn_sent(C.qcs[c], t));
+        } else if (C.cc == CC_HPCC) {
+            HpRW &h = C.hps[c];
+            h.sent++;
+            if (!hp_open(h)) rdy[j >> 5] &= ~(1u << (j & 31));
         }
         if (--cw.s_rem == 0) {
             rdy[j >> 5] &= ~(1u << (j & 31));
@@ -751,6 +822,16 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
         C.phead[vp] = h;
         C.head[pr.vbase + j * deg + lo] = h;
         rr = j + 1 == deg ? 0 : j + 1;
+        if (C.cc == CC_HPCC) {
+            /* telemetry of this switch (the descriptor counts the switches
+             * reached): tick, egress packets sent, backlog at the tick's
+             * start | rate << 24 */
+            const uint32_t c = desc >> C.cshift, slot = (desc >> 4) & ((1u << (C.cshift - 4)) - 1u);
+            uint32_t *r = C.hint + 3 * (C.hx * (C.hps[c].int_off + slot) + (desc & DESC_HOP_MASK) - 1);
+            r[0] = t;
+            r[1] = pushed + 1;
+            r[2] = C.bl[p] | (pr.rate << 24);
+        }
         transmit(C, a, p, pr, desc, t);
         pushed++;
         credit--;
@@ -887,6 +968,11 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     C.WA = H->WA;
     C.ccs = (CcRW *)at(H->o_cc);
     C.qcs = (QcnRW *)at(H->o_cc);
+    C.hps = (HpRW *)at(H->o_cc);
+    C.cshift = CC ? H->cshift : (uint32_t)DESC_SHIFT;
+    C.hx = H->hx;
+    C.hl = (uint32_t *)at(H->o_hl);
+    C.hint = (uint32_t *)at(H->o_int);
     C.ack = (uint16_t *)at(H->o_ack);
     C.bl = (uint32_t *)at(H->o_bl);
     C.ackm = (uint32_t *)at(H->o_ackm);

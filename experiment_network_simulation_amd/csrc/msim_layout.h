@@ -30,6 +30,7 @@
 /* ArenaHdr.cc: the experiment's congestion control (msim.h's MSIM_CC_* values) */
 #define CC_DCTCP 1u
 #define CC_DCQCN 2u
+#define CC_HPCC 3u
 #define MSIM_LAUNCH_TICKS (1u << 30)   /* most ticks one kernel launch simulates */
 
 /* group kinds */
@@ -164,7 +165,34 @@ struct QcnRW {
     uint64_t next_fp;    /* next send time, 1/65536 tick */
     uint32_t pad[2];
 };
-static_assert(sizeof(CcRW) == 64 && sizeof(QcnRW) == 64, "congestion-control slots");
+/* HPCC (Li et al., SIGCOMM 2019) per connection, in the same 64-byte slot;
+ * sent, acked, lat and aword where CcRW has them.  Telemetry: per connection,
+ * `slots` records of hx switches x 3 words (tick, egress packets sent,
+ * backlog | rate << 24) from word 3 * hx * int_off of o_int, record seq %
+ * slots for the packet with that sequence number; the last ACK's telemetry at
+ * o_hl, 3 * hx words per connection */
+#define HP_ETA 62259u           /* 0.95 in 1/65536 */
+#define HP_MAX_STAGE 5u
+#define HP_N 16u                /* flows expected to share a link, in W_AI */
+struct HpRW {
+    uint32_t w, wc;      /* window and reference window, 1/256 packet */
+    uint32_t sent, acked;
+    uint32_t U;          /* utilisation, 1/65536 */
+    uint32_t stage;
+    uint32_t hlast;      /* packets sent when Wc last changed */
+    uint32_t lat, aword;
+    uint32_t T;          /* base round trip 2 lat, ticks; the window cap in packets */
+    uint32_t wai;        /* additive step, 1/256 packet */
+    uint32_t have;       /* an ACK's telemetry has been recorded */
+    uint32_t nsw;        /* switches on the path */
+    uint32_t slots;      /* telemetry records (= T) */
+    uint32_t int_off;    /* first record */
+    uint32_t pad;
+};
+static_assert(sizeof(CcRW) == 64 && sizeof(QcnRW) == 64 && sizeof(HpRW) == 64, "congestion-control slots");
+static_assert(offsetof(CcRW, sent) == offsetof(HpRW, sent) && offsetof(CcRW, acked) == offsetof(HpRW, acked) &&
+              offsetof(CcRW, lat) == offsetof(HpRW, lat) && offsetof(CcRW, aword) == offsetof(HpRW, aword),
+              "shared fields");
 static_assert(offsetof(CcRW, lat) == offsetof(QcnRW, lat) && offsetof(CcRW, aword) == offsetof(QcnRW, aword),
               "shared fields");
 
@@ -213,7 +241,11 @@ struct ArenaHdr {        /* general format header */
      * pools, staging, backlogs, host state); a workgroup that cannot hold the
      * whole arena in LDS copies these two ranges there, back to back, and
      * leaves the per-connection state in HBM */
-    uint32_t ro_hot, rw_hot, pad_lb[1];
+    uint32_t ro_hot, rw_hot;
+    /* HPCC (cc = 3): general-path descriptors are conn << cshift | telemetry
+     * record << 4 | switches passed (cshift = DESC_SHIFT otherwise); hx
+     * switches per telemetry record; o_hl, o_int as HpRW describes */
+    uint32_t cshift, hx, o_hl, o_int;
 };
 
 /* ---- compact format ------------------------------------------------------

@@ -317,7 +317,7 @@ class Experiment:
     queue_pkts: int
     ecmp_seed: int
     pkt_bytes: int = PKT_BYTES
-    cc: int = CC_NONE          # CC_NONE, CC_DCTCP or CC_DCQCN
+    cc: int = CC_NONE          # CC_NONE, CC_DCTCP, CC_DCQCN or CC_HPCC
     ecn_k: int = 0             # DCTCP, DCQCN: marking threshold (packets)
     cwnd0: int = 0             # DCTCP: initial window (packets, >= 1)
     lb: int = LB_ECMP          # LB_ECMP or LB_SPRAY
@@ -483,8 +483,8 @@ def single_batch(topo: Topology, work: Workload, queue_pkts: int = 16, ecmp_seed
 # The five benchmark configurations
 # ---------------------------------------------------------------------------
 
-BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5, 6: 0xC6, 7: 0xC7, 8: 0xC8, 9: 0xC9, 10: 0xCA}
-FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000, 6: 768, 7: 256, 8: 256, 9: 256, 10: 256}
+BASE_SEED = {1: 0xC1, 2: 0xC2, 3: 0xC3, 4: 0xC4, 5: 0xC5, 6: 0xC6, 7: 0xC7, 8: 0xC8, 9: 0xC9, 10: 0xCA, 11: 0xCB}
+FULL_E = {1: 16, 2: 256, 3: 1024, 4: 4096, 5: 10000, 6: 768, 7: 256, 8: 256, 9: 256, 10: 256, 11: 256}
 CONFIG_NAMES = {
     1: "C1 ring all-reduce 1 MiB, 8 hosts on one switch, NC x C grid",
     2: "C2 ring all-reduce 64 MiB over a 4x8 leaf-spine with 4 spines",
@@ -497,6 +497,7 @@ CONFIG_NAMES = {
        "initial window swept",
     9: "C9 k=8 fat-tree with packet spraying: C4's groups and failures at a quarter of the bytes",
     10: "C10 k=8 fat-tree with DCQCN: C4's groups and failures at a quarter of the bytes, ECN threshold swept",
+    11: "C11 k=8 fat-tree with HPCC: C4's groups and failures at a quarter of the bytes",
 }
 
 
@@ -800,6 +801,19 @@ def _c10(e_list):
     return b
 
 
+def _c11(e_list):
+    """C4's experiments with every message a quarter of C4's (as in C8) and
+    HPCC, which has no per-experiment parameter."""
+    b = _c4(e_list)
+    for w in b.works:
+        for c in w.colls:
+            c.nbytes //= 4
+    for x in b.exps:
+        x.cc = CC_HPCC
+    b.name = "C11"
+    return b
+
+
 def make_config(cid: int, n_exp: Optional[int] = None, exp_ids: Optional[Sequence[int]] = None) -> Batch:
     """Batch for benchmark configuration cid (1..9).  Experiment e of a config is
     the same whatever subset is drawn, so exp_ids picks a sample of the full
@@ -807,7 +821,7 @@ def make_config(cid: int, n_exp: Optional[int] = None, exp_ids: Optional[Sequenc
     if exp_ids is None:
         exp_ids = range(FULL_E[cid] if n_exp is None else n_exp)
     e_list = list(exp_ids)
-    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5, 6: _c6, 7: _c7, 8: _c8, 9: _c9, 10: _c10}[cid](e_list)
+    b = {1: _c1, 2: _c2, 3: _c3, 4: _c4, 5: _c5, 6: _c6, 7: _c7, 8: _c8, 9: _c9, 10: _c10, 11: _c11}[cid](e_list)
     b.meta["config"] = cid
     b.meta["exp_ids"] = e_list
     return b

@@ -80,6 +80,7 @@ extern "C" {
 #define MSIM_CC_NONE 0
 #define MSIM_CC_DCTCP 1          /* ECN marks at switches, ACKs, a DCTCP window per connection */
 #define MSIM_CC_DCQCN 2          /* ECN marks at switches, CNPs, a DCQCN rate per connection */
+#define MSIM_CC_HPCC 3           /* in-band telemetry at switches, ACKs, an HPCC window per connection */
 #define MSIM_MAX_CWND 65535      /* packets */
 
 /* load balancing (exp_lb), Multiverse section 5: ECMP and packet spraying */
@@ -170,6 +171,28 @@ extern "C" {
  *   - a connection sends only at ticks t with t * 65536 >= its next send time
  *     N (initially 0); a packet sent at t sets N = max(N, t * 65536 - 65535) +
  *     floor(2^32 / RC).
+ *   With MSIM_CC_HPCC (HPCC, Li et al., SIGCOMM 2019, Algorithm 1, in integer
+ *   arithmetic; exp_ecn_k and exp_cwnd0 unused, may be NULL; no ECN marks):
+ *   - a packet leaving a switch egress at tick t records, for that switch,
+ *     (t, packets the egress has sent including this one, the egress's
+ *     backlog at the start of t as for ECN, the egress rate); each packet is
+ *     ACKed as under DCTCP and the ACK carries the packet's records;
+ *   - each connection keeps T = 2 L, a window W and reference window Wc (1/256
+ *     packet, initially T packets, always 1 .. T packets), U (1/65536,
+ *     initially 0) and an increase stage; W_AI = floor(T * 256 * 3277 /
+ *     (65536 * 16)), at least 1; it sends only while sent - acked < floor(W);
+ *   - ACKs are applied one by one in sequence order.  The first only records
+ *     its telemetry and sets the update mark to the packets sent.  A later
+ *     one: per switch i with dts = t_i - t_i(previous ACK) > 0, u_i =
+ *     floor(65536 (min(q_i, q_i prev) dts + (n_i - n_i prev) T) / (rate_i T
+ *     dts)); u and tau start at 0 and, switch by switch in path order, u_i >
+ *     u replaces them with (u_i, dts); tau is capped at T; U = floor(((T -
+ *     tau) U + tau u) / T).
+ *     If U >= 62259 (0.95) or the stage is 5: W = floor(Wc * 62259 / U) +
+ *     W_AI (W = T packets if U = 0), else W = Wc + W_AI, then clamped; if
+ *     the acknowledged count exceeds the update mark, Wc = W, the stage goes
+ *     to 0 (first case) or up by 1, and the mark becomes the packets sent;
+ *   - at most 8 switches per path (MSIM_MAX_SWITCH_HOPS).
  *   An experiment with congestion control runs on the general path.
  *   Load balancing exp_lb[e] (exp_lb NULL = MSIM_LB_ECMP for all): with
  *   MSIM_LB_SPRAY a packet with sequence number s (packets its connection sent

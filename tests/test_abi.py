@@ -224,6 +224,22 @@ def test_dcqcn_compile_and_validation(simmod, oracle):
     assert oracle.run(bb, 0)["rc"] == oracle.E_INVALID
 
 
+def test_hpcc_compile_and_validation(simmod, oracle):
+    """HPCC experiments compile onto the congestion-control kernel with a
+    telemetry record per packet a window can hold; HPCC with spraying is
+    rejected as the oracle rejects it."""
+    b = I.make_config(11, exp_ids=[0, 7])
+    s = simmod.Sim(b)
+    inf = s.info()
+    assert inf["n_compact"] == 0 and simmod.KERNEL_NAMES[inf["main_kernel"]] == "msim_megakernel_cc"
+    assert inf["max_arena_bytes"] > simmod.Sim(I.make_config(8, exp_ids=[0, 7])).info()["max_arena_bytes"]
+    for e in range(b.n_exp):
+        assert s.flow_count(e) == oracle.count(b, e)[1]
+    bb = I.single_batch(I.single_switch(2), I.xflows([(0, 1, 3)]), cc=I.CC_HPCC, lb=I.LB_SPRAY)
+    expect_error(simmod, bb, simmod.E_INVALID_SPEC)
+    assert oracle.run(bb, 0)["rc"] == oracle.E_INVALID
+
+
 def test_packet_spraying_compile_and_validation(simmod, oracle):
     """Sprayed experiments compile onto the spraying kernel; unknown modes and
     spraying with congestion control are rejected as the oracle rejects them."""

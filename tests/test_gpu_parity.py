@@ -628,6 +628,76 @@ def test_c10_sample(simmod, oracle):
     assert_flows(s, 0, o)
 
 
+def hpcc_batch(n, seed):
+    """Rings, broadcasts, trees and explicit flows on three fabrics (links of
+    rate 1 and 2, so telemetry of both rates) with HPCC; every other experiment
+    carries long explicit flows, every fourth a broadcast held back by a
+    computation."""
+    rng = np.random.default_rng(seed)
+    topos = [I.single_switch(8), I.leaf_spine(2, 4, 2, host_rate=1, up_rate=2), I.fat_tree(4)]
+    works, exps = [], []
+    for e in range(n):
+        t = e % 3
+        nh = [8, 8, 16][t]
+        hosts = [int(h) for h in rng.permutation(nh)]
+        colls = [I.ring(I.COLL_RING_AR, 4 * 8 * I.PKT_BYTES * int(rng.integers(1, 4)), hosts[:4],
+                        int(rng.integers(1, 3)), 2 * I.PKT_BYTES),
+                 I.bcast(24 * I.PKT_BYTES, hosts[4:7], int(rng.choice([1, 4, 8])))]
+        if t == 2:
+            colls.append(I.tree(32 * I.PKT_BYTES, hosts[8:15], 2, 4 * I.PKT_BYTES))
+        tasks = []
+        if e % 4 == 1:
+            colls.append(I.bcast(int(rng.integers(200, 1500)) * I.PKT_BYTES, [hosts[0], hosts[5]], 4))
+            tasks = [I.compute(int(rng.integers(100, 1500))), I.comm(len(colls) - 1, [0])]
+        w = I.Workload(colls)
+        w.tasks = tasks
+        top = 2500 if e % 2 == 0 else 40
+        pairs = [(hosts[i], hosts[(i + 3) % nh], int(rng.integers(1, top))) for i in range(nh)]
+        w.xsrc, w.xdst, w.xpkts = (np.array([p[k] for p in pairs], np.uint32) for k in range(3))
+        works.append(w)
+        exps.append(I.Experiment(t, e, int(rng.integers(2, 17)), int(rng.integers(0, 2**32)), I.PKT_BYTES,
+                                 I.CC_HPCC, 0, 0))
+    return I.Batch(topos, works, exps, "hpcc")
+
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_hpcc(simmod, oracle, force_global):
+    b = hpcc_batch(24, 31)
+    s, g = gpu_run(simmod, b, record=range(b.n_exp), force_global=force_global)
+    assert simmod.KERNEL_NAMES[s.info()["main_kernel"]] == "msim_megakernel_cc"
+    ref = oracle_all(oracle, b, flows=True)
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+        assert_flows(s, e, ref[e])
+
+
+def test_hpcc_pinned_scenarios_gpu(simmod, oracle):
+    """The scenarios the oracle's HPCC pins derive by hand (a single flow's
+    send ticks, an incast's first ticks), per flow on the GPU."""
+    w1 = I.Workload([I.bcast(30 * I.PKT_BYTES, [0, 1], 30)])
+    w2 = I.Workload([I.bcast(20 * I.PKT_BYTES, [0, 2], 20), I.bcast(20 * I.PKT_BYTES, [1, 2], 20)])
+    exps = [I.Experiment(0, 0, 16, 0, I.PKT_BYTES, I.CC_HPCC, 0, 0),
+            I.Experiment(1, 1, 16, 0, I.PKT_BYTES, I.CC_HPCC, 0, 0)]
+    b = I.Batch([I.single_switch(2), I.single_switch(3)], [w1, w2], exps, "hpcc-pins")
+    s, g = gpu_run(simmod, b, record=range(b.n_exp))
+    ref = oracle_all(oracle, b, flows=True)
+    assert list(np.asarray(ref[0]["sd"][:19], np.int64) - 1) == list(range(15)) + [16, 17, 18, 20]
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+        assert_flows(s, e, ref[e])
+
+
+def test_c11_sample(simmod, oracle):
+    ids = [0, 101, 255]
+    b = I.make_config(11, exp_ids=ids)
+    s, g = gpu_run(simmod, b, record=[0])
+    ref = oracle_all(oracle, b, flows=False)
+    for e in range(b.n_exp):
+        assert_exp(g, e, ref[e])
+    o = oracle.run(b, 0, flows=True)
+    assert_flows(s, 0, o)
+
+
 # ---------------------------------------------------------------------------
 # Packet spraying (per-packet equal-cost choice, in-order delivery)
 # ---------------------------------------------------------------------------
