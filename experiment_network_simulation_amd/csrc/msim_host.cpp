@@ -617,13 +617,9 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
             take(H.o_pnxt, (size_t)S * Q);
             take(H.o_popped, 8ull * nt);
             const uint32_t RP = R <= 1 ? 1 : (R <= 2 ? 2 : 4);
-            if (R == 1) {
-                take(H.o_elig, 4ull * nt);
-                take(H.o_fmask, 8ull * S);
-            } else {
-                H.o_elig = 0;
-                H.o_fmask = 0;
-            }
+            H.o_elig = 0;
+            if (R == 1) take(H.o_fmask, 8ull * S);
+            else H.o_fmask = 0;
             take(H.o_sdesc, (size_t)dt * nt * W * RP);
             take(H.o_crw, sizeof(CRW2) * nconn);
             H.lds_bytes = (uint32_t)off;
@@ -687,11 +683,11 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                         pv[sl].left = left[P.host];
                     } else {
                         R2.vbase = sw_of[port_node[p]] * rsz * rsz;
-                        const uint64_t all = Q == 64 ? ~0ull : ((1ull << Q) - 1ull);
-                        if (R == 1) ((uint64_t *)(A + H.o_fmask))[sl - SB] = all;
-                        else pv[sl].freem = all;
+                        pv[sl].freem = Q == 64 ? ~0ull : ((1ull << Q) - 1ull);
                     }
                 }
+                /* rate 1: every queue starts empty (head byte Q_EMPTY) */
+                if (R == 1) memset(A + H.o_nslot, (int)Q_EMPTY, Vc);
                 memcpy(A, &H, sizeof H);
                 out.rw_off = H.rw_off;
                 out.bytes = H.bytes;

@@ -1104,14 +1104,13 @@ struct CCtx {
     const LDSP uint16_t *cgrp;
     const LDSP uint8_t *lidx;
     LDSP CRW2 *crw;
-    LDSP uint32_t *elig;       /* rate 1: per output, inputs with a non-empty queue toward it */
-    LDSP uint64_t *fmask;      /* rate 1: per switch ingress (slot - SB), its free buffer slots */
+    LDSP uint64_t *fmask;      /* rate 1: per switch ingress (slot - SB), slots its outputs returned */
     LDSP uint8_t *L;           /* the LDS image, and byte offsets of two of its arrays */
     uint32_t o_nslot, o_pnxt;
     const LDSP CGrp *grp;
     LDSP DT *pdesc, *sdesc;
     uint32_t *rec;
-    uint32_t Q, W, R, n_flows, SB, nt;
+    uint32_t Q, W, R, n_flows, SB, nt, n_conn;
     uint32_t RP;               /* staging entries per (tick slot, port): R rounded up to 1, 2 or 4 */
     uint32_t S;                /* switch thread slots; pools are slot-major: [buffer slot][S] */
 };
@@ -1170,7 +1169,7 @@ __device__ __forceinline__ uint32_t csize(const CGrp &g, uint32_t idx, uint32_t 
     if (F == 2 && g.kind == GK_SEQ) return g.p;
     const uint32_t r = cdiv_S(g, pos);
     if (r + 1 < g.R) return g.p;
-    const uint32_t k = cchunk(g, idx, pos - r * g.S);
+    const uint32_t k = cchunk(g, idx, pos - __umul24(r, g.S));   /* r * S <= pos < 2^14 */
     return g.Xq + (k < g.Xr ? 1u : 0u);
 }
 
@@ -1181,7 +1180,7 @@ __device__ __forceinline__ uint32_t cfid(const CGrp &g, uint32_t idx, uint32_t p
     if (F != 0 && g.kind == GK_BCAST) return g.fid_base + idx * g.S + pos;
     if (F == 2 && g.kind == GK_TREE) return g.fid_base + pos * 2u * (g.N - 1u) + idx;
     if (F == 2 && g.kind == GK_SEQ) return g.fid_base + idx;
-    return g.fid_base + pos * g.N + idx;
+    return g.fid_base + __umul24(pos, g.N) + idx;               /* pos < 2^14, ring N <= 1024 */
 }
 
 template <int F>
@@ -1306,8 +1305,9 @@ __device__ __forceinline__ void chost_deliver(const CCtx<DT> &C, Acc &a, HostReg
         if (pos < cflows<F>(g)) cw.r_rem = (uint16_t)csize<F>(g, idx, pos);
         cwake_dependents<F>(C, a, hr, g, idx, c, t);
     }
-    if (any)
-        for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
+    /* at rate 1 the far output rewrites the entry every tick */
+    if (!R1 && any)
+        for (uint32_t k = 0; k < C.RP; k++) rec[k] = 0;
 }
 
 /* A host's pending activations (phase B): every connection at t = 0, then the
@@ -1323,6 +1323,115 @@ __device__ __forceinline__ void chost_pending(const CCtx<DT> &C, Acc &a, HostReg
         if (hr.pcnt > 2) ccheck<F>(C, a, hr, hr.p2, t);
         if (hr.pcnt > 3) ccheck<F>(C, a, hr, hr.p3, t);
         hr.pcnt = 0;
+    }
+}
+
+/* Connection cursors read in one 64-bit LDS access. */
+__device__ __forceinline__ CRW2 crw_load(const LDSP CRW2 *p)
+{
+    const uint64_t v = *(const LDSP uint64_t *)p;
+    CRW2 w;
+    w.s_st = (uint16_t)v; w.s_rem = (uint16_t)(v >> 16); w.r_pos = (uint16_t)(v >> 32); w.r_rem = (uint16_t)(v >> 48);
+    return w;
+}
+
+/* Makes the compiler hold v in a register at this point: a load above it is
+ * complete here and is not sunk into a later branch, so loads pinned together
+ * are waited for together. */
+template <typename T>
+__device__ __forceinline__ void pin(T &v)
+{
+    asm volatile("" : "+v"(v));
+}
+
+/* Rings only, rate 1: a host's arrivals and activations (phases A and B) for
+ * t > 0, the same rules as chost_deliver<0> followed by chost_pending<0>.
+ * At rate 1 at most one packet arrives per tick, and at most one flow left
+ * the NIC during the last tick.  So at most two connections leaving this host
+ * may start a flow now: the ring successor d of a connection c whose flow was
+ * fully received now (d's receive predecessor is that flow), and the pending
+ * connection p whose flow finished sending (its send predecessor).  The reads
+ * are issued in three rounds instead of one dependent access at a time.
+ * Rank i's connection of a ring receives from connection (i - 1) mod N of the
+ * same group, so d is c + 1 unless c is the group's last rank. */
+template <typename DT>
+__device__ __forceinline__ void chost_ring_r1(const CCtx<DT> &C, Acc &a, HostRegs &hr, LDSP DT *rec, uint32_t t)
+{
+    const bool pend = hr.pcnt != 0;
+    if (hr.pcnt > 1) a.fault = 1;
+    hr.pcnt = 0;
+    const uint32_t p = pend ? hr.p0 : 0u;
+    /* round 1: the arrival, and the pending connection's send state and group
+     * (the delivery below writes receive-side fields only) */
+    uint32_t e = rec[0];
+    uint32_t p_st = C.crw[p].s_st, p_gi = C.cgrp[p], p_li = C.lidx[p];
+    pin(e); pin(p_st); pin(p_gi); pin(p_li);
+    const bool got = e != 0;
+    const uint32_t c = got ? (e - 1) >> DESC_SHIFT : 0u;
+    const uint32_t c1 = c + 1u < C.n_conn ? c + 1u : c;
+    /* round 2: c's cursors and group, the send state of c + 1, p's group */
+    uint64_t cw = *(const LDSP uint64_t *)(C.crw + c);
+    uint32_t gi = C.cgrp[c];
+    uint32_t n_st = C.crw[c1].s_st, n_li = C.lidx[c1];
+    CGrp h = cgrp_load(C.grp + p_gi);
+    pin(cw); pin(gi); pin(n_st); pin(n_li);
+    pin(h.kind); pin(h.N); pin(h.S); pin(h.R); pin(h.p); pin(h.Xq); pin(h.Xr); pin(h.fid_base); pin(h.conn_base); pin(h.mS);
+    const uint32_t hN = h.N, hS = h.S, hR = h.R, hcb = h.conn_base;
+    const uint32_t r_pos = (uint32_t)(cw >> 32) & 0xFFFFu, r_rem = (uint32_t)(cw >> 48);
+    const bool fin = got && r_rem == 1u;            /* c's flow is now fully received */
+    const uint32_t pidx = p - hcb, ppos = p_st & C_POS_MASK;
+    const uint32_t cin = hcb + (pidx == 0 ? hN - 1u : pidx - 1u);
+    /* round 3: c's group in full, the receive position of p's predecessor */
+    CGrp g;
+    uint32_t cin_rpos = 0;
+    if (pend) cin_rpos = C.crw[cin].r_pos;
+    if (fin) g = cgrp_load(C.grp + gi);
+    pin(cin_rpos);
+    if (got) a.delivered++;
+    if (got && !fin) C.crw[c].r_rem = (uint16_t)(r_rem - 1u);
+    uint32_t d = MSIM_NONE, rpos = 0;
+    if (fin) {
+        const uint32_t idx = c - g.conn_base;
+        const uint32_t fid = cfid<0>(g, idx, r_pos);
+        a.tmax = t;
+        a.left--;
+        if (C.rec) C.rec[fid] = t;
+        rpos = r_pos + 1u;
+        const uint32_t nrem = rpos < __umul24(g.R, g.S) ? csize<0>(g, idx, rpos) : 0u;
+        *(LDSP uint32_t *)&C.crw[c].r_pos = rpos | (nrem << 16);
+        d = idx + 1u == g.N ? c + 1u - g.N : c + 1u;
+        if (d != c1) {                              /* c is the last rank: one more round */
+            n_st = C.crw[d].s_st;
+            n_li = C.lidx[d];
+        }
+        a.digest += mix64(((uint64_t)fid << 32) | t);
+    }
+    /* d waits for its receive predecessor, the flow over c, received through rpos */
+    if (fin && (n_st >> C_STATE_SHIFT) == CS_IDLE) {
+        const uint32_t dpos = n_st & C_POS_MASK;
+        if (dpos - __umul24(cdiv_S(g, dpos), g.S) == 0 || rpos >= dpos) {
+            const uint32_t didx = d - g.conn_base;
+            *(LDSP uint32_t *)&C.crw[d].s_st = (dpos | (CS_ACTIVE << C_STATE_SHIFT)) | (csize<0>(g, didx, dpos) << 16);
+            hr.ready |= 1ull << n_li;
+            a.last_act1 = t + 1;
+            if (C.rec) C.rec[C.n_flows + cfid<0>(g, didx, dpos)] = t;
+        }
+    }
+    if (pend) {
+        if (ppos >= __umul24(hR, hS)) {
+            C.crw[p].s_st = (uint16_t)(ppos | (CS_DONE << C_STATE_SHIFT));
+        } else {
+            /* cin's receive position as of now: c's, if this tick completed it */
+            const uint32_t rp = (fin && cin == c) ? rpos : cin_rpos;
+            if (ppos - __umul24(cdiv_S(h, ppos), hS) == 0 || rp >= ppos) {
+                *(LDSP uint32_t *)&C.crw[p].s_st = (ppos | (CS_ACTIVE << C_STATE_SHIFT)) | (csize<0>(h, pidx, ppos) << 16);
+                hr.ready |= 1ull << p_li;
+                a.last_act1 = t + 1;
+                if (C.rec) C.rec[C.n_flows + cfid<0>(h, pidx, ppos)] = t;
+            } else {
+                C.crw[p].s_st = (uint16_t)(ppos | (CS_IDLE << C_STATE_SHIFT));
+            }
+        }
     }
 }
 
@@ -1393,7 +1502,6 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     C.cgrp = (const LDSP uint16_t *)(L + H->o_cgrp);
     C.lidx = (const LDSP uint8_t *)(L + H->o_lidx);
     C.crw = (LDSP CRW2 *)(L + H->o_crw);
-    C.elig = (LDSP uint32_t *)(L + H->o_elig);
     C.fmask = (LDSP uint64_t *)(L + H->o_fmask);
     C.L = L;
     C.o_nslot = H->o_nslot;
@@ -1405,6 +1513,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     C.W = H->W;
     C.R = H->R;
     C.n_flows = H->n_flows;
+    C.n_conn = H->n_conn;
     C.SB = SB;
     C.nt = nt;
     C.RP = R1 ? 1u : (H->R <= 1 ? 1u : (H->R <= 2 ? 2u : 4u));
@@ -1426,7 +1535,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     hseen.w0 = R1 ? 0 : pv.hseen[0]; hseen.w1 = R1 ? 0 : pv.hseen[1];
     phead.w0 = R1 ? 0 : pv.phead[0]; phead.w1 = R1 ? 0 : pv.phead[1];
     arrv.w0 = R1 ? 0 : pv.arrv[0]; arrv.w1 = R1 ? 0 : pv.arrv[1];
-    uint64_t freem = R1 ? 0 : pv.freem;            /* rate 1: the free masks live in LDS */
+    uint64_t freem = pv.freem;                     /* switch ingress: free buffer slots */
     uint32_t popped = pv.popped, pushed = pv.pushed, rr = pv.rr;
     HostRegs hr;
     hr.ready = pv.ready;
@@ -1439,7 +1548,6 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     /* staging: the record of (tick slot, port) starts at slot * tstride + port * RP */
     const uint32_t RP = C.RP, tstride = nt * RP, wsz = C.W * tstride;
     const uint32_t doff = pr.delay * tstride, poff = pr.peer * RP, myoff = tid * RP;
-    const uint32_t mybit = 1u << local;            /* rate 1: this input's bit in its outputs' masks */
     const uint32_t pushed0 = pushed;               /* packet-hops of this run: pushed - pushed0 */
 
     Acc a;
@@ -1458,46 +1566,38 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     while (t < t_end) {
         /* ---------------- arrivals */
         if (R1 && is_sw) {
-            /* rate 1: at most one packet per ingress and tick.  First carry the
-             * popped count through t-1 into the buffer that tick t+1 reads; the
-             * outputs add this tick's pops to it while they forward. */
-            C.popped[(tp ^ nt) + tid] = C.popped[tp + tid];
-            LDSP DT *rec = C.sdesc + sb + myoff;
-            const uint32_t e = rec[0];
+            /* rate 1: at most one packet per ingress and tick.  This tick's pop
+             * count starts at zero; the outputs of this switch add to it while
+             * they forward, and the far outputs read it during tick t+1. */
+            C.popped[tp + tid] = 0;
+            const uint32_t e = C.sdesc[sb + myoff];
             if (e != 0) {
-                rec[0] = 0;
                 const uint32_t desc = e - 1;
                 const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
                 const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
-                const uint64_t fm = C.fmask[pool];
-                if (fm == 0 || o >= deg) {
+                const uint32_t vq = pr.vbase + o * RSZ + local;   /* queue (this input, o) */
+                const uint32_t head = C.nslot[vq], tail = C.arr[vq];
+                /* free slots: the register mask, refilled from the slots the
+                 * outputs returned only when it runs dry */
+                if (freem == 0)
+                    freem = __hip_atomic_exchange(C.fmask + pool, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                if (freem == 0 || o >= deg) {
                     a.fault = 1;
                 } else {
                     uint32_t s;
                     if (q32) {
-                        const uint32_t lo = (uint32_t)fm;
+                        const uint32_t lo = (uint32_t)freem;
                         s = __builtin_ctz(lo);
-                        C.fmask[pool] = lo & (lo - 1u);
+                        freem = lo & (lo - 1u);
                     } else {
-                        s = __builtin_ctzll(fm);
-                        C.fmask[pool] = fm & (fm - 1);
+                        s = __builtin_ctzll(freem);
+                        freem &= freem - 1;
                     }
                     C.pdesc[cpool(C, pool, s)] = (DT)e;
-                    const uint32_t vq = pr.vbase + o * RSZ + local;   /* queue (this input, o) */
-                    LDSP uint32_t *el = C.elig + qbase + o;
-                    /* the read precedes every lane's update of the mask, and only
-                     * this input changes its own bit during arrivals; several
-                     * inputs of one switch may set bits of one mask in one
-                     * instruction, hence the atomic.  Without branches: the new
-                     * slot goes to the head byte of an empty queue or behind the
-                     * tail of a non-empty one, and the OR adds nothing if the
-                     * queue was non-empty. */
-                    const uint32_t tail = C.arr[vq];
-                    const uint32_t nonempty = __hip_atomic_load(el, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & mybit;
-                    const uint32_t keep = 0u - (nonempty >> local);          /* all ones if non-empty */
+                    /* an empty queue has the head byte Q_EMPTY: the new slot
+                     * becomes its head, else it goes behind the tail */
                     const uint32_t at_head = C.o_nslot + vq, at_tail = C.o_pnxt + cpool(C, pool, tail);
-                    C.L[at_head ^ ((at_head ^ at_tail) & keep)] = (uint8_t)s;
-                    __hip_atomic_fetch_or(el, mybit & ~keep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    C.L[head == Q_EMPTY ? at_head : at_tail] = (uint8_t)s;
                     C.arr[vq] = (uint8_t)s;
                 }
             }
@@ -1541,8 +1641,12 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             LDSP DT *rec = C.sdesc + sb + myoff;
             /* the ring-only copy costs registers the faster-link kinds do not have */
             if (R1 && !X && rings_only) {
-                chost_deliver<0, R1>(C, a, hr, rec, t);
-                chost_pending<0>(C, a, hr, pr, t);
+                if (t != 0) {
+                    chost_ring_r1(C, a, hr, rec, t);
+                } else {
+                    chost_deliver<0, R1>(C, a, hr, rec, t);
+                    chost_pending<0>(C, a, hr, pr, t);
+                }
             } else {
                 chost_deliver<X ? 2 : 1, R1>(C, a, hr, rec, t);
                 chost_pending<X ? 2 : 1>(C, a, hr, pr, t);
@@ -1554,36 +1658,37 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         if (dst >= wsz) dst -= wsz;
         dst += poff;
         if (R1 && is_sw && alive) {
-            /* rate 1: one grant at most, cyclic from rr over the non-empty inputs */
-            /* one round of reads: the mask, the far credit, and this output's
-             * head-slot and tail-slot rows (one byte per input) */
-            const uint32_t E = C.elig[tid];
-            const int32_t credit = peer_host ? 1 : (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
+            /* rate 1: one grant at most, cyclic from rr over the non-empty
+             * queues toward this output, read from its row of head bytes;
+             * the credit counts the far ingress's pops through t-1 */
+            if (!peer_host) popped += C.popped[(tp ^ nt) + pr.peer];
+            const int32_t credit = peer_host ? 1 : (int32_t)Q - (int32_t)(pushed - popped);
             Row<W> hrow, trow;
             hrow.load(C.nslot + rowp);
             trow.load(C.arr + rowp);
-            if (E != 0 && credit > 0) {
-                const uint32_t up = E >> rr;
-                const uint32_t i = up ? rr + __builtin_ctz(up) : __builtin_ctz(E);
-                const uint32_t vq = rowp + i;                           /* queue (i, this output) */
-                const uint32_t qpool = qbase + i - SB;
-                const uint32_t s = hrow.get(i);
+            const uint64_t F = 0x8080808080808080ull;          /* a slot byte < 64 has bit 7 clear */
+            const int i = first_from<W>(~hrow.w0 & F, W == 2 ? (~hrow.w1 & F) : 0ull, rr);
+            uint32_t out = 0;                                          /* staged entry: desc + 1, or 0 */
+            if (i >= 0 && credit > 0) {
+                const uint32_t vq = rowp + (uint32_t)i;                 /* queue (i, this output) */
+                const uint32_t qpool = qbase + (uint32_t)i - SB;
+                const uint32_t s = hrow.get((uint32_t)i);
                 const uint32_t desc = C.pdesc[cpool(C, qpool, s)];
-                /* popping the tail empties the queue; the head byte of an empty
-                 * queue is rewritten by the next append, so both stores can go
-                 * unconditionally */
-                const bool emptied = s == trow.get(i);
-                C.elig[tid] = emptied ? E & ~(1u << i) : E;
-                C.nslot[vq] = C.pnxt[cpool(C, qpool, s)];
-                /* the slot goes straight back to the ingress's free mask and the
-                 * pop into its count for tick t+1 (other outputs of this switch
-                 * may hit the same ingress in the same instruction) */
+                const uint32_t next = C.pnxt[cpool(C, qpool, s)];
+                /* popping the tail empties the queue */
+                C.nslot[vq] = (uint8_t)(s == trow.get((uint32_t)i) ? Q_EMPTY : next);
+                /* the slot goes back to the ingress and the pop into its count
+                 * for this tick (other outputs of this switch may hit the same
+                 * ingress in the same instruction) */
                 __hip_atomic_fetch_or(C.fmask + qpool, 1ull << s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                __hip_atomic_fetch_add(C.popped + (tp ^ nt) + qbase + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                rr = i + 1 == deg ? 0 : i + 1;
-                ctransmit(C, a, desc, t, dst);
+                __hip_atomic_fetch_add(C.popped + tp + qbase + (uint32_t)i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                rr = (uint32_t)i + 1 == deg ? 0 : (uint32_t)i + 1;
+                out = desc + 1;
+                a.last_tx1 = t + 1;
                 pushed++;
             }
+            /* written every tick, so the far ingress never clears what it read */
+            C.sdesc[dst] = (DT)out;
         } else if (is_sw && alive) {
             Row<W> ar;
             ar.load(C.arr + rowp);
@@ -1611,7 +1716,10 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 credit--;
             }
         } else if (is_host && alive && pr.n_out) {
-            int32_t credit = (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
+            if (R1) popped += C.popped[(tp ^ nt) + pr.peer];
+            int32_t credit = (int32_t)Q - (int32_t)(pushed - (R1 ? popped : C.popped[tp + pr.peer]));
+            /* rate 1: the staged entry is written every tick (0 when idle) */
+            if (R1 && !(credit > 0 && hr.ready)) C.sdesc[dst] = 0;
             for (uint32_t m = 0; m < (R1 ? 1u : pr.rate) && credit > 0 && hr.ready; m++) {
                 const uint64_t rot = rr ? (hr.ready >> rr) | (hr.ready << (64 - rr)) : hr.ready;
                 const uint32_t j = (rr + (uint32_t)__builtin_ctzll(rot)) & 63u;

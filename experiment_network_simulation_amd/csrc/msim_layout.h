@@ -280,18 +280,21 @@ struct ArenaHdr2 {       /* 144 bytes */
  * far output sent for that tick, 0 = empty; RP = the largest rate rounded up
  * to 1, 2 or 4. */
 /* Queues when every link runs at rate 1 (R == 1): the byte of queue (i, o) in
- * o_nslot is its head slot and in o_arr its tail slot; o_elig holds, per
- * switch output thread slot, a 32-bit mask of the inputs whose queue toward it
- * is non-empty (set by the ingress on an append to an empty queue, cleared by
- * the output when it pops the tail); o_fmask holds each switch ingress's free
- * buffer slots (64 bits, index slot - SB), taken by the ingress and returned by
- * the output that pops; o_head is absent.  With a faster link, o_arr / o_head
- * bytes are running append / pop counts, the free masks live in registers and
- * o_elig / o_fmask are absent (0). */
-/* popped (switch ingress: packets forwarded out of it) is published twice,
- * indexed by tick parity: [(t&1) * nt + slot] holds the count through tick t-1
- * and is written at the end of tick t-1, so tick t's readers in other
- * wavefronts never see a value being overwritten. */
+ * o_nslot is its head slot, Q_EMPTY when the queue is empty (slots are < 64),
+ * and in o_arr its tail slot.  Each switch ingress keeps its free buffer slots
+ * in a register; an output that pops a slot returns it by an atomic OR into
+ * the ingress's word of o_fmask (index slot - SB), which the ingress takes back
+ * when its register runs dry.  o_head is absent.  With a faster link, o_arr /
+ * o_head bytes are running append / pop counts, the free masks live in
+ * registers and o_fmask is absent (0).  o_elig is unused (0). */
+#define Q_EMPTY 0xFFu
+/* popped, [2][nt]: with a faster link, switch ingress counts of packets
+ * forwarded, published twice by tick parity: [(t&1) * nt + slot] holds the
+ * count through tick t-1 and is written at the end of tick t-1, so tick t's
+ * readers in other wavefronts never see a value being overwritten.  At rate
+ * 1, [(t&1) * nt + slot] counts the pops of tick t alone: the ingress zeroes
+ * it when the tick starts, the outputs of its switch add to it, and the far
+ * output adds it to its own running count during tick t+1. */
 
 /* Collective group as the compact path reads it: the constant quotients of
  * the flow-size rules are precomputed, and pos / S is umulhi(pos << 8, mS),
