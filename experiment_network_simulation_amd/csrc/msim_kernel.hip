@@ -39,6 +39,13 @@
 #include "msim_layout.h"
 
 #define CHECK_EVERY 16u
+/* The compact path checks every CHECK_EVERY ticks for the first CHECK_LONG
+ * ticks of a run, then every CHECK_EVERY_LONG.  On the k=8 fat-tree batch a
+ * check cost close to a tick; an experiment that runs past CHECK_LONG ticks
+ * overshoots its end by fewer than CHECK_EVERY_LONG ticks in which nothing
+ * happens, and its results do not depend on when the end is seen. */
+#define CHECK_LONG 4096u
+#define CHECK_EVERY_LONG 256u
 #define LDSP __attribute__((address_space(3)))
 
 __device__ __forceinline__ uint64_t mix64(uint64_t z)
@@ -1115,13 +1122,15 @@ struct CCtx {
     uint32_t S;                /* switch thread slots; pools are slot-major: [buffer slot][S] */
 };
 
-/* A collective group copied out of LDS field by field. */
+/* A collective group copied out of LDS in three 16-byte loads (the table
+ * starts 16-byte aligned and a group is 48 bytes). */
 __device__ __forceinline__ CGrp cgrp_load(const LDSP CGrp *p)
 {
-    const LDSP CGrp &q = *p;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 a = ((const LDSP u32x4 *)p)[0], b = ((const LDSP u32x4 *)p)[1], c = ((const LDSP u32x4 *)p)[2];
     CGrp g;
-    g.kind = q.kind; g.N = q.N; g.S = q.S; g.R = q.R; g.p = q.p; g.Xq = q.Xq; g.Xr = q.Xr;
-    g.fid_base = q.fid_base; g.conn_base = q.conn_base; g.mS = q.mS; g.link = q.link;
+    g.kind = (uint16_t)a.x; g.N = (uint16_t)(a.x >> 16); g.S = a.y; g.R = a.z; g.p = a.w;
+    g.Xq = b.x; g.Xr = b.y; g.fid_base = b.z; g.conn_base = b.w; g.mS = c.x; g.link = c.y;
     return g;
 }
 
@@ -1555,6 +1564,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     a.tmax = a.last_tx1 = a.last_act1 = a.max_arr = 0;
     a.left = is_host ? pv.left : 0;
     a.fault = 0;
+    if (tid == 0) { sh.chk_any[0][0] = sh.chk_any[1][0] = 0; sh.chk_max[0][0] = sh.chk_max[1][0] = 0; }
     __syncthreads();
 
     const uint32_t t0 = stp->t_now;
@@ -1780,15 +1790,21 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         sb += tstride;
         if (sb == wsz) sb = 0;
         tp ^= nt;
-        if ((t - t0) % CHECK_EVERY == 0 || t == t_end) {
+        if (((t - t0) & ((t - t0) < CHECK_LONG ? CHECK_EVERY - 1u : CHECK_EVERY_LONG - 1u)) == 0 || t == t_end) {
             a.max_arr = a.last_tx1 ? a.last_tx1 - 1 + pr.delay : 0;
             uint32_t any = __ballot(a.left > 0) != 0ull;
             uint32_t ts = wave_max_u32(max(max(a.last_tx1, a.last_act1), a.max_arr));
-            if (lane == 0) { sh.chk_any[par][wave] = any; sh.chk_max[par][wave] = ts; }
+            /* one word per reduction, updated by one lane per wavefront; the
+             * other parity's words are cleared for the next check, which
+             * comes at least one barrier later */
+            if (lane == 0) {
+                if (any) atomicOr(&sh.chk_any[par][0], 1u);
+                atomicMax(&sh.chk_max[par][0], ts);
+            }
             __syncthreads();
-            any = 0;
-            ts = hist;
-            for (uint32_t w = 0; w < nwaves; w++) { any |= sh.chk_any[par][w]; ts = max(ts, sh.chk_max[par][w]); }
+            any = sh.chk_any[par][0];
+            ts = max(hist, sh.chk_max[par][0]);
+            if (tid == 0) { sh.chk_any[par ^ 1][0] = 0; sh.chk_max[par ^ 1][0] = 0; }
             par ^= 1;
             if (!any) { done = true; break; }
             if (ts <= t - 1) { dead = true; t_dead = ts; break; }

@@ -299,7 +299,7 @@ struct ArenaHdr2 {       /* 144 bytes */
 /* Collective group as the compact path reads it: the constant quotients of
  * the flow-size rules are precomputed, and pos / S is umulhi(pos << 8, mS),
  * exact for pos < 2^14 and S < 2^10. */
-struct CGrp {            /* 40 bytes */
+struct CGrp {            /* 48 bytes: three 16-byte loads */
     uint16_t kind, N;    /* ring / tree members; broadcast hops; send/recv receivers;
                             explicit: flow count (low 16 bits) */
     uint32_t S;          /* ring: steps per round; broadcast: partitions K; tree, send/recv: 1 */
@@ -310,7 +310,9 @@ struct CGrp {            /* 40 bytes */
     uint32_t fid_base, conn_base;
     uint32_t mS;         /* ceil(2^24 / S) */
     uint32_t link;       /* gated ring: its send/recv group; send/recv: first gated group; else MSIM_NONE */
+    uint32_t pad[2];
 };
+static_assert(sizeof(CGrp) == 48, "CGrp is read as three 16-byte words");
 
 struct CRW2 {            /* 8 bytes: compact connection cursors */
     uint16_t s_st, s_rem, r_pos, r_rem;
