@@ -1728,13 +1728,17 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         } else if (is_host && alive && pr.n_out) {
             if (R1) popped += C.popped[(tp ^ nt) + pr.peer];
             int32_t credit = (int32_t)Q - (int32_t)(pushed - (R1 ? popped : C.popped[tp + pr.peer]));
-            /* rate 1: the staged entry is written every tick (0 when idle) */
-            if (R1 && !(credit > 0 && hr.ready)) C.sdesc[dst] = 0;
+            uint32_t out = 0;      /* rate 1: the staged entry, written every tick (0 when idle) */
             for (uint32_t m = 0; m < (R1 ? 1u : pr.rate) && credit > 0 && hr.ready; m++) {
                 const uint64_t rot = rr ? (hr.ready >> rr) | (hr.ready << (64 - rr)) : hr.ready;
                 const uint32_t j = (rr + (uint32_t)__builtin_ctzll(rot)) & 63u;
                 const uint32_t c = C.hout[pr.vbase + j];
-                ctransmit(C, a, c << DESC_SHIFT, t, dst + m);
+                if (R1) {
+                    out = (c << DESC_SHIFT) + 1u;
+                    a.last_tx1 = t + 1;
+                } else {
+                    ctransmit(C, a, c << DESC_SHIFT, t, dst + m);
+                }
                 pushed++;
                 credit--;
                 rr = j + 1 == pr.n_out ? 0 : j + 1;
@@ -1749,14 +1753,21 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                         C.rec[2 * C.n_flows + cfid<X ? 2 : 1>(g, c - g.conn_base, pos)] = t + 1;
                     }
                     cw.s_st = (uint16_t)(pos + 1);
-                    /* append c to the pending list (selects, not branches) */
-                    hr.p0 = hr.pcnt == 0 ? c : hr.p0;
-                    hr.p1 = hr.pcnt == 1 ? c : hr.p1;
-                    hr.p2 = hr.pcnt == 2 ? c : hr.p2;
-                    hr.p3 = hr.pcnt == 3 ? c : hr.p3;
-                    hr.pcnt++;
+                    /* append c to the pending list (selects, not branches); at
+                     * rate 1 the list holds one entry at most */
+                    if (R1) {
+                        hr.p0 = c;
+                        hr.pcnt = 1;
+                    } else {
+                        hr.p0 = hr.pcnt == 0 ? c : hr.p0;
+                        hr.p1 = hr.pcnt == 1 ? c : hr.p1;
+                        hr.p2 = hr.pcnt == 2 ? c : hr.p2;
+                        hr.p3 = hr.pcnt == 3 ? c : hr.p3;
+                        hr.pcnt++;
+                    }
                 }
             }
+            if (R1) C.sdesc[dst] = (DT)out;
         }
         wave_lds_fence();
         /* ---------------- frees, and the popped count for tick t+1 */
