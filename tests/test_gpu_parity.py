@@ -258,6 +258,66 @@ def test_edge_cases(simmod, oracle, force_global):
     assert int(r["tick"][0]) == 0 and int(r["status"][0]) == 0
 
 
+def rate1_batch(n, seed):
+    """Seeded experiments whose links all run at rate 1 (the compact kernels
+    with per-tick pop counts, empty-queue head bytes and register free masks):
+    per-cable delays 1..4, buffers of 1..64 packets (both sides of the 32-slot
+    mask), 8- and 12-port switches, one to three rings with ragged channels, and
+    every fourth experiment mixing in a broadcast and explicit flows."""
+    rng = np.random.default_rng(seed)
+    b = I.Batch([], [], [], "rate1")
+    fabrics = [I.single_switch(8), I.single_switch(12), I.leaf_spine(3, 4, 2, 1, 1), I.fat_tree(4)]
+    for f in fabrics:
+        f.delay = rng.integers(1, 5, f.n_cables).astype(np.uint8)
+        b.topos.append(f)
+    queues = [1, 2, 5, 16, 31, 33, 64]
+    for e in range(n):
+        ti = e % len(fabrics)
+        hosts = [int(x) for x in rng.permutation(b.topos[ti].hosts())]
+        colls = []
+        for _ in range(int(rng.integers(1, 4))):
+            N = int(rng.integers(2, min(8, len(hosts)) + 1))
+            members = [int(x) for x in rng.choice(hosts, N, replace=False)]
+            nc = int(rng.integers(1, 4))
+            P = nc * N * int(rng.integers(1, 5)) + int(rng.integers(0, N))
+            kind = I.COLL_RING_AR if rng.integers(0, 2) else I.COLL_RING_AG
+            colls.append(I.ring(kind, P * I.PKT_BYTES, members, nc, int(rng.integers(1, 6)) * I.PKT_BYTES))
+        if e % 4 == 3:
+            colls.append(I.bcast(23 * I.PKT_BYTES, hosts[:3], 4))
+            w = I.xflows([(hosts[0], hosts[1], 7), (hosts[2], hosts[1], 5)])
+            w.colls = colls
+        else:
+            w = I.Workload(colls)
+        b.works.append(w)
+        b.exps.append(I.Experiment(ti, len(b.works) - 1, queues[e % len(queues)], int(rng.integers(0, 2**32))))
+    return b
+
+
+def test_rate1_paths_one_run_and_resumed(simmod, oracle):
+    """Rate-1 experiments run in one launch, and again resumed in random short
+    runs (the pop counts, free masks and pending entries held in registers are
+    saved and restored at every boundary): both match the oracle in every
+    experiment's totals and every flow's ticks."""
+    b = rate1_batch(24, 0x51)
+    o = oracle_all(oracle, b, flows=True)
+    s, r = gpu_run(simmod, b, record=range(b.n_exp))
+    assert s.info()["n_compact"] == b.n_exp
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+        assert_flows(s, e, o[e])
+    s2 = simmod.Sim(b, record=range(b.n_exp))
+    s2.bind()
+    rng = np.random.default_rng(7)
+    for _ in range(400):
+        s2.run(int(rng.integers(1, 40)))
+        r2 = s2.results()
+        if (r2["status"] != 1).all():
+            break
+    for e in range(b.n_exp):
+        assert_exp(r2, e, o[e])
+        assert_flows(s2, e, o[e])
+
+
 @pytest.mark.parametrize("threads", [64, 256])
 def test_block_size_does_not_matter(simmod, oracle, threads):
     """General path with fewer threads than ports (strided port loops)."""
