@@ -130,6 +130,19 @@ __device__ __forceinline__ int first_from(uint64_t n0, uint64_t n1, uint32_t rr)
  * the loads are independent, so their latencies overlap. */
 __device__ __forceinline__ void row_bytes(const uint8_t *p, uint32_t n, uint64_t &w0, uint64_t &w1)
 {
+    const uintptr_t ad = (uintptr_t)p;
+    if (n == 16 && (ad & 15u) == 0) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = *(const u32x4 *)p;
+        w0 = (uint64_t)v.x | ((uint64_t)v.y << 32);
+        w1 = (uint64_t)v.z | ((uint64_t)v.w << 32);
+        return;
+    }
+    if (n == 8 && (ad & 7u) == 0) {
+        w0 = *(const uint64_t *)p;
+        w1 = 0;
+        return;
+    }
     w0 = w1 = 0;
 #pragma unroll
     for (uint32_t i = 0; i < 16; i++)
