@@ -735,14 +735,17 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
 
 /* ---------------------------------------------------------------- phase D */
 
+/* The m-th packet an output sends in tick t.  Only this output stages packets
+ * at its far ingress, and that ingress empties the slot of arrival tick t + d
+ * when it reads it, W > d ticks before this output uses the slot again; so the
+ * slot holds exactly the m packets sent before this one in this tick. */
 __device__ __forceinline__ void transmit(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr, uint32_t desc,
-                                         uint32_t t)
+                                         uint32_t t, uint32_t m)
 {
     uint32_t ta = t + pr.delay;
     uint32_t si = pr.peer * C.W + ta % C.W;
-    uint32_t k = C.scnt[si];
-    C.scnt[si] = (uint8_t)(k + 1);
-    C.sdesc[si * C.R + k] = desc;
+    C.scnt[si] = (uint8_t)(m + 1);
+    C.sdesc[si * C.R + m] = desc;
     a.hops++;
     a.last_tx1 = t + 1;
     a.max_arr = max(a.max_arr, ta);
@@ -782,7 +785,7 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
         uint32_t desc = c << C.cshift;
         if (C.sp) desc = (c << C.sbits) | C.sseq[c]++;
         else if (C.cc == CC_HPCC) desc |= (C.hps[c].sent % C.hps[c].slots) << 4;   /* its telemetry record */
-        transmit(C, a, p, pr, desc, t);
+        transmit(C, a, p, pr, desc, t, m);
         pushed++;
         credit--;
         moved = true;
@@ -852,7 +855,7 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
             r[1] = pushed + 1;
             r[2] = C.bl[p] | (pr.rate << 24);
         }
-        transmit(C, a, p, pr, desc, t);
+        transmit(C, a, p, pr, desc, t, m);
         pushed++;
         credit--;
         moved = true;
