@@ -51,6 +51,27 @@ def cpu_baseline(batch, gpu_res, sample_ids, threads):
     return hops / dt, dt, hops, ok
 
 
+def copy_bandwidth(nbytes: int = 1 << 31, reps: int = 5) -> float:
+    """GB/s of a plain device-to-device copy (bytes read + bytes written per
+    second), the best of a few timed copies on the current stream."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (best / 1e3) / 1e9
+
+
 def measured_traffic(kernel: str, workload_cfg: int, n: int):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on this kernel source and this workload; else None."""
@@ -175,6 +196,9 @@ def main():
     achieved = alg_bytes / k_avg_s / 1e9
     log(f"[bench] kernel {k_ms} ms; packet-hops {hops}, delivered {delivered}, experiment-ticks {exp_ticks}")
 
+    copy_gbs = copy_bandwidth()
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s (read + write)")
+
     cpu = None
     if args.cpu_sample and n > 0:
         k = min(args.cpu_sample, n)
@@ -224,6 +248,8 @@ def main():
             "kernel": KERNEL_NAMES[info["main_kernel"]],
             "kernel_ms_avg": k_avg_s * 1e3,
             "alg_bytes_per_launch": alg_bytes,
+            "copy_gbs": copy_gbs,
+            "frac_of_copy": achieved / copy_gbs,
         },
         "cpu_baseline": cpu,
     }
@@ -299,6 +325,8 @@ def chunked_bench(args, cid, n, chunk):
                          f"{dt:.1f}s ({chops} packet-hops); GPU results identical on {ok}/{len(sample)}",
                "parity_ok": ok, "parity_n": len(sample)}
         log(f"[bench] CPU oracle {rate:.3e} packet-hops/s; parity {ok}/{len(sample)}")
+    copy_gbs = copy_bandwidth()
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s (read + write)")
     out = {
         "metric": "packet-hops/sec (batched, 1 GPU) + % of HBM roofline at E=4096",
         "value": hops / k_s,
@@ -327,6 +355,8 @@ def chunked_bench(args, cid, n, chunk):
             "kernel": "+".join(sorted(kernels)),
             "kernel_ms_avg": k_s * 1e3 / len(ids),
             "alg_bytes_per_launch": alg_bytes / len(ids),
+            "copy_gbs": copy_gbs,
+            "frac_of_copy": alg_bytes / k_s / 1e9 / copy_gbs,
         },
         "cpu_baseline": cpu,
     }
