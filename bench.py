@@ -10,8 +10,9 @@ HBM before the timed region starts.
 
 Prints one JSON line (rank 0): throughput, the roofline of the megakernel
 (algorithmic bytes: 8 B per packet-hop + 8 B per delivered packet, over the
-kernel's average launch time measured with HIP events on its stream) and the
-CPU oracle timed on a bounded sample of the same batch on the host's cores,
+kernel's average launch time measured with HIP events on its stream; when
+every experiment keeps its state in LDS, also against the chip's LDS read
+bandwidth as the library's probe kernel measures it) and the CPU oracle timed on a bounded sample of the same batch on the host's cores,
 with its results compared to the GPU's for those experiments.
 """
 
@@ -70,6 +71,29 @@ def copy_bandwidth(nbytes: int = 1 << 31, reps: int = 5) -> float:
     del src, dst
     torch.cuda.empty_cache()
     return 2 * nbytes / (best / 1e3) / 1e9
+
+
+def lds_bandwidth(reps: int = 5) -> dict:
+    """LDS read bandwidth of the whole chip, measured by the library's probe
+    kernel (conflict-free 16-byte reads, two 64 KiB workgroups per CU): the
+    best of a few timed launches on the current stream."""
+    import torch
+    from experiment_network_simulation_amd.sim import lds_probe
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = n_cu * 16
+    out = torch.empty(blocks * 1024, dtype=torch.int32, device="cuda:0")
+    lds_probe(out, blocks, 16)
+    best, nbytes = None, 0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        nbytes = lds_probe(out, blocks, 1024)
+        b.record()
+        b.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    gbs = nbytes / (best / 1e3) / 1e9
+    return {"gbs": gbs, "cus": n_cu, "bytes_per_clk_per_cu_at_2p4ghz": gbs * 1e9 / (n_cu * 2.4e9)}
 
 
 def measured_traffic(kernel: str, workload_cfg: int, n: int):
@@ -198,6 +222,13 @@ def main():
 
     copy_gbs = copy_bandwidth()
     log(f"[bench] device copy {copy_gbs:.0f} GB/s (read + write)")
+    lds = None
+    if info["n_lds_exp"] == n:
+        lb = lds_bandwidth()
+        log(f"[bench] LDS read {lb['gbs']:.0f} GB/s ({lb['bytes_per_clk_per_cu_at_2p4ghz']:.0f} B/clk/CU at 2.4 GHz)")
+        lds = {"peak": lb["gbs"], "achieved": achieved, "unit": "GB/s", "frac": achieved / lb["gbs"],
+               "peak_bytes_per_clk_per_cu_at_2p4ghz": lb["bytes_per_clk_per_cu_at_2p4ghz"],
+               "peak_source": "msim_lds_probe (measured, conflict-free 16-byte LDS reads)"}
 
     cpu = None
     if args.cpu_sample and n > 0:
@@ -250,6 +281,7 @@ def main():
             "alg_bytes_per_launch": alg_bytes,
             "copy_gbs": copy_gbs,
             "frac_of_copy": achieved / copy_gbs,
+            "lds": lds,
         },
         "cpu_baseline": cpu,
     }
@@ -357,6 +389,7 @@ def chunked_bench(args, cid, n, chunk):
             "alg_bytes_per_launch": alg_bytes / len(ids),
             "copy_gbs": copy_gbs,
             "frac_of_copy": alg_bytes / k_s / 1e9 / copy_gbs,
+            "lds": None,
         },
         "cpu_baseline": cpu,
     }

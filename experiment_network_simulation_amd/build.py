@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsim.so")
-SOURCES = [os.path.join(CSRC, "msim_kernel.hip"), os.path.join(CSRC, "msim_host.cpp")]
+SOURCES = [os.path.join(CSRC, "msim_kernel.hip"), os.path.join(CSRC, "msim_probe.hip"),
+           os.path.join(CSRC, "msim_host.cpp")]
 ARCH = os.environ.get("MSIM_OFFLOAD_ARCH", "gfx950")
 
 

@@ -29,7 +29,7 @@ KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h_r1", "msim_megakernel_c8
 
 EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_reset", "msim_results",
             "msim_flow_count", "msim_flow_ticks", "msim_task_count", "msim_task_ticks", "msim_get_info",
-            "msim_last_error", "msim_destroy"]
+            "msim_last_error", "msim_destroy", "msim_lds_probe"]
 
 _P8, _P32, _P64 = C.POINTER(C.c_uint8), C.POINTER(C.c_uint32), C.POINTER(C.c_uint64)
 
@@ -98,6 +98,7 @@ def load_library():
     lib.msim_last_error.restype = C.c_char_p
     lib.msim_destroy.argtypes = [vp]
     lib.msim_destroy.restype = None
+    lib.msim_lds_probe.argtypes = [vp, C.c_uint64, C.c_uint32, C.c_uint32, vp]
     for name in EXPORTED:
         if name not in ("msim_last_error", "msim_destroy"):
             getattr(lib, name).restype = C.c_int
@@ -116,6 +117,18 @@ def _stream_ptr(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def lds_probe(out, blocks: int, iters: int, stream=None) -> int:
+    """Launches the LDS read-bandwidth probe (msim_lds_probe) on the stream.
+    `out` is a device tensor of at least blocks x 4,096 bytes.  Returns the
+    bytes the launch reads from LDS; the caller times it on the same stream."""
+    lib = load_library()
+    nbytes = out.numel() * out.element_size()
+    rc = lib.msim_lds_probe(C.c_void_p(out.data_ptr()), nbytes, blocks, iters, C.c_void_p(_stream_ptr(stream)))
+    if rc != 0:
+        raise MsimError(rc, "msim_lds_probe: bad arguments or launch failure")
+    return blocks * 1024 * iters * 128
 
 
 class Sim:

@@ -357,6 +357,18 @@ const char *msim_last_error(const msim_ctx *ctx);
 /* Frees host-side state; the workspace stays the caller's. */
 void msim_destroy(msim_ctx *ctx);
 
+/* Measurement helper, not a step of the simulation: the LDS read bandwidth a
+ * CU sustains, against which the runs that keep their state in LDS are
+ * priced.  Launches `blocks` workgroups of 1,024 threads on hip_stream; each
+ * fills 64 KiB of LDS, then every thread issues iters x 8 conflict-free
+ * 16-byte LDS reads, so a launch reads blocks x 1,024 x iters x 128 bytes.
+ * The caller times the launch (events on hip_stream).  dev_out: caller-owned
+ * device memory of out_bytes >= blocks x 4,096 bytes; one 32-bit word per
+ * thread is written to it (a fold of what the thread read).  Asynchronous.
+ * MSIM_E_ARG for a NULL dev_out, too small an out_bytes, blocks == 0 or
+ * > 2^20, or iters == 0; MSIM_E_HIP if the launch fails. */
+int msim_lds_probe(void *dev_out, uint64_t out_bytes, uint32_t blocks, uint32_t iters, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

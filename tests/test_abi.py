@@ -265,3 +265,14 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_lds_probe_rejects_bad_arguments(simmod):
+    """The LDS probe validates its arguments before any HIP call."""
+    lib = simmod.load_library()
+    E = -5   # MSIM_E_ARG
+    assert lib.msim_lds_probe(None, 4096, 1, 1, None) == E          # no output buffer
+    assert lib.msim_lds_probe(1, 4095, 1, 1, None) == E             # output smaller than blocks x 4 KiB
+    assert lib.msim_lds_probe(1, 4096, 0, 1, None) == E             # no workgroups
+    assert lib.msim_lds_probe(1, 8 << 30, (1 << 20) + 1, 1, None) == E
+    assert lib.msim_lds_probe(1, 4096, 1, 0, None) == E             # no iterations
