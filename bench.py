@@ -128,7 +128,7 @@ def main():
     ap.add_argument("--force-global", action="store_true")
     ap.add_argument("--chunk", type=int, default=0,
                     help="run the batch in chunks of this many experiments, compiling the next chunk while the "
-                         "current one runs (default: whole batch; C5 at full size: 1024)")
+                         "current one runs (default: whole batch; C5 beyond 2048 experiments: 2048)")
     ap.add_argument("--dse", choices=["tune", "reshard"], default=None,
                     help="time a design-space-exploration driver instead: AutoCCL tuning or AlpaComm schedules")
     ap.add_argument("--dse-n", type=int, default=0, help="tuning tasks / resharding instances (default 256 / 64)")
@@ -161,7 +161,7 @@ def main():
 
     cid = args.config
     n = args.n_exp or I.FULL_E[cid]
-    chunk = args.chunk or (1024 if cid == 5 and n > 2048 else 0)
+    chunk = args.chunk or (2048 if cid == 5 and n > 2048 else 0)
     if chunk and chunk < n:
         return chunked_bench(args, cid, n, chunk)
     log(f"[bench] generating config C{cid} with {n} experiments")
