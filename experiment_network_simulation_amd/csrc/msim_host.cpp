@@ -54,6 +54,7 @@ struct Compiled {
     uint32_t nt = 0;       /* compact: thread slots */
     uint64_t n_flows = 0, n_conns = 0, n_ports = 0;
     uint64_t est_hops = 0, est_delivered = 0;
+    uint64_t est_ticks = 0;  /* longest ring's contention-free duration estimate (0: no ring) */
     uint32_t n_task = 0, o_trw = 0;   /* task graph (general format) */
     uint32_t split_bytes = 0;         /* general format: LDS bytes of the switch/NIC state alone */
     int err = 0;
@@ -276,6 +277,9 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
                 Grp g{};
                 g.kind = kind; g.N = N; g.S = S; g.R = (uint32_t)R; g.p = (uint32_t)p; g.X = (uint32_t)X;
                 g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size(); g.link = gate_grp;
+                /* R rounds of S chunk steps, each about a path latency (~6
+                 * ticks on the fabrics used) plus p - 1 packets */
+                out.est_ticks = std::max<uint64_t>(out.est_ticks, R * S * (p + 5));
                 fid += R * S * N;
                 if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
                 for (uint32_t i = 0; i < N; i++) {
@@ -974,12 +978,18 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
             ctx->recorded[opts->record_exp[i]] = 1;
         }
     }
-    /* longest-processing-time order: biggest experiments are claimed first */
+    /* longest-processing-time order: the longest experiments are claimed
+     * first.  A compact workgroup's tick costs about the same whatever the
+     * experiment, so duration follows ticks: the ring duration estimate comes
+     * first (equal bytes per experiment say little about it), then
+     * packet-hops */
     ctx->order.resize(E);
     for (uint32_t e = 0; e < E; e++) ctx->order[e] = e;
     std::stable_sort(ctx->order.begin(), ctx->order.end(), [&](uint32_t a, uint32_t b) {
-        if (ctx->exps[a].kind != ctx->exps[b].kind) return ctx->exps[a].kind < ctx->exps[b].kind;
-        return ctx->exps[a].est_hops > ctx->exps[b].est_hops;
+        const Compiled &x = ctx->exps[a], &y = ctx->exps[b];
+        if (x.kind != y.kind) return x.kind < y.kind;
+        if (x.est_ticks != y.est_ticks) return x.est_ticks > y.est_ticks;
+        return x.est_hops > y.est_hops;
     });
     for (uint32_t i = 0; i < E; i++) {
         uint32_t k = ctx->exps[ctx->order[i]].kind;
