@@ -19,6 +19,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+# the mutation tests point this at a copy of the oracle with a planted mistake
+OVERRIDE = os.environ.get("MSIM_ORACLE_LIB")
+if OVERRIDE:
+    LIB = OVERRIDE
 
 OK, S_INCOMPLETE, S_DEADLOCK = 0, 1, 2
 E_INVALID, E_UNROUTABLE, E_NOMEM, E_INVARIANT = -1, -2, -3, -4
@@ -27,6 +31,8 @@ NONE = 0xFFFFFFFF
 
 def build(force: bool = True) -> str:
     """Compiles oracle.c into liboracle.so (plain gcc, -O2)."""
+    if OVERRIDE:
+        return LIB
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Wno-unused-parameter",

@@ -16,6 +16,6 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def oracle():
     from oracle import oracle as O
-    if not os.path.exists(O.LIB) or os.path.getmtime(O.LIB) < os.path.getmtime(O.SRC):
+    if not O.OVERRIDE and (not os.path.exists(O.LIB) or os.path.getmtime(O.LIB) < os.path.getmtime(O.SRC)):
         O.build(force=True)
     return O

@@ -367,3 +367,73 @@ def test_oversubscribed_fat_tree_shape_and_routes(oracle, o):
     assert rc == 0
     for i, (a, c) in enumerate(pairs):
         assert pth["links"][i] == updown_distance(t, a, c)
+
+
+# ------------------------------------------- uneven chunks, the last-round fold
+
+UNEVEN = os.path.join(os.path.dirname(__file__), "golden", "ring_uneven_traces.json")
+
+
+@pytest.mark.parametrize("case", ["U1_allreduce_uneven", "U2_allgather_uneven", "U3_allreduce_fold",
+                                  "U4_two_channels_one_folds"])
+def test_ring_uneven_chunks_and_fold(oracle, case):
+    """Hand-derived per-flow sizes and ticks where chunk sizes differ, so the
+    chunk each rank sends at each step changes the timing: both all-reduce
+    halves, the all-gather, and a last round folded into the one before it."""
+    g = json.load(open(UNEVEN))[case]
+    N = g["N"]
+    kind = I.COLL_RING_AR if g["kind"] == "allreduce" else I.COLL_RING_AG
+    w = I.Workload([I.ring(kind, g["P"] * I.PKT_BYTES, range(N), g["nc"], g["p"] * I.PKT_BYTES)])
+    b = I.single_batch(I.single_switch(N), w, queue_pkts=16)
+    rc, fl = oracle.flows(b, 0)
+    assert rc == 0
+    assert [int(v) for v in fl["size"]] == g["size"]
+    if "rd" not in g:
+        return
+    r = oracle.run(b, 0, check=True, flows=True)
+    assert r["status"] == oracle.OK
+    assert [int(v) for v in r["act"]] == g["act"]
+    assert [int(v) for v in r["sd"]] == g["sd"]
+    assert [int(v) for v in r["rd"]] == g["rd"]
+    assert r["t_end"] == g["t_end"]
+
+
+def test_fold_flow_count():
+    """A last round of fewer than N packets joins the round before it: the
+    flow count is (R - 1) S N for the unfolded round count R (checked against
+    the oracle's count for several splits; R and the fold test are evaluated
+    here from the message size only)."""
+    from oracle import oracle as O
+    for (P, N, p, ag) in [(8, 3, 2, False), (7, 4, 1, True), (25, 4, 3, False), (31, 5, 3, True),
+                          (12, 3, 2, False), (14, 3, 2, False)]:
+        kind = I.COLL_RING_AG if ag else I.COLL_RING_AR
+        w = I.Workload([I.ring(kind, P * I.PKT_BYTES, range(N), 1, p * I.PKT_BYTES)])
+        rc, nf, _ = O.count(I.single_batch(I.single_switch(N), w), 0)
+        S = N - 1 if ag else 2 * (N - 1)
+        R = -(-P // (N * p))
+        folds = R > 1 and P - (R - 1) * N * p < N
+        assert rc == 0 and nf == (R - 1 if folds else R) * S * N, (P, N, p, ag)
+
+
+# --------------------------------------------------------------- the digest
+
+def test_mix64_is_splitmix64():
+    """The digest mixer is SplitMix64's output function (Steele, Lea and Flood,
+    OOPSLA 2014; Vigna's constants): applied to the generator's states
+    k * 0x9e3779b97f4a7c15 it must give the published first outputs of
+    SplitMix64 seeded with 0."""
+    from oracle import oracle as O
+    gamma = 0x9E3779B97F4A7C15
+    published = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC,
+                 0x1B39896A51A8749B]
+    for k, want in enumerate(published, start=1):
+        assert O.mix64((k * gamma) % 2**64) == want
+
+
+def test_digest_is_sum_over_flows(oracle):
+    """digest = sum over flows f of mix64((f << 32) | RD_f) mod 2^64, with the
+    mixer pinned above and RD taken from the per-flow result."""
+    for b, e in [(I.make_config(1, exp_ids=[5]), 0), (I.make_config(3, exp_ids=[7]), 0)]:
+        r = oracle.run(b, e, flows=True)
+        want = sum(oracle.mix64((f << 32) | int(t)) for f, t in enumerate(r["rd"])) % 2**64
+        assert r["digest"] == want
