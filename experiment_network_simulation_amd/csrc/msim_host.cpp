@@ -30,7 +30,8 @@
 static_assert(CC_DCTCP == MSIM_CC_DCTCP && CC_DCQCN == MSIM_CC_DCQCN && CC_HPCC == MSIM_CC_HPCC, "congestion-control codes");
 
 extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t kind, uint32_t grid, uint32_t block,
-                                      uint32_t lds, bool prepare, hipStream_t stream);
+                                      uint32_t lds, uint32_t *clear, uint32_t n_clear, hipStream_t stream);
+extern "C" hipError_t msim_scratch_words(uint32_t **out);
 extern "C" hipError_t msim_launch_reset(const KParams *kp, uint64_t o_rec_all, uint64_t rec_words,
                                         hipStream_t stream);
 extern "C" hipError_t msim_occupancy(uint32_t kind, uint32_t block, uint32_t lds, int *blocks_per_cu);
@@ -1211,16 +1212,18 @@ static KParams make_params(const msim_ctx *ctx, uint32_t max_ticks)
     return kp;
 }
 
-extern "C" int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *stream, uint32_t flags)
+/* The launches of one msim_run call.  The kernels count a port's packet-hops
+ * of one launch in 32 bits.  A port never sends more than its experiment's
+ * packet-hop total, so one launch per kernel kind suffices unless an
+ * experiment reaches 2^32 packet-hops; then launches of at most 2^30 ticks
+ * keep every port (rate <= 4) below 2^32 per launch.  claim_base == NULL: the
+ * queue counters are the workspace header's, one per kind, zeroed before each
+ * round of launches; otherwise launch i takes claim_base[i], all zeroed once
+ * before the first launch. */
+static int run_launches(msim_ctx *ctx, uint32_t max_ticks, hipStream_t stream, uint32_t *claim_base)
 {
-    if (!ctx) return MSIM_E_ARG;
-    if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_run before msim_bind");
-    (void)flags;
-    /* The kernels count a port's packet-hops of one launch in 32 bits.  A port
-     * never sends more than its experiment's packet-hop total, so one launch
-     * suffices unless an experiment reaches 2^32 packet-hops; then launches of
-     * at most 2^30 ticks keep every port (rate <= 4) below 2^32 per launch. */
     const uint64_t step = ctx->max_exp_hops < (1ull << 32) ? max_ticks : MSIM_LAUNCH_TICKS;
+    uint32_t launch = 0;
     for (uint64_t left = max_ticks; left > 0;) {
         const uint32_t chunk = (uint32_t)(left > step ? step : left);
         left -= chunk;
@@ -1231,13 +1234,56 @@ extern "C" int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *stream, uint32_
             kp.order_base = ctx->k_base[k];
             kp.n_run = ctx->k_count[k];
             kp.lds_bytes = ctx->k_lds[k];
-            hipError_t he = msim_launch_run(&kp, k, ctx->k_grid[k], ctx->k_block[k], ctx->k_lds[k], first,
-                                            (hipStream_t)stream);
+            uint32_t *clear = nullptr, n_clear = 0;
+            if (claim_base) {
+                kp.claim = claim_base + launch;
+                if (launch == 0) { clear = claim_base; n_clear = MSIM_SCRATCH_WORDS; }
+            } else {
+                kp.claim = ((WsHdr *)ctx->ws)->claim + k;
+                if (first) { clear = ((WsHdr *)ctx->ws)->claim; n_clear = MSIM_KINDS; }
+            }
+            hipError_t he = msim_launch_run(&kp, k, ctx->k_grid[k], ctx->k_block[k], ctx->k_lds[k], clear, n_clear,
+                                            stream);
             if (he != hipSuccess) return hip_fail(ctx, he, "kernel launch");
             first = false;
+            launch++;
         }
     }
     return MSIM_OK;
+}
+
+/* Number of kernel launches msim_run(max_ticks) makes. */
+static uint64_t n_launches(const msim_ctx *ctx, uint32_t max_ticks)
+{
+    const uint64_t step = ctx->max_exp_hops < (1ull << 32) ? max_ticks : MSIM_LAUNCH_TICKS;
+    uint64_t kinds = 0;
+    for (uint32_t k = 0; k < MSIM_KINDS; k++) kinds += ctx->k_count[k] ? 1 : 0;
+    const uint64_t chunks = max_ticks == 0 ? 0 : (max_ticks + step - 1) / step;
+    return chunks * kinds;
+}
+
+extern "C" int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *stream, uint32_t flags)
+{
+    if (!ctx) return MSIM_E_ARG;
+    if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_run before msim_bind");
+    (void)flags;
+    return run_launches(ctx, max_ticks, (hipStream_t)stream, nullptr);
+}
+
+extern "C" int msim_run_noalloc(msim_ctx *ctx, uint32_t max_ticks, void *stream, uint32_t flags)
+{
+    if (!ctx) return MSIM_E_ARG;
+    if (!ctx->bound) return ctx_fail(ctx, MSIM_E_STATE, "msim_run_noalloc before msim_bind");
+    (void)flags;
+    const uint64_t n = n_launches(ctx, max_ticks);
+    if (n > MSIM_SCRATCH_WORDS)
+        return ctx_fail(ctx, MSIM_E_LIMIT, "msim_run_noalloc: the call needs " + std::to_string(n) +
+                                           " kernel launches; its static queue counters hold " +
+                                           std::to_string(MSIM_SCRATCH_WORDS) + " (use msim_run or fewer max_ticks)");
+    uint32_t *words = nullptr;
+    hipError_t he = msim_scratch_words(&words);
+    if (he != hipSuccess) return hip_fail(ctx, he, "scratch symbol address");
+    return run_launches(ctx, max_ticks, (hipStream_t)stream, words);
 }
 
 extern "C" int msim_reset(msim_ctx *ctx, void *stream)

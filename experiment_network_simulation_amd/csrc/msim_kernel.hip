@@ -34,6 +34,7 @@
  */
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "msim_layout.h"
@@ -1906,12 +1907,11 @@ __device__ void megakernel_body(const KParams &kp)
 {
     extern __shared__ __align__(16) uint8_t lds_dyn[];
     __shared__ Shared sh;
-    WsHdr *wh = (WsHdr *)kp.ws;
     const uint64_t *arena_off = (const uint64_t *)(kp.ws + kp.o_arena_off);
     const uint32_t *order = (const uint32_t *)(kp.ws + kp.o_order) + kp.order_base;
     const ExpState *states = (const ExpState *)(kp.ws + kp.o_state);
     for (;;) {
-        if (threadIdx.x == 0) sh.exp = atomicAdd(&wh->claim[KIND], 1u);
+        if (threadIdx.x == 0) sh.exp = atomicAdd(kp.claim, 1u);
         __syncthreads();
         /* the same for every lane: saying so keeps everything derived from it
          * (arena, header fields, per-experiment flags) in scalar registers */
@@ -1964,11 +1964,17 @@ static const void *kernel_of(uint32_t kind)
     }
 }
 
-/* Prepares a launch: resets the experiment queue counters. */
-extern "C" __global__ void msim_prepare(KParams kp)
+/* Prepares launches: zeroes their experiment queue counters (a kernel, not a
+ * memset, so that a captured graph replays it faithfully). */
+extern "C" __global__ void msim_prepare(uint32_t *words, uint32_t n)
 {
-    if (blockIdx.x == 0 && threadIdx.x < MSIM_KINDS) ((WsHdr *)kp.ws)->claim[threadIdx.x] = 0;
+    if (blockIdx.x == 0 && threadIdx.x < n) words[threadIdx.x] = 0;
 }
+
+/* Experiment queue counters of msim_run_noalloc: MSIM_SCRATCH_WORDS words per
+ * GPU, held until the process ends.  Host code never passes this name to a
+ * kernel: it passes the device address msim_scratch_words() looked up. */
+static __device__ __align__(256) uint32_t scratch[MSIM_SCRATCH_WORDS];
 
 /* Restores every experiment to tick 0: copies the pristine mutable part back
  * into each arena, resets progress and clears recorded per-flow ticks. */
@@ -1999,11 +2005,34 @@ extern "C" __global__ void msim_reset_kernel(KParams kp, uint64_t o_rec_all, uin
 
 /* --------------------------------------------------------- host launchers */
 
-extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t kind, uint32_t grid, uint32_t block,
-                                      uint32_t lds, bool prepare, hipStream_t stream)
+/* Device address of `scratch` on the current device, looked up once per
+ * device with that device current. */
+extern "C" hipError_t msim_scratch_words(uint32_t **out)
 {
-    if (prepare) {
-        hipLaunchKernelGGL(msim_prepare, dim3(1), dim3(64), 0, stream, *kp);
+    static std::mutex mu;
+    static uint32_t *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = (uint32_t *)p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+/* Zeroes n_clear (<= 64) queue counters at clear if n_clear > 0, then launches a kernel kind. */
+extern "C" hipError_t msim_launch_run(const KParams *kp, uint32_t kind, uint32_t grid, uint32_t block,
+                                      uint32_t lds, uint32_t *clear, uint32_t n_clear, hipStream_t stream)
+{
+    if (n_clear) {
+        if (n_clear > 64) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(msim_prepare, dim3(1), dim3(64), 0, stream, clear, n_clear);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

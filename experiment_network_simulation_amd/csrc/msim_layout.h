@@ -364,11 +364,17 @@ struct ExpState {        /* 64 bytes */
 struct WsHdr {
     uint32_t claim[MSIM_KINDS]; /* experiment queue counters of a run, one per kernel kind */
     uint32_t n_exp;
-    uint32_t pad[58];
+    uint32_t pad[64 - MSIM_KINDS - 1];
 };
+static_assert(sizeof(WsHdr) == 256, "the workspace's first 256 bytes");
+
+/* msim_run_noalloc: experiment queue counters, one per kernel launch of a
+ * call, in a static device array of this many words instead of the workspace */
+#define MSIM_SCRATCH_WORDS 64   /* msim.h's MSIM_NOALLOC_LAUNCHES */
 
 struct KParams {
     uint8_t *ws;
+    uint32_t *claim;     /* this launch's experiment queue counter, zero when the launch starts */
     uint64_t o_state, o_arena_off, o_order, o_rec_off, o_pristine, o_rw_off;
     uint32_t n_exp;
     uint32_t max_ticks;

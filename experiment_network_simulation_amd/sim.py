@@ -27,7 +27,8 @@ KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h_r1", "msim_megakernel_c8
                 "msim_megakernel_c16w", "msim_megakernel_t", "msim_megakernel_cc", "msim_megakernel_c8h_r1_x",
                 "msim_megakernel_c16h_x", "msim_megakernel_sp"]
 
-EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_reset", "msim_results",
+EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_run_noalloc", "msim_reset",
+            "msim_results",
             "msim_flow_count", "msim_flow_ticks", "msim_task_count", "msim_task_ticks", "msim_get_info",
             "msim_last_error", "msim_destroy", "msim_lds_probe"]
 
@@ -87,6 +88,7 @@ def load_library():
     lib.msim_workspace_size.argtypes = [vp, _P64]
     lib.msim_bind.argtypes = [vp, vp, C.c_uint64, vp]
     lib.msim_run.argtypes = [vp, C.c_uint32, vp, C.c_uint32]
+    lib.msim_run_noalloc.argtypes = [vp, C.c_uint32, vp, C.c_uint32]
     lib.msim_reset.argtypes = [vp, vp]
     lib.msim_results.argtypes = [vp, vp, _P8, _P32, _P64, _P64, _P64]
     lib.msim_flow_count.argtypes = [vp, C.c_uint32, _P64]
@@ -195,6 +197,11 @@ class Sim:
 
     def run(self, max_ticks: int = 0xFFFFFFF0, stream=None):
         self._check(self._lib.msim_run(self._ctx, max_ticks, C.c_void_p(_stream_ptr(stream)), 0))
+
+    def run_noalloc(self, max_ticks: int = 0xFFFFFFF0, stream=None):
+        """msim_run_noalloc: the same run with the queue counters in the
+        library's static device array (no allocation anywhere)."""
+        self._check(self._lib.msim_run_noalloc(self._ctx, max_ticks, C.c_void_p(_stream_ptr(stream)), 0))
 
     def reset(self, stream=None):
         self._check(self._lib.msim_reset(self._ctx, C.c_void_p(_stream_ptr(stream))))

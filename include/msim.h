@@ -280,6 +280,25 @@ int msim_bind(msim_ctx *ctx, void *dev_workspace, uint64_t ws_bytes, void *hip_s
  */
 int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *hip_stream, uint32_t flags);
 
+/*
+ * msim_run_noalloc: msim_run for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, same kernels, same results as msim_run; the
+ * difference is where the kernels' experiment queue counters (one per kernel
+ * launch of the call) live: in a static device array of MSIM_NOALLOC_LAUNCHES
+ * 32-bit words that the library holds on each GPU until the process ends,
+ * instead of the workspace header.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); it zeroes the counters it uses with
+ * a kernel on hip_stream.  The workspace's device must be current.  A call
+ * needing more launches than MSIM_NOALLOC_LAUNCHES (one per kernel kind present
+ * in the batch, times ceil(max_ticks / 2^30) when an experiment moves 2^32 or
+ * more packet-hops) returns MSIM_E_LIMIT and launches nothing.  Every call on
+ * one GPU shares that GPU's counters: calls that overlap on one GPU (other
+ * streams, other host threads, other contexts) race and must not be made.
+ */
+#define MSIM_NOALLOC_LAUNCHES 64u
+int msim_run_noalloc(msim_ctx *ctx, uint32_t max_ticks, void *hip_stream, uint32_t flags);
+
 /* Restores every experiment to tick 0 (asynchronous, on hip_stream). */
 int msim_reset(msim_ctx *ctx, void *hip_stream);
 
