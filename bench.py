@@ -33,8 +33,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_cpu():
+    """Logical CPUs this process may run on, the machine's count, and the model name."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return usable, os.cpu_count() or usable, model
+
+
 def cpu_baseline(batch, gpu_res, sample_ids, threads):
-    """The oracle, untouched, on a sample of experiments, in parallel threads."""
+    """The oracle, untouched, on a sample of experiments, in parallel threads.
+    Returns its packet-hop rate, wall time, packet-hops, experiment-ticks and
+    how many sampled experiments the GPU matched exactly."""
     from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle as O
     ob = O.OracleBatch(batch.pack())
@@ -43,13 +62,26 @@ def cpu_baseline(batch, gpu_res, sample_ids, threads):
         res = list(ex.map(lambda e: O.run(ob, e), sample_ids))
     dt = time.perf_counter() - t0
     hops = sum(r["pkt_hops"] for r in res)
+    ticks = sum(r["t_end"] + 1 for r in res)
     ok = 0
     for e, r in zip(sample_ids, res):
         same = (r["rc"] == 0 and r["status"] == int(gpu_res["status"][e]) and r["t_end"] == int(gpu_res["tick"][e])
                 and r["pkt_hops"] == int(gpu_res["pkt_hops"][e]) and r["digest"] == int(gpu_res["digest"][e])
                 and r["delivered"] == int(gpu_res["delivered"][e]))
         ok += same
-    return hops / dt, dt, hops, ok
+    return hops / dt, dt, hops, ok, ticks
+
+
+def cpu_record(rate, dt, chops, ok, ticks, threads, n_sample, n, gpu_rate):
+    usable, machine, model = host_cpu()
+    return {"value": rate, "unit": "packet-hops/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_sample} of {n} experiments (every {n / n_sample:.0f}th index), run to completion in "
+                      f"{dt:.1f}s ({chops} packet-hops, {ticks} experiment-ticks); GPU results identical on "
+                      f"{ok}/{n_sample}",
+            "per_core": rate / threads, "experiment_ticks_per_s": ticks / dt,
+            "host_cpus_usable": usable, "host_cpus": machine, "host_cpu_model": model,
+            "gpu_over_oracle": gpu_rate / rate if rate else None,
+            "parity_ok": ok, "parity_n": n_sample}
 
 
 def copy_bandwidth(nbytes: int = 1 << 31, reps: int = 5) -> float:
@@ -123,9 +155,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=4, help="workload 1..5 (default 4: k=8 fat-tree, E=4096)")
     ap.add_argument("--n-exp", type=int, default=0, help="first n experiments only (default: the full batch)")
-    ap.add_argument("--cpu-sample", type=int, default=16, help="experiments in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=32,
+                    help="experiments in the CPU-oracle sample, evenly strided over the batch (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--force-global", action="store_true")
+    ap.add_argument("--no-ring-path", action="store_true",
+                    help="run ring-only experiments on the general compact kernels instead of the ring kernel")
+    ap.add_argument("--max-ticks", type=int, default=0xFFFFFFF0,
+                    help="tick budget of each run (default: to completion); a run that ends incomplete fails")
     ap.add_argument("--chunk", type=int, default=0,
                     help="run the batch in chunks of this many experiments, compiling the next chunk while the "
                          "current one runs (default: whole batch; C5 beyond 2048 experiments: 2048)")
@@ -169,7 +206,7 @@ def main():
     batch = I.make_config(cid, n_exp=n)
     log(f"[bench] generated in {time.perf_counter() - t:.1f}s; compiling")
     t = time.perf_counter()
-    sim = Sim(batch, force_global=args.force_global)
+    sim = Sim(batch, force_global=args.force_global, no_ring_path=args.no_ring_path)
     info = sim.info()
     log(f"[bench] compiled in {time.perf_counter() - t:.1f}s: {info}")
     dev = torch.device("cuda:0")
@@ -188,7 +225,7 @@ def main():
         sim.reset(stream)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        sim.run(stream=stream)
+        sim.run(max_ticks=args.max_ticks, stream=stream)
         ev1.record(stream)
         if timed:
             kernel_ms.append((ev0, ev1))
@@ -236,13 +273,14 @@ def main():
         sample = sorted(set(int(round(i * n / k)) for i in range(k)) - {n})
         threads = args.cpu_threads or min(16, os.cpu_count() or 1, len(sample))
         log(f"[bench] CPU oracle on {len(sample)} experiments with {threads} threads")
-        rate, dt, chops, ok = cpu_baseline(batch, res, sample, threads)
-        cpu = {"value": rate, "unit": "packet-hops/s", "cores": threads, "kind": "oracle",
-               "sample": f"{len(sample)} of {n} experiments (evenly spaced indices), run to completion in "
-                         f"{dt:.1f}s ({chops} packet-hops); GPU results identical on {ok}/{len(sample)}",
-               "parity_ok": ok, "parity_n": len(sample)}
+        rate, dt, chops, ok, oticks = cpu_baseline(batch, res, sample, threads)
+        cpu = cpu_record(rate, dt, chops, ok, oticks, threads, len(sample), n, value)
         log(f"[bench] CPU oracle {rate:.3e} packet-hops/s; parity {ok}/{len(sample)}")
 
+    traffic = measured_traffic(KERNEL_NAMES[info["main_kernel"]], cid, n)
+    traffic_src = ("rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel source on this workload, taken in a separate "
+                   "profiled run and stored in profiles/traffic.json, each scaled by a plain copy's calibration"
+                   if traffic is not None else "not measured for this kernel source and workload")
     out = {
         "metric": "packet-hops/sec (batched, 1 GPU) + % of HBM roofline at E=4096",
         "value": value,
@@ -275,7 +313,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(KERNEL_NAMES[info["main_kernel"]], cid, n),
+            "traffic": traffic,
+            "traffic_source": traffic_src,
             "kernel": KERNEL_NAMES[info["main_kernel"]],
             "kernel_ms_avg": k_avg_s * 1e3,
             "alg_bytes_per_launch": alg_bytes,
@@ -309,7 +348,7 @@ def chunked_bench(args, cid, n, chunk):
 
     def compile_chunk(k):
         b = I.make_config(cid, exp_ids=ids[k])
-        return b, Sim(b, force_global=args.force_global)
+        return b, Sim(b, force_global=args.force_global, no_ring_path=args.no_ring_path)
 
     res_all = {k: [] for k in ("status", "tick", "pkt_hops", "delivered", "digest")}
     k_ms, kernels = [], set()
@@ -351,11 +390,8 @@ def chunked_bench(args, cid, n, chunk):
         threads = args.cpu_threads or min(16, os.cpu_count() or 1, len(sample))
         sb = I.make_config(cid, exp_ids=sample)
         sres = {key: v[sample] for key, v in res.items()}
-        rate, dt, chops, ok = cpu_baseline(sb, sres, list(range(len(sample))), threads)
-        cpu = {"value": rate, "unit": "packet-hops/s", "cores": threads, "kind": "oracle",
-               "sample": f"{len(sample)} of {n} experiments (evenly spaced indices), run to completion in "
-                         f"{dt:.1f}s ({chops} packet-hops); GPU results identical on {ok}/{len(sample)}",
-               "parity_ok": ok, "parity_n": len(sample)}
+        rate, dt, chops, ok, oticks = cpu_baseline(sb, sres, list(range(len(sample))), threads)
+        cpu = cpu_record(rate, dt, chops, ok, oticks, threads, len(sample), n, hops / k_s)
         log(f"[bench] CPU oracle {rate:.3e} packet-hops/s; parity {ok}/{len(sample)}")
     copy_gbs = copy_bandwidth()
     log(f"[bench] device copy {copy_gbs:.0f} GB/s (read + write)")

@@ -131,6 +131,19 @@ uint32_t first_flow_size(const Grp &g, uint32_t idx)
     return g.X / g.N + (k < g.X % g.N ? 1u : 0u);
 }
 
+/* Whether the groups fit the ring format: ring channels without gates, few
+ * enough to index in a descriptor, each with flows that fit its fields. */
+bool ngrp_fits_ring(const std::vector<Grp> &grp)
+{
+    if (grp.empty() || grp.size() > RING_MAX_GRP) return false;
+    for (const Grp &g : grp) {
+        if (g.kind != GK_RING_AR && g.kind != GK_RING_AG) return false;
+        if (g.link != MSIM_NONE || g.N > RING_MAX_N || (uint64_t)g.R * g.S > C_POS_MASK) return false;
+        if (g.p >= 65535u || g.X / g.N + 1 >= 65535u) return false;
+    }
+    return true;
+}
+
 /* Launch bound of each kernel kind (threads per workgroup). */
 uint32_t kind_max_threads(uint32_t kind)
 {
@@ -139,7 +152,7 @@ uint32_t kind_max_threads(uint32_t kind)
     return 1024u;
 }
 
-int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compiled &out)
+int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool allow_ring, Compiled &out)
 {
     const uint32_t t = s->exp_topo[e], w = s->exp_work[e];
     if (t >= s->n_topo || w >= s->n_work) return fail(out, MSIM_E_INVALID_SPEC, "experiment %u: topology/workload index out of range", e);
@@ -558,6 +571,118 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, Compil
     out.n_conns = nconn;
     out.n_ports = n_ports;
 
+    /* ---- ring layout: rings only at rate 1 on small switches, where the
+     * experiment qualifies (the limits of msim_layout.h's ring format) */
+    if (allow_compact && allow_ring && n_task == 0 && cc == MSIM_CC_NONE && lb == MSIM_LB_ECMP && maxr == 1 &&
+        Q <= RING_MAX_Q && ngrp_fits_ring(grp) && nconn > 0) {
+        uint32_t maxdeg = 1, max_out = 0, n_sw = 0;
+        for (uint32_t n = 0; n < nn; n++)
+            if (layer[n] != 0) { maxdeg = std::max(maxdeg, deg[n]); n_sw++; }
+        for (uint32_t h = 0; h < n_hosts; h++) max_out = std::max(max_out, host[h].n_out);
+        bool ok = maxdeg <= RING_MAX_DEG && max_out <= RING_MAX_PAIRS;
+        for (const Conn &cn : conn) ok = ok && cn.links >= 1 && cn.links - 1 <= RING_MAX_HOPS;
+        const uint32_t SB = ((n_hosts + 63) / 64) * 64;
+        std::vector<uint32_t> slot(n_ports), sw_of(nn, MSIM_NONE);
+        uint32_t nt = SB, k_sw = 0;
+        for (uint32_t n = 0; n < nn && ok; n++) {
+            if (layer[n] == 0) { slot[pbase[n]] = host_of[n]; continue; }
+            if ((nt & 63) + deg[n] > 64) nt = (nt + 63) & ~63u;
+            sw_of[n] = k_sw++;
+            for (uint32_t q = pbase[n]; q < pbase[n + 1]; q++) slot[q] = nt++;
+        }
+        ok = ok && nt <= 1024;
+        if (ok) {
+            const uint32_t S = nt - SB;
+            ArenaHdr3 H{};
+            H.mode = MODE_RING; H.n_flows = (uint32_t)n_flows;
+            H.nt = nt; H.H = n_hosts; H.SB = SB; H.Q = Q; H.W = W; H.n_grp = ngrp; H.n_sw = n_sw;
+            size_t off = align16(sizeof(ArenaHdr3));
+            auto take = [&](uint32_t &field, size_t bytes) { field = (uint32_t)off; off = align16(off + bytes); };
+            take(H.o_grp, sizeof(RGrp) * ngrp);
+            H.rw_off = (uint32_t)off;
+            take(H.o_pair, sizeof(RPair) * (size_t)max_out * SB);
+            take(H.o_pdesc, 4ull * Q * S);
+            take(H.o_pnxt, (size_t)Q * S);
+            take(H.o_head, 64ull * n_sw);
+            take(H.o_nzw, 32ull * n_sw);
+            take(H.o_fw, 4ull * S);
+            take(H.o_pub, 8ull * nt);
+            take(H.o_sdesc, 4ull * W * nt);
+            H.lds_bytes = (uint32_t)off;
+            take(H.o_port, sizeof(RingPort) * nt);
+            take(H.o_priv, sizeof(RingPriv) * nt);
+            H.bytes = (uint32_t)off;
+            if (H.lds_bytes <= COMPACT_LDS_LIMIT) {
+                out.arena.assign(off, 0);
+                uint8_t *A = out.arena.data();
+                /* flow sizes: p in every round but the last, whose chunk k holds X/N + [k < X mod N] */
+                auto size_at = [](const Grp &g, uint32_t r, uint32_t pos) -> uint32_t {
+                    const uint32_t T1 = (g.R - 1) * g.S;
+                    if (pos < T1) return g.p;
+                    const uint32_t k = ring_chunk(g.kind, g.N, r, pos - T1);
+                    return g.X / g.N + (k < g.X % g.N ? 1u : 0u);
+                };
+                RGrp *rg = (RGrp *)(A + H.o_grp);
+                for (uint32_t k = 0; k < ngrp; k++) {
+                    const Grp &g = grp[k];
+                    rg[k].fid_base = g.fid_base; rg[k].N = g.N; rg[k].S = g.S; rg[k].RS = g.R * g.S;
+                    rg[k].p = g.p; rg[k].Xq = g.X / g.N;
+                    rg[k].T = 0;
+                    for (uint32_t b = 0; b < 3 * g.N; b++)
+                        if (b % g.N < g.X % g.N) rg[k].T |= 1u << b;
+                    rg[k].mS = (uint32_t)(((1ull << 24) + g.S - 1) / g.S);
+                }
+                RPair *pairs = (RPair *)(A + H.o_pair);
+                for (uint32_t h = 0; h < n_hosts; h++) {
+                    for (uint32_t k = 0; k < host[h].n_out; k++) {
+                        const uint32_t c = hout[host[h].out_off + k];
+                        const Conn &cn = conn[c];
+                        const Grp &g = grp[cn.grp];
+                        const uint32_t i = cn.idx, ri = i == 0 ? g.N - 1 : i - 1;
+                        /* the destination's pair whose partner is this connection */
+                        const uint32_t kdst = conn[g.conn_base + (i + 1) % g.N].lidx;
+                        uint32_t route3 = 0;
+                        for (uint32_t hop = 0; hop + 1 < cn.links; hop++)
+                            route3 |= ((cn.route >> (4 * hop)) & 7u) << (3 * hop);
+                        RPair &pp = pairs[(size_t)k * SB + h];
+                        pp.snd = (CS_ACTIVE << 30) | size_at(g, i, 0);
+                        pp.rcv = 0;
+                        pp.desc = route3 | (kdst << RD_PAIR_SHIFT) | (cn.grp << RD_GRP_SHIFT) | RD_VALID;
+                        pp.gi = cn.grp | (i << 10) | (ri << 20);
+                    }
+                }
+                memset(A + H.o_head, (int)Q_EMPTY, 64ull * n_sw);
+                RingPort *rp = (RingPort *)(A + H.o_port);
+                RingPriv *rv = (RingPriv *)(A + H.o_priv);
+                for (uint32_t q = 0; q < n_ports; q++) {
+                    const PortRO &P = port[q];
+                    const uint32_t sl = slot[q], fq = P.peer;
+                    RingPort &r = rp[sl];
+                    r.peer = slot[fq];
+                    r.flags = (uint8_t)(PF_USED | (P.alive ? PF_ALIVE : 0) | (P.is_host ? PF_HOST : 0) |
+                                        (P.peer_is_host ? PF_PEER_HOST : 0));
+                    r.local = P.local; r.deg = P.deg; r.delay = P.delay;
+                    if (P.is_host) {
+                        r.row = host[P.host].n_out;
+                        rv[sl].mask = host[P.host].n_out == 32 ? ~0u : ((1u << host[P.host].n_out) - 1u);
+                        rv[sl].tails = left[P.host];
+                    } else {
+                        r.row = sw_of[port_node[q]] * 8;
+                        rv[sl].mask = (1u << Q) - 1u;
+                    }
+                }
+                memcpy(A, &H, sizeof H);
+                out.rw_off = H.rw_off;
+                out.bytes = H.bytes;
+                out.lds_bytes = H.lds_bytes;
+                out.compact = true;
+                out.kind = KIND_RING;
+                out.nt = nt;
+                return MSIM_OK;
+            }
+        }
+    }
+
     /* ---- compact layout, where the experiment qualifies (no task graph, no
      * congestion control, ECMP) */
     if (allow_compact && n_task == 0 && cc == MSIM_CC_NONE && lb == MSIM_LB_ECMP) {
@@ -956,7 +1081,7 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
         for (;;) {
             uint32_t e = next.fetch_add(1);
             if (e >= E) break;
-            compile_exp(spec, e, !ctx->force_global, ctx->exps[e]);
+            compile_exp(spec, e, !ctx->force_global, !(opts && opts->no_ring_path), ctx->exps[e]);
         }
     };
     std::vector<std::thread> th;

@@ -7,30 +7,37 @@
  * moves every thread of the grid through one system at a time over all
  * experiments, each workgroup here claims one experiment at a time and runs its
  * whole tick loop alone: experiments never interact (single-process
- * multi-experiment, Multiverse section 2.2), so the only synchronisation is the
- * workgroup barrier between the two phases of a tick.  The experiment's state
+ * multi-experiment, Multiverse section 2.2), so the only synchronisation is a
+ * workgroup barrier between the phases of a tick.  The experiment's state
  * is copied into LDS when it fits and worked on in place in HBM otherwise.
  *
- * Tick t (the step order of Multiverse section 3.2 -- Schedule, Send, NIC send,
- * Forward, Transmit, NIC receive -- folded into two phases):
- *   phase A, one thread per port (ingress side):
- *     switch ingress: frees the buffer slots its egresses popped last tick,
- *       appends the packets arriving at tick t to their virtual output queue
- *       (the per-ingress to-do set of pull-based forwarding, section 4.2) and
- *       publishes how many packets have left it (the credit its feeder sees);
- *     host: takes delivery of arriving packets (a flow is received when its
- *       last packet lands), then activates every connection whose next flow has
- *       its predecessors met (the Schedule system, section 3.2).
- *   barrier
- *   phase D, one thread per port (output side), rounds m < rate:
- *     the output pulls from the ingresses of its node -- first eligible one
- *     going round from its round-robin pointer -- or, at a host, from its
- *     active connections, while credit (buffer room downstream) lasts, and
- *     writes the packet into the staging slot of the far ingress for tick
- *     t + delay.
- *   barrier
- * Every datum has one writer per phase (see msim_layout.h), so no atomics are
- * used inside the tick loop; the experiment queue counter is the only atomic.
+ * Tick t follows the step order of Multiverse section 3.2 (Schedule, Send,
+ * NIC send, Forward, Transmit, NIC receive) with the forwarding pull-based as
+ * in its section 4.2: every output pulls from the ingresses of its node.
+ * Each kernel family folds that order into as few barrier-separated phases as
+ * its data layout allows:
+ *   general path (run_experiment): phase A, one thread per port, takes the
+ *     arrivals of tick t (switch ingresses append to their virtual output
+ *     queues; hosts take deliveries and activate the flows they enable);
+ *     barrier; phase D, rounds m < rate, every output grants the first
+ *     eligible input going round from its pointer and stages the packet for
+ *     t + delay; barrier;
+ *   compact and ring paths (run_compact, run_ring): one thread per port with
+ *     every port of a switch inside one wavefront, so arrivals, forwarding
+ *     and (faster links) frees of a tick run in program order within the
+ *     wavefront and one barrier ends the tick.
+ * Writers.  Most state has one writer per phase.  The exceptions are LDS
+ * atomics between the ports of one switch, inside one wavefront: on the
+ * rate-1 compact path an output hands the slot it popped back to its ingress
+ * (OR) and counts the pop (add); on the ring path an output hands back the
+ * slot and an emptied-queue bit (OR) and counts the pop (add), and an ingress
+ * marks a queue non-empty in its output's word (OR).  Several ports of a
+ * switch may hit the same word in one instruction; OR and add do not depend on
+ * the order they are applied in, so results are identical on every run.  The
+ * other atomics: each workgroup claiming its next experiment, the general
+ * path's congestion-control ACK-pending masks (OR) and task-graph counts
+ * (subtract), and the periodic completion checks of the compact path (OR,
+ * max).
  */
 #include <hip/hip_runtime.h>
 
@@ -1877,6 +1884,357 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     __syncthreads();
 }
 
+/* ==================================================================== *
+ * Ring path: rings only (at most 10 ranks), every link at rate 1, switches
+ * of at most 8 ports, buffers of at most 16 packets (the ring format of
+ * msim_layout.h).
+ *
+ * One thread per port and one workgroup barrier per tick, as on the compact
+ * path.  With a dozen wavefronts sharing a CU's four SIMDs, the tick is bound
+ * by the vector instructions all of them issue (every wavefront runs each
+ * branch any of its lanes needs), so this path is built to keep that count
+ * low:
+ *   - a host's flow events touch one 16-byte pair record it alone owns and
+ *     the ring-channel record the arriving descriptor names, read in two
+ *     rounds; the last-round chunk sizes come from a precomputed bit mask;
+ *   - a switch ingress keeps its queues' tails, non-empty bits and free slots
+ *     in registers, and takes the egress from the descriptor, which carries
+ *     the remaining route;
+ *   - a switch output finds its candidates in an 8-bit word of non-empty
+ *     inputs, pops from the head slot row, and hands the freed slot (and an
+ *     emptied queue) back to the ingress with one LDS atomic OR, which the
+ *     ingress folds in once at the end of the tick, publishing its pop count
+ *     for the credit its feeder reads next tick.
+ * The atomic ORs are the one many-to-one write: up to 8 outputs of a switch
+ * may hand back slots of the same ingress, or mark the same output's word,
+ * in one instruction.  OR is order-independent, so results do not depend on
+ * the order the LDS applies them.
+ * ==================================================================== */
+
+/* First set bit of mask (nonzero) at or after bit rr, cyclically over 32 bits. */
+__device__ __forceinline__ uint32_t first_ready(uint32_t mask, uint32_t rr)
+{
+    const uint32_t rot = __builtin_amdgcn_alignbit(mask, mask, rr);   /* mask rotated right by rr */
+    return (rr + (uint32_t)__builtin_ctz(rot | (rot == 0 ? 1u : 0u))) & 31u;
+}
+
+/* Packets of the flow at position pos of the connection whose rank r gives
+ * r2N = r + 2N: p in every round but the last; in the last round the chunk
+ * (r - step) mod N holds Xq plus bit r + 2N - step of T. */
+__device__ __forceinline__ uint32_t rsize(const RGrp &g, uint32_t r2N, uint32_t pos)
+{
+    const uint32_t T1 = g.RS - g.S;
+    return pos < T1 ? g.p : g.Xq + ((g.T >> (r2N - (pos - T1))) & 1u);
+}
+
+__device__ __forceinline__ uint32_t rfid(const RGrp &g, uint32_t r, uint32_t pos)
+{
+    return g.fid_base + __umul24(pos, g.N) + r;  /* pos < 2^14, N <= 10 */
+}
+
+__device__ __forceinline__ RGrp rgrp_load(const LDSP RGrp *p)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 a = ((const LDSP u32x4 *)p)[0], b = ((const LDSP u32x4 *)p)[1];
+    RGrp g;
+    g.fid_base = a.x; g.N = a.y; g.S = a.z; g.RS = a.w; g.p = b.x; g.Xq = b.y; g.T = b.z; g.mS = b.w;
+    return g;
+}
+
+__device__ __forceinline__ RPair rpair_load(const LDSP RPair *p)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 a = *(const LDSP u32x4 *)p;
+    RPair r;
+    r.snd = a.x; r.rcv = a.y; r.desc = a.z; r.gi = a.w;
+    return r;
+}
+
+#define RP_REM(w) ((w) & 0xFFFFu)
+#define RP_POS(w) (((w) >> 16) & C_POS_MASK)
+#define RP_ST(w) ((w) >> 30)
+#define GI_GRP(w) ((w) & 1023u)
+#define GI_RANK(w) (((w) >> 10) & 1023u)
+#define GI_PRED(w) ((w) >> 20)
+
+__device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
+{
+    const uint32_t tid = threadIdx.x, nth = blockDim.x;
+    const uint32_t lane = tid & 63, wave = tid >> 6, nwaves = (nth + 63) >> 6;
+    ExpState *stp = (ExpState *)(kp.ws + kp.o_state) + x;
+    const ArenaHdr3 *H = (const ArenaHdr3 *)arena_g;
+    const uint32_t lds_bytes = H->lds_bytes, rw_off = H->rw_off;
+    {
+        const uint4 *src = (const uint4 *)arena_g;
+        uint4 *dst = (uint4 *)lds;
+        for (uint32_t i = tid; i < lds_bytes / 16; i += nth) dst[i] = src[i];
+    }
+    const uint32_t nt = H->nt, SB = H->SB, Q = H->Q, W = H->W, n_flows = H->n_flows;
+    const uint32_t S = nt - SB;                      /* switch slots: pool stride */
+    LDSP uint8_t *L = (LDSP uint8_t *)lds;
+    const LDSP RGrp *grp = (const LDSP RGrp *)(L + H->o_grp);
+    LDSP RPair *pair = (LDSP RPair *)(L + H->o_pair);
+    LDSP uint32_t *pdesc = (LDSP uint32_t *)(L + H->o_pdesc);
+    LDSP uint8_t *pnxt = L + H->o_pnxt;
+    LDSP uint8_t *head = L + H->o_head;
+    LDSP uint32_t *nzw = (LDSP uint32_t *)(L + H->o_nzw);
+    LDSP uint32_t *fw = (LDSP uint32_t *)(L + H->o_fw);
+    LDSP uint32_t *pub = (LDSP uint32_t *)(L + H->o_pub);
+    LDSP uint32_t *sdesc = (LDSP uint32_t *)(L + H->o_sdesc);
+    uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
+    uint32_t *rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
+
+    const bool used = tid < nt;
+    RingPort pr = {};
+    RingPriv pv = {};
+    if (used) {
+        pr = ((const RingPort *)(arena_g + H->o_port))[tid];
+        pv = ((const RingPriv *)(arena_g + H->o_priv))[tid];
+    }
+    const bool is_host = (pr.flags & (PF_USED | PF_HOST)) == (PF_USED | PF_HOST);
+    const bool is_sw = (pr.flags & (PF_USED | PF_HOST)) == PF_USED;
+    const bool alive = pr.flags & PF_ALIVE;
+    const bool peer_host = pr.flags & PF_PEER_HOST;
+    const bool feeds_sw = alive && !peer_host;                  /* its output has a credit to respect */
+    const uint32_t local = pr.local, deg = pr.deg;
+    const uint32_t n_out = is_host ? pr.row : 0u;
+    const uint32_t row = is_sw ? pr.row + local : 0u;          /* this port's switch row */
+    const uint32_t pool = is_sw ? tid - SB : 0u;               /* this ingress's buffer pool */
+    const uint32_t pool0 = is_sw ? tid - local - SB : 0u;      /* pool of its switch's port 0 */
+    const uint32_t hb0 = pr.row * 8u + local;                  /* head byte of queue (this ingress -> output 0) */
+    const uint32_t doff = pr.delay * nt, wsz = W * nt;
+    uint32_t pushed = pv.pushed, rr = pv.rr, mask = pv.mask, tails = pv.tails, ne = pv.ne, popped = pv.popped;
+    const uint32_t pushed0 = pushed;
+
+    uint32_t delivered = 0, tmax = 0, last_tx1 = 0, last_act1 = 0, fault = 0;
+    uint64_t digest = 0;
+    uint32_t left = is_host ? tails : 0u;
+    __syncthreads();
+
+    const uint32_t t0 = stp->t_now;
+    const uint32_t t_end = (uint64_t)t0 + kp.max_ticks > 0xFFFFFFF0ull ? 0xFFFFFFF0u : t0 + kp.max_ticks;
+    const uint32_t hist = max(max(stp->last_tx1, stp->last_act1), stp->max_arr);
+    /* every pair's first flow is active from tick 0 (the initial image says so) */
+    if (t0 == 0 && is_host && n_out) {
+        last_act1 = 1;
+        if (rec)
+            for (uint32_t k = 0; k < n_out; k++) {
+                const uint32_t gi = pair[k * SB + tid].gi;
+                rec[n_flows + rfid(rgrp_load(grp + GI_GRP(gi)), GI_RANK(gi), 0)] = 0;
+            }
+    }
+    LDSP RPair *pair_me = pair + tid;                          /* a host's pair records */
+    uint32_t t = t0, par = 0, sb = (t0 % W) * nt;
+    bool done = false, dead = false;
+    uint32_t t_dead = 0;
+    while (t < t_end) {
+        const uint32_t cw = (t & 1u) * nt, cr = cw ^ nt;           /* pop counts: this tick's / last tick's */
+        uint32_t dst = sb + doff;
+        if (dst >= wsz) dst -= wsz;
+        dst += pr.peer;
+        if (is_sw) {
+            /* ---- round 1: the arriving packet; the far ingress's pops through t-1 */
+            const uint32_t e = sdesc[sb + tid];
+            uint32_t pf = 0;
+            if (feeds_sw) pf = pub[cr + pr.peer];
+            /* arrival: append to the queue toward the egress the descriptor names */
+            if (e != 0) {
+                const uint32_t o = e & 7u;
+                if (mask == 0 || o >= deg) {
+                    fault = 1;
+                } else {
+                    const uint32_t s = (uint32_t)__builtin_ctz(mask);
+                    mask &= mask - 1;
+                    const uint32_t a = __umul24(s, S) + pool;
+                    pdesc[a] = (e & ~RD_ROUTE_MASK) | ((e >> 3) & (RD_ROUTE_MASK >> 3));
+                    pnxt[a] = (uint8_t)Q_EMPTY;
+                    if (ne & (1u << o)) {
+                        pnxt[__umul24((tails >> (4 * o)) & 15u, S) + pool] = (uint8_t)s;
+                    } else {
+                        head[hb0 + 8 * o] = (uint8_t)s;
+                        __hip_atomic_fetch_or(nzw + pr.row + o, 1u << local, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                    tails = (tails & ~(15u << (4 * o))) | (s << (4 * o));
+                    ne |= 1u << o;
+                }
+            }
+            wave_lds_fence();
+            /* ---- round 2: forwarding.  Candidates: the inputs whose queue
+             * toward this output holds a packet; the grant goes to the first
+             * from rr; credit is the far ingress's room as of the end of the
+             * last tick */
+            uint32_t out = 0;
+            if (alive) {
+                uint32_t nz = nzw[row];
+                uint64_t hrow = *(const LDSP uint64_t *)(head + row * 8u);
+                pin(nz); pin(hrow);
+                if (nz != 0 && (!feeds_sw || pushed - pf < Q)) {
+                    const uint32_t rot = (nz | (nz << 8)) >> rr;
+                    const uint32_t i = (rr + (uint32_t)__builtin_ctz(rot)) & 7u;
+                    const uint32_t s = (uint32_t)(hrow >> (8 * i)) & 0xFFu;
+                    const uint32_t qa = __umul24(s, S) + pool0 + i;
+                    /* ---- round 3: the packet and its successor in the queue */
+                    const uint32_t d = pdesc[qa];
+                    const uint32_t nx = pnxt[qa];
+                    head[row * 8u + i] = (uint8_t)nx;
+                    const bool emptied = nx == Q_EMPTY;
+                    __hip_atomic_fetch_or(fw + pool0 + i, (1u << s) | (emptied ? 1u << (16 + local) : 0u),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    if (emptied) nzw[row] = nz & ~(1u << i);
+                    out = d;
+                    pushed++;
+                    last_tx1 = t + 1;
+                    rr = i + 1 == deg ? 0u : i + 1;
+                }
+                sdesc[dst] = out;
+            }
+            wave_lds_fence();
+            /* ---- round 4: what the outputs of this switch took from this
+             * ingress during the tick; its pop count for tick t + 1 */
+            const uint32_t w = fw[pool];
+            if (w != 0) {
+                fw[pool] = 0;
+                mask |= w & 0xFFFFu;
+                ne &= ~(w >> 16);
+                popped += (uint32_t)__builtin_popcount(w & 0xFFFFu);
+            }
+            pub[cw + tid] = popped;
+        } else if (is_host) {
+            /* ---- round 1: the arriving packet, the far ingress's pops, and
+             * the first ready pair with, if its flow is about to finish
+             * sending, its channel */
+            const uint32_t e = sdesc[sb + tid];
+            uint32_t pf = 0;
+            if (alive) pf = pub[cr + pr.peer];
+            const bool any = mask != 0;
+            const uint32_t j = first_ready(mask, rr);
+            RPair pj;
+            RGrp gj;
+            if (any) pj = rpair_load(pair_me + __umul24(j, SB));
+            if (any && RP_REM(pj.snd) == 1u) gj = rgrp_load(grp + GI_GRP(pj.gi));
+            if (e != 0) delivered++;
+            /* ---- round 2, when a flow's last packet arrives: its pair and
+             * ring channel */
+            const uint32_t k = (e >> RD_PAIR_SHIFT) & 31u;
+            RPair pk;
+            RGrp gk;
+            bool woke = false;
+            if (e & RD_LAST) {
+                pk = rpair_load(pair_me + __umul24(k, SB));
+                gk = rgrp_load(grp + ((e >> RD_GRP_SHIFT) & 1023u));
+                /* the flow is received: RD = t */
+                const uint32_t ri = GI_PRED(pk.gi), rpos = pk.rcv;
+                const uint32_t fid = rfid(gk, ri, rpos);
+                digest += mix64(((uint64_t)fid << 32) | t);
+                tmax = t;
+                left--;
+                if (rpos >= gk.RS) fault = 1;                     /* a flow no one sends */
+                if (rec) rec[fid] = t;
+                const uint32_t np = rpos + 1u;
+                pk.rcv = np;
+                pair_me[__umul24(k, SB)].rcv = np;
+                /* the partner's next send waits on this receive (it is idle
+                 * only at a step > 0 of a round: step 0 waits on nothing but
+                 * its own last send) */
+                const uint32_t spos = RP_POS(pk.snd);
+                if (RP_ST(pk.snd) == CS_IDLE && np >= spos) {
+                    const uint32_t i = GI_RANK(pk.gi);
+                    pk.snd = (CS_ACTIVE << 30) | (spos << 16) | rsize(gk, i + 2u * gk.N, spos);
+                    mask |= 1u << k;
+                    last_act1 = t + 1;
+                    if (rec) rec[n_flows + rfid(gk, i, spos)] = t;
+                    pair_me[__umul24(k, SB)].snd = pk.snd;
+                    woke = true;
+                }
+            }
+            /* ---- the NIC: one packet of the first ready pair from rr, while
+             * the far ingress has room.  That pair is j, read before the
+             * barrier, unless a pair woken above comes first. */
+            uint32_t out = 0;
+            if (alive && mask != 0 && pushed - pf < Q) {
+                const uint32_t c = !any ? k : (woke && ((k - rr) & 31u) < ((j - rr) & 31u)) ? k : j;
+                const bool usek = (e & RD_LAST) && c == k;
+                uint32_t snd = usek ? pk.snd : pj.snd;
+                out = (usek ? pk.desc : pj.desc) | (RP_REM(snd) == 1u ? RD_LAST : 0u);
+                pushed++;
+                last_tx1 = t + 1;
+                rr = c + 1u == n_out ? 0u : c + 1u;
+                if (RP_REM(snd) == 1u) {
+                    /* the flow's last packet leaves: SD = t + 1 */
+                    const uint32_t gi = usek ? pk.gi : pj.gi, rpos = usek ? pk.rcv : pj.rcv;
+                    const RGrp g = usek ? gk : gj;
+                    const uint32_t spos = RP_POS(snd), np = spos + 1u;
+                    mask &= ~(1u << c);
+                    if (rec) rec[2 * n_flows + rfid(g, GI_RANK(gi), spos)] = t + 1;
+                    if (np >= g.RS) {
+                        snd = (CS_DONE << 30) | (np << 16);
+                    } else {
+                        /* the next flow starts at t + 1 if its receive
+                         * predecessor (the partner's flow np - 1) is in, or
+                         * if it opens a round; otherwise it waits for it */
+                        const uint32_t step = np - __umul24(__umulhi(np << 8, g.mS), g.S);
+                        if (step == 0 || rpos >= np) {
+                            snd = (CS_ACTIVE << 30) | (np << 16) | rsize(g, GI_RANK(gi) + 2u * g.N, np);
+                            mask |= 1u << c;
+                            last_act1 = t + 2;
+                            if (rec) rec[n_flows + rfid(g, GI_RANK(gi), np)] = t + 1;
+                        } else {
+                            snd = (CS_IDLE << 30) | (np << 16);
+                        }
+                    }
+                } else {
+                    snd -= 1u;
+                }
+                pair_me[__umul24(c, SB)].snd = snd;
+            }
+            if (alive) sdesc[dst] = out;
+        }
+        t++;
+        sb += nt;
+        if (sb == wsz) sb = 0;
+        if (((t - t0) & ((t - t0) < CHECK_LONG ? CHECK_EVERY - 1u : CHECK_EVERY_LONG - 1u)) == 0 || t == t_end) {
+            const uint32_t max_arr = last_tx1 ? last_tx1 - 1 + pr.delay : 0;
+            const uint32_t anyl = __ballot(left > 0) != 0ull;
+            const uint32_t ts = wave_max_u32(max(max(last_tx1, last_act1), max_arr));
+            /* one slot per wavefront and parity, rewritten by every check of
+             * that parity; the reads of a check end before the next check's
+             * barrier, so the next write to the same parity cannot race them */
+            if (lane == 0) { sh.chk_any[par][wave] = anyl; sh.chk_max[par][wave] = ts; }
+            __syncthreads();
+            uint32_t anyw = 0, tsw = hist;
+            for (uint32_t w = 0; w < nwaves; w++) { anyw |= sh.chk_any[par][w]; tsw = max(tsw, sh.chk_max[par][w]); }
+            par ^= 1;
+            if (!anyw) { done = true; break; }
+            if (tsw <= t - 1) { dead = true; t_dead = tsw; break; }
+        } else {
+            __syncthreads();
+        }
+    }
+
+    const uint32_t max_arr = last_tx1 ? last_tx1 - 1 + pr.delay : 0;
+    {
+        const uint4 *src = (const uint4 *)(lds + rw_off);
+        uint4 *dst = (uint4 *)(arena_g + rw_off);
+        for (uint32_t i = tid; i < (lds_bytes - rw_off) / 16; i += nth) dst[i] = src[i];
+    }
+    if (used) {
+        pv.pushed = pushed; pv.rr = rr; pv.mask = mask; pv.ne = ne; pv.popped = popped;
+        pv.tails = is_host ? left : tails;
+        ((RingPriv *)(arena_g + H->o_priv))[tid] = pv;
+    }
+    uint64_t s0 = wave_sum_u64(pushed - pushed0), s1 = wave_sum_u64(delivered), s2 = wave_sum_u64(digest);
+    uint32_t m0 = wave_max_u32(tmax), m1 = wave_max_u32(last_tx1), m2 = wave_max_u32(last_act1),
+             m3 = wave_max_u32(max_arr), m4 = wave_max_u32(fault);
+    if (lane == 0) {
+        sh.sum[0][wave] = s0; sh.sum[1][wave] = s1; sh.sum[2][wave] = s2;
+        sh.mx[0][wave] = m0; sh.mx[1][wave] = m1; sh.mx[2][wave] = m2; sh.mx[3][wave] = m3; sh.mx[4][wave] = m4;
+    }
+    __syncthreads();
+    if (tid == 0) finish_state(stp, sh, nwaves, t, done, dead, t_dead);
+    __syncthreads();
+}
+
 /* Kernel kinds: the general path (plain, with tasks, with congestion control),
  * and the compact path for 8- or 16-byte queue rows and 16- or 32-bit packet
  * descriptors, two of them also with trees, send/recv groups and gated rings.
@@ -1888,6 +2246,8 @@ __device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *
         constexpr bool T = KIND != 0, CC = KIND == KIND_GENERAL_CC, SP = KIND == KIND_GENERAL_SPRAY;
         if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true, T, CC, SP>(kp, x, arena, lds, sh);
         else run_experiment<false, T, CC, SP>(kp, x, arena, lds, sh);
+    } else if constexpr (KIND == KIND_RING) {
+        run_ring(kp, x, arena, lds, sh);
     } else if constexpr (KIND == KIND_COMPACT_X8) {
         run_compact<1, uint16_t, true, true>(kp, x, arena, lds, sh);
     } else if constexpr (KIND == KIND_COMPACT_X16) {
@@ -1943,6 +2303,8 @@ extern "C" __global__ void __launch_bounds__(768) msim_megakernel_c8h_r1_x(KPara
 extern "C" __global__ void __launch_bounds__(768) msim_megakernel_c16h_x(KParams kp) { megakernel_body<KIND_COMPACT_X16>(kp); }
 /* the general path with packet spraying (and a task graph if the experiment has one) */
 extern "C" __global__ void __launch_bounds__(512) msim_megakernel_sp(KParams kp) { megakernel_body<KIND_GENERAL_SPRAY>(kp); }
+/* rings only at rate 1 on switches of at most 8 ports (the ring format) */
+extern "C" __global__ void __launch_bounds__(1024) msim_megakernel_ring(KParams kp) { megakernel_body<KIND_RING>(kp); }
 
 static const void *kernel_of(uint32_t kind)
 {
@@ -1960,6 +2322,7 @@ static const void *kernel_of(uint32_t kind)
     case KIND_GENERAL_CC: return (const void *)msim_megakernel_cc;
     case KIND_COMPACT_X8: return (const void *)msim_megakernel_c8h_r1_x;
     case KIND_COMPACT_X16: return (const void *)msim_megakernel_c16h_x;
+    case KIND_RING: return (const void *)msim_megakernel_ring;
     default: return (const void *)msim_megakernel_sp;
     }
 }

@@ -8,8 +8,10 @@
  * cursors).  The same byte offsets are valid whether the arena is used in HBM
  * or copied into a workgroup's LDS, so one kernel serves both placements.
  *
- * State owners (each datum has exactly one writer per phase, so the tick loop
- * needs no atomics -- the pull discipline of Multiverse section 4.2):
+ * State owners of the general format (the pull discipline of Multiverse
+ * section 4.2: each datum has one writer per phase; the compact and ring
+ * formats below keep it except for the LDS atomics between the ports of one
+ * switch that msim_kernel.hip lists):
  *  - a switch ingress port q owns its buffer pool (pdesc/pnxt/fstk), the tail
  *    side of its virtual output queues (arr, tslot, fcur, hseen) and popped[q];
  *    it runs in phase A (arrivals, frees);
@@ -338,6 +340,106 @@ struct PortPriv {        /* 144 bytes: registers of a thread slot between runs *
     uint32_t left, pad[3];
 };
 
+/* ---- ring format ----------------------------------------------------------
+ * Experiments whose workload is rings only (at most 10 ranks each), every link
+ * at rate 1, switches of at most 8 ports, buffers of at most 16 packets, paths
+ * of at most 5 switches and at most 32 outgoing connections per host.  Thread
+ * slots as in the compact format.  Everything lives in LDS during a run except
+ * the per-thread registers (RingPriv, saved between runs) and the port table
+ * (RingPort).
+ *
+ * Pairs.  In a ring every host that sends on connection (i -> i+1) of a
+ * channel also receives on (i-1 -> i) of the same channel, and both flow
+ * predecessors of its sends are local: the previous send on the same
+ * connection and the previous receive on its partner.  A host's pair k joins
+ * its k-th outgoing connection (index order: the NIC's round-robin order) with
+ * that partner, so every flow event of a host touches one 16-byte record the
+ * host alone owns.  Record (k, host h) sits at index k * SB + h.
+ *
+ * Descriptor of a packet (32 bits): bits 0..14 the egress port at each
+ * remaining switch of its path, three bits each, the next switch's lowest;
+ * bits 15..19 the pair index at the destination host; bit 20 set on the last
+ * packet of a flow (a connection delivers in order, so its arrival completes
+ * the flow); bits 21..30 the ring channel (group); bit 31 set (a staging word
+ * of 0 means no packet).  A switch ingress stores it with its own hop shifted
+ * out.
+ *
+ * Switch state (row of a port = switch * 8 + local port):
+ *   pdesc[s * S + q], pnxt[s * S + q]  buffer slot s of ingress q (slot-major);
+ *                      pnxt = Q_EMPTY after the last packet of a queue;
+ *   head[row(o) * 8 + i]  head slot of queue (ingress i -> output o), written
+ *                      by the ingress when it appends to an empty queue and by
+ *                      the output when it pops;
+ *   nzw[row(o)]        bit i: queue (ingress i -> output o) holds a packet; set
+ *                      by the ingress (LDS atomic OR: several ingresses of a
+ *                      switch may set bits of one word in one instruction),
+ *                      cleared by the output when it pops the last packet;
+ *   fw[q]              what the outputs of its switch took from ingress q this
+ *                      tick: bit s = buffer slot s freed, bit 16 + o = queue
+ *                      (q -> o) emptied (LDS atomic OR); the ingress folds it
+ *                      into its registers at the end of the tick and clears it;
+ *   pub[t & 1][slot]   packets forwarded out of a switch ingress through tick
+ *                      t, written at the end of tick t: the credit its feeder
+ *                      reads at tick t + 1.
+ * Staging: sdesc[(t mod W) * nt + slot] = descriptor of the packet reaching
+ * that port at tick t, 0 for none, rewritten by its feeder every tick. */
+#define MODE_RING 3u
+#define RING_MAX_DEG 8u
+#define RING_MAX_Q 16u
+#define RING_MAX_PAIRS 32u
+#define RING_MAX_HOPS 5u
+#define RING_MAX_N 10u
+#define RD_ROUTE_MASK 0x7FFFu
+#define RD_PAIR_SHIFT 15
+#define RD_LAST 0x100000u
+#define RD_GRP_SHIFT 21
+#define RD_VALID 0x80000000u
+#define RING_MAX_GRP 1024u
+
+struct ArenaHdr3 {       /* 96 bytes */
+    uint32_t mode, bytes, rw_off, n_flows;
+    uint32_t lds_bytes, nt, H, SB;
+    uint32_t Q, W, n_grp, n_sw;
+    uint32_t o_grp, o_pair, o_pdesc, o_pnxt;
+    uint32_t o_head, o_nzw, o_fw, o_pub;
+    uint32_t o_sdesc, o_port, o_priv, pad;
+};
+
+struct RGrp {            /* 32 bytes: one ring channel */
+    uint32_t fid_base;   /* flow id of (round 0, step 0, rank 0) */
+    uint32_t N, S;       /* ranks; steps per round */
+    uint32_t RS;         /* flows per connection: rounds x steps */
+    uint32_t p;          /* packets per chunk of a full round */
+    uint32_t Xq;         /* last round of X packets: chunk k holds Xq + [k < X mod N] */
+    uint32_t T;          /* bit j, j < 3N: chunk j mod N of the last round holds Xq + 1 */
+    uint32_t mS;         /* ceil(2^24 / S): pos / S = umulhi(pos << 8, mS) for pos < 2^14 */
+};
+
+struct RPair {           /* 16 bytes */
+    uint32_t snd;        /* packets left in the active flow | position << 16 | state << 30 (CS_*) */
+    uint32_t rcv;        /* flows received over the partner connection */
+    uint32_t desc;       /* descriptor of the outgoing connection's packets at the first switch */
+    uint32_t gi;         /* group | rank of this host << 10 | rank of its predecessor << 20 */
+};
+
+struct RingPort {        /* 16 bytes, one per thread slot (HBM) */
+    uint32_t peer;       /* thread slot at the far end */
+    uint32_t row;        /* switch: its switch's first row (switch * 8); host: outgoing connections */
+    uint8_t flags, local, deg, delay;
+    uint32_t pad;
+};
+
+struct RingPriv {        /* 32 bytes: registers of a thread slot between runs */
+    uint32_t pushed, rr;
+    uint32_t mask;       /* switch: free buffer slots; host: pairs ready to send */
+    uint32_t tails;      /* switch: tail slot of each of its queues (4 bits each); host: flows left to receive */
+    uint32_t ne;         /* switch: bit o = queue toward o not empty */
+    uint32_t popped;     /* switch: packets forwarded out of this ingress */
+    uint32_t pad[2];
+};
+static_assert(sizeof(RGrp) == 32 && sizeof(RPair) == 16 && sizeof(RingPort) == 16 && sizeof(RingPriv) == 32,
+              "ring records");
+
 /* per-experiment progress and totals (workspace, outside the arena) */
 struct ExpState {        /* 64 bytes */
     uint32_t status;     /* MSIM_EXP_* */
@@ -353,13 +455,14 @@ struct ExpState {        /* 64 bytes */
 };
 
 /* workspace header */
-#define MSIM_KINDS 14
+#define MSIM_KINDS 15
 #define KIND_GENERAL_TASKS 9   /* the general path with a task graph */
 #define KIND_GENERAL_CC 10     /* the general path with congestion control (and tasks, if any) */
 #define KIND_COMPACT_X8 11     /* compact, 8-byte rows, rate 1, with trees / send-recv / gates */
 #define KIND_COMPACT_X16 12    /* compact, 16-byte rows, a faster link, with trees / send-recv / gates */
 #define KIND_GENERAL_SPRAY 13  /* the general path with packet spraying (and tasks, if any) */
 #define COMPACT_X_THREADS 768  /* launch bound of the two kinds above */
+#define KIND_RING 14           /* the ring format */
 
 struct WsHdr {
     uint32_t claim[MSIM_KINDS]; /* experiment queue counters of a run, one per kernel kind */

@@ -25,7 +25,7 @@ NONE = 0xFFFFFFFF
 KERNEL_NAMES = ["msim_megakernel", "msim_megakernel_c8h_r1", "msim_megakernel_c8h", "msim_megakernel_c8w_r1",
                 "msim_megakernel_c8w", "msim_megakernel_c16h_r1", "msim_megakernel_c16h", "msim_megakernel_c16w_r1",
                 "msim_megakernel_c16w", "msim_megakernel_t", "msim_megakernel_cc", "msim_megakernel_c8h_r1_x",
-                "msim_megakernel_c16h_x", "msim_megakernel_sp"]
+                "msim_megakernel_c16h_x", "msim_megakernel_sp", "msim_megakernel_ring"]
 
 EXPORTED = ["msim_create", "msim_workspace_size", "msim_bind", "msim_run", "msim_run_noalloc", "msim_reset",
             "msim_results",
@@ -60,7 +60,7 @@ class _Spec(C.Structure):
 class _Options(C.Structure):
     _fields_ = [("version", C.c_uint32), ("n_record", C.c_uint32), ("record_exp", _P32),
                 ("host_threads", C.c_uint32), ("force_global", C.c_uint32), ("block_threads", C.c_uint32),
-                ("reserved", C.c_uint32 * 8)]
+                ("no_ring_path", C.c_uint32), ("reserved", C.c_uint32 * 7)]
 
 
 class _Info(C.Structure):
@@ -137,7 +137,7 @@ class Sim:
     """A compiled batch.  create -> bind(workspace) -> run -> results."""
 
     def __init__(self, batch, record: Sequence[int] = (), force_global: bool = False, block_threads: int = 0,
-                 host_threads: int = 0):
+                 host_threads: int = 0, no_ring_path: bool = False):
         lib = load_library()
         p = batch.pack() if hasattr(batch, "pack") else batch
         self.packed = p
@@ -163,7 +163,7 @@ class Sim:
         self._rec = np.ascontiguousarray(np.asarray(list(record), np.uint32))
         self.record = [int(x) for x in self._rec]
         opts = _Options(ABI_VERSION, len(self._rec), _ptr(self._rec, _P32) if len(self._rec) else None,
-                        host_threads, 1 if force_global else 0, block_threads)
+                        host_threads, 1 if force_global else 0, block_threads, 1 if no_ring_path else 0)
         ctx = C.c_void_p()
         rc = lib.msim_create(C.byref(self._spec), C.byref(opts), C.byref(ctx))
         if rc != OK:

@@ -240,7 +240,9 @@ typedef struct msim_options {
     uint32_t host_threads;       /* threads for the host-side compile; 0 = all cores */
     uint32_t force_global;       /* 1: keep experiment state in HBM even where it fits in LDS */
     uint32_t block_threads;      /* 0 = automatic; else 64..1024, multiple of 64 */
-    uint32_t reserved[8];
+    uint32_t no_ring_path;       /* 1: run ring-only experiments on the general compact kernels too
+                                    (msim_megakernel_c8h_r1 and kin) instead of msim_megakernel_ring */
+    uint32_t reserved[7];
 } msim_options;
 
 typedef struct msim_ctx msim_ctx; /* opaque; owned by the library */

@@ -147,18 +147,45 @@ def test_c4_sample(simmod, oracle, force_global):
     assert_flows(s, 0, oracle.run(b, 0, flows=True))
 
 
+# C5 experiments spanning every oversubscription level (1, 2, 4) and the
+# smallest and largest buffers the draw gives each (16/17 and 128 packets)
+C5_IDS = [0, 1, 11, 134, 265, 294, 242, 43, 9, 2, 3, 4, 5, 6, 7, 8]
+
+
 def test_c5_sample(simmod, oracle):
-    """Three full-size k=16 fat-tree experiments (one per oversubscription
-    level, 6144 ports and 521,216 Zipf all-to-all flows each) on the general
-    path, state in HBM."""
-    b = I.make_config(5, exp_ids=[0, 1, 11])
-    assert sorted(x.topo for x in b.exps) == [0, 1, 2]
-    log("C5 sample", [(x.topo, x.queue_pkts) for x in b.exps])
+    """Sixteen full-size k=16 fat-tree experiments (6144 ports and 521,216 Zipf
+    all-to-all flows each) on the general path, state in HBM: every
+    oversubscription level, buffers of 16 to 128 packets."""
+    b = I.make_config(5, exp_ids=C5_IDS)
+    names = sorted({b.topos[x.topo].name for x in b.exps})
+    assert names == ["fattree16o1", "fattree16o2", "fattree16o4"]
+    qs = [x.queue_pkts for x in b.exps]
+    assert min(qs) == 16 and max(qs) == 128
+    log("C5 sample", [(b.topos[x.topo].name, x.queue_pkts) for x in b.exps])
     s, r = gpu_run(simmod, b, record=[0])
     o = oracle_all(oracle, b, flows=False)
     for e in range(b.n_exp):
         assert_exp(r, e, o[e])
     assert_flows(s, 0, oracle.run(b, 0, flows=True))
+
+
+@pytest.mark.parametrize("no_ring_path", [False, True])
+def test_c4_stratified(simmod, oracle, no_ring_path):
+    """C4 sampled evenly over the whole batch: every 64th of its 4096
+    experiments (all NC, chunk and failure draws the batch holds), on the ring
+    kernel and on the general compact kernel."""
+    ids = list(range(0, 4096, 64))
+    b = I.make_config(4, exp_ids=ids)
+    log("C4 stratified", len(ids), "no_ring_path", no_ring_path)
+    s = simmod.Sim(b, no_ring_path=no_ring_path)
+    want = "msim_megakernel_c8h_r1" if no_ring_path else "msim_megakernel_ring"
+    assert simmod.KERNEL_NAMES[s.info()["main_kernel"]] == want
+    s.bind()
+    s.run()
+    r = s.results()
+    o = oracle_all(oracle, b)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
 
 
 # ------------------------------------------------------------ semantics
