@@ -25,6 +25,13 @@
  *    call.  Device memory (the workspace) is allocated by the caller and must
  *    outlive the context; the library allocates no device memory itself.
  *  - A context is used from one host thread at a time.
+ *  - Sizing follows compiling: msim_create compiles on the host, then
+ *    msim_workspace_size and msim_bind size and fill the caller's workspace.
+ *  - msim_run only enqueues; the run status (MSIM_S_*) comes from msim_results.
+ *  - Results go to host arrays.  Per-flow ticks are kept only for the
+ *    experiments named at create (msim_options.record_exp).
+ *  - An experiment's tick stops at 0xFFFFFFF0; one that reaches it stays
+ *    MSIM_EXP_INCOMPLETE (there is no overflow error).
  *
  * Time is counted in integer ticks (one tick = the smallest link delay,
  * Multiverse section 5); data in whole packets of exp_pkt_bytes bytes.
@@ -259,7 +266,13 @@ typedef struct msim_ctx msim_ctx; /* opaque; owned by the library */
  */
 int msim_create(const msim_batch_spec *spec, const msim_options *opts, msim_ctx **out);
 
-/* Bytes of device workspace msim_bind needs (256-byte aligned start). */
+/* Bytes of device workspace msim_bind needs (256-byte aligned start): the
+ * experiment-major state store of every experiment of the batch (Multiverse
+ * section 3.3: the state of all experiments kept in one centralised store, as
+ * columns the simulation steps work on), its pristine copy for msim_reset, and
+ * the per-flow tick records of the recorded experiments.  The caller allocates
+ * it (device memory from its own allocator, e.g. a torch tensor) and keeps it
+ * alive as long as the context.  MSIM_E_ARG for a NULL argument. */
 int msim_workspace_size(const msim_ctx *ctx, uint64_t *bytes);
 
 /*
@@ -278,7 +291,8 @@ int msim_bind(msim_ctx *ctx, void *dev_workspace, uint64_t ws_bytes, void *hip_s
  * result.  Experiments are independent; their state
  * stays in the workspace between calls, so several calls continue where the
  * previous one stopped.  Returns MSIM_OK once enqueued; per-experiment outcome
- * comes from msim_results.  flags: reserved, pass 0.
+ * comes from msim_results.  flags: reserved, pass 0 (per-flow recording is
+ * chosen per experiment at msim_create, see msim_options.record_exp).
  */
 int msim_run(msim_ctx *ctx, uint32_t max_ticks, void *hip_stream, uint32_t flags);
 
@@ -305,6 +319,10 @@ int msim_run_noalloc(msim_ctx *ctx, uint32_t max_ticks, void *hip_stream, uint32
 int msim_reset(msim_ctx *ctx, void *hip_stream);
 
 /*
+ * The outcome of every experiment: Multiverse section 3.1 has the network
+ * simulator report each flow's completion back to the system simulator; per
+ * experiment that is the completion tick (the last flow's arrival), and the
+ * digest condenses every flow's completion tick into one number.
  * Waits for hip_stream, then copies per-experiment results to host arrays
  * (any pointer may be NULL to skip it), each of n_exp entries:
  *   exp_status    MSIM_EXP_*;
@@ -321,12 +339,16 @@ int msim_reset(msim_ctx *ctx, void *hip_stream);
 int msim_results(msim_ctx *ctx, void *hip_stream, uint8_t *exp_status, uint32_t *exp_tick,
                  uint64_t *exp_pkt_hops, uint64_t *exp_delivered, uint64_t *exp_digest);
 
-/* Number of flows of experiment exp (flows are numbered per experiment: the
+/* Number of flows of experiment exp: the point-to-point flows the collective
+ * algorithms are turned into (Multiverse section 3.1; AutoCCL section 2.3 for
+ * a ring's channels and chunks).  Flows are numbered per experiment: the
  * collectives in input order -- a ring by channel, round, step, rank; a
- * broadcast by hop, partition -- then the explicit flows). */
+ * broadcast by hop, partition -- then the explicit flows.  MSIM_E_ARG for an
+ * experiment index out of range. */
 int msim_flow_count(const msim_ctx *ctx, uint32_t exp, uint64_t *n_flows);
 
 /*
+ * Flow completion as Multiverse section 3.1 reports it, flow by flow.
  * Per-flow ticks of a recorded experiment (listed in msim_options.record_exp):
  * arrival of the last packet (rd), activation (act) and last send + 1 (sd),
  * 0xFFFFFFFF where the event has not happened.  Arrays of n_flows entries, or
