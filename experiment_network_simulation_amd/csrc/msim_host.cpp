@@ -605,8 +605,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
             take(H.o_pnxt, (size_t)Q * S);
             take(H.o_head, 64ull * n_sw);
             take(H.o_nzw, 32ull * n_sw);
-            take(H.o_fw, 4ull * S);
-            take(H.o_pub, 8ull * nt);
+            take(H.o_fw, 8ull * (S + 1));
             take(H.o_sdesc, 4ull * W * nt);
             H.lds_bytes = (uint32_t)off;
             take(H.o_port, sizeof(RingPort) * nt);

@@ -1971,6 +1971,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     }
     const uint32_t nt = H->nt, SB = H->SB, Q = H->Q, W = H->W, n_flows = H->n_flows;
     const uint32_t S = nt - SB;                      /* switch slots: pool stride */
+    const uint32_t FWS = S + 1;                      /* one half of fw; word S of each half stays 0 */
     LDSP uint8_t *L = (LDSP uint8_t *)lds;
     const LDSP RGrp *grp = (const LDSP RGrp *)(L + H->o_grp);
     LDSP RPair *pair = (LDSP RPair *)(L + H->o_pair);
@@ -1979,7 +1980,6 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     LDSP uint8_t *head = L + H->o_head;
     LDSP uint32_t *nzw = (LDSP uint32_t *)(L + H->o_nzw);
     LDSP uint32_t *fw = (LDSP uint32_t *)(L + H->o_fw);
-    LDSP uint32_t *pub = (LDSP uint32_t *)(L + H->o_pub);
     LDSP uint32_t *sdesc = (LDSP uint32_t *)(L + H->o_sdesc);
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     uint32_t *rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
@@ -1995,15 +1995,21 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     const bool is_sw = (pr.flags & (PF_USED | PF_HOST)) == PF_USED;
     const bool alive = pr.flags & PF_ALIVE;
     const bool peer_host = pr.flags & PF_PEER_HOST;
-    const bool feeds_sw = alive && !peer_host;                  /* its output has a credit to respect */
-    const uint32_t local = pr.local, deg = pr.deg;
+    const bool buffered = alive && !peer_host;                 /* its output feeds a switch buffer */
+    /* the credit bound of this port's output: Q toward a switch buffer, none
+     * toward a host, nothing over a failed cable */
+    const uint32_t qcap = !alive ? 0u : buffered ? Q : 0xFFFFFFFFu;
+    /* the fw word of the buffer this port's output feeds (word S: always 0) */
+    const uint32_t peer_pool = buffered ? pr.peer - SB : S;
+    const uint32_t local = pr.local;
     const uint32_t n_out = is_host ? pr.row : 0u;
     const uint32_t row = is_sw ? pr.row + local : 0u;          /* this port's switch row */
-    const uint32_t pool = is_sw ? tid - SB : 0u;               /* this ingress's buffer pool */
+    const uint32_t pool = is_sw ? tid - SB : S;                /* this ingress's buffer pool */
     const uint32_t pool0 = is_sw ? tid - local - SB : 0u;      /* pool of its switch's port 0 */
     const uint32_t hb0 = pr.row * 8u + local;                  /* head byte of queue (this ingress -> output 0) */
+    const uint32_t lbit16 = 1u << (16 + local);
     const uint32_t doff = pr.delay * nt, wsz = W * nt;
-    uint32_t pushed = pv.pushed, rr = pv.rr, mask = pv.mask, tails = pv.tails, ne = pv.ne, popped = pv.popped;
+    uint32_t pushed = pv.pushed, rr = pv.rr, mask = pv.mask, tails = pv.tails, ne = pv.ne, seen = pv.seen;
     const uint32_t pushed0 = pushed;
 
     uint32_t delivered = 0, tmax = 0, last_tx1 = 0, last_act1 = 0, fault = 0;
@@ -2027,86 +2033,109 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     uint32_t t = t0, par = 0, sb = (t0 % W) * nt;
     bool done = false, dead = false;
     uint32_t t_dead = 0;
-    while (t < t_end) {
-        const uint32_t cw = (t & 1u) * nt, cr = cw ^ nt;           /* pop counts: this tick's / last tick's */
-        uint32_t dst = sb + doff;
-        if (dst >= wsz) dst -= wsz;
-        dst += pr.peer;
-        if (is_sw) {
-            /* ---- round 1: the arriving packet; the far ingress's pops through t-1 */
-            const uint32_t e = sdesc[sb + tid];
-            uint32_t pf = 0;
-            if (feeds_sw) pf = pub[cr + pr.peer];
+    /* the next tick at whose end the workgroup checks for completion */
+    auto next_check = [&]() -> uint32_t {
+        const uint32_t d = t - t0;
+        const uint32_t nd = d < CHECK_LONG ? (d + CHECK_EVERY) & ~(CHECK_EVERY - 1u)
+                                           : (d + CHECK_EVERY_LONG) & ~(CHECK_EVERY_LONG - 1u);
+        return t0 + min(nd, t_end - t0);
+    };
+    uint32_t t_chk = next_check();
+    /* a word that stays 0: what a lane without a port reads as its arrival,
+     * and where it writes its (empty) departure */
+    LDSP uint32_t *const zero = fw + S;
+    /* every wavefront holds hosts only or switch ports only */
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(wave);
+    const bool w_host = wv * 64u < SB, w_sw = !w_host && wv * 64u < nt;
+    /* with every delay 1, the staging words this lane reads and writes at
+     * ticks of parity 0 and 1 */
+    const bool port = pr.flags & PF_USED;                      /* slots of absent hosts and gaps have none */
+    LDSP uint32_t *const rd1[2] = {port ? sdesc + tid : zero, port ? sdesc + nt + tid : zero};
+    LDSP uint32_t *const wr1[2] = {port ? sdesc + nt + pr.peer : zero, port ? sdesc + pr.peer : zero};
+
+    /* One tick t.  P is t & 1 when the caller knows it at compile time (every
+     * delay 1: staging has two slots, so the addresses of a tick of either
+     * parity are loop constants), else P is 2 and both come from t. */
+    auto tick = [&](auto PC) -> bool {
+        constexpr uint32_t PK = decltype(PC)::value;
+        const uint32_t P = PK < 2 ? PK : (t & 1u);
+        LDSP uint32_t *rdp, *wrp;                               /* staging: this tick's arrival, departure */
+        if constexpr (PK < 2) {
+            rdp = rd1[PK];
+            wrp = wr1[PK];
+        } else {
+            uint32_t dst = sb + doff;
+            if (dst >= wsz) dst -= wsz;
+            rdp = port ? sdesc + sb + tid : zero;
+            wrp = port ? sdesc + dst + pr.peer : zero;
+        }
+        LDSP uint32_t *fw_prev = fw + (P ^ 1u) * FWS;           /* what the outputs took at t - 1 */
+        LDSP uint32_t *fw_cur = fw + P * FWS;                   /* ... take at t */
+        if (w_sw) {
+            /* ---- round 1: the arriving packet; what the outputs took from
+             * this buffer and from the one it feeds during t - 1 */
+            const uint32_t e = *rdp;
+            const uint32_t w = fw_prev[pool];
+            const uint32_t pw = fw_prev[peer_pool];
+            fw_cur[pool] = 0u;
+            mask |= w & 0xFFFFu;
+            ne &= ~(w >> 16);
+            seen += (uint32_t)__builtin_popcount(pw & 0xFFFFu);
             /* arrival: append to the queue toward the egress the descriptor names */
             if (e != 0) {
                 const uint32_t o = e & 7u;
-                if (mask == 0 || o >= deg) {
-                    fault = 1;
-                } else {
-                    const uint32_t s = (uint32_t)__builtin_ctz(mask);
-                    mask &= mask - 1;
-                    const uint32_t a = __umul24(s, S) + pool;
-                    pdesc[a] = (e & ~RD_ROUTE_MASK) | ((e >> 3) & (RD_ROUTE_MASK >> 3));
-                    pnxt[a] = (uint8_t)Q_EMPTY;
-                    if (ne & (1u << o)) {
-                        pnxt[__umul24((tails >> (4 * o)) & 15u, S) + pool] = (uint8_t)s;
-                    } else {
-                        head[hb0 + 8 * o] = (uint8_t)s;
-                        __hip_atomic_fetch_or(nzw + pr.row + o, 1u << local, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_WORKGROUP);
-                    }
-                    tails = (tails & ~(15u << (4 * o))) | (s << (4 * o));
-                    ne |= 1u << o;
-                }
+                fault |= mask == 0 ? 1u : 0u;
+                const uint32_t s = mask ? (uint32_t)__builtin_ctz(mask) : Q - 1u;
+                mask &= mask - 1;
+                const uint32_t a = __umul24(s, S) + pool;
+                pdesc[a] = (e & ~RD_ROUTE_MASK) | ((e >> 3) & (RD_ROUTE_MASK >> 3));
+                pnxt[a] = (uint8_t)Q_EMPTY;
+                const uint32_t o4 = o * 4u;
+                /* link behind the queue's tail, or make it the head; the
+                 * output's non-empty bit is already set when the queue holds
+                 * packets, so setting it again changes nothing */
+                LDSP uint8_t *lnk = (ne & (1u << o)) ? pnxt + __umul24((tails >> o4) & 15u, S) + pool
+                                                     : head + hb0 + 8 * o;
+                *lnk = (uint8_t)s;
+                __hip_atomic_fetch_or(nzw + pr.row + o, 1u << local, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                tails = (tails & ~(15u << o4)) | (s << o4);
+                ne |= 1u << o;
             }
             wave_lds_fence();
             /* ---- round 2: forwarding.  Candidates: the inputs whose queue
              * toward this output holds a packet; the grant goes to the first
-             * from rr; credit is the far ingress's room as of the end of the
-             * last tick */
+             * from rr; credit is the far buffer's room as of the end of t - 1 */
+            uint32_t nz = nzw[row];
+            uint64_t hrow = *(const LDSP uint64_t *)(head + row * 8u);
+            pin(nz); pin(hrow);
             uint32_t out = 0;
-            if (alive) {
-                uint32_t nz = nzw[row];
-                uint64_t hrow = *(const LDSP uint64_t *)(head + row * 8u);
-                pin(nz); pin(hrow);
-                if (nz != 0 && (!feeds_sw || pushed - pf < Q)) {
-                    const uint32_t rot = (nz | (nz << 8)) >> rr;
-                    const uint32_t i = (rr + (uint32_t)__builtin_ctz(rot)) & 7u;
-                    const uint32_t s = (uint32_t)(hrow >> (8 * i)) & 0xFFu;
-                    const uint32_t qa = __umul24(s, S) + pool0 + i;
-                    /* ---- round 3: the packet and its successor in the queue */
-                    const uint32_t d = pdesc[qa];
-                    const uint32_t nx = pnxt[qa];
-                    head[row * 8u + i] = (uint8_t)nx;
-                    const bool emptied = nx == Q_EMPTY;
-                    __hip_atomic_fetch_or(fw + pool0 + i, (1u << s) | (emptied ? 1u << (16 + local) : 0u),
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    if (emptied) nzw[row] = nz & ~(1u << i);
-                    out = d;
-                    pushed++;
-                    last_tx1 = t + 1;
-                    rr = i + 1 == deg ? 0u : i + 1;
-                }
-                sdesc[dst] = out;
+            if (nz != 0 && pushed - seen < qcap) {
+                /* nz != 0; bits at or above deg are 0, so a search from
+                 * rr == deg wraps to input 0 */
+                const uint32_t i = (rr + (uint32_t)__builtin_ctz(__builtin_amdgcn_alignbit(nz, nz, rr))) & 7u;
+                const uint32_t s = (uint32_t)(hrow >> (8 * i)) & 0xFFu;
+                const uint32_t qa = __umul24(s, S) + pool0 + i;
+                /* ---- round 3: the packet and its successor in the queue */
+                const uint32_t d = pdesc[qa];
+                const uint32_t nx = pnxt[qa];
+                head[row * 8u + i] = (uint8_t)nx;
+                const bool emptied = nx == Q_EMPTY;
+                __hip_atomic_fetch_or(fw_cur + pool0 + i, (1u << s) | (emptied ? lbit16 : 0u),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                nzw[row] = emptied ? nz & ~(1u << i) : nz;
+                out = d;
+                pushed++;
+                last_tx1 = t + 1;
+                rr = i + 1;
             }
-            wave_lds_fence();
-            /* ---- round 4: what the outputs of this switch took from this
-             * ingress during the tick; its pop count for tick t + 1 */
-            const uint32_t w = fw[pool];
-            if (w != 0) {
-                fw[pool] = 0;
-                mask |= w & 0xFFFFu;
-                ne &= ~(w >> 16);
-                popped += (uint32_t)__builtin_popcount(w & 0xFFFFu);
-            }
-            pub[cw + tid] = popped;
-        } else if (is_host) {
-            /* ---- round 1: the arriving packet, the far ingress's pops, and
+            *wrp = out;
+        } else if (w_host) {
+            /* ---- round 1: the arriving packet, the far buffer's pops, and
              * the first ready pair with, if its flow is about to finish
              * sending, its channel */
-            const uint32_t e = sdesc[sb + tid];
-            uint32_t pf = 0;
-            if (alive) pf = pub[cr + pr.peer];
+            const uint32_t e = *rdp;
+            const uint32_t pw = fw_prev[peer_pool];
+            seen += (uint32_t)__builtin_popcount(pw & 0xFFFFu);
             const bool any = mask != 0;
             const uint32_t j = first_ready(mask, rr);
             RPair pj;
@@ -2149,17 +2178,17 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 }
             }
             /* ---- the NIC: one packet of the first ready pair from rr, while
-             * the far ingress has room.  That pair is j, read before the
-             * barrier, unless a pair woken above comes first. */
+             * the far buffer has room.  That pair is j, read in round 1,
+             * unless a pair woken above comes first. */
             uint32_t out = 0;
-            if (alive && mask != 0 && pushed - pf < Q) {
+            if (mask != 0 && pushed - seen < qcap) {
                 const uint32_t c = !any ? k : (woke && ((k - rr) & 31u) < ((j - rr) & 31u)) ? k : j;
                 const bool usek = (e & RD_LAST) && c == k;
                 uint32_t snd = usek ? pk.snd : pj.snd;
                 out = (usek ? pk.desc : pj.desc) | (RP_REM(snd) == 1u ? RD_LAST : 0u);
                 pushed++;
                 last_tx1 = t + 1;
-                rr = c + 1u == n_out ? 0u : c + 1u;
+                rr = c + 1u;   /* 32 rotates as 0; c + 1 == n_out wraps over empty bits */
                 if (RP_REM(snd) == 1u) {
                     /* the flow's last packet leaves: SD = t + 1 */
                     const uint32_t gi = usek ? pk.gi : pj.gi, rpos = usek ? pk.rcv : pj.rcv;
@@ -2188,12 +2217,14 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 }
                 pair_me[__umul24(c, SB)].snd = snd;
             }
-            if (alive) sdesc[dst] = out;
+            *wrp = out;
         }
         t++;
-        sb += nt;
-        if (sb == wsz) sb = 0;
-        if (((t - t0) & ((t - t0) < CHECK_LONG ? CHECK_EVERY - 1u : CHECK_EVERY_LONG - 1u)) == 0 || t == t_end) {
+        if constexpr (PK == 2) {
+            sb += nt;
+            if (sb == wsz) sb = 0;
+        }
+        if (t == t_chk) {
             const uint32_t max_arr = last_tx1 ? last_tx1 - 1 + pr.delay : 0;
             const uint32_t anyl = __ballot(left > 0) != 0ull;
             const uint32_t ts = wave_max_u32(max(max(last_tx1, last_act1), max_arr));
@@ -2205,11 +2236,26 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
             uint32_t anyw = 0, tsw = hist;
             for (uint32_t w = 0; w < nwaves; w++) { anyw |= sh.chk_any[par][w]; tsw = max(tsw, sh.chk_max[par][w]); }
             par ^= 1;
-            if (!anyw) { done = true; break; }
-            if (tsw <= t - 1) { dead = true; t_dead = tsw; break; }
+            if (!anyw) { done = true; return true; }
+            if (tsw <= t - 1) { dead = true; t_dead = tsw; return true; }
+            if (t >= t_end) return true;
+            t_chk = next_check();
         } else {
             __syncthreads();
         }
+        return false;
+    };
+    if (W == 2) {
+        /* every delay is 1: ticks in pairs, even then odd */
+        bool stop = t >= t_end;
+        if (!stop && (t & 1u)) stop = tick(std::integral_constant<uint32_t, 1>());
+        while (!stop) {
+            if (tick(std::integral_constant<uint32_t, 0>())) break;
+            stop = tick(std::integral_constant<uint32_t, 1>());
+        }
+    } else {
+        while (t < t_end)
+            if (tick(std::integral_constant<uint32_t, 2>())) break;
     }
 
     const uint32_t max_arr = last_tx1 ? last_tx1 - 1 + pr.delay : 0;
@@ -2219,7 +2265,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
         for (uint32_t i = tid; i < (lds_bytes - rw_off) / 16; i += nth) dst[i] = src[i];
     }
     if (used) {
-        pv.pushed = pushed; pv.rr = rr; pv.mask = mask; pv.ne = ne; pv.popped = popped;
+        pv.pushed = pushed; pv.rr = rr; pv.mask = mask; pv.ne = ne; pv.seen = seen;
         pv.tails = is_host ? left : tails;
         ((RingPriv *)(arena_g + H->o_priv))[tid] = pv;
     }

@@ -374,13 +374,15 @@ struct PortPriv {        /* 144 bytes: registers of a thread slot between runs *
  *                      by the ingress (LDS atomic OR: several ingresses of a
  *                      switch may set bits of one word in one instruction),
  *                      cleared by the output when it pops the last packet;
- *   fw[q]              what the outputs of its switch took from ingress q this
- *                      tick: bit s = buffer slot s freed, bit 16 + o = queue
- *                      (q -> o) emptied (LDS atomic OR); the ingress folds it
- *                      into its registers at the end of the tick and clears it;
- *   pub[t & 1][slot]   packets forwarded out of a switch ingress through tick
- *                      t, written at the end of tick t: the credit its feeder
- *                      reads at tick t + 1.
+ *   fw[t & 1][q]       what the outputs of its switch took from ingress q at
+ *                      tick t: bit s = buffer slot s freed, bit 16 + o = queue
+ *                      (q -> o) emptied (LDS atomic OR).  Read at tick t + 1 by
+ *                      the ingress, which folds it into its registers, and by
+ *                      the port that feeds q, which counts the pops for its
+ *                      credit; cleared by the ingress at tick t + 2 before its
+ *                      outputs write it again.  Each half holds S + 1 words;
+ *                      word S stays 0 (the word a port without a far buffer
+ *                      reads).
  * Staging: sdesc[(t mod W) * nt + slot] = descriptor of the packet reaching
  * that port at tick t, 0 for none, rewritten by its feeder every tick. */
 #define MODE_RING 3u
@@ -401,7 +403,7 @@ struct ArenaHdr3 {       /* 96 bytes */
     uint32_t lds_bytes, nt, H, SB;
     uint32_t Q, W, n_grp, n_sw;
     uint32_t o_grp, o_pair, o_pdesc, o_pnxt;
-    uint32_t o_head, o_nzw, o_fw, o_pub;
+    uint32_t o_head, o_nzw, o_fw, pad1;
     uint32_t o_sdesc, o_port, o_priv, pad;
 };
 
@@ -434,7 +436,7 @@ struct RingPriv {        /* 32 bytes: registers of a thread slot between runs */
     uint32_t mask;       /* switch: free buffer slots; host: pairs ready to send */
     uint32_t tails;      /* switch: tail slot of each of its queues (4 bits each); host: flows left to receive */
     uint32_t ne;         /* switch: bit o = queue toward o not empty */
-    uint32_t popped;     /* switch: packets forwarded out of this ingress */
+    uint32_t seen;       /* packets forwarded out of the far buffer, as counted from its fw words */
     uint32_t pad[2];
 };
 static_assert(sizeof(RGrp) == 32 && sizeof(RPair) == 16 && sizeof(RingPort) == 16 && sizeof(RingPriv) == 32,
