@@ -2013,7 +2013,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     const uint32_t pushed0 = pushed;
 
     uint32_t delivered = 0, tmax = 0, last_tx1 = 0, last_act1 = 0, fault = 0;
-    uint64_t digest = 0;
+    uint64_t digest = 0, fault_w = 0;
     uint32_t left = is_host ? tails : 0u;
     __syncthreads();
 
@@ -2056,7 +2056,11 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     /* One tick t.  P is t & 1 when the caller knows it at compile time (every
      * delay 1: staging has two slots, so the addresses of a tick of either
      * parity are loop constants), else P is 2 and both come from t. */
-    auto tick = [&](auto PC) -> bool {
+    /* KC: the kind of this wavefront (1 hosts, 2 switch ports, 0 none); each
+     * kind runs its own copy of the loop, so values live in one kind's
+     * registers never have to be merged with another's */
+    auto tick = [&](auto KC, auto PC) -> bool {
+        constexpr uint32_t KK = decltype(KC)::value;
         constexpr uint32_t PK = decltype(PC)::value;
         const uint32_t P = PK < 2 ? PK : (t & 1u);
         LDSP uint32_t *rdp, *wrp;                               /* staging: this tick's arrival, departure */
@@ -2071,7 +2075,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
         }
         LDSP uint32_t *fw_prev = fw + (P ^ 1u) * FWS;           /* what the outputs took at t - 1 */
         LDSP uint32_t *fw_cur = fw + P * FWS;                   /* ... take at t */
-        if (w_sw) {
+        if constexpr (KK == 2) {
             /* ---- round 1: the arriving packet; what the outputs took from
              * this buffer and from the one it feeds during t - 1 */
             const uint32_t e = *rdp;
@@ -2084,11 +2088,14 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
             /* arrival: append to the queue toward the egress the descriptor names */
             if (e != 0) {
                 const uint32_t o = e & 7u;
-                fault |= mask == 0 ? 1u : 0u;
-                const uint32_t s = mask ? (uint32_t)__builtin_ctz(mask) : Q - 1u;
+                fault_w |= __ballot(mask == 0);
+                const uint32_t s = (uint32_t)__builtin_ctz(mask | 0x8000u);   /* in range even when mask is 0 */
                 mask &= mask - 1;
                 const uint32_t a = __umul24(s, S) + pool;
-                pdesc[a] = (e & ~RD_ROUTE_MASK) | ((e >> 3) & (RD_ROUTE_MASK >> 3));
+                /* drop this switch's hop: the bits shifted into the top of the
+                 * route field are never read, since a path has at most
+                 * RING_MAX_HOPS switches */
+                pdesc[a] = ((e >> 3) & RD_ROUTE_MASK) | (e & ~RD_ROUTE_MASK);
                 pnxt[a] = (uint8_t)Q_EMPTY;
                 const uint32_t o4 = o * 4u;
                 /* link behind the queue's tail, or make it the head; the
@@ -2129,29 +2136,25 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 rr = i + 1;
             }
             *wrp = out;
-        } else if (w_host) {
+        } else if constexpr (KK == 1) {
             /* ---- round 1: the arriving packet, the far buffer's pops, and
-             * the first ready pair with, if its flow is about to finish
-             * sending, its channel */
+             * the first ready pair from rr */
             const uint32_t e = *rdp;
             const uint32_t pw = fw_prev[peer_pool];
             seen += (uint32_t)__builtin_popcount(pw & 0xFFFFu);
             const bool any = mask != 0;
-            const uint32_t j = first_ready(mask, rr);
-            RPair pj;
-            RGrp gj;
-            if (any) pj = rpair_load(pair_me + __umul24(j, SB));
-            if (any && RP_REM(pj.snd) == 1u) gj = rgrp_load(grp + GI_GRP(pj.gi));
+            const uint32_t j = any ? (rr + (uint32_t)__builtin_ctz(__builtin_amdgcn_alignbit(mask, mask, rr))) & 31u : 0u;
+            const RPair pj = rpair_load(pair_me + __umul24(j, SB));
             if (e != 0) delivered++;
             /* ---- round 2, when a flow's last packet arrives: its pair and
              * ring channel */
             const uint32_t k = (e >> RD_PAIR_SHIFT) & 31u;
-            RPair pk;
-            RGrp gk;
+            const bool last = e & RD_LAST;
+            uint32_t k_snd = 0, k_rcv = 0;
             bool woke = false;
-            if (e & RD_LAST) {
-                pk = rpair_load(pair_me + __umul24(k, SB));
-                gk = rgrp_load(grp + ((e >> RD_GRP_SHIFT) & 1023u));
+            if (last) {
+                const RPair pk = rpair_load(pair_me + __umul24(k, SB));
+                const RGrp gk = rgrp_load(grp + ((e >> RD_GRP_SHIFT) & 1023u));
                 /* the flow is received: RD = t */
                 const uint32_t ri = GI_PRED(pk.gi), rpos = pk.rcv;
                 const uint32_t fid = rfid(gk, ri, rpos);
@@ -2160,39 +2163,42 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 left--;
                 if (rpos >= gk.RS) fault = 1;                     /* a flow no one sends */
                 if (rec) rec[fid] = t;
-                const uint32_t np = rpos + 1u;
-                pk.rcv = np;
-                pair_me[__umul24(k, SB)].rcv = np;
+                k_rcv = rpos + 1u;
+                pair_me[__umul24(k, SB)].rcv = k_rcv;
                 /* the partner's next send waits on this receive (it is idle
                  * only at a step > 0 of a round: step 0 waits on nothing but
                  * its own last send) */
-                const uint32_t spos = RP_POS(pk.snd);
-                if (RP_ST(pk.snd) == CS_IDLE && np >= spos) {
+                k_snd = pk.snd;
+                const uint32_t spos = RP_POS(k_snd);
+                if (RP_ST(k_snd) == CS_IDLE && k_rcv >= spos) {
                     const uint32_t i = GI_RANK(pk.gi);
-                    pk.snd = (CS_ACTIVE << 30) | (spos << 16) | rsize(gk, i + 2u * gk.N, spos);
+                    k_snd = (CS_ACTIVE << 30) | (spos << 16) | rsize(gk, i + 2u * gk.N, spos);
                     mask |= 1u << k;
                     last_act1 = t + 1;
                     if (rec) rec[n_flows + rfid(gk, i, spos)] = t;
-                    pair_me[__umul24(k, SB)].snd = pk.snd;
+                    pair_me[__umul24(k, SB)].snd = k_snd;
                     woke = true;
                 }
             }
             /* ---- the NIC: one packet of the first ready pair from rr, while
              * the far buffer has room.  That pair is j, read in round 1,
-             * unless a pair woken above comes first. */
+             * unless a pair woken above comes first; pair k's record was
+             * rewritten above, so its values come from registers. */
             uint32_t out = 0;
             if (mask != 0 && pushed - seen < qcap) {
-                const uint32_t c = !any ? k : (woke && ((k - rr) & 31u) < ((j - rr) & 31u)) ? k : j;
-                const bool usek = (e & RD_LAST) && c == k;
-                uint32_t snd = usek ? pk.snd : pj.snd;
-                out = (usek ? pk.desc : pj.desc) | (RP_REM(snd) == 1u ? RD_LAST : 0u);
+                const bool kfirst = woke && (!any || ((k - rr) & 31u) < ((j - rr) & 31u));
+                const uint32_t c = kfirst ? k : j;
+                const bool usek = last && c == k;
+                uint32_t snd = usek ? k_snd : pj.snd;
+                const uint32_t gi = usek ? pair_me[__umul24(k, SB)].gi : pj.gi;
+                out = (usek ? pair_me[__umul24(k, SB)].desc : pj.desc) | (RP_REM(snd) == 1u ? RD_LAST : 0u);
                 pushed++;
                 last_tx1 = t + 1;
                 rr = c + 1u;   /* 32 rotates as 0; c + 1 == n_out wraps over empty bits */
                 if (RP_REM(snd) == 1u) {
                     /* the flow's last packet leaves: SD = t + 1 */
-                    const uint32_t gi = usek ? pk.gi : pj.gi, rpos = usek ? pk.rcv : pj.rcv;
-                    const RGrp g = usek ? gk : gj;
+                    const uint32_t rpos = usek ? k_rcv : pj.rcv;
+                    const RGrp g = rgrp_load(grp + GI_GRP(gi));
                     const uint32_t spos = RP_POS(snd), np = spos + 1u;
                     mask &= ~(1u << c);
                     if (rec) rec[2 * n_flows + rfid(g, GI_RANK(gi), spos)] = t + 1;
@@ -2245,20 +2251,28 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
         }
         return false;
     };
-    if (W == 2) {
-        /* every delay is 1: ticks in pairs, even then odd */
-        bool stop = t >= t_end;
-        if (!stop && (t & 1u)) stop = tick(std::integral_constant<uint32_t, 1>());
-        while (!stop) {
-            if (tick(std::integral_constant<uint32_t, 0>())) break;
-            stop = tick(std::integral_constant<uint32_t, 1>());
+    auto loop = [&](auto KC) {
+        if (W == 2) {
+            /* every delay is 1: ticks in pairs, even then odd */
+            bool stop = t >= t_end;
+            if (!stop && (t & 1u)) stop = tick(KC, std::integral_constant<uint32_t, 1>());
+            while (!stop) {
+                if (tick(KC, std::integral_constant<uint32_t, 0>())) break;
+                stop = tick(KC, std::integral_constant<uint32_t, 1>());
+            }
+        } else {
+            while (t < t_end)
+                if (tick(KC, std::integral_constant<uint32_t, 2>())) break;
         }
-    } else {
-        while (t < t_end)
-            if (tick(std::integral_constant<uint32_t, 2>())) break;
-    }
+    };
+    /* every wavefront passes the same barriers: the loops differ only in
+     * what a tick does between them */
+    if (w_host) loop(std::integral_constant<uint32_t, 1>());
+    else if (w_sw) loop(std::integral_constant<uint32_t, 2>());
+    else loop(std::integral_constant<uint32_t, 0>());
 
     const uint32_t max_arr = last_tx1 ? last_tx1 - 1 + pr.delay : 0;
+    if (fault_w) fault = 1;
     {
         const uint4 *src = (const uint4 *)(lds + rw_off);
         uint4 *dst = (uint4 *)(arena_g + rw_off);
