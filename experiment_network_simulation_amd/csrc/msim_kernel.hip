@@ -2007,13 +2007,13 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     const uint32_t pool = is_sw ? tid - SB : S;                /* this ingress's buffer pool */
     const uint32_t pool0 = is_sw ? tid - local - SB : 0u;      /* pool of its switch's port 0 */
     const uint32_t hb0 = pr.row * 8u + local;                  /* head byte of queue (this ingress -> output 0) */
-    const uint32_t lbit16 = 1u << (16 + local);
     const uint32_t doff = pr.delay * nt, wsz = W * nt;
     uint32_t pushed = pv.pushed, rr = pv.rr, mask = pv.mask, tails = pv.tails, ne = pv.ne, seen = pv.seen;
     const uint32_t pushed0 = pushed;
 
     uint32_t delivered = 0, tmax = 0, last_tx1 = 0, last_act1 = 0, fault = 0;
-    uint64_t digest = 0, fault_w = 0;
+    uint64_t digest = 0;
+    uint32_t fmin = ~0u;                                       /* least free-slot mask an arrival met */
     uint32_t left = is_host ? tails : 0u;
     __syncthreads();
 
@@ -2088,7 +2088,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
             /* arrival: append to the queue toward the egress the descriptor names */
             if (e != 0) {
                 const uint32_t o = e & 7u;
-                fault_w |= __ballot(mask == 0);
+                fmin = min(fmin, mask);                           /* 0: a packet met a full buffer */
                 const uint32_t s = (uint32_t)__builtin_ctz(mask | 0x8000u);   /* in range even when mask is 0 */
                 mask &= mask - 1;
                 const uint32_t a = __umul24(s, S) + pool;
@@ -2126,10 +2126,11 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 const uint32_t d = pdesc[qa];
                 const uint32_t nx = pnxt[qa];
                 head[row * 8u + i] = (uint8_t)nx;
-                const bool emptied = nx == Q_EMPTY;
-                __hip_atomic_fetch_or(fw_cur + pool0 + i, (1u << s) | (emptied ? lbit16 : 0u),
+                /* 1 when the queue is now empty: slots are below 16, Q_EMPTY is 0xFF */
+                const uint32_t em = nx >> 7;
+                __hip_atomic_fetch_or(fw_cur + pool0 + i, (1u << s) | (em << (16 + local)),
                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                nzw[row] = emptied ? nz & ~(1u << i) : nz;
+                nzw[row] = nz & ~(em << i);
                 out = d;
                 pushed++;
                 last_tx1 = t + 1;
@@ -2272,7 +2273,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     else loop(std::integral_constant<uint32_t, 0>());
 
     const uint32_t max_arr = last_tx1 ? last_tx1 - 1 + pr.delay : 0;
-    if (fault_w) fault = 1;
+    if (fmin == 0) fault = 1;
     {
         const uint4 *src = (const uint4 *)(lds + rw_off);
         uint4 *dst = (uint4 *)(arena_g + rw_off);
