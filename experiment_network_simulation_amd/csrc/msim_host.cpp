@@ -607,6 +607,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
             take(H.o_nzw, 32ull * n_sw);
             take(H.o_fw, 8ull * (S + 1));
             take(H.o_sdesc, 4ull * W * nt);
+            take(H.o_dq, 8ull * RING_DQ * SB);
             H.lds_bytes = (uint32_t)off;
             take(H.o_port, sizeof(RingPort) * nt);
             take(H.o_priv, sizeof(RingPriv) * nt);

@@ -1981,6 +1981,8 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     LDSP uint32_t *nzw = (LDSP uint32_t *)(L + H->o_nzw);
     LDSP uint32_t *fw = (LDSP uint32_t *)(L + H->o_fw);
     LDSP uint32_t *sdesc = (LDSP uint32_t *)(L + H->o_sdesc);
+    /* a host's received flows not yet mixed into its digest (host lanes only) */
+    LDSP uint64_t *dq = (LDSP uint64_t *)(L + H->o_dq) + (tid < SB ? tid : 0u) * RING_DQ;
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     uint32_t *rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
@@ -2008,12 +2010,29 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     const uint32_t pool0 = is_sw ? tid - local - SB : 0u;      /* pool of its switch's port 0 */
     const uint32_t hb0 = pr.row * 8u + local;                  /* head byte of queue (this ingress -> output 0) */
     const uint32_t doff = pr.delay * nt, wsz = W * nt;
+    /* this ingress's buffer slot s: pd_me + s * S words, pn_me + s * S bytes */
+    LDSP uint8_t *const pd_me = (LDSP uint8_t *)(pdesc + pool);
+    LDSP uint8_t *const pn_me = pnxt + pool;
+    const uint32_t S4 = S * 4u;
     uint32_t pushed = pv.pushed, rr = pv.rr, mask = pv.mask, tails = pv.tails, ne = pv.ne, seen = pv.seen;
     const uint32_t pushed0 = pushed;
 
     uint32_t delivered = 0, tmax = 0, last_tx1 = 0, last_act1 = 0, fault = 0;
     uint64_t digest = 0;
     uint32_t fmin = ~0u;                                       /* least free-slot mask an arrival met */
+    uint32_t qn = 0;                                           /* entries in this host's digest queue */
+    uint32_t last_w = 0;                                       /* switch wavefront, every delay 1: last send + 1 */
+    /* mix the queued (flow, RD) words of every host of the wavefront at once:
+     * one pass over RING_DQ entries instead of one mix per tick with an
+     * arrival somewhere in the wavefront */
+    auto flush_digest = [&]() {
+#pragma unroll
+        for (uint32_t k = 0; k < RING_DQ; k++) {
+            const uint64_t z = dq[k];
+            if (k < qn) digest += mix64(z);
+        }
+        qn = 0;
+    };
     uint32_t left = is_host ? tails : 0u;
     __syncthreads();
 
@@ -2084,25 +2103,24 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
             fw_cur[pool] = 0u;
             mask |= w & 0xFFFFu;
             ne &= ~(w >> 16);
-            seen += (uint32_t)__builtin_popcount(pw & 0xFFFFu);
+            seen += (uint32_t)__builtin_popcount((uint32_t)(uint16_t)pw);
             /* arrival: append to the queue toward the egress the descriptor names */
             if (e != 0) {
                 const uint32_t o = e & 7u;
                 fmin = min(fmin, mask);                           /* 0: a packet met a full buffer */
                 const uint32_t s = (uint32_t)__builtin_ctz(mask | 0x8000u);   /* in range even when mask is 0 */
                 mask &= mask - 1;
-                const uint32_t a = __umul24(s, S) + pool;
                 /* drop this switch's hop: the bits shifted into the top of the
                  * route field are never read, since a path has at most
                  * RING_MAX_HOPS switches */
-                pdesc[a] = ((e >> 3) & RD_ROUTE_MASK) | (e & ~RD_ROUTE_MASK);
-                pnxt[a] = (uint8_t)Q_EMPTY;
+                *(LDSP uint32_t *)(pd_me + __umul24(s, S4)) = ((e >> 3) & RD_ROUTE_MASK) | (e & ~RD_ROUTE_MASK);
+                pn_me[__umul24(s, S)] = (uint8_t)Q_EMPTY;
                 const uint32_t o4 = o * 4u;
                 /* link behind the queue's tail, or make it the head; the
                  * output's non-empty bit is already set when the queue holds
                  * packets, so setting it again changes nothing */
-                LDSP uint8_t *lnk = (ne & (1u << o)) ? pnxt + __umul24((tails >> o4) & 15u, S) + pool
-                                                     : head + hb0 + 8 * o;
+                LDSP uint8_t *lnk = __builtin_amdgcn_ubfe(ne, o, 1) ? pn_me + __umul24(__builtin_amdgcn_ubfe(tails, o4, 4), S)
+                                                                     : head + hb0 + 8 * o;
                 *lnk = (uint8_t)s;
                 __hip_atomic_fetch_or(nzw + pr.row + o, 1u << local, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 tails = (tails & ~(15u << o4)) | (s << o4);
@@ -2116,7 +2134,11 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
             uint64_t hrow = *(const LDSP uint64_t *)(head + row * 8u);
             pin(nz); pin(hrow);
             uint32_t out = 0;
-            if (nz != 0 && pushed - seen < qcap) {
+            const bool go = nz != 0 && pushed - seen < qcap;
+            if constexpr (PK < 2) {
+                if (__ballot(go) != 0ull) last_w = t + 1;          /* every delay is 1: the wavefront's latest send */
+            }
+            if (go) {
                 /* nz != 0; bits at or above deg are 0, so a search from
                  * rr == deg wraps to input 0 */
                 const uint32_t i = (rr + (uint32_t)__builtin_ctz(__builtin_amdgcn_alignbit(nz, nz, rr))) & 7u;
@@ -2133,7 +2155,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 nzw[row] = nz & ~(em << i);
                 out = d;
                 pushed++;
-                last_tx1 = t + 1;
+                if constexpr (PK == 2) last_tx1 = t + 1;
                 rr = i + 1;
             }
             *wrp = out;
@@ -2159,7 +2181,8 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 /* the flow is received: RD = t */
                 const uint32_t ri = GI_PRED(pk.gi), rpos = pk.rcv;
                 const uint32_t fid = rfid(gk, ri, rpos);
-                digest += mix64(((uint64_t)fid << 32) | t);
+                dq[qn] = ((uint64_t)fid << 32) | t;
+                qn++;
                 tmax = t;
                 left--;
                 if (rpos >= gk.RS) fault = 1;                     /* a flow no one sends */
@@ -2225,6 +2248,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 pair_me[__umul24(c, SB)].snd = snd;
             }
             *wrp = out;
+            if (__ballot(qn == RING_DQ) != 0ull) flush_digest();
         }
         t++;
         if constexpr (PK == 2) {
@@ -2232,6 +2256,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
             if (sb == wsz) sb = 0;
         }
         if (t == t_chk) {
+            last_tx1 = max(last_tx1, last_w);
             const uint32_t max_arr = last_tx1 ? last_tx1 - 1 + pr.delay : 0;
             const uint32_t anyl = __ballot(left > 0) != 0ull;
             const uint32_t ts = wave_max_u32(max(max(last_tx1, last_act1), max_arr));
@@ -2272,6 +2297,8 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     else if (w_sw) loop(std::integral_constant<uint32_t, 2>());
     else loop(std::integral_constant<uint32_t, 0>());
 
+    if (w_host) flush_digest();
+    last_tx1 = max(last_tx1, last_w);
     const uint32_t max_arr = last_tx1 ? last_tx1 - 1 + pr.delay : 0;
     if (fmin == 0) fault = 1;
     {

@@ -384,7 +384,10 @@ struct PortPriv {        /* 144 bytes: registers of a thread slot between runs *
  *                      word S stays 0 (the word a port without a far buffer
  *                      reads).
  * Staging: sdesc[(t mod W) * nt + slot] = descriptor of the packet reaching
- * that port at tick t, 0 for none, rewritten by its feeder every tick. */
+ * that port at tick t, 0 for none, rewritten by its feeder every tick.
+ * Digest queue: dq[host * RING_DQ + k], the (flow << 32 | RD) words a host
+ * has received but not yet mixed into its digest; a wavefront mixes all its
+ * hosts' queues together once one of them is full, and at the end of a run. */
 #define MODE_RING 3u
 #define RING_MAX_DEG 8u
 #define RING_MAX_Q 16u
@@ -397,13 +400,14 @@ struct PortPriv {        /* 144 bytes: registers of a thread slot between runs *
 #define RD_GRP_SHIFT 21
 #define RD_VALID 0x80000000u
 #define RING_MAX_GRP 1024u
+#define RING_DQ 4u
 
 struct ArenaHdr3 {       /* 96 bytes */
     uint32_t mode, bytes, rw_off, n_flows;
     uint32_t lds_bytes, nt, H, SB;
     uint32_t Q, W, n_grp, n_sw;
     uint32_t o_grp, o_pair, o_pdesc, o_pnxt;
-    uint32_t o_head, o_nzw, o_fw, pad1;
+    uint32_t o_head, o_nzw, o_fw, o_dq;
     uint32_t o_sdesc, o_port, o_priv, pad;
 };
 
