@@ -155,6 +155,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=4, help="workload 1..5 (default 4: k=8 fat-tree, E=4096)")
     ap.add_argument("--n-exp", type=int, default=0, help="first n experiments only (default: the full batch)")
+    ap.add_argument("--exp-ids", type=str, default="",
+                    help="comma-separated experiment indices of the config to run instead (e.g. 21: one C3 A=16, K=1 broadcast)")
     ap.add_argument("--cpu-sample", type=int, default=32,
                     help="experiments in the CPU-oracle sample, evenly strided over the batch (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -197,13 +199,14 @@ def main():
     from experiment_network_simulation_amd.sim import KERNEL_NAMES, Sim
 
     cid = args.config
-    n = args.n_exp or I.FULL_E[cid]
-    chunk = args.chunk or (2048 if cid == 5 and n > 2048 else 0)
+    ids = [int(v) for v in args.exp_ids.split(",") if v.strip()] if args.exp_ids else None
+    n = len(ids) if ids else (args.n_exp or I.FULL_E[cid])
+    chunk = 0 if ids else (args.chunk or (2048 if cid == 5 and n > 2048 else 0))
     if chunk and chunk < n:
         return chunked_bench(args, cid, n, chunk)
     log(f"[bench] generating config C{cid} with {n} experiments")
     t = time.perf_counter()
-    batch = I.make_config(cid, n_exp=n)
+    batch = I.make_config(cid, exp_ids=ids) if ids else I.make_config(cid, n_exp=n)
     log(f"[bench] generated in {time.perf_counter() - t:.1f}s; compiling")
     t = time.perf_counter()
     sim = Sim(batch, force_global=args.force_global, no_ring_path=args.no_ring_path)
@@ -297,6 +300,7 @@ def main():
         "config": {
             "workload": I.CONFIG_NAMES[cid],
             "experiments": n,
+            **({"exp_ids": ids} if ids else {}),
             "pkt_bytes": I.PKT_BYTES,
             "experiment_ticks_per_s": exp_ticks * args.steps / wall,
             "packet_hops_per_step": hops,
@@ -388,7 +392,7 @@ def chunked_bench(args, cid, n, chunk):
         kk = min(args.cpu_sample, n)
         sample = sorted(set(int(round(i * n / kk)) for i in range(kk)) - {n})
         threads = args.cpu_threads or min(16, os.cpu_count() or 1, len(sample))
-        sb = I.make_config(cid, exp_ids=sample)
+        sb = I.make_config(cid, exp_ids=[ids[i] for i in sample] if ids else sample)
         sres = {key: v[sample] for key, v in res.items()}
         rate, dt, chops, ok, oticks = cpu_baseline(sb, sres, list(range(len(sample))), threads)
         cpu = cpu_record(rate, dt, chops, ok, oticks, threads, len(sample), n, hops / k_s)

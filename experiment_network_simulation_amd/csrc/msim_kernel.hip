@@ -30,8 +30,9 @@
  * atomics between the ports of one switch, inside one wavefront: on the
  * rate-1 compact path an output hands the slot it popped back to its ingress
  * (OR) and counts the pop (add); on the ring path an output hands back the
- * slot and an emptied-queue bit (OR) and counts the pop (add), and an ingress
- * marks a queue non-empty in its output's word (OR).  Several ports of a
+ * slot and an emptied-queue bit (OR) into a word the ingress and the port
+ * feeding it read next tick, and an ingress marks a queue non-empty in its
+ * output's word (OR).  Several ports of a
  * switch may hit the same word in one instruction; OR and add do not depend on
  * the order they are applied in, so results are identical on every run.  The
  * other atomics: each workgroup claiming its next experiment, the general
