@@ -392,7 +392,7 @@ def chunked_bench(args, cid, n, chunk):
         kk = min(args.cpu_sample, n)
         sample = sorted(set(int(round(i * n / kk)) for i in range(kk)) - {n})
         threads = args.cpu_threads or min(16, os.cpu_count() or 1, len(sample))
-        sb = I.make_config(cid, exp_ids=[ids[i] for i in sample] if ids else sample)
+        sb = I.make_config(cid, exp_ids=sample)
         sres = {key: v[sample] for key, v in res.items()}
         rate, dt, chops, ok, oticks = cpu_baseline(sb, sres, list(range(len(sample))), threads)
         cpu = cpu_record(rate, dt, chops, ok, oticks, threads, len(sample), n, hops / k_s)
