@@ -129,23 +129,24 @@ def lds_bandwidth(reps: int = 5) -> dict:
 
 
 def measured_traffic(kernel: str, workload_cfg: int, n: int):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on this kernel source and this workload; else None."""
+    """HBM bytes per launch (for a chunked run: over all its launches) from the
+    committed rocprofv3 counter runs in profiles/traffic.json, if one was
+    taken on this kernel source, this kernel and this workload; else None."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     try:
-        rec = json.load(open(os.path.join(here, "profiles", "traffic.json")))
+        recs = json.load(open(os.path.join(here, "profiles", "traffic.json")))
     except (OSError, ValueError):
         return None
     csrc = os.path.join(here, "experiment_network_simulation_amd", "csrc")
     h = hashlib.sha256()
     for f in ("msim_kernel.hip", "msim_layout.h"):
         h.update(open(os.path.join(csrc, f), "rb").read())
-    if rec.get("kernel") != kernel or rec.get("kernel_source_sha256") != h.hexdigest():
-        return None
-    if workload_cfg != 4 or n != 4096:
-        return None
-    return rec["traffic_bytes_per_launch"]
+    for rec in recs if isinstance(recs, list) else [recs]:
+        if (rec.get("kernel") == kernel and rec.get("kernel_source_sha256") == h.hexdigest()
+                and rec.get("config") == workload_cfg and rec.get("experiments") == n):
+            return rec["traffic_bytes_per_launch"]
+    return None
 
 
 def main():
@@ -423,7 +424,10 @@ def chunked_bench(args, cid, n, chunk):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": alg_bytes / k_s / 1e9 / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("+".join(sorted(kernels)), cid, n),
+            "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE over all launches of this run's kernel source and "
+                              "workload, in profiles/traffic.json, each scaled by a plain copy's calibration (null: "
+                              "not measured for this source)",
             "kernel": "+".join(sorted(kernels)),
             "kernel_ms_avg": k_s * 1e3 / len(ids),
             "alg_bytes_per_launch": alg_bytes / len(ids),
