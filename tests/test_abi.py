@@ -276,3 +276,44 @@ def test_lds_probe_rejects_bad_arguments(simmod):
     assert lib.msim_lds_probe(1, 4096, 0, 1, None) == E             # no workgroups
     assert lib.msim_lds_probe(1, 8 << 30, (1 << 20) + 1, 1, None) == E
     assert lib.msim_lds_probe(1, 4096, 1, 0, None) == E             # no iterations
+
+
+def test_bench_traffic_records(tmp_path, monkeypatch):
+    """The bench line's measured HBM traffic comes from profiles/traffic.json
+    only for the kernel, workload and kernel source it was taken on: a
+    different kernel, config, experiment count or source text gives None."""
+    import importlib
+    import json
+    import shutil
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    # a copy of the tree's bench, its profiles record and the kernel sources
+    for d in ("profiles", os.path.join("experiment_network_simulation_amd", "csrc")):
+        os.makedirs(tmp_path / d, exist_ok=True)
+    shutil.copy(os.path.join(root, "bench.py"), tmp_path / "bench.py")
+    for f in ("msim_kernel.hip", "msim_layout.h"):
+        shutil.copy(os.path.join(root, "experiment_network_simulation_amd", "csrc", f),
+                    tmp_path / "experiment_network_simulation_amd" / "csrc" / f)
+    recs = json.load(open(os.path.join(root, "profiles", "traffic.json")))
+    json.dump(recs, open(tmp_path / "profiles" / "traffic.json", "w"))
+    monkeypatch.syspath_prepend(str(tmp_path))
+    sys.modules.pop("bench", None)
+    bench = importlib.import_module("bench")
+    assert bench.__file__.startswith(str(tmp_path))
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("msim_kernel.hip", "msim_layout.h"):
+        h.update(open(tmp_path / "experiment_network_simulation_amd" / "csrc" / f, "rb").read())
+    for r in recs:
+        # a record taken on an older source is simply not used
+        want = r["traffic_bytes_per_launch"] if r["kernel_source_sha256"] == h.hexdigest() else None
+        assert bench.measured_traffic(r["kernel"], r["config"], r["experiments"]) == want
+        assert bench.measured_traffic(r["kernel"] + "_x", r["config"], r["experiments"]) is None
+        assert bench.measured_traffic(r["kernel"], r["config"] + 1, r["experiments"]) is None
+        assert bench.measured_traffic(r["kernel"], r["config"], r["experiments"] - 1) is None
+    # any edit of the kernel source, a comment included, retires the records
+    k = tmp_path / "experiment_network_simulation_amd" / "csrc" / "msim_layout.h"
+    k.write_text(k.read_text() + "\n")
+    for r in recs:
+        assert bench.measured_traffic(r["kernel"], r["config"], r["experiments"]) is None
+    sys.modules.pop("bench", None)
