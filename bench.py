@@ -56,10 +56,20 @@ def cpu_baseline(batch, gpu_res, sample_ids, threads):
     how many sampled experiments the GPU matched exactly."""
     from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle as O
+    import threading
     ob = O.OracleBatch(batch.pack())
     t0 = time.perf_counter()
+    lock, finished = threading.Lock(), [0]
+
+    def one(e):
+        r = O.run(ob, e)
+        with lock:
+            finished[0] += 1
+            log(f"[bench] CPU oracle: {finished[0]}/{len(sample_ids)} experiments done "
+                f"({time.perf_counter() - t0:.0f}s)")
+        return r
     with ThreadPoolExecutor(threads) as ex:
-        res = list(ex.map(lambda e: O.run(ob, e), sample_ids))
+        res = list(ex.map(one, sample_ids))
     dt = time.perf_counter() - t0
     hops = sum(r["pkt_hops"] for r in res)
     ticks = sum(r["t_end"] + 1 for r in res)
