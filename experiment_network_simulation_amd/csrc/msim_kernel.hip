@@ -2120,11 +2120,11 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
                 /* link behind the queue's tail, or make it the head; the
                  * output's non-empty bit is already set when the queue holds
                  * packets, so setting it again changes nothing */
-                LDSP uint8_t *lnk = __builtin_amdgcn_ubfe(ne, o, 1) ? pn_me + __umul24(__builtin_amdgcn_ubfe(tails, o4, 4), S)
-                                                                     : head + hb0 + 8 * o;
+                const uint32_t tl = __builtin_amdgcn_ubfe(tails, o4, 4);
+                LDSP uint8_t *lnk = __builtin_amdgcn_ubfe(ne, o, 1) ? pn_me + __umul24(tl, S) : head + hb0 + 8 * o;
                 *lnk = (uint8_t)s;
                 __hip_atomic_fetch_or(nzw + pr.row + o, 1u << local, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                tails = (tails & ~(15u << o4)) | (s << o4);
+                tails += (s - tl) << o4;                          /* the tail nibble becomes s */
                 ne |= 1u << o;
             }
             wave_lds_fence();
@@ -2137,7 +2137,9 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
             uint32_t out = 0;
             const bool go = nz != 0 && pushed - seen < qcap;
             if constexpr (PK < 2) {
-                if (__ballot(go) != 0ull) last_w = t + 1;          /* every delay is 1: the wavefront's latest send */
+                /* every delay is 1: the wavefront's latest send (the two lane
+                 * masks the comparisons already produce) */
+                if ((__ballot(nz != 0) & __ballot(pushed - seen < qcap)) != 0ull) last_w = t + 1;
             }
             if (go) {
                 /* nz != 0; bits at or above deg are 0, so a search from
