@@ -1903,9 +1903,16 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
  *     the remaining route;
  *   - a switch output finds its candidates in an 8-bit word of non-empty
  *     inputs, pops from the head slot row, and hands the freed slot (and an
- *     emptied queue) back to the ingress with one LDS atomic OR, which the
- *     ingress folds in once at the end of the tick, publishing its pop count
- *     for the credit its feeder reads next tick.
+ *     emptied queue) back to the ingress with one LDS atomic OR into a word
+ *     of this tick's parity.  At the next tick's first read round the
+ *     ingress folds that word into its registers and the port feeding it
+ *     counts its slot bits as pops for its credit; the ingress clears the
+ *     word a tick later, before its outputs write it again;
+ *   - hosts queue each received (flow, RD) word in LDS, and a wavefront
+ *     mixes every host's queue into the digest together once one is full;
+ *   - host, switch and empty wavefronts run separate copies of the tick loop
+ *     (same barriers), and when every delay is 1 ticks run in even/odd pairs
+ *     so every staging and hand-back address is a loop constant.
  * The atomic ORs are the one many-to-one write: up to 8 outputs of a switch
  * may hand back slots of the same ingress, or mark the same output's word,
  * in one instruction.  OR is order-independent, so results do not depend on
