@@ -703,7 +703,9 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
         C.fcur[vi] = (uint8_t)f;
         C.hseen[vi] = (uint8_t)((o < 8 ? g0 : g1) >> sh);
     }
-    if (popped) pw.popped += popped;
+    /* the far output's credit count: it reads it from its own port state,
+     * so this scattered write happens only when slots were freed */
+    if (popped) C.ps[pr.peer].popped += popped;
     /* append the packets that arrive now */
     uint32_t si = q * C.W + slot;
     uint32_t n = C.scnt[si];
@@ -765,7 +767,7 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
     const HostRO hr = C.host[pr.host];
     if (!pr.alive || hr.n_out == 0) return;
     PortRW &pw = C.ps[p];
-    int32_t credit = (int32_t)C.Q - (int32_t)(pw.pushed - C.ps[pr.peer].popped);
+    int32_t credit = (int32_t)C.Q - (int32_t)(pw.pushed - pw.popped);
     uint32_t rr = pw.rr, pushed = pw.pushed;
     const uint32_t nw = (hr.n_out + 31) >> 5;
     uint32_t *rdy = C.ready + hr.rdy_off;
@@ -831,7 +833,7 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
     const uint32_t deg = pr.deg, lo = pr.local, Q = C.Q;
     PortRW &pw = C.ps[p];
     int32_t credit = pr.peer_is_host ? (int32_t)pr.rate
-                                     : (int32_t)Q - (int32_t)(pw.pushed - C.ps[pr.peer].popped);
+                                     : (int32_t)Q - (int32_t)(pw.pushed - pw.popped);
     uint32_t rr = pw.rr, pushed = pw.pushed;
     const uint32_t prow = pr.vbase + lo * deg;     /* popper-major row of this output */
     /* packets waiting at each input for this output: appended - popped, bytewise */
@@ -942,8 +944,17 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     const uint32_t ro_hot = H->ro_hot, rw_hot = H->rw_hot;
     /* placement: the whole arena in LDS (IN_LDS); else, if it fits, only the
      * switch / NIC state ([0, ro_hot) then [rw_off, rw_hot), back to back);
-     * else all in HBM */
+     * else, if it fits, only the port table, which every port reads twice a
+     * tick; else all in HBM */
     const bool split = !IN_LDS && kp.lds_bytes && ro_hot + (rw_hot - rw_off) <= kp.lds_bytes;
+    const uint32_t port_b = (H->n_ports * (uint32_t)sizeof(PortRO) + 15u) & ~15u;
+    const bool ports = !IN_LDS && !split && kp.lds_bytes && port_b <= kp.lds_bytes;
+    if (ports) {
+        const uint4 *src = (const uint4 *)(arena_g + H->o_port);
+        uint4 *dst = (uint4 *)lds;
+        for (uint32_t i = tid; i < port_b / 16; i += nth) dst[i] = src[i];
+        __syncthreads();
+    }
     if (IN_LDS || split) {
         const uint4 *src = (const uint4 *)arena_g;
         uint4 *dst = (uint4 *)lds;
@@ -963,7 +974,7 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
         return arena_g + off;
     };
     Ctx C;
-    C.port = (const PortRO *)at(H->o_port);
+    C.port = ports ? (const PortRO *)lds : (const PortRO *)at(H->o_port);
     C.conn = (const ConnRO *)at(H->o_conn);
     C.grp = (const Grp *)at(H->o_grp);
     C.hout = (const uint32_t *)at(H->o_hout);

@@ -116,7 +116,7 @@ struct HostRO {          /* 16 bytes */
 };
 
 struct PortRW {          /* 16 bytes */
-    uint32_t popped;     /* switch ingress: packets forwarded out of it (phase A) */
+    uint32_t popped;     /* output: packets its far switch ingress has forwarded (that ingress adds them in phase A) */
     uint32_t pushed;     /* output: packets sent on it (phase D) */
     uint32_t rr;         /* output: round-robin pointer */
     uint32_t ftop;       /* switch ingress: free-slot stack height */
@@ -242,7 +242,8 @@ struct ArenaHdr {        /* general format header */
      * switch phases and the host NICs touch each tick (ports, hosts, queues,
      * pools, staging, backlogs, host state); a workgroup that cannot hold the
      * whole arena in LDS copies these two ranges there, back to back, and
-     * leaves the per-connection state in HBM */
+     * leaves the per-connection state in HBM; one that cannot hold these
+     * either copies the port table alone (n_ports PortRO from o_port) */
     uint32_t ro_hot, rw_hot;
     /* HPCC (cc = 3): general-path descriptors are conn << cshift | telemetry
      * record << 4 | switches passed (cshift = DESC_SHIFT otherwise); hx
