@@ -56,7 +56,7 @@ struct Compiled {
     uint64_t n_flows = 0, n_conns = 0, n_ports = 0;
     uint64_t est_hops = 0, est_delivered = 0;
     uint64_t est_ticks = 0;  /* busiest link: packets over rate, flows on their ECMP paths (a lower bound on ticks unless sprayed) */
-    uint64_t est_ring = 0;   /* longest ring's contention-free duration estimate (0: no ring) */
+    uint64_t ring_pmin = 0;  /* smallest ring chunk in packets (0: no ring) */
     uint32_t n_task = 0, o_trw = 0;   /* task graph (general format) */
     uint32_t split_bytes = 0;         /* general format: LDS bytes of the switch/NIC state alone */
     uint32_t port_bytes = 0;          /* general format: LDS bytes of the port table alone */
@@ -293,9 +293,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
                 Grp g{};
                 g.kind = kind; g.N = N; g.S = S; g.R = (uint32_t)R; g.p = (uint32_t)p; g.X = (uint32_t)X;
                 g.fid_base = (uint32_t)fid; g.conn_base = (uint32_t)conn.size(); g.link = gate_grp;
-                /* R rounds of S chunk steps, each about a path latency (~6
-                 * ticks on the fabrics used) plus p - 1 packets */
-                out.est_ring = std::max<uint64_t>(out.est_ring, R * S * (p + 5));
+                out.ring_pmin = out.ring_pmin ? std::min<uint64_t>(out.ring_pmin, p) : p;
                 fid += R * S * N;
                 if (fid >= MSIM_NONE) return fail(out, MSIM_E_LIMIT, "experiment %u: too many flows", e);
                 for (uint32_t i = 0; i < N; i++) {
@@ -1113,21 +1111,21 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
         }
     }
     /* longest-processing-time order: the longest experiments are claimed
-     * first, by an estimate of their duration.  Ring-format experiments
-     * (equal bytes each) take the rings' contention-free duration: their
-     * ticks follow the busiest link's load more closely (correlation 0.96
-     * against 0.89 on the k=8 fat-tree batch), but the whole batch finished
-     * 0.7 % later in that order, the cost of a tick varying with the channel
-     * count.  Every other kind takes the busiest link's load, then
-     * packet-hops (on the k=16 fat-tree all-to-all batch, 2.8 % sooner than
-     * packet-hops alone) */
+     * first, by an estimate of their duration: the busiest link's load (a
+     * bound on the ticks), then packet-hops.  A ring-format tick costs more
+     * the smaller the chunks, each chunk's end being a flow's completion and
+     * the next one's start at every rank: measured on the k=8 fat-tree
+     * batch, about 1,058 + 5,400 / p cycles per tick for chunks of p
+     * packets, so those experiments weigh their load by (p + 4) / p for
+     * their smallest chunk (duration correlation 0.95 against 0.89 for the
+     * load alone) */
     ctx->order.resize(E);
     for (uint32_t e = 0; e < E; e++) ctx->order[e] = e;
     std::stable_sort(ctx->order.begin(), ctx->order.end(), [&](uint32_t a, uint32_t b) {
         const Compiled &x = ctx->exps[a], &y = ctx->exps[b];
         if (x.kind != y.kind) return x.kind < y.kind;
-        const uint64_t ex = x.kind == KIND_RING ? x.est_ring : x.est_ticks,
-                       ey = y.kind == KIND_RING ? y.est_ring : y.est_ticks;
+        const uint64_t ex = x.kind == KIND_RING && x.ring_pmin ? x.est_ticks * (x.ring_pmin + 4) / x.ring_pmin : x.est_ticks,
+                       ey = y.kind == KIND_RING && y.ring_pmin ? y.est_ticks * (y.ring_pmin + 4) / y.ring_pmin : y.est_ticks;
         if (ex != ey) return ex > ey;
         return x.est_hops > y.est_hops;
     });
