@@ -745,16 +745,14 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
             take(H.o_hout, (size_t)dt * nconn);
             H.rw_off = (uint32_t)off;
             take(H.o_arr, Vc);
-            if (R != 1) take(H.o_head, Vc);
-            else H.o_head = 0;
+            H.o_head = 0;
             take(H.o_nslot, Vc);
             take(H.o_pdesc, (size_t)dt * S * Q);
             take(H.o_pnxt, (size_t)S * Q);
             take(H.o_popped, 8ull * nt);
             const uint32_t RP = R <= 1 ? 1 : (R <= 2 ? 2 : 4);
             H.o_elig = 0;
-            if (R == 1) take(H.o_fmask, 8ull * S);
-            else H.o_fmask = 0;
+            take(H.o_fmask, 8ull * S);
             take(H.o_sdesc, (size_t)dt * nt * W * RP);
             take(H.o_crw, sizeof(CRW2) * nconn);
             H.lds_bytes = (uint32_t)off;
@@ -821,8 +819,8 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
                         pv[sl].freem = Q == 64 ? ~0ull : ((1ull << Q) - 1ull);
                     }
                 }
-                /* rate 1: every queue starts empty (head byte Q_EMPTY) */
-                if (R == 1) memset(A + H.o_nslot, (int)Q_EMPTY, Vc);
+                /* every queue starts empty (head byte Q_EMPTY) */
+                memset(A + H.o_nslot, (int)Q_EMPTY, Vc);
                 memcpy(A, &H, sizeof H);
                 out.rw_off = H.rw_off;
                 out.bytes = H.bytes;

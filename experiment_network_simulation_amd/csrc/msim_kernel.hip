@@ -23,13 +23,13 @@
  *     eligible input going round from its pointer and stages the packet for
  *     t + delay; barrier;
  *   compact and ring paths (run_compact, run_ring): one thread per port with
- *     every port of a switch inside one wavefront, so arrivals, forwarding
- *     and (faster links) frees of a tick run in program order within the
- *     wavefront and one barrier ends the tick.
+ *     every port of a switch inside one wavefront, so the arrivals and the
+ *     forwarding of a tick run in program order within the wavefront and one
+ *     barrier ends the tick.
  * Writers.  Most state has one writer per phase.  The exceptions are LDS
  * atomics between the ports of one switch, inside one wavefront: on the
- * rate-1 compact path an output hands the slot it popped back to its ingress
- * (OR) and counts the pop (add); on the ring path an output hands back the
+ * compact path an output hands the slot it popped back to its ingress (OR)
+ * and counts the pop (add); on the ring path an output hands back the
  * slot and an emptied-queue bit (OR) into a word the ingress and the port
  * feeding it read next tick, and an ingress marks a queue non-empty in its
  * output's word (OR).  Several ports of a
@@ -1140,14 +1140,14 @@ struct Row {
 /* LDS-qualified pointers keep address arithmetic in 32 bits. */
 template <typename DT>
 struct CCtx {
-    LDSP uint8_t *arr, *head, *nslot, *pnxt;
+    LDSP uint8_t *arr, *nslot, *pnxt;
     LDSP uint32_t *popped;     /* [2][nt], tick parity */
     const LDSP uint32_t *route;
     const LDSP DT *hout;
     const LDSP uint16_t *cgrp;
     const LDSP uint8_t *lidx;
     LDSP CRW2 *crw;
-    LDSP uint64_t *fmask;      /* rate 1: per switch ingress (slot - SB), slots its outputs returned */
+    LDSP uint64_t *fmask;      /* per switch ingress (slot - SB), slots its outputs returned */
     LDSP uint8_t *L;           /* the LDS image, and byte offsets of two of its arrays */
     uint32_t o_nslot, o_pnxt;
     const LDSP CGrp *grp;
@@ -1504,15 +1504,17 @@ __device__ __forceinline__ void wave_lds_fence()
 /*
  * One tick t of a compact experiment, per wavefront, with one workgroup
  * barrier at its end:
- *   arrivals    switch ingress: packets with arrival tick t join their queue;
- *               host: deliveries, then activations (Schedule);
- *   forwarding  every output pulls while credit lasts (credit from the far
- *               ingress's popped count through t-1, published last tick);
- *   frees       switch ingress: releases the slots its egresses popped during
- *               this tick and publishes its popped count for tick t+1.
+ *   arrivals    switch ingress: zeroes its pop count for tick t, then the
+ *               packets with arrival tick t join their queue, in slots taken
+ *               from its free mask; host: deliveries, then activations
+ *               (Schedule);
+ *   forwarding  every output pulls, up to its rate, while credit lasts (the
+ *               far ingress's pops through t-1, added up tick by tick); each
+ *               pop returns its slot to the ingress's free word and counts in
+ *               the ingress's pop count for tick t.
  * Arrivals read staging written at least one barrier earlier (delay >= 1);
  * forwarding reads queues filled by the arrivals of the same switch (same
- * wavefront); the frees read heads advanced by the same switch's outputs.
+ * wavefront), and the slots it returns are taken again from the next tick on.
  */
 template <int W, typename DT, bool R1, bool X>
 __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
@@ -1538,7 +1540,6 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     LDSP uint8_t *L = (LDSP uint8_t *)lds;
     CCtx<DT> C;
     C.arr = L + H->o_arr;
-    C.head = L + H->o_head;
     C.nslot = L + H->o_nslot;
     C.pnxt = L + H->o_pnxt;
     C.popped = (LDSP uint32_t *)(L + H->o_popped);
@@ -1573,13 +1574,6 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     const bool peer_host = pr.flags & PF_PEER_HOST;
     constexpr uint32_t RSZ = 8u * W;              /* bytes per VOQ row: one per input port */
     const uint32_t deg = pr.deg, local = pr.local, Q = C.Q;
-    /* byte rows of the counter-based queues (rate-1 kinds keep their queue state in LDS) */
-    Row<W> tslot, fcur, hseen, phead, arrv;
-    tslot.w0 = R1 ? 0 : pv.tslot[0]; tslot.w1 = R1 ? 0 : pv.tslot[1];
-    fcur.w0 = R1 ? 0 : pv.fcur[0]; fcur.w1 = R1 ? 0 : pv.fcur[1];
-    hseen.w0 = R1 ? 0 : pv.hseen[0]; hseen.w1 = R1 ? 0 : pv.hseen[1];
-    phead.w0 = R1 ? 0 : pv.phead[0]; phead.w1 = R1 ? 0 : pv.phead[1];
-    arrv.w0 = R1 ? 0 : pv.arrv[0]; arrv.w1 = R1 ? 0 : pv.arrv[1];
     uint64_t freem = pv.freem;                     /* switch ingress: free buffer slots */
     uint32_t popped = pv.popped, pushed = pv.pushed, rr = pv.rr;
     HostRegs hr;
@@ -1611,13 +1605,18 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     uint32_t t_dead = 0;
     while (t < t_end) {
         /* ---------------- arrivals */
-        if (R1 && is_sw) {
-            /* rate 1: at most one packet per ingress and tick.  This tick's pop
-             * count starts at zero; the outputs of this switch add to it while
-             * they forward, and the far outputs read it during tick t+1. */
+        if (is_sw) {
+            /* this tick's pop count starts at zero; the outputs of this switch
+             * add to it while they forward, and the far outputs read it during
+             * tick t+1.  At most RP packets arrive per ingress and tick. */
             C.popped[tp + tid] = 0;
-            const uint32_t e = C.sdesc[sb + myoff];
-            if (e != 0) {
+            LDSP DT *rec = C.sdesc + sb + myoff;
+            bool any = false;
+            for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
+                const uint32_t e = rec[k];
+                if (e == 0) break;
+                any = true;
+                /* e = descriptor + 1: the same packet with its hop index advanced */
                 const uint32_t desc = e - 1;
                 const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
                 const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
@@ -1629,36 +1628,8 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     freem = __hip_atomic_exchange(C.fmask + pool, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 if (freem == 0 || o >= deg) {
                     a.fault = 1;
-                } else {
-                    uint32_t s;
-                    if (q32) {
-                        const uint32_t lo = (uint32_t)freem;
-                        s = __builtin_ctz(lo);
-                        freem = lo & (lo - 1u);
-                    } else {
-                        s = __builtin_ctzll(freem);
-                        freem &= freem - 1;
-                    }
-                    C.pdesc[cpool(C, pool, s)] = (DT)e;
-                    /* an empty queue has the head byte Q_EMPTY: the new slot
-                     * becomes its head, else it goes behind the tail */
-                    const uint32_t at_head = C.o_nslot + vq, at_tail = C.o_pnxt + cpool(C, pool, tail);
-                    C.L[head == Q_EMPTY ? at_head : at_tail] = (uint8_t)s;
-                    C.arr[vq] = (uint8_t)s;
+                    continue;
                 }
-            }
-        } else if (is_sw) {
-            LDSP DT *rec = C.sdesc + sb + myoff;
-            bool any = false;
-            for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
-                const uint32_t e = rec[k];
-                if (e == 0) break;
-                any = true;
-                /* e = descriptor + 1: the same packet with its hop index advanced */
-                const uint32_t desc = e - 1;
-                const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
-                const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
-                if (freem == 0 || o >= deg) { a.fault = 1; continue; }
                 uint32_t s;
                 if (q32) {
                     const uint32_t lo = (uint32_t)freem;
@@ -1669,20 +1640,16 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     freem &= freem - 1;
                 }
                 C.pdesc[cpool(C, pool, s)] = (DT)e;
-                const uint32_t av = arrv.get(o);
-                const uint32_t vp = pr.vbase + o * RSZ + local;
-                if (av == hseen.get(o)) {
-                    C.nslot[vp] = (uint8_t)s;
-                    if (!R1) fcur.set(o, s);
-                } else {
-                    C.pnxt[cpool(C, pool, tslot.get(o))] = (uint8_t)s;
-                }
-                tslot.set(o, s);
-                arrv.set(o, av + 1);
-                C.arr[vp] = (uint8_t)(av + 1);
+                /* an empty queue has the head byte Q_EMPTY: the new slot
+                 * becomes its head, else it goes behind the tail */
+                const uint32_t at_head = C.o_nslot + vq, at_tail = C.o_pnxt + cpool(C, pool, tail);
+                C.L[head == Q_EMPTY ? at_head : at_tail] = (uint8_t)s;
+                C.arr[vq] = (uint8_t)s;
             }
-            if (any)
-                for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) rec[k] = 0;
+            /* rate 1: the feeding output rewrites its entry every tick; faster
+             * links stage only what they send, so the reader clears */
+            if (!R1 && any)
+                for (uint32_t k = 0; k < C.RP; k++) rec[k] = 0;
         } else if (is_host) {
             LDSP DT *rec = C.sdesc + sb + myoff;
             /* the ring-only copy costs registers the faster-link kinds do not have */
@@ -1703,67 +1670,49 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
         uint32_t dst = sb + doff;
         if (dst >= wsz) dst -= wsz;
         dst += poff;
-        if (R1 && is_sw && alive) {
-            /* rate 1: one grant at most, cyclic from rr over the non-empty
-             * queues toward this output, read from its row of head bytes;
-             * the credit counts the far ingress's pops through t-1 */
+        if (is_sw && alive) {
+            /* up to rate grants, each cyclic from rr over the non-empty queues
+             * toward this output, read from its row of head bytes; the credit
+             * counts the far ingress's pops through t-1 */
             if (!peer_host) popped += C.popped[(tp ^ nt) + pr.peer];
-            const int32_t credit = peer_host ? 1 : (int32_t)Q - (int32_t)(pushed - popped);
+            int32_t credit = peer_host ? (int32_t)pr.rate : (int32_t)Q - (int32_t)(pushed - popped);
             Row<W> hrow, trow;
             hrow.load(C.nslot + rowp);
             trow.load(C.arr + rowp);
             const uint64_t F = 0x8080808080808080ull;          /* a slot byte < 64 has bit 7 clear */
-            const int i = first_from<W>(~hrow.w0 & F, W == 2 ? (~hrow.w1 & F) : 0ull, rr);
-            uint32_t out = 0;                                          /* staged entry: desc + 1, or 0 */
-            if (i >= 0 && credit > 0) {
+            uint32_t out = 0;                                          /* rate 1: staged entry, desc + 1 or 0 */
+            for (uint32_t m = 0; m < (R1 ? 1u : pr.rate) && credit > 0; m++) {
+                const int i = first_from<W>(~hrow.w0 & F, W == 2 ? (~hrow.w1 & F) : 0ull, rr);
+                if (i < 0) break;
                 const uint32_t vq = rowp + (uint32_t)i;                 /* queue (i, this output) */
                 const uint32_t qpool = qbase + (uint32_t)i - SB;
                 const uint32_t s = hrow.get((uint32_t)i);
                 const uint32_t desc = C.pdesc[cpool(C, qpool, s)];
                 const uint32_t next = C.pnxt[cpool(C, qpool, s)];
                 /* popping the tail empties the queue */
-                C.nslot[vq] = (uint8_t)(s == trow.get((uint32_t)i) ? Q_EMPTY : next);
+                const uint32_t nh = s == trow.get((uint32_t)i) ? Q_EMPTY : next;
+                C.nslot[vq] = (uint8_t)nh;
+                if (!R1) hrow.set((uint32_t)i, nh);
                 /* the slot goes back to the ingress and the pop into its count
                  * for this tick (other outputs of this switch may hit the same
                  * ingress in the same instruction) */
                 __hip_atomic_fetch_or(C.fmask + qpool, 1ull << s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 __hip_atomic_fetch_add(C.popped + tp + qbase + (uint32_t)i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 rr = (uint32_t)i + 1 == deg ? 0 : (uint32_t)i + 1;
-                out = desc + 1;
-                a.last_tx1 = t + 1;
-                pushed++;
-            }
-            /* written every tick, so the far ingress never clears what it read */
-            C.sdesc[dst] = (DT)out;
-        } else if (is_sw && alive) {
-            Row<W> ar;
-            ar.load(C.arr + rowp);
-            int32_t credit = peer_host ? (int32_t)pr.rate : (int32_t)Q - (int32_t)(pushed - C.popped[tp + pr.peer]);
-            uint64_t v0 = bytes_sub(ar.w0, phead.w0);
-            uint64_t v1 = W == 2 ? bytes_sub(ar.w1, phead.w1) : 0ull;
-            for (uint32_t m = 0; m < (R1 ? 1u : pr.rate) && credit > 0; m++) {
-                const int i = first_from<W>(bytes_nz(v0), bytes_nz(v1), rr);
-                if (i < 0) break;
-                const uint32_t vp = rowp + (uint32_t)i;
-                const uint32_t qpool = qbase + (uint32_t)i - SB;
-                const uint32_t s = C.nslot[vp];
-                const uint32_t desc = C.pdesc[cpool(C, qpool, s)];
-                C.nslot[vp] = C.pnxt[cpool(C, qpool, s)];
-                const uint32_t hb = phead.get((uint32_t)i) + 1;
-                phead.set((uint32_t)i, hb);
-                C.head[pr.vbase + (uint32_t)i * RSZ + local] = (uint8_t)hb;   /* running pop count */
-                if (!R1) {
-                    if (i < 8) v0 -= 1ull << (8 * i);
-                    else v1 -= 1ull << (8 * (i - 8));
+                if (R1) {
+                    out = desc + 1;
+                    a.last_tx1 = t + 1;
+                } else {
+                    ctransmit(C, a, desc, t, dst + m);
                 }
-                rr = (uint32_t)i + 1 == deg ? 0 : (uint32_t)i + 1;
-                ctransmit(C, a, desc, t, dst + m);
                 pushed++;
                 credit--;
             }
+            /* written every tick, so the far ingress never clears what it read */
+            if (R1) C.sdesc[dst] = (DT)out;
         } else if (is_host && alive && pr.n_out) {
-            if (R1) popped += C.popped[(tp ^ nt) + pr.peer];
-            int32_t credit = (int32_t)Q - (int32_t)(pushed - (R1 ? popped : C.popped[tp + pr.peer]));
+            popped += C.popped[(tp ^ nt) + pr.peer];
+            int32_t credit = (int32_t)Q - (int32_t)(pushed - popped);
             uint32_t out = 0;      /* rate 1: the staged entry, written every tick (0 when idle) */
             for (uint32_t m = 0; m < (R1 ? 1u : pr.rate) && credit > 0 && hr.ready; m++) {
                 const uint64_t rot = rr ? (hr.ready >> rr) | (hr.ready << (64 - rr)) : hr.ready;
@@ -1806,33 +1755,6 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             if (R1) C.sdesc[dst] = (DT)out;
         }
         wave_lds_fence();
-        /* ---------------- frees, and the popped count for tick t+1 */
-        if (!R1 && is_sw) {
-            Row<W> hd;
-            hd.load(C.head + rowp);
-            uint64_t d0 = bytes_sub(hd.w0, hseen.w0);
-            uint64_t d1 = W == 2 ? bytes_sub(hd.w1, hseen.w1) : 0ull;
-            if (d0 | d1) {
-                uint64_t m0 = bytes_nz(d0), m1 = bytes_nz(d1);
-                while (m0 | m1) {
-                    uint32_t o;
-                    if (m0) { o = __builtin_ctzll(m0) >> 3; m0 &= m0 - 1; }
-                    else { o = 8 + (__builtin_ctzll(m1) >> 3); m1 &= m1 - 1; }
-                    const uint32_t k = (uint32_t)((o < 8 ? d0 : d1) >> (8 * (o & 7))) & 0xFFu;
-                    popped += k;
-                    uint32_t f = fcur.get(o);
-                    for (uint32_t j = 0; j < k; j++) {
-                        const uint32_t s = f;
-                        f = C.pnxt[cpool(C, pool, s)];
-                        if (q32) freem = (uint32_t)freem | (1u << s);
-                        else freem |= 1ull << s;
-                    }
-                    fcur.set(o, f);
-                }
-                hseen = hd;
-            }
-            C.popped[(tp ^ nt) + tid] = popped;
-        }
         t++;
         sb += tstride;
         if (sb == wsz) sb = 0;
@@ -1872,11 +1794,6 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
     }
     if (used) {
         pv = PortPriv{};
-        pv.tslot[0] = tslot.w0; pv.tslot[1] = tslot.w1;
-        pv.fcur[0] = fcur.w0; pv.fcur[1] = fcur.w1;
-        pv.hseen[0] = hseen.w0; pv.hseen[1] = hseen.w1;
-        pv.phead[0] = phead.w0; pv.phead[1] = phead.w1;
-        pv.arrv[0] = arrv.w0; pv.arrv[1] = arrv.w1;
         pv.freem = freem;
         pv.popped = popped; pv.pushed = pushed; pv.rr = rr;
         pv.ready = hr.ready; pv.pcnt = hr.pcnt;

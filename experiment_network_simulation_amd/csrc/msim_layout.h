@@ -282,22 +282,17 @@ struct ArenaHdr2 {       /* 144 bytes */
  * entries at (w * nt + p) * RP, entry m = descriptor + 1 of the m-th packet the
  * far output sent for that tick, 0 = empty; RP = the largest rate rounded up
  * to 1, 2 or 4. */
-/* Queues when every link runs at rate 1 (R == 1): the byte of queue (i, o) in
- * o_nslot is its head slot, Q_EMPTY when the queue is empty (slots are < 64),
- * and in o_arr its tail slot.  Each switch ingress keeps its free buffer slots
- * in a register; an output that pops a slot returns it by an atomic OR into
- * the ingress's word of o_fmask (index slot - SB), which the ingress takes back
- * when its register runs dry.  o_head is absent.  With a faster link, o_arr /
- * o_head bytes are running append / pop counts, the free masks live in
- * registers and o_fmask is absent (0).  o_elig is unused (0). */
+/* Queues: the byte of queue (i, o) in o_nslot is its head slot, Q_EMPTY when
+ * the queue is empty (slots are < 64), and in o_arr its tail slot.  Each
+ * switch ingress keeps its free buffer slots in a register; an output that
+ * pops a slot returns it by an atomic OR into the ingress's word of o_fmask
+ * (index slot - SB), which the ingress takes back when its register runs dry.
+ * o_head and o_elig are unused (0). */
 #define Q_EMPTY 0xFFu
-/* popped, [2][nt]: with a faster link, switch ingress counts of packets
- * forwarded, published twice by tick parity: [(t&1) * nt + slot] holds the
- * count through tick t-1 and is written at the end of tick t-1, so tick t's
- * readers in other wavefronts never see a value being overwritten.  At rate
- * 1, [(t&1) * nt + slot] counts the pops of tick t alone: the ingress zeroes
- * it when the tick starts, the outputs of its switch add to it, and the far
- * output adds it to its own running count during tick t+1. */
+/* popped, [2][nt]: [(t&1) * nt + slot] counts the pops from switch ingress
+ * slot during tick t alone: the ingress zeroes it when the tick starts, the
+ * outputs of its switch add to it, and the far output adds it to its own
+ * running count during tick t+1. */
 
 /* Collective group as the compact path reads it: the constant quotients of
  * the flow-size rules are precomputed, and pos / S is umulhi(pos << 8, mS),
@@ -332,11 +327,11 @@ struct PortRO2 {         /* 16 bytes, one per thread slot (HBM) */
 #define PF_PEER_HOST 4u
 #define PF_USED 8u
 
-struct PortPriv {        /* 144 bytes: registers of a thread slot between runs */
-    uint64_t tslot[2], fcur[2], hseen[2], phead[2], arrv[2];
+struct PortPriv {        /* 64 bytes: registers of a thread slot between runs */
     uint64_t freem;      /* switch ingress: free buffer slots */
     uint64_t ready;      /* host: connections with packets to send */
-    uint32_t popped, pushed, rr, pcnt;
+    uint32_t popped;     /* the far ingress's pops through the last tick */
+    uint32_t pushed, rr, pcnt;
     uint32_t pend[4];
     uint32_t left, pad[3];
 };
