@@ -881,16 +881,12 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
         take(H.o_rwoff, 4ull * (nconn + 1));
     }
     H.rw_off = (uint32_t)off;
-    take(H.o_arr, n_voq);
-    take(H.o_phead, n_voq);
+    take(H.o_tail, n_voq);
     take(H.o_nslot, n_voq);
-    take(H.o_head, n_voq);
-    take(H.o_tslot, n_voq);
-    take(H.o_fcur, n_voq);
-    take(H.o_hseen, n_voq);
+    take(H.o_fmask, 32ull * n_swp);
+    take(H.o_popc, 8ull * n_ports);
     take(H.o_pdesc, 4ull * n_swp * Q);
     take(H.o_pnxt, (size_t)n_swp * Q);
-    take(H.o_fstk, (size_t)n_swp * Q);
     take(H.o_pstate, sizeof(PortRW) * n_ports);
     take(H.o_scnt, (size_t)n_ports * W);
     take(H.o_sdesc, 4ull * n_ports * W * R);
@@ -920,6 +916,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
         for (const Conn &cn : conn) max_lat = std::max(max_lat, cn.lat);
         while (H.WA <= max_lat) H.WA <<= 1;
         take(H.o_bl, 4ull * n_ports);
+        take(H.o_qlen, 4ull * n_ports);
         take(H.o_ackm, 4ull * H.WA * words);
     }
     take(H.o_hstate, sizeof(HostRW) * n_hosts);
@@ -966,12 +963,12 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
     if (ngrp) memcpy(A + H.o_grp, grp.data(), sizeof(Grp) * ngrp);
     if (nconn) memcpy(A + H.o_hout, hout.data(), 4ull * nconn);
     if (n_hosts) memcpy(A + H.o_host, host.data(), sizeof(HostRO) * n_hosts);
-    PortRW *ps = (PortRW *)(A + H.o_pstate);
+    /* every queue starts empty, every buffer slot free */
+    memset(A + H.o_nslot, (int)Q_EMPTY, n_voq);
     for (uint32_t p = 0; p < n_ports; p++) {
         if (port[p].is_host) continue;
-        uint8_t *fs = A + H.o_fstk + (size_t)(gport[p].host + gport[p].local) * Q;
-        for (uint32_t k = 0; k < Q; k++) fs[k] = (uint8_t)k;
-        ps[p].ftop = Q;
+        uint64_t *fm = (uint64_t *)(A + H.o_fmask) + 4ull * (gport[p].host + gport[p].local);
+        for (uint32_t k = 0; k < Q; k++) fm[k >> 6] |= 1ull << (k & 63);
     }
     ConnRW *cs = (ConnRW *)(A + H.o_cstate);
     for (uint32_t c = 0; c < nconn; c++) cs[c].r_rem = first_flow_size(grp[conn[c].grp], conn[c].idx);

@@ -71,9 +71,11 @@ struct Ctx {
     const Grp *grp;
     const uint32_t *hout;
     const HostRO *host;
-    uint8_t *arr, *phead, *nslot, *head, *tslot, *fcur, *hseen;
+    uint8_t *tail, *nslot;
     uint32_t *pdesc;
-    uint8_t *pnxt, *fstk;
+    uint8_t *pnxt;
+    uint64_t *fmask;
+    uint32_t *popc, *qlen;
     PortRW *ps;
     uint8_t *scnt;
     uint32_t *sdesc;
@@ -100,13 +102,6 @@ struct Ctx {
     const uint16_t *cand;
     uint32_t *sseq, *rnext, *rbits;
 };
-
-/* per-byte a - b (mod 256) of eight packed bytes */
-__device__ __forceinline__ uint64_t bytes_sub(uint64_t a, uint64_t b)
-{
-    const uint64_t H = 0x8080808080808080ull;
-    return ((a | H) - (b & ~H)) ^ ((a ^ ~b) & H);
-}
 
 /* 0x80 in every byte of d that is not zero */
 __device__ __forceinline__ uint64_t bytes_nz(uint64_t d)
@@ -162,12 +157,18 @@ __device__ __forceinline__ void row_bytes(const uint8_t *p, uint32_t n, uint64_t
         }
 }
 
-/* Sum of the 16 bytes of (w0, w1). */
-__device__ __forceinline__ uint32_t bytes_sum(uint64_t w0, uint64_t w1)
+/* Byte o of a row held as two packed words, and its replacement. */
+__device__ __forceinline__ uint32_t row_get(uint64_t w0, uint64_t w1, uint32_t o)
 {
-    const uint64_t M = 0x00FF00FF00FF00FFull;
-    const uint64_t h = (w0 & M) + ((w0 >> 8) & M) + (w1 & M) + ((w1 >> 8) & M);   /* four 16-bit lanes */
-    return (uint32_t)((h * 0x0001000100010001ull) >> 48);
+    return (uint32_t)(((o < 8 ? w0 : w1) >> (8 * (o & 7))) & 0xFFu);
+}
+
+__device__ __forceinline__ void row_set(uint64_t &w0, uint64_t &w1, uint32_t o, uint32_t v)
+{
+    const uint32_t sh = 8 * (o & 7);
+    const uint64_t keep = ~(0xFFull << sh), b = (uint64_t)(v & 0xFFu) << sh;
+    if (o < 8) w0 = (w0 & keep) | b;
+    else w1 = (w1 & keep) | b;
 }
 
 struct Acc {
@@ -672,43 +673,17 @@ __device__ __forceinline__ bool tasks_pending(const Ctx &C, uint32_t first, uint
 
 __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q, const PortRO &pr, uint32_t slot)
 {
+    /* the packets that arrive now, if any, join the queue toward the egress
+     * their route names; nothing else happens at an ingress */
+    const uint32_t si = q * C.W + slot;
+    const uint32_t n = C.scnt[si];
+    if (n == 0) return;
     const uint32_t deg = pr.deg, i = pr.local, Q = C.Q;
-    const uint32_t vrow = pr.vbase + i * deg;      /* ingress-major row of this ingress */
     const uint32_t qp = pr.host + i;               /* this ingress's buffer pool */
-    uint8_t *pnxt = C.pnxt + qp * Q;
-    uint8_t *fstk = C.fstk + qp * Q;
-    PortRW &pw = C.ps[q];
-    uint32_t ftop = pw.ftop;
-    uint32_t popped = 0;
-    /* free the slots of the packets the egresses took last tick: the pop
-     * counts of this ingress's queues against what it has already freed */
-    uint64_t g0, g1, e0, e1;
-    row_bytes(C.head + vrow, deg, g0, g1);
-    row_bytes(C.hseen + vrow, deg, e0, e1);
-    const uint64_t k0 = bytes_sub(g0, e0), k1 = bytes_sub(g1, e1);
-    uint64_t n0 = bytes_nz(k0), n1 = bytes_nz(k1);
-    while (n0 | n1) {
-        const uint32_t o = n0 ? (uint32_t)__builtin_ctzll(n0) >> 3 : 8u + ((uint32_t)__builtin_ctzll(n1) >> 3);
-        if (o < 8) n0 &= n0 - 1; else n1 &= n1 - 1;
-        const uint32_t sh = 8 * (o & 7);
-        const uint32_t k = (uint32_t)(((o < 8 ? k0 : k1) >> sh) & 0xFFu);
-        const uint32_t vi = vrow + o;
-        popped += k;
-        uint32_t f = C.fcur[vi];
-        for (uint32_t j = 0; j < k; j++) {
-            uint32_t s = f;
-            f = pnxt[s];
-            fstk[ftop++] = (uint8_t)s;
-        }
-        C.fcur[vi] = (uint8_t)f;
-        C.hseen[vi] = (uint8_t)((o < 8 ? g0 : g1) >> sh);
-    }
-    /* the far output's credit count: it reads it from its own port state,
-     * so this scattered write happens only when slots were freed */
-    if (popped) C.ps[pr.peer].popped += popped;
-    /* append the packets that arrive now */
-    uint32_t si = q * C.W + slot;
-    uint32_t n = C.scnt[si];
+    /* its free slots: a 256-bit mask the outputs return slots to */
+    uint64_t *fm = C.fmask + 4u * qp;
+    const uint32_t nw = (Q + 63u) >> 6;
+    uint64_t m0 = fm[0], m1 = nw > 1 ? fm[1] : 0ull, m2 = nw > 2 ? fm[2] : 0ull, m3 = nw > 3 ? fm[3] : 0ull;
     for (uint32_t k = 0; k < n; k++) {
         uint32_t desc = C.sdesc[si * C.R + k];
         uint32_t c, o;
@@ -724,24 +699,30 @@ __device__ __forceinline__ void phase_a_switch(const Ctx &C, Acc &a, uint32_t q,
             c = (desc & ~DESC_MARK) >> C.cshift;
             o = (C.conn[c].route >> (4 * (desc & DESC_HOP_MASK))) & 0xFu;
         }
-        if (ftop == 0 || o >= deg) { a.fault = 1; continue; }   /* cannot happen while credits hold */
+        /* the lowest free slot */
+        uint32_t s;
+        if (m0) { s = (uint32_t)__builtin_ctzll(m0); m0 &= m0 - 1; }
+        else if (m1) { s = 64u + (uint32_t)__builtin_ctzll(m1); m1 &= m1 - 1; }
+        else if (m2) { s = 128u + (uint32_t)__builtin_ctzll(m2); m2 &= m2 - 1; }
+        else if (m3) { s = 192u + (uint32_t)__builtin_ctzll(m3); m3 &= m3 - 1; }
+        else s = Q_EMPTY;
+        if (s == Q_EMPTY || o >= deg) { a.fault = 1; continue; }   /* cannot happen while credits hold */
         /* ECN: marked when the egress's backlog before this tick reaches K */
         if (C.cc && C.bl[pr.base + o] >= C.ecn_k) desc |= DESC_MARK;
-        uint32_t s = fstk[--ftop];
         C.pdesc[qp * Q + s] = C.sp ? desc : desc + 1;    /* ECMP: on to the next switch of the route */
-        uint32_t vi = vrow + o;
-        uint32_t vp = pr.vbase + o * deg + i;
-        if (C.arr[vp] == C.hseen[vi]) {
-            C.nslot[vp] = (uint8_t)s;
-            C.fcur[vi] = (uint8_t)s;
-        } else {
-            pnxt[C.tslot[vi]] = (uint8_t)s;
-        }
-        C.tslot[vi] = (uint8_t)s;
-        C.arr[vp] = (uint8_t)(C.arr[vp] + 1);
+        /* an empty queue (head byte Q_EMPTY) gets s as its head, else s goes
+         * behind its tail */
+        const uint32_t vp = pr.vbase + o * deg + i;
+        if (C.nslot[vp] == Q_EMPTY) C.nslot[vp] = (uint8_t)s;
+        else C.pnxt[qp * Q + C.tail[vp]] = (uint8_t)s;
+        C.tail[vp] = (uint8_t)s;
+        if (C.cc) __hip_atomic_fetch_add(C.qlen + pr.base + o, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    if (n) C.scnt[si] = 0;
-    pw.ftop = ftop;
+    C.scnt[si] = 0;
+    fm[0] = m0;
+    if (nw > 1) fm[1] = m1;
+    if (nw > 2) fm[2] = m2;
+    if (nw > 3) fm[3] = m3;
 }
 
 /* ---------------------------------------------------------------- phase D */
@@ -762,12 +743,29 @@ __device__ __forceinline__ void transmit(const Ctx &C, Acc &a, uint32_t p, const
     a.max_arr = max(a.max_arr, ta);
 }
 
+/* Output p's credit toward a switch buffer: Q minus the packets it sent that
+ * the far ingress has not yet forwarded.  The far switch's outputs count the
+ * packets they take from that ingress during tick t in popc[t & 1][p]; p adds
+ * the count of t - 1 to its running total and clears it for tick t + 1. */
+__device__ __forceinline__ int32_t buffer_credit(const Ctx &C, PortRW &pw, uint32_t p, uint32_t t)
+{
+    uint32_t *pc = C.popc + ((t + 1u) & 1u) * C.n_ports + p;
+    const uint32_t add = *pc;
+    uint32_t popped = pw.popped;
+    if (add) {
+        *pc = 0;
+        popped += add;
+        pw.popped = popped;
+    }
+    return (int32_t)C.Q - (int32_t)(pw.pushed - popped);
+}
+
 __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr, uint32_t t)
 {
     const HostRO hr = C.host[pr.host];
     if (!pr.alive || hr.n_out == 0) return;
     PortRW &pw = C.ps[p];
-    int32_t credit = (int32_t)C.Q - (int32_t)(pw.pushed - pw.popped);
+    int32_t credit = buffer_credit(C, pw, p, t);
     uint32_t rr = pw.rr, pushed = pw.pushed;
     const uint32_t nw = (hr.n_out + 31) >> 5;
     uint32_t *rdy = C.ready + hr.rdy_off;
@@ -832,29 +830,37 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
     if (!pr.alive) return;
     const uint32_t deg = pr.deg, lo = pr.local, Q = C.Q;
     PortRW &pw = C.ps[p];
-    int32_t credit = pr.peer_is_host ? (int32_t)pr.rate
-                                     : (int32_t)Q - (int32_t)(pw.pushed - pw.popped);
-    uint32_t rr = pw.rr, pushed = pw.pushed;
     const uint32_t prow = pr.vbase + lo * deg;     /* popper-major row of this output */
-    /* packets waiting at each input for this output: appended - popped, bytewise */
-    uint64_t a0, a1, h0, h1;
-    row_bytes(C.arr + prow, deg, a0, a1);
-    row_bytes(C.phead + prow, deg, h0, h1);
-    uint64_t d0 = bytes_sub(a0, h0), d1 = bytes_sub(a1, h1);
-    bool moved = false;
+    /* each input's queue toward this output: its head slot, Q_EMPTY when empty */
+    uint64_t h0, h1;
+    row_bytes(C.nslot + prow, deg, h0, h1);
+    int32_t credit = pr.peer_is_host ? (int32_t)pr.rate : buffer_credit(C, pw, p, t);
+    /* 0x80 in the byte of every input whose queue holds a packet */
+    const uint64_t k0 = deg >= 8 ? ~0ull : (1ull << (8 * deg)) - 1ull;
+    const uint64_t k1 = deg >= 16 ? ~0ull : deg <= 8 ? 0ull : (1ull << (8 * (deg - 8))) - 1ull;
+    uint64_t e0 = bytes_nz(~h0) & k0, e1 = bytes_nz(~h1) & k1;
+    uint32_t rr = pw.rr, pushed = pw.pushed;
+    uint32_t taken = 0;
     for (uint32_t m = 0; m < pr.rate && credit > 0; m++) {
-        const int jj = first_from<2>(bytes_nz(d0), bytes_nz(d1), rr);
+        const int jj = first_from<2>(e0, e1, rr);
         if (jj < 0) break;
         const uint32_t j = (uint32_t)jj;
-        if (j < 8) d0 -= 1ull << (8 * j); else d1 -= 1ull << (8 * (j - 8));
-        uint32_t vp = prow + j;
-        uint32_t qi = pr.host + j;                 /* switch ports: pr.host is the pool of port 0 */
-        uint32_t s = C.nslot[vp];
-        uint32_t desc = C.pdesc[qi * Q + s];
-        C.nslot[vp] = C.pnxt[qi * Q + s];   /* qi: pool of input j */
-        uint8_t h = (uint8_t)(C.phead[vp] + 1);
-        C.phead[vp] = h;
-        C.head[pr.vbase + j * deg + lo] = h;
+        const uint32_t vp = prow + j;
+        const uint32_t qi = pr.host + j;           /* switch ports: pr.host is the pool of port 0 */
+        const uint32_t s = row_get(h0, h1, j);
+        const uint32_t desc = C.pdesc[qi * Q + s];
+        /* popping the tail empties the queue */
+        const uint32_t nh = s == C.tail[vp] ? Q_EMPTY : C.pnxt[qi * Q + s];
+        C.nslot[vp] = (uint8_t)nh;
+        row_set(h0, h1, j, nh);
+        if (nh == Q_EMPTY) {
+            if (j < 8) e0 &= ~(0x80ull << (8 * j)); else e1 &= ~(0x80ull << (8 * (j - 8)));
+        }
+        /* the slot goes back to input j's free mask, and the pop into the
+         * count the output feeding input j reads next tick */
+        __hip_atomic_fetch_or(C.fmask + 4u * qi + (s >> 6), 1ull << (s & 63u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(C.popc + (t & 1u) * C.n_ports + C.port[pr.base + j].peer, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
         rr = j + 1 == deg ? 0 : j + 1;
         if (C.cc == CC_HPCC) {
             /* telemetry of this switch (the descriptor counts the switches
@@ -869,11 +875,15 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
         transmit(C, a, p, pr, desc, t, m);
         pushed++;
         credit--;
-        moved = true;
+        taken++;
     }
-    if (moved) { pw.rr = rr; pw.pushed = pushed; }
+    if (taken) { pw.rr = rr; pw.pushed = pushed; }
     /* packets arrived and not yet forwarded: what next tick's arrivals see */
-    if (C.cc) C.bl[p] = bytes_sum(d0, d1);
+    if (C.cc) {
+        const uint32_t ql = C.qlen[p] - taken;
+        C.qlen[p] = ql;
+        C.bl[p] = ql;
+    }
 }
 
 /* ------------------------------------------------------------ reductions */
@@ -979,16 +989,13 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     C.grp = (const Grp *)at(H->o_grp);
     C.hout = (const uint32_t *)at(H->o_hout);
     C.host = (const HostRO *)at(H->o_host);
-    C.arr = at(H->o_arr);
-    C.phead = at(H->o_phead);
+    C.tail = at(H->o_tail);
     C.nslot = at(H->o_nslot);
-    C.head = at(H->o_head);
-    C.tslot = at(H->o_tslot);
-    C.fcur = at(H->o_fcur);
-    C.hseen = at(H->o_hseen);
     C.pdesc = (uint32_t *)at(H->o_pdesc);
     C.pnxt = at(H->o_pnxt);
-    C.fstk = at(H->o_fstk);
+    C.fmask = (uint64_t *)at(H->o_fmask);
+    C.popc = (uint32_t *)at(H->o_popc);
+    C.qlen = (uint32_t *)at(H->o_qlen);
     C.ps = (PortRW *)at(H->o_pstate);
     C.scnt = at(H->o_scnt);
     C.sdesc = (uint32_t *)at(H->o_sdesc);

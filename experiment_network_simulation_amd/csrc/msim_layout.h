@@ -9,15 +9,18 @@
  * or copied into a workgroup's LDS, so one kernel serves both placements.
  *
  * State owners of the general format (the pull discipline of Multiverse
- * section 4.2: each datum has one writer per phase; the compact and ring
- * formats below keep it except for the LDS atomics between the ports of one
- * switch that msim_kernel.hip lists):
- *  - a switch ingress port q owns its buffer pool (pdesc/pnxt/fstk), the tail
- *    side of its virtual output queues (arr, tslot, fcur, hseen) and popped[q];
- *    it runs in phase A (arrivals, frees);
- *  - a switch output port o owns the head side of the queues it drains (phead,
- *    nslot, head), its round-robin pointer, pushed[o] and the staging slots of
- *    the ingress it feeds; it runs in phase D (grant, pop, transmit);
+ * section 4.2: each datum has one writer per phase, except for the
+ * order-independent atomics named below and in msim_kernel.hip):
+ *  - a switch ingress port q owns its buffer pool's descriptors and links
+ *    (pdesc/pnxt), the tail side of its virtual output queues (tail, and the
+ *    head byte of an empty queue) and its free-slot mask; it runs in phase A
+ *    (arrivals);
+ *  - a switch output port o owns the head side of the queues it drains
+ *    (nslot), its round-robin pointer, pushed and popped counts and the
+ *    staging slots of the ingress it feeds; it runs in phase D (grant, pop,
+ *    transmit), returning each popped slot to its ingress's free mask and
+ *    counting the pop for the output feeding that ingress, both by atomic
+ *    OR / add (several outputs may take from one ingress in a tick);
  *  - a host owns its NIC (phase D), its deliveries and activations (phase A),
  *    the sender cursors of its outgoing connections and the receiver cursors of
  *    its incoming ones.
@@ -116,10 +119,10 @@ struct HostRO {          /* 16 bytes */
 };
 
 struct PortRW {          /* 16 bytes */
-    uint32_t popped;     /* output: packets its far switch ingress has forwarded (that ingress adds them in phase A) */
+    uint32_t popped;     /* output: packets its far switch ingress forwarded through the last tick */
     uint32_t pushed;     /* output: packets sent on it (phase D) */
     uint32_t rr;         /* output: round-robin pointer */
-    uint32_t ftop;       /* switch ingress: free-slot stack height */
+    uint32_t pad;
 };
 
 struct ConnRW {          /* 16 bytes */
@@ -220,8 +223,13 @@ struct ArenaHdr {        /* general format header */
     uint32_t n_ports, n_hosts, n_conn, n_grp;
     uint32_t Q, W, R, n_voq;
     uint32_t o_port, o_conn, o_grp, o_hout, o_host;
-    uint32_t o_arr, o_phead, o_nslot, o_head, o_tslot, o_fcur, o_hseen;
-    uint32_t o_pdesc, o_pnxt, o_fstk, o_pstate, o_scnt, o_sdesc, o_cstate, o_hstate, o_ready;
+    /* queue (ingress i, output o) of a switch: byte vbase + o * deg + i of
+     * o_nslot (head slot, Q_EMPTY when empty) and o_tail (tail slot); the
+     * ingress's free slots: four words at o_fmask + 32 * pool; o_popc[2][n_ports]:
+     * packets taken during tick t from the ingress output p feeds, in
+     * [t & 1][p]; o_qlen[p] (congestion control): packets queued for output p */
+    uint32_t o_tail, o_nslot, o_fmask, o_popc, o_qlen;
+    uint32_t o_pdesc, o_pnxt, o_pstate, o_scnt, o_sdesc, o_cstate, o_hstate, o_ready;
     uint32_t n_task, o_task, o_tpred, o_trw;
     /* congestion control: ACKs of connection c due at tick t are counted in the
      * 16-bit word o_ack[c * WA + t % WA] (ACKs | marked << 8), written by c's
