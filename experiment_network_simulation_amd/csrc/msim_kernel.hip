@@ -1618,12 +1618,9 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
              * tick t+1.  At most RP packets arrive per ingress and tick. */
             C.popped[tp + tid] = 0;
             LDSP DT *rec = C.sdesc + sb + myoff;
-            bool any = false;
-            for (uint32_t k = 0; k < (R1 ? 1u : C.RP); k++) {
-                const uint32_t e = rec[k];
-                if (e == 0) break;
-                any = true;
-                /* e = descriptor + 1: the same packet with its hop index advanced */
+            /* one arriving packet: e = descriptor + 1, the same packet with its
+             * hop index advanced */
+            auto arrive = [&](uint32_t e) {
                 const uint32_t desc = e - 1;
                 const uint32_t c = desc >> DESC_SHIFT, hop = desc & DESC_HOP_MASK;
                 const uint32_t o = (C.route[c] >> (4 * hop)) & 0xFu;
@@ -1635,7 +1632,7 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                     freem = __hip_atomic_exchange(C.fmask + pool, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 if (freem == 0 || o >= deg) {
                     a.fault = 1;
-                    continue;
+                    return;
                 }
                 uint32_t s;
                 if (q32) {
@@ -1652,11 +1649,41 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
                 const uint32_t at_head = C.o_nslot + vq, at_tail = C.o_pnxt + cpool(C, pool, tail);
                 C.L[head == Q_EMPTY ? at_head : at_tail] = (uint8_t)s;
                 C.arr[vq] = (uint8_t)s;
+            };
+            if (R1) {
+                /* the feeding output rewrites its entry every tick */
+                const uint32_t e = rec[0];
+                if (e != 0) arrive(e);
+            } else {
+                /* the RP (2 or 4) entries of the record in one read; they fill
+                 * in order, and the reader clears what was staged */
+                uint32_t e4[4];
+                if (C.RP == 1) {
+                    e4[0] = rec[0]; e4[1] = e4[2] = e4[3] = 0;
+                } else if (sizeof(DT) == 2 && C.RP == 2) {
+                    const uint32_t w = *(const LDSP uint32_t *)rec;
+                    e4[0] = w & 0xFFFFu; e4[1] = w >> 16; e4[2] = e4[3] = 0;
+                } else if (sizeof(DT) == 2) {
+                    const uint64_t w = *(const LDSP uint64_t *)rec;
+                    e4[0] = (uint32_t)w & 0xFFFFu; e4[1] = (uint32_t)w >> 16;
+                    e4[2] = (uint32_t)(w >> 32) & 0xFFFFu; e4[3] = (uint32_t)(w >> 48);
+                } else if (C.RP == 2) {
+                    const uint64_t w = *(const LDSP uint64_t *)rec;
+                    e4[0] = (uint32_t)w; e4[1] = (uint32_t)(w >> 32); e4[2] = e4[3] = 0;
+                } else {
+                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                    const u32x4 w = *(const LDSP u32x4 *)rec;
+                    e4[0] = w.x; e4[1] = w.y; e4[2] = w.z; e4[3] = w.w;
+                }
+#pragma unroll
+                for (uint32_t k = 0; k < 4; k++)
+                    if (e4[k] != 0) arrive(e4[k]);
+                if (e4[0] != 0) {
+                    if (C.RP * sizeof(DT) == 4) *(LDSP uint32_t *)rec = 0u;
+                    else if (C.RP * sizeof(DT) == 8) *(LDSP uint64_t *)rec = 0ull;
+                    else for (uint32_t k = 0; k < C.RP; k++) rec[k] = 0;
+                }
             }
-            /* rate 1: the feeding output rewrites its entry every tick; faster
-             * links stage only what they send, so the reader clears */
-            if (!R1 && any)
-                for (uint32_t k = 0; k < C.RP; k++) rec[k] = 0;
         } else if (is_host) {
             LDSP DT *rec = C.sdesc + sb + myoff;
             /* the ring-only copy costs registers the faster-link kinds do not have */
@@ -1688,9 +1715,13 @@ __device__ void run_compact(const KParams &kp, uint32_t x, uint8_t *arena_g, uin
             trow.load(C.arr + rowp);
             const uint64_t F = 0x8080808080808080ull;          /* a slot byte < 64 has bit 7 clear */
             uint32_t out = 0;                                          /* rate 1: staged entry, desc + 1 or 0 */
-            for (uint32_t m = 0; m < (R1 ? 1u : pr.rate) && credit > 0; m++) {
+            /* a loop count the whole wavefront shares (the largest rate), each
+             * lane's rate and credit as guards: no per-lane loop exits */
+            for (uint32_t m = 0; m < (R1 ? 1u : C.RP); m++) {
+                if (!R1 && (m >= pr.rate || credit <= 0)) continue;
+                if (R1 && credit <= 0) continue;
                 const int i = first_from<W>(~hrow.w0 & F, W == 2 ? (~hrow.w1 & F) : 0ull, rr);
-                if (i < 0) break;
+                if (i < 0) continue;
                 const uint32_t vq = rowp + (uint32_t)i;                 /* queue (i, this output) */
                 const uint32_t qpool = qbase + (uint32_t)i - SB;
                 const uint32_t s = hrow.get((uint32_t)i);
