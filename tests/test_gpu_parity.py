@@ -210,6 +210,30 @@ def test_resume_equals_single_run(simmod, oracle):
     assert_flows(s, 1, oracle.run(b, 1, flows=True))
 
 
+@pytest.mark.parametrize("cid", [1, 2])
+def test_general_path_resumed(simmod, oracle, cid):
+    """The general path with its state in HBM, in random short runs: the
+    per-tick pop counts (kept by tick parity), free-slot masks and queue
+    slots carried across launch boundaries give the oracle's totals and
+    flow ticks (C1: rate 1; C2: uplinks at rate 2)."""
+    b = I.make_config(cid, n_exp=4)
+    s = simmod.Sim(b, record=[1], force_global=True)
+    s.bind()
+    inf = s.info()
+    assert inf["n_lds_exp"] == 0 and inf["lds_bytes"] == 0 and inf["main_kernel"] == 0
+    rng = np.random.default_rng(cid)
+    longest = {1: 100, 2: 3000}[cid]          # a few dozen runs per experiment
+    for _ in range(400):
+        s.run(int(rng.integers(1, longest)))
+        r = s.results()
+        if (r["status"] != 1).all():
+            break
+    o = oracle_all(oracle, b)
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+    assert_flows(s, 1, oracle.run(b, 1, flows=True))
+
+
 def test_incomplete_matches_oracle(simmod, oracle):
     b = I.make_config(1, n_exp=4)
     s, r = gpu_run(simmod, b, max_ticks=100)
