@@ -374,7 +374,8 @@ typedef struct msim_info {
     uint32_t n_exp;
     uint32_t block_threads;      /* threads per workgroup (one workgroup simulates one experiment at a time) */
     uint32_t grid_blocks;        /* persistent workgroups launched by msim_run (0 before bind) */
-    uint32_t lds_bytes;          /* dynamic LDS per workgroup (0: experiment state stays in HBM) */
+    uint32_t lds_bytes;          /* dynamic LDS per workgroup (0: none; an experiment whose state stays in
+                                    HBM may still copy its port table into it) */
     uint32_t n_lds_exp;          /* experiments whose state is worked on in LDS */
     uint32_t n_compact;          /* of those, experiments on the compact path (one thread per port) */
     uint32_t main_kernel;        /* kernel running most experiments: 0 msim_megakernel (general path);
