@@ -1113,14 +1113,22 @@ extern "C" int msim_create(const msim_batch_spec *spec, const msim_options *opts
      * batch, about 1,058 + 5,400 / p cycles per tick for chunks of p
      * packets, so those experiments weigh their load by (p + 4) / p for
      * their smallest chunk (duration correlation 0.95 against 0.89 for the
-     * load alone) */
+     * load alone).  The general path walks every port every tick, so its
+     * tick costs about the port count (on the k=16 fat-tree batch, 2.4e-8 s
+     * per port-tick at every oversubscription): those experiments weigh their
+     * load by their ports.  A compact tick costs about the same whatever the
+     * experiment (one thread per port) */
+    auto est = [](const Compiled &c) -> uint64_t {
+        if (c.kind == KIND_RING && c.ring_pmin) return c.est_ticks * (c.ring_pmin + 4) / c.ring_pmin;
+        if (!c.compact && c.kind != KIND_RING) return c.est_ticks * c.n_ports;
+        return c.est_ticks;
+    };
     ctx->order.resize(E);
     for (uint32_t e = 0; e < E; e++) ctx->order[e] = e;
     std::stable_sort(ctx->order.begin(), ctx->order.end(), [&](uint32_t a, uint32_t b) {
         const Compiled &x = ctx->exps[a], &y = ctx->exps[b];
         if (x.kind != y.kind) return x.kind < y.kind;
-        const uint64_t ex = x.kind == KIND_RING && x.ring_pmin ? x.est_ticks * (x.ring_pmin + 4) / x.ring_pmin : x.est_ticks,
-                       ey = y.kind == KIND_RING && y.ring_pmin ? y.est_ticks * (y.ring_pmin + 4) / y.ring_pmin : y.est_ticks;
+        const uint64_t ex = est(x), ey = est(y);
         if (ex != ey) return ex > ey;
         return x.est_hops > y.est_hops;
     });
