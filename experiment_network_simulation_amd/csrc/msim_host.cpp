@@ -884,7 +884,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
     take(H.o_tail, n_voq);
     take(H.o_nslot, n_voq);
     take(H.o_fmask, 32ull * n_swp);
-    take(H.o_popc, 8ull * n_ports);
+    take(H.o_ow, 4ull * n_ports);
     take(H.o_pdesc, 4ull * n_swp * Q);
     take(H.o_pnxt, (size_t)n_swp * Q);
     take(H.o_pstate, sizeof(PortRW) * n_ports);

@@ -75,7 +75,7 @@ struct Ctx {
     uint32_t *pdesc;
     uint8_t *pnxt;
     uint64_t *fmask;
-    uint32_t *popc, *qlen;
+    uint32_t *ow, *qlen;
     PortRW *ps;
     uint8_t *scnt;
     uint32_t *sdesc;
@@ -743,30 +743,24 @@ __device__ __forceinline__ void transmit(const Ctx &C, Acc &a, uint32_t p, const
     a.max_arr = max(a.max_arr, ta);
 }
 
-/* Output p's credit toward a switch buffer: Q minus the packets it sent that
- * the far ingress has not yet forwarded.  The far switch's outputs count the
- * packets they take from that ingress during tick t in popc[t & 1][p]; p adds
- * the count of t - 1 to its running total and clears it for tick t + 1. */
-__device__ __forceinline__ int32_t buffer_credit(const Ctx &C, PortRW &pw, uint32_t p, uint32_t t)
-{
-    uint32_t *pc = C.popc + ((t + 1u) & 1u) * C.n_ports + p;
-    const uint32_t add = *pc;
-    uint32_t popped = pw.popped;
-    if (add) {
-        *pc = 0;
-        popped += add;
-        pw.popped = popped;
-    }
-    return (int32_t)C.Q - (int32_t)(pw.pushed - popped);
-}
+/* Output p's word: packets sent and not yet forwarded by the far ingress
+ * (bits 0-7), the packets the far switch's outputs took from that ingress
+ * during ticks of parity 0 (bits 8-15) and 1 (bits 16-23), and a switch
+ * output's round-robin pointer (bits 24-31).  Those outputs add to the byte
+ * of their tick's parity; p, at tick t, reads the byte of t - 1, takes it off
+ * its in-flight count and clears it with one atomic add that also records
+ * what it sent, so neither side overwrites the other's byte. */
+__device__ __forceinline__ uint32_t pops_shift(uint32_t t) { return 8u + 8u * (t & 1u); }
 
 __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr, uint32_t t)
 {
     const HostRO hr = C.host[pr.host];
     if (!pr.alive || hr.n_out == 0) return;
     PortRW &pw = C.ps[p];
-    int32_t credit = buffer_credit(C, pw, p, t);
-    uint32_t rr = pw.rr, pushed = pw.pushed;
+    const uint32_t ow = C.ow[p], shp = pops_shift(t + 1u);
+    const uint32_t pp = (ow >> shp) & 0xFFu;
+    int32_t credit = (int32_t)C.Q - (int32_t)((ow & 0xFFu) - pp);
+    uint32_t rr = pw.rr, pushed = 0;
     const uint32_t nw = (hr.n_out + 31) >> 5;
     uint32_t *rdy = C.ready + hr.rdy_off;
     HostRW &hw = C.hs[pr.host];
@@ -822,7 +816,9 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
             hw.pend[hw.pcnt++] = c;
         }
     }
-    if (moved) { pw.rr = rr; pw.pushed = pushed; }
+    if (moved) pw.rr = rr;
+    const uint32_t delta = (pushed - pp) - (pp << shp);
+    if (delta) __hip_atomic_fetch_add(C.ow + p, delta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr, uint32_t t)
@@ -834,12 +830,15 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
     /* each input's queue toward this output: its head slot, Q_EMPTY when empty */
     uint64_t h0, h1;
     row_bytes(C.nslot + prow, deg, h0, h1);
-    int32_t credit = pr.peer_is_host ? (int32_t)pr.rate : buffer_credit(C, pw, p, t);
+    const uint32_t ow = C.ow[p], shp = pops_shift(t + 1u);
+    const uint32_t pp = (ow >> shp) & 0xFFu;
+    int32_t credit = pr.peer_is_host ? (int32_t)pr.rate : (int32_t)Q - (int32_t)((ow & 0xFFu) - pp);
     /* 0x80 in the byte of every input whose queue holds a packet */
     const uint64_t k0 = deg >= 8 ? ~0ull : (1ull << (8 * deg)) - 1ull;
     const uint64_t k1 = deg >= 16 ? ~0ull : deg <= 8 ? 0ull : (1ull << (8 * (deg - 8))) - 1ull;
     uint64_t e0 = bytes_nz(~h0) & k0, e1 = bytes_nz(~h1) & k1;
-    uint32_t rr = pw.rr, pushed = pw.pushed;
+    const uint32_t rr0 = ow >> 24;
+    uint32_t rr = rr0, pushed = C.cc == CC_HPCC ? pw.pushed : 0u;
     uint32_t taken = 0;
     for (uint32_t m = 0; m < pr.rate && credit > 0; m++) {
         const int jj = first_from<2>(e0, e1, rr);
@@ -859,7 +858,7 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
         /* the slot goes back to input j's free mask, and the pop into the
          * count the output feeding input j reads next tick */
         __hip_atomic_fetch_or(C.fmask + 4u * qi + (s >> 6), 1ull << (s & 63u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_add(C.popc + (t & 1u) * C.n_ports + C.port[pr.base + j].peer, 1u, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(C.ow + C.port[pr.base + j].peer, 1u << pops_shift(t), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
         rr = j + 1 == deg ? 0 : j + 1;
         if (C.cc == CC_HPCC) {
@@ -877,7 +876,10 @@ __device__ __forceinline__ void phase_d_switch(const Ctx &C, Acc &a, uint32_t p,
         credit--;
         taken++;
     }
-    if (taken) { pw.rr = rr; pw.pushed = pushed; }
+    if (C.cc == CC_HPCC && taken) pw.pushed = pushed;
+    /* an output toward a host counts nothing in flight */
+    const uint32_t delta = (pr.peer_is_host ? 0u : taken - pp) - (pp << shp) + ((rr - rr0) << 24);
+    if (delta) __hip_atomic_fetch_add(C.ow + p, delta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     /* packets arrived and not yet forwarded: what next tick's arrivals see */
     if (C.cc) {
         const uint32_t ql = C.qlen[p] - taken;
@@ -994,7 +996,7 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     C.pdesc = (uint32_t *)at(H->o_pdesc);
     C.pnxt = at(H->o_pnxt);
     C.fmask = (uint64_t *)at(H->o_fmask);
-    C.popc = (uint32_t *)at(H->o_popc);
+    C.ow = (uint32_t *)at(H->o_ow);
     C.qlen = (uint32_t *)at(H->o_qlen);
     C.ps = (PortRW *)at(H->o_pstate);
     C.scnt = at(H->o_scnt);

@@ -16,11 +16,12 @@
  *    head byte of an empty queue) and its free-slot mask; it runs in phase A
  *    (arrivals);
  *  - a switch output port o owns the head side of the queues it drains
- *    (nslot), its round-robin pointer, pushed and popped counts and the
+ *    (nslot), the in-flight and round-robin bytes of its output word and the
  *    staging slots of the ingress it feeds; it runs in phase D (grant, pop,
  *    transmit), returning each popped slot to its ingress's free mask and
- *    counting the pop for the output feeding that ingress, both by atomic
- *    OR / add (several outputs may take from one ingress in a tick);
+ *    counting the pop in the word of the output feeding that ingress, both
+ *    by atomic OR / add (several outputs may take from one ingress in a
+ *    tick), and updates its own word with one atomic add;
  *  - a host owns its NIC (phase D), its deliveries and activations (phase A),
  *    the sender cursors of its outgoing connections and the receiver cursors of
  *    its incoming ones.
@@ -119,10 +120,10 @@ struct HostRO {          /* 16 bytes */
 };
 
 struct PortRW {          /* 16 bytes */
-    uint32_t popped;     /* output: packets its far switch ingress forwarded through the last tick */
-    uint32_t pushed;     /* output: packets sent on it (phase D) */
-    uint32_t rr;         /* output: round-robin pointer */
-    uint32_t pad;
+    uint32_t pad0;
+    uint32_t pushed;     /* switch output under HPCC: packets sent on it (its telemetry) */
+    uint32_t rr;         /* host NIC: round-robin pointer over its connections */
+    uint32_t pad1;
 };
 
 struct ConnRW {          /* 16 bytes */
@@ -225,10 +226,12 @@ struct ArenaHdr {        /* general format header */
     uint32_t o_port, o_conn, o_grp, o_hout, o_host;
     /* queue (ingress i, output o) of a switch: byte vbase + o * deg + i of
      * o_nslot (head slot, Q_EMPTY when empty) and o_tail (tail slot); the
-     * ingress's free slots: four words at o_fmask + 32 * pool; o_popc[2][n_ports]:
-     * packets taken during tick t from the ingress output p feeds, in
-     * [t & 1][p]; o_qlen[p] (congestion control): packets queued for output p */
-    uint32_t o_tail, o_nslot, o_fmask, o_popc, o_qlen;
+     * ingress's free slots: four words at o_fmask + 32 * pool; o_ow[p]: output
+     * p's word (packets in flight toward the far ingress, the packets taken
+     * from that ingress during ticks of parity 0 and 1, a switch output's
+     * round-robin pointer; one byte each); o_qlen[p] (congestion control):
+     * packets queued for output p */
+    uint32_t o_tail, o_nslot, o_fmask, o_ow, o_qlen;
     uint32_t o_pdesc, o_pnxt, o_pstate, o_scnt, o_sdesc, o_cstate, o_hstate, o_ready;
     uint32_t n_task, o_task, o_tpred, o_trw;
     /* congestion control: ACKs of connection c due at tick t are counted in the
