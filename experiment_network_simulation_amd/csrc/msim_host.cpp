@@ -920,6 +920,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
         take(H.o_ackm, 4ull * H.WA * words);
     }
     take(H.o_hstate, sizeof(HostRW) * n_hosts);
+    take(H.o_hpc, n_hosts);
     take(H.o_ready, 4ull * words);
     /* [rw_off, rw_hot) with [0, ro_hot): the state of the switch and NIC phases,
      * placed in LDS on its own when the whole arena does not fit */

@@ -76,6 +76,7 @@ struct Ctx {
     uint8_t *pnxt;
     uint64_t *fmask;
     uint32_t *ow, *qlen;
+    uint8_t *hpc;        /* per host: connections whose flow finished sending last tick */
     PortRW *ps;
     uint8_t *scnt;
     uint32_t *sdesc;
@@ -500,6 +501,12 @@ __device__ __forceinline__ uint32_t spray_pick(uint32_t mask, uint32_t c, uint32
 __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, const PortRO &pr,
                                              uint32_t t, uint32_t slot)
 {
+    const uint32_t si = p * C.W + slot;
+    const uint32_t n = C.scnt[si];
+    /* without congestion control a host has nothing to do in a tick with no
+     * arrival and no flow that finished sending in the last one */
+    const uint32_t np = C.hpc[pr.host];
+    if (!C.cc && n == 0 && np == 0 && t != 0) return;
     const HostRO hr = C.host[pr.host];
     HostRW &hw = C.hs[pr.host];
     if (C.cc) {
@@ -546,8 +553,6 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
             }
         }
     }
-    uint32_t si = p * C.W + slot;
-    uint32_t n = C.scnt[si];
     for (uint32_t k = 0; k < n; k++) {
         const uint32_t desc = C.sdesc[si * C.R + k];
         uint32_t c, in_order = 1;
@@ -614,9 +619,8 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
     if (t == 0) {
         for (uint32_t j = 0; j < hr.n_out; j++) check_conn(C, a, C.hout[hr.out_off + j], hr.rdy_off, t);
     } else {
-        uint32_t np = hw.pcnt;
         for (uint32_t k = 0; k < np; k++) check_conn(C, a, hw.pend[k], hr.rdy_off, t);
-        if (np) hw.pcnt = 0;
+        if (np) C.hpc[pr.host] = 0;
     }
 }
 
@@ -813,7 +817,7 @@ __device__ __forceinline__ void phase_d_host(const Ctx &C, Acc &a, uint32_t p, c
                 C.rec[2 * C.n_flows + flow_id(C.grp[cr.grp], cr, c, pos)] = t + 1;
             }
             cw.s_pos = (pos + 1) | (CS_WAIT << CS_SHIFT);
-            hw.pend[hw.pcnt++] = c;
+            hw.pend[C.hpc[pr.host]++] = c;
         }
     }
     if (moved) pw.rr = rr;
@@ -997,6 +1001,7 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     C.pnxt = at(H->o_pnxt);
     C.fmask = (uint64_t *)at(H->o_fmask);
     C.ow = (uint32_t *)at(H->o_ow);
+    C.hpc = at(H->o_hpc);
     C.qlen = (uint32_t *)at(H->o_qlen);
     C.ps = (PortRW *)at(H->o_pstate);
     C.scnt = at(H->o_scnt);

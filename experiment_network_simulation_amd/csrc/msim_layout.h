@@ -203,7 +203,7 @@ static_assert(offsetof(CcRW, lat) == offsetof(QcnRW, lat) && offsetof(CcRW, awor
               "shared fields");
 
 struct HostRW {          /* 32 bytes */
-    uint32_t pcnt;       /* connections whose flow finished sending last tick */
+    uint32_t pad0;
     uint32_t started;    /* first activation pass done */
     uint32_t left;       /* flows still to be received by this host */
     uint32_t pad;
@@ -249,6 +249,7 @@ struct ArenaHdr {        /* general format header */
      * packets delivered in order; o_rbits: per connection, a bitmap of arrived
      * sequence numbers, words o_rwoff[c] .. o_rwoff[c+1]-1 */
     uint32_t lb, sbits, seed, o_spi, o_cand, o_sseq, o_rnext, o_rwoff, o_rbits;
+    uint32_t o_hpc;      /* per host, one byte: connections whose flow finished sending last tick */
     /* split placement: [0, ro_hot) and [rw_off, rw_hot) hold everything the
      * switch phases and the host NICs touch each tick (ports, hosts, queues,
      * pools, staging, backlogs, host state); a workgroup that cannot hold the
