@@ -294,6 +294,15 @@ def edge_batch():
     ft = I.fat_tree(4)
     ft.delay = np.asarray([1 + (c % 3) for c in range(ft.n_cables)], np.uint8)
     add(ft, I.Workload([I.ring(I.COLL_RING_AR, 64 * I.PKT_BYTES, [0, 5, 10, 15, 3, 8], 2, I.PKT_BYTES)]), q=4, seed=7)
+    # deep buffers that fill: three senders at rate 4 (or 2) into one rate-1
+    # output, so each ingress holds up to Q packets and slots past 64, 128 and
+    # 192 (every word of a general-path free mask) are taken and returned
+    deep4 = I.topology_from_cables([0, 0, 0, 0, 1], [(0, 4, 4, 4, 1, 1), (1, 4, 4, 4, 2, 1),
+                                                     (2, 4, 4, 4, 1, 1), (3, 4, 1, 1, 1, 1)])
+    add(deep4, I.xflows([(0, 3, 300), (1, 3, 280), (2, 3, 310)]), q=255)
+    deep2 = I.topology_from_cables([0, 0, 0, 0, 1], [(0, 4, 2, 2, 1, 1), (1, 4, 2, 2, 1, 1),
+                                                     (2, 4, 2, 2, 3, 1), (3, 4, 1, 1, 1, 1)])
+    add(deep2, I.xflows([(0, 3, 200), (1, 3, 150), (2, 3, 170), (3, 0, 40)]), q=130)
     return b
 
 
