@@ -601,7 +601,7 @@ __device__ __forceinline__ void phase_a_host(const Ctx &C, Acc &a, uint32_t p, c
         uint32_t pos = cw.r_pos;
         uint32_t fid = flow_id(g, cr, c, pos);
         a.digest += mix64(((uint64_t)fid << 32) | t);
-        a.tmax = t;
+        a.tmax = max(a.tmax, t);         /* a task this lane started may finish later */
         a.left--;
         hw.left--;
         if (C.rec) C.rec[fid] = t;
@@ -900,6 +900,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return v;
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v)
 {
     for (int o = 32; o > 0; o >>= 1) {
@@ -915,6 +921,8 @@ struct Shared {
     uint32_t exp;
     uint32_t chk_any[2][16];
     uint32_t chk_max[2][16];
+    uint32_t chk_net[2][16];   /* task graphs: the network's last busy tick, per wavefront */
+    uint32_t chk_nxt[2][16];   /* ... and the next finish of a running task */
     uint64_t sum[3][16];
     uint32_t mx[5][16];
 };
@@ -1050,6 +1058,11 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
     const uint32_t t0 = stp->t_now;
     const uint32_t t_end = (uint64_t)t0 + kp.max_ticks > 0xFFFFFFF0ull ? 0xFFFFFFF0u : t0 + kp.max_ticks;
     const uint32_t hist = max(max(stp->last_tx1, stp->last_act1), stp->max_arr);
+    /* task graphs without congestion control or spraying (whose timers and
+     * sequence numbers advance with the clock) may skip the ticks of an idle
+     * network; hist_net: the network's last busy tick in earlier runs */
+    constexpr bool SKIP = TASKS && !CC && !SP;
+    const uint32_t hist_net = max(stp->last_tx1 ? stp->last_tx1 + C.W - 2u : 0u, stp->last_act1);
 
     Acc a;
     a.hops = a.delivered = a.digest = 0;
@@ -1092,13 +1105,40 @@ __device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, 
             uint32_t any = __ballot(a.left > 0 || (TASKS && tasks_pending(C, tid, nth, t))) != 0ull;
             uint32_t ts = wave_max_u32(max(max(a.last_tx1, a.last_act1), a.max_arr));
             if (lane == 0) { sh.chk_any[par][wave] = any; sh.chk_max[par][wave] = ts; }
+            if constexpr (SKIP) {
+                /* the network's last busy tick: the last arrival a transmission
+                 * can make (delay < W) and the last activation; and the first
+                 * tick at which a running task finishes */
+                const uint32_t net = wave_max_u32(max(a.last_tx1 ? a.last_tx1 + C.W - 2u : 0u, a.last_act1));
+                uint32_t nx = MSIM_NONE;
+                for (uint32_t k = tid; k < C.n_task; k += nth) {
+                    const TaskRW tw = C.trw[k];
+                    if (tw.start != MSIM_NONE && tw.finish != MSIM_NONE && tw.finish >= t) nx = min(nx, tw.finish);
+                }
+                nx = wave_min_u32(nx);
+                if (lane == 0) { sh.chk_net[par][wave] = net; sh.chk_nxt[par][wave] = nx; }
+            }
             __syncthreads();
             any = 0;
             ts = hist;
-            for (uint32_t w = 0; w < nwaves; w++) { any |= sh.chk_any[par][w]; ts = max(ts, sh.chk_max[par][w]); }
+            uint32_t net = hist_net, nx = MSIM_NONE;
+            for (uint32_t w = 0; w < nwaves; w++) {
+                any |= sh.chk_any[par][w];
+                ts = max(ts, sh.chk_max[par][w]);
+                if (SKIP) { net = max(net, sh.chk_net[par][w]); nx = min(nx, sh.chk_nxt[par][w]); }
+            }
             par ^= 1;
             if (!any) { done = true; break; }
             if (ts <= t - 1) { dead = true; t_dead = ts; break; }
+            /* a task graph with an idle network: nothing is queued, staged
+             * or about to be sent or activated, so no tick before the next
+             * task finish can change any state; the tick loop goes there
+             * directly (the identical state, only the clock advanced) */
+            if (SKIP && net <= t - 1 && nx != MSIM_NONE && nx > t) {
+                t = min(nx, t_end);
+                slot = t % C.W;
+                if (t >= t_end) break;
+            }
         } else {
             __syncthreads();
         }

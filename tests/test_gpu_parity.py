@@ -526,6 +526,53 @@ def test_task_graphs(simmod, oracle, force_global):
         assert np.array_equal(tt["start"], o[e]["task_start"]) and np.array_equal(tt["finish"], o[e]["task_finish"])
 
 
+def long_task_batch(n, seed):
+    """task_batch with compute tasks of 100 to 2,000 ticks, so the network
+    idles for long stretches between the phases of each graph."""
+    b = task_batch(n, seed)
+    rng = np.random.default_rng(seed + 1)
+    for w in b.works:
+        for tk in w.tasks:
+            if tk.kind == I.TASK_COMPUTE:
+                tk.ticks = int(rng.integers(100, 2000))
+    return b
+
+
+@pytest.mark.parametrize("force_global", [False, True])
+def test_task_graphs_idle_network(simmod, oracle, force_global):
+    """Where a task graph leaves the network empty the general path skips
+    ticks: in one run, in random short runs, and in a run stopped inside an
+    idle stretch, every flow's and every task's ticks (or the stopped state)
+    equal the oracle's."""
+    b = long_task_batch(12, 33)
+    log("long task graphs", b.n_exp, "force_global", force_global)
+    o = oracle_all(oracle, b, flows=True)
+    s, r = gpu_run(simmod, b, record=range(b.n_exp), force_global=force_global)
+    assert simmod.KERNEL_NAMES[s.info()["main_kernel"]] == "msim_megakernel_t"
+    for e in range(b.n_exp):
+        assert_exp(r, e, o[e])
+        assert_flows(s, e, o[e])
+        tt = s.task_ticks(e)
+        assert np.array_equal(tt["start"], o[e]["task_start"]) and np.array_equal(tt["finish"], o[e]["task_finish"])
+    s2 = simmod.Sim(b, record=range(b.n_exp), force_global=force_global)
+    s2.bind()
+    rng = np.random.default_rng(5)
+    for _ in range(400):
+        s2.run(int(rng.integers(1, 700)))
+        r2 = s2.results()
+        if (r2["status"] != 1).all():
+            break
+    for e in range(b.n_exp):
+        assert_exp(r2, e, o[e])
+        assert_flows(s2, e, o[e])
+    stop = 1500
+    s3, r3 = gpu_run(simmod, b, force_global=force_global, max_ticks=stop)
+    for e in range(b.n_exp):
+        oe = oracle.run(b, e, max_ticks=stop)
+        got = (int(r3["status"][e]), int(r3["tick"][e]), int(r3["pkt_hops"][e]), int(r3["digest"][e]))
+        assert got == (oe["status"], oe["t_end"], oe["pkt_hops"], oe["digest"]), f"experiment {e}"
+
+
 def test_c7_sample(simmod, oracle):
     """Two full-size training iterations (tasks, intra-server collectives, DP
     all-reduce buckets on the k=8 fat-tree)."""
