@@ -957,22 +957,29 @@ __device__ void finish_state(ExpState *stp, const Shared &sh, uint32_t nwaves, u
 
 /* ----------------------------------------------------------- one experiment */
 
-template <bool IN_LDS, bool TASKS, bool CC, bool SP>
-__device__ void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_t *lds, Shared &sh)
+/* Where an experiment's arena lives while it runs.  A compile-time choice,
+ * so that every array whose place is fixed is addressed as LDS or as global
+ * memory; only the split placement picks per array at run time (generic
+ * addressing, whose waits cover both LDS and memory accesses). */
+enum { PL_LDS = 0, PL_SPLIT = 1, PL_PORTS = 2, PL_HBM = 3 };
+
+template <int PL, bool TASKS, bool CC, bool SP>
+__device__ __attribute__((always_inline)) void run_experiment(const KParams &kp, uint32_t x, uint8_t *arena_g,
+                                                              uint8_t *lds, Shared &sh)
 {
+    constexpr bool IN_LDS = PL == PL_LDS;
     const uint32_t tid = threadIdx.x, nth = blockDim.x;
     const uint32_t lane = tid & 63, wave = tid >> 6, nwaves = (nth + 63) >> 6;
     ExpState *stp = (ExpState *)(kp.ws + kp.o_state) + x;
     const ArenaHdr *H = (const ArenaHdr *)arena_g;
     const uint32_t arena_bytes = H->bytes, rw_off = H->rw_off;
     const uint32_t ro_hot = H->ro_hot, rw_hot = H->rw_hot;
-    /* placement: the whole arena in LDS (IN_LDS); else, if it fits, only the
-     * switch / NIC state ([0, ro_hot) then [rw_off, rw_hot), back to back);
-     * else, if it fits, only the port table, which every port reads twice a
-     * tick; else all in HBM */
-    const bool split = !IN_LDS && kp.lds_bytes && ro_hot + (rw_hot - rw_off) <= kp.lds_bytes;
+    /* placement (chosen by place_of): the whole arena in LDS; else, if it
+     * fits, only the switch / NIC state ([0, ro_hot) then [rw_off, rw_hot),
+     * back to back); else, if it fits, only the port table, which every port
+     * reads twice a tick; else all in HBM */
+    constexpr bool split = PL == PL_SPLIT, ports = PL == PL_PORTS;
     const uint32_t port_b = (H->n_ports * (uint32_t)sizeof(PortRO) + 15u) & ~15u;
-    const bool ports = !IN_LDS && !split && kp.lds_bytes && port_b <= kp.lds_bytes;
     if (ports) {
         const uint4 *src = (const uint4 *)(arena_g + H->o_port);
         uint4 *dst = (uint4 *)lds;
@@ -2350,13 +2357,30 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
  * and the compact path for 8- or 16-byte queue rows and 16- or 32-bit packet
  * descriptors, two of them also with trees, send/recv groups and gated rings.
  * Each kind is its own kernel so that each gets its own register allocation. */
+/* The placement of a general-path arena: all of it in LDS if it fits; else
+ * its switch and NIC state if that fits; else its port table if that fits;
+ * else nothing. */
+__device__ __forceinline__ int place_of(const KParams &kp, const ArenaHdr *H)
+{
+    if (H->bytes <= kp.lds_bytes) return PL_LDS;
+    if (kp.lds_bytes && H->ro_hot + (H->rw_hot - H->rw_off) <= kp.lds_bytes) return PL_SPLIT;
+    const uint32_t port_b = (H->n_ports * (uint32_t)sizeof(PortRO) + 15u) & ~15u;
+    if (kp.lds_bytes && port_b <= kp.lds_bytes) return PL_PORTS;
+    return PL_HBM;
+}
+
 template <int KIND>
 __device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *arena, uint8_t *lds, Shared &sh)
 {
     if constexpr (KIND == 0 || KIND == KIND_GENERAL_TASKS || KIND == KIND_GENERAL_CC || KIND == KIND_GENERAL_SPRAY) {
         constexpr bool T = KIND != 0, CC = KIND == KIND_GENERAL_CC, SP = KIND == KIND_GENERAL_SPRAY;
-        if (((const ArenaHdr *)arena)->bytes <= kp.lds_bytes) run_experiment<true, T, CC, SP>(kp, x, arena, lds, sh);
-        else run_experiment<false, T, CC, SP>(kp, x, arena, lds, sh);
+        /* every placement is its own inlined copy of the tick loop */
+        switch (place_of(kp, (const ArenaHdr *)arena)) {
+        case PL_LDS: run_experiment<PL_LDS, T, CC, SP>(kp, x, arena, lds, sh); break;
+        case PL_SPLIT: run_experiment<PL_SPLIT, T, CC, SP>(kp, x, arena, lds, sh); break;
+        case PL_PORTS: run_experiment<PL_PORTS, T, CC, SP>(kp, x, arena, lds, sh); break;
+        default: run_experiment<PL_HBM, T, CC, SP>(kp, x, arena, lds, sh); break;
+        }
     } else if constexpr (KIND == KIND_RING) {
         run_ring(kp, x, arena, lds, sh);
     } else if constexpr (KIND == KIND_COMPACT_X8) {
@@ -2374,7 +2398,7 @@ __device__ __forceinline__ void run_one(const KParams &kp, uint32_t x, uint8_t *
 /* Persistent loop: each workgroup claims the next experiment of its kind (the
  * order array lists the biggest experiments first) until none are left. */
 template <int KIND>
-__device__ void megakernel_body(const KParams &kp)
+__device__ __forceinline__ void megakernel_body(const KParams &kp)
 {
     extern __shared__ __align__(16) uint8_t lds_dyn[];
     __shared__ Shared sh;
