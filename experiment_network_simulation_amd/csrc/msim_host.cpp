@@ -942,6 +942,44 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
     }
     if (off > 0xFFFFFFF0ull) return fail(out, MSIM_E_LIMIT, "experiment %u: state of %zu bytes too large", e, off);
     H.bytes = (uint32_t)off;
+    {
+        /* the kernel addresses the switch and NIC state as LDS and the rest as
+         * global memory when only the former fits in LDS, taking each array's
+         * side from this order: check that every array lies on its side */
+        const uint64_t hot_lo[2] = {0, H.rw_off}, hot_hi[2] = {H.ro_hot, H.rw_hot};
+        auto within = [&](uint32_t o, uint64_t bytes, bool hot) {
+            if (bytes == 0) return true;
+            const bool in0 = o >= hot_lo[0] && o + bytes <= hot_hi[0], in1 = o >= hot_lo[1] && o + bytes <= hot_hi[1];
+            const bool out0 = o + bytes <= hot_lo[0] || o >= hot_hi[0], out1 = o + bytes <= hot_lo[1] || o >= hot_hi[1];
+            return hot ? (in0 || in1) : (out0 && out1);
+        };
+        const uint64_t WA = H.WA;
+        const bool ok = within(H.o_port, sizeof(PortRO) * n_ports, true) && within(H.o_host, sizeof(HostRO) * n_hosts, true) &&
+            within(H.o_spi, lb == MSIM_LB_SPRAY ? 4ull * n_ports : 0, true) &&
+            within(H.o_tail, n_voq, true) && within(H.o_nslot, n_voq, true) && within(H.o_fmask, 32ull * n_swp, true) &&
+            within(H.o_ow, 4ull * n_ports, true) && within(H.o_pdesc, 4ull * n_swp * Q, true) &&
+            within(H.o_pnxt, (uint64_t)n_swp * Q, true) && within(H.o_pstate, sizeof(PortRW) * n_ports, true) &&
+            within(H.o_scnt, (uint64_t)n_ports * W, true) && within(H.o_sdesc, 4ull * n_ports * W * R, true) &&
+            within(H.o_bl, cc != MSIM_CC_NONE ? 4ull * n_ports : 0, true) &&
+            within(H.o_qlen, cc != MSIM_CC_NONE ? 4ull * n_ports : 0, true) &&
+            within(H.o_ackm, cc != MSIM_CC_NONE ? 4ull * WA * words : 0, true) &&
+            within(H.o_hstate, sizeof(HostRW) * n_hosts, true) && within(H.o_hpc, n_hosts, true) &&
+            within(H.o_ready, 4ull * words, true) &&
+            within(H.o_conn, sizeof(ConnRO) * nconn, false) && within(H.o_grp, sizeof(Grp) * ngrp, false) &&
+            within(H.o_hout, 4ull * nconn, false) && within(H.o_task, sizeof(TaskRO) * n_task, false) &&
+            within(H.o_tpred, 4ull * tpred.size(), false) && within(H.o_cstate, sizeof(ConnRW) * nconn, false) &&
+            within(H.o_trw, sizeof(TaskRW) * n_task, false) &&
+            within(H.o_cc, cc != MSIM_CC_NONE ? sizeof(CcRW) * nconn : 0, false) &&
+            within(H.o_ack, cc != MSIM_CC_NONE ? 2ull * nconn * WA : 0, false) &&
+            within(H.o_hl, cc == MSIM_CC_HPCC ? 12ull * H.hx * nconn : 0, false) &&
+            within(H.o_int, cc == MSIM_CC_HPCC ? 12ull * H.hx * int_records : 0, false) &&
+            within(H.o_cand, lb == MSIM_LB_SPRAY ? 2ull * cand_tbl.size() : 0, false) &&
+            within(H.o_rwoff, lb == MSIM_LB_SPRAY ? 4ull * (nconn + 1) : 0, false) &&
+            within(H.o_sseq, lb == MSIM_LB_SPRAY ? 4ull * nconn : 0, false) &&
+            within(H.o_rnext, lb == MSIM_LB_SPRAY ? 4ull * nconn : 0, false) &&
+            within(H.o_rbits, lb == MSIM_LB_SPRAY ? 4ull * rwoff[nconn] : 0, false);
+        if (!ok) return fail(out, MSIM_E_LIMIT, "experiment %u: internal error: general layout order", e);
+    }
     out.arena.assign(off, 0);
     uint8_t *A = out.arena.data();
     memcpy(A, &H, sizeof H);

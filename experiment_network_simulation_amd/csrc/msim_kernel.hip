@@ -958,9 +958,8 @@ __device__ void finish_state(ExpState *stp, const Shared &sh, uint32_t nwaves, u
 /* ----------------------------------------------------------- one experiment */
 
 /* Where an experiment's arena lives while it runs.  A compile-time choice,
- * so that every array whose place is fixed is addressed as LDS or as global
- * memory; only the split placement picks per array at run time (generic
- * addressing, whose waits cover both LDS and memory accesses). */
+ * so that every array is addressed as LDS or as global memory, never
+ * generically (a generic access's wait covers both LDS and memory). */
 enum { PL_LDS = 0, PL_SPLIT = 1, PL_PORTS = 2, PL_HBM = 3 };
 
 template <int PL, bool TASKS, bool CC, bool SP>
@@ -998,67 +997,77 @@ __device__ __attribute__((always_inline)) void run_experiment(const KParams &kp,
         }
         __syncthreads();
     }
-    auto at = [&](uint32_t off) -> uint8_t * {
-        if (IN_LDS) return lds + off;
-        if (split && off < ro_hot) return lds + off;
-        if (split && off >= rw_off && off < rw_hot) return lds + ro_hot + (off - rw_off);
-        return arena_g + off;
+    /* The layout puts the switch and NIC state (port, host and sprayed-port
+     * tables; queues, pools, staging, port and host state, backlogs, ACK
+     * masks, ready words) in [0, ro_hot) and [rw_off, rw_hot), and the
+     * per-connection and per-task state (hot and cold arrays below) outside;
+     * the host checks that every array lies where this says.  So each array's
+     * place is known here at compile time and addressed as LDS or as global
+     * memory, never generically. */
+    auto hot = [&](uint32_t off) -> uint8_t * {
+        if constexpr (PL == PL_LDS) return lds + off;
+        else if constexpr (PL == PL_SPLIT) return off < ro_hot ? lds + off : lds + ro_hot + (off - rw_off);
+        else return arena_g + off;
+    };
+    auto cold = [&](uint32_t off) -> uint8_t * {
+        if constexpr (PL == PL_LDS) return lds + off;
+        else return arena_g + off;
     };
     Ctx C;
-    C.port = ports ? (const PortRO *)lds : (const PortRO *)at(H->o_port);
-    C.conn = (const ConnRO *)at(H->o_conn);
-    C.grp = (const Grp *)at(H->o_grp);
-    C.hout = (const uint32_t *)at(H->o_hout);
-    C.host = (const HostRO *)at(H->o_host);
-    C.tail = at(H->o_tail);
-    C.nslot = at(H->o_nslot);
-    C.pdesc = (uint32_t *)at(H->o_pdesc);
-    C.pnxt = at(H->o_pnxt);
-    C.fmask = (uint64_t *)at(H->o_fmask);
-    C.ow = (uint32_t *)at(H->o_ow);
-    C.hpc = at(H->o_hpc);
-    C.qlen = (uint32_t *)at(H->o_qlen);
-    C.ps = (PortRW *)at(H->o_pstate);
-    C.scnt = at(H->o_scnt);
-    C.sdesc = (uint32_t *)at(H->o_sdesc);
-    C.cs = (ConnRW *)at(H->o_cstate);
-    C.hs = (HostRW *)at(H->o_hstate);
-    C.ready = (uint32_t *)at(H->o_ready);
+    C.port = ports ? (const PortRO *)lds : (const PortRO *)hot(H->o_port);
+    C.conn = (const ConnRO *)cold(H->o_conn);
+    C.grp = (const Grp *)cold(H->o_grp);
+    C.hout = (const uint32_t *)cold(H->o_hout);
+    C.host = (const HostRO *)hot(H->o_host);
+    C.tail = hot(H->o_tail);
+    C.nslot = hot(H->o_nslot);
+    C.pdesc = (uint32_t *)hot(H->o_pdesc);
+    C.pnxt = hot(H->o_pnxt);
+    C.fmask = (uint64_t *)hot(H->o_fmask);
+    C.ow = (uint32_t *)hot(H->o_ow);
+    C.hpc = hot(H->o_hpc);
+    C.qlen = (uint32_t *)hot(H->o_qlen);
+    C.ps = (PortRW *)hot(H->o_pstate);
+    C.scnt = hot(H->o_scnt);
+    C.sdesc = (uint32_t *)hot(H->o_sdesc);
+    C.cs = (ConnRW *)cold(H->o_cstate);
+    C.hs = (HostRW *)hot(H->o_hstate);
+    C.ready = (uint32_t *)hot(H->o_ready);
     C.n_ports = H->n_ports;
     C.Q = H->Q;
     C.W = H->W;
     C.R = H->R;
     C.n_flows = H->n_flows;
     C.n_task = H->n_task;
-    C.task = (const TaskRO *)at(H->o_task);
-    C.tpred = (const uint32_t *)at(H->o_tpred);
-    C.trw = (TaskRW *)at(H->o_trw);
+    C.task = (const TaskRO *)cold(H->o_task);
+    C.tpred = (const uint32_t *)cold(H->o_tpred);
+    C.trw = (TaskRW *)cold(H->o_trw);
     /* a compile-time 0 in the kernels without congestion control removes its
      * code (and registers) from them */
     C.cc = CC ? H->cc : 0u;
     C.ecn_k = H->ecn_k;
     C.WA = H->WA;
-    C.ccs = (CcRW *)at(H->o_cc);
-    C.qcs = (QcnRW *)at(H->o_cc);
-    C.hps = (HpRW *)at(H->o_cc);
+    C.ccs = (CcRW *)cold(H->o_cc);
+    C.qcs = (QcnRW *)cold(H->o_cc);
+    C.hps = (HpRW *)cold(H->o_cc);
     C.cshift = CC ? H->cshift : (uint32_t)DESC_SHIFT;
     C.hx = H->hx;
-    C.hl = (uint32_t *)at(H->o_hl);
-    C.hint = (uint32_t *)at(H->o_int);
-    C.ack = (uint16_t *)at(H->o_ack);
-    C.bl = (uint32_t *)at(H->o_bl);
-    C.ackm = (uint32_t *)at(H->o_ackm);
+    C.hl = (uint32_t *)cold(H->o_hl);
+    C.hint = (uint32_t *)cold(H->o_int);
+    C.ack = (uint16_t *)cold(H->o_ack);
+    C.bl = (uint32_t *)hot(H->o_bl);
+    C.ackm = (uint32_t *)hot(H->o_ackm);
     C.n_rdy = H->n_rdy;
     C.sp = SP ? H->lb : 0u;       /* a compile-time 0 elsewhere, as for C.cc */
     C.sbits = H->sbits;
     C.seed = H->seed;
     C.n_hosts = H->n_hosts;
-    C.spi = (const uint32_t *)at(H->o_spi);
-    C.cand = (const uint16_t *)at(H->o_cand);
-    C.rwoff = (const uint32_t *)at(H->o_rwoff);
-    C.sseq = (uint32_t *)at(H->o_sseq);
-    C.rnext = (uint32_t *)at(H->o_rnext);
-    C.rbits = (uint32_t *)at(H->o_rbits);
+    C.spi = (const uint32_t *)hot(H->o_spi);
+    C.cand = (const uint16_t *)cold(H->o_cand);
+    C.rwoff = (const uint32_t *)cold(H->o_rwoff);
+    C.sseq = (uint32_t *)cold(H->o_sseq);
+    C.rnext = (uint32_t *)cold(H->o_rnext);
+    C.rbits = (uint32_t *)cold(H->o_rbits);
     uint64_t roff = ((const uint64_t *)(kp.ws + kp.o_rec_off))[x];
     C.rec = roff == ~0ull ? nullptr : (uint32_t *)(kp.ws + roff);
 
