@@ -9,7 +9,10 @@
  * whole tick loop alone: experiments never interact (single-process
  * multi-experiment, Multiverse section 2.2), so the only synchronisation is a
  * workgroup barrier between the phases of a tick.  The experiment's state
- * is copied into LDS when it fits and worked on in place in HBM otherwise.
+ * is copied into LDS when it fits; on the general path, when it does not, the
+ * switch and NIC state, or else the port table, go to LDS and the rest is
+ * worked on in place in HBM (each placement its own inlined copy of the tick
+ * loop, so every access is an LDS or a global one).
  *
  * Tick t follows the step order of Multiverse section 3.2 (Schedule, Send,
  * NIC send, Forward, Transmit, NIC receive) with the forwarding pull-based as
@@ -35,10 +38,13 @@
  * output's word (OR).  Several ports of a
  * switch may hit the same word in one instruction; OR and add do not depend on
  * the order they are applied in, so results are identical on every run.  The
- * other atomics: each workgroup claiming its next experiment, the general
- * path's congestion-control ACK-pending masks (OR) and task-graph counts
- * (subtract), and the periodic completion checks of the compact path (OR,
- * max).
+ * other atomics: each workgroup claiming its next experiment; on the
+ * general path, where the ports of a switch span wavefronts, an output
+ * returning a popped slot to its ingress's free mask (OR), counting the pop
+ * into the word of the output feeding that ingress and updating its own word
+ * (add), the congestion-control queue lengths (add) and ACK-pending masks
+ * (OR) and the task-graph counts (subtract); and the periodic completion
+ * checks of the compact path (OR, max).
  */
 #include <hip/hip_runtime.h>
 
