@@ -1005,11 +1005,11 @@ __device__ __attribute__((always_inline)) void run_experiment(const KParams &kp,
     }
     /* The layout puts the switch and NIC state (port, host and sprayed-port
      * tables; queues, pools, staging, port and host state, backlogs, ACK
-     * masks, ready words) in [0, ro_hot) and [rw_off, rw_hot), and the
-     * per-connection and per-task state (hot and cold arrays below) outside;
-     * the host checks that every array lies where this says.  So each array's
-     * place is known here at compile time and addressed as LDS or as global
-     * memory, never generically. */
+     * masks, ready words: the arrays taken with hot() below) in [0, ro_hot)
+     * and [rw_off, rw_hot), and the per-connection and per-task state (taken
+     * with cold()) outside them; the host checks that every array lies on its
+     * side.  So each array's place is known here at compile time and
+     * addressed as LDS or as global memory, never generically. */
     auto hot = [&](uint32_t off) -> uint8_t * {
         if constexpr (PL == PL_LDS) return lds + off;
         else if constexpr (PL == PL_SPLIT) return off < ro_hot ? lds + off : lds + ro_hot + (off - rw_off);
