@@ -48,6 +48,19 @@ def test_create_reports_sizes(simmod):
     assert [s.flow_count(e) for e in range(4)] == [896, 448, 224, 112]
 
 
+def test_general_layouts_keep_their_sides(simmod):
+    # The general kernels address the switch and NIC state as LDS and the
+    # per-connection state as global memory when only the former fits in LDS,
+    # taking each array's side from the layout order; msim_create checks every
+    # array's side and fails otherwise.  Every general-path kind compiles here:
+    # plain (C5, k=16 fat-tree), task graph (C7), DCTCP (C8), spraying (C9),
+    # DCQCN (C10), HPCC (C11).
+    for cid, kind in [(5, 0), (7, 9), (8, 10), (9, 13), (10, 10), (11, 10)]:
+        s = simmod.Sim(I.make_config(cid, n_exp=2))
+        inf = s.info()
+        assert inf["n_exp"] == 2 and inf["n_compact"] == 0 and inf["main_kernel"] == kind, (cid, inf)
+
+
 def test_flow_counts_match_oracle(simmod, oracle):
     for cid, n in [(2, 6), (3, 28)]:
         b = I.make_config(cid, n_exp=n)
