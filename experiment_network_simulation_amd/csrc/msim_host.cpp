@@ -146,6 +146,84 @@ bool ngrp_fits_ring(const std::vector<Grp> &grp)
     return true;
 }
 
+/* Staging words of the ring format.  Port slot u's word is read by u and
+ * written by the port at the far end of u's cable; stg[u] is chosen so that
+ * the 64 lanes of every wavefront read 64 different LDS banks and write 64
+ * different banks.  It is a proper colouring, with 64 colours, of the edges
+ * u: (u's wavefront as reader, its far end's wavefront as writer) of a
+ * bipartite multigraph in which no node has more than 64 edges, so such a
+ * colouring exists (Konig); it is built edge by edge: take a colour ca free
+ * at the reader and cb free at the writer; if ca is taken at the writer, swap
+ * ca and cb along the path of ca / cb edges that starts there (the path
+ * cannot reach the reader, which has no ca edge), which frees ca at the
+ * writer.  The slots of colour c take c, c + 64, c + 128, ...  Returns false
+ * if a check of the result fails. */
+bool ring_staging(const std::vector<uint32_t> &slot, const std::vector<PortRO> &port, uint32_t n_ports, uint32_t nt,
+                  std::vector<uint32_t> &stg)
+{
+    const uint32_t NW = (nt + 63) / 64;
+    std::vector<int32_t> at_r((size_t)NW * 64, -1), at_w((size_t)NW * 64, -1), col(n_ports, -1);
+    std::vector<uint32_t> rw(n_ports), ww(n_ports);
+    for (uint32_t q = 0; q < n_ports; q++) {
+        rw[q] = slot[q] / 64;
+        ww[q] = slot[port[q].peer] / 64;
+    }
+    std::vector<int32_t> path;
+    for (uint32_t q = 0; q < n_ports; q++) {
+        const uint32_t a = rw[q], b = ww[q];
+        int32_t ca = -1, cb = -1;
+        for (int32_t c = 0; c < 64 && ca < 0; c++)
+            if (at_r[a * 64 + c] < 0) ca = c;
+        for (int32_t c = 0; c < 64 && cb < 0; c++)
+            if (at_w[b * 64 + c] < 0) cb = c;
+        if (ca < 0 || cb < 0) return false;
+        if (at_w[b * 64 + ca] >= 0) {
+            path.clear();
+            uint32_t node = b;
+            bool writer = true;
+            int32_t c = ca;
+            for (;;) {
+                const int32_t e = writer ? at_w[node * 64 + c] : at_r[node * 64 + c];
+                if (e < 0) break;
+                path.push_back(e);
+                node = writer ? rw[e] : ww[e];
+                writer = !writer;
+                c = c == ca ? cb : ca;
+            }
+            for (int32_t e : path) {
+                at_r[rw[e] * 64 + col[e]] = -1;
+                at_w[ww[e] * 64 + col[e]] = -1;
+            }
+            for (int32_t e : path) {
+                col[e] = col[e] == ca ? cb : ca;
+                at_r[rw[e] * 64 + col[e]] = e;
+                at_w[ww[e] * 64 + col[e]] = e;
+            }
+        }
+        col[q] = ca;
+        at_r[a * 64 + ca] = (int32_t)q;
+        at_w[b * 64 + ca] = (int32_t)q;
+    }
+    stg.assign(nt, 0);
+    std::vector<uint32_t> cnt(64, 0);
+    for (uint32_t q = 0; q < n_ports; q++) stg[slot[q]] = (uint32_t)col[q] + 64u * cnt[col[q]]++;
+    /* checks: every word below NW * 64 and used once; within a wavefront, the
+     * words read and the words written fall in 64 different banks */
+    std::vector<uint8_t> used((size_t)NW * 64, 0);
+    std::vector<uint64_t> rb(NW, 0), wb(NW, 0);
+    for (uint32_t q = 0; q < n_ports; q++) {
+        const uint32_t w = stg[slot[q]];
+        if (w >= NW * 64 || used[w]) return false;
+        used[w] = 1;
+        const uint64_t bit = 1ull << (w & 63);
+        const uint32_t wr = slot[port[q].peer] / 64;     /* the wavefront writing this word */
+        if ((rb[rw[q]] & bit) || (wb[wr] & bit)) return false;
+        rb[rw[q]] |= bit;
+        wb[wr] |= bit;
+    }
+    return true;
+}
+
 /* Launch bound of each kernel kind (threads per workgroup). */
 uint32_t kind_max_threads(uint32_t kind)
 {
@@ -596,8 +674,11 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
             for (uint32_t q = pbase[n]; q < pbase[n + 1]; q++) slot[q] = nt++;
         }
         ok = ok && nt <= 1024;
+        std::vector<uint32_t> stg;
+        if (ok && !ring_staging(slot, port, n_ports, nt, stg))
+            return fail(out, MSIM_E_LIMIT, "experiment %u: internal error: ring staging slots", e);
         if (ok) {
-            const uint32_t S = nt - SB;
+            const uint32_t S = nt - SB, NS = (nt + 63) & ~63u;
             ArenaHdr3 H{};
             H.mode = MODE_RING; H.n_flows = (uint32_t)n_flows;
             H.nt = nt; H.H = n_hosts; H.SB = SB; H.Q = Q; H.W = W; H.n_grp = ngrp; H.n_sw = n_sw;
@@ -611,7 +692,7 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
             take(H.o_head, 64ull * n_sw);
             take(H.o_nzw, 32ull * n_sw);
             take(H.o_fw, 8ull * (S + 1));
-            take(H.o_sdesc, 4ull * W * nt);
+            take(H.o_sdesc, 4ull * W * NS);
             take(H.o_dq, 8ull * RING_DQ * SB);
             H.lds_bytes = (uint32_t)off;
             take(H.o_port, sizeof(RingPort) * nt);
@@ -667,6 +748,8 @@ int compile_exp(const msim_batch_spec *s, uint32_t e, bool allow_compact, bool a
                     r.flags = (uint8_t)(PF_USED | (P.alive ? PF_ALIVE : 0) | (P.is_host ? PF_HOST : 0) |
                                         (P.peer_is_host ? PF_PEER_HOST : 0));
                     r.local = P.local; r.deg = P.deg; r.delay = P.delay;
+                    r.stg = (uint16_t)stg[sl];
+                    r.pstg = (uint16_t)stg[slot[fq]];
                     if (P.is_host) {
                         r.row = host[P.host].n_out;
                         rv[sl].mask = host[P.host].n_out == 32 ? ~0u : ((1u << host[P.host].n_out) - 1u);

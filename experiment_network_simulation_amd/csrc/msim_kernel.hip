@@ -2052,7 +2052,11 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     const uint32_t pool = is_sw ? tid - SB : S;                /* this ingress's buffer pool */
     const uint32_t pool0 = is_sw ? tid - local - SB : 0u;      /* pool of its switch's port 0 */
     const uint32_t hb0 = pr.row * 8u + local;                  /* head byte of queue (this ingress -> output 0) */
-    const uint32_t doff = pr.delay * nt, wsz = W * nt;
+    /* staging: tick slots of NS words; this lane's word is pr.stg, its far
+     * end's pr.pstg (a permutation of the slots under which every wavefront
+     * reads, and writes, 64 different LDS banks) */
+    const uint32_t NS = (nt + 63) & ~63u;
+    const uint32_t doff = pr.delay * NS, wsz = W * NS;
     /* this ingress's buffer slot s: pd_me + s * S words, pn_me + s * S bytes */
     LDSP uint8_t *const pd_me = (LDSP uint8_t *)(pdesc + pool);
     LDSP uint8_t *const pn_me = pnxt + pool;
@@ -2092,7 +2096,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
             }
     }
     LDSP RPair *pair_me = pair + tid;                          /* a host's pair records */
-    uint32_t t = t0, par = 0, sb = (t0 % W) * nt;
+    uint32_t t = t0, par = 0, sb = (t0 % W) * NS;
     bool done = false, dead = false;
     uint32_t t_dead = 0;
     /* the next tick at whose end the workgroup checks for completion */
@@ -2112,8 +2116,8 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
     /* with every delay 1, the staging words this lane reads and writes at
      * ticks of parity 0 and 1 */
     const bool port = pr.flags & PF_USED;                      /* slots of absent hosts and gaps have none */
-    LDSP uint32_t *const rd1[2] = {port ? sdesc + tid : zero, port ? sdesc + nt + tid : zero};
-    LDSP uint32_t *const wr1[2] = {port ? sdesc + nt + pr.peer : zero, port ? sdesc + pr.peer : zero};
+    LDSP uint32_t *const rd1[2] = {port ? sdesc + pr.stg : zero, port ? sdesc + NS + pr.stg : zero};
+    LDSP uint32_t *const wr1[2] = {port ? sdesc + NS + pr.pstg : zero, port ? sdesc + pr.pstg : zero};
 
     /* One tick t.  P is t & 1 when the caller knows it at compile time (every
      * delay 1: staging has two slots, so the addresses of a tick of either
@@ -2132,8 +2136,8 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
         } else {
             uint32_t dst = sb + doff;
             if (dst >= wsz) dst -= wsz;
-            rdp = port ? sdesc + sb + tid : zero;
-            wrp = port ? sdesc + dst + pr.peer : zero;
+            rdp = port ? sdesc + sb + pr.stg : zero;
+            wrp = port ? sdesc + dst + pr.pstg : zero;
         }
         LDSP uint32_t *fw_prev = fw + (P ^ 1u) * FWS;           /* what the outputs took at t - 1 */
         LDSP uint32_t *fw_cur = fw + P * FWS;                   /* ... take at t */
@@ -2297,7 +2301,7 @@ __device__ void run_ring(const KParams &kp, uint32_t x, uint8_t *arena_g, uint8_
         }
         t++;
         if constexpr (PK == 2) {
-            sb += nt;
+            sb += NS;
             if (sb == wsz) sb = 0;
         }
         if (t == t_chk) {

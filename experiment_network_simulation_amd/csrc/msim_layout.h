@@ -391,8 +391,15 @@ struct PortPriv {        /* 64 bytes: registers of a thread slot between runs */
  *                      outputs write it again.  Each half holds S + 1 words;
  *                      word S stays 0 (the word a port without a far buffer
  *                      reads).
- * Staging: sdesc[(t mod W) * nt + slot] = descriptor of the packet reaching
- * that port at tick t, 0 for none, rewritten by its feeder every tick.
+ * Staging: sdesc[(t mod W) * NS + stg(slot)] = descriptor of the packet
+ * reaching that port at tick t, 0 for none, rewritten by its feeder every
+ * tick; NS = nt rounded up to 64.  stg permutes the slots so that the 64
+ * lanes of every wavefront read 64 different LDS banks (their own words) and
+ * write 64 different banks (their far ends' words): a colouring with 64
+ * colours (stg mod 64) of the edges of the bipartite multigraph that joins,
+ * for every port slot, its wavefront as reader and its far end's wavefront as
+ * writer, which exists since no wavefront has more than 64 lanes (Konig's
+ * edge-colouring theorem); slots of one colour take stg = colour + 64 k.
  * Digest queue: dq[host * RING_DQ + k], the (flow << 32 | RD) words a host
  * has received but not yet mixed into its digest; a wavefront mixes all its
  * hosts' queues together once one of them is full, and at the end of a run. */
@@ -440,7 +447,8 @@ struct RingPort {        /* 16 bytes, one per thread slot (HBM) */
     uint32_t peer;       /* thread slot at the far end */
     uint32_t row;        /* switch: its switch's first row (switch * 8); host: outgoing connections */
     uint8_t flags, local, deg, delay;
-    uint32_t pad;
+    uint16_t stg;        /* this slot's staging word within a tick slot of the staging ring */
+    uint16_t pstg;       /* ... and the far end's, where this slot's output stages its packet */
 };
 
 struct RingPriv {        /* 32 bytes: registers of a thread slot between runs */
