@@ -61,6 +61,18 @@ def test_general_layouts_keep_their_sides(simmod):
         assert inf["n_exp"] == 2 and inf["n_compact"] == 0 and inf["main_kernel"] == kind, (cid, inf)
 
 
+def test_ring_staging_slots_for_every_c4_experiment(simmod):
+    # The ring layout permutes the staging words so that every wavefront's
+    # reads and writes fall in 64 different LDS banks; msim_create builds the
+    # edge colouring and checks it (one word per port, below the padded slot
+    # count, 64 banks per wavefront on both sides), failing otherwise.  All
+    # 4096 C4 experiments (failed cables included) and C1 take the ring path.
+    for cid, n in [(1, 16), (4, 4096)]:
+        s = simmod.Sim(I.make_config(cid))
+        inf = s.info()
+        assert inf["n_exp"] == n and simmod.KERNEL_NAMES[inf["main_kernel"]] == "msim_megakernel_ring", (cid, inf)
+
+
 def test_flow_counts_match_oracle(simmod, oracle):
     for cid, n in [(2, 6), (3, 28)]:
         b = I.make_config(cid, n_exp=n)
