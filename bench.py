@@ -142,6 +142,27 @@ def measured_traffic(kernel: str, workload_cfg: int, n: int):
     """HBM bytes per launch (for a chunked run: over all its launches) from the
     committed rocprofv3 counter runs in profiles/traffic.json, if one was
     taken on this kernel source, this kernel and this workload; else None."""
+    rec = traffic_record(kernel, workload_cfg, n)
+    return rec["traffic_bytes_per_launch"] if rec is not None else None
+
+
+def traffic_source(kernel: str, workload_cfg: int, n: int, chunked: bool = False) -> str:
+    """Where the bench line's roofline.traffic comes from, with the record's
+    note on the source its counters were taken on, if it has one."""
+    rec = traffic_record(kernel, workload_cfg, n)
+    if rec is None:
+        return "not measured for this kernel source and workload"
+    src = ("rocprofv3 FETCH_SIZE + WRITE_SIZE " + ("over all launches " if chunked else "") +
+           "of this kernel source on this workload, taken in a separate profiled run and stored in "
+           "profiles/traffic.json, each scaled by a plain copy's calibration")
+    if rec.get("source_note"):
+        src += "; " + rec["source_note"] + " (" + rec.get("counters_taken_on_sha256", "")[:8] + ")"
+    return src
+
+
+def traffic_record(kernel: str, workload_cfg: int, n: int):
+    """The profiles/traffic.json record for this kernel source, kernel and
+    workload, or None."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     try:
@@ -155,7 +176,7 @@ def measured_traffic(kernel: str, workload_cfg: int, n: int):
     for rec in recs if isinstance(recs, list) else [recs]:
         if (rec.get("kernel") == kernel and rec.get("kernel_source_sha256") == h.hexdigest()
                 and rec.get("config") == workload_cfg and rec.get("experiments") == n):
-            return rec["traffic_bytes_per_launch"]
+            return rec
     return None
 
 
@@ -292,9 +313,7 @@ def main():
         log(f"[bench] CPU oracle {rate:.3e} packet-hops/s; parity {ok}/{len(sample)}")
 
     traffic = measured_traffic(KERNEL_NAMES[info["main_kernel"]], cid, n)
-    traffic_src = ("rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel source on this workload, taken in a separate "
-                   "profiled run and stored in profiles/traffic.json, each scaled by a plain copy's calibration"
-                   if traffic is not None else "not measured for this kernel source and workload")
+    traffic_src = traffic_source(KERNEL_NAMES[info["main_kernel"]], cid, n)
     out = {
         "metric": "packet-hops/sec (batched, 1 GPU) + % of HBM roofline at E=4096",
         "value": value,
@@ -435,9 +454,7 @@ def chunked_bench(args, cid, n, chunk):
             "unit": "GB/s",
             "frac": alg_bytes / k_s / 1e9 / HBM_PEAK_GBS,
             "traffic": measured_traffic("+".join(sorted(kernels)), cid, n),
-            "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE over all launches of this run's kernel source and "
-                              "workload, in profiles/traffic.json, each scaled by a plain copy's calibration (null: "
-                              "not measured for this source)",
+            "traffic_source": traffic_source("+".join(sorted(kernels)), cid, n, chunked=True),
             "kernel": "+".join(sorted(kernels)),
             "kernel_ms_avg": k_s * 1e3 / len(ids),
             "alg_bytes_per_launch": alg_bytes / len(ids),
